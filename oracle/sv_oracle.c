@@ -1,0 +1,308 @@
+/*
+ * CPU oracle for the compensated-tree float32 sum and the shifted/centred
+ * float32 variance.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark may call it; the product path never
+ * does.  It shares no code, header or constant with the HIP library.
+ *
+ * Sources (cited by page title and section):
+ *   [VAR]  S. Pennacchio, "Variance in float32 with a first-element shift, a
+ *          local centring and a compensated tree sum" (Oct 2026): §1 (the
+ *          naive and the two-term reference formulae), §2 steps 1-4 (the
+ *          kernel), §3 (results tables).
+ *   [ORD]  "Reduction order and compensation solve related but different
+ *          problems": sequential vs pairwise order, the Kahan recurrence.
+ *   [KAHAN] "Kahan's Summation Formula" (blog post): the sequential naive and
+ *          Kahan loops over 10^6 copies of 0.001f.
+ *   TwoSum itself is the published error-free transformation that [VAR] §2
+ *   step 3 cites (Ogita-Rump-Oishi 2005 Alg. 3.1, Shewchuk 1997 Thm 7); the
+ *   pages name it but do not print it.
+ *
+ * Arithmetic contract: IEEE binary32, round to nearest even, every operation
+ * rounded on its own (no FMA contraction, no reassociation, no flush of
+ * subnormals).  Build with -O2 -ffp-contract=off -fno-fast-math on x86-64
+ * (SSE scalar float, so no excess precision).
+ *
+ * Readings of the pages that the pages leave open are marked READING and are
+ * listed in the design notes of the repository.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if defined(__FAST_MATH__)
+#error "the oracle must not be built with fast-math"
+#endif
+#if defined(__FLT_EVAL_METHOD__) && __FLT_EVAL_METHOD__ != 0
+#error "float expressions must be evaluated in float (FLT_EVAL_METHOD 0)"
+#endif
+
+/* ------------------------------------------------------------------ */
+/* TwoSum: s = fl(a+b) and the exact rounding error e, s + e == a + b. */
+/* ------------------------------------------------------------------ */
+static inline float two_sum(float a, float b, float *err) {
+    float s = a + b;
+    float bv = s - a;          /* the part of s that came from b   */
+    float av = s - bv;         /* the part of s that came from a   */
+    float ea = a - av;
+    float eb = b - bv;
+    *err = ea + eb;
+    return s;
+}
+
+float orc_two_sum(float a, float b, float *err) { return two_sum(a, b, err); }
+
+/* Smallest power of two >= n (n >= 1). */
+static int64_t pow2_ceil(int64_t n) {
+    int64_t p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+/*
+ * READING (tree topology, [VAR] §2 step 3): the n values are padded with
+ * +0 to P = 2^ceil(log2 n) (or to the caller's larger power of two) and each
+ * level adds adjacent pairs (2k, 2k+1).  Node k of level l thus covers
+ * elements [k*2^l, (k+1)*2^l).
+ *
+ * Compensated tree: level by level, s'_k = fl(s_2k + s_2k+1) with TwoSum
+ * error e_k, and the error array carries c'_k = fl(fl(c_2k + c_2k+1) + e_k).
+ * The result is fl(s_0 + c_0).
+ * READING (non-finite root): if s_0 is Inf or NaN the result is s_0, so that
+ * Inf and NaN inputs give what a plain sum gives.
+ *
+ * x is read with a stride of `stride` floats.  `pad_to` = 0 means P; a larger
+ * power of two pads further (used to check that extra zero padding leaves
+ * the bits unchanged).  Returns NaN for an invalid pad_to.
+ */
+float orc_tree_sum_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to) {
+    if (n <= 0) return 0.0f;
+    int64_t P = pow2_ceil(n);
+    if (pad_to != 0) {
+        if (pad_to < P || (pad_to & (pad_to - 1)) != 0) return NAN;
+        P = pad_to;
+    }
+    float *s = (float *)malloc((size_t)P * sizeof(float));
+    float *c = (float *)malloc((size_t)P * sizeof(float));
+    if (!s || !c) { free(s); free(c); return NAN; }
+    for (int64_t i = 0; i < P; ++i) {
+        s[i] = (i < n) ? x[i * stride] : 0.0f;
+        c[i] = 0.0f;
+    }
+    for (int64_t len = P; len > 1; len >>= 1) {
+        for (int64_t k = 0; k < len / 2; ++k) {
+            float e;
+            float sk = two_sum(s[2 * k], s[2 * k + 1], &e);
+            float ck = (c[2 * k] + c[2 * k + 1]) + e;
+            s[k] = sk;
+            c[k] = ck;
+        }
+    }
+    float root_s = s[0], root_c = c[0];
+    free(s);
+    free(c);
+    if (!isfinite(root_s)) return root_s;
+    return root_s + root_c;
+}
+
+/* Same topology without the error array: the plain pairwise tree. */
+float orc_tree_plain_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to) {
+    if (n <= 0) return 0.0f;
+    int64_t P = pow2_ceil(n);
+    if (pad_to != 0) {
+        if (pad_to < P || (pad_to & (pad_to - 1)) != 0) return NAN;
+        P = pad_to;
+    }
+    float *s = (float *)malloc((size_t)P * sizeof(float));
+    if (!s) return NAN;
+    for (int64_t i = 0; i < P; ++i) s[i] = (i < n) ? x[i * stride] : 0.0f;
+    for (int64_t len = P; len > 1; len >>= 1)
+        for (int64_t k = 0; k < len / 2; ++k) s[k] = s[2 * k] + s[2 * k + 1];
+    float r = s[0];
+    free(s);
+    return r;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sequential sums ([KAHAN], [ORD]): comparators, not on the hot path.  */
+/* ------------------------------------------------------------------ */
+float orc_seq_naive_f32(const float *x, int64_t n) {
+    float sum = 0.0f;
+    for (int64_t i = 0; i < n; ++i) sum = sum + x[i];
+    return sum;
+}
+
+/* The Kahan recurrence in the blog's form: the stored correction is
+ * subtracted from the next input, and the new correction is the difference
+ * of the sums minus the adjusted input. */
+float orc_seq_kahan_f32(const float *x, int64_t n) {
+    float sum = 0.0f, corr = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float adj = x[i] - corr;
+        float t = sum + adj;
+        corr = (t - sum) - adj;
+        sum = t;
+    }
+    return sum;
+}
+
+/* Neumaier's variant ([ORD]): the branch on magnitudes picks which operand's
+ * low part was lost; the accumulated correction is added at the end. */
+float orc_seq_neumaier_f32(const float *x, int64_t n) {
+    float sum = 0.0f, corr = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float t = sum + x[i];
+        if (fabsf(sum) >= fabsf(x[i]))
+            corr = corr + ((sum - t) + x[i]);
+        else
+            corr = corr + ((x[i] - t) + sum);
+        sum = t;
+    }
+    return sum + corr;
+}
+
+/* ------------------------------------------------------------------ */
+/* Variance of one slice                                                */
+/* ------------------------------------------------------------------ */
+
+/* READING (max(., 0), [VAR] §1 and §2 step 4): NaN propagates (a NaN input
+ * to the max returns NaN), any other value <= 0 gives +0. */
+static inline float max0_nan(float v) {
+    if (v != v) return v;
+    return (v > 0.0f) ? v : 0.0f;
+}
+
+/* READING (ddof rescale, [VAR] §2 step 4): applied after the max as
+ * v * fl(fl(n) / fl(max(n - ddof, 0))); nothing is done when ddof == 0. */
+static inline float ddof_scale(float v, int64_t n, int64_t ddof) {
+    if (ddof == 0) return v;
+    int64_t den = n - ddof;
+    if (den < 0) den = 0;
+    float f = (float)n / (float)den;
+    return v * f;
+}
+
+/* Gather one slice (n elements at `stride`) into a contiguous buffer. */
+static void gather(const float *x, int64_t n, int64_t stride, float *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = x[i * stride];
+}
+
+/*
+ * The kernel of [VAR] §2, one slice.
+ *   step 1  x0 = x[0]; y_i = fl(x_i - x0)
+ *   step 2  m = fl(Sy / fl(n)); d_i = fl(y_i - m)
+ *           READING: Sy is the compensated tree of y when comp_sy != 0 (the
+ *           default), the plain tree of the same topology otherwise.
+ *   step 3  S1 = Tree(d), S2 = Tree(q) with q_i = fl(d_i * d_i)
+ *   step 4  v = max(fl(fl(S2/n) - fl(b*b)), 0) with b = fl(S1/n), then the
+ *           ddof rescale; mean = fl(x0 + m).
+ * READING (empty slice): n == 0 gives var = mean = NaN.
+ */
+static void var_kernel_slice(const float *x, int64_t n, int64_t stride, int64_t ddof,
+                             int comp_sy, float *buf, float *var, float *mean) {
+    if (n <= 0) {
+        *var = NAN;
+        *mean = NAN;
+        return;
+    }
+    gather(x, n, stride, buf);
+    float x0 = buf[0];
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - x0;               /* y */
+    float sy = comp_sy ? orc_tree_sum_f32(buf, n, 1, 0) : orc_tree_plain_f32(buf, n, 1, 0);
+    float fn = (float)n;
+    float m = sy / fn;
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;                /* d */
+    float s1 = orc_tree_sum_f32(buf, n, 1, 0);
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] * buf[i];           /* q */
+    float s2 = orc_tree_sum_f32(buf, n, 1, 0);
+    float a = s2 / fn;
+    float b = s1 / fn;
+    float bb = b * b;
+    float v = max0_nan(a - bb);
+    *var = ddof_scale(v, n, ddof);
+    *mean = x0 + m;
+}
+
+/*
+ * READING (mean in the naive and reference formulae, [VAR] §1): mean(u) is
+ * the plain pairwise tree of u multiplied by the rounded reciprocal fl(1/n).
+ * The identical-values table of [VAR] §3 fixes this choice (a correctly
+ * rounded division would give 0 for the naive formula in every row).
+ */
+static float mean_recip(const float *u, int64_t n) {
+    float inv = 1.0f / (float)n;
+    return orc_tree_plain_f32(u, n, 1, 0) * inv;
+}
+
+/* The two-term reference formula of [VAR] §1: m = mean(x), d = x - m,
+ * v = max(mean(d^2) - mean(d)^2, 0), then the ddof rescale. */
+static void var_reference_slice(const float *x, int64_t n, int64_t stride, int64_t ddof,
+                                float *buf, float *buf2, float *var, float *mean) {
+    if (n <= 0) {
+        *var = NAN;
+        *mean = NAN;
+        return;
+    }
+    gather(x, n, stride, buf);
+    float m = mean_recip(buf, n);
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;
+    for (int64_t i = 0; i < n; ++i) buf2[i] = buf[i] * buf[i];
+    float md = mean_recip(buf, n);
+    float mq = mean_recip(buf2, n);
+    float v = max0_nan(mq - md * md);
+    *var = ddof_scale(v, n, ddof);
+    *mean = m;
+}
+
+/* The naive formula of [VAR] §1: mean((x - mean(x))^2), then the ddof rescale. */
+static void var_naive_slice(const float *x, int64_t n, int64_t stride, int64_t ddof,
+                            float *buf, float *var, float *mean) {
+    if (n <= 0) {
+        *var = NAN;
+        *mean = NAN;
+        return;
+    }
+    gather(x, n, stride, buf);
+    float m = mean_recip(buf, n);
+    for (int64_t i = 0; i < n; ++i) {
+        float d = buf[i] - m;
+        buf[i] = d * d;
+    }
+    *var = ddof_scale(mean_recip(buf, n), n, ddof);
+    *mean = m;
+}
+
+/*
+ * Batched entry points over a row-major [rows, cols] array.
+ *   axis 1: rows slices of length cols (contiguous)
+ *   axis 0: cols slices of length rows (stride cols)
+ * method: 0 kernel (comp_sy 1), 1 kernel with a plain Sy tree, 2 two-term
+ * reference, 3 naive.  mean may be NULL.  Returns 0, or -1 on bad arguments.
+ */
+int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
+                     int method, float *var, float *mean) {
+    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || method < 0 || method > 3)
+        return -1;
+    int64_t nslices = axis == 1 ? rows : cols;
+    int64_t n = axis == 1 ? cols : rows;
+    int64_t stride = axis == 1 ? 1 : cols;
+    int64_t sstride = axis == 1 ? cols : 1;
+    float *buf = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    float *buf2 = (float *)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!buf || !buf2) { free(buf); free(buf2); return -2; }
+    for (int64_t s = 0; s < nslices; ++s) {
+        const float *xs = x + s * sstride;
+        float v, mu;
+        switch (method) {
+        case 0: var_kernel_slice(xs, n, stride, ddof, 1, buf, &v, &mu); break;
+        case 1: var_kernel_slice(xs, n, stride, ddof, 0, buf, &v, &mu); break;
+        case 2: var_reference_slice(xs, n, stride, ddof, buf, buf2, &v, &mu); break;
+        default: var_naive_slice(xs, n, stride, ddof, buf, &v, &mu); break;
+        }
+        var[s] = v;
+        if (mean) mean[s] = mu;
+    }
+    free(buf);
+    free(buf2);
+    return 0;
+}
