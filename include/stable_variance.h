@@ -1,0 +1,141 @@
+/*
+ * stable_variance.h - C ABI of libstable_variance.so (MI355X / gfx950).
+ *
+ * Accurate float32 reductions by a compensated pairwise tree:
+ *
+ *   sv_tree_sum_f32   the sum of n float32 values by a binary tree of TwoSum
+ *                     additions whose exact rounding errors are carried up a
+ *                     second array (Pennacchio, "Variance in float32 with a
+ *                     first-element shift, a local centring and a compensated
+ *                     tree sum", §2 step 3).
+ *   sv_variance_f32   the variance and the mean of each slice of a row-major
+ *                     [rows, cols] array along an axis (same page, §2 steps
+ *                     1-4): shift by the slice's first element, local
+ *                     centring, compensated trees of d and d^2, two-term
+ *                     correction and ddof rescale.
+ *
+ * Arithmetic: IEEE binary32, round to nearest even, every operation rounded
+ * on its own (no FMA contraction, no reassociation, subnormals kept).
+ *
+ * Tree topology (fixed, independent of launch geometry, stream and run):
+ * the n values are padded with +0 to a power of two and each level adds
+ * adjacent pairs, so node k of level l covers elements [k*2^l, (k+1)*2^l).
+ * A node combines (s_l, c_l) and (s_r, c_r) into s = fl(s_l + s_r) with the
+ * TwoSum error e, and c = fl(fl(c_l + c_r) + e).  A tree's value is
+ * fl(s + c) at the root, or s when s is Inf or NaN.  Results are therefore
+ * bit-identical from run to run and equal to the CPU oracle's.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers only (memory from hipMalloc / torch on the current HIP
+ *     device); the caller owns every buffer.  Host pointers are not accepted.
+ *   - The call validates its arguments on the host first.  On any error it
+ *     returns a nonzero status, launches nothing and leaves the outputs
+ *     untouched; sv_last_error_message() then describes the error.
+ *   - The call is asynchronous: it enqueues work on `stream` (a hipStream_t;
+ *     NULL is the default stream) and returns.  Outputs are valid once the
+ *     stream has been synchronised.  Inputs must stay valid until then.
+ *   - Calls never throw and never allocate device memory.
+ *   - Calls that share a workspace must be ordered (same stream); two
+ *     concurrent calls need two workspaces.
+ */
+#ifndef STABLE_VARIANCE_H
+#define STABLE_VARIANCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef int sv_status;
+#define SV_OK 0
+#define SV_ERR_INVALID_ARGUMENT 1 /* bad size, axis, ddof or null pointer        */
+#define SV_ERR_WORKSPACE 2        /* workspace missing, too small or misaligned  */
+#define SV_ERR_NO_DEVICE 3        /* no usable HIP device                        */
+#define SV_ERR_HIP 4              /* a HIP runtime call or a launch failed       */
+#define SV_ERR_UNSUPPORTED 5      /* shape outside what this build supports      */
+
+/* Version of this ABI (SV_ABI_VERSION of the header the library was built with). */
+int sv_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *sv_status_string(sv_status status);
+
+/* Description of the last error raised on the calling thread ("" if none).
+ * The pointer stays valid until the next call on the same thread. */
+const char *sv_last_error_message(void);
+
+/*
+ * Bytes of workspace sv_tree_sum_f32 needs for n values (0 for n <= 0,
+ * (size_t)-1 for an unsupported n).  The workspace must be 256-byte aligned
+ * and ZERO-FILLED before its first use; every successful call leaves it
+ * zero-filled again, so it can be reused by later calls in stream order.
+ */
+size_t sv_tree_sum_f32_workspace_size(int64_t n);
+
+/*
+ * out[0] = compensated tree sum of x[0 .. n).
+ *   x          device pointer to n float32 values (any alignment; n > 0)
+ *   n          number of values, 0 <= n <= 2^40 (n == 0 writes +0)
+ *   out        device pointer to one float32
+ *   workspace  device buffer of sv_tree_sum_f32_workspace_size(n) bytes,
+ *              zero-filled before first use (see above); may be NULL when
+ *              that size is 0
+ *   stream     hipStream_t or NULL
+ * Source: Pennacchio, "Variance in float32 ...", §2 step 3 (the tree of
+ * TwoSum additions with the errors carried up a second array).
+ */
+sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace sv_variance_f32 needs (currently 0 for every supported
+ * shape; (size_t)-1 for an unsupported one).  Same zero-fill contract as
+ * above when nonzero.
+ */
+size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
+
+/*
+ * Variance (and mean) of each slice of the row-major [rows, cols] float32
+ * array x, along `axis`:
+ *   axis 1 or -1  rows slices, each the cols contiguous values of a row;
+ *                 var_out/mean_out have rows entries
+ *   axis 0 or -2  cols slices, each the rows values of a column (stride
+ *                 cols); var_out/mean_out have cols entries
+ * For each slice x[0..n) (Pennacchio, "Variance in float32 ...", §2):
+ *   step 1  y_i = fl(x_i - x_0)
+ *   step 2  m = fl(Tree(y) / fl(n)),  d_i = fl(y_i - m)
+ *   step 3  S1 = Tree(d),  S2 = Tree(fl(d_i * d_i))
+ *   step 4  var = max(fl(fl(S2/n) - fl(b*b)), 0) with b = fl(S1/n), where a
+ *           NaN stays NaN and any other value <= 0 gives +0; if ddof != 0
+ *           var = fl(var * fl(fl(n) / fl(max(n - ddof, 0))));
+ *           mean = fl(x_0 + m).
+ * An empty slice (n == 0) gives var = mean = NaN.
+ *   ddof       >= 0
+ *   mean_out   may be NULL (the mean is then not written)
+ *   workspace  may be NULL when sv_variance_f32_workspace_size(...) == 0
+ * rows and cols must be >= 0 with rows * cols < 2^40.
+ */
+sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
+                          float *var_out, float *mean_out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * Launch-geometry tuning for tests and benchmarks.  A knob only changes how
+ * the work is mapped onto the GPU, never a result bit.  Keys:
+ *   "load_path"   0 = coalesced loads transposed through LDS (default),
+ *                 1 = per-lane contiguous loads
+ *   "reset"       any value: restore every default
+ * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  Not thread
+ * safe with concurrent calls.
+ */
+sv_status sv_set_tuning(const char *key, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STABLE_VARIANCE_H */

@@ -1,0 +1,179 @@
+"""Accurate float32 reductions on MI355X: compensated-tree sum and variance.
+
+Thin Python binding over the C ABI of ``libstable_variance.so``
+(``include/stable_variance.h``).  It only marshals arguments: every step of
+the computation runs in the HIP kernels.  PyTorch provides device memory and
+the current stream.  There is no CPU fallback: if the library is missing or
+no GPU is visible, the calls raise.
+
+    tree_sum(x)                    -> 0-d float32 tensor, compensated tree sum
+    var(x, dim=-1, ddof=0, return_mean=False)
+                                   -> per-slice variance (and mean) of a 2-D
+                                      (or 1-D) float32 tensor
+
+Method: Pennacchio, "Variance in float32 with a first-element shift, a local
+centring and a compensated tree sum", §2 steps 1-4.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB as _LIB_PATH
+
+__all__ = ["tree_sum", "var", "capi", "library_path", "SvError", "set_tuning"]
+
+SV_OK = 0
+_STATUS = {1: "SV_ERR_INVALID_ARGUMENT", 2: "SV_ERR_WORKSPACE", 3: "SV_ERR_NO_DEVICE", 4: "SV_ERR_HIP",
+           5: "SV_ERR_UNSUPPORTED"}
+
+
+class SvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def capi():
+    """The loaded C library with argument types declared (raises if absent)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise ImportError(
+                        f"libstable_variance.so is not built ({_LIB_PATH}); run __graft_entry__.build()")
+                L = ctypes.CDLL(_LIB_PATH)
+                i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+                L.sv_abi_version.restype = ctypes.c_int
+                L.sv_abi_version.argtypes = []
+                L.sv_status_string.restype = ctypes.c_char_p
+                L.sv_status_string.argtypes = [ctypes.c_int]
+                L.sv_last_error_message.restype = ctypes.c_char_p
+                L.sv_last_error_message.argtypes = []
+                L.sv_tree_sum_f32_workspace_size.restype = sz
+                L.sv_tree_sum_f32_workspace_size.argtypes = [i64]
+                L.sv_tree_sum_f32.restype = ctypes.c_int
+                L.sv_tree_sum_f32.argtypes = [vp, i64, vp, vp, sz, vp]
+                L.sv_variance_f32_workspace_size.restype = sz
+                L.sv_variance_f32_workspace_size.argtypes = [i64, i64, ctypes.c_int]
+                L.sv_variance_f32.restype = ctypes.c_int
+                L.sv_variance_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
+                L.sv_set_tuning.restype = ctypes.c_int
+                L.sv_set_tuning.argtypes = [ctypes.c_char_p, i64]
+                _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != SV_OK:
+        msg = capi().sv_last_error_message().decode(errors="replace")
+        raise SvError(status, msg)
+
+
+def set_tuning(key: str, value: int) -> None:
+    """Launch-geometry knob (never changes results); see the C header."""
+    _check(capi().sv_set_tuning(key.encode(), int(value)))
+
+
+# Workspaces: one zero-filled buffer per (device, stream); the library leaves
+# it zero-filled after every call, so it is reused in stream order.
+_workspaces: dict = {}
+
+
+def _workspace(nbytes: int, device, stream_handle: int):
+    import torch
+
+    if nbytes == 0:
+        return None
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _check_tensor(x, name="x"):
+    import torch
+
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {x.dtype}")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {x.device}")
+
+
+def tree_sum(x):
+    """Compensated pairwise tree sum of all elements of a float32 tensor."""
+    import torch
+
+    _check_tensor(x)
+    x = x.contiguous().reshape(-1)
+    n = x.numel()
+    L = capi()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        out = torch.empty((), dtype=torch.float32, device=x.device)
+        need = L.sv_tree_sum_f32_workspace_size(n)
+        if need == ctypes.c_size_t(-1).value:
+            raise SvError(5, f"tree_sum: n = {n} is not supported")
+        ws = _workspace(need, x.device, stream)
+        _check(L.sv_tree_sum_f32(x.data_ptr() if n else None, n, out.data_ptr(),
+                                 ws.data_ptr() if ws is not None else None, need, stream))
+    return out
+
+
+def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
+    """Variance of each slice of a 2-D (or 1-D) float32 tensor along ``dim``.
+
+    Returns a float32 tensor of the non-reduced length (and the mean when
+    ``return_mean``).
+    """
+    import torch
+
+    _check_tensor(x)
+    if x.dim() == 1:
+        x2 = x.reshape(1, -1)
+        axis = 1
+        squeeze = True
+    elif x.dim() == 2:
+        x2 = x
+        if dim not in (0, 1, -1, -2):
+            raise ValueError(f"dim {dim} out of range for a 2-D tensor")
+        axis = dim % 2
+        squeeze = False
+    else:
+        raise ValueError("var expects a 1-D or 2-D tensor")
+    if ddof < 0:
+        raise ValueError("ddof must be >= 0")
+    x2 = x2.contiguous()
+    rows, cols = x2.shape
+    ns = rows if axis == 1 else cols
+    L = capi()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        out = torch.empty(ns, dtype=torch.float32, device=x.device)
+        mean = torch.empty(ns, dtype=torch.float32, device=x.device) if return_mean else None
+        need = L.sv_variance_f32_workspace_size(rows, cols, axis)
+        if need == ctypes.c_size_t(-1).value:
+            raise SvError(5, f"var: shape {tuple(x2.shape)} along axis {axis} is not supported")
+        ws = _workspace(need, x.device, stream)
+        _check(L.sv_variance_f32(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof),
+                                 out.data_ptr() if ns else None,
+                                 mean.data_ptr() if (mean is not None and ns) else None,
+                                 ws.data_ptr() if ws is not None else None, need, stream))
+    if squeeze:
+        out = out.reshape(())
+        mean = mean.reshape(()) if mean is not None else None
+    return (out, mean) if return_mean else out

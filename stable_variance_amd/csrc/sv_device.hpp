@@ -1,0 +1,287 @@
+// Device building blocks of the compensated pairwise tree on gfx950 (CDNA4).
+//
+// Method: Pennacchio, "Variance in float32 with a first-element shift, a
+// local centring and a compensated tree sum", §2 step 3: a binary tree whose
+// levels add pairs of partial sums with TwoSum, the exact errors carried up a
+// second array, the result being the final sum plus the final carry.
+//
+// Topology (fixed): values padded with +0 to a power of two, adjacent pairs
+// at each level, so a node covers a power-of-two aligned range.  On the GPU a
+// lane owns E consecutive values (in-lane levels), the 64 lanes of a wave own
+// 64 consecutive lane ranges (6 cross-lane levels) and the waves of a
+// workgroup own consecutive wave ranges (LDS levels).  Larger power-of-two
+// tiles than the data needs only add +0 padding, which leaves the result bits
+// unchanged (TwoSum(a, +0) = (a, +0) up to the sign of a zero, and the carry
+// of a compensated tree is never -0).
+//
+// Node order.  TwoSum's error is the unique exact value a + b - fl(a + b), so
+// a node combined as (left, right) or (right, left) has the same bits on a
+// finite sum; the cross-lane levels use that freedom.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#if defined(__FAST_MATH__)
+#error "stable_variance must be built without fast-math (TwoSum needs exact IEEE rounding)"
+#endif
+#if defined(__FINITE_MATH_ONLY__) && __FINITE_MATH_ONLY__
+#error "stable_variance must be built without finite-math-only"
+#endif
+
+namespace sv {
+
+struct Node {
+  float s;  // partial sum
+  float c;  // carried rounding errors
+};
+
+// ---------------------------------------------------------------- nodes
+
+// TwoSum of the two partial sums, the error added to the sum of the carries.
+__device__ __forceinline__ Node combine(Node l, Node r) {
+  const float s = l.s + r.s;
+  const float bv = s - l.s;
+  const float av = s - bv;
+  const float e = (l.s - av) + (r.s - bv);
+  return {s, (l.c + r.c) + e};
+}
+
+// A level-1 node from two raw values.  The carry is fl(fl(0 + 0) + e), i.e.
+// e with a -0 turned into +0 (needed for the exact sign of an all -0 sum).
+__device__ __forceinline__ Node leaf_canon(float a, float b) {
+  const float s = a + b;
+  const float bv = s - a;
+  const float av = s - bv;
+  const float e = (a - av) + (b - bv);
+  return {s, 0.0f + e};
+}
+
+// Level-1 node whose carry keeps e as is.  Only the sign of a zero carry can
+// differ from leaf_canon, which the variance outputs never see (S1 enters
+// squared, and the sum of y or of d^2 is never -0).
+__device__ __forceinline__ Node leaf_fast(float a, float b) {
+  const float s = a + b;
+  const float bv = s - a;
+  const float av = s - bv;
+  return {s, (a - av) + (b - bv)};
+}
+
+// Nodes of non-negative values (the tree of d^2): every partial sum is >= 0,
+// so the larger operand is known after one max/min, and Fast2Sum (Dekker)
+// gives the same exact error as TwoSum in 3 operations instead of 4.  The
+// sum itself is formed from the operands directly, so a NaN still
+// propagates through s; a non-finite s makes the root return s anyway.
+__device__ __forceinline__ Node combine_nn(Node l, Node r) {
+  const float s = l.s + r.s;
+  const float hi = __builtin_fmaxf(l.s, r.s);
+  const float lo = __builtin_fminf(l.s, r.s);
+  const float e = lo - (s - hi);
+  return {s, (l.c + r.c) + e};
+}
+
+__device__ __forceinline__ Node leaf_nn(float a, float b) {
+  const float s = a + b;
+  const float hi = __builtin_fmaxf(a, b);
+  const float lo = __builtin_fminf(a, b);
+  return {s, lo - (s - hi)};
+}
+
+// Value of a tree at its root: fl(s + c), or s when s is Inf or NaN.
+__device__ __forceinline__ float root_value(Node n) {
+  return __builtin_isfinite(n.s) ? n.s + n.c : n.s;
+}
+
+__device__ __forceinline__ Node zero_node() { return {0.0f, 0.0f}; }
+
+// ---------------------------------------------------------------- in-lane trees
+
+enum LeafKind { LEAF_CANON = 0, LEAF_FAST = 1, LEAF_NN = 2 };
+
+// Compensated tree over v[OFF .. OFF+N) (N a power of two >= 2).
+template <int LEAF, int OFF, int N, int E>
+__device__ __forceinline__ Node lane_tree(const float (&v)[E]) {
+  static_assert(N >= 2 && (N & (N - 1)) == 0, "power of two");
+  if constexpr (N == 2) {
+    if constexpr (LEAF == LEAF_CANON) return leaf_canon(v[OFF], v[OFF + 1]);
+    else if constexpr (LEAF == LEAF_FAST) return leaf_fast(v[OFF], v[OFF + 1]);
+    else return leaf_nn(v[OFF], v[OFF + 1]);
+  } else {
+    const Node l = lane_tree<LEAF, OFF, N / 2, E>(v);
+    const Node r = lane_tree<LEAF, OFF + N / 2, N / 2, E>(v);
+    if constexpr (LEAF == LEAF_NN) return combine_nn(l, r);
+    else return combine(l, r);
+  }
+}
+
+// Tree over an array of nodes nd[OFF .. OFF+N).
+template <int OFF, int N, int K>
+__device__ __forceinline__ Node node_tree(const Node (&nd)[K]) {
+  if constexpr (N == 1) {
+    return nd[OFF];
+  } else {
+    return combine(node_tree<OFF, N / 2, K>(nd), node_tree<OFF + N / 2, N / 2, K>(nd));
+  }
+}
+
+// The two trees of the second pass, d_i = fl(y_i - m) and q_i = fl(d_i*d_i),
+// built leaf pair by leaf pair so that only log2(E) partial nodes stay live.
+// MASK: element OFF+i of this lane is beyond the slice when OFF+i >= valid;
+// its d and q are then +0 (the padding of the tree), not fl(0 - m).
+template <bool MASK, int OFF, int N, int E>
+__device__ __forceinline__ void lane_tree_dq(const float (&y)[E], float m, int valid, Node &nd, Node &nq) {
+  if constexpr (N == 2) {
+    float d0 = y[OFF] - m;
+    float d1 = y[OFF + 1] - m;
+    if constexpr (MASK) {
+      d0 = (OFF < valid) ? d0 : 0.0f;
+      d1 = (OFF + 1 < valid) ? d1 : 0.0f;
+    }
+    const float q0 = d0 * d0;
+    const float q1 = d1 * d1;
+    nd = leaf_fast(d0, d1);
+    nq = leaf_nn(q0, q1);
+  } else {
+    Node ld, lq, rd, rq;
+    lane_tree_dq<MASK, OFF, N / 2, E>(y, m, valid, ld, lq);
+    lane_tree_dq<MASK, OFF + N / 2, N / 2, E>(y, m, valid, rd, rq);
+    nd = combine(ld, rd);
+    nq = combine_nn(lq, rq);
+  }
+}
+
+// ---------------------------------------------------------------- cross-lane levels
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls (gfx9 family)
+constexpr int DPP_QUAD_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ Node dpp_node(Node n) {
+  return {dpp<CTRL>(n.s), dpp<CTRL>(n.c)};
+}
+
+__device__ __forceinline__ Node shfl_xor_node(Node n, int mask) {
+  return {__shfl_xor(n.s, mask, 64), __shfl_xor(n.c, mask, 64)};
+}
+
+// The six cross-lane levels: lane k's node covers lane range k; afterwards
+// every lane holds the wave's node.  Level 1 pairs lanes (2k, 2k+1), level 2
+// pairs of pairs, and so on.  The mirror permutations reach the right sibling
+// because all lanes of the previous group already hold the same node.
+template <bool NN>
+__device__ __forceinline__ Node wave_tree(Node n) {
+  auto comb = [](Node a, Node b) { return NN ? combine_nn(a, b) : combine(a, b); };
+  n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
+  n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
+  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
+  n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
+  n = comb(n, shfl_xor_node(n, 16));
+  n = comb(n, shfl_xor_node(n, 32));
+  return n;
+}
+
+// ---------------------------------------------------------------- loads
+
+// Wave-scope ordering of LDS traffic between the lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of floats of LDS one wave needs to transpose a 64*E tile: each
+// reader lane's E values are padded by 4 floats so that neither the
+// coalesced 16-byte writes nor the lane-contiguous 16-byte reads of 16
+// consecutive lanes share a bank.
+template <int E>
+constexpr int lds_floats_per_wave() { return 64 * (E + 4); }
+
+// Values p[lane*E + i], i < E, of a 64*E tile starting at p; elements at or
+// beyond `len` read as 0 (len may be <= 0).
+//
+// LOADP 0: coalesced loads (each instruction covers 64 consecutive 16-byte
+//          chunks, or 64 consecutive floats when !VEC), transposed through
+//          this wave's LDS region into lane-contiguous order.
+// LOADP 1: each lane loads its own E contiguous values directly.
+// VEC: 16-byte loads, p must be 16-byte aligned.
+// A wave whose tile lies entirely inside the data takes a branch-free path;
+// a ragged tile (the slice's last) loads single floats at clamped addresses.
+template <int E, bool VEC, int LOADP>
+__device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t len, float *__restrict__ lds,
+                                          float (&v)[E], int lane) {
+  static_assert(E >= 4 && (E & (E - 1)) == 0, "E must be a power of two >= 4");
+  constexpr int J = E / 4;
+  constexpr int STR = E + 4;
+  constexpr int TILE = 64 * E;
+  const bool full = len >= TILE;  // wave-uniform
+  // ragged: number of valid values in [0, TILE], and a safe index for loads
+  const int lim = len <= 0 ? 0 : (len >= TILE ? TILE : (int)len);
+  const int last = lim > 0 ? lim - 1 : 0;
+  if constexpr (LOADP == 1) {
+    const int e0 = lane * E;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if constexpr (VEC) {
+          const float4 g = *reinterpret_cast<const float4 *>(p + e0 + 4 * j);
+          v[4 * j] = g.x; v[4 * j + 1] = g.y; v[4 * j + 2] = g.z; v[4 * j + 3] = g.w;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[4 * j + t] = p[e0 + 4 * j + t];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = e0 + i;
+        const float g = p[e < last ? e : last];
+        v[i] = (e < lim) ? g : 0.0f;
+      }
+    }
+  } else {
+    if (full && VEC) {
+      float4 g[J];
+#pragma unroll
+      for (int k = 0; k < J; ++k) g[k] = *reinterpret_cast<const float4 *>(p + 256 * k + 4 * lane);
+#pragma unroll
+      for (int k = 0; k < J; ++k) {
+        const int e = 256 * k + 4 * lane;
+        *reinterpret_cast<float4 *>(lds + (e / E) * STR + (e % E)) = g[k];
+      }
+    } else {
+      float g[E];
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int e = 64 * k + lane;
+        if (full) {
+          g[k] = p[e];
+        } else {
+          const float t = p[e < last ? e : last];
+          g[k] = (e < lim) ? t : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int e = 64 * k + lane;
+        lds[(e / E) * STR + (e % E)] = g[k];
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float4 t = *reinterpret_cast<const float4 *>(lds + lane * STR + 4 * j);
+      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+    wave_lds_sync();
+  }
+}
+
+}  // namespace sv

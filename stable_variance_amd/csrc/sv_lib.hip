@@ -1,0 +1,551 @@
+// libstable_variance: compensated-tree float32 sum and variance on gfx950.
+//
+// Method: Pennacchio, "Variance in float32 with a first-element shift, a
+// local centring and a compensated tree sum", §2 steps 1-4.  The C ABI is
+// declared (and its contract stated) in include/stable_variance.h.
+//
+// Kernels
+//   k_tree_sum   one workgroup per group of 2^g tiles of 64*E*W values; tile
+//                nodes are combined in tree order, each group node is written
+//                to the workspace, and the last workgroup to finish (a ticket
+//                counter) combines the group nodes in tree order.
+//   k_var_rows   axis 1: one workgroup per row; the W waves own consecutive
+//                64*E ranges of the row, each lane E consecutive values.  The
+//                row stays in registers between the two passes (y, then d and
+//                d^2), so HBM is read once.
+//   k_var_cols   axis 0: lanes own columns (coalesced across a row), waves own
+//                consecutive blocks of E rows, so every tree level before the
+//                cross-wave ones is in-lane.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/stable_variance.h"
+#include "sv_device.hpp"
+
+using sv::Node;
+
+namespace {
+
+// ------------------------------------------------------------------ device helpers
+
+// Combine the wave nodes of the W waves of a workgroup (wave w covers the
+// w-th consecutive range).  Every thread returns the workgroup's node.
+template <int W, bool NN>
+__device__ __forceinline__ Node block_tree(Node n, Node *slots, int w, int lane) {
+  if constexpr (W == 1) {
+    return n;
+  } else {
+    if (lane == 0) slots[w] = n;
+    __syncthreads();
+    Node nd[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) nd[i] = slots[i];
+    __syncthreads();
+    if constexpr (NN) {
+      // pairwise over W nodes with the non-negative node
+      Node t[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) t[i] = nd[i];
+#pragma unroll
+      for (int len = W; len > 1; len >>= 1)
+#pragma unroll
+        for (int k = 0; k < len / 2; ++k) t[k] = sv::combine_nn(t[2 * k], t[2 * k + 1]);
+      return t[0];
+    } else {
+      return sv::node_tree<0, W, W>(nd);
+    }
+  }
+}
+
+// Step 4 of the method: two-term correction, NaN-propagating max with 0,
+// ddof rescale, and the mean x0 + m.
+__device__ __forceinline__ void finalize(Node nd, Node nq, float x0, float m, int64_t n, int64_t ddof,
+                                         float *var_out, float *mean_out) {
+  const float fn = (float)n;
+  const float s1 = sv::root_value(nd);
+  const float s2 = sv::root_value(nq);
+  const float a = s2 / fn;
+  const float b = s1 / fn;
+  const float bb = b * b;
+  float v = a - bb;
+  v = (v != v) ? v : ((v > 0.0f) ? v : 0.0f);
+  if (ddof != 0) {
+    int64_t den = n - ddof;
+    if (den < 0) den = 0;
+    const float f = fn / (float)den;
+    v = v * f;
+  }
+  *var_out = v;
+  if (mean_out) *mean_out = x0 + m;
+}
+
+__device__ __forceinline__ void store_node_agent(Node *dst, Node v) {
+  __hip_atomic_store(reinterpret_cast<unsigned *>(&dst->s), __builtin_bit_cast(unsigned, v.s), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(reinterpret_cast<unsigned *>(&dst->c), __builtin_bit_cast(unsigned, v.c), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ Node load_node_agent(const Node *src) {
+  const unsigned s = __hip_atomic_load(reinterpret_cast<const unsigned *>(&src->s), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned c = __hip_atomic_load(reinterpret_cast<const unsigned *>(&src->c), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return {__builtin_bit_cast(float, s), __builtin_bit_cast(float, c)};
+}
+
+// ------------------------------------------------------------------ tree sum
+
+constexpr int SUM_E = 64;
+constexpr int SUM_W = 4;
+constexpr int64_t SUM_TILE = 64LL * SUM_E * SUM_W;  // 16384 values per tile
+constexpr int SUM_MAX_GROUP = 1024;                 // tiles per workgroup (2^10)
+constexpr int SUM_TOP_PER_THREAD = 32;              // group nodes per thread at the top
+constexpr int SUM_MAX_BLOCKS = 64 * SUM_W * SUM_TOP_PER_THREAD;  // 8192
+constexpr size_t SUM_WS_HEADER = 256;               // ticket counter, padded
+
+template <int E, int W, bool VEC, int LOADP>
+__global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_group,
+                                                     Node *__restrict__ part, unsigned *__restrict__ counter,
+                                                     float *__restrict__ out) {
+  constexpr int64_t TILE = 64LL * E * W;
+  constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
+  constexpr int KG = SUM_MAX_GROUP / (64 * W);
+  static_assert(KG >= 1 && SUM_MAX_GROUP % (64 * W) == 0, "group layout");
+  __shared__ float lds[W * LPW];
+  __shared__ Node slots[W];
+  __shared__ Node gnodes[SUM_MAX_GROUP];
+  __shared__ unsigned is_last;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t G = 1LL << log2_group;
+  const int64_t t_begin = (int64_t)blockIdx.x * G;
+
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t t = t_begin + g;
+    Node tn = sv::zero_node();
+    if (t * TILE < n) {  // uniform over the workgroup
+      const int64_t base = t * TILE + (int64_t)w * 64 * E;
+      float v[E];
+      sv::load_tile<E, VEC, LOADP>(x + base, n - base, lds + w * LPW, v, lane);
+      Node ln = sv::lane_tree<sv::LEAF_CANON, 0, E, E>(v);
+      ln = sv::wave_tree<false>(ln);
+      tn = block_tree<W, false>(ln, slots, w, lane);
+    }
+    if (threadIdx.x == 0) gnodes[g] = tn;
+  }
+  __syncthreads();
+
+  Node grp;
+  if (G == 1) {
+    grp = gnodes[0];
+  } else {
+    // Tree over the G tile nodes (padded with zero nodes to SUM_MAX_GROUP).
+    Node nd[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int idx = threadIdx.x * KG + k;
+      nd[k] = (idx < G) ? gnodes[idx] : sv::zero_node();
+    }
+    Node r = sv::node_tree<0, KG, KG>(nd);
+    r = sv::wave_tree<false>(r);
+    grp = block_tree<W, false>(r, slots, w, lane);
+  }
+
+  if (threadIdx.x == 0) {
+    store_node_agent(part + blockIdx.x, grp);
+    __threadfence();
+    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (ticket == gridDim.x - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+
+  // Last workgroup: tree over the gridDim.x group nodes, padded with zeros.
+  constexpr int K = SUM_TOP_PER_THREAD;
+  static_assert(64 * W * K == SUM_MAX_BLOCKS, "top layout");
+  Node nd[K];
+  const int nb = (int)gridDim.x;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int idx = threadIdx.x * K + k;
+    nd[k] = (idx < nb) ? load_node_agent(part + idx) : sv::zero_node();
+  }
+  Node r = sv::node_tree<0, K, K>(nd);
+  r = sv::wave_tree<false>(r);
+  r = block_tree<W, false>(r, slots, w, lane);
+  if (threadIdx.x == 0) {
+    out[0] = sv::root_value(r);
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) out[i] = value;
+}
+
+// ------------------------------------------------------------------ variance, axis 1
+
+template <int E, int W, bool VEC, int LOADP>
+__global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t ddof,
+                                                     float *__restrict__ var_out, float *__restrict__ mean_out) {
+  constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
+  __shared__ float lds[W * LPW];
+  __shared__ Node slots[3][W];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const float *__restrict__ p = x + row * ld;
+  const int64_t base = (int64_t)w * 64 * E;
+
+  float v[E];
+  sv::load_tile<E, VEC, LOADP>(p + base, n - base, lds + w * LPW, v, lane);
+  const float x0 = p[0];
+
+  // step 1: shift by the first element (padding stays +0)
+  const bool full = base + 64 * E <= n;
+  int64_t vl = n - base - (int64_t)lane * E;
+  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+  }
+
+  // step 2: m = Tree(y) / n
+  Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+  ny = sv::wave_tree<false>(ny);
+  ny = block_tree<W, false>(ny, slots[0], w, lane);
+  const float m = sv::root_value(ny) / (float)n;
+
+  // step 3: Tree(d), Tree(d^2)
+  Node nd, nq;
+  if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+  else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+  nd = sv::wave_tree<false>(nd);
+  nq = sv::wave_tree<true>(nq);
+  nd = block_tree<W, false>(nd, slots[1], w, lane);
+  nq = block_tree<W, true>(nq, slots[2], w, lane);
+
+  // step 4
+  if (threadIdx.x == 0) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+}
+
+// ------------------------------------------------------------------ variance, axis 0
+
+template <int E, int W>
+__global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
+                                                     float *__restrict__ var_out, float *__restrict__ mean_out) {
+  __shared__ Node sy[W][64];
+  __shared__ Node sd[W][64];
+  __shared__ Node sq[W][64];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const bool colok = col < C;
+  const int64_t r0 = (int64_t)w * E;
+
+  // Loads: for a fixed row the 64 lanes read 64 consecutive floats.  Out of
+  // range rows/columns read a clamped in-range address and are replaced by 0.
+  const bool full = r0 + E <= R;
+  const bool allcols = (int64_t)blockIdx.x * 64 + 64 <= C;
+  const int64_t ccol = colok ? col : C - 1;
+  float v[E];
+  if (full && allcols) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = x[(r0 + i) * C + col];
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t r = r0 + i;
+      const float t = x[(r < R ? r : R - 1) * C + ccol];
+      v[i] = (colok && r < R) ? t : 0.0f;
+    }
+  }
+  const float x0 = x[ccol];
+  int64_t vl = R - r0;
+  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+  }
+
+  Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+  sy[w][lane] = ny;
+  __syncthreads();
+  {
+    Node nn[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) nn[i] = sy[i][lane];
+    ny = sv::node_tree<0, W, W>(nn);
+  }
+  const float m = sv::root_value(ny) / (float)R;
+
+  Node nd, nq;
+  if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+  else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+  sd[w][lane] = nd;
+  sq[w][lane] = nq;
+  __syncthreads();
+  if (w == 0 && colok) {
+    Node a[W], b[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      a[i] = sd[i][lane];
+      b[i] = sq[i][lane];
+    }
+#pragma unroll
+    for (int len = W; len > 1; len >>= 1)
+#pragma unroll
+      for (int k = 0; k < len / 2; ++k) {
+        a[k] = sv::combine(a[2 * k], a[2 * k + 1]);
+        b[k] = sv::combine_nn(b[2 * k], b[2 * k + 1]);
+      }
+    finalize(a[0], b[0], x0, m, R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+thread_local char g_err[512];
+int g_load_path = 0;  // 0: LDS transpose, 1: per-lane contiguous loads
+
+sv_status fail(sv_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sv_status ok() {
+  g_err[0] = 0;
+  return SV_OK;
+}
+
+sv_status check_device() {
+  int cnt = 0;
+  const hipError_t e = hipGetDeviceCount(&cnt);
+  if (e != hipSuccess || cnt <= 0) return fail(SV_ERR_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  return SV_OK;
+}
+
+sv_status check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_log2(int64_t v) {
+  int l = 0;
+  while ((1LL << l) < v) ++l;
+  return l;
+}
+
+constexpr int64_t SUM_MAX_N = 1LL << 37;
+constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
+constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel
+constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
+
+struct SumPlan {
+  int log2_group;
+  int64_t blocks;
+};
+
+SumPlan plan_sum(int64_t n) {
+  const int64_t tiles = (n + SUM_TILE - 1) / SUM_TILE;
+  int lg = ceil_log2(tiles) - ceil_log2(SUM_MAX_BLOCKS);
+  if (lg < 0) lg = 0;
+  const int64_t G = 1LL << lg;
+  return {lg, (tiles + G - 1) / G};
+}
+
+size_t sum_workspace_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  const SumPlan p = plan_sum(n);
+  return SUM_WS_HEADER + (size_t)p.blocks * sizeof(Node);
+}
+
+template <bool VEC, int LOADP>
+void launch_sum(const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
+                hipStream_t st) {
+  k_tree_sum<SUM_E, SUM_W, VEC, LOADP><<<dim3((unsigned)p.blocks), dim3(64 * SUM_W), 0, st>>>(x, n, p.log2_group, part,
+                                                                                                 counter, out);
+}
+
+template <int E, int W>
+void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
+                    float *mean, hipStream_t st) {
+  const dim3 grid((unsigned)rows), block(64 * W);
+  if (vec) {
+    if (g_load_path == 0) k_var_rows<E, W, true, 0><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
+    else k_var_rows<E, W, true, 1><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
+  } else {
+    if (g_load_path == 0) k_var_rows<E, W, false, 0><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
+    else k_var_rows<E, W, false, 1><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
+  }
+}
+
+template <int E, int W>
+void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
+  const dim3 grid((unsigned)((C + 63) / 64)), block(64 * W);
+  k_var_cols<E, W><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char *sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_INVALID_ARGUMENT: return "SV_ERR_INVALID_ARGUMENT";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE";
+    case SV_ERR_NO_DEVICE: return "SV_ERR_NO_DEVICE";
+    case SV_ERR_HIP: return "SV_ERR_HIP";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+    default: return "SV_ERR_UNKNOWN";
+  }
+}
+
+const char *sv_last_error_message(void) { return g_err; }
+
+size_t sv_tree_sum_f32_workspace_size(int64_t n) {
+  if (n > SUM_MAX_N) return (size_t)-1;
+  return sum_workspace_bytes(n);
+}
+
+sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: n = %lld < 0", (long long)n);
+  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f32: n = %lld above 2^37", (long long)n);
+  if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: out is NULL");
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: x is NULL with n > 0");
+  const size_t need = sum_workspace_bytes(n);
+  if (need > 0) {
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f32: workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f32: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f32: workspace is not 256-byte aligned");
+  }
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (n == 0) {
+    k_fill<<<1, 64, 0, st>>>(out, 1, 0.0f);
+    return check_launch("sv_tree_sum_f32");
+  }
+  const SumPlan p = plan_sum(n);
+  unsigned *counter = reinterpret_cast<unsigned *>(workspace);
+  Node *part = reinterpret_cast<Node *>(reinterpret_cast<char *>(workspace) + SUM_WS_HEADER);
+  const bool vec = aligned16(x);
+  if (vec) {
+    if (g_load_path == 0) launch_sum<true, 0>(x, n, p, part, counter, out, st);
+    else launch_sum<true, 1>(x, n, p, part, counter, out, st);
+  } else {
+    if (g_load_path == 0) launch_sum<false, 0>(x, n, p, part, counter, out, st);
+    else launch_sum<false, 1>(x, n, p, part, counter, out, st);
+  }
+  return check_launch("sv_tree_sum_f32");
+}
+
+size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis) {
+  if (rows < 0 || cols < 0) return (size_t)-1;
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2) return (size_t)-1;
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t n = ax1 ? cols : rows;
+  if (ax1 ? (n > ROWS_MAX_N) : (n > COLS_MAX_R)) return (size_t)-1;
+  return 0;
+}
+
+sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, float *var_out,
+                          float *mean_out, void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (rows < 0 || cols < 0)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: negative shape [%lld, %lld]", (long long)rows,
+                (long long)cols);
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: axis %d not in {0, 1, -1, -2}", axis);
+  if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: ddof = %lld < 0", (long long)ddof);
+  if (cols > 0 && rows > VAR_MAX_ELEMS / cols)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: rows * cols above 2^40");
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t nslices = ax1 ? rows : cols;
+  const int64_t n = ax1 ? cols : rows;
+  if (nslices == 0) return ok();
+  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: var_out is NULL");
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: x is NULL");
+  if (nslices > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: %lld slices exceed the grid", (long long)nslices);
+  if (ax1 && n > ROWS_MAX_N)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: axis-1 slices of length %lld above %lld", (long long)n,
+                (long long)ROWS_MAX_N);
+  if (!ax1 && n > COLS_MAX_R)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: axis-0 slices of length %lld above %lld", (long long)n,
+                (long long)COLS_MAX_R);
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (n == 0) {
+    const unsigned blocks = (unsigned)((nslices + 255) / 256);
+    k_fill<<<blocks, 256, 0, st>>>(var_out, nslices, __builtin_nanf(""));
+    if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
+    return check_launch("sv_variance_f32");
+  }
+  if (ax1) {
+    const bool vec = aligned16(x) && (cols % 4 == 0);
+    if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    else if (n <= 1024) launch_rows_ew<16, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    else if (n <= 4096) launch_rows_ew<64, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    else launch_rows_ew<64, 4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+  } else {
+    if (n <= 4) launch_cols_ew<4, 1>(x, rows, cols, ddof, var_out, mean_out, st);
+    else if (n <= 16) launch_cols_ew<16, 1>(x, rows, cols, ddof, var_out, mean_out, st);
+    else if (n <= 64) launch_cols_ew<64, 1>(x, rows, cols, ddof, var_out, mean_out, st);
+    else if (n <= 128) launch_cols_ew<64, 2>(x, rows, cols, ddof, var_out, mean_out, st);
+    else if (n <= 256) launch_cols_ew<64, 4>(x, rows, cols, ddof, var_out, mean_out, st);
+    else if (n <= 512) launch_cols_ew<64, 8>(x, rows, cols, ddof, var_out, mean_out, st);
+    else launch_cols_ew<64, 16>(x, rows, cols, ddof, var_out, mean_out, st);
+  }
+  return check_launch("sv_variance_f32");
+}
+
+sv_status sv_set_tuning(const char *key, int64_t value) {
+  if (!key) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: key is NULL");
+  if (strcmp(key, "load_path") == 0) {
+    if (value != 0 && value != 1) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: load_path must be 0 or 1");
+    g_load_path = (int)value;
+    return ok();
+  }
+  if (strcmp(key, "reset") == 0) {
+    g_load_path = 0;
+    return ok();
+  }
+  return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: unknown key '%s'", key);
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function the header declares, and
+reject bad arguments on the host before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import stable_variance_amd as sv
+from stable_variance_amd import build as libbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stable_variance.h")
+
+SV_ERR_INVALID_ARGUMENT, SV_ERR_WORKSPACE, SV_ERR_NO_DEVICE, SV_ERR_UNSUPPORTED = 1, 2, 3, 5
+BAD = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails on the host first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(libbuild.LIB):
+        libbuild.build()
+    return sv.capi()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("sv_tree_sum_f32", "sv_variance_f32", "sv_tree_sum_f32_workspace_size",
+              "sv_variance_f32_workspace_size", "sv_status_string", "sv_last_error_message", "sv_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.sv_abi_version() == 1
+    assert L.sv_status_string(0) == b"SV_OK"
+    assert L.sv_status_string(3) == b"SV_ERR_NO_DEVICE"
+    assert L.sv_status_string(99) == b"SV_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(L):
+    assert L.sv_tree_sum_f32_workspace_size(0) == 0
+    # one tile of 16384 values -> header + one group node
+    assert L.sv_tree_sum_f32_workspace_size(1) == 256 + 8
+    assert L.sv_tree_sum_f32_workspace_size(16384) == 256 + 8
+    assert L.sv_tree_sum_f32_workspace_size(16385) == 256 + 16
+    assert L.sv_tree_sum_f32_workspace_size(10 ** 8) == 256 + 8 * 6104
+    assert L.sv_tree_sum_f32_workspace_size(1 << 40) == ctypes.c_size_t(-1).value
+    assert L.sv_variance_f32_workspace_size(4096, 4096, 1) == 0
+    assert L.sv_variance_f32_workspace_size(1000, 64, 0) == 0
+    assert L.sv_variance_f32_workspace_size(1, 64, 3) == ctypes.c_size_t(-1).value
+
+
+def test_sum_argument_errors(L):
+    assert L.sv_tree_sum_f32(BAD, -1, BAD, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert b"n = -1" in L.sv_last_error_message()
+    assert L.sv_tree_sum_f32(BAD, 10, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_tree_sum_f32(None, 10, BAD, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_tree_sum_f32(BAD, 10, BAD, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100000), 8, None) == SV_ERR_WORKSPACE
+    assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100010), 4096, None) == SV_ERR_WORKSPACE
+    assert b"aligned" in L.sv_last_error_message()
+    assert L.sv_tree_sum_f32(BAD, 1 << 38, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
+
+
+def test_variance_argument_errors(L):
+    out = ctypes.c_void_p(0x2000)
+    assert L.sv_variance_f32(BAD, -1, 4, 1, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f32(BAD, 4, 4, 2, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f32(BAD, 4, 4, 1, -1, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f32(BAD, 4, 4, 1, 0, None, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f32(None, 4, 4, 1, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f32(BAD, 1 << 21, 1 << 20, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
+    # an empty set of slices is a successful no-op
+    assert L.sv_variance_f32(None, 0, 5, 1, 0, None, None, None, 0, None) == 0
+
+
+def test_tuning_knob_validation(L):
+    assert L.sv_set_tuning(b"load_path", 2) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_set_tuning(b"nope", 0) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_set_tuning(b"load_path", 1) == 0
+    assert L.sv_set_tuning(b"reset", 0) == 0
+
+
+def test_no_device_is_reported(L):
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; the no-device path is checked on GPU-less hosts")
+    ws = ctypes.c_void_p(0x100000)
+    assert L.sv_tree_sum_f32(BAD, 10, BAD, ws, 4096, None) == SV_ERR_NO_DEVICE
+    assert L.sv_variance_f32(BAD, 4, 4, 1, 0, BAD, None, None, 0, None) == SV_ERR_NO_DEVICE
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+
+    with pytest.raises(TypeError):
+        sv.tree_sum([1.0, 2.0])
+    with pytest.raises(TypeError):
+        sv.var(torch.zeros(3, 3, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        sv.var(torch.zeros(3, 3))  # CPU tensor: no fallback
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # The package must not import, link or run anything under oracle/.
+    pkg = os.path.join(ROOT, "stable_variance_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "sv_oracle" not in text, f

@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact where the tree topology is mirrored (always, for this library);
+NaN results only need to be NaN on both sides (payloads are not specified).
+Every input is seeded; shapes span several tiles and ragged tails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from stable_variance_amd import build as libbuild
+
+    if libbuild.is_stale():
+        libbuild.build()
+    return torch, torch.device("cuda:0")
+
+
+@pytest.fixture(params=[0, 1], ids=["lds_transpose", "lane_loads"])
+def load_path(request, torch_dev):
+    import stable_variance_amd as sv
+
+    sv.set_tuning("load_path", request.param)
+    yield request.param
+    sv.set_tuning("reset", 0)
+
+
+def same_bits(a, b):
+    a = np.asarray(a, np.float32).ravel()
+    b = np.asarray(b, np.float32).ravel()
+    if a.shape != b.shape:
+        return False
+    nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(nan | (a.view(np.uint32) == b.view(np.uint32))))
+
+
+def gpu_sum(torch_dev, x):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    r = sv.tree_sum(t)
+    torch.cuda.synchronize()
+    return np.float32(r.item())
+
+
+def gpu_var(torch_dev, a, axis, ddof=0):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    v, m = sv.var(t, dim=axis, ddof=ddof, return_mean=True)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), m.cpu().numpy()
+
+
+# ------------------------------------------------------------------ sums
+
+def test_sum_printed_fixtures(torch_dev, load_path):
+    for x in (W.sum_thousandths(), W.sum_pm1e16()):
+        assert same_bits(gpu_sum(torch_dev, x), oracle.tree_sum(x))
+    assert gpu_sum(torch_dev, W.sum_pm1e16()) == 10000.0
+
+
+def test_sum_permutations_same_bits(torch_dev):
+    x, perms = W.sum_normal_perms()
+    want = oracle.tree_sum(x)
+    assert same_bits(gpu_sum(torch_dev, x), want)
+    for p in perms:
+        assert same_bits(gpu_sum(torch_dev, p), oracle.tree_sum(p))
+        assert same_bits(gpu_sum(torch_dev, p), want)
+
+
+SUM_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 4095, 4096, 4097, 16383, 16384, 16385,
+             65537, 1_000_003]
+
+
+@pytest.mark.parametrize("n", SUM_SIZES)
+def test_sum_sizes_random_and_adversarial(torch_dev, load_path, n):
+    rng = np.random.default_rng(n)
+    for x in (rng.normal(0, 1, n).astype(np.float32), W.adversarial_values(n, n + 7),
+              W.sum_cancelling_pairs(n, 0.02, seed=n)):
+        assert same_bits(gpu_sum(torch_dev, x), oracle.tree_sum(x)), n
+
+
+def test_sum_unaligned_pointer(torch_dev, load_path):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    rng = np.random.default_rng(77)
+    base = rng.normal(0, 1, 100_003).astype(np.float32)
+    t = torch.from_numpy(base).to(dev)
+    for off in (1, 2, 3):
+        r = sv.tree_sum(t[off:])
+        assert same_bits(r.item(), oracle.tree_sum(base[off:]))
+
+
+def test_sum_zero_signs_and_specials(torch_dev):
+    cases = [np.zeros(0, np.float32), np.full(5, -0.0, np.float32), np.full(16384, -0.0, np.float32),
+             np.array([-0.0, 0.0, -0.0], np.float32), np.array([1, np.inf, 2], np.float32),
+             np.array([np.inf, -np.inf], np.float32), np.array([np.nan, 1.0], np.float32),
+             np.array([3e38, 3e38, -3e38], np.float32), np.array([1e-45, 1e-45, -2e-45, 1e-40], np.float32)]
+    for x in cases:
+        assert same_bits(gpu_sum(torch_dev, x), oracle.tree_sum(x)), x
+
+
+def test_sum_workspace_left_zero_and_deterministic(torch_dev):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    x = W.sum_cancelling_pairs(3_000_000, 0.01, seed=5)
+    t = torch.from_numpy(x).to(dev)
+    r0 = sv.tree_sum(t).item()
+    for _ in range(5):
+        assert same_bits(sv.tree_sum(t).item(), r0)
+    torch.cuda.synchronize()
+    for ws in sv._workspaces.values():
+        assert int(ws.count_nonzero().item()) == 0
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        r1 = sv.tree_sum(t)
+    s.synchronize()
+    assert same_bits(r1.item(), r0)
+
+
+def test_sum_full_size_1e8(torch_dev):
+    # 10^8 values (400 MB): 99% N(0,1), 1% large cancelling pairs, seed 3.
+    x = W.sum_cancelling_pairs()
+    got = gpu_sum(torch_dev, x)
+    assert same_bits(got, oracle.tree_sum(x))
+
+
+def test_sum_grouped_tiles(torch_dev):
+    # Above 8192 tiles each workgroup combines a group of tiles: 1.5e8 values.
+    x = np.random.default_rng(8).normal(0, 1, 150_000_000).astype(np.float32)
+    assert same_bits(gpu_sum(torch_dev, x), oracle.tree_sum(x))
+
+
+# ------------------------------------------------------------------ variance
+
+def check_var(torch_dev, a, axis, ddof=0):
+    v, m = gpu_var(torch_dev, a, axis, ddof)
+    ov, om = oracle.variance(a, axis=axis, ddof=ddof)
+    assert same_bits(v, ov), (a.shape, axis, ddof, np.flatnonzero(v.view(np.uint32) != ov.view(np.uint32))[:5])
+    assert same_bits(m, om), (a.shape, axis, ddof)
+    return v
+
+
+def test_variance_page_datasets(torch_dev, load_path):
+    for name, a, axis, _ in W.datasets_d1_d4():
+        v = check_var(torch_dev, a, axis)
+        v64 = oracle.var_f64(a, axis=axis)
+        er = oracle.max_rel_err(oracle.variance(a, axis=axis, method=oracle.METHOD_REFERENCE)[0], v64)
+        ek = oracle.max_rel_err(v, v64)
+        assert ek <= 4 * U and ek <= er, (name, ek, er)
+
+
+@pytest.mark.parametrize("c", [1.0, 1e10, 1e30, 1e38])
+@pytest.mark.parametrize("ddof", [0, 1])
+def test_variance_constants_exact_zero(torch_dev, c, ddof):
+    a = W.constant(c)
+    v = check_var(torch_dev, a, 0, ddof)
+    assert np.all(v == 0.0)
+    v = check_var(torch_dev, a.T.copy(), 1, ddof)
+    assert np.all(v == 0.0)
+
+
+def test_variance_4096_square(torch_dev, load_path):
+    a = W.c4_matrix()
+    v = check_var(torch_dev, a, 1)
+    v64 = oracle.var_f64(a, axis=1)
+    assert oracle.max_rel_err(v, v64) <= 4 * U
+
+
+ROW_NS = [1, 2, 3, 5, 64, 255, 256, 257, 1000, 1023, 1024, 1025, 4095, 4096, 4097, 10000, 16384]
+
+
+@pytest.mark.parametrize("n", ROW_NS)
+def test_variance_rows_shapes(torch_dev, load_path, n):
+    rng = np.random.default_rng(n)
+    rows = 37
+    a = rng.normal(1e4, 1, (rows, n)).astype(np.float32)
+    check_var(torch_dev, a, 1, 0)
+    check_var(torch_dev, a, 1, 1)
+    b = W.adversarial_values(rows * n, n).reshape(rows, n)
+    check_var(torch_dev, b, 1, 0)
+
+
+COL_RS = [1, 2, 3, 4, 5, 16, 17, 64, 65, 100, 128, 129, 256, 257, 512, 513, 1000, 1024]
+
+
+@pytest.mark.parametrize("R", COL_RS)
+def test_variance_cols_shapes(torch_dev, R):
+    rng = np.random.default_rng(R)
+    for C in (1, 63, 64, 65, 200):
+        a = rng.normal(-3e3, 2, (R, C)).astype(np.float32)
+        check_var(torch_dev, a, 0, 0)
+        check_var(torch_dev, a, 0, 2)
+    b = W.adversarial_values(R * 70, R).reshape(R, 70)
+    check_var(torch_dev, b, 0, 0)
+
+
+def test_variance_empty_slices(torch_dev):
+    v, m = gpu_var(torch_dev, np.zeros((3, 0), np.float32), 1)
+    assert np.all(np.isnan(v)) and np.all(np.isnan(m))
+    v, m = gpu_var(torch_dev, np.zeros((0, 4), np.float32), 0)
+    assert np.all(np.isnan(v)) and v.shape == (4,)
+
+
+def test_variance_unsupported_shape_leaves_output(torch_dev):
+    import ctypes
+
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    L = sv.capi()
+    x = torch.zeros(2, 20000, device=dev)
+    out = torch.full((2,), 7.0, device=dev)
+    st = L.sv_variance_f32(x.data_ptr(), 2, 20000, 1, 0, out.data_ptr(), None, None, 0, None)
+    assert st == 5
+    assert torch.all(out == 7.0)
+    assert L.sv_variance_f32_workspace_size(2, 20000, 1) == ctypes.c_size_t(-1).value
