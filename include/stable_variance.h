@@ -70,19 +70,21 @@ const char *sv_last_error_message(void);
 
 /*
  * Bytes of workspace sv_tree_sum_f32 needs for n values (0 for n <= 0,
- * (size_t)-1 for an unsupported n).  The workspace must be 256-byte aligned
- * and ZERO-FILLED before its first use; every successful call leaves it
- * zero-filled again, so it can be reused by later calls in stream order.
+ * (size_t)-1 for an unsupported n).  The workspace must be 256-byte aligned.
+ * Its first 256 bytes hold a ticket counter that must be ZERO before the
+ * first use; every call leaves them zero again, so the workspace can be
+ * reused by later calls in stream order.  The rest is scratch (per-workgroup
+ * partial nodes) and needs no initialisation.
  */
 size_t sv_tree_sum_f32_workspace_size(int64_t n);
 
 /*
  * out[0] = compensated tree sum of x[0 .. n).
  *   x          device pointer to n float32 values (any alignment; n > 0)
- *   n          number of values, 0 <= n <= 2^40 (n == 0 writes +0)
+ *   n          number of values, 0 <= n <= 2^37 (n == 0 writes +0)
  *   out        device pointer to one float32
- *   workspace  device buffer of sv_tree_sum_f32_workspace_size(n) bytes,
- *              zero-filled before first use (see above); may be NULL when
+ *   workspace  device buffer of sv_tree_sum_f32_workspace_size(n) bytes
+ *              whose first 256 bytes are zero (see above); may be NULL when
  *              that size is 0
  *   stream     hipStream_t or NULL
  * Source: Pennacchio, "Variance in float32 ...", §2 step 3 (the tree of
@@ -93,8 +95,8 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
 
 /*
  * Bytes of workspace sv_variance_f32 needs (currently 0 for every supported
- * shape; (size_t)-1 for an unsupported one).  Same zero-fill contract as
- * above when nonzero.
+ * shape; (size_t)-1 for an unsupported one).  Same contract as above (first
+ * 256 bytes zero) when nonzero.
  */
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
 

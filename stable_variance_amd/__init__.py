@@ -85,8 +85,9 @@ def set_tuning(key: str, value: int) -> None:
     _check(capi().sv_set_tuning(key.encode(), int(value)))
 
 
-# Workspaces: one zero-filled buffer per (device, stream); the library leaves
-# it zero-filled after every call, so it is reused in stream order.
+# Workspaces: one buffer per (device, stream), zero-filled when allocated; the
+# library leaves its ticket counter (first 256 bytes) at zero after every
+# call, so it is reused in stream order.
 _workspaces: dict = {}
 
 

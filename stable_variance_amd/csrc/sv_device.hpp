@@ -213,7 +213,8 @@ constexpr int lds_floats_per_wave() { return 64 * (E + 4); }
 // LOADP 1: each lane loads its own E contiguous values directly.
 // VEC: 16-byte loads, p must be 16-byte aligned.
 // A wave whose tile lies entirely inside the data takes a branch-free path;
-// a ragged tile (the slice's last) loads single floats at clamped addresses.
+// a ragged tile (the slice's last) loads single floats at addresses clamped
+// to [0, len); a tile entirely beyond the data loads nothing.
 template <int E, bool VEC, int LOADP>
 __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t len, float *__restrict__ lds,
                                           float (&v)[E], int lane) {
@@ -225,6 +226,11 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
   // ragged: number of valid values in [0, TILE], and a safe index for loads
   const int lim = len <= 0 ? 0 : (len >= TILE ? TILE : (int)len);
   const int last = lim > 0 ? lim - 1 : 0;
+  if (lim == 0) {  // the whole tile lies beyond the data: no load at all
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = 0.0f;
+    return;
+  }
   if constexpr (LOADP == 1) {
     const int e0 = lane * E;
     if (full) {
