@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the accurate float32 reduction path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * the variance of a [4096, 4096] float32 array along axis 1 (ddof 0,
+    N(1e4, 1), seed 2) -- shift, compensated trees of y, d and d^2,
+    two-term correction (the timing shape of the method page's §3);
+  * the compensated tree sum of 10^8 float32 values (99% N(0,1), 1% large
+    exactly cancelling +/- pairs, seed 3).
+Inputs are resident in HBM before timing starts.  Several copies of each
+input are cycled so that the 256 MB Infinity Cache cannot serve them
+(6 x 64 MiB variance inputs, 2 x 400 MB sum inputs).
+
+Prints ONE JSON line: whole-step throughput in GElem/s (10^9 input elements
+per second), a roofline entry for the dominant kernel (the 10^8 sum; HBM
+bound), the variance kernel's own entry, and the CPU oracle timed on the
+host as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --calibrate-copy     (a plain 400 MB copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GElem/s + % HBM peak: fp32 TwoSum-tree variance [4096,4096], 1e8-elem sum"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD datasheet
+VALU_PEAK_TOPS = 39.3216       # 256 CU x 64 lanes x 2.4 GHz plain (non-packed) FP32 ops
+VAR_ROWS, VAR_COLS = 4096, 4096
+SUM_N = 100_000_000
+N_VAR_COPIES, N_SUM_COPIES = 6, 2
+# Algorithmic bytes per launch: every input value read once, outputs written once.
+VAR_BYTES = VAR_ROWS * VAR_COLS * 4 + 2 * VAR_ROWS * 4
+SUM_BYTES = SUM_N * 4 + 4
+# Plain FP32 VALU operations the method needs per variance element (see the design notes):
+# shift 1, Tree(y) 7, centre 1, square 1, Tree(d) 7, Tree(d^2) 6.
+VAR_OPS_PER_ELEM = 23
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "tree_sum_1e8_counters.txt")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in ("stable_variance_amd/csrc/sv_lib.hip", "stable_variance_amd/csrc/sv_device.hpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_traffic():
+    """HBM bytes per launch of the sum kernel from the committed rocprofv3
+    counter summary, or None when absent or taken on other kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(SUM_N, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": SUM_N * 4, "bytes_written": SUM_N * 4, "launches": 3}))
+
+
+def cpu_baseline(c4_host, c5_host):
+    """The oracle (single-threaded C, as it stands) on the same workload:
+    the full [4096,4096] variance and the full 10^8 sum, repeated until about
+    10 s have passed (at most 30 repetitions)."""
+    import oracle
+
+    oracle.lib()
+    reps, t_total = 0, 0.0
+    while reps < 30 and t_total < 10.0:
+        t0 = time.perf_counter()
+        oracle.variance(c4_host, axis=1)
+        oracle.tree_sum(c5_host)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    elems = (VAR_ROWS * VAR_COLS + SUM_N) * reps
+    return {"value": round(elems / t_total / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+            "sample": f"full workload ({VAR_ROWS}x{VAR_COLS} variance + {SUM_N} sum) x {reps} reps, "
+                      f"{t_total:.1f} s, single-threaded C oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+              f"(the method has no multi-GPU step here).", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    import stable_variance_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    L = sv.capi()
+
+    # ---------------- inputs (host generation, then resident in HBM)
+    c4_host = W.c4_matrix()
+    c5_host = W.sum_cancelling_pairs()
+    c4 = [torch.from_numpy(c4_host).to(dev)]
+    for k in range(1, N_VAR_COPIES):
+        c4.append(torch.roll(c4[0], shifts=97 * k, dims=1).contiguous())
+    c5 = [torch.from_numpy(c5_host).to(dev)]
+    for k in range(1, N_SUM_COPIES):
+        c5.append(torch.roll(c5[0], shifts=1_000_003 * k).contiguous())
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ws_bytes = L.sv_tree_sum_f32_workspace_size(SUM_N)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    var_out = torch.empty(VAR_ROWS, dtype=torch.float32, device=dev)
+    mean_out = torch.empty(VAR_ROWS, dtype=torch.float32, device=dev)
+    sum_out = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(L.sv_last_error_message().decode())
+
+    def run_var(i):
+        a = c4[i % N_VAR_COPIES]
+        check(L.sv_variance_f32(a.data_ptr(), VAR_ROWS, VAR_COLS, 1, 0, var_out.data_ptr(), mean_out.data_ptr(),
+                                None, 0, sh))
+
+    def run_sum(i):
+        b = c5[i % N_SUM_COPIES]
+        check(L.sv_tree_sum_f32(b.data_ptr(), SUM_N, sum_out.data_ptr(), ws.data_ptr(), ws_bytes, sh))
+
+    # ---------------- warmup
+    for i in range(args.warmup):
+        run_var(i)
+        run_sum(i)
+    torch.cuda.synchronize()
+
+    # ---------------- timed region: K steps, per-kernel HIP events on the launch stream
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        run_var(i)
+        ev[i][1].record(stream)
+        run_sum(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    var_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(K))
+    sum_ms = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(K))
+    var_avg = sum(var_ms) / K
+    sum_avg = sum(sum_ms) / K
+
+    # ---------------- parity spot check at full size (the timed launch configuration)
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        run_var(0)
+        run_sum(0)
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(0).choice(VAR_ROWS, 16, replace=False)
+        ov, om = oracle.variance(c4_host[rows], axis=1)
+        gv = var_out.cpu().numpy()[rows]
+        gm = mean_out.cpu().numpy()[rows]
+        ok_var = bool(np.array_equal(gv.view(np.uint32), ov.view(np.uint32)) and
+                      np.array_equal(gm.view(np.uint32), om.view(np.uint32)))
+        os_ = oracle.tree_sum(c5_host)
+        ok_sum = bool(np.float32(sum_out.item()).view(np.uint32) == np.float32(os_).view(np.uint32))
+        parity = {"variance_16_rows_bit_exact": ok_var, "sum_bit_exact": ok_sum}
+
+    # ---------------- context: library reductions on the same buffers
+    def time_op(fn, reps=20):
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    torch_var_ms = time_op(lambda i: torch.var(c4[i % N_VAR_COPIES], dim=1, correction=0))
+    torch_sum_ms = time_op(lambda i: torch.sum(c5[i % N_SUM_COPIES]))
+
+    elems = VAR_ROWS * VAR_COLS + SUM_N
+    value = elems * K / wall / 1e9
+    sum_gbs = SUM_BYTES / (sum_avg * 1e-3) / 1e9
+    var_gbs = VAR_BYTES / (var_avg * 1e-3) / 1e9
+    var_tops = VAR_ROWS * VAR_COLS * VAR_OPS_PER_ELEM / (var_avg * 1e-3) / 1e12
+    traffic = read_counter_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GElem/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "variance [4096,4096] axis 1 ddof 0 N(1e4,1) seed 2 + tree sum of 1e8 "
+                               "(99% N(0,1), 1% +/-U(1e6,1e8) cancelling pairs, seed 3)",
+                   "variance_shape": [VAR_ROWS, VAR_COLS], "sum_n": SUM_N,
+                   "input_copies": {"variance": N_VAR_COPIES, "sum": N_SUM_COPIES}},
+        "roofline": {"bound": "hbm", "kernel": "k_tree_sum (1e8 values)", "achieved": round(sum_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sum_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(sum_avg, 5),
+                     "algorithmic_bytes_per_launch": SUM_BYTES},
+        "variance_kernel": {"kernel": "k_var_rows (4096x4096, axis 1)", "avg_launch_ms": round(var_avg, 5),
+                            "gelem_s": round(VAR_ROWS * VAR_COLS / (var_avg * 1e-3) / 1e9, 2),
+                            "hbm": {"achieved": round(var_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(var_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": VAR_BYTES},
+                            "alu": {"achieved": round(var_tops, 2), "peak": VALU_PEAK_TOPS, "unit": "Tops/s",
+                                    "frac": round(var_tops / VALU_PEAK_TOPS, 4),
+                                    "ops_per_element": VAR_OPS_PER_ELEM}},
+        "sum_kernel": {"avg_launch_ms": round(sum_avg, 5), "min_ms": round(sum_ms[0], 5),
+                       "gelem_s": round(SUM_N / (sum_avg * 1e-3) / 1e9, 2)},
+        "context": {"torch_var_correction0_ms": round(torch_var_ms, 5),
+                    "kernel_over_torch_var": round(var_avg / torch_var_ms, 3),
+                    "torch_sum_ms": round(torch_sum_ms, 5),
+                    "torch_sum_gbs": round(SUM_BYTES / (torch_sum_ms * 1e-3) / 1e9, 1),
+                    "pages_kernel_over_reference": {"kaggle_cpu": 2.27, "kaggle_gpu": 2.19}},
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c4_host, c5_host)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

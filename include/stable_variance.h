@@ -81,7 +81,7 @@ size_t sv_tree_sum_f32_workspace_size(int64_t n);
 /*
  * out[0] = compensated tree sum of x[0 .. n).
  *   x          device pointer to n float32 values (any alignment; n > 0)
- *   n          number of values, 0 <= n <= 2^37 (n == 0 writes +0)
+ *   n          number of values, 0 <= n <= 2^35 (n == 0 writes +0)
  *   out        device pointer to one float32
  *   workspace  device buffer of sv_tree_sum_f32_workspace_size(n) bytes
  *              whose first 256 bytes are zero (see above); may be NULL when

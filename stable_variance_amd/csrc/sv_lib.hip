@@ -90,6 +90,10 @@ __device__ __forceinline__ void store_node_agent(Node *dst, Node v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// s_waitcnt vmcnt(0): every vector memory operation of this wave, including
+// the device-coherent stores above, has completed.
+__device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ Node load_node_agent(const Node *src) {
   const unsigned s = __hip_atomic_load(reinterpret_cast<const unsigned *>(&src->s), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -103,7 +107,7 @@ __device__ __forceinline__ Node load_node_agent(const Node *src) {
 constexpr int SUM_E = 64;
 constexpr int SUM_W = 4;
 constexpr int64_t SUM_TILE = 64LL * SUM_E * SUM_W;  // 16384 values per tile
-constexpr int SUM_MAX_GROUP = 1024;                 // tiles per workgroup (2^10)
+constexpr int SUM_MAX_GROUP = 256;                  // tiles per workgroup (2^8)
 constexpr int SUM_TOP_PER_THREAD = 32;              // group nodes per thread at the top
 constexpr int SUM_MAX_BLOCKS = 64 * SUM_W * SUM_TOP_PER_THREAD;  // 8192
 constexpr size_t SUM_WS_HEADER = 256;               // ticket counter, padded
@@ -157,15 +161,20 @@ __global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x
     grp = block_tree<W, false>(r, slots, w, lane);
   }
 
+  // Publish the group node, then take a ticket.  The node is written with a
+  // device-coherent (agent scope) store and read back below with
+  // device-coherent loads, so no cache writeback or invalidation is needed;
+  // waiting for the store's completion (vmcnt 0) before the ticket increment
+  // orders the two.  An agent-scope release fence would instead write back the
+  // whole L2 of the XCD once per workgroup.
   if (threadIdx.x == 0) {
     store_node_agent(part + blockIdx.x, grp);
-    __threadfence();
-    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmem_stores();
+    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (ticket == gridDim.x - 1) ? 1u : 0u;
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
 
   // Last workgroup: tree over the gridDim.x group nodes, padded with zeros.
   constexpr int K = SUM_TOP_PER_THREAD;
@@ -358,7 +367,7 @@ int ceil_log2(int64_t v) {
   return l;
 }
 
-constexpr int64_t SUM_MAX_N = 1LL << 37;
+constexpr int64_t SUM_MAX_N = 1LL << 35;
 constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
 constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel
 constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
@@ -438,7 +447,7 @@ size_t sv_tree_sum_f32_workspace_size(int64_t n) {
 sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
                           void *stream) {
   if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: n = %lld < 0", (long long)n);
-  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f32: n = %lld above 2^37", (long long)n);
+  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f32: n = %lld above 2^35", (long long)n);
   if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: out is NULL");
   if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: x is NULL with n > 0");
   const size_t need = sum_workspace_bytes(n);

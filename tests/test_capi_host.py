@@ -58,7 +58,7 @@ def test_workspace_sizes(L):
     assert L.sv_tree_sum_f32_workspace_size(16384) == 256 + 8
     assert L.sv_tree_sum_f32_workspace_size(16385) == 256 + 16
     assert L.sv_tree_sum_f32_workspace_size(10 ** 8) == 256 + 8 * 6104
-    assert L.sv_tree_sum_f32_workspace_size(1 << 40) == ctypes.c_size_t(-1).value
+    assert L.sv_tree_sum_f32_workspace_size((1 << 35) + 1) == ctypes.c_size_t(-1).value
     assert L.sv_variance_f32_workspace_size(4096, 4096, 1) == 0
     assert L.sv_variance_f32_workspace_size(1000, 64, 0) == 0
     assert L.sv_variance_f32_workspace_size(1, 64, 3) == ctypes.c_size_t(-1).value
@@ -73,7 +73,7 @@ def test_sum_argument_errors(L):
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100000), 8, None) == SV_ERR_WORKSPACE
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100010), 4096, None) == SV_ERR_WORKSPACE
     assert b"aligned" in L.sv_last_error_message()
-    assert L.sv_tree_sum_f32(BAD, 1 << 38, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_tree_sum_f32(BAD, (1 << 35) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
 def test_variance_argument_errors(L):
