@@ -81,7 +81,7 @@ size_t sv_tree_sum_f32_workspace_size(int64_t n);
 /*
  * out[0] = compensated tree sum of x[0 .. n).
  *   x          device pointer to n float32 values (any alignment; n > 0)
- *   n          number of values, 0 <= n <= 2^35 (n == 0 writes +0)
+ *   n          number of values, 0 <= n <= 2^36 (n == 0 writes +0)
  *   out        device pointer to one float32
  *   workspace  device buffer of sv_tree_sum_f32_workspace_size(n) bytes
  *              whose first 256 bytes are zero (see above); may be NULL when
@@ -127,10 +127,19 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
 
 /*
  * Launch-geometry tuning for tests and benchmarks.  A knob only changes how
- * the work is mapped onto the GPU, never a result bit.  Keys:
- *   "load_path"   0 = coalesced loads transposed through LDS (default),
- *                 1 = per-lane contiguous loads
- *   "reset"       any value: restore every default
+ * the work is mapped onto the GPU, never a result bit.  Keys (defaults are
+ * the fastest settings measured on MI355X):
+ *   "sum_load_path"  tree sum: 0 = coalesced 16-byte loads transposed through
+ *                    LDS into lane-contiguous order (default), 1 = each lane
+ *                    loads its own contiguous values
+ *   "sum_nt"         tree sum: 1 = non-temporal loads (default), 0 = ordinary
+ *   "sum_e"          values per lane in a tree-sum chunk: 16 or 32 (default)
+ *   "sum_depth"      tree-sum chunks in flight per wave: 2 (default) or 4
+ *   "sum_blocks"     target number of tree-sum workgroups, 1..8192 (default
+ *                    2048); each wave then streams a power-of-two run of chunks
+ *   "var_load_path"  row variance: as sum_load_path (default 1)
+ *   "var_nt"         row variance: as sum_nt (default 0)
+ *   "reset"          any value: restore every default
  * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  Not thread
  * safe with concurrent calls.
  */

@@ -215,7 +215,27 @@ constexpr int lds_floats_per_wave() { return 64 * (E + 4); }
 // A wave whose tile lies entirely inside the data takes a branch-free path;
 // a ragged tile (the slice's last) loads single floats at addresses clamped
 // to [0, len); a tile entirely beyond the data loads nothing.
-template <int E, bool VEC, int LOADP>
+typedef float sv_v4f __attribute__((ext_vector_type(4)));
+
+// 16-byte and 4-byte loads; NT marks them non-temporal (streamed data that
+// is read once and should not displace other lines in the caches).
+template <bool NT>
+__device__ __forceinline__ float4 ld4(const float *p) {
+  if constexpr (NT) {
+    const sv_v4f v = __builtin_nontemporal_load(reinterpret_cast<const sv_v4f *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const float4 *>(p);
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ float ld1(const float *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int E, bool VEC, int LOADP, bool NT = false>
 __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t len, float *__restrict__ lds,
                                           float (&v)[E], int lane) {
   static_assert(E >= 4 && (E & (E - 1)) == 0, "E must be a power of two >= 4");
@@ -237,11 +257,11 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (VEC) {
-          const float4 g = *reinterpret_cast<const float4 *>(p + e0 + 4 * j);
+          const float4 g = ld4<NT>(p + e0 + 4 * j);
           v[4 * j] = g.x; v[4 * j + 1] = g.y; v[4 * j + 2] = g.z; v[4 * j + 3] = g.w;
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[4 * j + t] = p[e0 + 4 * j + t];
+          for (int t = 0; t < 4; ++t) v[4 * j + t] = ld1<NT>(p + e0 + 4 * j + t);
         }
       }
     } else {
@@ -256,7 +276,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
     if (full && VEC) {
       float4 g[J];
 #pragma unroll
-      for (int k = 0; k < J; ++k) g[k] = *reinterpret_cast<const float4 *>(p + 256 * k + 4 * lane);
+      for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + 256 * k + 4 * lane);
 #pragma unroll
       for (int k = 0; k < J; ++k) {
         const int e = 256 * k + 4 * lane;
@@ -268,7 +288,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
       for (int k = 0; k < E; ++k) {
         const int e = 64 * k + lane;
         if (full) {
-          g[k] = p[e];
+          g[k] = ld1<NT>(p + e);
         } else {
           const float t = p[e < last ? e : last];
           g[k] = (e < lim) ? t : 0.0f;
@@ -289,5 +309,90 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
     wave_lds_sync();
   }
 }
+
+// ---------------------------------------------------------------- streamed chunks
+
+// A chunk is the 64*E consecutive values one wave reduces in one step.  Its
+// load is split in two so that the next chunk's loads can be in flight while
+// the current one is reduced:
+//   issue()   starts the loads into `raw` (no wait),
+//   finish()  turns `raw` into lane-contiguous values v[i] = chunk[lane*E+i]
+//             (through this wave's LDS region when LOADP == 0).
+// Raw layouts: LOADP 0 and VEC: raw[4k+t] = chunk[256k + 4*lane + t];
+//              LOADP 0, !VEC:   raw[k]    = chunk[64k + lane];
+//              LOADP 1:         raw[i]    = chunk[lane*E + i].
+// Values at or beyond `len` are 0; a chunk entirely beyond the data issues no
+// load; a ragged one loads at addresses clamped to [0, len).
+template <int E, bool VEC, int LOADP, bool NT>
+struct Chunk {
+  static_assert(E >= 4 && (E & (E - 1)) == 0, "E must be a power of two >= 4");
+  static constexpr int J = E / 4;
+  static constexpr int STR = E + 4;
+  static constexpr int SIZE = 64 * E;
+
+  __device__ static __forceinline__ int raw_index(int i, int lane) {
+    if constexpr (LOADP == 1) return lane * E + i;
+    else if constexpr (VEC) return 256 * (i / 4) + 4 * lane + (i % 4);
+    else return 64 * i + lane;
+  }
+
+  __device__ static __forceinline__ void issue(const float *__restrict__ p, int64_t len, int lane, float (&raw)[E]) {
+    const int lim = len <= 0 ? 0 : (len >= SIZE ? SIZE : (int)len);
+    if (lim == SIZE) {
+      if constexpr (VEC) {
+#pragma unroll
+        for (int k = 0; k < J; ++k) {
+          const int e = (LOADP == 1) ? lane * E + 4 * k : 256 * k + 4 * lane;
+          const float4 g = ld4<NT>(p + e);
+          raw[4 * k] = g.x; raw[4 * k + 1] = g.y; raw[4 * k + 2] = g.z; raw[4 * k + 3] = g.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) raw[i] = ld1<NT>(p + raw_index(i, lane));
+      }
+    } else if (lim == 0) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) raw[i] = 0.0f;
+    } else {
+      const int last = lim - 1;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = raw_index(i, lane);
+        const float t = p[e < last ? e : last];
+        raw[i] = (e < lim) ? t : 0.0f;
+      }
+    }
+  }
+
+  __device__ static __forceinline__ void finish(const float (&raw)[E], float *__restrict__ lds, int lane,
+                                                float (&v)[E]) {
+    if constexpr (LOADP == 1) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = raw[i];
+    } else {
+      if constexpr (VEC) {
+#pragma unroll
+        for (int k = 0; k < J; ++k) {
+          const int e = 256 * k + 4 * lane;
+          *reinterpret_cast<float4 *>(lds + (e / E) * STR + (e % E)) =
+              make_float4(raw[4 * k], raw[4 * k + 1], raw[4 * k + 2], raw[4 * k + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int e = 64 * i + lane;
+          lds[(e / E) * STR + (e % E)] = raw[i];
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const float4 t = *reinterpret_cast<const float4 *>(lds + lane * STR + 4 * j);
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+      }
+      wave_lds_sync();
+    }
+  }
+};
 
 }  // namespace sv

@@ -23,6 +23,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "../../include/stable_variance.h"
 #include "sv_device.hpp"
 
@@ -104,62 +106,71 @@ __device__ __forceinline__ Node load_node_agent(const Node *src) {
 
 // ------------------------------------------------------------------ tree sum
 
-constexpr int SUM_E = 64;
-constexpr int SUM_W = 4;
-constexpr int64_t SUM_TILE = 64LL * SUM_E * SUM_W;  // 16384 values per tile
-constexpr int SUM_MAX_GROUP = 256;                  // tiles per workgroup (2^8)
+constexpr int SUM_W = 4;                            // waves per workgroup
 constexpr int SUM_TOP_PER_THREAD = 32;              // group nodes per thread at the top
-constexpr int SUM_MAX_BLOCKS = 64 * SUM_W * SUM_TOP_PER_THREAD;  // 8192
+constexpr int SUM_MAX_BLOCKS = 64 * SUM_W * SUM_TOP_PER_THREAD;  // 8192 workgroups
+constexpr int SUM_MAX_LOG2_GROUP = 16;              // chunks per wave <= 2^16
 constexpr size_t SUM_WS_HEADER = 256;               // ticket counter, padded
 
-template <int E, int W, bool VEC, int LOADP>
-__global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_group,
+// Each wave streams its own run of G = 2^log2_g consecutive chunks of 64*E
+// values (chunks beyond n are zero nodes), reducing chunk j while the loads
+// of chunk j+1 are in flight, and combines the chunk nodes in tree order
+// with a binary-counter stack.  The W wave nodes of a workgroup are
+// consecutive, so their tree is the workgroup's group node; it goes to the
+// workspace and the last workgroup to take a ticket reduces the group nodes.
+template <int E, int W, bool VEC, int LOADP, bool NT, int D>
+__global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_g,
                                                      Node *__restrict__ part, unsigned *__restrict__ counter,
                                                      float *__restrict__ out) {
-  constexpr int64_t TILE = 64LL * E * W;
+  using C = sv::Chunk<E, VEC, LOADP, NT>;
   constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
-  constexpr int KG = SUM_MAX_GROUP / (64 * W);
-  static_assert(KG >= 1 && SUM_MAX_GROUP % (64 * W) == 0, "group layout");
   __shared__ float lds[W * LPW];
+  __shared__ Node wstack[W][SUM_MAX_LOG2_GROUP + 1];
   __shared__ Node slots[W];
-  __shared__ Node gnodes[SUM_MAX_GROUP];
   __shared__ unsigned is_last;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t G = 1LL << log2_group;
-  const int64_t t_begin = (int64_t)blockIdx.x * G;
+  const int64_t G = 1LL << log2_g;
+  const int64_t c0 = ((int64_t)blockIdx.x * W + w) * G;  // first chunk of this wave
+  float *const my_lds = lds + w * LPW;
+  Node *const st = wstack[w];
+  int sp = 0;  // meaningful in lane 0
 
-  for (int64_t g = 0; g < G; ++g) {
-    const int64_t t = t_begin + g;
-    Node tn = sv::zero_node();
-    if (t * TILE < n) {  // uniform over the workgroup
-      const int64_t base = t * TILE + (int64_t)w * 64 * E;
-      float v[E];
-      sv::load_tile<E, VEC, LOADP>(x + base, n - base, lds + w * LPW, v, lane);
-      Node ln = sv::lane_tree<sv::LEAF_CANON, 0, E, E>(v);
-      ln = sv::wave_tree<false>(ln);
-      tn = block_tree<W, false>(ln, slots, w, lane);
+  auto reduce_chunk = [&](const float (&raw)[E], int64_t j) {
+    float v[E];
+    C::finish(raw, my_lds, lane, v);
+    Node nd = sv::lane_tree<sv::LEAF_CANON, 0, E, E>(v);
+    nd = sv::wave_tree<false>(nd);
+    if (lane == 0) {
+      for (int64_t k = j; k & 1; k >>= 1) nd = sv::combine(st[--sp], nd);
+      st[sp++] = nd;
     }
-    if (threadIdx.x == 0) gnodes[g] = tn;
-  }
-  __syncthreads();
+  };
+  auto chunk_ptr = [&](int64_t c) { return x + c * C::SIZE; };
+  auto chunk_len = [&](int64_t c) { return n - c * C::SIZE; };
 
-  Node grp;
-  if (G == 1) {
-    grp = gnodes[0];
-  } else {
-    // Tree over the G tile nodes (padded with zero nodes to SUM_MAX_GROUP).
-    Node nd[KG];
+  // Ring of D register buffers: chunk j is reduced while chunks j+1 .. j+D-1
+  // are loading.  G is a power of two; runs shorter than D use a smaller ring.
+  auto stream = [&](auto depth) {
+    constexpr int DD = decltype(depth)::value;
+    float r[DD][E];
 #pragma unroll
-    for (int k = 0; k < KG; ++k) {
-      const int idx = threadIdx.x * KG + k;
-      nd[k] = (idx < G) ? gnodes[idx] : sv::zero_node();
+    for (int u = 0; u < DD - 1; ++u) C::issue(chunk_ptr(c0 + u), chunk_len(c0 + u), lane, r[u]);
+    for (int64_t j = 0; j < G; j += DD) {
+#pragma unroll
+      for (int u = 0; u < DD; ++u) {
+        const int64_t ahead = j + u + DD - 1;
+        if (ahead < G) C::issue(chunk_ptr(c0 + ahead), chunk_len(c0 + ahead), lane, r[(u + DD - 1) % DD]);
+        reduce_chunk(r[u], j + u);
+      }
     }
-    Node r = sv::node_tree<0, KG, KG>(nd);
-    r = sv::wave_tree<false>(r);
-    grp = block_tree<W, false>(r, slots, w, lane);
-  }
+  };
+  if (G >= D) stream(std::integral_constant<int, D>{});
+  else if (G >= 2) stream(std::integral_constant<int, 2>{});
+  else stream(std::integral_constant<int, 1>{});
+  if (lane == 0) slots[w] = st[0];
+  __syncthreads();
 
   // Publish the group node, then take a ticket.  The node is written with a
   // device-coherent (agent scope) store and read back below with
@@ -168,7 +179,10 @@ __global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x
   // orders the two.  An agent-scope release fence would instead write back the
   // whole L2 of the XCD once per workgroup.
   if (threadIdx.x == 0) {
-    store_node_agent(part + blockIdx.x, grp);
+    Node nd[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) nd[i] = slots[i];
+    store_node_agent(part + blockIdx.x, sv::node_tree<0, W, W>(nd));
     wait_vmem_stores();
     const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (ticket == gridDim.x - 1) ? 1u : 0u;
@@ -177,16 +191,23 @@ __global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x
   if (!is_last) return;
 
   // Last workgroup: tree over the gridDim.x group nodes, padded with zeros.
+  // Each thread owns K consecutive nodes, read in batches of 8 (subtrees of
+  // 8 nodes) to keep few registers live.
   constexpr int K = SUM_TOP_PER_THREAD;
-  static_assert(64 * W * K == SUM_MAX_BLOCKS, "top layout");
-  Node nd[K];
+  constexpr int B = 8;
+  static_assert(64 * W * K == SUM_MAX_BLOCKS && K % B == 0, "top layout");
   const int nb = (int)gridDim.x;
+  Node sub[K / B];
+  for (int b = 0; b < K / B; ++b) {
+    Node nd[B];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int idx = threadIdx.x * K + k;
-    nd[k] = (idx < nb) ? load_node_agent(part + idx) : sv::zero_node();
+    for (int k = 0; k < B; ++k) {
+      const int idx = threadIdx.x * K + b * B + k;
+      nd[k] = (idx < nb) ? load_node_agent(part + idx) : sv::zero_node();
+    }
+    sub[b] = sv::node_tree<0, B, B>(nd);
   }
-  Node r = sv::node_tree<0, K, K>(nd);
+  Node r = sv::node_tree<0, K / B, K / B>(sub);
   r = sv::wave_tree<false>(r);
   r = block_tree<W, false>(r, slots, w, lane);
   if (threadIdx.x == 0) {
@@ -202,7 +223,7 @@ __global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
 
 // ------------------------------------------------------------------ variance, axis 1
 
-template <int E, int W, bool VEC, int LOADP>
+template <int E, int W, bool VEC, int LOADP, bool NT>
 __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
   constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
@@ -216,7 +237,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   const int64_t base = (int64_t)w * 64 * E;
 
   float v[E];
-  sv::load_tile<E, VEC, LOADP>(p + base, n - base, lds + w * LPW, v, lane);
+  sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, lane);
   const float x0 = p[0];
 
   // step 1: shift by the first element (padding stays +0)
@@ -331,7 +352,17 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 // ------------------------------------------------------------------ host side
 
 thread_local char g_err[512];
-int g_load_path = 0;  // 0: LDS transpose, 1: per-lane contiguous loads
+// Launch-geometry tuning (never changes a result bit).
+struct Tuning {
+  int sum_load_path = 0;      // 0: coalesced loads + LDS transpose, 1: per-lane contiguous loads
+  int sum_nt = 1;             // non-temporal loads of the summed input
+  int sum_e = 32;             // values per lane in a tree-sum chunk: 16 or 32
+  int sum_depth = 2;          // chunks in flight per wave (register ring): 2 or 4
+  int64_t sum_blocks = 2048;  // target workgroup count of the tree sum
+  int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
+  int var_nt = 0;             // non-temporal loads in the row-variance kernel
+};
+Tuning g_tune;
 
 sv_status fail(sv_status st, const char *fmt, ...) {
   va_list ap;
@@ -367,47 +398,82 @@ int ceil_log2(int64_t v) {
   return l;
 }
 
-constexpr int64_t SUM_MAX_N = 1LL << 35;
+constexpr int64_t SUM_MAX_N = 1LL << 36;
 constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
 constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel
 constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
 
 struct SumPlan {
-  int log2_group;
-  int64_t blocks;
+  int e;
+  int log2_g;      // chunks per wave = 2^log2_g
+  int64_t blocks;  // workgroups (<= SUM_MAX_BLOCKS)
 };
 
-SumPlan plan_sum(int64_t n) {
-  const int64_t tiles = (n + SUM_TILE - 1) / SUM_TILE;
-  int lg = ceil_log2(tiles) - ceil_log2(SUM_MAX_BLOCKS);
-  if (lg < 0) lg = 0;
-  const int64_t G = 1LL << lg;
-  return {lg, (tiles + G - 1) / G};
+// Chunks of 64*e values; each wave of a SUM_W-wave workgroup streams 2^g of
+// them.  g is the smallest value that keeps the workgroup count at or below
+// `target_blocks`; with g capped at SUM_MAX_LOG2_GROUP the count stays at or
+// below SUM_MAX_BLOCKS for every n <= SUM_MAX_N.
+SumPlan plan_sum(int64_t n, int e, int64_t target_blocks) {
+  const int64_t chunk = 64LL * e;
+  const int64_t chunks = (n + chunk - 1) / chunk;
+  const int64_t waves = (chunks + SUM_W - 1) / SUM_W;
+  if (target_blocks > SUM_MAX_BLOCKS) target_blocks = SUM_MAX_BLOCKS;
+  if (target_blocks < 1) target_blocks = 1;
+  int g = 0;
+  while (g < SUM_MAX_LOG2_GROUP && ((waves + (1LL << g) - 1) >> g) > target_blocks) ++g;
+  return {e, g, (waves + (1LL << g) - 1) >> g};
 }
 
 size_t sum_workspace_bytes(int64_t n) {
   if (n <= 0) return 0;
-  const SumPlan p = plan_sum(n);
+  // sized for the largest workgroup count any tuning can produce
+  const SumPlan p = plan_sum(n, 16, SUM_MAX_BLOCKS);
   return SUM_WS_HEADER + (size_t)p.blocks * sizeof(Node);
 }
 
-template <bool VEC, int LOADP>
-void launch_sum(const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
-                hipStream_t st) {
-  k_tree_sum<SUM_E, SUM_W, VEC, LOADP><<<dim3((unsigned)p.blocks), dim3(64 * SUM_W), 0, st>>>(x, n, p.log2_group, part,
-                                                                                                 counter, out);
+template <int E, bool VEC, int LOADP, bool NT>
+void launch_sum_t(const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
+                  hipStream_t st) {
+  const dim3 grid((unsigned)p.blocks), block(64 * SUM_W);
+  if (g_tune.sum_depth == 4) k_tree_sum<E, SUM_W, VEC, LOADP, NT, 4><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
+  else k_tree_sum<E, SUM_W, VEC, LOADP, NT, 2><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
+}
+
+template <int E>
+void launch_sum_e(bool vec, const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
+                  hipStream_t st) {
+  const int sel = (vec ? 4 : 0) + (g_tune.sum_load_path ? 2 : 0) + (g_tune.sum_nt ? 1 : 0);
+  switch (sel) {
+    case 0: launch_sum_t<E, false, 0, false>(x, n, p, part, counter, out, st); break;
+    case 1: launch_sum_t<E, false, 0, true>(x, n, p, part, counter, out, st); break;
+    case 2: launch_sum_t<E, false, 1, false>(x, n, p, part, counter, out, st); break;
+    case 3: launch_sum_t<E, false, 1, true>(x, n, p, part, counter, out, st); break;
+    case 4: launch_sum_t<E, true, 0, false>(x, n, p, part, counter, out, st); break;
+    case 5: launch_sum_t<E, true, 0, true>(x, n, p, part, counter, out, st); break;
+    case 6: launch_sum_t<E, true, 1, false>(x, n, p, part, counter, out, st); break;
+    default: launch_sum_t<E, true, 1, true>(x, n, p, part, counter, out, st); break;
+  }
+}
+
+template <int E, int W, bool VEC, int LOADP, bool NT>
+void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
+                   hipStream_t st) {
+  k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), 0, st>>>(x, n, ld, ddof, var, mean);
 }
 
 template <int E, int W>
 void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                     float *mean, hipStream_t st) {
-  const dim3 grid((unsigned)rows), block(64 * W);
-  if (vec) {
-    if (g_load_path == 0) k_var_rows<E, W, true, 0><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
-    else k_var_rows<E, W, true, 1><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
-  } else {
-    if (g_load_path == 0) k_var_rows<E, W, false, 0><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
-    else k_var_rows<E, W, false, 1><<<grid, block, 0, st>>>(x, n, ld, ddof, var, mean);
+  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
+  switch (sel) {
+    case 0: launch_rows_t<E, W, false, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 1: launch_rows_t<E, W, false, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 2: launch_rows_t<E, W, false, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 3: launch_rows_t<E, W, false, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 4: launch_rows_t<E, W, true, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 5: launch_rows_t<E, W, true, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 6: launch_rows_t<E, W, true, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    default: launch_rows_t<E, W, true, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
   }
 }
 
@@ -447,7 +513,7 @@ size_t sv_tree_sum_f32_workspace_size(int64_t n) {
 sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
                           void *stream) {
   if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: n = %lld < 0", (long long)n);
-  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f32: n = %lld above 2^35", (long long)n);
+  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f32: n = %lld above 2^36", (long long)n);
   if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: out is NULL");
   if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: x is NULL with n > 0");
   const size_t need = sum_workspace_bytes(n);
@@ -466,17 +532,12 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
     k_fill<<<1, 64, 0, st>>>(out, 1, 0.0f);
     return check_launch("sv_tree_sum_f32");
   }
-  const SumPlan p = plan_sum(n);
   unsigned *counter = reinterpret_cast<unsigned *>(workspace);
   Node *part = reinterpret_cast<Node *>(reinterpret_cast<char *>(workspace) + SUM_WS_HEADER);
   const bool vec = aligned16(x);
-  if (vec) {
-    if (g_load_path == 0) launch_sum<true, 0>(x, n, p, part, counter, out, st);
-    else launch_sum<true, 1>(x, n, p, part, counter, out, st);
-  } else {
-    if (g_load_path == 0) launch_sum<false, 0>(x, n, p, part, counter, out, st);
-    else launch_sum<false, 1>(x, n, p, part, counter, out, st);
-  }
+  const SumPlan p = plan_sum(n, g_tune.sum_e, g_tune.sum_blocks);
+  if (p.e == 16) launch_sum_e<16>(vec, x, n, p, part, counter, out, st);
+  else launch_sum_e<32>(vec, x, n, p, part, counter, out, st);
   return check_launch("sv_tree_sum_f32");
 }
 
@@ -545,13 +606,33 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
 
 sv_status sv_set_tuning(const char *key, int64_t value) {
   if (!key) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: key is NULL");
-  if (strcmp(key, "load_path") == 0) {
-    if (value != 0 && value != 1) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: load_path must be 0 or 1");
-    g_load_path = (int)value;
+  auto flag = [&](int *dst) {
+    if (value != 0 && value != 1) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: %s must be 0 or 1", key);
+    *dst = (int)value;
+    return ok();
+  };
+  if (strcmp(key, "sum_load_path") == 0) return flag(&g_tune.sum_load_path);
+  if (strcmp(key, "sum_nt") == 0) return flag(&g_tune.sum_nt);
+  if (strcmp(key, "var_load_path") == 0) return flag(&g_tune.var_load_path);
+  if (strcmp(key, "var_nt") == 0) return flag(&g_tune.var_nt);
+  if (strcmp(key, "sum_e") == 0) {
+    if (value != 16 && value != 32) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: sum_e must be 16 or 32");
+    g_tune.sum_e = (int)value;
+    return ok();
+  }
+  if (strcmp(key, "sum_depth") == 0) {
+    if (value != 2 && value != 4) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: sum_depth must be 2 or 4");
+    g_tune.sum_depth = (int)value;
+    return ok();
+  }
+  if (strcmp(key, "sum_blocks") == 0) {
+    if (value < 1 || value > SUM_MAX_BLOCKS)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: sum_blocks must be in [1, %d]", SUM_MAX_BLOCKS);
+    g_tune.sum_blocks = value;
     return ok();
   }
   if (strcmp(key, "reset") == 0) {
-    g_load_path = 0;
+    g_tune = Tuning{};
     return ok();
   }
   return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: unknown key '%s'", key);

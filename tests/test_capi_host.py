@@ -53,12 +53,13 @@ def test_abi_version_and_status_strings(L):
 
 def test_workspace_sizes(L):
     assert L.sv_tree_sum_f32_workspace_size(0) == 0
-    # one tile of 16384 values -> header + one group node
+    # sized for the smallest tile (4096 values): header + one node per workgroup
     assert L.sv_tree_sum_f32_workspace_size(1) == 256 + 8
-    assert L.sv_tree_sum_f32_workspace_size(16384) == 256 + 8
-    assert L.sv_tree_sum_f32_workspace_size(16385) == 256 + 16
+    assert L.sv_tree_sum_f32_workspace_size(4096) == 256 + 8
+    assert L.sv_tree_sum_f32_workspace_size(4097) == 256 + 16
+    # 24415 tiles -> groups of 4 tiles -> 6104 workgroups (at most 8192)
     assert L.sv_tree_sum_f32_workspace_size(10 ** 8) == 256 + 8 * 6104
-    assert L.sv_tree_sum_f32_workspace_size((1 << 35) + 1) == ctypes.c_size_t(-1).value
+    assert L.sv_tree_sum_f32_workspace_size((1 << 36) + 1) == ctypes.c_size_t(-1).value
     assert L.sv_variance_f32_workspace_size(4096, 4096, 1) == 0
     assert L.sv_variance_f32_workspace_size(1000, 64, 0) == 0
     assert L.sv_variance_f32_workspace_size(1, 64, 3) == ctypes.c_size_t(-1).value
@@ -73,7 +74,7 @@ def test_sum_argument_errors(L):
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100000), 8, None) == SV_ERR_WORKSPACE
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100010), 4096, None) == SV_ERR_WORKSPACE
     assert b"aligned" in L.sv_last_error_message()
-    assert L.sv_tree_sum_f32(BAD, (1 << 35) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_tree_sum_f32(BAD, (1 << 36) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
 def test_variance_argument_errors(L):
@@ -89,9 +90,14 @@ def test_variance_argument_errors(L):
 
 
 def test_tuning_knob_validation(L):
-    assert L.sv_set_tuning(b"load_path", 2) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_set_tuning(b"sum_load_path", 2) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(b"nope", 0) == SV_ERR_INVALID_ARGUMENT
-    assert L.sv_set_tuning(b"load_path", 1) == 0
+    assert L.sv_set_tuning(None, 0) == SV_ERR_INVALID_ARGUMENT
+    for key, good, bad in ((b"sum_load_path", 1, 2), (b"sum_nt", 0, -1), (b"var_load_path", 0, 5),
+                           (b"var_nt", 1, 2), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0)):
+        assert L.sv_set_tuning(key, good) == 0, key
+        assert L.sv_set_tuning(key, bad) == SV_ERR_INVALID_ARGUMENT, key
+    assert L.sv_set_tuning(b"sum_blocks", 8193) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(b"reset", 0) == 0
 
 

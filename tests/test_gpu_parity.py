@@ -29,11 +29,44 @@ def torch_dev():
     return torch, torch.device("cuda:0")
 
 
-@pytest.fixture(params=[0, 1], ids=["lds_transpose", "lane_loads"])
-def load_path(request, torch_dev):
+# Launch geometries the results must not depend on (knobs of sv_set_tuning).
+SUM_GEOMETRIES = {
+    "default": {},
+    "e16": {"sum_e": 16},
+    "depth4_few_blocks": {"sum_depth": 4, "sum_blocks": 64},
+    "one_chunk_per_wave": {"sum_blocks": 8192, "sum_e": 16},
+    "lane_loads_plain": {"sum_load_path": 1, "sum_nt": 0},
+    "single_workgroup": {"sum_blocks": 1},
+}
+VAR_GEOMETRIES = {
+    "default": {},
+    "lds_transpose_nt": {"var_load_path": 0, "var_nt": 1},
+    "lds_transpose": {"var_load_path": 0, "var_nt": 0},
+}
+
+
+def _apply(knobs):
     import stable_variance_amd as sv
 
-    sv.set_tuning("load_path", request.param)
+    sv.set_tuning("reset", 0)
+    for k, v in knobs.items():
+        sv.set_tuning(k, v)
+
+
+@pytest.fixture(params=list(SUM_GEOMETRIES), ids=list(SUM_GEOMETRIES))
+def sum_geometry(request, torch_dev):
+    import stable_variance_amd as sv
+
+    _apply(SUM_GEOMETRIES[request.param])
+    yield request.param
+    sv.set_tuning("reset", 0)
+
+
+@pytest.fixture(params=list(VAR_GEOMETRIES), ids=list(VAR_GEOMETRIES))
+def var_geometry(request, torch_dev):
+    import stable_variance_amd as sv
+
+    _apply(VAR_GEOMETRIES[request.param])
     yield request.param
     sv.set_tuning("reset", 0)
 
@@ -69,7 +102,7 @@ def gpu_var(torch_dev, a, axis, ddof=0):
 
 # ------------------------------------------------------------------ sums
 
-def test_sum_printed_fixtures(torch_dev, load_path):
+def test_sum_printed_fixtures(torch_dev, sum_geometry):
     for x in (W.sum_thousandths(), W.sum_pm1e16()):
         assert same_bits(gpu_sum(torch_dev, x), oracle.tree_sum(x))
     assert gpu_sum(torch_dev, W.sum_pm1e16()) == 10000.0
@@ -89,14 +122,14 @@ SUM_SIZES = [1, 2, 3, 4, 5, 63, 64, 65, 255, 256, 257, 4095, 4096, 4097, 16383, 
 
 
 @pytest.mark.parametrize("n", SUM_SIZES)
-def test_sum_sizes_random_and_adversarial(torch_dev, load_path, n):
+def test_sum_sizes_random_and_adversarial(torch_dev, sum_geometry, n):
     rng = np.random.default_rng(n)
     for x in (rng.normal(0, 1, n).astype(np.float32), W.adversarial_values(n, n + 7),
               W.sum_cancelling_pairs(n, 0.02, seed=n)):
         assert same_bits(gpu_sum(torch_dev, x), oracle.tree_sum(x)), n
 
 
-def test_sum_unaligned_pointer(torch_dev, load_path):
+def test_sum_unaligned_pointer(torch_dev, sum_geometry):
     import stable_variance_amd as sv
 
     torch, dev = torch_dev
@@ -137,10 +170,19 @@ def test_sum_workspace_left_zero_and_deterministic(torch_dev):
 
 
 def test_sum_full_size_1e8(torch_dev):
-    # 10^8 values (400 MB): 99% N(0,1), 1% large cancelling pairs, seed 3.
+    # 10^8 values (400 MB): 99% N(0,1), 1% large cancelling pairs, seed 3,
+    # in the benchmark's launch configuration and in two others.
+    import stable_variance_amd as sv
+
     x = W.sum_cancelling_pairs()
-    got = gpu_sum(torch_dev, x)
-    assert same_bits(got, oracle.tree_sum(x))
+    want = oracle.tree_sum(x)
+    for knobs in ({}, {"sum_e": 16, "sum_depth": 4, "sum_blocks": 512}, {"sum_blocks": 8192}):
+        _apply(knobs)
+        assert same_bits(gpu_sum(torch_dev, x), want), knobs
+    sv.set_tuning("reset", 0)
+    # float64 context: the 1e8 sum is ill-conditioned (large cancelling pairs)
+    exact = float(oracle.exact_sum(x))
+    assert abs(float(want) - exact) <= 1e-6 * abs(exact) + 1e-3
 
 
 def test_sum_grouped_tiles(torch_dev):
@@ -159,7 +201,7 @@ def check_var(torch_dev, a, axis, ddof=0):
     return v
 
 
-def test_variance_page_datasets(torch_dev, load_path):
+def test_variance_page_datasets(torch_dev, var_geometry):
     for name, a, axis, _ in W.datasets_d1_d4():
         v = check_var(torch_dev, a, axis)
         v64 = oracle.var_f64(a, axis=axis)
@@ -178,7 +220,7 @@ def test_variance_constants_exact_zero(torch_dev, c, ddof):
     assert np.all(v == 0.0)
 
 
-def test_variance_4096_square(torch_dev, load_path):
+def test_variance_4096_square(torch_dev, var_geometry):
     a = W.c4_matrix()
     v = check_var(torch_dev, a, 1)
     v64 = oracle.var_f64(a, axis=1)
@@ -189,7 +231,7 @@ ROW_NS = [1, 2, 3, 5, 64, 255, 256, 257, 1000, 1023, 1024, 1025, 4095, 4096, 409
 
 
 @pytest.mark.parametrize("n", ROW_NS)
-def test_variance_rows_shapes(torch_dev, load_path, n):
+def test_variance_rows_shapes(torch_dev, var_geometry, n):
     rng = np.random.default_rng(n)
     rows = 37
     a = rng.normal(1e4, 1, (rows, n)).astype(np.float32)
