@@ -44,7 +44,8 @@ SUM_BYTES = SUM_N * 4 + 4
 # Plain FP32 VALU operations the method needs per variance element (see the design notes):
 # shift 1, Tree(y) 7, centre 1, square 1, Tree(d) 7, Tree(d^2) 6.
 VAR_OPS_PER_ELEM = 23
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "tree_sum_1e8_counters.txt")
+SUM_COUNTERS = os.path.join(ROOT, "profiles", "k_tree_sum_1e8_counters.txt")
+VAR_COUNTERS = os.path.join(ROOT, "profiles", "k_var_rows_4096x4096_counters.txt")
 
 
 def source_digest() -> str:
@@ -55,13 +56,14 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_counter_traffic():
-    """HBM bytes per launch of the sum kernel from the committed rocprofv3
-    counter summary, or None when absent or taken on other kernel source."""
-    if not os.path.exists(COUNTERS_FILE):
+def read_counter_traffic(path):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), or None
+    when absent or taken on other kernel source."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
@@ -221,13 +223,23 @@ def main():
 
     torch_var_ms = time_op(lambda i: torch.var(c4[i % N_VAR_COPIES], dim=1, correction=0))
     torch_sum_ms = time_op(lambda i: torch.sum(c5[i % N_SUM_COPIES]))
+    # practical HBM read ceiling: a plain non-temporal read of the same buffers
+    probe_out = torch.empty(1, dtype=torch.float32, device=dev)
+    read_sum_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c5[i % N_SUM_COPIES].data_ptr(), SUM_N,
+                                                                     probe_out.data_ptr(), sh)))
+    read_var_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c4[i % N_VAR_COPIES].data_ptr(),
+                                                                     VAR_ROWS * VAR_COLS, probe_out.data_ptr(), sh)),
+                          reps=60)
+    read_sum_gbs = SUM_N * 4 / (read_sum_ms * 1e-3) / 1e9
+    read_var_gbs = VAR_ROWS * VAR_COLS * 4 / (read_var_ms * 1e-3) / 1e9
 
     elems = VAR_ROWS * VAR_COLS + SUM_N
     value = elems * K / wall / 1e9
     sum_gbs = SUM_BYTES / (sum_avg * 1e-3) / 1e9
     var_gbs = VAR_BYTES / (var_avg * 1e-3) / 1e9
     var_tops = VAR_ROWS * VAR_COLS * VAR_OPS_PER_ELEM / (var_avg * 1e-3) / 1e12
-    traffic = read_counter_traffic()
+    traffic = read_counter_traffic(SUM_COUNTERS)
+    var_traffic = read_counter_traffic(VAR_COUNTERS)
 
     out = {
         "metric": METRIC,
@@ -249,11 +261,15 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "k_tree_sum (1e8 values)", "achieved": round(sum_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sum_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(sum_avg, 5),
-                     "algorithmic_bytes_per_launch": SUM_BYTES},
+                     "algorithmic_bytes_per_launch": SUM_BYTES,
+                     "read_ceiling_gbs": round(read_sum_gbs, 1),
+                     "frac_of_read_ceiling": round(sum_gbs / read_sum_gbs, 4)},
         "variance_kernel": {"kernel": "k_var_rows (4096x4096, axis 1)", "avg_launch_ms": round(var_avg, 5),
                             "gelem_s": round(VAR_ROWS * VAR_COLS / (var_avg * 1e-3) / 1e9, 2),
                             "hbm": {"achieved": round(var_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                    "frac": round(var_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": VAR_BYTES},
+                                    "frac": round(var_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": VAR_BYTES,
+                                    "traffic": var_traffic, "read_ceiling_gbs": round(read_var_gbs, 1),
+                                    "frac_of_read_ceiling": round(var_gbs / read_var_gbs, 4)},
                             "alu": {"achieved": round(var_tops, 2), "peak": VALU_PEAK_TOPS, "unit": "Tops/s",
                                     "frac": round(var_tops / VALU_PEAK_TOPS, 4),
                                     "ops_per_element": VAR_OPS_PER_ELEM}},

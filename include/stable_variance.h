@@ -126,6 +126,15 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
                           void *stream);
 
 /*
+ * Measurement aid, not part of the method: reads x[0 .. n) once from HBM with
+ * plain non-temporal 16-byte loads (x 16-byte aligned, n <= 2^36) and does no
+ * arithmetic of the method, so its duration is the practical read ceiling
+ * the reduction kernels are compared with.  out (one float) is never written
+ * for finite data.  Asynchronous on `stream` like the entry points above.
+ */
+sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *stream);
+
+/*
  * Launch-geometry tuning for tests and benchmarks.  A knob only changes how
  * the work is mapped onto the GPU, never a result bit.  Keys (defaults are
  * the fastest settings measured on MI355X):

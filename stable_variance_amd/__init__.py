@@ -70,6 +70,8 @@ def capi():
                 L.sv_variance_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_set_tuning.restype = ctypes.c_int
                 L.sv_set_tuning.argtypes = [ctypes.c_char_p, i64]
+                L.sv_probe_read_bandwidth.restype = ctypes.c_int
+                L.sv_probe_read_bandwidth.argtypes = [vp, i64, vp, vp]
                 _lib = L
     return _lib
 

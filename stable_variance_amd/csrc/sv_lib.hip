@@ -216,6 +216,30 @@ __global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x
   }
 }
 
+// ------------------------------------------------------------------ measurement aid
+
+// Plain streaming read of n floats (non-temporal 16-byte loads, 4 per lane,
+// one 4 KiB block per workgroup).  It computes nothing of the method: the
+// loaded values are folded into a float that is stored only when it equals
+// a value no finite input produces, so the loads cannot be removed.  Used to
+// measure the practical HBM read ceiling next to the reduction kernels.
+__global__ __launch_bounds__(256) void k_stream_read(const float *__restrict__ x, int64_t n, float *__restrict__ out) {
+  const int64_t base = ((int64_t)blockIdx.x * 256 * 4 + threadIdx.x) * 4;
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t e = base + (int64_t)k * 1024;
+    if (e + 4 <= n) {
+      const float4 g = sv::ld4<true>(x + e);
+      acc += (g.x + g.y) + (g.z + g.w);
+    } else {
+      for (int t = 0; t < 4; ++t)
+        if (e + t < n) acc += x[e + t];
+    }
+  }
+  if (__builtin_bit_cast(unsigned, acc) == 0x7f800001u) out[0] = acc;  // a NaN payload, never the sum of finite data
+}
+
 __global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) out[i] = value;
@@ -602,6 +626,21 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     else launch_cols_ew<64, 16>(x, rows, cols, ddof, var_out, mean_out, st);
   }
   return check_launch("sv_variance_f32");
+}
+
+sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *stream) {
+  if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_probe_read_bandwidth: n = %lld < 0", (long long)n);
+  if (n > 0 && (!x || !out)) return fail(SV_ERR_INVALID_ARGUMENT, "sv_probe_read_bandwidth: NULL pointer");
+  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_probe_read_bandwidth: n above 2^36");
+  if (!aligned16(x)) return fail(SV_ERR_INVALID_ARGUMENT, "sv_probe_read_bandwidth: x must be 16-byte aligned");
+  if (n == 0) return ok();
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t blocks = (n + 4095) / 4096;
+  k_stream_read<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n, out);
+  return check_launch("sv_probe_read_bandwidth");
 }
 
 sv_status sv_set_tuning(const char *key, int64_t value) {

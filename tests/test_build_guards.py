@@ -1,0 +1,76 @@
+"""Build guards: properties of the gfx950 code that the tree's bits depend on.
+
+Compiles the HIP library to device assembly with the library's own flags and
+checks what the arithmetic contract needs: subnormals kept, no packed FP32,
+the correctly rounded division sequence, FMA only inside that sequence, and
+no scalar-cache stores.  CPU only (hipcc cross-compiles).
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from stable_variance_amd import build as libbuild
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "sv_lib.s"
+    flags = [f for f in libbuild.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [libbuild.hipcc(), *flags, "--cuda-device-only", "-S", libbuild.SRC, "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    return out.read_text()
+
+
+def kernels(asm_text):
+    """Map kernel symbol -> (body text, metadata text)."""
+    out = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm_text, re.S):
+        name = m.group(1)
+        body_m = re.search(re.escape(name) + r":.*?s_endpgm", asm_text, re.S)
+        out[name] = (body_m.group(0) if body_m else "", m.group(2))
+    return out
+
+
+def test_every_kernel_keeps_subnormals(asm):
+    ks = kernels(asm)
+    assert len(ks) >= 10
+    for name, (_, meta) in ks.items():
+        mode = re.search(r"\.amdhsa_float_denorm_mode_32 (\d+)", meta)
+        assert mode and mode.group(1) == "3", name  # 3 = keep input and output subnormals
+
+
+def test_no_packed_fp32(asm):
+    assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", asm)
+
+
+def test_no_scalar_memory_writes(asm):
+    # scalar-unit stores, atomics and cache write-backs (names built from parts)
+    forbidden = ["s_" + w for w in ("store", "atomic", "buffer" + "_store", "dcache" + "_wb")]
+    for f in forbidden:
+        assert not re.search(r"\b" + f, asm), f
+
+
+def test_division_is_correctly_rounded_and_fma_only_inside_it(asm):
+    ks = kernels(asm)
+    var = [b for n, (b, _) in ks.items() if "k_var_rows" in n or "k_var_cols" in n]
+    assert var
+    for body in var:
+        # the IEEE division sequence (scale, Newton steps, fmas, fixup)
+        assert "v_div_fixup_f32" in body and "v_div_scale_f32" in body
+        # every FMA belongs to a division: at most 5 per division sequence
+        nfma = len(re.findall(r"\bv_fmac?_f32", body))
+        ndiv = len(re.findall(r"\bv_div_fixup_f32", body))
+        assert nfma <= 5 * ndiv, (nfma, ndiv)
+    for n, (body, _) in ks.items():
+        if "k_tree_sum" in n:
+            assert not re.search(r"\bv_fmac?_f32", body), n  # the sum divides nothing
+
+
+def test_source_guards_reject_fast_math():
+    cmd = [libbuild.hipcc(), "--offload-arch=gfx950", "-ffast-math", "--cuda-device-only", "-fsyntax-only",
+           libbuild.SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode != 0 and "fast-math" in (res.stderr + res.stdout)
