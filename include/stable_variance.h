@@ -148,6 +148,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    2048); each wave then streams a power-of-two run of chunks
  *   "var_load_path"  row variance: as sum_load_path (default 1)
  *   "var_nt"         row variance: as sum_nt (default 0)
+ *   "var_rows_per_wave"  rows of 1025..4096 values one wave pipelines (the
+ *                    next row's loads in flight while one is reduced): 1
+ *                    (default), 2, 4 or 8
  *   "reset"          any value: restore every default
  * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  Not thread
  * safe with concurrent calls.

@@ -98,6 +98,15 @@ __device__ __forceinline__ Node zero_node() { return {0.0f, 0.0f}; }
 
 enum LeafKind { LEAF_CANON = 0, LEAF_FAST = 1, LEAF_NN = 2 };
 
+// Subtrees of at least this many values are scheduled one after the other
+// (a scheduling barrier between siblings): the compiler then interleaves
+// only within a subtree, which keeps about log2(E) partial nodes live instead
+// of a whole tree level.
+#ifndef SV_SCHED_BLOCK
+#define SV_SCHED_BLOCK 16
+#endif
+constexpr int SCHED_BLOCK = SV_SCHED_BLOCK;
+
 // Compensated tree over v[OFF .. OFF+N) (N a power of two >= 2).
 template <int LEAF, int OFF, int N, int E>
 __device__ __forceinline__ Node lane_tree(const float (&v)[E]) {
@@ -108,7 +117,9 @@ __device__ __forceinline__ Node lane_tree(const float (&v)[E]) {
     else return leaf_nn(v[OFF], v[OFF + 1]);
   } else {
     const Node l = lane_tree<LEAF, OFF, N / 2, E>(v);
+    if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
     const Node r = lane_tree<LEAF, OFF + N / 2, N / 2, E>(v);
+    if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
     if constexpr (LEAF == LEAF_NN) return combine_nn(l, r);
     else return combine(l, r);
   }
@@ -144,7 +155,9 @@ __device__ __forceinline__ void lane_tree_dq(const float (&y)[E], float m, int v
   } else {
     Node ld, lq, rd, rq;
     lane_tree_dq<MASK, OFF, N / 2, E>(y, m, valid, ld, lq);
+    if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
     lane_tree_dq<MASK, OFF + N / 2, N / 2, E>(y, m, valid, rd, rq);
+    if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
     nd = combine(ld, rd);
     nq = combine_nn(lq, rq);
   }

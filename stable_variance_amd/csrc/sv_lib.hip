@@ -295,6 +295,66 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   if (threadIdx.x == 0) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
 }
 
+// Axis 1, n <= 64*E: each wave owns R consecutive rows (one lane holds E
+// consecutive values of a row) and reduces row k while the loads of row k+1
+// are in flight, so HBM streaming and the three trees overlap.  The waves of
+// a workgroup are independent (no barrier).
+template <int E, int R, bool VEC, int LOADP, bool NT, int MINW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_var_rows_pipe(
+    const float *__restrict__ x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *__restrict__ var_out,
+    float *__restrict__ mean_out) {
+  using C = sv::Chunk<E, VEC, LOADP, NT>;
+  constexpr int W = 4;
+  constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
+  __shared__ float lds[W * LPW];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t r0 = ((int64_t)blockIdx.x * W + w) * R;
+  float *const my_lds = lds + w * LPW;
+  const bool full = (n == 64 * E);
+  const int64_t vl = n - (int64_t)lane * E;
+  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
+
+  // the buffer holds the raw loads of row r on entry and is reused in place
+  auto process = [&](float (&v)[E], int64_t r) {
+    if (r >= rows) return;
+    if constexpr (LOADP == 0) C::finish(v, my_lds, lane, v);
+    const float x0 = x[r * ld];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+    }
+    Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+    ny = sv::wave_tree<false>(ny);
+    const float m = sv::root_value(ny) / (float)n;
+    Node nd, nq;
+    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+    nd = sv::wave_tree<false>(nd);
+    nq = sv::wave_tree<true>(nq);
+    if (lane == 0) finalize(nd, nq, x0, m, n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
+  };
+  auto issue_row = [&](int64_t r, float (&v)[E]) { C::issue(x + r * ld, r < rows ? n : (int64_t)0, lane, v); };
+
+  float ra[E], rb[E];
+  issue_row(r0, ra);
+  if constexpr (R == 1) {
+    process(ra, r0);
+  } else {
+    static_assert(R % 2 == 0, "R is 1 or even");
+#pragma unroll 1
+    for (int k = 0; k < R; k += 2) {
+      issue_row(r0 + k + 1, rb);
+      process(ra, r0 + k);
+      if (k + 2 < R) issue_row(r0 + k + 2, ra);
+      process(rb, r0 + k + 1);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ variance, axis 0
 
 template <int E, int W>
@@ -385,6 +445,7 @@ struct Tuning {
   int64_t sum_blocks = 2048;  // target workgroup count of the tree sum
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
+  int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
 };
 Tuning g_tune;
 
@@ -501,6 +562,30 @@ void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t l
   }
 }
 
+template <int R, bool VEC, int LOADP, bool NT>
+void launch_pipe_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
+                   hipStream_t st) {
+  const int64_t waves = (rows + R - 1) / R;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  k_var_rows_pipe<64, R, VEC, LOADP, NT, 2><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
+}
+
+template <int R>
+void launch_pipe_r(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
+                   float *mean, hipStream_t st) {
+  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
+  switch (sel) {
+    case 0: launch_pipe_t<R, false, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 1: launch_pipe_t<R, false, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 2: launch_pipe_t<R, false, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 3: launch_pipe_t<R, false, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 4: launch_pipe_t<R, true, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 5: launch_pipe_t<R, true, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
+    case 6: launch_pipe_t<R, true, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
+    default: launch_pipe_t<R, true, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
+  }
+}
+
 template <int E, int W>
 void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
   const dim3 grid((unsigned)((C + 63) / 64)), block(64 * W);
@@ -614,7 +699,13 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     const bool vec = aligned16(x) && (cols % 4 == 0);
     if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     else if (n <= 1024) launch_rows_ew<16, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    else if (n <= 4096) launch_rows_ew<64, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    else if (n <= 4096) {
+      const int R = g_tune.var_rows_per_wave;
+      if (R == 2) launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else if (R == 4) launch_pipe_r<4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else if (R == 8) launch_pipe_r<8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else launch_rows_ew<64, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    }
     else launch_rows_ew<64, 4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
   } else {
     if (n <= 4) launch_cols_ew<4, 1>(x, rows, cols, ddof, var_out, mean_out, st);
@@ -654,6 +745,12 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
   if (strcmp(key, "sum_nt") == 0) return flag(&g_tune.sum_nt);
   if (strcmp(key, "var_load_path") == 0) return flag(&g_tune.var_load_path);
   if (strcmp(key, "var_nt") == 0) return flag(&g_tune.var_nt);
+  if (strcmp(key, "var_rows_per_wave") == 0) {
+    if (value != 1 && value != 2 && value != 4 && value != 8)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_rows_per_wave must be 1, 2, 4 or 8");
+    g_tune.var_rows_per_wave = (int)value;
+    return ok();
+  }
   if (strcmp(key, "sum_e") == 0) {
     if (value != 16 && value != 32) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: sum_e must be 16 or 32");
     g_tune.sum_e = (int)value;
