@@ -68,13 +68,16 @@ const char *sv_status_string(sv_status status);
  * The pointer stays valid until the next call on the same thread. */
 const char *sv_last_error_message(void);
 
+/* Bytes of ticket counters at the start of a tree-sum workspace. */
+#define SV_TREE_SUM_COUNTER_BYTES 33024
+
 /*
  * Bytes of workspace sv_tree_sum_f32 needs for n values (0 for n <= 0,
  * (size_t)-1 for an unsupported n).  The workspace must be 256-byte aligned.
- * Its first 256 bytes hold a ticket counter that must be ZERO before the
- * first use; every call leaves them zero again, so the workspace can be
- * reused by later calls in stream order.  The rest is scratch (per-workgroup
- * partial nodes) and needs no initialisation.
+ * Its first SV_TREE_SUM_COUNTER_BYTES bytes hold ticket counters that must
+ * be ZERO before the first use; every call leaves them zero again, so the
+ * workspace can be reused by later calls in stream order.  The rest is
+ * scratch (partial nodes) and needs no initialisation.
  */
 size_t sv_tree_sum_f32_workspace_size(int64_t n);
 
@@ -84,7 +87,7 @@ size_t sv_tree_sum_f32_workspace_size(int64_t n);
  *   n          number of values, 0 <= n <= 2^36 (n == 0 writes +0)
  *   out        device pointer to one float32
  *   workspace  device buffer of sv_tree_sum_f32_workspace_size(n) bytes
- *              whose first 256 bytes are zero (see above); may be NULL when
+ *              whose counter bytes are zero (see above); may be NULL when
  *              that size is 0
  *   stream     hipStream_t or NULL
  * Source: Pennacchio, "Variance in float32 ...", §2 step 3 (the tree of
@@ -95,8 +98,7 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
 
 /*
  * Bytes of workspace sv_variance_f32 needs (currently 0 for every supported
- * shape; (size_t)-1 for an unsupported one).  Same contract as above (first
- * 256 bytes zero) when nonzero.
+ * shape; (size_t)-1 for an unsupported one).
  */
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
 
@@ -145,7 +147,7 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "sum_e"          values per lane in a tree-sum chunk: 16 or 32 (default)
  *   "sum_depth"      tree-sum chunks in flight per wave: 2 (default) or 4
  *   "sum_blocks"     target number of tree-sum workgroups, 1..8192 (default
- *                    2048); each wave then streams a power-of-two run of chunks
+ *                    8192); each wave then streams a power-of-two run of chunks
  *   "var_load_path"  row variance: as sum_load_path (default 1)
  *   "var_nt"         row variance: as sum_nt (default 0)
  *   "var_rows_per_wave"  rows of 1025..4096 values one wave pipelines (the

@@ -88,8 +88,8 @@ def set_tuning(key: str, value: int) -> None:
 
 
 # Workspaces: one buffer per (device, stream), zero-filled when allocated; the
-# library leaves its ticket counter (first 256 bytes) at zero after every
-# call, so it is reused in stream order.
+# library leaves its ticket counters at zero after every call, so it is
+# reused in stream order.
 _workspaces: dict = {}
 
 

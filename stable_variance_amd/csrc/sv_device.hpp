@@ -201,6 +201,24 @@ __device__ __forceinline__ Node wave_tree(Node n) {
   return n;
 }
 
+// The same six levels when lane L holds the range of virtual lane
+// v(L) = 4*(L % 16) + L / 16 (the layout of the LDS-DMA row buffers below):
+// virtual bits 0 and 1 are lane bits 4 and 5, virtual bits 2..5 are lane bits
+// 0..3.  The first two levels need the exact partner (lane xor 16, xor 32);
+// after them the quad permutations are exact and the mirrors again reach the
+// sibling because the lower lanes already agree.
+template <bool NN>
+__device__ __forceinline__ Node wave_tree_vlane(Node n) {
+  auto comb = [](Node a, Node b) { return NN ? combine_nn(a, b) : combine(a, b); };
+  n = comb(n, shfl_xor_node(n, 16));
+  n = comb(n, shfl_xor_node(n, 32));
+  n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
+  n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
+  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
+  n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
+  return n;
+}
+
 // ---------------------------------------------------------------- loads
 
 // Wave-scope ordering of LDS traffic between the lanes of one wave.

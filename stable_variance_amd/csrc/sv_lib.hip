@@ -107,10 +107,13 @@ __device__ __forceinline__ Node load_node_agent(const Node *src) {
 // ------------------------------------------------------------------ tree sum
 
 constexpr int SUM_W = 4;                            // waves per workgroup
-constexpr int SUM_TOP_PER_THREAD = 32;              // group nodes per thread at the top
-constexpr int SUM_MAX_BLOCKS = 64 * SUM_W * SUM_TOP_PER_THREAD;  // 8192 workgroups
+constexpr int SUM_MAX_BLOCKS = 8192;                // workgroups of one tree-sum launch
 constexpr int SUM_MAX_LOG2_GROUP = 16;              // chunks per wave <= 2^16
-constexpr size_t SUM_WS_HEADER = 256;               // ticket counter, padded
+constexpr int SUM_GROUP = 64;                       // workgroups per first-level ticket
+static_assert(SV_TREE_SUM_COUNTER_BYTES == 256 * (1 + SUM_MAX_BLOCKS / SUM_GROUP), "header constant");
+constexpr int SUM_COUNTER_STRIDE = 64;              // counters 256 bytes apart
+// counters: the top one, then one per group of SUM_GROUP workgroups
+constexpr size_t SUM_WS_HEADER = 256 * (1 + SUM_MAX_BLOCKS / SUM_GROUP);
 
 // Each wave streams its own run of G = 2^log2_g consecutive chunks of 64*E
 // values (chunks beyond n are zero nodes), reducing chunk j while the loads
@@ -118,8 +121,11 @@ constexpr size_t SUM_WS_HEADER = 256;               // ticket counter, padded
 // with a binary-counter stack.  The W wave nodes of a workgroup are
 // consecutive, so their tree is the workgroup's group node; it goes to the
 // workspace and the last workgroup to take a ticket reduces the group nodes.
+#ifndef SV_SUM_MINW
+#define SV_SUM_MINW 1
+#endif
 template <int E, int W, bool VEC, int LOADP, bool NT, int D>
-__global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_g,
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_MINW, 8))) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_g,
                                                      Node *__restrict__ part, unsigned *__restrict__ counter,
                                                      float *__restrict__ out) {
   using C = sv::Chunk<E, VEC, LOADP, NT>;
@@ -172,47 +178,68 @@ __global__ __launch_bounds__(64 * W) void k_tree_sum(const float *__restrict__ x
   if (lane == 0) slots[w] = st[0];
   __syncthreads();
 
-  // Publish the group node, then take a ticket.  The node is written with a
-  // device-coherent (agent scope) store and read back below with
-  // device-coherent loads, so no cache writeback or invalidation is needed;
-  // waiting for the store's completion (vmcnt 0) before the ticket increment
-  // orders the two.  An agent-scope release fence would instead write back the
-  // whole L2 of the XCD once per workgroup.
+  // Two-level ticket.  Workgroups are grouped by SUM_GROUP consecutive
+  // indices; each publishes its node and takes a ticket on its group's
+  // counter; the last of a group reduces the group's nodes (an aligned run,
+  // so a node of the same tree) and takes a ticket on the top counter; the
+  // last group reduces the group nodes and writes the result.  Separate
+  // counters keep the same-address atomics to SUM_GROUP per counter instead
+  // of one per workgroup on a single address.
+  //
+  // Nodes are written with device-coherent (agent scope) stores and read
+  // with device-coherent loads, so no cache writeback or invalidation is
+  // needed; waiting for the stores' completion (vmcnt 0) before the ticket
+  // increment orders the two.  An agent-scope release fence would instead
+  // write back the whole L2 of the XCD for every workgroup.
+  const int nb = (int)gridDim.x;
+  const int grp = (int)blockIdx.x / SUM_GROUP;
+  const int ngroups = (nb + SUM_GROUP - 1) / SUM_GROUP;
+  const int in_group = (grp == ngroups - 1) ? nb - grp * SUM_GROUP : SUM_GROUP;
+  unsigned *const top_counter = counter;
+  unsigned *const grp_counter = counter + SUM_COUNTER_STRIDE * (1 + grp);
+  Node *const grp_nodes = part + SUM_MAX_BLOCKS;
   if (threadIdx.x == 0) {
     Node nd[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nd[i] = slots[i];
     store_node_agent(part + blockIdx.x, sv::node_tree<0, W, W>(nd));
     wait_vmem_stores();
-    const unsigned ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (ticket == gridDim.x - 1) ? 1u : 0u;
+    const unsigned ticket = __hip_atomic_fetch_add(grp_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (ticket == (unsigned)in_group - 1) ? 1u : 0u;
   }
   __syncthreads();
-  if (!is_last) return;
+  if (!is_last || w != 0) return;
 
-  // Last workgroup: tree over the gridDim.x group nodes, padded with zeros.
-  // Each thread owns K consecutive nodes, read in batches of 8 (subtrees of
-  // 8 nodes) to keep few registers live.
-  constexpr int K = SUM_TOP_PER_THREAD;
-  constexpr int B = 8;
-  static_assert(64 * W * K == SUM_MAX_BLOCKS && K % B == 0, "top layout");
-  const int nb = (int)gridDim.x;
-  Node sub[K / B];
-  for (int b = 0; b < K / B; ++b) {
-    Node nd[B];
-#pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const int idx = threadIdx.x * K + b * B + k;
-      nd[k] = (idx < nb) ? load_node_agent(part + idx) : sv::zero_node();
+  // Last workgroup of its group (wave 0): tree over the group's SUM_GROUP
+  // block nodes (one per lane, zero past the grid).
+  {
+    const int idx = grp * SUM_GROUP + lane;
+    Node g = (idx < nb) ? load_node_agent(part + idx) : sv::zero_node();
+    g = sv::wave_tree<false>(g);
+    unsigned top_ticket = 0;
+    if (lane == 0) {
+      __hip_atomic_store(grp_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      store_node_agent(grp_nodes + grp, g);
+      wait_vmem_stores();
+      top_ticket = __hip_atomic_fetch_add(top_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    sub[b] = sv::node_tree<0, B, B>(nd);
+    top_ticket = __shfl(top_ticket, 0, 64);
+    if (top_ticket != (unsigned)ngroups - 1) return;
   }
-  Node r = sv::node_tree<0, K / B, K / B>(sub);
-  r = sv::wave_tree<false>(r);
-  r = block_tree<W, false>(r, slots, w, lane);
-  if (threadIdx.x == 0) {
+
+  // Last group: tree over the ngroups group nodes (two per lane), padded
+  // with zeros to SUM_MAX_BLOCKS / SUM_GROUP.
+  static_assert(SUM_MAX_BLOCKS / SUM_GROUP == 128, "two group nodes per lane");
+  Node t[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = 2 * lane + k;
+    t[k] = (idx < ngroups) ? load_node_agent(grp_nodes + idx) : sv::zero_node();
+  }
+  Node r = sv::wave_tree<false>(sv::combine(t[0], t[1]));
+  if (lane == 0) {
     out[0] = sv::root_value(r);
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(top_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -355,6 +382,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW, 8))) 
   }
 }
 
+// Axis 1, rows of n <= 4096 values with n % 4 == 0 and 16-byte aligned rows:
+// the row's loads go straight from HBM into LDS (global_load_lds, 16 bytes
+// per lane and 1 KiB per instruction) without passing through registers.  A
+// wave owns R consecutive rows: it waits for row k in its LDS buffer, copies
+// it into registers, starts the DMA of row k+1 into the same buffer and then
+// reduces row k, so the next row streams in while the three trees run.  The
+// waves of a workgroup are independent.
+//
+// LDS row buffer: 16 blocks of 1 KiB (one DMA instruction each), each block
+// followed by 16 bytes of padding (260 floats per block).  Lane L reads the 64
+// consecutive values of virtual lane v(L) = 4*(L % 16) + L/16, which lie in
+// block L % 16 at offset 64*(L/16): 16 consecutive lanes then hit 16 distinct
+// 4-bank groups.  The cross-lane tree follows the virtual lane order.
+constexpr int DMA_BLK_F = 260;              // floats per 1 KiB block + padding
+constexpr int DMA_ROW_F = 16 * DMA_BLK_F;   // one row buffer (16,640 bytes)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int R, int W>
+__global__ __launch_bounds__(64 * W) void k_var_rows_dma(const float *__restrict__ x, int64_t rows, int64_t n,
+                                                         int64_t ld, int64_t ddof, float *__restrict__ var_out,
+                                                         float *__restrict__ mean_out) {
+  constexpr int E = 64;
+  __shared__ float lds[W][DMA_ROW_F];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t r0 = ((int64_t)blockIdx.x * W + w) * R;
+  const int vl = 4 * (lane % 16) + lane / 16;  // virtual lane
+  const bool full = (n == 64 * E);
+  const int64_t vv = n - (int64_t)vl * E;
+  const int valid = vv < 0 ? 0 : (vv > E ? E : (int)vv);
+  float *const buf = lds[w];
+
+  // Start the DMA of row r (lanes past n load nothing).
+  auto dma_row = [&](int64_t r) {
+    const float *src = x + r * ld + 4 * lane;
+    if (full) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        __builtin_amdgcn_global_load_lds((glb_void_t *)(src + 256 * k), (lds_void_t *)(buf + k * DMA_BLK_F), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (256 * k + 4 * lane < n)
+          __builtin_amdgcn_global_load_lds((glb_void_t *)(src + 256 * k), (lds_void_t *)(buf + k * DMA_BLK_F), 16, 0,
+                                           0);
+    }
+  };
+
+  if (r0 < rows) dma_row(r0);
+#pragma unroll 1
+  for (int k = 0; k < R; ++k) {
+    const int64_t r = r0 + k;
+    if (r >= rows) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): row k is in LDS
+    float v[E];
+    const float *src = buf + (lane % 16) * DMA_BLK_F + (lane / 16) * 64;
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      const float4 t = *reinterpret_cast<const float4 *>(src + 4 * j);
+      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before the buffer is refilled
+    if (k + 1 < R && r + 1 < rows) dma_row(r + 1);
+
+    const float x0 = x[r * ld];
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+    }
+    Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+    ny = sv::wave_tree_vlane<false>(ny);
+    const float m = sv::root_value(ny) / (float)n;
+    Node nd, nq;
+    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+    nd = sv::wave_tree_vlane<false>(nd);
+    nq = sv::wave_tree_vlane<true>(nq);
+    if (lane == 0) finalize(nd, nq, x0, m, n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
+  }
+}
+
 // ------------------------------------------------------------------ variance, axis 0
 
 template <int E, int W>
@@ -442,10 +555,11 @@ struct Tuning {
   int sum_nt = 1;             // non-temporal loads of the summed input
   int sum_e = 32;             // values per lane in a tree-sum chunk: 16 or 32
   int sum_depth = 2;          // chunks in flight per wave (register ring): 2 or 4
-  int64_t sum_blocks = 2048;  // target workgroup count of the tree sum
+  int64_t sum_blocks = 8192;  // target workgroup count of the tree sum
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
   int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
+  int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
 };
 Tuning g_tune;
 
@@ -511,9 +625,9 @@ SumPlan plan_sum(int64_t n, int e, int64_t target_blocks) {
 
 size_t sum_workspace_bytes(int64_t n) {
   if (n <= 0) return 0;
-  // sized for the largest workgroup count any tuning can produce
-  const SumPlan p = plan_sum(n, 16, SUM_MAX_BLOCKS);
-  return SUM_WS_HEADER + (size_t)p.blocks * sizeof(Node);
+  // counters, then one node per workgroup (room for the largest grid) and
+  // one per group of SUM_GROUP workgroups
+  return SUM_WS_HEADER + (size_t)(SUM_MAX_BLOCKS + SUM_MAX_BLOCKS / SUM_GROUP) * sizeof(Node);
 }
 
 template <int E, bool VEC, int LOADP, bool NT>
@@ -699,7 +813,14 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     const bool vec = aligned16(x) && (cols % 4 == 0);
     if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     else if (n <= 1024) launch_rows_ew<16, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    else if (n <= 4096) {
+    else if (n <= 4096 && vec && g_tune.var_dma_rows > 0) {
+      const int R = g_tune.var_dma_rows;
+      const int64_t waves = (rows + R - 1) / R;
+      const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+      if (R == 2) k_var_rows_dma<2, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
+      else if (R == 4) k_var_rows_dma<4, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
+      else k_var_rows_dma<8, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
+    } else if (n <= 4096) {
       const int R = g_tune.var_rows_per_wave;
       if (R == 2) launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
       else if (R == 4) launch_pipe_r<4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
@@ -749,6 +870,12 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     if (value != 1 && value != 2 && value != 4 && value != 8)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_rows_per_wave must be 1, 2, 4 or 8");
     g_tune.var_rows_per_wave = (int)value;
+    return ok();
+  }
+  if (strcmp(key, "var_dma_rows") == 0) {
+    if (value != 0 && value != 2 && value != 4 && value != 8)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_dma_rows must be 0, 2, 4 or 8");
+    g_tune.var_dma_rows = (int)value;
     return ok();
   }
   if (strcmp(key, "sum_e") == 0) {

@@ -53,12 +53,11 @@ def test_abi_version_and_status_strings(L):
 
 def test_workspace_sizes(L):
     assert L.sv_tree_sum_f32_workspace_size(0) == 0
-    # sized for the smallest tile (4096 values): header + one node per workgroup
-    assert L.sv_tree_sum_f32_workspace_size(1) == 256 + 8
-    assert L.sv_tree_sum_f32_workspace_size(4096) == 256 + 8
-    assert L.sv_tree_sum_f32_workspace_size(4097) == 256 + 16
-    # 24415 tiles -> groups of 4 tiles -> 6104 workgroups (at most 8192)
-    assert L.sv_tree_sum_f32_workspace_size(10 ** 8) == 256 + 8 * 6104
+    # counters (one top + one per 64 workgroups, 256 bytes apart), then a node
+    # per workgroup (up to 8192) and per group of 64 workgroups
+    want = 33024 + 8 * (8192 + 128)
+    for n in (1, 4096, 4097, 10 ** 8, 1 << 36):
+        assert L.sv_tree_sum_f32_workspace_size(n) == want
     assert L.sv_tree_sum_f32_workspace_size((1 << 36) + 1) == ctypes.c_size_t(-1).value
     assert L.sv_variance_f32_workspace_size(4096, 4096, 1) == 0
     assert L.sv_variance_f32_workspace_size(1000, 64, 0) == 0
@@ -72,7 +71,7 @@ def test_sum_argument_errors(L):
     assert L.sv_tree_sum_f32(None, 10, BAD, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_tree_sum_f32(BAD, 10, BAD, None, 0, None) == SV_ERR_WORKSPACE
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100000), 8, None) == SV_ERR_WORKSPACE
-    assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100010), 4096, None) == SV_ERR_WORKSPACE
+    assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100010), 1 << 20, None) == SV_ERR_WORKSPACE
     assert b"aligned" in L.sv_last_error_message()
     assert L.sv_tree_sum_f32(BAD, (1 << 36) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
 
@@ -107,7 +106,7 @@ def test_no_device_is_reported(L):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is visible; the no-device path is checked on GPU-less hosts")
     ws = ctypes.c_void_p(0x100000)
-    assert L.sv_tree_sum_f32(BAD, 10, BAD, ws, 4096, None) == SV_ERR_NO_DEVICE
+    assert L.sv_tree_sum_f32(BAD, 10, BAD, ws, 1 << 20, None) == SV_ERR_NO_DEVICE
     assert L.sv_variance_f32(BAD, 4, 4, 1, 0, BAD, None, None, 0, None) == SV_ERR_NO_DEVICE
 
 
