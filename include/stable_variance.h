@@ -97,8 +97,13 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
                           size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of workspace sv_variance_f32 needs (currently 0 for every supported
- * shape; (size_t)-1 for an unsupported one).
+ * Bytes of workspace sv_variance_f32 needs: 0 when every slice fits one
+ * workgroup (axis 1: n <= 16384 values; axis 0: n <= 1024 values), else
+ * 24 bytes per 16384-value (axis 1) or 1024-value (axis 0) chunk of every
+ * slice plus 4 bytes per slice (long slices are reduced in chunks, reading
+ * the input twice).  (size_t)-1 for an unsupported shape (a slice of more
+ * than 8192 chunks, a bad axis, rows * cols >= 2^40).  The workspace must be
+ * 256-byte aligned and needs no initialisation.
  */
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
 
@@ -120,8 +125,10 @@ size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
  * An empty slice (n == 0) gives var = mean = NaN.
  *   ddof       >= 0
  *   mean_out   may be NULL (the mean is then not written)
- *   workspace  may be NULL when sv_variance_f32_workspace_size(...) == 0
- * rows and cols must be >= 0 with rows * cols < 2^40.
+ *   workspace  device buffer of sv_variance_f32_workspace_size(...) bytes;
+ *              may be NULL when that size is 0
+ * rows and cols must be >= 0 with rows * cols < 2^40; a slice may hold at
+ * most 8192 chunks (axis 1: 134,217,728 values; axis 0: 8,388,608 values).
  */
 sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
                           float *var_out, float *mean_out, void *workspace, size_t workspace_bytes,

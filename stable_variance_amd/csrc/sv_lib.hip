@@ -546,6 +546,208 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
   }
 }
 
+// ------------------------------------------------------------------ long slices
+
+// Slices longer than one workgroup's registers hold are cut into aligned
+// chunks (a chunk is a node of the slice's tree) and reduced in four
+// launches: y-tree node per chunk -> per slice m = Tree(y)/n -> d- and
+// d^2-tree nodes per chunk -> per slice top trees and step 4.  The input is
+// read twice.  Workspace per slice: nchunks y nodes, 2*nchunks d/d^2 nodes
+// and m.
+
+constexpr int LS_TOP_PER_THREAD = 32;                      // chunk nodes per thread at the top
+constexpr int LS_MAX_CHUNKS = 256 * LS_TOP_PER_THREAD;     // 8192 chunks per slice
+constexpr int64_t LS_ROW_CHUNK = 64LL * 64 * 4;            // axis 1: 16384 values (4 waves x 64 lanes x 64)
+constexpr int64_t LS_COL_CHUNK = 64LL * 16;                // axis 0: 1024 rows (16 waves x 64)
+
+struct LongWs {
+  Node *ny;   // [nslices][nch]
+  Node *nd;   // [nslices][nch]
+  Node *nq;   // [nslices][nch]
+  float *m;   // [nslices]
+};
+
+// Axis 1, pass 0 or 1 over chunk c of row r (block index = r * nch + c).
+template <int PASS, bool VEC>
+__global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t nch,
+                                                   LongWs ws) {
+  constexpr int E = 64, W = 4;
+  __shared__ Node slots[2][W];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x / nch;
+  const int64_t c = (int64_t)blockIdx.x % nch;
+  const float *__restrict__ row = x + r * ld;
+  const int64_t base = c * LS_ROW_CHUNK + (int64_t)w * 64 * E;
+  float v[E];
+  float dummy_lds[1];
+  sv::load_tile<E, VEC, 1, false>(row + base, n - base, dummy_lds, v, lane);
+  const float x0 = row[0];
+  const bool full = base + 64 * E <= n;
+  const int64_t vl = n - base - (int64_t)lane * E;
+  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+  }
+  const int64_t out = r * nch + c;
+  if constexpr (PASS == 0) {
+    Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+    ny = sv::wave_tree<false>(ny);
+    ny = block_tree<W, false>(ny, slots[0], w, lane);
+    if (threadIdx.x == 0) ws.ny[out] = ny;
+  } else {
+    const float m = ws.m[r];
+    Node nd, nq;
+    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+    nd = sv::wave_tree<false>(nd);
+    nq = sv::wave_tree<true>(nq);
+    nd = block_tree<W, false>(nd, slots[0], w, lane);
+    nq = block_tree<W, true>(nq, slots[1], w, lane);
+    if (threadIdx.x == 0) {
+      ws.nd[out] = nd;
+      ws.nq[out] = nq;
+    }
+  }
+}
+
+// Axis 0, pass 0 or 1 over rows [c*1024, (c+1)*1024) of 64 columns
+// (block index = colblock * nch + c); lanes own columns, the 16 waves own
+// consecutive blocks of 64 rows.
+template <int PASS>
+__global__ __launch_bounds__(1024) void k_long_cols(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                    LongWs ws) {
+  constexpr int E = 64, W = 16;
+  __shared__ Node s0[W][64];
+  __shared__ Node s1[W][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t cb = (int64_t)blockIdx.x / nch;
+  const int64_t c = (int64_t)blockIdx.x % nch;
+  const int64_t col = cb * 64 + lane;
+  const bool colok = col < C;
+  const int64_t ccol = colok ? col : C - 1;
+  const int64_t r0 = c * LS_COL_CHUNK + (int64_t)w * E;
+  const bool full = r0 + E <= R;
+  float v[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t rr = r0 + i;
+    const float t = x[(rr < R ? rr : R - 1) * C + ccol];
+    v[i] = (rr < R) ? t : 0.0f;
+  }
+  const float x0 = x[ccol];
+  const int64_t vl = R - r0;
+  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+  }
+  const int64_t out = ccol * nch + c;
+  if constexpr (PASS == 0) {
+    s0[w][lane] = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+    __syncthreads();
+    if (w == 0 && colok) {
+      Node nn[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) nn[i] = s0[i][lane];
+      ws.ny[out] = sv::node_tree<0, W, W>(nn);
+    }
+  } else {
+    const float m = ws.m[ccol];
+    Node nd, nq;
+    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+    s0[w][lane] = nd;
+    s1[w][lane] = nq;
+    __syncthreads();
+    if (w == 0 && colok) {
+      Node a[W], b[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        a[i] = s0[i][lane];
+        b[i] = s1[i][lane];
+      }
+#pragma unroll
+      for (int len = W; len > 1; len >>= 1)
+#pragma unroll
+        for (int k = 0; k < len / 2; ++k) {
+          a[k] = sv::combine(a[2 * k], a[2 * k + 1]);
+          b[k] = sv::combine_nn(b[2 * k], b[2 * k + 1]);
+        }
+      ws.nd[out] = a[0];
+      ws.nq[out] = b[0];
+    }
+  }
+}
+
+// Tree over the nch chunk nodes of one slice (one workgroup per slice), the
+// chunk nodes padded with zeros to LS_MAX_CHUNKS.
+template <bool NN>
+__device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t nch, Node *slots) {
+  constexpr int K = LS_TOP_PER_THREAD;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  Node sub[K / 8];
+#pragma unroll
+  for (int b = 0; b < K / 8; ++b) {
+    Node nd[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t idx = (int64_t)threadIdx.x * K + b * 8 + k;
+      nd[k] = idx < nch ? nodes[idx] : sv::zero_node();
+    }
+    if constexpr (NN) {
+#pragma unroll
+      for (int len = 8; len > 1; len >>= 1)
+#pragma unroll
+        for (int k = 0; k < len / 2; ++k) nd[k] = sv::combine_nn(nd[2 * k], nd[2 * k + 1]);
+      sub[b] = nd[0];
+    } else {
+      sub[b] = sv::node_tree<0, 8, 8>(nd);
+    }
+  }
+  Node r;
+  if constexpr (NN) {
+#pragma unroll
+    for (int len = K / 8; len > 1; len >>= 1)
+#pragma unroll
+      for (int k = 0; k < len / 2; ++k) sub[k] = sv::combine_nn(sub[2 * k], sub[2 * k + 1]);
+    r = sub[0];
+  } else {
+    r = sv::node_tree<0, K / 8, K / 8>(sub);
+  }
+  r = sv::wave_tree<NN>(r);
+  return block_tree<4, NN>(r, slots, w, lane);
+}
+
+// PASS 0: m = Tree(y) / n.  PASS 1: the top trees of d and d^2 and step 4.
+// One 256-thread workgroup per slice; the slice's first value is at
+// x[s * sstride].
+template <int PASS>
+__global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, int64_t n, int64_t sstride,
+                                                  int64_t nch, int64_t ddof, LongWs ws, float *__restrict__ var_out,
+                                                  float *__restrict__ mean_out) {
+  __shared__ Node slots[2][4];
+  const int64_t sl = blockIdx.x;
+  if constexpr (PASS == 0) {
+    const Node ny = top_tree<false>(ws.ny + sl * nch, nch, slots[0]);
+    if (threadIdx.x == 0) ws.m[sl] = sv::root_value(ny) / (float)n;
+  } else {
+    const Node nd = top_tree<false>(ws.nd + sl * nch, nch, slots[0]);
+    const Node nq = top_tree<true>(ws.nq + sl * nch, nch, slots[1]);
+    if (threadIdx.x == 0)
+      finalize(nd, nq, x[sl * sstride], ws.m[sl], n, ddof, var_out + sl, mean_out ? mean_out + sl : nullptr);
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 thread_local char g_err[512];
@@ -601,6 +803,18 @@ constexpr int64_t SUM_MAX_N = 1LL << 36;
 constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
 constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel
 constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
+
+// Long-slice workspace: y, d and d^2 chunk nodes per slice, then m.
+size_t long_ws_bytes(int64_t nslices, int64_t nch) {
+  return (size_t)nslices * (size_t)nch * 3 * sizeof(Node) + (size_t)nslices * sizeof(float);
+}
+
+LongWs long_ws(void *workspace, int64_t nslices, int64_t nch) {
+  char *p = reinterpret_cast<char *>(workspace);
+  const size_t nodes = (size_t)nslices * (size_t)nch * sizeof(Node);
+  return {reinterpret_cast<Node *>(p), reinterpret_cast<Node *>(p + nodes), reinterpret_cast<Node *>(p + 2 * nodes),
+          reinterpret_cast<float *>(p + 3 * nodes)};
+}
 
 struct SumPlan {
   int e;
@@ -767,16 +981,18 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis) {
   if (rows < 0 || cols < 0) return (size_t)-1;
   if (axis != 0 && axis != 1 && axis != -1 && axis != -2) return (size_t)-1;
+  if (cols > 0 && rows > VAR_MAX_ELEMS / cols) return (size_t)-1;
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t n = ax1 ? cols : rows;
-  if (ax1 ? (n > ROWS_MAX_N) : (n > COLS_MAX_R)) return (size_t)-1;
-  return 0;
+  const int64_t nslices = ax1 ? rows : cols;
+  if (ax1 ? (n <= ROWS_MAX_N) : (n <= COLS_MAX_R)) return 0;
+  const int64_t nch = ax1 ? (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK : (n + LS_COL_CHUNK - 1) / LS_COL_CHUNK;
+  if (nch > LS_MAX_CHUNKS) return (size_t)-1;
+  return long_ws_bytes(nslices, nch);
 }
 
 sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, float *var_out,
                           float *mean_out, void *workspace, size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (rows < 0 || cols < 0)
     return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: negative shape [%lld, %lld]", (long long)rows,
                 (long long)cols);
@@ -793,12 +1009,21 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
   if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: x is NULL");
   if (nslices > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: %lld slices exceed the grid", (long long)nslices);
-  if (ax1 && n > ROWS_MAX_N)
-    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: axis-1 slices of length %lld above %lld", (long long)n,
-                (long long)ROWS_MAX_N);
-  if (!ax1 && n > COLS_MAX_R)
-    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: axis-0 slices of length %lld above %lld", (long long)n,
-                (long long)COLS_MAX_R);
+  const bool is_long = ax1 ? (n > ROWS_MAX_N) : (n > COLS_MAX_R);
+  const int64_t nch = !is_long ? 0
+                      : ax1    ? (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK
+                               : (n + LS_COL_CHUNK - 1) / LS_COL_CHUNK;
+  if (is_long) {
+    if (nch > LS_MAX_CHUNKS)
+      return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: slices of length %lld exceed %d chunks", (long long)n,
+                  LS_MAX_CHUNKS);
+    const size_t need = long_ws_bytes(nslices, nch);
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_f32: workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(SV_ERR_WORKSPACE, "sv_variance_f32: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(SV_ERR_WORKSPACE, "sv_variance_f32: workspace is not 256-byte aligned");
+  }
   const sv_status dev = check_device();
   if (dev != SV_OK) return dev;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -807,6 +1032,27 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     const unsigned blocks = (unsigned)((nslices + 255) / 256);
     k_fill<<<blocks, 256, 0, st>>>(var_out, nslices, __builtin_nanf(""));
     if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
+    return check_launch("sv_variance_f32");
+  }
+  if (is_long) {
+    const LongWs ws = long_ws(workspace, nslices, nch);
+    if (ax1) {
+      const bool vec = aligned16(x) && (cols % 4 == 0);
+      const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
+      if (vec) k_long_rows<0, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      else k_long_rows<0, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      k_long_top<0><<<top, 256, 0, st>>>(x, n, cols, nch, ddof, ws, var_out, mean_out);
+      if (vec) k_long_rows<1, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      else k_long_rows<1, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      k_long_top<1><<<top, 256, 0, st>>>(x, n, cols, nch, ddof, ws, var_out, mean_out);
+    } else {
+      const int64_t ncb = (cols + 63) / 64;
+      const dim3 grid((unsigned)(ncb * nch)), block(1024), top((unsigned)cols);
+      k_long_cols<0><<<grid, block, 0, st>>>(x, rows, cols, nch, ws);
+      k_long_top<0><<<top, 256, 0, st>>>(x, rows, 1, nch, ddof, ws, var_out, mean_out);
+      k_long_cols<1><<<grid, block, 0, st>>>(x, rows, cols, nch, ws);
+      k_long_top<1><<<top, 256, 0, st>>>(x, rows, 1, nch, ddof, ws, var_out, mean_out);
+    }
     return check_launch("sv_variance_f32");
   }
   if (ax1) {

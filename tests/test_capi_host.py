@@ -62,6 +62,11 @@ def test_workspace_sizes(L):
     assert L.sv_variance_f32_workspace_size(4096, 4096, 1) == 0
     assert L.sv_variance_f32_workspace_size(1000, 64, 0) == 0
     assert L.sv_variance_f32_workspace_size(1, 64, 3) == ctypes.c_size_t(-1).value
+    # long slices: 24 bytes per chunk (16384 values on axis 1, 1024 on axis 0) + 4 per slice
+    assert L.sv_variance_f32_workspace_size(3, 16385, 1) == 3 * 2 * 24 + 3 * 4
+    assert L.sv_variance_f32_workspace_size(1025, 7, 0) == 7 * 2 * 24 + 7 * 4
+    assert L.sv_variance_f32_workspace_size(1, 8192 * 16384, 1) == 8192 * 24 + 4
+    assert L.sv_variance_f32_workspace_size(1, 8192 * 16384 + 1, 1) == ctypes.c_size_t(-1).value
 
 
 def test_sum_argument_errors(L):
@@ -86,6 +91,12 @@ def test_variance_argument_errors(L):
     assert L.sv_variance_f32(BAD, 1 << 21, 1 << 20, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
     # an empty set of slices is a successful no-op
     assert L.sv_variance_f32(None, 0, 5, 1, 0, None, None, None, 0, None) == 0
+    # long slices need a workspace of the advertised size, 256-byte aligned
+    assert L.sv_variance_f32(BAD, 2, 20000, 1, 0, out, None, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_f32(BAD, 2, 20000, 1, 0, out, None, ctypes.c_void_p(0x100000), 8, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_f32(BAD, 2, 20000, 1, 0, out, None, ctypes.c_void_p(0x100040), 4096, None) == \
+        SV_ERR_WORKSPACE
+    assert L.sv_variance_f32(BAD, 1, 8192 * 16384 + 1, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
 def test_tuning_knob_validation(L):

@@ -265,15 +265,55 @@ def test_variance_empty_slices(torch_dev):
 
 
 def test_variance_unsupported_shape_leaves_output(torch_dev):
+    # Rejected on the host (a slice of more than 8192 chunks) before any
+    # access: the small buffer is never read and the output is untouched.
     import ctypes
 
     import stable_variance_amd as sv
 
     torch, dev = torch_dev
     L = sv.capi()
-    x = torch.zeros(2, 20000, device=dev)
-    out = torch.full((2,), 7.0, device=dev)
-    st = L.sv_variance_f32(x.data_ptr(), 2, 20000, 1, 0, out.data_ptr(), None, None, 0, None)
+    x = torch.zeros(16, device=dev)
+    out = torch.full((1,), 7.0, device=dev)
+    big = 8192 * 16384 + 1
+    st = L.sv_variance_f32(x.data_ptr(), 1, big, 1, 0, out.data_ptr(), None, None, 0, None)
     assert st == 5
     assert torch.all(out == 7.0)
-    assert L.sv_variance_f32_workspace_size(2, 20000, 1) == ctypes.c_size_t(-1).value
+    assert L.sv_variance_f32_workspace_size(1, big, 1) == ctypes.c_size_t(-1).value
+
+
+LONG_ROW_NS = [16385, 20000, 32768, 50001, 100003]
+
+
+@pytest.mark.parametrize("n", LONG_ROW_NS)
+def test_variance_long_rows(torch_dev, n):
+    # axis-1 slices beyond one workgroup: chunked two-pass path
+    rng = np.random.default_rng(n)
+    a = rng.normal(5e3, 3, (5, n)).astype(np.float32)
+    check_var(torch_dev, a, 1, 0)
+    check_var(torch_dev, a, 1, 3)
+    b = W.adversarial_values(3 * n, n).reshape(3, n)
+    check_var(torch_dev, b, 1, 0)
+    c = np.ascontiguousarray(a[:, 1:])  # misaligned rows (n-1 values, odd row stride)
+    check_var(torch_dev, c, 1, 0)
+
+
+@pytest.mark.parametrize("R", [1025, 2048, 3000, 5000])
+def test_variance_long_cols(torch_dev, R):
+    rng = np.random.default_rng(R)
+    for C in (1, 64, 130):
+        a = rng.normal(-7e3, 0.5, (R, C)).astype(np.float32)
+        check_var(torch_dev, a, 0, 0)
+        check_var(torch_dev, a, 0, 1)
+    b = W.adversarial_values(R * 33, R).reshape(R, 33)
+    check_var(torch_dev, b, 0, 0)
+
+
+def test_variance_single_long_row(torch_dev):
+    # one slice of 2^22 + 3 values (256 chunks) and its constant version
+    rng = np.random.default_rng(22)
+    n = (1 << 22) + 3
+    a = rng.normal(1e6, 1, (1, n)).astype(np.float32)
+    check_var(torch_dev, a, 1, 0)
+    v = check_var(torch_dev, np.full((1, n), np.float32(1e38)), 1, 0)
+    assert v[0] == 0.0
