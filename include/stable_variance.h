@@ -135,6 +135,26 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
                           void *stream);
 
 /*
+ * Complex64 variance (Pennacchio, "Variance in float32 ...", §2: a complex
+ * input is split into its real and imaginary parts and the two variances
+ * are added, which is E|z - mean(z)|^2).
+ *   z          device pointer to a row-major [rows, cols] complex64 array
+ *              (interleaved re, im float32 pairs), 8-byte aligned
+ *   axis       as for sv_variance_f32
+ *   var_out    float32, one per slice: fl(var(re) + var(im)), each part
+ *              computed exactly as sv_variance_f32 computes it
+ *   mean_out   complex64 (interleaved), one per slice, or NULL:
+ *              (mean(re), mean(im))
+ *   workspace  sv_variance_c64_workspace_size(rows, cols, axis) bytes,
+ *              256-byte aligned, no initialisation (axis 1 stages the split
+ *              parts: 8 bytes per input value)
+ * Errors and asynchrony as for sv_variance_f32.
+ */
+size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis);
+sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, int64_t ddof, float *var_out,
+                          float *mean_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Measurement aid, not part of the method: reads x[0 .. n) once from HBM with
  * plain non-temporal 16-byte loads (x 16-byte aligned, n <= 2^36) and does no
  * arithmetic of the method, so its duration is the practical read ceiling

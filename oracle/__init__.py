@@ -289,4 +289,7 @@ def variance_complex(z, axis: int = -1, ddof: int = 0, method: int = METHOD_KERN
     z = np.asarray(z, dtype=np.complex64)
     vr, mr = variance(np.ascontiguousarray(z.real), axis=axis, ddof=ddof, method=method)
     vi, mi = variance(np.ascontiguousarray(z.imag), axis=axis, ddof=ddof, method=method)
-    return (vr + vi).astype(np.float32), (mr + 1j * mi.astype(np.complex64)).astype(np.complex64)
+    mean = np.empty(mr.shape, np.complex64)
+    mean.real = mr
+    mean.imag = mi
+    return (vr + vi).astype(np.float32), mean

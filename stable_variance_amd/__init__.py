@@ -70,6 +70,10 @@ def capi():
                 L.sv_variance_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_set_tuning.restype = ctypes.c_int
                 L.sv_set_tuning.argtypes = [ctypes.c_char_p, i64]
+                L.sv_variance_c64_workspace_size.restype = sz
+                L.sv_variance_c64_workspace_size.argtypes = [i64, i64, ctypes.c_int]
+                L.sv_variance_c64.restype = ctypes.c_int
+                L.sv_variance_c64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_probe_read_bandwidth.restype = ctypes.c_int
                 L.sv_probe_read_bandwidth.argtypes = [vp, i64, vp, vp]
                 _lib = L
@@ -87,18 +91,19 @@ def set_tuning(key: str, value: int) -> None:
     _check(capi().sv_set_tuning(key.encode(), int(value)))
 
 
-# Workspaces: one buffer per (device, stream), zero-filled when allocated; the
-# library leaves its ticket counters at zero after every call, so it is
-# reused in stream order.
+# Workspaces, one per (kind, device, stream).  The tree sum's buffer is
+# zero-filled when allocated and the library leaves its ticket counters at
+# zero after every call; the variance's buffer is scratch.  They are never
+# shared: scratch use would leave nonzero counters behind.
 _workspaces: dict = {}
 
 
-def _workspace(nbytes: int, device, stream_handle: int):
+def _workspace(kind: str, nbytes: int, device, stream_handle: int):
     import torch
 
     if nbytes == 0:
         return None
-    key = (device.index, stream_handle)
+    key = (kind, device.index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
@@ -106,13 +111,14 @@ def _workspace(nbytes: int, device, stream_handle: int):
     return ws
 
 
-def _check_tensor(x, name="x"):
+def _check_tensor(x, name="x", complex_ok=False):
     import torch
 
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if x.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32, got {x.dtype}")
+    ok = (torch.float32, torch.complex64) if complex_ok else (torch.float32,)
+    if x.dtype not in ok:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in ok)}, got {x.dtype}")
     if x.device.type != "cuda":
         raise ValueError(f"{name} must be on a HIP device, got {x.device}")
 
@@ -131,21 +137,24 @@ def tree_sum(x):
         need = L.sv_tree_sum_f32_workspace_size(n)
         if need == ctypes.c_size_t(-1).value:
             raise SvError(5, f"tree_sum: n = {n} is not supported")
-        ws = _workspace(need, x.device, stream)
+        ws = _workspace("sum", need, x.device, stream)
         _check(L.sv_tree_sum_f32(x.data_ptr() if n else None, n, out.data_ptr(),
                                  ws.data_ptr() if ws is not None else None, need, stream))
     return out
 
 
 def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
-    """Variance of each slice of a 2-D (or 1-D) float32 tensor along ``dim``.
+    """Variance of each slice of a 2-D (or 1-D) float32 or complex64 tensor
+    along ``dim``.
 
-    Returns a float32 tensor of the non-reduced length (and the mean when
-    ``return_mean``).
+    Returns a float32 tensor of the non-reduced length (and the mean, float32
+    or complex64, when ``return_mean``).  For complex64 data the variance is
+    var(re) + var(im), each part as for float32.
     """
     import torch
 
-    _check_tensor(x)
+    _check_tensor(x, complex_ok=True)
+    is_complex = x.dtype == torch.complex64
     if x.dim() == 1:
         x2 = x.reshape(1, -1)
         axis = 1
@@ -164,18 +173,20 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     rows, cols = x2.shape
     ns = rows if axis == 1 else cols
     L = capi()
+    fn = L.sv_variance_c64 if is_complex else L.sv_variance_f32
+    wsz = L.sv_variance_c64_workspace_size if is_complex else L.sv_variance_f32_workspace_size
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
         out = torch.empty(ns, dtype=torch.float32, device=x.device)
-        mean = torch.empty(ns, dtype=torch.float32, device=x.device) if return_mean else None
-        need = L.sv_variance_f32_workspace_size(rows, cols, axis)
+        mean = torch.empty(ns, dtype=x.dtype, device=x.device) if return_mean else None
+        need = wsz(rows, cols, axis)
         if need == ctypes.c_size_t(-1).value:
             raise SvError(5, f"var: shape {tuple(x2.shape)} along axis {axis} is not supported")
-        ws = _workspace(need, x.device, stream)
-        _check(L.sv_variance_f32(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof),
-                                 out.data_ptr() if ns else None,
-                                 mean.data_ptr() if (mean is not None and ns) else None,
-                                 ws.data_ptr() if ws is not None else None, need, stream))
+        ws = _workspace("var", need, x.device, stream)
+        _check(fn(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof),
+                  out.data_ptr() if ns else None,
+                  mean.data_ptr() if (mean is not None and ns) else None,
+                  ws.data_ptr() if ws is not None else None, need, stream))
     if squeeze:
         out = out.reshape(())
         mean = mean.reshape(()) if mean is not None else None

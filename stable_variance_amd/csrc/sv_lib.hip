@@ -243,6 +243,30 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
   }
 }
 
+// ------------------------------------------------------------------ complex64
+
+// Complex data as two float32 arrays (Pennacchio, "Variance in float32 ...",
+// §2: the real and imaginary parts are split and their variances added).
+// Row r of a [rows, cols] complex64 array (interleaved re, im) becomes rows
+// 2r (re) and 2r+1 (im) of a [2*rows, cols] float32 array.
+__global__ __launch_bounds__(256) void k_split_rows(const float *__restrict__ z, int64_t rows, int64_t cols,
+                                                    float *__restrict__ out) {
+  const int64_t total = rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / cols, c = i % cols;
+    const float2 v = reinterpret_cast<const float2 *>(z)[i];
+    out[(2 * r) * cols + c] = v.x;
+    out[(2 * r + 1) * cols + c] = v.y;
+  }
+}
+
+// var[j] = fl(v[2j] + v[2j+1]): the variance of the real part plus that of
+// the imaginary part.
+__global__ __launch_bounds__(256) void k_pair_add(const float *__restrict__ v, int64_t count, float *__restrict__ out) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j < count) out[j] = v[2 * j] + v[2 * j + 1];
+}
+
 // ------------------------------------------------------------------ measurement aid
 
 // Plain streaming read of n floats (non-temporal 16-byte loads, 4 per lane,
@@ -1084,6 +1108,73 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     else launch_cols_ew<64, 16>(x, rows, cols, ddof, var_out, mean_out, st);
   }
   return check_launch("sv_variance_f32");
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis) {
+  if (rows < 0 || cols < 0) return (size_t)-1;
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2) return (size_t)-1;
+  if (cols > 0 && rows > VAR_MAX_ELEMS / 2 / cols) return (size_t)-1;
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t nslices = ax1 ? rows : cols;
+  const size_t inner = ax1 ? sv_variance_f32_workspace_size(2 * rows, cols, 1)
+                           : sv_variance_f32_workspace_size(rows, 2 * cols, 0);
+  if (inner == (size_t)-1) return (size_t)-1;
+  size_t b = align256((size_t)2 * nslices * sizeof(float));  // per-component variances
+  if (ax1) b += align256((size_t)2 * rows * cols * sizeof(float));  // split rows
+  return b + inner;
+}
+
+sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, int64_t ddof, float *var_out,
+                          float *mean_out, void *workspace, size_t workspace_bytes, void *stream) {
+  if (rows < 0 || cols < 0)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: negative shape [%lld, %lld]", (long long)rows,
+                (long long)cols);
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: axis %d not in {0, 1, -1, -2}", axis);
+  if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: ddof = %lld < 0", (long long)ddof);
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t nslices = ax1 ? rows : cols;
+  if (nslices == 0) return ok();
+  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: var_out is NULL");
+  if (rows * cols > 0 && !z) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: z is NULL");
+  if (reinterpret_cast<uintptr_t>(z) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: z is not 8-byte aligned");
+  const size_t need = sv_variance_c64_workspace_size(rows, cols, axis);
+  if (need == (size_t)-1) return fail(SV_ERR_UNSUPPORTED, "sv_variance_c64: shape [%lld, %lld] not supported",
+                                      (long long)rows, (long long)cols);
+  if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace is not 256-byte aligned");
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  char *wp = reinterpret_cast<char *>(workspace);
+  float *vparts = reinterpret_cast<float *>(wp);
+  wp += align256((size_t)2 * nslices * sizeof(float));
+  sv_status rc;
+  if (ax1) {
+    float *split = reinterpret_cast<float *>(wp);
+    wp += align256((size_t)2 * rows * cols * sizeof(float));
+    const size_t inner = sv_variance_f32_workspace_size(2 * rows, cols, 1);
+    if (rows * cols > 0) {
+      const int64_t total = rows * cols;
+      const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
+      k_split_rows<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(z, rows, cols, split);
+      rc = check_launch("sv_variance_c64");
+      if (rc != SV_OK) return rc;
+    }
+    rc = sv_variance_f32(split, 2 * rows, cols, 1, ddof, vparts, mean_out, inner ? wp : nullptr, inner, stream);
+  } else {
+    const size_t inner = sv_variance_f32_workspace_size(rows, 2 * cols, 0);
+    rc = sv_variance_f32(z, rows, 2 * cols, 0, ddof, vparts, mean_out, inner ? wp : nullptr, inner, stream);
+  }
+  if (rc != SV_OK) return rc;
+  k_pair_add<<<dim3((unsigned)((nslices + 255) / 256)), dim3(256), 0, st>>>(vparts, nslices, var_out);
+  return check_launch("sv_variance_c64");
 }
 
 sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *stream) {

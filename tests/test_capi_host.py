@@ -99,6 +99,22 @@ def test_variance_argument_errors(L):
     assert L.sv_variance_f32(BAD, 1, 8192 * 16384 + 1, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
+def test_complex_argument_errors_and_sizes(L):
+    out = ctypes.c_void_p(0x2000)
+    # axis 0: per-component variances (2*cols floats) + the float view's own workspace (0 here)
+    assert L.sv_variance_c64_workspace_size(1000, 64, 0) == 512
+    # axis 1: per-component variances + split rows (8 bytes per value)
+    assert L.sv_variance_c64_workspace_size(64, 1000, 1) == 512 + 64 * 1000 * 8
+    assert L.sv_variance_c64_workspace_size(2, 3, 5) == ctypes.c_size_t(-1).value
+    assert L.sv_variance_c64(BAD, -1, 4, 1, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_c64(BAD, 4, 4, 7, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_c64(BAD, 4, 4, 1, -2, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_c64(ctypes.c_void_p(0x1004), 4, 4, 1, 0, out, None, None, 0, None) == \
+        SV_ERR_INVALID_ARGUMENT  # not 8-byte aligned
+    assert L.sv_variance_c64(BAD, 4, 4, 1, 0, out, None, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_c64(None, 0, 4, 1, 0, None, None, None, 0, None) == 0
+
+
 def test_tuning_knob_validation(L):
     assert L.sv_set_tuning(b"sum_load_path", 2) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(b"nope", 0) == SV_ERR_INVALID_ARGUMENT

@@ -162,8 +162,9 @@ def test_sum_workspace_left_zero_and_deterministic(torch_dev):
     for _ in range(5):
         assert same_bits(sv.tree_sum(t).item(), r0)
     torch.cuda.synchronize()
-    for ws in sv._workspaces.values():
-        assert int(ws[:33024].count_nonzero().item()) == 0  # the ticket counters are back to 0
+    for (kind, _, _), ws in sv._workspaces.items():
+        if kind == "sum":
+            assert int(ws[:33024].count_nonzero().item()) == 0  # the ticket counters are back to 0
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         r1 = sv.tree_sum(t)
@@ -317,3 +318,58 @@ def test_variance_single_long_row(torch_dev):
     check_var(torch_dev, a, 1, 0)
     v = check_var(torch_dev, np.full((1, n), np.float32(1e38)), 1, 0)
     assert v[0] == 0.0
+
+
+# ------------------------------------------------------------------ complex64
+
+def gpu_var_c64(torch_dev, z, axis, ddof=0):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    t = torch.from_numpy(np.ascontiguousarray(z, np.complex64)).to(dev)
+    v, m = sv.var(t, dim=axis, ddof=ddof, return_mean=True)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), m.cpu().numpy()
+
+
+def check_var_c64(torch_dev, z, axis, ddof=0):
+    v, m = gpu_var_c64(torch_dev, z, axis, ddof)
+    ov, om = oracle.variance_complex(z, axis=axis, ddof=ddof)
+    assert same_bits(v, ov), (z.shape, axis, ddof)
+    assert same_bits(m.view(np.float32), om.view(np.float32)), (z.shape, axis, ddof)
+    return v
+
+
+def test_complex_printed_values(torch_dev):
+    # Method page §2/§3: the complex check and the complex identical-values row.
+    from conftest import read_kv
+
+    g = read_kv("complex_check.txt")
+    z = np.array([complex(s.replace(" ", "")) for s in g["values"].split(",")], np.complex64)[None, :]
+    v = check_var_c64(torch_dev, z, 1)
+    assert v[0] == float(g["variance"])
+    zc = np.full((1, int(g["identical_count"])), complex(g["identical"]), np.complex64)
+    v = check_var_c64(torch_dev, zc, 1)
+    assert v[0] == float(g["identical_variance"])
+
+
+@pytest.mark.parametrize("shape", [(64, 1000), (3, 4096), (5, 20000), (1000, 64), (2000, 3), (1, 1), (7, 2)])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_complex_shapes(torch_dev, shape, axis):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    re = rng.normal(1e4, 1, shape)
+    im = rng.normal(-3e3, 0.5, shape)
+    z = (re + 1j * im).astype(np.complex64)
+    check_var_c64(torch_dev, z, axis, 0)
+    check_var_c64(torch_dev, z, axis, 1)
+
+
+def test_complex_then_sum_share_nothing(torch_dev):
+    # a scratch-using variance between two sums must not disturb the sums'
+    # ticket counters
+    x = W.sum_cancelling_pairs(2_000_000, 0.01, seed=9)
+    want = oracle.tree_sum(x)
+    assert same_bits(gpu_sum(torch_dev, x), want)
+    z = (np.random.default_rng(1).normal(0, 1, (3, 30000)) * (1 + 1j)).astype(np.complex64)
+    check_var_c64(torch_dev, z, 1)
+    assert same_bits(gpu_sum(torch_dev, x), want)
