@@ -155,6 +155,26 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
                           float *mean_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The variants of the method page's ablation (Pennacchio, "Variance in
+ * float32 ...", §4: one step changed at a time) and the two formulae of its
+ * §1, for accuracy and speed comparisons.  `variant`:
+ *   0  the method (same result as sv_variance_f32)
+ *   2  two-term reference formula: m = mean(x), d = x - m,
+ *      var = max(mean(d^2) - mean(d)^2, 0); mean() = plain tree * fl(1/n);
+ *      no shift (the returned mean is m)
+ *   3  naive formula: var = mean((x - mean(x))^2), means as in 2
+ *   4  shift + centring, plain trees, no two-term: var = max(S2/n, 0)
+ *   5  shift + centring + two-term, plain trees
+ *   6  no shift, two-term, compensated trees (the returned mean is m)
+ *   7  shift + centring, compensated trees, no two-term
+ * "Plain tree" is the same adjacent-pair topology without the error array.
+ * Shapes: axis 1 with n <= 16384, axis 0 with n <= 1024 (else
+ * SV_ERR_UNSUPPORTED).  No workspace; otherwise as sv_variance_f32.
+ */
+sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int variant,
+                                  float *var_out, float *mean_out, void *stream);
+
+/*
  * Measurement aid, not part of the method: reads x[0 .. n) once from HBM with
  * plain non-temporal 16-byte loads (x 16-byte aligned, n <= 2^36) and does no
  * arithmetic of the method, so its duration is the practical read ceiling

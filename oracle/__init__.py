@@ -46,6 +46,12 @@ METHOD_KERNEL = 0
 METHOD_KERNEL_PLAIN_SY = 1
 METHOD_REFERENCE = 2
 METHOD_NAIVE = 3
+# Ablation rows of the method page's §4 (one step changed at a time)
+METHOD_SHIFT_PLAIN_NO2T = 4      # shift + centring, plain tree, no two-term
+METHOD_SHIFT_PLAIN_2T = 5        # shift + centring + two-term, plain tree
+METHOD_NOSHIFT_COMP_2T = 6       # no shift, two-term, compensated tree
+METHOD_SHIFT_COMP_NO2T = 7       # shift + centring, compensated tree, no two-term
+METHOD_SHIFT_KAHAN_NO2T = 8      # shift + centring, sequential Kahan scan, no two-term
 
 _lib = None
 

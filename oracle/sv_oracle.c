@@ -224,6 +224,52 @@ static void var_kernel_slice(const float *x, int64_t n, int64_t stride, int64_t 
 }
 
 /*
+ * Ablation variants of [VAR] §4, one step changed at a time.  Flags:
+ *   shift    y = x - x0 (else y = x and mean = m)
+ *   sum_kind 0 plain tree, 1 compensated tree, 2 sequential Kahan scan
+ *            (the Kahan form of [KAHAN]) for every sum of the slice
+ *   twoterm  v = max(S2/n - (S1/n)^2, 0) (else v = max(S2/n, 0))
+ * READING: "no two-term" is v = max(S2/n, 0); the Kahan-scan row of the
+ * table ("shift + centring, Kahan sequential scan") has no two-term step,
+ * like the other rows whose label does not add one.
+ */
+static float slice_sum(const float *v, int64_t n, int sum_kind) {
+    if (sum_kind == 0) return orc_tree_plain_f32(v, n, 1, 0);
+    if (sum_kind == 1) return orc_tree_sum_f32(v, n, 1, 0);
+    return orc_seq_kahan_f32(v, n);
+}
+
+static void var_variant_slice(const float *x, int64_t n, int64_t stride, int64_t ddof, int shift, int sum_kind,
+                              int twoterm, float *buf, float *var, float *mean) {
+    if (n <= 0) {
+        *var = NAN;
+        *mean = NAN;
+        return;
+    }
+    gather(x, n, stride, buf);
+    float x0 = buf[0];
+    if (shift)
+        for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - x0;             /* y */
+    float fn = (float)n;
+    float m = slice_sum(buf, n, sum_kind) / fn;
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;                  /* d */
+    float s1 = twoterm ? slice_sum(buf, n, sum_kind) : 0.0f;
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] * buf[i];             /* q */
+    float s2 = slice_sum(buf, n, sum_kind);
+    float a = s2 / fn;
+    float v;
+    if (twoterm) {
+        float b = s1 / fn;
+        float bb = b * b;
+        v = max0_nan(a - bb);
+    } else {
+        v = max0_nan(a);
+    }
+    *var = ddof_scale(v, n, ddof);
+    *mean = shift ? x0 + m : m;
+}
+
+/*
  * READING (mean in the naive and reference formulae, [VAR] §1): mean(u) is
  * the plain pairwise tree of u multiplied by the rounded reciprocal fl(1/n).
  * The identical-values table of [VAR] §3 fixes this choice (a correctly
@@ -277,11 +323,17 @@ static void var_naive_slice(const float *x, int64_t n, int64_t stride, int64_t d
  *   axis 1: rows slices of length cols (contiguous)
  *   axis 0: cols slices of length rows (stride cols)
  * method: 0 kernel (comp_sy 1), 1 kernel with a plain Sy tree, 2 two-term
- * reference, 3 naive.  mean may be NULL.  Returns 0, or -1 on bad arguments.
+ * reference, 3 naive, and the [VAR] §4 ablation rows:
+ *   4 shift + centring, plain tree, no two-term
+ *   5 shift + centring + two-term, plain tree
+ *   6 no shift, two-term, compensated tree
+ *   7 shift + centring, compensated tree, no two-term
+ *   8 shift + centring, sequential Kahan scan, no two-term
+ * mean may be NULL.  Returns 0, or -1 on bad arguments.
  */
 int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
                      int method, float *var, float *mean) {
-    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || method < 0 || method > 3)
+    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || method < 0 || method > 8)
         return -1;
     int64_t nslices = axis == 1 ? rows : cols;
     int64_t n = axis == 1 ? cols : rows;
@@ -297,7 +349,12 @@ int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64
         case 0: var_kernel_slice(xs, n, stride, ddof, 1, buf, &v, &mu); break;
         case 1: var_kernel_slice(xs, n, stride, ddof, 0, buf, &v, &mu); break;
         case 2: var_reference_slice(xs, n, stride, ddof, buf, buf2, &v, &mu); break;
-        default: var_naive_slice(xs, n, stride, ddof, buf, &v, &mu); break;
+        case 3: var_naive_slice(xs, n, stride, ddof, buf, &v, &mu); break;
+        case 4: var_variant_slice(xs, n, stride, ddof, 1, 0, 0, buf, &v, &mu); break;
+        case 5: var_variant_slice(xs, n, stride, ddof, 1, 0, 1, buf, &v, &mu); break;
+        case 6: var_variant_slice(xs, n, stride, ddof, 0, 1, 1, buf, &v, &mu); break;
+        case 7: var_variant_slice(xs, n, stride, ddof, 1, 1, 0, buf, &v, &mu); break;
+        default: var_variant_slice(xs, n, stride, ddof, 1, 2, 0, buf, &v, &mu); break;
         }
         var[s] = v;
         if (mean) mean[s] = mu;

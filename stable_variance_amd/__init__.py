@@ -22,7 +22,7 @@ import threading
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["tree_sum", "var", "capi", "library_path", "SvError", "set_tuning"]
+__all__ = ["tree_sum", "var", "var_variant", "capi", "library_path", "SvError", "set_tuning", "VARIANTS"]
 
 SV_OK = 0
 _STATUS = {1: "SV_ERR_INVALID_ARGUMENT", 2: "SV_ERR_WORKSPACE", 3: "SV_ERR_NO_DEVICE", 4: "SV_ERR_HIP",
@@ -74,6 +74,8 @@ def capi():
                 L.sv_variance_c64_workspace_size.argtypes = [i64, i64, ctypes.c_int]
                 L.sv_variance_c64.restype = ctypes.c_int
                 L.sv_variance_c64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
+                L.sv_variance_variant_f32.restype = ctypes.c_int
+                L.sv_variance_variant_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
                 L.sv_probe_read_bandwidth.restype = ctypes.c_int
                 L.sv_probe_read_bandwidth.argtypes = [vp, i64, vp, vp]
                 _lib = L
@@ -190,4 +192,39 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     if squeeze:
         out = out.reshape(())
         mean = mean.reshape(()) if mean is not None else None
+    return (out, mean) if return_mean else out
+
+
+# Ablation variants of the method page's §4 (see sv_variance_variant_f32).
+VARIANTS = {
+    "kernel": 0,
+    "reference": 2,
+    "naive": 3,
+    "shift_plain_no2t": 4,
+    "shift_plain_2t": 5,
+    "noshift_comp_2t": 6,
+    "shift_comp_no2t": 7,
+}
+
+
+def var_variant(x, variant, dim: int = -1, ddof: int = 0, return_mean: bool = False):
+    """One of the ablation variants (a name of VARIANTS or its number) on a
+    2-D float32 tensor; single-workgroup shapes only."""
+    import torch
+
+    _check_tensor(x)
+    code = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    axis = 1 if x.dim() == 1 else dim % 2
+    x2 = x2.contiguous()
+    rows, cols = x2.shape
+    ns = rows if axis == 1 else cols
+    L = capi()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        out = torch.empty(ns, dtype=torch.float32, device=x.device)
+        mean = torch.empty(ns, dtype=torch.float32, device=x.device) if return_mean else None
+        _check(L.sv_variance_variant_f32(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof), code,
+                                         out.data_ptr() if ns else None,
+                                         mean.data_ptr() if (mean is not None and ns) else None, stream))
     return (out, mean) if return_mean else out

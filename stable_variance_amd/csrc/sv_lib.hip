@@ -63,6 +63,91 @@ __device__ __forceinline__ Node block_tree(Node n, Node *slots, int w, int lane)
   }
 }
 
+// Variants of the slice computation (the ablation rows of the method page's
+// §4, numbered as the C ABI's `variant`).  V_KERNEL is the method.
+enum Variant {
+  V_KERNEL = 0,           // shift + centring + two-term, compensated trees
+  V_REFERENCE = 2,        // two-term formula: means as plain tree * fl(1/n), no shift
+  V_NAIVE = 3,            // mean((x - mean(x))^2), means as plain tree * fl(1/n)
+  V_SHIFT_PLAIN_NO2T = 4,
+  V_SHIFT_PLAIN_2T = 5,
+  V_NOSHIFT_COMP_2T = 6,
+  V_SHIFT_COMP_NO2T = 7,
+};
+template <int V>
+struct VariantFlags {
+  static constexpr bool shift = V == V_KERNEL || V == V_SHIFT_PLAIN_NO2T || V == V_SHIFT_PLAIN_2T ||
+                                V == V_SHIFT_COMP_NO2T;
+  static constexpr bool comp = V == V_KERNEL || V == V_NOSHIFT_COMP_2T || V == V_SHIFT_COMP_NO2T;
+  static constexpr bool twoterm = V == V_KERNEL || V == V_REFERENCE || V == V_SHIFT_PLAIN_2T || V == V_NOSHIFT_COMP_2T;
+  static constexpr bool recip = V == V_REFERENCE || V == V_NAIVE;
+};
+
+// The value of a slice sum: the compensated tree's root, or the plain tree
+// (the s part of the same nodes: s is formed as in a plain pairwise tree).
+template <bool COMP>
+__device__ __forceinline__ float tree_value(Node n) {
+  return COMP ? sv::root_value(n) : n.s;
+}
+
+// m from the slice sum of y: a division by fl(n), or the product with
+// fl(1/n) for the formulae whose means are tree * fl(1/n).
+template <int V>
+__device__ __forceinline__ float local_mean(Node ny, int64_t n) {
+  using F = VariantFlags<V>;
+  const float sy = tree_value<F::comp>(ny);
+  const float fn = (float)n;
+  if constexpr (F::recip) {
+    const float inv = 1.0f / fn;
+    return sy * inv;
+  } else {
+    return sy / fn;
+  }
+}
+
+__device__ __forceinline__ float max0_nan(float v) { return (v != v) ? v : ((v > 0.0f) ? v : 0.0f); }
+
+__device__ __forceinline__ float ddof_rescale(float v, int64_t n, int64_t ddof) {
+  if (ddof == 0) return v;
+  int64_t den = n - ddof;
+  if (den < 0) den = 0;
+  const float f = (float)n / (float)den;
+  return v * f;
+}
+
+// Step 4 of a variant (see finalize for the method itself).
+template <int V>
+__device__ __forceinline__ void finalize_v(Node nd, Node nq, float x0, float m, int64_t n, int64_t ddof,
+                                           float *var_out, float *mean_out) {
+  using F = VariantFlags<V>;
+  const float fn = (float)n;
+  const float s1 = tree_value<F::comp>(nd);
+  const float s2 = tree_value<F::comp>(nq);
+  float v;
+  if constexpr (F::recip) {
+    const float inv = 1.0f / fn;
+    const float a = s2 * inv;
+    if constexpr (F::twoterm) {
+      const float b = s1 * inv;
+      const float bb = b * b;
+      v = max0_nan(a - bb);
+    } else {
+      v = a;
+    }
+  } else {
+    const float a = s2 / fn;
+    if constexpr (F::twoterm) {
+      const float b = s1 / fn;
+      const float bb = b * b;
+      v = max0_nan(a - bb);
+    } else {
+      v = max0_nan(a);
+    }
+  }
+  *var_out = ddof_rescale(v, n, ddof);
+  if (mean_out) *mean_out = F::shift ? x0 + m : m;
+}
+
 // Step 4 of the method: two-term correction, NaN-propagating max with 0,
 // ddof rescale, and the mean x0 + m.
 __device__ __forceinline__ void finalize(Node nd, Node nq, float x0, float m, int64_t n, int64_t ddof,
@@ -298,9 +383,10 @@ __global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
 
 // ------------------------------------------------------------------ variance, axis 1
 
-template <int E, int W, bool VEC, int LOADP, bool NT>
+template <int E, int W, bool VEC, int LOADP, bool NT, int V = V_KERNEL>
 __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
+  using F = VariantFlags<V>;
   constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
   __shared__ float lds[W * LPW];
   __shared__ Node slots[3][W];
@@ -319,19 +405,21 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   const bool full = base + 64 * E <= n;
   int64_t vl = n - base - (int64_t)lane * E;
   const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
-  if (full) {
+  if constexpr (F::shift) {
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
-  } else {
+      for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+    } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+      for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+    }
   }
 
   // step 2: m = Tree(y) / n
   Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
   ny = sv::wave_tree<false>(ny);
   ny = block_tree<W, false>(ny, slots[0], w, lane);
-  const float m = sv::root_value(ny) / (float)n;
+  const float m = local_mean<V>(ny, n);
 
   // step 3: Tree(d), Tree(d^2)
   Node nd, nq;
@@ -343,7 +431,10 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   nq = block_tree<W, true>(nq, slots[2], w, lane);
 
   // step 4
-  if (threadIdx.x == 0) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+  if (threadIdx.x == 0) {
+    if constexpr (V == V_KERNEL) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+    else finalize_v<V>(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+  }
 }
 
 // Axis 1, n <= 64*E: each wave owns R consecutive rows (one lane holds E
@@ -494,9 +585,10 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_dma(const float *__restrict
 
 // ------------------------------------------------------------------ variance, axis 0
 
-template <int E, int W>
+template <int E, int W, int V = V_KERNEL>
 __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
+  using F = VariantFlags<V>;
   __shared__ Node sy[W][64];
   __shared__ Node sd[W][64];
   __shared__ Node sq[W][64];
@@ -525,14 +617,17 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
     }
   }
   const float x0 = x[ccol];
+
   int64_t vl = R - r0;
   const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
-  if (full) {
+  if constexpr (F::shift) {
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
-  } else {
+      for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+    } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+      for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+    }
   }
 
   Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
@@ -544,7 +639,7 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
     for (int i = 0; i < W; ++i) nn[i] = sy[i][lane];
     ny = sv::node_tree<0, W, W>(nn);
   }
-  const float m = sv::root_value(ny) / (float)R;
+  const float m = local_mean<V>(ny, R);
 
   Node nd, nq;
   if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
@@ -566,7 +661,8 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
         a[k] = sv::combine(a[2 * k], a[2 * k + 1]);
         b[k] = sv::combine_nn(b[2 * k], b[2 * k + 1]);
       }
-    finalize(a[0], b[0], x0, m, R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+    if constexpr (V == V_KERNEL) finalize(a[0], b[0], x0, m, R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+    else finalize_v<V>(a[0], b[0], x0, m, R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
   }
 }
 
@@ -944,6 +1040,37 @@ void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *v
   k_var_cols<E, W><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
 }
 
+template <int V>
+void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t cols, int64_t ddof, float *var,
+                    float *mean, hipStream_t st) {
+  if (ax1) {
+    const int64_t n = cols;
+    const dim3 grid((unsigned)rows);
+#define SV_ROWS(E, W)                                                                                 \
+  do {                                                                                                \
+    if (vec) k_var_rows<E, W, true, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean); \
+    else k_var_rows<E, W, false, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean);   \
+  } while (0)
+    if (n <= 256) SV_ROWS(4, 1);
+    else if (n <= 1024) SV_ROWS(16, 1);
+    else if (n <= 4096) SV_ROWS(64, 1);
+    else SV_ROWS(64, 4);
+#undef SV_ROWS
+  } else {
+    const int64_t n = rows;
+    const dim3 grid((unsigned)((cols + 63) / 64));
+#define SV_COLS(E, W) k_var_cols<E, W, V><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var, mean)
+    if (n <= 4) SV_COLS(4, 1);
+    else if (n <= 16) SV_COLS(16, 1);
+    else if (n <= 64) SV_COLS(64, 1);
+    else if (n <= 128) SV_COLS(64, 2);
+    else if (n <= 256) SV_COLS(64, 4);
+    else if (n <= 512) SV_COLS(64, 8);
+    else SV_COLS(64, 16);
+#undef SV_COLS
+  }
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -1108,6 +1235,49 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     else launch_cols_ew<64, 16>(x, rows, cols, ddof, var_out, mean_out, st);
   }
   return check_launch("sv_variance_f32");
+}
+
+sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int variant,
+                                  float *var_out, float *mean_out, void *stream) {
+  if (rows < 0 || cols < 0)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: negative shape [%lld, %lld]", (long long)rows,
+                (long long)cols);
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: axis %d not in {0, 1, -1, -2}", axis);
+  if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: ddof = %lld < 0", (long long)ddof);
+  if (variant != V_KERNEL && variant != V_REFERENCE && variant != V_NAIVE && variant != V_SHIFT_PLAIN_NO2T &&
+      variant != V_SHIFT_PLAIN_2T && variant != V_NOSHIFT_COMP_2T && variant != V_SHIFT_COMP_NO2T)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: unknown variant %d", variant);
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t nslices = ax1 ? rows : cols;
+  const int64_t n = ax1 ? cols : rows;
+  if (nslices == 0) return ok();
+  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: var_out is NULL");
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: x is NULL");
+  if (nslices > 0x7fffffffLL || (ax1 ? n > ROWS_MAX_N : n > COLS_MAX_R))
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_variant_f32: shape [%lld, %lld] along axis %d not supported",
+                (long long)rows, (long long)cols, axis);
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (n == 0) {
+    const unsigned blocks = (unsigned)((nslices + 255) / 256);
+    k_fill<<<blocks, 256, 0, st>>>(var_out, nslices, __builtin_nanf(""));
+    if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
+    return check_launch("sv_variance_variant_f32");
+  }
+  const bool vec = aligned16(x) && (cols % 4 == 0);
+  switch (variant) {
+    case V_KERNEL: launch_variant<V_KERNEL>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_REFERENCE: launch_variant<V_REFERENCE>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_NAIVE: launch_variant<V_NAIVE>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_SHIFT_PLAIN_NO2T: launch_variant<V_SHIFT_PLAIN_NO2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_SHIFT_PLAIN_2T: launch_variant<V_SHIFT_PLAIN_2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_NOSHIFT_COMP_2T: launch_variant<V_NOSHIFT_COMP_2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    default: launch_variant<V_SHIFT_COMP_NO2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+  }
+  return check_launch("sv_variance_variant_f32");
 }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }

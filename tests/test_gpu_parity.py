@@ -373,3 +373,51 @@ def test_complex_then_sum_share_nothing(torch_dev):
     z = (np.random.default_rng(1).normal(0, 1, (3, 30000)) * (1 + 1j)).astype(np.complex64)
     check_var_c64(torch_dev, z, 1)
     assert same_bits(gpu_sum(torch_dev, x), want)
+
+
+# ------------------------------------------------------------------ ablation variants
+
+GPU_VARIANTS = {"kernel": 0, "reference": 2, "naive": 3, "shift_plain_no2t": 4, "shift_plain_2t": 5,
+                "noshift_comp_2t": 6, "shift_comp_no2t": 7}
+
+
+def same_bits_or_zero(a, b):
+    # the plain trees of unshifted data may differ in the sign of an exact
+    # zero (a larger zero padding turns -0 into +0); everything else is exact
+    a = np.asarray(a, np.float32).ravel()
+    b = np.asarray(b, np.float32).ravel()
+    both_zero = (a == 0) & (b == 0)
+    nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(nan | both_zero | (a.view(np.uint32) == b.view(np.uint32))))
+
+
+@pytest.mark.parametrize("name", list(GPU_VARIANTS))
+def test_variants_against_oracle(torch_dev, name):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    code = GPU_VARIANTS[name]
+    cases = [(a, ax) for _, a, ax, _ in W.datasets_d1_d4()]
+    rng = np.random.default_rng(code)
+    cases += [(rng.normal(1e4, 1, (9, 4096)).astype(np.float32), 1), (rng.normal(0, 3, (5, 10000)).astype(np.float32), 1),
+              (rng.normal(-5, 1, (700, 70)).astype(np.float32), 0), (W.adversarial_values(6 * 300, code).reshape(6, 300), 1),
+              (np.full((1, 3), np.float32(1e38)), 1), (W.constant(1e30), 0)]
+    for a, ax in cases:
+        for ddof in (0, 1):
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            v, m = sv.var_variant(t, code, dim=ax, ddof=ddof, return_mean=True)
+            torch.cuda.synchronize()
+            ov, om = oracle.variance(a, axis=ax, ddof=ddof, method=code)
+            assert same_bits_or_zero(v.cpu().numpy(), ov), (name, a.shape, ax, ddof)
+            assert same_bits_or_zero(m.cpu().numpy(), om), (name, a.shape, ax, ddof)
+
+
+def test_variant_zero_matches_the_main_entry_point(torch_dev):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    a = torch.from_numpy(W.c4_matrix()).to(dev)
+    v0 = sv.var_variant(a, "kernel", dim=1)
+    v1 = sv.var(a, dim=1)
+    torch.cuda.synchronize()
+    assert torch.equal(v0.view(torch.int32), v1.view(torch.int32))
