@@ -195,11 +195,17 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "sum_depth"      tree-sum chunks in flight per wave: 2 (default) or 4
  *   "sum_blocks"     target number of tree-sum workgroups, 1..8192 (default
  *                    8192); each wave then streams a power-of-two run of chunks
- *   "var_load_path"  row variance: as sum_load_path (default 1)
+ *   "var_load_path"  row variance: as sum_load_path (default 1), or 2 =
+ *                    coalesced loads transposed through LDS in four stages of
+ *                    16 lanes each (a quarter of the LDS of path 0)
  *   "var_nt"         row variance: as sum_nt (default 0)
  *   "var_rows_per_wave"  rows of 1025..4096 values one wave pipelines (the
  *                    next row's loads in flight while one is reduced): 1
  *                    (default), 2, 4 or 8
+ *   "var_dma_rows"   rows of 1025..4096 values per wave staged by direct
+ *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
+ *   "var_split"      waves sharing one row of 1025..4096 values: 1, 2
+ *                    (default), 4 or 8 (64, 32, 16 or 8 values per lane)
  *   "reset"          any value: restore every default
  * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  Not thread
  * safe with concurrent calls.

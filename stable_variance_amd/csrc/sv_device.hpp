@@ -181,8 +181,34 @@ __device__ __forceinline__ Node dpp_node(Node n) {
   return {dpp<CTRL>(n.s), dpp<CTRL>(n.c)};
 }
 
-__device__ __forceinline__ Node shfl_xor_node(Node n, int mask) {
-  return {__shfl_xor(n.s, mask, 64), __shfl_xor(n.c, mask, 64)};
+// Cross-row exchanges of gfx950 (one VALU instruction per register, no LDS):
+// v_permlane16_swap on two copies of x leaves, in every lane L, x[L] and
+// x[L ^ 16] in the two registers (one in each); v_permlane32_swap likewise
+// for x[L ^ 32].  Which register holds the lane's own value does not matter:
+// the node combine is symmetric bit for bit.  Written as inline assembly
+// because the compiler builtin's second result has been miscompiled (read as
+// a copy of the first) once the results feed arithmetic.  The wait states
+// around the instruction cover the VALU-write-then-permlane hazards.
+struct NodePair { Node a, b; };
+
+template <int XOR>
+__device__ __forceinline__ void swap_halves(float v, float &a, float &b) {
+  static_assert(XOR == 16 || XOR == 32, "lane distance 16 or 32");
+  unsigned x = __builtin_bit_cast(unsigned, v), y = x;
+  if constexpr (XOR == 16)
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  else
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+
+template <int XOR>
+__device__ __forceinline__ NodePair swap_node(Node n) {
+  NodePair p;
+  swap_halves<XOR>(n.s, p.a.s, p.b.s);
+  swap_halves<XOR>(n.c, p.a.c, p.b.c);
+  return p;
 }
 
 // The six cross-lane levels: lane k's node covers lane range k; afterwards
@@ -196,9 +222,10 @@ __device__ __forceinline__ Node wave_tree(Node n) {
   n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
   n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
   n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
-  n = comb(n, shfl_xor_node(n, 16));
-  n = comb(n, shfl_xor_node(n, 32));
-  return n;
+  NodePair p = swap_node<16>(n);
+  n = comb(p.a, p.b);
+  p = swap_node<32>(n);
+  return comb(p.a, p.b);
 }
 
 // The same six levels when lane L holds the range of virtual lane
@@ -210,8 +237,10 @@ __device__ __forceinline__ Node wave_tree(Node n) {
 template <bool NN>
 __device__ __forceinline__ Node wave_tree_vlane(Node n) {
   auto comb = [](Node a, Node b) { return NN ? combine_nn(a, b) : combine(a, b); };
-  n = comb(n, shfl_xor_node(n, 16));
-  n = comb(n, shfl_xor_node(n, 32));
+  NodePair p = swap_node<16>(n);
+  n = comb(p.a, p.b);
+  p = swap_node<32>(n);
+  n = comb(p.a, p.b);
   n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
   n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
   n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
@@ -234,6 +263,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // consecutive lanes share a bank.
 template <int E>
 constexpr int lds_floats_per_wave() { return 64 * (E + 4); }
+
+// LDS floats for the staged transpose (LOADP 2): one quarter of the lanes'
+// ranges at a time, each padded by 4 floats.
+template <int E>
+constexpr int lds_floats_staged() { return 16 * (E + 4); }
 
 // Values p[lane*E + i], i < E, of a 64*E tile starting at p; elements at or
 // beyond `len` read as 0 (len may be <= 0).
@@ -282,7 +316,39 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
     for (int i = 0; i < E; ++i) v[i] = 0.0f;
     return;
   }
-  if constexpr (LOADP == 1) {
+  if constexpr (LOADP == 2) {
+    // Staged transpose: coalesced 16-byte loads (instruction k covers values
+    // [256k, 256k + 256)), then four stages through a quarter-size LDS region:
+    // stage s holds the ranges of lanes 16s..16s+15, which read them back.
+    static_assert(E % 16 == 0, "staged transpose needs E multiple of 16");
+    constexpr int KS = J / 4;  // load instructions per stage
+    if (full && VEC) {
+      float4 g[J];
+#pragma unroll
+      for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + 256 * k + 4 * lane);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          const int e = 256 * (st * KS + j) + 4 * lane;  // value index in the tile
+          const int r = e / E - 16 * st;                 // reader lane within the stage
+          *reinterpret_cast<float4 *>(lds + r * STR + (e % E)) = g[st * KS + j];
+        }
+        wave_lds_sync();
+        if (lane / 16 == st) {
+#pragma unroll
+          for (int j = 0; j < J; ++j) {
+            const float4 t = *reinterpret_cast<const float4 *>(lds + (lane - 16 * st) * STR + 4 * j);
+            v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+          }
+        }
+        wave_lds_sync();
+      }
+      return;
+    }
+    // other cases: per-lane loads as LOADP 1
+  }
+  if constexpr (LOADP == 1 || LOADP == 2) {
     const int e0 = lane * E;
     if (full) {
 #pragma unroll

@@ -387,7 +387,7 @@ template <int E, int W, bool VEC, int LOADP, bool NT, int V = V_KERNEL>
 __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
   using F = VariantFlags<V>;
-  constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
+  constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : (LOADP == 2) ? sv::lds_floats_staged<E>() : 1;
   __shared__ float lds[W * LPW];
   __shared__ Node slots[3][W];
 
@@ -881,6 +881,7 @@ struct Tuning {
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
   int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
+  int var_split = 2;          // waves sharing one row (1, 2, 4, 8) for 1024 < n <= 4096
   int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
 };
 Tuning g_tune;
@@ -994,10 +995,25 @@ void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t 
   k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), 0, st>>>(x, n, ld, ddof, var, mean);
 }
 
+// A row shared by W waves of E values per lane: per-lane loads only.
+template <int E, int W>
+void launch_rows_split(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
+                       float *mean, hipStream_t st) {
+  if (vec) launch_rows_t<E, W, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+  else launch_rows_t<E, W, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+}
+
 template <int E, int W>
 void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                     float *mean, hipStream_t st) {
-  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
+  if constexpr (E % 16 == 0) {
+    if (g_tune.var_load_path == 2) {
+      if (vec) launch_rows_t<E, W, true, 2, false>(x, rows, n, ld, ddof, var, mean, st);
+      else launch_rows_t<E, W, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+      return;
+    }
+  }
+  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path != 0 ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
   switch (sel) {
     case 0: launch_rows_t<E, W, false, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
     case 1: launch_rows_t<E, W, false, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
@@ -1021,7 +1037,7 @@ void launch_pipe_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t 
 template <int R>
 void launch_pipe_r(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                    float *mean, hipStream_t st) {
-  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
+  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path != 0 ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
   switch (sel) {
     case 0: launch_pipe_t<R, false, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
     case 1: launch_pipe_t<R, false, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
@@ -1053,7 +1069,7 @@ void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t co
   } while (0)
     if (n <= 256) SV_ROWS(4, 1);
     else if (n <= 1024) SV_ROWS(16, 1);
-    else if (n <= 4096) SV_ROWS(64, 1);
+    else if (n <= 4096) SV_ROWS(32, 2);  // the default geometry of the main kernel
     else SV_ROWS(64, 4);
 #undef SV_ROWS
   } else {
@@ -1222,6 +1238,9 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
       if (R == 2) launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
       else if (R == 4) launch_pipe_r<4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
       else if (R == 8) launch_pipe_r<8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else if (g_tune.var_split == 2) launch_rows_split<32, 2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else if (g_tune.var_split == 4) launch_rows_split<16, 4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else if (g_tune.var_split == 8) launch_rows_split<8, 8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
       else launch_rows_ew<64, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     }
     else launch_rows_ew<64, 4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
@@ -1371,8 +1390,18 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
   };
   if (strcmp(key, "sum_load_path") == 0) return flag(&g_tune.sum_load_path);
   if (strcmp(key, "sum_nt") == 0) return flag(&g_tune.sum_nt);
-  if (strcmp(key, "var_load_path") == 0) return flag(&g_tune.var_load_path);
+  if (strcmp(key, "var_load_path") == 0) {
+    if (value < 0 || value > 2) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_load_path must be 0, 1 or 2");
+    g_tune.var_load_path = (int)value;
+    return ok();
+  }
   if (strcmp(key, "var_nt") == 0) return flag(&g_tune.var_nt);
+  if (strcmp(key, "var_split") == 0) {
+    if (value != 1 && value != 2 && value != 4 && value != 8)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_split must be 1, 2, 4 or 8");
+    g_tune.var_split = (int)value;
+    return ok();
+  }
   if (strcmp(key, "var_rows_per_wave") == 0) {
     if (value != 1 && value != 2 && value != 4 && value != 8)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_rows_per_wave must be 1, 2, 4 or 8");

@@ -119,7 +119,7 @@ def test_tuning_knob_validation(L):
     assert L.sv_set_tuning(b"sum_load_path", 2) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(b"nope", 0) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(None, 0) == SV_ERR_INVALID_ARGUMENT
-    for key, good, bad in ((b"sum_load_path", 1, 2), (b"sum_nt", 0, -1), (b"var_load_path", 0, 5),
+    for key, good, bad in ((b"sum_load_path", 1, 2), (b"sum_nt", 0, -1), (b"var_load_path", 2, 5),
                            (b"var_nt", 1, 2), (b"var_rows_per_wave", 4, 3), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0)):
         assert L.sv_set_tuning(key, good) == 0, key
         assert L.sv_set_tuning(key, bad) == SV_ERR_INVALID_ARGUMENT, key
