@@ -12,6 +12,8 @@ Contents
   * :func:`np_tree_sum` / :func:`np_tree_plain`: the same trees written as
     vectorised numpy float32 levels (a second implementation of the
     definition, used to cross-check the C code, not as a pin).
+  * :mod:`oracle.adn`: the Ahrens-Demmel-Nguyen binned reproducible sum of
+    the "SyclReproSum" README, as a closed form and as its float32 steps.
   * Exact truth: :func:`exact_sum` (integer arithmetic on the float32
     mantissas) and :func:`round_f32` (round-to-nearest-even of an exact
     dyadic value), :func:`var_f64` (float64 variance, the method page's
