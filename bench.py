@@ -46,11 +46,17 @@ SUM_BYTES = SUM_N * 4 + 4
 VAR_OPS_PER_ELEM = 23
 SUM_COUNTERS = os.path.join(ROOT, "profiles", "k_tree_sum_1e8_counters.txt")
 VAR_COUNTERS = os.path.join(ROOT, "profiles", "k_var_rows_4096x4096_counters.txt")
+ADN_COUNTERS = os.path.join(ROOT, "profiles", "k_adn_sum_1e8_counters.txt")
+ADN_FOLD = 3
+# float-sum throughput printed on the ADN page ("Scalar-sum throughput", GElements/s)
+ADN_PAGE_FLOAT_GELEMS = {"NVIDIA GB10": 55.4, "NVIDIA RTX PRO 4500 Blackwell": 135.1,
+                         "AMD Radeon Pro W7500": 16.0, "Intel Arc Pro B70": 54.2}
 
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for rel in ("stable_variance_amd/csrc/sv_lib.hip", "stable_variance_amd/csrc/sv_device.hpp"):
+    for rel in ("stable_variance_amd/csrc/sv_lib.hip", "stable_variance_amd/csrc/sv_adn.hip",
+                "stable_variance_amd/csrc/sv_device.hpp"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -260,6 +266,34 @@ def main():
     variants = {k: {"ms": round(v, 5), "ratio_to_reference": round(v / variant_ms["reference"], 3)}
                 for k, v in variant_ms.items()}
 
+    # second workload: the ADN binned reproducible sum of the same 10^8 values
+    adn_need = L.sv_adn_sum_f32_workspace_size(SUM_N)
+    adn_ws = torch.zeros(adn_need, dtype=torch.uint8, device=dev)
+    adn_out = torch.empty((), dtype=torch.float32, device=dev)
+    adn_ms = time_op(lambda i: check(L.sv_adn_sum_f32(c5[i % N_SUM_COPIES].data_ptr(), SUM_N, ADN_FOLD,
+                                                     adn_out.data_ptr(), adn_ws.data_ptr(), adn_need, sh)), reps=40)
+    adn_gbs = SUM_BYTES / (adn_ms * 1e-3) / 1e9
+    adn = {"kernel": f"k_adn_sum<{ADN_FOLD}, 16> (1e8 values)", "fold": ADN_FOLD, "avg_launch_ms": round(adn_ms, 5),
+           "gelem_s": round(SUM_N / (adn_ms * 1e-3) / 1e9, 2),
+           "hbm": {"achieved": round(adn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(adn_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": SUM_BYTES,
+                   "traffic": read_counter_traffic(ADN_COUNTERS), "read_ceiling_gbs": round(read_sum_gbs, 1),
+                   "frac_of_read_ceiling": round(adn_gbs / read_sum_gbs, 4)},
+           "over_tree_sum": round(adn_ms / sum_avg, 3),
+           "pages_float_sum_gelem_s": ADN_PAGE_FLOAT_GELEMS, "bit_exact": None, "cpu_oracle": None}
+    if not args.no_cpu_baseline:
+        from oracle import adn as oracle_adn
+
+        check(L.sv_adn_sum_f32(c5[0].data_ptr(), SUM_N, ADN_FOLD, adn_out.data_ptr(), adn_ws.data_ptr(), adn_need, sh))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        want = oracle_adn.adn_sum(c5_host, ADN_FOLD)
+        t_or = time.perf_counter() - t0
+        adn["bit_exact"] = bool(np.float32(adn_out.item()).view(np.uint32) == np.float32(want).view(np.uint32))
+        adn["cpu_oracle"] = {"value": round(SUM_N / t_or / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+                             "sample": f"the full 10^8 sum once, {t_or:.1f} s, numpy closed form (float64 steps, "
+                                       f"integer sums)"}
+
     elems = VAR_ROWS * VAR_COLS + SUM_N
     value = elems * K / wall / 1e9
     sum_gbs = SUM_BYTES / (sum_avg * 1e-3) / 1e9
@@ -309,6 +343,7 @@ def main():
                     "kernel_over_reference_formula": round(var_avg / variant_ms["reference"], 3),
                     "pages_kernel_over_reference": {"kaggle_cpu": 2.27, "kaggle_gpu": 2.19},
                     "ablation_4096x4096": variants},
+        "adn_sum": adn,
         "parity": parity,
     }
     if not args.no_cpu_baseline:

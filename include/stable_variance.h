@@ -175,6 +175,49 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
                                   float *var_out, float *mean_out, void *stream);
 
 /*
+ * Ahrens-Demmel-Nguyen binned reproducible sum of float32 values, as the
+ * "SyclReproSum" README describes it ("How It Works", "Accumulator capacity",
+ * "Template Parameters"): every value is deposited into `fold` (K) primary
+ * values on a fixed global grid of 13-bit exponent bins, plus K carry
+ * counts; primaries renormalise into carries every 512 deposits; partial
+ * accumulators merge exactly; the total is converted to float through a
+ * running double value.  The result has the same bits for any order of the
+ * values, any launch geometry and any run.
+ *
+ * Readings where the page is silent (the CPU oracle takes the same ones):
+ *   - bins b = 0..21 hold the weights 2^(13b - 146) .. 2^(13b - 134); the
+ *     folds are bins top, top-1, .., top-K+1, where top is the smallest bin
+ *     with |x| < 2^(13 top - 134) for every finite x, and at least K-1;
+ *   - each fold rounds what reaches it to its unit, to nearest with ties
+ *     away from zero (the sticky bit), and passes the exact rest on; the
+ *     rounding of the last fold is the only loss (at most
+ *     N * 2^(-13(K-1)) * max|x| in total, the page's dominant error term);
+ *   - the result is float(y), y the running double sum of the exact fold
+ *     values from the coarsest fold; an empty sum or a sum of zeros is +0;
+ *   - any NaN, or +Inf together with -Inf, gives 0x7fc00000; otherwise a
+ *     single-signed Inf gives that Inf (both from the page); a finite total
+ *     beyond the float range gives +-Inf.
+ *
+ * x: n device floats (any alignment; 16-byte alignment takes vector loads).
+ * fold: 2 .. SV_ADN_MAX_FOLD (the page allows up to 21: 9..21 return
+ *   SV_ERR_UNSUPPORTED here; outside 2..21 SV_ERR_INVALID_ARGUMENT).
+ * n: 0 .. SV_ADN_MAX_COUNT (the page's capacity for float; above it
+ *   SV_ERR_UNSUPPORTED before anything else is touched).
+ * out: one device float.
+ * workspace: device memory of sv_adn_sum_f32_workspace_size(n) bytes (0 for
+ *   n == 0), 256-byte aligned; its first SV_ADN_SUM_COUNTER_BYTES bytes are
+ *   ticket counters that must be zero before the first use and that every
+ *   call leaves zero; calls sharing a workspace must be ordered on one
+ *   stream.  Errors and asynchrony as for sv_tree_sum_f32.
+ */
+#define SV_ADN_MAX_FOLD 8
+#define SV_ADN_MAX_COUNT 4294966784LL
+#define SV_ADN_SUM_COUNTER_BYTES 33024
+size_t sv_adn_sum_f32_workspace_size(int64_t n);
+sv_status sv_adn_sum_f32(const float *x, int64_t n, int fold, float *out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
  * Measurement aid, not part of the method: reads x[0 .. n) once from HBM with
  * plain non-temporal 16-byte loads (x 16-byte aligned, n <= 2^36) and does no
  * arithmetic of the method, so its duration is the practical read ceiling
@@ -206,6 +249,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
  *   "var_split"      waves sharing one row of 1025..4096 values: 1, 2
  *                    (default), 4 or 8 (64, 32, 16 or 8 values per lane)
+ *   "adn_e"          values per lane in an ADN-sum chunk: 16 (default) or 32
+ *                    (32 only with three folds; other counts use 16)
+ *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)
  *   "reset"          any value: restore every default
  * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  Not thread
  * safe with concurrent calls.

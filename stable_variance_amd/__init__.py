@@ -76,6 +76,10 @@ def capi():
                 L.sv_variance_c64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_variance_variant_f32.restype = ctypes.c_int
                 L.sv_variance_variant_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
+                L.sv_adn_sum_f32_workspace_size.restype = sz
+                L.sv_adn_sum_f32_workspace_size.argtypes = [i64]
+                L.sv_adn_sum_f32.restype = ctypes.c_int
+                L.sv_adn_sum_f32.argtypes = [vp, i64, ctypes.c_int, vp, vp, sz, vp]
                 L.sv_probe_read_bandwidth.restype = ctypes.c_int
                 L.sv_probe_read_bandwidth.argtypes = [vp, i64, vp, vp]
                 _lib = L
@@ -142,6 +146,27 @@ def tree_sum(x):
         ws = _workspace("sum", need, x.device, stream)
         _check(L.sv_tree_sum_f32(x.data_ptr() if n else None, n, out.data_ptr(),
                                  ws.data_ptr() if ws is not None else None, need, stream))
+    return out
+
+
+def adn_sum(x, fold: int = 3):
+    """Ahrens-Demmel-Nguyen binned reproducible sum of all elements of a
+    float32 tensor, with ``fold`` bins (same bits for any order)."""
+    import torch
+
+    _check_tensor(x)
+    x = x.contiguous().reshape(-1)
+    n = x.numel()
+    L = capi()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        out = torch.empty((), dtype=torch.float32, device=x.device)
+        need = L.sv_adn_sum_f32_workspace_size(n)
+        if need == ctypes.c_size_t(-1).value:
+            raise SvError(5, f"adn_sum: n = {n} exceeds the accumulator capacity")
+        ws = _workspace("adn", need, x.device, stream)
+        _check(L.sv_adn_sum_f32(x.data_ptr() if n else None, n, int(fold), out.data_ptr(),
+                                ws.data_ptr() if ws is not None else None, need, stream))
     return out
 
 

@@ -7,7 +7,9 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "sv_lib.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "sv_device.hpp"), os.path.join(ROOT, "include", "stable_variance.h")]
+SRCS = [SRC, os.path.join(HERE, "csrc", "sv_adn.hip")]
+DEPS = SRCS + [os.path.join(HERE, "csrc", "sv_device.hpp"), os.path.join(HERE, "csrc", "sv_host.hpp"),
+               os.path.join(ROOT, "include", "stable_variance.h")]
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libstable_variance.so")
 
@@ -29,16 +31,34 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the HIP library; returns the path of the shared object."""
+    """Compile the HIP sources (in parallel) and link the shared object; returns its path."""
     os.makedirs(OUT_DIR, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src in SRCS:
+        obj = os.path.join(OUT_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
+        cmd = [hipcc(), *flags, "-c", src, "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    errors = []
+    for cmd, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            errors.append(" ".join(cmd) + "\n" + out + err)
+        elif verbose:
+            print(" ".join(cmd))
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, SRC, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+        raise RuntimeError("link failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
     os.replace(tmp, LIB)
+    for obj in objs:
+        os.remove(obj)
     return LIB
 
 

@@ -248,6 +248,23 @@ __device__ __forceinline__ Node wave_tree_vlane(Node n) {
   return n;
 }
 
+// ---------------------------------------------------------------- device-coherent words
+
+// Relaxed agent-scope (device-coherent) 32-bit store and load: they bypass
+// the non-coherent caches, so a value published by one workgroup is seen by
+// another without a cache writeback or invalidation.
+__device__ __forceinline__ void store_u32_agent(unsigned *dst, unsigned v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned load_u32_agent(const unsigned *src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt vmcnt(0): every vector memory operation of this wave, including
+// the device-coherent stores above, has completed.
+__device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------- loads
 
 // Wave-scope ordering of LDS traffic between the lanes of one wave.

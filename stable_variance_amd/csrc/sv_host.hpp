@@ -1,0 +1,30 @@
+// Host helpers shared by the library's translation units: status reporting
+// for the C ABI (one thread-local message per host thread) and argument
+// checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/stable_variance.h"
+
+namespace svh {
+
+// Records a printf-style message for sv_last_error_message and returns st.
+__attribute__((visibility("hidden"))) sv_status fail(sv_status st, const char *fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+// Clears the message and returns SV_OK.
+__attribute__((visibility("hidden"))) sv_status ok();
+// SV_ERR_NO_DEVICE unless a HIP device is visible.
+__attribute__((visibility("hidden"))) sv_status check_device();
+// SV_ERR_HIP if the last launch on this host thread failed, else ok().
+__attribute__((visibility("hidden"))) sv_status check_launch(const char *what);
+__attribute__((visibility("hidden"))) const char *last_error();
+// Tuning keys of the ADN sum ("reset" restores them); *handled is false for
+// a key it does not know.
+__attribute__((visibility("hidden"))) sv_status adn_set_tuning(const char *key, int64_t value, bool *handled);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+}  // namespace svh

@@ -27,8 +27,51 @@
 
 #include "../../include/stable_variance.h"
 #include "sv_device.hpp"
+#include "sv_host.hpp"
 
 using sv::Node;
+
+// ------------------------------------------------------------------ shared host helpers
+
+namespace svh {
+
+thread_local char g_err[512];
+
+sv_status fail(sv_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sv_status ok() {
+  g_err[0] = 0;
+  return SV_OK;
+}
+
+sv_status check_device() {
+  int cnt = 0;
+  const hipError_t e = hipGetDeviceCount(&cnt);
+  if (e != hipSuccess || cnt <= 0) return fail(SV_ERR_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
+  return SV_OK;
+}
+
+sv_status check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+const char *last_error() { return g_err; }
+
+}  // namespace svh
+
+using svh::check_device;
+using svh::check_launch;
+using svh::fail;
+using svh::ok;
+using svh::aligned16;
 
 namespace {
 
@@ -171,21 +214,15 @@ __device__ __forceinline__ void finalize(Node nd, Node nq, float x0, float m, in
 }
 
 __device__ __forceinline__ void store_node_agent(Node *dst, Node v) {
-  __hip_atomic_store(reinterpret_cast<unsigned *>(&dst->s), __builtin_bit_cast(unsigned, v.s), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(reinterpret_cast<unsigned *>(&dst->c), __builtin_bit_cast(unsigned, v.c), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  sv::store_u32_agent(reinterpret_cast<unsigned *>(&dst->s), __builtin_bit_cast(unsigned, v.s));
+  sv::store_u32_agent(reinterpret_cast<unsigned *>(&dst->c), __builtin_bit_cast(unsigned, v.c));
 }
 
-// s_waitcnt vmcnt(0): every vector memory operation of this wave, including
-// the device-coherent stores above, has completed.
-__device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+using sv::wait_vmem_stores;
 
 __device__ __forceinline__ Node load_node_agent(const Node *src) {
-  const unsigned s = __hip_atomic_load(reinterpret_cast<const unsigned *>(&src->s), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned c = __hip_atomic_load(reinterpret_cast<const unsigned *>(&src->c), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned s = sv::load_u32_agent(reinterpret_cast<const unsigned *>(&src->s));
+  const unsigned c = sv::load_u32_agent(reinterpret_cast<const unsigned *>(&src->c));
   return {__builtin_bit_cast(float, s), __builtin_bit_cast(float, c)};
 }
 
@@ -870,7 +907,6 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
 
 // ------------------------------------------------------------------ host side
 
-thread_local char g_err[512];
 // Launch-geometry tuning (never changes a result bit).
 struct Tuning {
   int sum_load_path = 0;      // 0: coalesced loads + LDS transpose, 1: per-lane contiguous loads
@@ -885,34 +921,6 @@ struct Tuning {
   int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
 };
 Tuning g_tune;
-
-sv_status fail(sv_status st, const char *fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof g_err, fmt, ap);
-  va_end(ap);
-  return st;
-}
-
-sv_status ok() {
-  g_err[0] = 0;
-  return SV_OK;
-}
-
-sv_status check_device() {
-  int cnt = 0;
-  const hipError_t e = hipGetDeviceCount(&cnt);
-  if (e != hipSuccess || cnt <= 0) return fail(SV_ERR_NO_DEVICE, "no HIP device available (%s)", hipGetErrorString(e));
-  return SV_OK;
-}
-
-sv_status check_launch(const char *what) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
-  return ok();
-}
-
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int ceil_log2(int64_t v) {
   int l = 0;
@@ -1107,7 +1115,7 @@ const char *sv_status_string(sv_status s) {
   }
 }
 
-const char *sv_last_error_message(void) { return g_err; }
+const char *sv_last_error_message(void) { return svh::last_error(); }
 
 size_t sv_tree_sum_f32_workspace_size(int64_t n) {
   if (n > SUM_MAX_N) return (size_t)-1;
@@ -1430,10 +1438,13 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     g_tune.sum_blocks = value;
     return ok();
   }
+  bool handled = false;
+  const sv_status adn = svh::adn_set_tuning(key, value, &handled);
   if (strcmp(key, "reset") == 0) {
     g_tune = Tuning{};
     return ok();
   }
+  if (handled) return adn;
   return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: unknown key '%s'", key);
 }
 

@@ -99,6 +99,33 @@ def test_variance_argument_errors(L):
     assert L.sv_variance_f32(BAD, 1, 8192 * 16384 + 1, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
+def test_adn_sizes_and_argument_errors(L):
+    # counters (33024 bytes), then an 80-byte record per workgroup (up to
+    # 8192) and per group of 64 workgroups
+    want = 33024 + 80 * (8192 + 128)
+    assert L.sv_adn_sum_f32_workspace_size(0) == 0
+    for n in (1, 4097, 10 ** 8, 4_294_966_784):
+        assert L.sv_adn_sum_f32_workspace_size(n) == want
+    assert L.sv_adn_sum_f32_workspace_size(4_294_966_785) == ctypes.c_size_t(-1).value
+    assert L.sv_adn_sum_f32_workspace_size(-1) == ctypes.c_size_t(-1).value
+    ws = ctypes.c_void_p(0x100000)
+    assert L.sv_adn_sum_f32(BAD, -1, 3, BAD, ws, want, None) == SV_ERR_INVALID_ARGUMENT
+    for fold in (0, 1, 22):
+        assert L.sv_adn_sum_f32(BAD, 10, fold, BAD, ws, want, None) == SV_ERR_INVALID_ARGUMENT
+    for fold in (9, 21):
+        assert L.sv_adn_sum_f32(BAD, 10, fold, BAD, ws, want, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_adn_sum_f32(BAD, 4_294_966_785, 3, BAD, ws, want, None) == SV_ERR_UNSUPPORTED
+    assert b"capacity" in L.sv_last_error_message()
+    assert L.sv_adn_sum_f32(BAD, 10, 3, None, ws, want, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_adn_sum_f32(None, 10, 3, BAD, ws, want, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_adn_sum_f32(BAD, 10, 3, BAD, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_adn_sum_f32(BAD, 10, 3, BAD, ws, want - 1, None) == SV_ERR_WORKSPACE
+    assert L.sv_adn_sum_f32(BAD, 10, 3, BAD, ctypes.c_void_p(0x100080), want, None) == SV_ERR_WORKSPACE
+    assert L.sv_set_tuning(b"adn_e", 16) == 0 and L.sv_set_tuning(b"adn_e", 8) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_set_tuning(b"adn_blocks", 1) == 0 and L.sv_set_tuning(b"adn_blocks", 8193) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_set_tuning(b"reset", 0) == 0
+
+
 def test_complex_argument_errors_and_sizes(L):
     out = ctypes.c_void_p(0x2000)
     # axis 0: per-component variances (2*cols floats) + the float view's own workspace (0 here)
@@ -135,6 +162,7 @@ def test_no_device_is_reported(L):
     ws = ctypes.c_void_p(0x100000)
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ws, 1 << 20, None) == SV_ERR_NO_DEVICE
     assert L.sv_variance_f32(BAD, 4, 4, 1, 0, BAD, None, None, 0, None) == SV_ERR_NO_DEVICE
+    assert L.sv_adn_sum_f32(BAD, 10, 3, BAD, ws, 1 << 20, None) == SV_ERR_NO_DEVICE
 
 
 def test_python_binding_rejects_bad_tensors():

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads as W
 from oracle import adn
 
 
@@ -24,17 +25,7 @@ def bits(v):
 
 
 def datasets(seed):
-    rng = np.random.default_rng(seed)
-    yield "normal", rng.standard_normal(700).astype(np.float32)
-    yield "wide", (rng.standard_normal(600) * np.exp2(rng.integers(-60, 60, 600))).astype(np.float32)
-    yield "cancel", np.concatenate([v := (rng.uniform(1e6, 1e8, 200)).astype(np.float32), -v,
-                                    rng.standard_normal(300).astype(np.float32)])
-    yield "subnormal", (rng.integers(-2000, 2000, 400) * np.float32(2.0 ** -149)).astype(np.float32)
-    yield "huge", (rng.standard_normal(300) * np.float32(3e37)).astype(np.float32)
-    yield "mixed_huge", np.concatenate([rng.standard_normal(200).astype(np.float32),
-                                        np.float32([2.0 ** 113, -2.0 ** 113, 3.3e38, 1.0e34])])
-    # halves of the first two folds' units (1024 and 2^-3 here): ties at both
-    yield "ties", (rng.integers(-40, 41, 500) * 512.0 + rng.integers(-64, 65, 500) * 2.0 ** -4).astype(np.float32)
+    return W.sum_mixed_sets(seed)
 
 
 @pytest.mark.parametrize("fold", [2, 3, 4, 6])

@@ -103,3 +103,22 @@ def adversarial_values(n: int, seed: int) -> np.ndarray:
     v[kinds == 1] = -0.0
     v[kinds == 2] = (sign[kinds == 2] * rng.uniform(1, 2, (kinds == 2).sum()) * 2.0 ** -140).astype(np.float32)
     return v
+
+
+def sum_mixed_sets(seed: int, scale: int = 1):
+    """Named float32 vectors for order-independent sums: normal, wide exponent
+    range, cancelling pairs, subnormal, huge (up to 3.3e38, including values
+    at or above 2^113) and values on the halves of power-of-two units (ties).
+    ``scale`` multiplies every length."""
+    rng = np.random.default_rng(seed)
+    s = scale
+    yield "normal", rng.standard_normal(700 * s).astype(np.float32)
+    yield "wide", (rng.standard_normal(600 * s) * np.exp2(rng.integers(-60, 60, 600 * s))).astype(np.float32)
+    v = rng.uniform(1e6, 1e8, 200 * s).astype(np.float32)
+    yield "cancel", np.concatenate([v, -v, rng.standard_normal(300 * s).astype(np.float32)])
+    yield "subnormal", (rng.integers(-2000, 2000, 400 * s) * np.float32(2.0 ** -149)).astype(np.float32)
+    yield "huge", (rng.standard_normal(300 * s) * np.float32(3e37)).astype(np.float32)
+    yield "mixed_huge", np.concatenate([rng.standard_normal(200 * s).astype(np.float32),
+                                        np.float32([2.0 ** 113, -2.0 ** 113, 3.3e38, 1.0e34])])
+    yield "ties", (rng.integers(-40, 41, 500 * s) * 512.0
+                   + rng.integers(-64, 65, 500 * s) * 2.0 ** -4).astype(np.float32)
