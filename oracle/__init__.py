@@ -54,6 +54,7 @@ METHOD_SHIFT_PLAIN_2T = 5        # shift + centring + two-term, plain tree
 METHOD_NOSHIFT_COMP_2T = 6       # no shift, two-term, compensated tree
 METHOD_SHIFT_COMP_NO2T = 7       # shift + centring, compensated tree, no two-term
 METHOD_SHIFT_KAHAN_NO2T = 8      # shift + centring, sequential Kahan scan, no two-term
+METHOD_KERNEL_DW = 9             # the method with double-word carries in all three trees
 
 _lib = None
 
@@ -78,7 +79,7 @@ def lib():
         i64 = ctypes.c_int64
         L.orc_two_sum.restype = ctypes.c_float
         L.orc_two_sum.argtypes = [ctypes.c_float, ctypes.c_float, fp]
-        for name in ("orc_tree_sum_f32", "orc_tree_plain_f32"):
+        for name in ("orc_tree_sum_f32", "orc_tree_plain_f32", "orc_tree_sum_dw_f32"):
             f = getattr(L, name)
             f.restype = ctypes.c_float
             f.argtypes = [fp, i64, i64, i64]
@@ -116,6 +117,13 @@ def tree_sum(x, pad_to: int = 0) -> np.float32:
     """Compensated pairwise tree sum ([VAR] §2 step 3) of a 1-D float32 array."""
     a = _f32c(x).ravel()
     return np.float32(lib().orc_tree_sum_f32(_ptr(a), a.size, 1, int(pad_to)))
+
+
+def tree_sum_dw(x, pad_to: int = 0) -> np.float32:
+    """Compensated tree with double-word carries: each node's pair is
+    renormalised with TwoSum (see ``orc_tree_sum_dw_f32``)."""
+    a = _f32c(x).ravel()
+    return np.float32(lib().orc_tree_sum_dw_f32(_ptr(a), a.size, 1, int(pad_to)))
 
 
 def tree_plain(x, pad_to: int = 0) -> np.float32:
@@ -197,6 +205,32 @@ def np_tree_sum(x, pad_to: int = 0) -> np.ndarray:
             e = (l - av) + (r - bv)
             c = (c[..., 0::2] + c[..., 1::2]) + e
             s = t
+        s, c = s[..., 0], c[..., 0]
+        return np.where(np.isfinite(s), s + c, s).astype(np.float32)
+
+
+def np_tree_sum_dw(x, pad_to: int = 0) -> np.ndarray:
+    """Double-word-carry tree along the last axis, vectorised levels."""
+    a = np.asarray(x, dtype=np.float32)
+    if a.shape[-1] == 0:
+        return np.zeros(a.shape[:-1], np.float32)
+    s = _pad_pow2(a, pad_to)
+    c = np.zeros_like(s)
+    with np.errstate(invalid="ignore", over="ignore"):
+        while s.shape[-1] > 1:
+            l, r = s[..., 0::2], s[..., 1::2]
+            t = l + r
+            bv = t - l
+            av = t - bv
+            e = (l - av) + (r - bv)
+            u = (c[..., 0::2] + c[..., 1::2]) + e
+            s2 = t + u                     # renormalise (t, u) with TwoSum ...
+            bv = s2 - t
+            av = s2 - bv
+            c2 = (t - av) + (u - bv)
+            fin = np.isfinite(t)           # ... unless the sum is Inf or NaN
+            s = np.where(fin, s2, t).astype(np.float32)
+            c = np.where(fin, c2, u).astype(np.float32)
         s, c = s[..., 0], c[..., 0]
         return np.where(np.isfinite(s), s + c, s).astype(np.float32)
 

@@ -105,6 +105,54 @@ float orc_tree_sum_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to
     return root_s + root_c;
 }
 
+/*
+ * Double-word carries: the same topology and the same node, followed by a
+ * renormalisation of the pair with TwoSum, (s, c) <- TwoSum(s', c') with
+ * s' = fl(s_2k + s_2k+1) and c' = fl(fl(c_2k + c_2k+1) + e_k).  The pair
+ * then stays a normalised double-word (|c| <= ulp(s)/2), so the carry is
+ * rounded relative to ulp(s) at every node instead of growing unchecked.
+ * READING ([ORD] points to wider or expansion-based accumulators for
+ * stronger guarantees; this is the double-word form of the method's own
+ * node): leaves are nodes of two values with zero carries, the result is
+ * fl(s_0 + c_0) with the same root guard as the compensated tree, and a
+ * node whose sum is Inf or NaN is not renormalised (fl(Inf + NaN) would turn
+ * an Inf into NaN), so Inf and NaN behave as in the compensated tree.
+ */
+float orc_tree_sum_dw_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to) {
+    if (n <= 0) return 0.0f;
+    int64_t P = pow2_ceil(n);
+    if (pad_to != 0) {
+        if (pad_to < P || (pad_to & (pad_to - 1)) != 0) return NAN;
+        P = pad_to;
+    }
+    float *s = (float *)malloc((size_t)P * sizeof(float));
+    float *c = (float *)malloc((size_t)P * sizeof(float));
+    if (!s || !c) { free(s); free(c); return NAN; }
+    for (int64_t i = 0; i < P; ++i) {
+        s[i] = (i < n) ? x[i * stride] : 0.0f;
+        c[i] = 0.0f;
+    }
+    for (int64_t len = P; len > 1; len >>= 1) {
+        for (int64_t k = 0; k < len / 2; ++k) {
+            float e, r;
+            float sk = two_sum(s[2 * k], s[2 * k + 1], &e);
+            float ck = (c[2 * k] + c[2 * k + 1]) + e;
+            if (isfinite(sk)) {
+                s[k] = two_sum(sk, ck, &r);
+                c[k] = r;
+            } else {           /* keep Inf (or NaN) in s: the root guard returns it */
+                s[k] = sk;
+                c[k] = ck;
+            }
+        }
+    }
+    float root_s = s[0], root_c = c[0];
+    free(s);
+    free(c);
+    if (!isfinite(root_s)) return root_s;
+    return root_s + root_c;
+}
+
 /* Same topology without the error array: the plain pairwise tree. */
 float orc_tree_plain_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to) {
     if (n <= 0) return 0.0f;
@@ -227,7 +275,8 @@ static void var_kernel_slice(const float *x, int64_t n, int64_t stride, int64_t 
  * Ablation variants of [VAR] §4, one step changed at a time.  Flags:
  *   shift    y = x - x0 (else y = x and mean = m)
  *   sum_kind 0 plain tree, 1 compensated tree, 2 sequential Kahan scan
- *            (the Kahan form of [KAHAN]) for every sum of the slice
+ *            (the Kahan form of [KAHAN]), 3 compensated tree with
+ *            double-word carries, for every sum of the slice
  *   twoterm  v = max(S2/n - (S1/n)^2, 0) (else v = max(S2/n, 0))
  * READING: "no two-term" is v = max(S2/n, 0); the Kahan-scan row of the
  * table ("shift + centring, Kahan sequential scan") has no two-term step,
@@ -236,6 +285,7 @@ static void var_kernel_slice(const float *x, int64_t n, int64_t stride, int64_t 
 static float slice_sum(const float *v, int64_t n, int sum_kind) {
     if (sum_kind == 0) return orc_tree_plain_f32(v, n, 1, 0);
     if (sum_kind == 1) return orc_tree_sum_f32(v, n, 1, 0);
+    if (sum_kind == 3) return orc_tree_sum_dw_f32(v, n, 1, 0);
     return orc_seq_kahan_f32(v, n);
 }
 
@@ -329,11 +379,12 @@ static void var_naive_slice(const float *x, int64_t n, int64_t stride, int64_t d
  *   6 no shift, two-term, compensated tree
  *   7 shift + centring, compensated tree, no two-term
  *   8 shift + centring, sequential Kahan scan, no two-term
+ *   9 the method with double-word carries in all three trees
  * mean may be NULL.  Returns 0, or -1 on bad arguments.
  */
 int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
                      int method, float *var, float *mean) {
-    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || method < 0 || method > 8)
+    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || method < 0 || method > 9)
         return -1;
     int64_t nslices = axis == 1 ? rows : cols;
     int64_t n = axis == 1 ? cols : rows;
@@ -354,7 +405,8 @@ int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64
         case 5: var_variant_slice(xs, n, stride, ddof, 1, 0, 1, buf, &v, &mu); break;
         case 6: var_variant_slice(xs, n, stride, ddof, 0, 1, 1, buf, &v, &mu); break;
         case 7: var_variant_slice(xs, n, stride, ddof, 1, 1, 0, buf, &v, &mu); break;
-        default: var_variant_slice(xs, n, stride, ddof, 1, 2, 0, buf, &v, &mu); break;
+        case 8: var_variant_slice(xs, n, stride, ddof, 1, 2, 0, buf, &v, &mu); break;
+        default: var_variant_slice(xs, n, stride, ddof, 1, 3, 1, buf, &v, &mu); break;
         }
         var[s] = v;
         if (mean) mean[s] = mu;
