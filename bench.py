@@ -294,6 +294,32 @@ def main():
                              "sample": f"the full 10^8 sum once, {t_or:.1f} s, numpy closed form (float64 steps, "
                                        f"integer sums)"}
 
+    # carry variant: the same tree with double-word (renormalised) carries
+    dw_ms = time_op(lambda i: check(L.sv_tree_sum_dw_f32(c5[i % N_SUM_COPIES].data_ptr(), SUM_N,
+                                                        sum_out.data_ptr(), ws.data_ptr(), ws_bytes, sh)), reps=40)
+    dw_gbs = SUM_BYTES / (dw_ms * 1e-3) / 1e9
+    dw = {"kernel": "k_tree_sum<32, ..., NODE_DW> (1e8 values)", "avg_launch_ms": round(dw_ms, 5),
+          "gelem_s": round(SUM_N / (dw_ms * 1e-3) / 1e9, 2),
+          "hbm": {"achieved": round(dw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(dw_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": SUM_BYTES,
+                  "frac_of_read_ceiling": round(dw_gbs / read_sum_gbs, 4)},
+          "over_tree_sum": round(dw_ms / sum_avg, 3), "bit_exact": None, "accuracy": None, "cpu_oracle": None}
+    if not args.no_cpu_baseline:
+        check(L.sv_tree_sum_dw_f32(c5[0].data_ptr(), SUM_N, sum_out.data_ptr(), ws.data_ptr(), ws_bytes, sh))
+        torch.cuda.synchronize()
+        got_dw = np.float32(sum_out.item())
+        t0 = time.perf_counter()
+        want_dw = oracle.tree_sum_dw(c5_host)
+        t_dw = time.perf_counter() - t0
+        exact = oracle.exact_sum(c5_host)
+        dw["bit_exact"] = bool(got_dw.view(np.uint32) == np.float32(want_dw).view(np.uint32))
+        rel = lambda v: abs(float(v) - float(exact)) / abs(float(exact))
+        dw["accuracy"] = {"exact_sum": float(exact), "dw_value": float(got_dw), "dw_rel_err": rel(got_dw),
+                          "plain_value": float(os_), "plain_rel_err": rel(os_),
+                          "dw_is_correctly_rounded": bool(got_dw == oracle.round_f32(exact))}
+        dw["cpu_oracle"] = {"value": round(SUM_N / t_dw / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
+                            "sample": f"the full 10^8 sum once, {t_dw:.2f} s, single-threaded C oracle"}
+
     elems = VAR_ROWS * VAR_COLS + SUM_N
     value = elems * K / wall / 1e9
     sum_gbs = SUM_BYTES / (sum_avg * 1e-3) / 1e9
@@ -343,6 +369,7 @@ def main():
                     "kernel_over_reference_formula": round(var_avg / variant_ms["reference"], 3),
                     "pages_kernel_over_reference": {"kaggle_cpu": 2.27, "kaggle_gpu": 2.19},
                     "ablation_4096x4096": variants},
+        "tree_sum_dw_carry": dw,
         "adn_sum": adn,
         "parity": parity,
     }

@@ -97,6 +97,23 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
                           size_t workspace_bytes, void *stream);
 
 /*
+ * The same tree with double-word carries: after every node the pair (s, c)
+ * is renormalised with TwoSum, so that |c| <= ulp(s)/2 and each carry
+ * addition is rounded relative to the node's own value.  Per node the added
+ * error is at most about 3 u^2 (|s_l| + |s_r|) (u = 2^-24) instead of growing
+ * with the depth, which matters when large partial sums cancel: on the 10^8
+ * cancelling-pairs workload the plain carry ends 3.9e-7 from the exact sum,
+ * this one at the correctly rounded value.  Arguments, workspace (the same
+ * size and counter rules as sv_tree_sum_f32), errors and asynchrony as for
+ * sv_tree_sum_f32.
+ * Source: "Reduction order and compensation solve related but different
+ * problems" (wider or expansion-based accumulators for stronger
+ * guarantees), applied to the method's own node.
+ */
+sv_status sv_tree_sum_dw_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
  * Bytes of workspace sv_variance_f32 needs: 0 when every slice fits one
  * workgroup (axis 1: n <= 16384 values; axis 0: n <= 1024 values), else
  * 24 bytes per 16384-value (axis 1) or 1024-value (axis 0) chunk of every

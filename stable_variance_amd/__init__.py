@@ -76,6 +76,8 @@ def capi():
                 L.sv_variance_c64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_variance_variant_f32.restype = ctypes.c_int
                 L.sv_variance_variant_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
+                L.sv_tree_sum_dw_f32.restype = ctypes.c_int
+                L.sv_tree_sum_dw_f32.argtypes = [vp, i64, vp, vp, sz, vp]
                 L.sv_adn_sum_f32_workspace_size.restype = sz
                 L.sv_adn_sum_f32_workspace_size.argtypes = [i64]
                 L.sv_adn_sum_f32.restype = ctypes.c_int
@@ -129,14 +131,20 @@ def _check_tensor(x, name="x", complex_ok=False):
         raise ValueError(f"{name} must be on a HIP device, got {x.device}")
 
 
-def tree_sum(x):
-    """Compensated pairwise tree sum of all elements of a float32 tensor."""
+def tree_sum(x, carry: str = "plain"):
+    """Compensated pairwise tree sum of all elements of a float32 tensor.
+
+    ``carry="dw"`` renormalises every node's (sum, carry) pair (double-word
+    carries, ``sv_tree_sum_dw_f32``)."""
     import torch
 
     _check_tensor(x)
+    if carry not in ("plain", "dw"):
+        raise ValueError(f"carry must be 'plain' or 'dw', got {carry!r}")
     x = x.contiguous().reshape(-1)
     n = x.numel()
     L = capi()
+    fn = L.sv_tree_sum_f32 if carry == "plain" else L.sv_tree_sum_dw_f32
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
         out = torch.empty((), dtype=torch.float32, device=x.device)
@@ -144,8 +152,8 @@ def tree_sum(x):
         if need == ctypes.c_size_t(-1).value:
             raise SvError(5, f"tree_sum: n = {n} is not supported")
         ws = _workspace("sum", need, x.device, stream)
-        _check(L.sv_tree_sum_f32(x.data_ptr() if n else None, n, out.data_ptr(),
-                                 ws.data_ptr() if ws is not None else None, need, stream))
+        _check(fn(x.data_ptr() if n else None, n, out.data_ptr(), ws.data_ptr() if ws is not None else None, need,
+                  stream))
     return out
 
 

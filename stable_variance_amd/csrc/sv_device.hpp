@@ -87,6 +87,35 @@ __device__ __forceinline__ Node leaf_nn(float a, float b) {
   return {s, lo - (s - hi)};
 }
 
+// Double-word node: the compensated node, then the pair renormalised with
+// TwoSum, (s, c) <- TwoSum(s, c), so that |c| <= ulp(s)/2 after every node.
+// The renormalisation of a pair that TwoSum produced returns it unchanged,
+// so zero padding still leaves the bits alone; TwoSum is symmetric in its
+// operands, so the node is too.  A pair whose sum is Inf or NaN stays as it
+// is (Inf + NaN would turn an Inf into NaN; the root guard returns s).
+__device__ __forceinline__ Node renorm_dw(Node n) {
+  const float s = n.s + n.c;
+  const float bv = s - n.s;
+  const float av = s - bv;
+  const float c = (n.s - av) + (n.c - bv);
+  const bool fin = __builtin_isfinite(n.s);
+  return {fin ? s : n.s, fin ? c : n.c};
+}
+
+__device__ __forceinline__ Node combine_dw(Node l, Node r) { return renorm_dw(combine(l, r)); }
+
+__device__ __forceinline__ Node leaf_dw(float a, float b) { return renorm_dw(leaf_canon(a, b)); }
+
+// Node kinds of the cross-lane and node-array trees.
+enum NodeKind { NODE_TWOSUM = 0, NODE_NN = 1, NODE_DW = 2 };
+
+template <int KIND>
+__device__ __forceinline__ Node combine_k(Node l, Node r) {
+  if constexpr (KIND == NODE_NN) return combine_nn(l, r);
+  else if constexpr (KIND == NODE_DW) return combine_dw(l, r);
+  else return combine(l, r);
+}
+
 // Value of a tree at its root: fl(s + c), or s when s is Inf or NaN.
 __device__ __forceinline__ float root_value(Node n) {
   return __builtin_isfinite(n.s) ? n.s + n.c : n.s;
@@ -96,7 +125,7 @@ __device__ __forceinline__ Node zero_node() { return {0.0f, 0.0f}; }
 
 // ---------------------------------------------------------------- in-lane trees
 
-enum LeafKind { LEAF_CANON = 0, LEAF_FAST = 1, LEAF_NN = 2 };
+enum LeafKind { LEAF_CANON = 0, LEAF_FAST = 1, LEAF_NN = 2, LEAF_DW = 3 };
 
 // Subtrees of at least this many values are scheduled one after the other
 // (a scheduling barrier between siblings): the compiler then interleaves
@@ -114,6 +143,7 @@ __device__ __forceinline__ Node lane_tree(const float (&v)[E]) {
   if constexpr (N == 2) {
     if constexpr (LEAF == LEAF_CANON) return leaf_canon(v[OFF], v[OFF + 1]);
     else if constexpr (LEAF == LEAF_FAST) return leaf_fast(v[OFF], v[OFF + 1]);
+    else if constexpr (LEAF == LEAF_DW) return leaf_dw(v[OFF], v[OFF + 1]);
     else return leaf_nn(v[OFF], v[OFF + 1]);
   } else {
     const Node l = lane_tree<LEAF, OFF, N / 2, E>(v);
@@ -121,17 +151,18 @@ __device__ __forceinline__ Node lane_tree(const float (&v)[E]) {
     const Node r = lane_tree<LEAF, OFF + N / 2, N / 2, E>(v);
     if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
     if constexpr (LEAF == LEAF_NN) return combine_nn(l, r);
+    else if constexpr (LEAF == LEAF_DW) return combine_dw(l, r);
     else return combine(l, r);
   }
 }
 
 // Tree over an array of nodes nd[OFF .. OFF+N).
-template <int OFF, int N, int K>
+template <int OFF, int N, int K, int KIND = NODE_TWOSUM>
 __device__ __forceinline__ Node node_tree(const Node (&nd)[K]) {
   if constexpr (N == 1) {
     return nd[OFF];
   } else {
-    return combine(node_tree<OFF, N / 2, K>(nd), node_tree<OFF + N / 2, N / 2, K>(nd));
+    return combine_k<KIND>(node_tree<OFF, N / 2, K, KIND>(nd), node_tree<OFF + N / 2, N / 2, K, KIND>(nd));
   }
 }
 
@@ -215,9 +246,9 @@ __device__ __forceinline__ NodePair swap_node(Node n) {
 // every lane holds the wave's node.  Level 1 pairs lanes (2k, 2k+1), level 2
 // pairs of pairs, and so on.  The mirror permutations reach the right sibling
 // because all lanes of the previous group already hold the same node.
-template <bool NN>
+template <int KIND>
 __device__ __forceinline__ Node wave_tree(Node n) {
-  auto comb = [](Node a, Node b) { return NN ? combine_nn(a, b) : combine(a, b); };
+  auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
   n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
   n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
   n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
@@ -234,9 +265,9 @@ __device__ __forceinline__ Node wave_tree(Node n) {
 // 0..3.  The first two levels need the exact partner (lane xor 16, xor 32);
 // after them the quad permutations are exact and the mirrors again reach the
 // sibling because the lower lanes already agree.
-template <bool NN>
+template <int KIND>
 __device__ __forceinline__ Node wave_tree_vlane(Node n) {
-  auto comb = [](Node a, Node b) { return NN ? combine_nn(a, b) : combine(a, b); };
+  auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
   NodePair p = swap_node<16>(n);
   n = comb(p.a, p.b);
   p = swap_node<32>(n);

@@ -246,7 +246,7 @@ constexpr size_t SUM_WS_HEADER = 256 * (1 + SUM_MAX_BLOCKS / SUM_GROUP);
 #ifndef SV_SUM_MINW
 #define SV_SUM_MINW 1
 #endif
-template <int E, int W, bool VEC, int LOADP, bool NT, int D>
+template <int E, int W, bool VEC, int LOADP, bool NT, int D, int KIND = sv::NODE_TWOSUM>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_MINW, 8))) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_g,
                                                      Node *__restrict__ part, unsigned *__restrict__ counter,
                                                      float *__restrict__ out) {
@@ -268,10 +268,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
   auto reduce_chunk = [&](const float (&raw)[E], int64_t j) {
     float v[E];
     C::finish(raw, my_lds, lane, v);
-    Node nd = sv::lane_tree<sv::LEAF_CANON, 0, E, E>(v);
-    nd = sv::wave_tree<false>(nd);
+    Node nd = sv::lane_tree<KIND == sv::NODE_DW ? sv::LEAF_DW : sv::LEAF_CANON, 0, E, E>(v);
+    nd = sv::wave_tree<KIND>(nd);
     if (lane == 0) {
-      for (int64_t k = j; k & 1; k >>= 1) nd = sv::combine(st[--sp], nd);
+      for (int64_t k = j; k & 1; k >>= 1) nd = sv::combine_k<KIND>(st[--sp], nd);
       st[sp++] = nd;
     }
   };
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
     Node nd[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nd[i] = slots[i];
-    store_node_agent(part + blockIdx.x, sv::node_tree<0, W, W>(nd));
+    store_node_agent(part + blockIdx.x, sv::node_tree<0, W, W, KIND>(nd));
     wait_vmem_stores();
     const unsigned ticket = __hip_atomic_fetch_add(grp_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (ticket == (unsigned)in_group - 1) ? 1u : 0u;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
   {
     const int idx = grp * SUM_GROUP + lane;
     Node g = (idx < nb) ? load_node_agent(part + idx) : sv::zero_node();
-    g = sv::wave_tree<false>(g);
+    g = sv::wave_tree<KIND>(g);
     unsigned top_ticket = 0;
     if (lane == 0) {
       __hip_atomic_store(grp_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
     const int idx = 2 * lane + k;
     t[k] = (idx < ngroups) ? load_node_agent(grp_nodes + idx) : sv::zero_node();
   }
-  Node r = sv::wave_tree<false>(sv::combine(t[0], t[1]));
+  Node r = sv::wave_tree<KIND>(sv::combine_k<KIND>(t[0], t[1]));
   if (lane == 0) {
     out[0] = sv::root_value(r);
     __hip_atomic_store(top_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
 
   // step 2: m = Tree(y) / n
   Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-  ny = sv::wave_tree<false>(ny);
+  ny = sv::wave_tree<sv::NODE_TWOSUM>(ny);
   ny = block_tree<W, false>(ny, slots[0], w, lane);
   const float m = local_mean<V>(ny, n);
 
@@ -462,8 +462,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   Node nd, nq;
   if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
   else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-  nd = sv::wave_tree<false>(nd);
-  nq = sv::wave_tree<true>(nq);
+  nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
+  nq = sv::wave_tree<sv::NODE_NN>(nq);
   nd = block_tree<W, false>(nd, slots[1], w, lane);
   nq = block_tree<W, true>(nq, slots[2], w, lane);
 
@@ -507,13 +507,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW, 8))) 
       for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
     }
     Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree<false>(ny);
+    ny = sv::wave_tree<sv::NODE_TWOSUM>(ny);
     const float m = sv::root_value(ny) / (float)n;
     Node nd, nq;
     if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
     else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = sv::wave_tree<false>(nd);
-    nq = sv::wave_tree<true>(nq);
+    nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
+    nq = sv::wave_tree<sv::NODE_NN>(nq);
     if (lane == 0) finalize(nd, nq, x0, m, n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
   };
   auto issue_row = [&](int64_t r, float (&v)[E]) { C::issue(x + r * ld, r < rows ? n : (int64_t)0, lane, v); };
@@ -609,13 +609,13 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_dma(const float *__restrict
       for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
     }
     Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree_vlane<false>(ny);
+    ny = sv::wave_tree_vlane<sv::NODE_TWOSUM>(ny);
     const float m = sv::root_value(ny) / (float)n;
     Node nd, nq;
     if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
     else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = sv::wave_tree_vlane<false>(nd);
-    nq = sv::wave_tree_vlane<true>(nq);
+    nd = sv::wave_tree_vlane<sv::NODE_TWOSUM>(nd);
+    nq = sv::wave_tree_vlane<sv::NODE_NN>(nq);
     if (lane == 0) finalize(nd, nq, x0, m, n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
   }
 }
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
   const int64_t out = r * nch + c;
   if constexpr (PASS == 0) {
     Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree<false>(ny);
+    ny = sv::wave_tree<sv::NODE_TWOSUM>(ny);
     ny = block_tree<W, false>(ny, slots[0], w, lane);
     if (threadIdx.x == 0) ws.ny[out] = ny;
   } else {
@@ -761,8 +761,8 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
     Node nd, nq;
     if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
     else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = sv::wave_tree<false>(nd);
-    nq = sv::wave_tree<true>(nq);
+    nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
+    nq = sv::wave_tree<sv::NODE_NN>(nq);
     nd = block_tree<W, false>(nd, slots[0], w, lane);
     nq = block_tree<W, true>(nq, slots[1], w, lane);
     if (threadIdx.x == 0) {
@@ -881,7 +881,7 @@ __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t
   } else {
     r = sv::node_tree<0, K / 8, K / 8>(sub);
   }
-  r = sv::wave_tree<NN>(r);
+  r = sv::wave_tree<NN ? sv::NODE_NN : sv::NODE_TWOSUM>(r);
   return block_tree<4, NN>(r, slots, w, lane);
 }
 
@@ -979,6 +979,16 @@ void launch_sum_t(const float *x, int64_t n, const SumPlan &p, Node *part, unsig
   const dim3 grid((unsigned)p.blocks), block(64 * SUM_W);
   if (g_tune.sum_depth == 4) k_tree_sum<E, SUM_W, VEC, LOADP, NT, 4><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
   else k_tree_sum<E, SUM_W, VEC, LOADP, NT, 2><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
+}
+
+// The double-word-carry sum in the default load configuration (coalesced
+// loads through LDS, non-temporal, two chunks in flight).
+template <int E>
+void launch_sum_dw(bool vec, const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
+                   hipStream_t st) {
+  const dim3 grid((unsigned)p.blocks), block(64 * SUM_W);
+  if (vec) k_tree_sum<E, SUM_W, true, 0, true, 2, sv::NODE_DW><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
+  else k_tree_sum<E, SUM_W, false, 0, true, 2, sv::NODE_DW><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
 }
 
 template <int E>
@@ -1122,19 +1132,19 @@ size_t sv_tree_sum_f32_workspace_size(int64_t n) {
   return sum_workspace_bytes(n);
 }
 
-sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
-                          void *stream) {
-  if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: n = %lld < 0", (long long)n);
-  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f32: n = %lld above 2^36", (long long)n);
-  if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: out is NULL");
-  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f32: x is NULL with n > 0");
+static sv_status tree_sum_impl(const char *who, bool dw, const float *x, int64_t n, float *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "%s: n = %lld < 0", who, (long long)n);
+  if (n > SUM_MAX_N) return fail(SV_ERR_UNSUPPORTED, "%s: n = %lld above 2^36", who, (long long)n);
+  if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "%s: out is NULL", who);
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "%s: x is NULL with n > 0", who);
   const size_t need = sum_workspace_bytes(n);
   if (need > 0) {
-    if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f32: workspace is NULL (%zu bytes needed)", need);
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", who, need);
     if (workspace_bytes < need)
-      return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f32: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+      return fail(SV_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", who, workspace_bytes, need);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f32: workspace is not 256-byte aligned");
+      return fail(SV_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", who);
   }
   const sv_status dev = check_device();
   if (dev != SV_OK) return dev;
@@ -1142,15 +1152,30 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
   (void)hipGetLastError();
   if (n == 0) {
     k_fill<<<1, 64, 0, st>>>(out, 1, 0.0f);
-    return check_launch("sv_tree_sum_f32");
+    return check_launch(who);
   }
   unsigned *counter = reinterpret_cast<unsigned *>(workspace);
   Node *part = reinterpret_cast<Node *>(reinterpret_cast<char *>(workspace) + SUM_WS_HEADER);
   const bool vec = aligned16(x);
   const SumPlan p = plan_sum(n, g_tune.sum_e, g_tune.sum_blocks);
-  if (p.e == 16) launch_sum_e<16>(vec, x, n, p, part, counter, out, st);
-  else launch_sum_e<32>(vec, x, n, p, part, counter, out, st);
-  return check_launch("sv_tree_sum_f32");
+  if (dw) {
+    if (p.e == 16) launch_sum_dw<16>(vec, x, n, p, part, counter, out, st);
+    else launch_sum_dw<32>(vec, x, n, p, part, counter, out, st);
+  } else {
+    if (p.e == 16) launch_sum_e<16>(vec, x, n, p, part, counter, out, st);
+    else launch_sum_e<32>(vec, x, n, p, part, counter, out, st);
+  }
+  return check_launch(who);
+}
+
+sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return tree_sum_impl("sv_tree_sum_f32", false, x, n, out, workspace, workspace_bytes, stream);
+}
+
+sv_status sv_tree_sum_dw_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  return tree_sum_impl("sv_tree_sum_dw_f32", true, x, n, out, workspace, workspace_bytes, stream);
 }
 
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis) {

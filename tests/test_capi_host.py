@@ -79,6 +79,11 @@ def test_sum_argument_errors(L):
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ctypes.c_void_p(0x100010), 1 << 20, None) == SV_ERR_WORKSPACE
     assert b"aligned" in L.sv_last_error_message()
     assert L.sv_tree_sum_f32(BAD, (1 << 36) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
+    # the double-word-carry sum shares the checks and the workspace rules
+    assert L.sv_tree_sum_dw_f32(BAD, -1, BAD, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_tree_sum_dw_f32(BAD, 10, BAD, None, 0, None) == SV_ERR_WORKSPACE
+    assert b"sv_tree_sum_dw_f32" in L.sv_last_error_message()
+    assert L.sv_tree_sum_dw_f32(BAD, (1 << 36) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
 def test_variance_argument_errors(L):

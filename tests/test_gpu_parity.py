@@ -425,3 +425,52 @@ def test_variant_zero_matches_the_main_entry_point(torch_dev):
     v1 = sv.var(a, dim=1)
     torch.cuda.synchronize()
     assert torch.equal(v0.view(torch.int32), v1.view(torch.int32))
+
+
+# ------------------------------------------------------------------ double-word carries
+
+def gpu_sum_dw(torch_dev, x, offset=0):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    x = np.ascontiguousarray(x, np.float32)
+    if offset:
+        buf = torch.zeros(x.size + offset, dtype=torch.float32, device=dev)
+        buf[offset:] = torch.from_numpy(x).to(dev)
+        t = buf[offset:]
+    else:
+        t = torch.from_numpy(x).to(dev)
+    r = sv.tree_sum(t, carry="dw")
+    torch.cuda.synchronize()
+    return np.float32(r.item())
+
+
+DW_GEOMETRIES = {"default": {}, "e16_few_blocks": {"sum_e": 16, "sum_blocks": 64}, "single_workgroup": {"sum_blocks": 1}}
+
+
+@pytest.mark.parametrize("knobs", list(DW_GEOMETRIES.values()), ids=list(DW_GEOMETRIES))
+def test_sum_dw_sizes_and_specials(torch_dev, knobs):
+    import stable_variance_amd as sv
+
+    _apply(knobs)
+    try:
+        for n in (0, 1, 2, 3, 63, 2048, 2049, 65536 + 7, 1_000_003):
+            for x in (W.adversarial_values(n, seed=n), W.sum_cancelling_pairs(n, 0.3, seed=n + 1)):
+                assert same_bits(gpu_sum_dw(torch_dev, x), oracle.tree_sum_dw(x)), (knobs, n)
+                assert same_bits(gpu_sum_dw(torch_dev, x, offset=1), oracle.tree_sum_dw(x)), (knobs, n, "unaligned")
+        for special in ([np.inf, 1.0, -3.0], [np.inf, -np.inf, 2.0], [np.nan, 1.0], [3e38, 3e38, -1.0]):
+            x = np.concatenate([np.random.default_rng(3).standard_normal(5000).astype(np.float32),
+                                np.array(special, np.float32)])
+            assert same_bits(gpu_sum_dw(torch_dev, x), oracle.tree_sum_dw(x)), special
+    finally:
+        sv.set_tuning("reset", 0)
+
+
+def test_sum_dw_cancelling_sets_and_full_workload(torch_dev):
+    for n, frac, seed in ((1 << 16, 0.3, 1), (1 << 20, 0.1, 1), (1 << 22, 0.05, 0)):
+        x = W.sum_cancelling_pairs(n, frac, seed=seed)
+        assert same_bits(gpu_sum_dw(torch_dev, x), oracle.tree_sum_dw(x)), (n, frac, seed)
+    x = W.sum_cancelling_pairs()
+    want = oracle.tree_sum_dw(x)
+    assert same_bits(gpu_sum_dw(torch_dev, x), want)
+    assert want == oracle.round_f32(oracle.exact_sum(x))   # 3735.104, correctly rounded
