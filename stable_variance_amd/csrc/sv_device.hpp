@@ -279,6 +279,61 @@ __device__ __forceinline__ Node wave_tree_vlane(Node n) {
   return n;
 }
 
+// ---------------------------------------------------------------- permuted lane order
+
+// Lane L holding the range of virtual lane v(L) = 2 (L mod 32) + L / 32: the
+// tree's first cross-lane level then pairs lanes L and L ^ 32, virtual bits
+// 1..5 are lane bits 0..4, and the level order below follows.
+__device__ __forceinline__ int vlane_pair32(int lane) { return 2 * (lane & 31) + (lane >> 5); }
+
+// Lane l's value of v, as a wave-uniform (scalar) value.
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// v_permlane32_swap on two registers: afterwards lanes 0..31 hold x of their
+// own lane and of lane + 32, lanes 32..63 y of lane - 32 and of their own.
+__device__ __forceinline__ void swap32_two(float x, float y, float &a, float &b) {
+  unsigned u = __builtin_bit_cast(unsigned, x), t = __builtin_bit_cast(unsigned, y);
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(u), "+v"(t));
+  a = __builtin_bit_cast(float, u);
+  b = __builtin_bit_cast(float, t);
+}
+
+// The six cross-lane levels in the permuted order (lane xor 32 first, then
+// xor 1, 2, the two mirrors, xor 16); every lane ends with the wave's node.
+template <int KIND>
+__device__ __forceinline__ Node wave_tree_p32(Node n) {
+  auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
+  NodePair p = swap_node<32>(n);
+  n = comb(p.a, p.b);
+  n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
+  n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
+  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
+  n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
+  p = swap_node<16>(n);
+  return comb(p.a, p.b);
+}
+
+// The d and d^2 trees of a wave together, in the permuted order: one swap of
+// the two registers gives lanes 0..31 the pairs of the d tree and lanes
+// 32..63 those of the d^2 tree, and the remaining five levels run once for
+// both.  Lanes 0..31 return the wave's d node, lanes 32..63 its d^2 node.
+// The d^2 levels use the TwoSum node: on non-negative operands its error is
+// the same exact value, with the same sign of zero, as the Fast2Sum form.
+__device__ __forceinline__ Node wave_tree_dq(Node nd, Node nq) {
+  Node a, b;
+  swap32_two(nd.s, nq.s, a.s, b.s);
+  swap32_two(nd.c, nq.c, a.c, b.c);
+  Node n = combine(a, b);
+  n = combine(n, dpp_node<DPP_QUAD_XOR1>(n));
+  n = combine(n, dpp_node<DPP_QUAD_XOR2>(n));
+  n = combine(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
+  n = combine(n, dpp_node<DPP_ROW_MIRROR>(n));
+  const NodePair p = swap_node<16>(n);
+  return combine(p.a, p.b);
+}
+
 // ---------------------------------------------------------------- device-coherent words
 
 // Relaxed agent-scope (device-coherent) 32-bit store and load: they bypass

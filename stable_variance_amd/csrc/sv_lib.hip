@@ -349,16 +349,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
     if (top_ticket != (unsigned)ngroups - 1) return;
   }
 
-  // Last group: tree over the ngroups group nodes (two per lane), padded
-  // with zeros to SUM_MAX_BLOCKS / SUM_GROUP.
-  static_assert(SUM_MAX_BLOCKS / SUM_GROUP == 128, "two group nodes per lane");
-  Node t[2];
+  // Last group: tree over the ngroups group nodes (GPL consecutive ones per
+  // lane), padded with zeros to SUM_MAX_BLOCKS / SUM_GROUP.
+  constexpr int GPL = SUM_MAX_BLOCKS / SUM_GROUP / 64;
+  static_assert(GPL >= 1 && (GPL & (GPL - 1)) == 0, "group nodes per lane: a power of two");
+  Node t[GPL];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int idx = 2 * lane + k;
+  for (int k = 0; k < GPL; ++k) {
+    const int idx = GPL * lane + k;
     t[k] = (idx < ngroups) ? load_node_agent(grp_nodes + idx) : sv::zero_node();
   }
-  Node r = sv::wave_tree<KIND>(sv::combine_k<KIND>(t[0], t[1]));
+  Node r = sv::wave_tree<KIND>(sv::node_tree<0, GPL, GPL, KIND>(t));
   if (lane == 0) {
     out[0] = sv::root_value(r);
     __hip_atomic_store(top_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -429,19 +430,20 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   __shared__ Node slots[3][W];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
+  const int vl = sv::vlane_pair32(lane);  // this lane holds the range of virtual lane vl
   const int64_t row = blockIdx.x;
   const float *__restrict__ p = x + row * ld;
   const int64_t base = (int64_t)w * 64 * E;
 
   float v[E];
-  sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, lane);
+  sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, vl);
   const float x0 = p[0];
 
   // step 1: shift by the first element (padding stays +0)
   const bool full = base + 64 * E <= n;
-  int64_t vl = n - base - (int64_t)lane * E;
-  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
+  int64_t left = n - base - (int64_t)vl * E;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
   if constexpr (F::shift) {
     if (full) {
 #pragma unroll
@@ -454,18 +456,42 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
 
   // step 2: m = Tree(y) / n
   Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-  ny = sv::wave_tree<sv::NODE_TWOSUM>(ny);
-  ny = block_tree<W, false>(ny, slots[0], w, lane);
+  ny = sv::wave_tree_p32<sv::NODE_TWOSUM>(ny);
+  if constexpr (W > 1) {
+    if (lane == 0) slots[0][w] = ny;
+    __syncthreads();
+    Node t[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) t[i] = slots[0][i];
+    ny = sv::node_tree<0, W, W>(t);
+  }
   const float m = local_mean<V>(ny, n);
 
-  // step 3: Tree(d), Tree(d^2)
+  // step 3: Tree(d), Tree(d^2): lanes 0..31 end with the wave's d node,
+  // lanes 32..63 with its d^2 node
   Node nd, nq;
   if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
   else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-  nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
-  nq = sv::wave_tree<sv::NODE_NN>(nq);
-  nd = block_tree<W, false>(nd, slots[1], w, lane);
-  nq = block_tree<W, true>(nq, slots[2], w, lane);
+  const Node ndq = sv::wave_tree_dq(nd, nq);
+  nd = {sv::readlane_f(ndq.s, 0), sv::readlane_f(ndq.c, 0)};
+  nq = {sv::readlane_f(ndq.s, 32), sv::readlane_f(ndq.c, 32)};
+  if constexpr (W > 1) {
+    // one LDS round for both trees (their slots are not reused: no second barrier)
+    if (lane == 0) {
+      slots[1][w] = nd;
+      slots[2][w] = nq;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    Node td[W], tq[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      td[i] = slots[1][i];
+      tq[i] = slots[2][i];
+    }
+    nd = sv::node_tree<0, W, W>(td);
+    nq = sv::node_tree<0, W, W, sv::NODE_NN>(tq);
+  }
 
   // step 4
   if (threadIdx.x == 0) {
@@ -1013,12 +1039,19 @@ void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t 
   k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), 0, st>>>(x, n, ld, ddof, var, mean);
 }
 
-// A row shared by W waves of E values per lane: per-lane loads only.
+// A row shared by W waves of E values per lane; 16-byte loads follow
+// var_load_path (0 coalesced + LDS transpose, 1 per lane, 2 coalesced +
+// staged transpose), scalar loads are per lane.
 template <int E, int W>
 void launch_rows_split(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                        float *mean, hipStream_t st) {
-  if (vec) launch_rows_t<E, W, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
-  else launch_rows_t<E, W, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+  if (!vec) launch_rows_t<E, W, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+  else if (g_tune.var_load_path == 0) launch_rows_t<E, W, true, 0, false>(x, rows, n, ld, ddof, var, mean, st);
+  else if (g_tune.var_load_path == 2 && E % 16 == 0) {
+    if constexpr (E % 16 == 0) launch_rows_t<E, W, true, 2, false>(x, rows, n, ld, ddof, var, mean, st);
+  } else {
+    launch_rows_t<E, W, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+  }
 }
 
 template <int E, int W>
