@@ -10,7 +10,9 @@
 //                to the workspace, and the last workgroup to finish (a ticket
 //                counter) combines the group nodes in tree order.
 //   k_var_rows   axis 1: one workgroup per row; the W waves own consecutive
-//                64*E ranges of the row, each lane E consecutive values.  The
+//                64*E ranges of the row, each lane E consecutive values (lane
+//                L holds the range of virtual lane 2 (L mod 32) + L / 32, so
+//                that the d and d^2 trees share their cross-lane levels).  The
 //                row stays in registers between the two passes (y, then d and
 //                d^2), so HBM is read once.
 //   k_var_cols   axis 0: lanes own columns (coalesced across a row), waves own
