@@ -264,8 +264,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    (default), 2, 4 or 8
  *   "var_dma_rows"   rows of 1025..4096 values per wave staged by direct
  *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
- *   "var_split"      waves sharing one row of 1025..4096 values: 1, 2
- *                    (default), 4 or 8 (64, 32, 16 or 8 values per lane)
+ *   "var_split"      waves sharing one row of 1025..4096 values: 1, 2, 4
+ *                    (default) or 8 (64, 32, 16 or 8 values per lane)
+ *   "var_lds_pad"    unused dynamic LDS bytes per row workgroup, 0..65536
+ *                    (default 0): a cap on resident waves, for measurements
  *   "adn_e"          values per lane in an ADN-sum chunk: 16 (default) or 32
  *                    (32 only with three folds; other counts use 16)
  *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)

@@ -945,8 +945,9 @@ struct Tuning {
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
   int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
-  int var_split = 2;          // waves sharing one row (1, 2, 4, 8) for 1024 < n <= 4096
+  int var_split = 4;          // waves sharing one row (1, 2, 4, 8) for 1024 < n <= 4096
   int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
+  int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
 };
 Tuning g_tune;
 
@@ -1038,7 +1039,9 @@ void launch_sum_e(bool vec, const float *x, int64_t n, const SumPlan &p, Node *p
 template <int E, int W, bool VEC, int LOADP, bool NT>
 void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
                    hipStream_t st) {
-  k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), 0, st>>>(x, n, ld, ddof, var, mean);
+  // var_lds_pad: unused dynamic LDS per workgroup, a cap on resident waves
+  k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), (size_t)g_tune.var_lds_pad, st>>>(
+      x, n, ld, ddof, var, mean);
 }
 
 // A row shared by W waves of E values per lane; 16-byte loads follow
@@ -1122,7 +1125,7 @@ void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t co
   } while (0)
     if (n <= 256) SV_ROWS(4, 1);
     else if (n <= 1024) SV_ROWS(16, 1);
-    else if (n <= 4096) SV_ROWS(32, 2);  // the default geometry of the main kernel
+    else if (n <= 4096) SV_ROWS(16, 4);  // the default geometry of the main kernel
     else SV_ROWS(64, 4);
 #undef SV_ROWS
   } else {
@@ -1464,6 +1467,11 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_nt") == 0) return flag(&g_tune.var_nt);
+  if (strcmp(key, "var_lds_pad") == 0) {
+    if (value < 0 || value > 65536) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_lds_pad must be in [0, 65536]");
+    g_tune.var_lds_pad = (int)value;
+    return ok();
+  }
   if (strcmp(key, "var_split") == 0) {
     if (value != 1 && value != 2 && value != 4 && value != 8)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_split must be 1, 2, 4 or 8");

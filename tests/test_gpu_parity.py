@@ -44,7 +44,8 @@ VAR_GEOMETRIES = {
     "lds_transpose": {"var_load_path": 0, "var_nt": 0},
     "staged_transpose": {"var_load_path": 2},
     "split1": {"var_split": 1},
-    "split4": {"var_split": 4},
+    "split2": {"var_split": 2},
+    "occupancy_capped": {"var_lds_pad": 20000},
     "split8": {"var_split": 8},
     "pipelined_rows2": {"var_rows_per_wave": 2},
     "pipelined_rows8_lds": {"var_rows_per_wave": 8, "var_load_path": 0},
