@@ -87,6 +87,8 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_float
             f.argtypes = [fp, i64]
+        L.orc_tree_node_f32.restype = ctypes.c_int
+        L.orc_tree_node_f32.argtypes = [fp, i64, i64, fp, fp]
         L.orc_variance_f32.restype = ctypes.c_int
         L.orc_variance_f32.argtypes = [fp, i64, i64, ctypes.c_int, i64, ctypes.c_int, fp, fp]
         _lib = L
@@ -124,6 +126,67 @@ def tree_sum_dw(x, pad_to: int = 0) -> np.float32:
     renormalised with TwoSum (see ``orc_tree_sum_dw_f32``)."""
     a = _f32c(x).ravel()
     return np.float32(lib().orc_tree_sum_dw_f32(_ptr(a), a.size, 1, int(pad_to)))
+
+
+def tree_sum_threads(x, threads: int) -> np.float32:
+    """The compensated tree of ``x`` computed on up to ``threads`` host
+    threads: the padded tree is cut into 2^k aligned subtrees (one per
+    thread, in C, which runs without the GIL), whose root nodes are then
+    combined level by level with the same node.  Same bits as tree_sum."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    a = _f32c(x).ravel()
+    n = a.size
+    if n == 0:
+        return np.float32(0.0)
+    P = 1 << max(0, (n - 1).bit_length())
+    T = 1
+    while T * 2 <= max(1, threads) and P // (T * 2) >= 1:
+        T *= 2
+    cs = P // T
+
+    def node(i):
+        lo = i * cs
+        piece = np.ascontiguousarray(a[lo:min(lo + cs, n)])
+        s, c = ctypes.c_float(0.0), ctypes.c_float(0.0)
+        rc = lib().orc_tree_node_f32(_ptr(piece), piece.size, cs, ctypes.byref(s), ctypes.byref(c))
+        if rc != 0:
+            raise RuntimeError("orc_tree_node_f32 failed")
+        return np.float32(s.value), np.float32(c.value)
+
+    with ThreadPoolExecutor(max_workers=T) as ex:
+        nodes = list(ex.map(node, range(T)))
+    with np.errstate(invalid="ignore", over="ignore"):
+        while len(nodes) > 1:
+            nxt = []
+            for k in range(0, len(nodes), 2):
+                (sl, cl), (sr, cr) = nodes[k], nodes[k + 1]
+                s, e = two_sum(sl, sr)
+                nxt.append((s, np.float32(np.float32(cl + cr) + e)))
+            nodes = nxt
+        s, c = nodes[0]
+        return s if not np.isfinite(s) else np.float32(s + c)
+
+
+def variance_threads(x, axis: int, threads: int, ddof: int = 0):
+    """oracle.variance over blocks of slices on up to ``threads`` host
+    threads (slices are independent; same bits)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    a = np.ascontiguousarray(x, np.float32)
+    ax = axis % 2
+    nsl = a.shape[0] if ax == 1 else a.shape[1]
+    T = max(1, min(threads, nsl))
+    bounds = [(i * nsl // T, (i + 1) * nsl // T) for i in range(T)]
+
+    def part(b):
+        lo, hi = b
+        blk = a[lo:hi] if ax == 1 else np.ascontiguousarray(a[:, lo:hi])
+        return variance(blk, axis=ax, ddof=ddof)
+
+    with ThreadPoolExecutor(max_workers=T) as ex:
+        res = list(ex.map(part, bounds))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
 
 
 def tree_plain(x, pad_to: int = 0) -> np.float32:

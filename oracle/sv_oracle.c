@@ -153,6 +153,38 @@ float orc_tree_sum_dw_f32(const float *x, int64_t n, int64_t stride, int64_t pad
     return root_s + root_c;
 }
 
+/*
+ * The root node (s_0, c_0) of the compensated tree over x padded to pad_to
+ * (a power of two >= n; n may be 0).  An aligned subtree of a larger tree,
+ * so that a sum can be cut into 2^k pieces computed separately and their
+ * nodes combined with the same rule: the bits equal the whole tree's.
+ * Returns 0, or -1 for a bad pad_to.
+ */
+int orc_tree_node_f32(const float *x, int64_t n, int64_t pad_to, float *s_out, float *c_out) {
+    if (n < 0 || pad_to < 1 || (pad_to & (pad_to - 1)) != 0 || pad_to < n) return -1;
+    float *s = (float *)malloc((size_t)pad_to * sizeof(float));
+    float *c = (float *)malloc((size_t)pad_to * sizeof(float));
+    if (!s || !c) { free(s); free(c); return -1; }
+    for (int64_t i = 0; i < pad_to; ++i) {
+        s[i] = (i < n) ? x[i] : 0.0f;
+        c[i] = 0.0f;
+    }
+    for (int64_t len = pad_to; len > 1; len >>= 1) {
+        for (int64_t k = 0; k < len / 2; ++k) {
+            float e;
+            float sk = two_sum(s[2 * k], s[2 * k + 1], &e);
+            float ck = (c[2 * k] + c[2 * k + 1]) + e;
+            s[k] = sk;
+            c[k] = ck;
+        }
+    }
+    *s_out = s[0];
+    *c_out = c[0];
+    free(s);
+    free(c);
+    return 0;
+}
+
 /* Same topology without the error array: the plain pairwise tree. */
 float orc_tree_plain_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to) {
     if (n <= 0) return 0.0f;

@@ -425,3 +425,23 @@ def test_ablation_kahan_scan_is_the_blog_recurrence():
     assert v[0] == 0.0 and mu[0] == np.float32(0.001)
     # unshifted sum check through the d^2 tree is not available; the loop
     # itself is pinned by test_kahan_blog_outputs.
+
+
+def test_threaded_oracle_splits_exactly():
+    # The all-cores timing of the oracle cuts the sum into aligned subtrees
+    # and the variance into blocks of slices; both must give the same bits.
+    import workloads as W
+
+    for n in (1, 2, 3, 5, 1000, 4097, 300_001):
+        y = W.adversarial_values(n, seed=n)
+        want = np.float32(oracle.tree_sum(y)).view(np.uint32)
+        for t in (1, 2, 3, 8):
+            assert np.float32(oracle.tree_sum_threads(y, t)).view(np.uint32) == want, (n, t)
+    a = W.c4_matrix()[:300]
+    v1, m1 = oracle.variance(a, axis=1)
+    v8, m8 = oracle.variance_threads(a, 1, 8)
+    assert np.array_equal(v1.view(np.uint32), v8.view(np.uint32)) and np.array_equal(m1.view(np.uint32), m8.view(np.uint32))
+    b = np.ascontiguousarray(a[:, :200])
+    v1, m1 = oracle.variance(b, axis=0)
+    v8, m8 = oracle.variance_threads(b, 0, 8)
+    assert np.array_equal(v1.view(np.uint32), v8.view(np.uint32)) and np.array_equal(m1.view(np.uint32), m8.view(np.uint32))
