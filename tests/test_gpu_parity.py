@@ -249,6 +249,38 @@ def test_variance_rows_shapes(torch_dev, var_geometry, n):
     check_var(torch_dev, b, 1, 0)
 
 
+def special_rows(n, seed):
+    """Rows with NaN, +Inf, -Inf, both infinities, values whose differences
+    or squares overflow, and subnormal-only rows, at seeded positions."""
+    rng = np.random.default_rng(seed)
+    a = rng.normal(5.0, 2.0, (8, n)).astype(np.float32)
+    pos = lambda: int(rng.integers(0, n))
+    a[0, pos()] = np.nan
+    a[1, pos()] = np.inf
+    a[2, pos()] = -np.inf
+    a[3, pos()] = np.inf
+    a[3, pos()] = -np.inf
+    a[4, :] = rng.choice(np.float32([3e38, -3e38]), n)          # d = x - x0 and d^2 overflow
+    a[5, :] = (rng.integers(-50, 50, n) * np.float32(2.0 ** -149)).astype(np.float32)
+    a[6, :] = np.float32(1e38)
+    a[6, pos()] = np.float32(-1e38)                            # one far value: d^2 = inf
+    a[7, :] = np.nan
+    return a
+
+
+@pytest.mark.parametrize("n", [3, 64, 1000, 4096, 10000, 20000])
+def test_variance_specials_rows(torch_dev, var_geometry, n):
+    a = special_rows(n, seed=n)
+    for ddof in (0, 1):
+        check_var(torch_dev, a, 1, ddof)
+
+
+@pytest.mark.parametrize("R", [3, 64, 1000, 1500])
+def test_variance_specials_cols(torch_dev, R):
+    a = np.ascontiguousarray(special_rows(R, seed=R + 7).T)
+    check_var(torch_dev, a, 0, 0)
+
+
 COL_RS = [1, 2, 3, 4, 5, 16, 17, 64, 65, 100, 128, 129, 256, 257, 512, 513, 1000, 1024]
 
 
