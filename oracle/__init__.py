@@ -87,6 +87,13 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_float
             f.argtypes = [fp, i64]
+        dp = ctypes.POINTER(ctypes.c_double)
+        L.orc_two_sum_f64.restype = ctypes.c_double
+        L.orc_two_sum_f64.argtypes = [ctypes.c_double, ctypes.c_double, dp]
+        L.orc_tree_sum_f64.restype = ctypes.c_double
+        L.orc_tree_sum_f64.argtypes = [dp, i64, i64, i64]
+        L.orc_variance_f64.restype = ctypes.c_int
+        L.orc_variance_f64.argtypes = [dp, i64, i64, ctypes.c_int, i64, ctypes.c_int, dp, dp]
         L.orc_tree_node_f32.restype = ctypes.c_int
         L.orc_tree_node_f32.argtypes = [fp, i64, i64, fp, fp]
         L.orc_variance_f32.restype = ctypes.c_int
@@ -187,6 +194,40 @@ def variance_threads(x, axis: int, threads: int, ddof: int = 0):
     with ThreadPoolExecutor(max_workers=T) as ex:
         res = list(ex.map(part, bounds))
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def two_sum_f64(a: float, b: float) -> tuple[float, float]:
+    e = ctypes.c_double(0.0)
+    s = lib().orc_two_sum_f64(float(a), float(b), ctypes.byref(e))
+    return s, e.value
+
+
+def tree_sum_f64(x, pad_to: int = 0) -> np.float64:
+    """Compensated pairwise tree in binary64 (same topology and readings)."""
+    a = np.ascontiguousarray(x, np.float64).ravel()
+    return np.float64(lib().orc_tree_sum_f64(_dptr(a), a.size, 1, int(pad_to)))
+
+
+def variance_f64(x, axis: int = -1, ddof: int = 0, method: int = METHOD_KERNEL):
+    """The method (METHOD_KERNEL) or the two-term reference (METHOD_REFERENCE)
+    on a 2-D float64 array, every operation in binary64."""
+    a = np.ascontiguousarray(x, np.float64)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+        axis = 1
+    rows, cols = a.shape
+    ax = axis % 2
+    ns = rows if ax == 1 else cols
+    var = np.empty(ns, np.float64)
+    mean = np.empty(ns, np.float64)
+    rc = lib().orc_variance_f64(_dptr(a), rows, cols, ax, int(ddof), int(method), _dptr(var), _dptr(mean))
+    if rc != 0:
+        raise ValueError(f"orc_variance_f64 failed ({rc})")
+    return var, mean
 
 
 def tree_plain(x, pad_to: int = 0) -> np.float32:

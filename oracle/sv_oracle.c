@@ -447,3 +447,143 @@ int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64
     free(buf2);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* The method in binary64 (the float64 path; [VAR] §5 lists float64 as  */
+/* not measured on the page).  The same steps, topology and readings as */
+/* the float32 functions above, every operation in double.             */
+/* ------------------------------------------------------------------ */
+static inline double two_sum_d(double a, double b, double *err) {
+    double s = a + b;
+    double bv = s - a;
+    double av = s - bv;
+    *err = (a - av) + (b - bv);
+    return s;
+}
+
+double orc_two_sum_f64(double a, double b, double *err) { return two_sum_d(a, b, err); }
+
+/* Compensated tree in double: same padding, pairing, carry and root guard. */
+double orc_tree_sum_f64(const double *x, int64_t n, int64_t stride, int64_t pad_to) {
+    if (n <= 0) return 0.0;
+    int64_t P = pow2_ceil(n);
+    if (pad_to != 0) {
+        if (pad_to < P || (pad_to & (pad_to - 1)) != 0) return NAN;
+        P = pad_to;
+    }
+    double *s = (double *)malloc((size_t)P * sizeof(double));
+    double *c = (double *)malloc((size_t)P * sizeof(double));
+    if (!s || !c) { free(s); free(c); return NAN; }
+    for (int64_t i = 0; i < P; ++i) {
+        s[i] = (i < n) ? x[i * stride] : 0.0;
+        c[i] = 0.0;
+    }
+    for (int64_t len = P; len > 1; len >>= 1) {
+        for (int64_t k = 0; k < len / 2; ++k) {
+            double e;
+            double sk = two_sum_d(s[2 * k], s[2 * k + 1], &e);
+            double ck = (c[2 * k] + c[2 * k + 1]) + e;
+            s[k] = sk;
+            c[k] = ck;
+        }
+    }
+    double root_s = s[0], root_c = c[0];
+    free(s);
+    free(c);
+    if (!isfinite(root_s)) return root_s;
+    return root_s + root_c;
+}
+
+static double tree_plain_d(const double *x, int64_t n) {
+    if (n <= 0) return 0.0;
+    int64_t P = pow2_ceil(n);
+    double *s = (double *)malloc((size_t)P * sizeof(double));
+    if (!s) return NAN;
+    for (int64_t i = 0; i < P; ++i) s[i] = (i < n) ? x[i] : 0.0;
+    for (int64_t len = P; len > 1; len >>= 1)
+        for (int64_t k = 0; k < len / 2; ++k) s[k] = s[2 * k] + s[2 * k + 1];
+    double r = s[0];
+    free(s);
+    return r;
+}
+
+static inline double max0_nan_d(double v) {
+    if (v != v) return v;
+    return (v > 0.0) ? v : 0.0;
+}
+
+static inline double ddof_scale_d(double v, int64_t n, int64_t ddof) {
+    if (ddof == 0) return v;
+    int64_t den = n - ddof;
+    if (den < 0) den = 0;
+    double f = (double)n / (double)den;
+    return v * f;
+}
+
+/* The kernel of [VAR] §2 on one slice, in double. */
+static void var_kernel_slice_d(const double *x, int64_t n, int64_t stride, int64_t ddof, double *buf,
+                               double *var, double *mean) {
+    if (n <= 0) {
+        *var = NAN;
+        *mean = NAN;
+        return;
+    }
+    for (int64_t i = 0; i < n; ++i) buf[i] = x[i * stride];
+    double x0 = buf[0];
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - x0;
+    double fn = (double)n;
+    double m = orc_tree_sum_f64(buf, n, 1, 0) / fn;
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;
+    double s1 = orc_tree_sum_f64(buf, n, 1, 0);
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] * buf[i];
+    double s2 = orc_tree_sum_f64(buf, n, 1, 0);
+    double a = s2 / fn;
+    double b = s1 / fn;
+    double bb = b * b;
+    *var = ddof_scale_d(max0_nan_d(a - bb), n, ddof);
+    *mean = x0 + m;
+}
+
+/* The two-term reference formula of [VAR] §1 in double (means as the plain
+ * tree times fl(1/n), as in float32). */
+static void var_reference_slice_d(const double *x, int64_t n, int64_t stride, int64_t ddof, double *buf,
+                                  double *buf2, double *var, double *mean) {
+    if (n <= 0) {
+        *var = NAN;
+        *mean = NAN;
+        return;
+    }
+    for (int64_t i = 0; i < n; ++i) buf[i] = x[i * stride];
+    double inv = 1.0 / (double)n;
+    double m = tree_plain_d(buf, n) * inv;
+    for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;
+    for (int64_t i = 0; i < n; ++i) buf2[i] = buf[i] * buf[i];
+    double md = tree_plain_d(buf, n) * inv;
+    double mq = tree_plain_d(buf2, n) * inv;
+    *var = ddof_scale_d(max0_nan_d(mq - md * md), n, ddof);
+    *mean = m;
+}
+
+/* Variance of a row-major double [rows, cols] array; method 0 the kernel,
+ * 2 the two-term reference.  Returns 0, or -1 on bad arguments. */
+int orc_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int method,
+                     double *var, double *mean) {
+    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || (method != 0 && method != 2)) return -1;
+    int64_t nslices = axis == 1 ? rows : cols;
+    int64_t n = axis == 1 ? cols : rows;
+    int64_t stride = axis == 1 ? 1 : cols;
+    int64_t sstride = axis == 1 ? cols : 1;
+    double *buf = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *buf2 = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (!buf || !buf2) { free(buf); free(buf2); return -2; }
+    for (int64_t s = 0; s < nslices; ++s) {
+        double v, mu;
+        if (method == 0) var_kernel_slice_d(x + s * sstride, n, stride, ddof, buf, &v, &mu);
+        else var_reference_slice_d(x + s * sstride, n, stride, ddof, buf, buf2, &v, &mu);
+        var[s] = v;
+        if (mean) mean[s] = mu;
+    }
+    free(buf);
+    free(buf2);
+    return 0;
+}
