@@ -56,7 +56,7 @@ ADN_PAGE_FLOAT_GELEMS = {"NVIDIA GB10": 55.4, "NVIDIA RTX PRO 4500 Blackwell": 1
 def source_digest() -> str:
     h = hashlib.sha256()
     for rel in ("stable_variance_amd/csrc/sv_lib.hip", "stable_variance_amd/csrc/sv_adn.hip",
-                "stable_variance_amd/csrc/sv_device.hpp"):
+                "stable_variance_amd/csrc/sv_f64.hip", "stable_variance_amd/csrc/sv_device.hpp"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -354,6 +354,43 @@ def main():
         dw["cpu_oracle"] = {"value": round(SUM_N / t_dw / 1e9, 5), "unit": "GElem/s", "cores": 1, "kind": "oracle",
                             "sample": f"the full 10^8 sum once, {t_dw:.2f} s, single-threaded C oracle"}
 
+    # the float64 path: the same workloads in double (2 + 4 copies)
+    c5d = [t.to(torch.float64) for t in c5]
+    c4d = [c4[k].to(torch.float64) for k in range(4)]
+    need64 = L.sv_tree_sum_f64_workspace_size(SUM_N)
+    ws64 = torch.zeros(need64, dtype=torch.uint8, device=dev)
+    out64 = torch.empty((), dtype=torch.float64, device=dev)
+    var64 = torch.empty(VAR_ROWS, dtype=torch.float64, device=dev)
+    mean64 = torch.empty(VAR_ROWS, dtype=torch.float64, device=dev)
+    sum64_ms = time_op(lambda i: check(L.sv_tree_sum_f64(c5d[i % 2].data_ptr(), SUM_N, out64.data_ptr(),
+                                                        ws64.data_ptr(), need64, sh)), reps=30)
+    var64_ms = time_op(lambda i: check(L.sv_variance_f64(c4d[i % 4].data_ptr(), VAR_ROWS, VAR_COLS, 1, 0,
+                                                        var64.data_ptr(), mean64.data_ptr(), sh)), reps=40)
+    read64_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c5d[i % 2].data_ptr(), 2 * SUM_N,
+                                                                   probe_out.data_ptr(), sh)), reps=20)
+    top = torch.full((1, 3), 1e307, dtype=torch.float64, device=dev)
+    top_var = torch.empty(1, dtype=torch.float64, device=dev)
+    check(L.sv_variance_f64(top.data_ptr(), 1, 3, 1, 0, top_var.data_ptr(), None, sh))
+    torch.cuda.synchronize()
+    f64 = {"sum_1e8": {"avg_launch_ms": round(sum64_ms, 5), "gb_s": round(8 * SUM_N / (sum64_ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(8 * SUM_N / (sum64_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "read_ceiling_gbs": round(8 * SUM_N / (read64_ms * 1e-3) / 1e9, 1)},
+           "variance_4096x4096": {"avg_launch_ms": round(var64_ms, 5),
+                                  "gb_s": round(8 * VAR_ROWS * VAR_COLS / (var64_ms * 1e-3) / 1e9, 1),
+                                  "hbm_frac": round(8 * VAR_ROWS * VAR_COLS / (var64_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "variance_of_1e307_x3": float(top_var.item()), "bit_exact": None}
+    if not args.no_cpu_baseline:
+        check(L.sv_tree_sum_f64(c5d[0].data_ptr(), SUM_N, out64.data_ptr(), ws64.data_ptr(), need64, sh))
+        check(L.sv_variance_f64(c4d[0].data_ptr(), VAR_ROWS, VAR_COLS, 1, 0, var64.data_ptr(), mean64.data_ptr(), sh))
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(1).choice(VAR_ROWS, 16, replace=False)
+        ov64, om64 = oracle.variance_f64(c4_host[rows].astype(np.float64), axis=1)
+        ok64 = (np.float64(out64.item()) == oracle.tree_sum_f64(c5_host.astype(np.float64)) and
+                np.array_equal(var64.cpu().numpy()[rows].view(np.uint64), ov64.view(np.uint64)) and
+                np.array_equal(mean64.cpu().numpy()[rows].view(np.uint64), om64.view(np.uint64)))
+        f64["bit_exact"] = bool(ok64)
+    del c5d, c4d
+
     elems = VAR_ROWS * VAR_COLS + SUM_N
     value = elems * K / wall / 1e9
     sum_gbs = SUM_BYTES / (sum_avg * 1e-3) / 1e9
@@ -406,6 +443,7 @@ def main():
                     "pages_kernel_over_reference": {"kaggle_cpu": 2.27, "kaggle_gpu": 2.19},
                     "ablation_4096x4096": variants},
         "tree_sum_dw_carry": dw,
+        "float64_path": f64,
         "adn_sum": adn,
         "parity": parity,
     }

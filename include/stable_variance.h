@@ -192,6 +192,29 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
                                   float *var_out, float *mean_out, void *stream);
 
 /*
+ * The method in binary64 (the float64 path): the compensated tree sum and
+ * the variance of Pennacchio, "Variance in float32 ...", §2 steps 1-4, with
+ * every operation in double (§5 of that page lists float64 as not
+ * measured).  Same topology, carries, root guard, max, ddof and empty-slice
+ * readings as the float32 entry points.
+ *
+ * sv_tree_sum_f64: x n device doubles (8-byte aligned), 0 <= n <= 2^35;
+ *   out one device double; workspace of sv_tree_sum_f64_workspace_size(n)
+ *   bytes, 256-byte aligned, whose first SV_TREE_SUM_COUNTER_BYTES bytes are
+ *   ticket counters with the same rules as for sv_tree_sum_f32.
+ * sv_variance_f64: x row-major [rows, cols] device doubles (8-byte aligned);
+ *   slices of at most 8192 values on axis 1 and 1024 on axis 0 (else
+ *   SV_ERR_UNSUPPORTED); var_out (and mean_out if not NULL) one double per
+ *   slice; no workspace.
+ * Errors and asynchrony as for the float32 entry points.
+ */
+size_t sv_tree_sum_f64_workspace_size(int64_t n);
+sv_status sv_tree_sum_f64(const double *x, int64_t n, double *out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, double *var_out,
+                          double *mean_out, void *stream);
+
+/*
  * Ahrens-Demmel-Nguyen binned reproducible sum of float32 values, as the
  * "SyclReproSum" README describes it ("How It Works", "Accumulator capacity",
  * "Template Parameters"): every value is deposited into `fold` (K) primary

@@ -76,6 +76,12 @@ def capi():
                 L.sv_variance_c64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_variance_variant_f32.restype = ctypes.c_int
                 L.sv_variance_variant_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
+                L.sv_tree_sum_f64_workspace_size.restype = sz
+                L.sv_tree_sum_f64_workspace_size.argtypes = [i64]
+                L.sv_tree_sum_f64.restype = ctypes.c_int
+                L.sv_tree_sum_f64.argtypes = [vp, i64, vp, vp, sz, vp]
+                L.sv_variance_f64.restype = ctypes.c_int
+                L.sv_variance_f64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp]
                 L.sv_tree_sum_dw_f32.restype = ctypes.c_int
                 L.sv_tree_sum_dw_f32.argtypes = [vp, i64, vp, vp, sz, vp]
                 L.sv_adn_sum_f32_workspace_size.restype = sz
@@ -119,12 +125,12 @@ def _workspace(kind: str, nbytes: int, device, stream_handle: int):
     return ws
 
 
-def _check_tensor(x, name="x", complex_ok=False):
+def _check_tensor(x, name="x", complex_ok=False, double_ok=False):
     import torch
 
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    ok = (torch.float32, torch.complex64) if complex_ok else (torch.float32,)
+    ok = (torch.float32,) + ((torch.complex64,) if complex_ok else ()) + ((torch.float64,) if double_ok else ())
     if x.dtype not in ok:
         raise TypeError(f"{name} must be {' or '.join(str(d) for d in ok)}, got {x.dtype}")
     if x.device.type != "cuda":
@@ -132,26 +138,31 @@ def _check_tensor(x, name="x", complex_ok=False):
 
 
 def tree_sum(x, carry: str = "plain"):
-    """Compensated pairwise tree sum of all elements of a float32 tensor.
+    """Compensated pairwise tree sum of all elements of a float32 (or
+    float64: every operation in double) tensor.
 
     ``carry="dw"`` renormalises every node's (sum, carry) pair (double-word
     carries, ``sv_tree_sum_dw_f32``)."""
     import torch
 
-    _check_tensor(x)
+    _check_tensor(x, double_ok=True)
     if carry not in ("plain", "dw"):
         raise ValueError(f"carry must be 'plain' or 'dw', got {carry!r}")
+    is_double = x.dtype == torch.float64
+    if is_double and carry != "plain":
+        raise ValueError("double-word carries are built for float32 input only")
     x = x.contiguous().reshape(-1)
     n = x.numel()
     L = capi()
-    fn = L.sv_tree_sum_f32 if carry == "plain" else L.sv_tree_sum_dw_f32
+    fn = L.sv_tree_sum_f64 if is_double else (L.sv_tree_sum_f32 if carry == "plain" else L.sv_tree_sum_dw_f32)
+    wsz = L.sv_tree_sum_f64_workspace_size if is_double else L.sv_tree_sum_f32_workspace_size
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-        out = torch.empty((), dtype=torch.float32, device=x.device)
-        need = L.sv_tree_sum_f32_workspace_size(n)
+        out = torch.empty((), dtype=x.dtype, device=x.device)
+        need = wsz(n)
         if need == ctypes.c_size_t(-1).value:
             raise SvError(5, f"tree_sum: n = {n} is not supported")
-        ws = _workspace("sum", need, x.device, stream)
+        ws = _workspace("sum64" if is_double else "sum", need, x.device, stream)
         _check(fn(x.data_ptr() if n else None, n, out.data_ptr(), ws.data_ptr() if ws is not None else None, need,
                   stream))
     return out
@@ -179,8 +190,8 @@ def adn_sum(x, fold: int = 3):
 
 
 def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
-    """Variance of each slice of a 2-D (or 1-D) float32 or complex64 tensor
-    along ``dim``.
+    """Variance of each slice of a 2-D (or 1-D) float32, float64 or complex64
+    tensor along ``dim`` (float64: the method with every operation in double).
 
     Returns a float32 tensor of the non-reduced length (and the mean, float32
     or complex64, when ``return_mean``).  For complex64 data the variance is
@@ -188,8 +199,9 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     """
     import torch
 
-    _check_tensor(x, complex_ok=True)
+    _check_tensor(x, complex_ok=True, double_ok=True)
     is_complex = x.dtype == torch.complex64
+    is_double = x.dtype == torch.float64
     if x.dim() == 1:
         x2 = x.reshape(1, -1)
         axis = 1
@@ -208,6 +220,18 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     rows, cols = x2.shape
     ns = rows if axis == 1 else cols
     L = capi()
+    if is_double:
+        with torch.cuda.device(x.device):
+            stream = torch.cuda.current_stream(x.device).cuda_stream
+            out = torch.empty(ns, dtype=torch.float64, device=x.device)
+            mean = torch.empty(ns, dtype=torch.float64, device=x.device) if return_mean else None
+            _check(L.sv_variance_f64(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof),
+                                     out.data_ptr() if ns else None,
+                                     mean.data_ptr() if (mean is not None and ns) else None, stream))
+        if squeeze:
+            out = out.reshape(())
+            mean = mean.reshape(()) if mean is not None else None
+        return (out, mean) if return_mean else out
     fn = L.sv_variance_c64 if is_complex else L.sv_variance_f32
     wsz = L.sv_variance_c64_workspace_size if is_complex else L.sv_variance_f32_workspace_size
     with torch.cuda.device(x.device):

@@ -1,0 +1,584 @@
+// The method in binary64 on gfx950: the compensated tree sum and the stable
+// variance with every operation in double.
+//
+// Method: Pennacchio, "Variance in float32 with a first-element shift, a
+// local centring and a compensated tree sum", §2 steps 1-4, carried out in
+// double (§5 of that page lists float64 as not measured).  Same tree
+// topology, carries, root guard, max and ddof readings as the float32 path.
+//
+// The loads reuse the float32 tiles: a run of 2^k doubles is a run of
+// 2^(k+1) floats, and a lane that holds 2E consecutive floats holds E
+// consecutive doubles (low word first).  Cross-lane moves of a double are two
+// 32-bit moves (DPP or permlane swap).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/stable_variance.h"
+#include "sv_device.hpp"
+#include "sv_host.hpp"
+
+using svh::check_device;
+using svh::check_launch;
+using svh::fail;
+using svh::ok;
+
+namespace {
+
+// ------------------------------------------------------------------ nodes
+
+struct NodeD {
+  double s, c;
+};
+
+__device__ __forceinline__ NodeD combine_d(NodeD l, NodeD r) {
+  const double s = l.s + r.s;
+  const double bv = s - l.s;
+  const double av = s - bv;
+  const double e = (l.s - av) + (r.s - bv);
+  return {s, (l.c + r.c) + e};
+}
+
+// Leaves: the sum keeps the carry as 0 + e (the oracle's (0 + 0) + e); the
+// variance trees keep e (only a zero's sign differs, which no output sees).
+__device__ __forceinline__ NodeD leaf_canon_d(double a, double b) {
+  const double s = a + b;
+  const double bv = s - a;
+  const double av = s - bv;
+  return {s, 0.0 + ((a - av) + (b - bv))};
+}
+
+__device__ __forceinline__ NodeD leaf_fast_d(double a, double b) {
+  const double s = a + b;
+  const double bv = s - a;
+  const double av = s - bv;
+  return {s, (a - av) + (b - bv)};
+}
+
+// Non-negative operands (the d^2 tree): Fast2Sum after a max/min gives the
+// same exact error as TwoSum.
+__device__ __forceinline__ NodeD combine_nn_d(NodeD l, NodeD r) {
+  const double s = l.s + r.s;
+  const double hi = __builtin_fmax(l.s, r.s);
+  const double lo = __builtin_fmin(l.s, r.s);
+  return {s, (l.c + r.c) + (lo - (s - hi))};
+}
+
+__device__ __forceinline__ NodeD leaf_nn_d(double a, double b) {
+  const double s = a + b;
+  const double hi = __builtin_fmax(a, b);
+  const double lo = __builtin_fmin(a, b);
+  return {s, lo - (s - hi)};
+}
+
+__device__ __forceinline__ double root_value_d(NodeD n) { return __builtin_isfinite(n.s) ? n.s + n.c : n.s; }
+
+template <bool NN>
+__device__ __forceinline__ NodeD comb_d(NodeD l, NodeD r) {
+  if constexpr (NN) return combine_nn_d(l, r);
+  else return combine_d(l, r);
+}
+
+enum { LEAF_CANON_D = 0, LEAF_FAST_D = 1, LEAF_NN_D = 2 };
+
+template <int LEAF, int OFF, int N, int E>
+__device__ __forceinline__ NodeD lane_tree_d(const double (&v)[E]) {
+  if constexpr (N == 2) {
+    if constexpr (LEAF == LEAF_CANON_D) return leaf_canon_d(v[OFF], v[OFF + 1]);
+    else if constexpr (LEAF == LEAF_FAST_D) return leaf_fast_d(v[OFF], v[OFF + 1]);
+    else return leaf_nn_d(v[OFF], v[OFF + 1]);
+  } else {
+    const NodeD l = lane_tree_d<LEAF, OFF, N / 2, E>(v);
+    const NodeD r = lane_tree_d<LEAF, OFF + N / 2, N / 2, E>(v);
+    return comb_d<LEAF == LEAF_NN_D>(l, r);
+  }
+}
+
+template <int OFF, int N, int K, bool NN>
+__device__ __forceinline__ NodeD node_tree_d(const NodeD (&nd)[K]) {
+  if constexpr (N == 1) return nd[OFF];
+  else return comb_d<NN>(node_tree_d<OFF, N / 2, K, NN>(nd), node_tree_d<OFF + N / 2, N / 2, K, NN>(nd));
+}
+
+// d = y - m and q = d * d, then their trees, leaf pair by leaf pair; entries
+// at or past `valid` are +0 (padding), not fl(0 - m).
+template <bool MASK, int OFF, int N, int E>
+__device__ __forceinline__ void lane_tree_dq_d(const double (&y)[E], double m, int valid, NodeD &nd, NodeD &nq) {
+  if constexpr (N == 2) {
+    double d0 = y[OFF] - m;
+    double d1 = y[OFF + 1] - m;
+    if constexpr (MASK) {
+      d0 = (OFF < valid) ? d0 : 0.0;
+      d1 = (OFF + 1 < valid) ? d1 : 0.0;
+    }
+    nd = leaf_fast_d(d0, d1);
+    nq = leaf_nn_d(d0 * d0, d1 * d1);
+  } else {
+    NodeD ld, lq, rd, rq;
+    lane_tree_dq_d<MASK, OFF, N / 2, E>(y, m, valid, ld, lq);
+    lane_tree_dq_d<MASK, OFF + N / 2, N / 2, E>(y, m, valid, rd, rq);
+    nd = combine_d(ld, rd);
+    nq = combine_nn_d(lq, rq);
+  }
+}
+
+// ------------------------------------------------------------------ cross-lane
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ NodeD dpp_node_d(NodeD n) {
+  return {dpp_d<CTRL>(n.s), dpp_d<CTRL>(n.c)};
+}
+
+// A lane's double and its partner's (lane ^ XOR): both words of each copy go
+// through the same permlane swap (the float helper), so the two results hold
+// the two doubles, in some order; the node is symmetric.
+template <int XOR>
+__device__ __forceinline__ void swap_d(double v, double &a, double &b) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  float la, lb, ha, hb;
+  sv::swap_halves<XOR>(__builtin_bit_cast(float, (unsigned)u), la, lb);
+  sv::swap_halves<XOR>(__builtin_bit_cast(float, (unsigned)(u >> 32)), ha, hb);
+  a = __builtin_bit_cast(double, ((unsigned long long)__builtin_bit_cast(unsigned, ha) << 32) |
+                                     __builtin_bit_cast(unsigned, la));
+  b = __builtin_bit_cast(double, ((unsigned long long)__builtin_bit_cast(unsigned, hb) << 32) |
+                                     __builtin_bit_cast(unsigned, lb));
+}
+
+template <int XOR, bool NN>
+__device__ __forceinline__ NodeD swap_level_d(NodeD n) {
+  NodeD a, b;
+  swap_d<XOR>(n.s, a.s, b.s);
+  swap_d<XOR>(n.c, a.c, b.c);
+  return comb_d<NN>(a, b);
+}
+
+// The six cross-lane levels (lane k holds range k); every lane ends with the
+// wave's node.  The mirrors reach the sibling because the lower lanes agree.
+template <bool NN>
+__device__ __forceinline__ NodeD wave_tree_d(NodeD n) {
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR>(n));
+  n = swap_level_d<16, NN>(n);
+  return swap_level_d<32, NN>(n);
+}
+
+// E doubles from 2E floats held lane-contiguously (low word first).
+template <int E>
+__device__ __forceinline__ void floats_to_doubles(const float (&f)[2 * E], double (&d)[E]) {
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    d[i] = __builtin_bit_cast(double, ((unsigned long long)__builtin_bit_cast(unsigned, f[2 * i + 1]) << 32) |
+                                          __builtin_bit_cast(unsigned, f[2 * i]));
+}
+
+__device__ __forceinline__ void store_node_d(NodeD *dst, NodeD v) {
+  unsigned *w = reinterpret_cast<unsigned *>(dst);
+  const unsigned long long s = __builtin_bit_cast(unsigned long long, v.s);
+  const unsigned long long c = __builtin_bit_cast(unsigned long long, v.c);
+  sv::store_u32_agent(w, (unsigned)s);
+  sv::store_u32_agent(w + 1, (unsigned)(s >> 32));
+  sv::store_u32_agent(w + 2, (unsigned)c);
+  sv::store_u32_agent(w + 3, (unsigned)(c >> 32));
+}
+
+__device__ __forceinline__ NodeD load_node_d(const NodeD *src) {
+  const unsigned *w = reinterpret_cast<const unsigned *>(src);
+  const unsigned long long s = ((unsigned long long)sv::load_u32_agent(w + 1) << 32) | sv::load_u32_agent(w);
+  const unsigned long long c = ((unsigned long long)sv::load_u32_agent(w + 3) << 32) | sv::load_u32_agent(w + 2);
+  return {__builtin_bit_cast(double, s), __builtin_bit_cast(double, c)};
+}
+
+// ------------------------------------------------------------------ tree sum
+
+constexpr int S64_W = 4;                 // waves per workgroup
+constexpr int S64_EF = 32;               // floats per lane per chunk (16 doubles)
+constexpr int S64_E = S64_EF / 2;
+constexpr int S64_CHUNK = 64 * S64_E;    // doubles per chunk
+constexpr int S64_MAX_BLOCKS = 8192;
+constexpr int S64_GROUP = 64;
+constexpr int S64_COUNTER_STRIDE = 64;
+constexpr int S64_MAX_LOG2_G = 16;
+constexpr size_t S64_WS_HEADER = 256 * (1 + S64_MAX_BLOCKS / S64_GROUP);
+constexpr int64_t S64_MAX_N = 1LL << 35;
+static_assert(S64_WS_HEADER == SV_TREE_SUM_COUNTER_BYTES, "same counter layout as the float32 sum");
+
+// Each wave reduces a power-of-two run of chunks of 1024 doubles in tree
+// order (the next chunk loading meanwhile), keeps chunk nodes on a
+// binary-counter stack, and the workgroup's waves form its node; the
+// two-level ticket of the float32 sum combines the workgroups.
+template <bool VEC>
+__global__ __launch_bounds__(64 * S64_W) void k_tree_sum_f64(const double *__restrict__ x, int64_t n, int log2_g,
+                                                             NodeD *__restrict__ part,
+                                                             unsigned *__restrict__ counter,
+                                                             double *__restrict__ out) {
+  using C = sv::Chunk<S64_EF, VEC, 0, true>;
+  constexpr int LPW = sv::lds_floats_per_wave<S64_EF>();
+  __shared__ float lds[S64_W * LPW];
+  __shared__ NodeD wstack[S64_W][S64_MAX_LOG2_G + 1];
+  __shared__ NodeD slots[S64_W];
+  __shared__ unsigned is_last;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t G = 1LL << log2_g;
+  const int64_t c0 = ((int64_t)blockIdx.x * S64_W + w) * G;
+  const float *__restrict__ xf = reinterpret_cast<const float *>(x);
+  const int64_t nf = 2 * n;
+  float *const my_lds = lds + w * LPW;
+  NodeD *const st = wstack[w];
+  int sp = 0;
+
+  auto reduce = [&](const float (&raw)[S64_EF], int64_t j) {
+    float vf[S64_EF];
+    C::finish(raw, my_lds, lane, vf);
+    double v[S64_E];
+    floats_to_doubles<S64_E>(vf, v);
+    NodeD nd = lane_tree_d<LEAF_CANON_D, 0, S64_E, S64_E>(v);
+    nd = wave_tree_d<false>(nd);
+    if (lane == 0) {
+      for (int64_t k = j; k & 1; k >>= 1) nd = combine_d(st[--sp], nd);
+      st[sp++] = nd;
+    }
+  };
+  auto issue = [&](int64_t c, float (&raw)[S64_EF]) {
+    C::issue(xf + c * C::SIZE, nf - c * C::SIZE, lane, raw);
+  };
+  {
+    // every load block below is unconditional, so the wait counts stay exact
+    float ra[S64_EF], rb[S64_EF];
+    int64_t j = 0;
+    issue(c0, ra);
+    while (j + 2 < G) {
+      issue(c0 + j + 1, rb);
+      reduce(ra, j);
+      issue(c0 + j + 2, ra);
+      reduce(rb, j + 1);
+      j += 2;
+    }
+    if (j + 1 < G) {
+      issue(c0 + j + 1, rb);
+      reduce(ra, j);
+      reduce(rb, j + 1);
+    } else {
+      reduce(ra, j);
+    }
+  }
+  if (lane == 0) slots[w] = st[0];
+  __syncthreads();
+
+  const int nb = (int)gridDim.x;
+  const int grp = (int)blockIdx.x / S64_GROUP;
+  const int ngroups = (nb + S64_GROUP - 1) / S64_GROUP;
+  const int in_group = (grp == ngroups - 1) ? nb - grp * S64_GROUP : S64_GROUP;
+  unsigned *const top_counter = counter;
+  unsigned *const grp_counter = counter + S64_COUNTER_STRIDE * (1 + grp);
+  NodeD *const grp_nodes = part + S64_MAX_BLOCKS;
+  if (threadIdx.x == 0) {
+    NodeD nd[S64_W];
+#pragma unroll
+    for (int i = 0; i < S64_W; ++i) nd[i] = slots[i];
+    store_node_d(part + blockIdx.x, node_tree_d<0, S64_W, S64_W, false>(nd));
+    sv::wait_vmem_stores();
+    const unsigned ticket = __hip_atomic_fetch_add(grp_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (ticket == (unsigned)in_group - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!is_last || w != 0) return;
+  {
+    const int idx = grp * S64_GROUP + lane;
+    NodeD g = (idx < nb) ? load_node_d(part + idx) : NodeD{0.0, 0.0};
+    g = wave_tree_d<false>(g);
+    unsigned top_ticket = 0;
+    if (lane == 0) {
+      __hip_atomic_store(grp_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      store_node_d(grp_nodes + grp, g);
+      sv::wait_vmem_stores();
+      top_ticket = __hip_atomic_fetch_add(top_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    top_ticket = __builtin_amdgcn_readfirstlane(top_ticket);
+    if (top_ticket != (unsigned)ngroups - 1) return;
+  }
+  constexpr int GPL = S64_MAX_BLOCKS / S64_GROUP / 64;
+  NodeD t[GPL];
+#pragma unroll
+  for (int k = 0; k < GPL; ++k) {
+    const int idx = GPL * lane + k;
+    t[k] = (idx < ngroups) ? load_node_d(grp_nodes + idx) : NodeD{0.0, 0.0};
+  }
+  const NodeD r = wave_tree_d<false>(node_tree_d<0, GPL, GPL, false>(t));
+  if (lane == 0) {
+    out[0] = root_value_d(r);
+    __hip_atomic_store(top_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ void k_zero_d(double *out) { out[0] = 0.0; }
+
+// ------------------------------------------------------------------ variance
+
+__device__ __forceinline__ double max0_nan_d(double v) { return (v != v) ? v : ((v > 0.0) ? v : 0.0); }
+
+__device__ __forceinline__ void finalize_d(NodeD nd, NodeD nq, double x0, double m, int64_t n, int64_t ddof,
+                                           double *var_out, double *mean_out) {
+  const double fn = (double)n;
+  const double a = root_value_d(nq) / fn;
+  const double b = root_value_d(nd) / fn;
+  double v = max0_nan_d(a - b * b);
+  if (ddof != 0) {
+    int64_t den = n - ddof;
+    if (den < 0) den = 0;
+    v = v * (fn / (double)den);
+  }
+  *var_out = v;
+  if (mean_out) *mean_out = x0 + m;
+}
+
+// Axis 1: one workgroup per row, W waves own consecutive 64*E ranges, each
+// lane E consecutive doubles; the row stays in registers between passes.
+template <int E, int W, bool VEC>
+__global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restrict__ x, int64_t n, int64_t ld,
+                                                         int64_t ddof, double *__restrict__ var_out,
+                                                         double *__restrict__ mean_out) {
+  __shared__ NodeD slots[3][W];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
+  const double *__restrict__ p = x + row * ld;
+  const int64_t base = (int64_t)w * 64 * E;
+
+  float vf[2 * E];
+  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(p + base), 2 * (n - base), nullptr, vf, lane);
+  double v[E];
+  floats_to_doubles<E>(vf, v);
+  const double x0 = p[0];
+
+  const bool full = base + 64 * E <= n;
+  const int64_t left = n - base - (int64_t)lane * E;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0;
+  }
+
+  NodeD ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
+  if constexpr (W > 1) {
+    if (lane == 0) slots[0][w] = ny;
+    __syncthreads();
+    NodeD t[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) t[i] = slots[0][i];
+    ny = node_tree_d<0, W, W, false>(t);
+  }
+  const double m = root_value_d(ny) / (double)n;
+
+  NodeD nd, nq;
+  if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
+  else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
+  nd = wave_tree_d<false>(nd);
+  nq = wave_tree_d<true>(nq);
+  if constexpr (W > 1) {
+    if (lane == 0) {
+      slots[1][w] = nd;
+      slots[2][w] = nq;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    NodeD td[W], tq[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      td[i] = slots[1][i];
+      tq[i] = slots[2][i];
+    }
+    nd = node_tree_d<0, W, W, false>(td);
+    nq = node_tree_d<0, W, W, true>(tq);
+  }
+  if (threadIdx.x == 0) finalize_d(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+}
+
+// Axis 0: lanes own columns (a row of 64 consecutive doubles per load), the
+// W waves own consecutive blocks of E rows; levels below the cross-wave ones
+// are in-lane.
+template <int E, int W>
+__global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restrict__ x, int64_t R, int64_t C,
+                                                         int64_t ddof, double *__restrict__ var_out,
+                                                         double *__restrict__ mean_out) {
+  __shared__ NodeD sy[W][64];
+  __shared__ NodeD sd[W][64];
+  __shared__ NodeD sq[W][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const bool colok = col < C;
+  const int64_t r0 = (int64_t)w * E;
+  const bool full = r0 + E <= R;
+  const int64_t ccol = colok ? col : C - 1;
+  double v[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t r = r0 + i;
+    const double t = x[(r < R ? r : R - 1) * C + ccol];
+    v[i] = (colok && r < R) ? t : 0.0;
+  }
+  const double x0 = x[ccol];
+  const int64_t left = R - r0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0;
+  }
+  NodeD ny = lane_tree_d<LEAF_FAST_D, 0, E, E>(v);
+  sy[w][lane] = ny;
+  __syncthreads();
+  {
+    NodeD nn[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) nn[i] = sy[i][lane];
+    ny = node_tree_d<0, W, W, false>(nn);
+  }
+  const double m = root_value_d(ny) / (double)R;
+  NodeD nd, nq;
+  if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
+  else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
+  sd[w][lane] = nd;
+  sq[w][lane] = nq;
+  __syncthreads();
+  if (w == 0 && colok) {
+    NodeD a[W], b[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      a[i] = sd[i][lane];
+      b[i] = sq[i][lane];
+    }
+    finalize_d(node_tree_d<0, W, W, false>(a), node_tree_d<0, W, W, true>(b), x0, m, R, ddof, var_out + col,
+               mean_out ? mean_out + col : nullptr);
+  }
+}
+
+__global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) {
+    a[i] = __builtin_nan("");
+    if (b) b[i] = __builtin_nan("");
+  }
+}
+
+constexpr int64_t V64_ROWS_MAX_N = 8192;
+constexpr int64_t V64_COLS_MAX_R = 1024;
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_tree_sum_f64_workspace_size(int64_t n) {
+  if (n < 0 || n > S64_MAX_N) return (size_t)-1;
+  if (n == 0) return 0;
+  return S64_WS_HEADER + (size_t)(S64_MAX_BLOCKS + S64_MAX_BLOCKS / S64_GROUP) * sizeof(NodeD);
+}
+
+sv_status sv_tree_sum_f64(const double *x, int64_t n, double *out, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f64: n = %lld < 0", (long long)n);
+  if (n > S64_MAX_N) return fail(SV_ERR_UNSUPPORTED, "sv_tree_sum_f64: n = %lld above 2^35", (long long)n);
+  if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f64: out is NULL");
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f64: x is NULL with n > 0");
+  if (reinterpret_cast<uintptr_t>(x) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_tree_sum_f64: x is not 8-byte aligned");
+  const size_t need = sv_tree_sum_f64_workspace_size(n);
+  if (n > 0) {
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f64: workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f64: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!svh::aligned256(workspace)) return fail(SV_ERR_WORKSPACE, "sv_tree_sum_f64: workspace is not 256-byte aligned");
+  }
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (n == 0) {
+    k_zero_d<<<1, 1, 0, st>>>(out);
+    return check_launch("sv_tree_sum_f64");
+  }
+  const int64_t chunks = (n + S64_CHUNK - 1) / S64_CHUNK;
+  const int64_t wgs = (chunks + S64_W - 1) / S64_W;
+  int g = 0;
+  while (g < S64_MAX_LOG2_G && ((wgs + (1LL << g) - 1) >> g) > S64_MAX_BLOCKS) ++g;
+  const int64_t blocks = (wgs + (1LL << g) - 1) >> g;
+  unsigned *counter = reinterpret_cast<unsigned *>(workspace);
+  NodeD *part = reinterpret_cast<NodeD *>(reinterpret_cast<char *>(workspace) + S64_WS_HEADER);
+  const dim3 grid((unsigned)blocks), block(64 * S64_W);
+  if (svh::aligned16(x)) k_tree_sum_f64<true><<<grid, block, 0, st>>>(x, n, g, part, counter, out);
+  else k_tree_sum_f64<false><<<grid, block, 0, st>>>(x, n, g, part, counter, out);
+  return check_launch("sv_tree_sum_f64");
+}
+
+sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, double *var_out,
+                          double *mean_out, void *stream) {
+  if (rows < 0 || cols < 0)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: negative shape [%lld, %lld]", (long long)rows,
+                (long long)cols);
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2)
+    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: axis %d not in {0, 1, -1, -2}", axis);
+  if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: ddof = %lld < 0", (long long)ddof);
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t nslices = ax1 ? rows : cols;
+  const int64_t n = ax1 ? cols : rows;
+  if (nslices == 0) return ok();
+  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: var_out is NULL");
+  if (rows * cols > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is NULL");
+  if (reinterpret_cast<uintptr_t>(x) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is not 8-byte aligned");
+  if ((ax1 && n > V64_ROWS_MAX_N) || (!ax1 && n > V64_COLS_MAX_R) || nslices > (int64_t)UINT32_MAX)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: slices of %lld values along axis %d are not supported "
+                "(at most %lld on axis 1, %lld on axis 0)", (long long)n, ax1 ? 1 : 0,
+                (long long)V64_ROWS_MAX_N, (long long)V64_COLS_MAX_R);
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (n == 0) {
+    k_fill_nan_d<<<dim3((unsigned)((nslices + 255) / 256)), dim3(256), 0, st>>>(var_out, mean_out, nslices);
+    return check_launch("sv_variance_f64");
+  }
+  if (ax1) {
+    const bool vec = svh::aligned16(x) && (cols % 2 == 0);
+    const dim3 grid((unsigned)rows);
+#define SV_ROWS64(E, W)                                                                                      \
+  do {                                                                                                       \
+    if (vec) k_var_rows_f64<E, W, true><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var_out, mean_out); \
+    else k_var_rows_f64<E, W, false><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var_out, mean_out);    \
+  } while (0)
+    if (n <= 256) SV_ROWS64(4, 1);
+    else if (n <= 1024) SV_ROWS64(16, 1);
+    else if (n <= 4096) SV_ROWS64(16, 4);
+    else SV_ROWS64(16, 8);
+#undef SV_ROWS64
+  } else {
+    const dim3 grid((unsigned)((cols + 63) / 64));
+#define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)
+    if (n <= 4) SV_COLS64(4, 1);
+    else if (n <= 16) SV_COLS64(16, 1);
+    else if (n <= 64) SV_COLS64(16, 4);
+    else if (n <= 256) SV_COLS64(16, 16);
+    else if (n <= 512) SV_COLS64(32, 16);
+    else SV_COLS64(64, 16);
+#undef SV_COLS64
+  }
+  return check_launch("sv_variance_f64");
+}
+
+}  // extern "C"

@@ -62,15 +62,16 @@ def test_no_scalar_memory_writes(asm):
 
 def test_division_is_correctly_rounded_and_fma_only_inside_it(asm):
     ks = kernels(asm)
-    var = [b for n, (b, _) in ks.items() if "k_var_rows" in n or "k_var_cols" in n]
+    var = [(n, b) for n, (b, _) in ks.items() if ("k_var_rows" in n or "k_var_cols" in n)]
     assert var
-    for body in var:
+    for n, body in var:
+        t = "f64" if "_f64" in n else "f32"
         # the IEEE division sequence (scale, Newton steps, fmas, fixup)
-        assert "v_div_fixup_f32" in body and "v_div_scale_f32" in body
-        # every FMA belongs to a division: at most 5 per division sequence
-        nfma = len(re.findall(r"\bv_fmac?_f32", body))
-        ndiv = len(re.findall(r"\bv_div_fixup_f32", body))
-        assert nfma <= 5 * ndiv, (nfma, ndiv)
+        assert f"v_div_fixup_{t}" in body and f"v_div_scale_{t}" in body, n
+        # every FMA belongs to a division: at most 5 (f32) or 6 (f64) per sequence
+        nfma = len(re.findall(r"\bv_fmac?_f(32|64)", body))
+        ndiv = len(re.findall(r"\bv_div_fixup_f(32|64)", body))
+        assert nfma <= (6 if t == "f64" else 5) * ndiv, (n, nfma, ndiv)
     for n, (body, _) in ks.items():
         if "k_tree_sum" in n or "k_adn_sum" in n:
             # the sums divide nothing; the ADN conversion's double adds stay unfused

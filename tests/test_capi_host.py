@@ -131,6 +131,24 @@ def test_adn_sizes_and_argument_errors(L):
     assert L.sv_set_tuning(b"reset", 0) == 0
 
 
+def test_f64_sizes_and_argument_errors(L):
+    # same counter header as the float32 sum, 16-byte nodes
+    assert L.sv_tree_sum_f64_workspace_size(0) == 0
+    assert L.sv_tree_sum_f64_workspace_size(10 ** 8) == 33024 + 16 * (8192 + 128)
+    assert L.sv_tree_sum_f64_workspace_size((1 << 35) + 1) == ctypes.c_size_t(-1).value
+    assert L.sv_tree_sum_f64(BAD, -1, BAD, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_tree_sum_f64(ctypes.c_void_p(0x1004), 10, BAD, ctypes.c_void_p(0x100000), 1 << 20, None) == \
+        SV_ERR_INVALID_ARGUMENT  # not 8-byte aligned
+    assert L.sv_tree_sum_f64(BAD, 10, BAD, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_tree_sum_f64(BAD, (1 << 35) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
+    out = ctypes.c_void_p(0x2000)
+    assert L.sv_variance_f64(BAD, 4, 4, 3, 0, out, None, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f64(BAD, 4, 4, 1, -1, out, None, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f64(BAD, 2, 8193, 1, 0, out, None, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_variance_f64(BAD, 1025, 2, 0, 0, out, None, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_variance_f64(None, 0, 5, 1, 0, None, None, None) == 0
+
+
 def test_complex_argument_errors_and_sizes(L):
     out = ctypes.c_void_p(0x2000)
     # axis 0: per-component variances (2*cols floats) + the float view's own workspace (0 here)
@@ -176,7 +194,7 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(TypeError):
         sv.tree_sum([1.0, 2.0])
     with pytest.raises(TypeError):
-        sv.var(torch.zeros(3, 3, dtype=torch.float64))
+        sv.var(torch.zeros(3, 3, dtype=torch.float16))
     with pytest.raises(ValueError):
         sv.var(torch.zeros(3, 3))  # CPU tensor: no fallback
 

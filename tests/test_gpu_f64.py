@@ -1,0 +1,129 @@
+"""GPU parity of the float64 path (the method with every operation in
+double) against the binary64 oracle: bit-exact, NaN as NaN."""
+import numpy as np
+import pytest
+import torch  # noqa: F401  (imported at collection: the first import is slow on a fresh box)
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from stable_variance_amd import build as libbuild
+
+    if libbuild.is_stale():
+        libbuild.build()
+    return torch, torch.device("cuda:0")
+
+
+def same_bits64(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    if a.shape != b.shape:
+        return False
+    nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(nan | (a.view(np.uint64) == b.view(np.uint64))))
+
+
+def gpu_sum64(torch_dev, x, offset=0):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    x = np.ascontiguousarray(x, np.float64)
+    if offset:
+        buf = torch.zeros(x.size + offset, dtype=torch.float64, device=dev)
+        buf[offset:] = torch.from_numpy(x).to(dev)
+        t = buf[offset:]
+    else:
+        t = torch.from_numpy(x).to(dev)
+    r = sv.tree_sum(t)
+    torch.cuda.synchronize()
+    return np.float64(r.item())
+
+
+def check_var64(torch_dev, a, axis, ddof=0):
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    v, m = sv.var(torch.from_numpy(np.ascontiguousarray(a, np.float64)).to(dev), dim=axis, ddof=ddof,
+                  return_mean=True)
+    torch.cuda.synchronize()
+    ov, om = oracle.variance_f64(a, axis=axis, ddof=ddof)
+    v, m = v.cpu().numpy(), m.cpu().numpy()
+    assert same_bits64(v, ov), (a.shape, axis, ddof, np.flatnonzero(v.view(np.uint64) != ov.view(np.uint64))[:5])
+    assert same_bits64(m, om), (a.shape, axis, ddof)
+    return v
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 1023, 1024, 1025, 4096 + 3, 65537, 1_000_003])
+def test_sum64_sizes(torch_dev, n):
+    rng = np.random.default_rng(n)
+    for x in (rng.standard_normal(n) * np.exp2(rng.integers(-300, 300, n)),
+              W.adversarial_values(n, seed=n).astype(np.float64),
+              W.sum_cancelling_pairs(n, 0.3, seed=n).astype(np.float64) * 1e200):
+        want = oracle.tree_sum_f64(x)
+        assert same_bits64(gpu_sum64(torch_dev, x), want), n
+        assert same_bits64(gpu_sum64(torch_dev, x, offset=1), want), (n, "8-byte aligned only")
+
+
+def test_sum64_specials_and_large(torch_dev):
+    rng = np.random.default_rng(40)
+    base = rng.standard_normal(100_000)
+    for extra in ([np.inf], [np.inf, -np.inf], [np.nan], [1.7e308, 1.7e308]):
+        x = np.concatenate([base, np.array(extra)])
+        assert same_bits64(gpu_sum64(torch_dev, x), oracle.tree_sum_f64(x)), extra
+    x = rng.standard_normal(30_000_000)
+    assert same_bits64(gpu_sum64(torch_dev, x), oracle.tree_sum_f64(x))
+
+
+def test_var64_page_datasets_and_square(torch_dev):
+    for name, a, axis, _ in W.datasets_d1_d4():
+        check_var64(torch_dev, a.astype(np.float64), axis)
+        check_var64(torch_dev, a.astype(np.float64), axis, 1)
+    check_var64(torch_dev, W.c4_matrix().astype(np.float64)[:1024], 1)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 64, 255, 256, 257, 1000, 1024, 1025, 4095, 4096, 4097, 8192])
+def test_var64_rows(torch_dev, n):
+    rng = np.random.default_rng(n)
+    a = rng.normal(1e8, 3, (19, n))
+    check_var64(torch_dev, a, 1)
+    check_var64(torch_dev, a, 1, 2)
+    b = W.adversarial_values(19 * n, n).astype(np.float64).reshape(19, n) * 1e250
+    check_var64(torch_dev, b, 1)
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 512, 513, 1000, 1024])
+def test_var64_cols(torch_dev, R):
+    rng = np.random.default_rng(R)
+    for C in (1, 63, 64, 65, 130):
+        a = rng.normal(-5e3, 2, (R, C))
+        check_var64(torch_dev, a, 0)
+        check_var64(torch_dev, a, 0, 1)
+
+
+def test_var64_top_of_range_and_specials(torch_dev):
+    # float64 [1e307]*3 (the page's "not measured" case): the method gives 0
+    for c in (1e307, 1e308, -1.7e308):
+        v = check_var64(torch_dev, np.full((2, 3), c), 1)
+        assert np.all(v == 0.0)
+    a = np.random.default_rng(41).normal(0, 1, (6, 500))
+    a[0, 7] = np.nan
+    a[1, 9] = np.inf
+    a[2, 3] = np.inf
+    a[2, 4] = -np.inf
+    a[3, :] = 1.7e308 * np.sign(np.random.default_rng(42).standard_normal(500))
+    check_var64(torch_dev, a, 1)
+    check_var64(torch_dev, np.ascontiguousarray(a.T), 0)
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    v = sv.var(torch.zeros((3, 0), dtype=torch.float64, device=dev), dim=1)
+    assert torch.isnan(v).all()
