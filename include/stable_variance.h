@@ -114,13 +114,20 @@ sv_status sv_tree_sum_dw_f32(const float *x, int64_t n, float *out, void *worksp
                              void *stream);
 
 /*
- * Bytes of workspace sv_variance_f32 needs: 0 when every slice fits one
- * workgroup (axis 1: n <= 16384 values; axis 0: n <= 1024 values), else
- * 24 bytes per 16384-value (axis 1) or 1024-value (axis 0) chunk of every
- * slice plus 4 bytes per slice (long slices are reduced in chunks, reading
- * the input twice).  (size_t)-1 for an unsupported shape (a slice of more
- * than 8192 chunks, a bad axis, rows * cols >= 2^40).  The workspace must be
- * 256-byte aligned and needs no initialisation.
+ * Bytes of workspace sv_variance_f32 needs.
+ *   axis 1: 0 when every row fits one workgroup (n <= 16384 values), else 24
+ *           bytes per 16384-value chunk of every row plus 4 bytes per row
+ *           (long rows are reduced in chunks, reading the input twice).
+ *   axis 0: whenever rows and cols are both nonzero: three arrays of 8
+ *           bytes per 64-row chunk per column and 4 bytes per column, each
+ *           rounded up to 256 bytes.  Columns longer than one workgroup holds
+ *           (by default more than 1024 rows) are reduced in row chunks,
+ *           reading the input twice; the size does not depend on the tuning
+ *           knobs.
+ * (size_t)-1 for an unsupported shape (an axis-1 row of more than 8192
+ * chunks, a bad axis, rows * cols >= 2^40).  The workspace must be 256-byte
+ * aligned; it is scratch (no initialisation, nothing kept between calls), so
+ * calls that share one must be ordered on one stream.
  */
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
 
@@ -144,8 +151,8 @@ size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
  *   mean_out   may be NULL (the mean is then not written)
  *   workspace  device buffer of sv_variance_f32_workspace_size(...) bytes;
  *              may be NULL when that size is 0
- * rows and cols must be >= 0 with rows * cols < 2^40; a slice may hold at
- * most 8192 chunks (axis 1: 134,217,728 values; axis 0: 8,388,608 values).
+ * rows and cols must be >= 0 with rows * cols < 2^40; an axis-1 row may hold
+ * at most 8192 chunks (134,217,728 values).
  */
 sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
                           float *var_out, float *mean_out, void *workspace, size_t workspace_bytes,
@@ -287,11 +294,24 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    (default), 2, 4 or 8
  *   "var_dma_rows"   rows of 1025..4096 values per wave staged by direct
  *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
- *   "var_split"      waves sharing one row of 1025..4096 values: 1, 2, 4
- *                    (default) or 8 (64, 32, 16 or 8 values per lane)
+ *   "var_split"      rows of 1025..16384 values: waves per 4096 values of
+ *                    the row's power-of-two tile, 1, 2 (default), 4 or 8
+ *                    (64, 32, 16 or 8 values per lane; a 2048-value tile
+ *                    takes at most 32 values per lane, a 16384-value tile at
+ *                    most 16 waves)
  *   "var_lds_pad"    unused dynamic LDS bytes per row workgroup, 0..65536
  *                    (default 0): a cap on resident waves, for measurements
- *   "adn_e"          values per lane in an ADN-sum chunk: 16 (default) or 32
+ *   "var_cols_single_max"  axis 0: columns of up to this many rows are
+ *                    held by one workgroup and read once (0..1024, default
+ *                    1024); longer columns are reduced in row chunks
+ *   "var_cols_waves" axis 0, chunked: waves per workgroup, 4, 8 or 16
+ *                    (default): chunks of 64, 128 or 256 rows
+ *   "sum_xcd"        tree sum: 1 = renumber the workgroups so that each of the
+ *                    eight dies (XCDs) streams one contiguous region; 0 =
+ *                    dispatch order, consecutive regions spread over the dies
+ *                    (default, faster on MI355X)
+ *   "var_xcd"        row variance: as sum_xcd, over rows (default 0)
+ *   "adn_e"         values per lane in an ADN-sum chunk: 16 (default) or 32
  *                    (32 only with three folds; other counts use 16)
  *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)
  *   "reset"          any value: restore every default

@@ -107,8 +107,9 @@ def set_tuning(key: str, value: int) -> None:
 
 # Workspaces, one per (kind, device, stream).  The tree sum's buffer is
 # zero-filled when allocated and the library leaves its ticket counters at
-# zero after every call; the variance's buffer is scratch.  They are never
-# shared: scratch use would leave nonzero counters behind.
+# zero after every call; the variance's buffer is scratch (its axis-0 ticket
+# counters are cleared inside every call).  They are never shared: scratch
+# use would leave nonzero counters behind in a sum workspace.
 _workspaces: dict = {}
 
 

@@ -36,6 +36,19 @@ struct Node {
   float c;  // carried rounding errors
 };
 
+// ---------------------------------------------------------------- launch order
+
+// The eight dies (XCDs) of the chip take a grid's workgroups round robin in
+// dispatch order: workgroup b runs on die b mod 8.  xcd_contiguous renumbers
+// the grid so that each die's workgroups get one contiguous run of logical
+// indices (die x takes the x-th run, the first nb mod 8 runs one longer), so
+// a die streams one region of the buffer.  A bijection of [0, nb): results
+// depend only on logical indices, so the renumbering changes no bit.
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, die = b & 7, i = b >> 3;
+  return (die < r ? die * (q + 1) : r * (q + 1) + (die - r) * q) + i;
+}
+
 // ---------------------------------------------------------------- nodes
 
 // TwoSum of the two partial sums, the error added to the sum of the carries.
@@ -379,10 +392,12 @@ constexpr int lds_floats_staged() { return 16 * (E + 4); }
 //          chunks, or 64 consecutive floats when !VEC), transposed through
 //          this wave's LDS region into lane-contiguous order.
 // LOADP 1: each lane loads its own E contiguous values directly.
-// VEC: 16-byte loads, p must be 16-byte aligned.
+// VEC: 16-byte loads; p must be 16-byte aligned and len, when below the
+// tile, a multiple of 4.
 // A wave whose tile lies entirely inside the data takes a branch-free path;
-// a ragged tile (the slice's last) loads single floats at addresses clamped
-// to [0, len); a tile entirely beyond the data loads nothing.
+// a ragged tile (the slice's last) loads at addresses clamped to [0, len)
+// (whole 16-byte groups when VEC, single floats otherwise); a tile entirely
+// beyond the data loads nothing.
 typedef float sv_v4f __attribute__((ext_vector_type(4)));
 
 // 16-byte and 4-byte loads; NT marks them non-temporal (streamed data that
@@ -464,6 +479,18 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
           for (int t = 0; t < 4; ++t) v[4 * j + t] = ld1<NT>(p + e0 + 4 * j + t);
         }
       }
+    } else if constexpr (VEC) {
+      // lim is a multiple of 4 (16-byte aligned rows of a multiple of 4
+      // values), so each 16-byte group is wholly inside or wholly beyond the
+      // data: clamped 16-byte loads, every one issued
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int e = e0 + 4 * j;
+        const float4 g = ld4<NT>(p + (e < lim ? e : lim - 4));
+        const bool in = e < lim;
+        v[4 * j] = in ? g.x : 0.0f; v[4 * j + 1] = in ? g.y : 0.0f;
+        v[4 * j + 2] = in ? g.z : 0.0f; v[4 * j + 3] = in ? g.w : 0.0f;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < E; ++i) {
@@ -473,7 +500,22 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
       }
     }
   } else {
-    if (full && VEC) {
+    if (VEC && !full) {
+      // as above: whole 16-byte groups, clamped, then the same transpose
+      float4 g[J];
+#pragma unroll
+      for (int k = 0; k < J; ++k) {
+        const int e = 256 * k + 4 * lane;
+        const float4 t = ld4<NT>(p + (e < lim ? e : lim - 4));
+        const bool in = e < lim;
+        g[k] = make_float4(in ? t.x : 0.0f, in ? t.y : 0.0f, in ? t.z : 0.0f, in ? t.w : 0.0f);
+      }
+#pragma unroll
+      for (int k = 0; k < J; ++k) {
+        const int e = 256 * k + 4 * lane;
+        *reinterpret_cast<float4 *>(lds + (e / E) * STR + (e % E)) = g[k];
+      }
+    } else if (full && VEC) {
       float4 g[J];
 #pragma unroll
       for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + 256 * k + 4 * lane);

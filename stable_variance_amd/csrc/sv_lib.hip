@@ -251,7 +251,7 @@ constexpr size_t SUM_WS_HEADER = 256 * (1 + SUM_MAX_BLOCKS / SUM_GROUP);
 template <int E, int W, bool VEC, int LOADP, bool NT, int D, int KIND = sv::NODE_TWOSUM>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_MINW, 8))) void k_tree_sum(const float *__restrict__ x, int64_t n, int log2_g,
                                                      Node *__restrict__ part, unsigned *__restrict__ counter,
-                                                     float *__restrict__ out) {
+                                                     float *__restrict__ out, int xcd) {
   using C = sv::Chunk<E, VEC, LOADP, NT>;
   constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
   __shared__ float lds[W * LPW];
@@ -262,7 +262,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t G = 1LL << log2_g;
-  const int64_t c0 = ((int64_t)blockIdx.x * W + w) * G;  // first chunk of this wave
+  const int nb = (int)gridDim.x;
+  const int bid = xcd ? sv::xcd_contiguous((int)blockIdx.x, nb) : (int)blockIdx.x;  // logical workgroup
+  const int64_t c0 = ((int64_t)bid * W + w) * G;  // first chunk of this wave
   float *const my_lds = lds + w * LPW;
   Node *const st = wstack[w];
   int sp = 0;  // meaningful in lane 0
@@ -315,8 +317,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
   // needed; waiting for the stores' completion (vmcnt 0) before the ticket
   // increment orders the two.  An agent-scope release fence would instead
   // write back the whole L2 of the XCD for every workgroup.
-  const int nb = (int)gridDim.x;
-  const int grp = (int)blockIdx.x / SUM_GROUP;
+  const int grp = bid / SUM_GROUP;
   const int ngroups = (nb + SUM_GROUP - 1) / SUM_GROUP;
   const int in_group = (grp == ngroups - 1) ? nb - grp * SUM_GROUP : SUM_GROUP;
   unsigned *const top_counter = counter;
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
     Node nd[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nd[i] = slots[i];
-    store_node_agent(part + blockIdx.x, sv::node_tree<0, W, W, KIND>(nd));
+    store_node_agent(part + bid, sv::node_tree<0, W, W, KIND>(nd));
     wait_vmem_stores();
     const unsigned ticket = __hip_atomic_fetch_add(grp_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (ticket == (unsigned)in_group - 1) ? 1u : 0u;
@@ -425,7 +426,8 @@ __global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
 
 template <int E, int W, bool VEC, int LOADP, bool NT, int V = V_KERNEL>
 __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t ddof,
-                                                     float *__restrict__ var_out, float *__restrict__ mean_out) {
+                                                     float *__restrict__ var_out, float *__restrict__ mean_out,
+                                                     int xcd) {
   using F = VariantFlags<V>;
   constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : (LOADP == 2) ? sv::lds_floats_staged<E>() : 1;
   __shared__ float lds[W * LPW];
@@ -434,10 +436,14 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int vl = sv::vlane_pair32(lane);  // this lane holds the range of virtual lane vl
-  const int64_t row = blockIdx.x;
+  const int64_t row = xcd ? sv::xcd_contiguous((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
   const float *__restrict__ p = x + row * ld;
   const int64_t base = (int64_t)w * 64 * E;
 
+  // A wave whose range lies wholly beyond the row holds only padding: its
+  // nodes are (+0, +0), which is what its trees would compute, so it skips
+  // them (the branch is wave-uniform).
+  const bool empty = base >= n;
   float v[E];
   sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, vl);
   const float x0 = p[0];
@@ -457,8 +463,11 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   }
 
   // step 2: m = Tree(y) / n
-  Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-  ny = sv::wave_tree_p32<sv::NODE_TWOSUM>(ny);
+  Node ny = sv::zero_node();
+  if (!empty) {
+    ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+    ny = sv::wave_tree_p32<sv::NODE_TWOSUM>(ny);
+  }
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
@@ -471,12 +480,14 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
 
   // step 3: Tree(d), Tree(d^2): lanes 0..31 end with the wave's d node,
   // lanes 32..63 with its d^2 node
-  Node nd, nq;
-  if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
-  else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-  const Node ndq = sv::wave_tree_dq(nd, nq);
-  nd = {sv::readlane_f(ndq.s, 0), sv::readlane_f(ndq.c, 0)};
-  nq = {sv::readlane_f(ndq.s, 32), sv::readlane_f(ndq.c, 32)};
+  Node nd = sv::zero_node(), nq = sv::zero_node();
+  if (!empty) {
+    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+    const Node ndq = sv::wave_tree_dq(nd, nq);
+    nd = {sv::readlane_f(ndq.s, 0), sv::readlane_f(ndq.c, 0)};
+    nq = {sv::readlane_f(ndq.s, 32), sv::readlane_f(ndq.c, 32)};
+  }
   if constexpr (W > 1) {
     // one LDS round for both trees (their slots are not reused: no second barrier)
     if (lane == 0) {
@@ -731,19 +742,251 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
   }
 }
 
+// ------------------------------------------------------------------ variance, axis 0, chunked
+
+// Axis 0 with the column's rows cut into chunks of CH = E*W rows (aligned
+// nodes of the column's tree).  A workgroup owns one chunk of a block of
+// 64*V adjacent columns: lane L holds columns [V*L, V*L + V) of the block (one
+// 16-byte load per row when V = 4, so a wave reads 1 KiB of each row) for the
+// E consecutive rows of its wave, and wave w owns rows [w*E, (w+1)*E) of the
+// chunk.  Three or four launches, ordered by the stream (each reads what the
+// previous ones wrote; the workspace is scratch):
+//   k_cols_y    the y-tree node of every (chunk, column)
+//   k_cols_m    per column m = Tree(y)/n, the tree over its chunk nodes (for
+//               at most 32 chunks per column each k_cols_dq workgroup forms
+//               the m of its own columns instead, and this launch is skipped)
+//   k_cols_dq   the tile read again (mostly from the chip's last-level cache
+//               when the input fits in it): the d- and d^2-tree node of
+//               every (chunk, column)
+//   k_cols_fin  per column the trees over its d and d^2 chunk nodes, step 4
+
+constexpr int CC_E = 16;             // rows per lane in a chunk
+constexpr int CC_MIN_W = 4;          // the workspace is sized for the shortest chunk
+constexpr int CC_GROUP = 32;         // chunk nodes per group of the per-column trees
+
+struct ColsWs {
+  Node *ny;  // [nch][C] y-tree node of each chunk of each column
+  Node *nd;  // [nch][C] d-tree nodes
+  Node *nq;  // [nch][C] d^2-tree nodes
+  float *m;  // [C]
+};
+
+// Loads rows [r0, r0 + E) of the V columns starting at c0 (c0 a multiple of
+// V).  Columns past C read the last in-range columns instead (their results
+// are never written); rows past R read row R-1 (masked to +0 afterwards).
+template <int V, int E>
+__device__ __forceinline__ void load_cols_tile(const float *__restrict__ x, int64_t R, int64_t C, int64_t c0,
+                                               int64_t r0, bool full, float (&v)[V][E]) {
+  const int64_t cc = c0 < C ? c0 : C - V;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t r = full ? r0 + i : (r0 + i < R ? r0 + i : R - 1);
+    const float *p = x + r * C + cc;
+    if constexpr (V == 4) {
+      const float4 g = *reinterpret_cast<const float4 *>(p);
+      v[0][i] = g.x;
+      v[1][i] = g.y;
+      v[2][i] = g.z;
+      v[3][i] = g.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k][i] = p[k];
+    }
+  }
+}
+
+// Step 1 on a tile: y = x - x0, and +0 for rows past the slice.
+template <int V, int E>
+__device__ __forceinline__ void shift_cols_tile(float (&v)[V][E], const float (&x0)[V], bool full, int valid) {
+#pragma unroll
+  for (int k = 0; k < V; ++k)
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[k][i] = (full || i < valid) ? v[k][i] - x0[k] : 0.0f;
+}
+
+// Tree over p[0], p[stride], ..., p[(count-1)*stride] padded with zero nodes
+// to a power of two: aligned groups of CC_GROUP nodes level by level, each
+// group node written back in place of the group's first node.  One thread
+// per column.
+template <int KIND>
+__device__ Node chunk_tree(Node *p, int64_t stride, int64_t count) {
+  while (true) {
+    const int64_t groups = (count + CC_GROUP - 1) / CC_GROUP;
+    Node last = sv::zero_node();
+    for (int64_t g = 0; g < groups; ++g) {
+      Node sub[CC_GROUP / 8];
+#pragma unroll
+      for (int b = 0; b < CC_GROUP / 8; ++b) {
+        Node nd[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // every load is issued (an index past the end reads the last node),
+          // so the group's loads are in flight together
+          const int64_t idx = g * CC_GROUP + b * 8 + k;
+          const Node t = p[(idx < count ? idx : count - 1) * stride];
+          nd[k] = idx < count ? t : sv::zero_node();
+        }
+        sub[b] = sv::node_tree<0, 8, 8, KIND>(nd);
+      }
+      last = sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8, KIND>(sub);
+      if (groups > 1) p[g * stride] = last;
+    }
+    if (groups == 1) return last;
+    count = groups;
+  }
+}
+
+template <int V, int W>
+__global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                   ColsWs ws) {
+  constexpr int E = CC_E, NC = 64 * V;
+  static_assert(64 * W >= NC, "one thread per column of the block");
+  __shared__ Node s[W][V][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t c0 = cb * NC + (int64_t)lane * V;
+  const int64_t r0 = j * (E * W) + (int64_t)w * E;
+  const bool full = r0 + E <= R;
+  const int64_t left = R - r0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+
+  float v[V][E];
+  load_cols_tile<V, E>(x, R, C, c0, r0, full, v);
+  float x0[V];
+  const int64_t cc = c0 < C ? c0 : C - V;
+#pragma unroll
+  for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
+  shift_cols_tile<V, E>(v, x0, full, valid);
+#pragma unroll
+  for (int k = 0; k < V; ++k) s[w][k][lane] = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k]);
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < NC) {
+    const int k = t >> 6, l = t & 63;  // thread t combines column V*l + k of the block
+    const int64_t col = cb * NC + (int64_t)l * V + k;
+    if (col < C) {
+      Node nn[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) nn[i] = s[i][k][l];
+      ws.ny[j * C + col] = sv::node_tree<0, W, W>(nn);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cols_m(int64_t R, int64_t C, int64_t nch, ColsWs ws) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= C) return;
+  const Node ny = chunk_tree<sv::NODE_TWOSUM>(ws.ny + col, C, nch);
+  ws.m[col] = sv::root_value(ny) / (float)R;
+}
+
+// Tree over the nch <= CC_GROUP chunk nodes p[0], p[stride], ... (one group,
+// nothing written back).
+__device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int64_t nch) {
+  Node sub[CC_GROUP / 8];
+#pragma unroll
+  for (int b = 0; b < CC_GROUP / 8; ++b) {
+    Node nd[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t idx = b * 8 + k;
+      const Node t = p[(idx < nch ? idx : nch - 1) * stride];
+      nd[k] = idx < nch ? t : sv::zero_node();
+    }
+    sub[b] = sv::node_tree<0, 8, 8>(nd);
+  }
+  return sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8>(sub);
+}
+
+// MLOCAL: nch <= CC_GROUP, and every workgroup forms m for its own columns
+// from their y chunk nodes (no k_cols_m launch); else m comes from k_cols_m.
+template <int V, int W, bool MLOCAL>
+__global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                    ColsWs ws) {
+  constexpr int E = CC_E, NC = 64 * V;
+  static_assert(64 * W >= NC, "one thread per column of the block");
+  __shared__ Node sd[W][V][64];
+  __shared__ Node sq[W][V][64];
+  __shared__ float sm[V][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t c0 = cb * NC + (int64_t)lane * V;
+  const int64_t r0 = j * (E * W) + (int64_t)w * E;
+  const bool full = r0 + E <= R;
+  const int64_t left = R - r0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+
+  float v[V][E];
+  load_cols_tile<V, E>(x, R, C, c0, r0, full, v);
+  float x0[V], m[V];
+  const int64_t cc = c0 < C ? c0 : C - V;
+  if constexpr (MLOCAL) {
+    const int t = threadIdx.x;
+    if (t < NC) {
+      const int k = t >> 6, l = t & 63;  // thread t: column V*l + k of the block (clamped like the loads)
+      const int64_t col = cb * NC + (int64_t)l * V + k;
+      const int64_t ccol = col < C ? col : C - 1;
+      sm[k][l] = sv::root_value(chunk_tree_1(ws.ny + ccol, C, nch)) / (float)R;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    x0[k] = x[cc + k];
+    m[k] = MLOCAL ? sm[k][lane] : ws.m[cc + k];
+  }
+  shift_cols_tile<V, E>(v, x0, full, valid);
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    Node nd, nq;
+    if (full) sv::lane_tree_dq<false, 0, E, E>(v[k], m[k], E, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v[k], m[k], valid, nd, nq);
+    sd[w][k][lane] = nd;
+    sq[w][k][lane] = nq;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < NC) {
+    const int k = t >> 6, l = t & 63;  // thread t combines column V*l + k of the block
+    const int64_t col = cb * NC + (int64_t)l * V + k;
+    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][l];  // for k_cols_fin
+    if (col < C) {
+      Node a[W], b[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        a[i] = sd[i][k][l];
+        b[i] = sq[i][k][l];
+      }
+      ws.nd[j * C + col] = sv::node_tree<0, W, W>(a);
+      ws.nq[j * C + col] = sv::node_tree<0, W, W, sv::NODE_NN>(b);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cols_fin(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                  int64_t ddof, ColsWs ws, float *__restrict__ var_out,
+                                                  float *__restrict__ mean_out) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= C) return;
+  const Node nd = chunk_tree<sv::NODE_TWOSUM>(ws.nd + col, C, nch);
+  const Node nq = chunk_tree<sv::NODE_NN>(ws.nq + col, C, nch);
+  finalize(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+}
+
 // ------------------------------------------------------------------ long slices
 
-// Slices longer than one workgroup's registers hold are cut into aligned
-// chunks (a chunk is a node of the slice's tree) and reduced in four
-// launches: y-tree node per chunk -> per slice m = Tree(y)/n -> d- and
-// d^2-tree nodes per chunk -> per slice top trees and step 4.  The input is
-// read twice.  Workspace per slice: nchunks y nodes, 2*nchunks d/d^2 nodes
-// and m.
+// Rows longer than one workgroup's registers hold (axis 1, n > 16384) are
+// cut into aligned chunks (a chunk is a node of the row's tree) and reduced
+// in four launches: y-tree node per chunk -> per row m = Tree(y)/n -> d- and
+// d^2-tree nodes per chunk -> per row top trees and step 4.  The input is
+// read twice.  Workspace per row: nchunks y nodes, 2*nchunks d/d^2 nodes and
+// m.
 
 constexpr int LS_TOP_PER_THREAD = 32;                      // chunk nodes per thread at the top
 constexpr int LS_MAX_CHUNKS = 256 * LS_TOP_PER_THREAD;     // 8192 chunks per slice
 constexpr int64_t LS_ROW_CHUNK = 64LL * 64 * 4;            // axis 1: 16384 values (4 waves x 64 lanes x 64)
-constexpr int64_t LS_COL_CHUNK = 64LL * 16;                // axis 0: 1024 rows (16 waves x 64)
 
 struct LongWs {
   Node *ny;   // [nslices][nch]
@@ -800,134 +1043,40 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
   }
 }
 
-// Axis 0, pass 0 or 1 over rows [c*1024, (c+1)*1024) of 64 columns
-// (block index = colblock * nch + c); lanes own columns, the 16 waves own
-// consecutive blocks of 64 rows.
-template <int PASS>
-__global__ __launch_bounds__(1024) void k_long_cols(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
-                                                    LongWs ws) {
-  constexpr int E = 64, W = 16;
-  __shared__ Node s0[W][64];
-  __shared__ Node s1[W][64];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int64_t cb = (int64_t)blockIdx.x / nch;
-  const int64_t c = (int64_t)blockIdx.x % nch;
-  const int64_t col = cb * 64 + lane;
-  const bool colok = col < C;
-  const int64_t ccol = colok ? col : C - 1;
-  const int64_t r0 = c * LS_COL_CHUNK + (int64_t)w * E;
-  const bool full = r0 + E <= R;
-  float v[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const int64_t rr = r0 + i;
-    const float t = x[(rr < R ? rr : R - 1) * C + ccol];
-    v[i] = (rr < R) ? t : 0.0f;
-  }
-  const float x0 = x[ccol];
-  const int64_t vl = R - r0;
-  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
-  if (full) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
-  }
-  const int64_t out = ccol * nch + c;
-  if constexpr (PASS == 0) {
-    s0[w][lane] = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    __syncthreads();
-    if (w == 0 && colok) {
-      Node nn[W];
-#pragma unroll
-      for (int i = 0; i < W; ++i) nn[i] = s0[i][lane];
-      ws.ny[out] = sv::node_tree<0, W, W>(nn);
-    }
-  } else {
-    const float m = ws.m[ccol];
-    Node nd, nq;
-    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
-    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    s0[w][lane] = nd;
-    s1[w][lane] = nq;
-    __syncthreads();
-    if (w == 0 && colok) {
-      Node a[W], b[W];
-#pragma unroll
-      for (int i = 0; i < W; ++i) {
-        a[i] = s0[i][lane];
-        b[i] = s1[i][lane];
-      }
-#pragma unroll
-      for (int len = W; len > 1; len >>= 1)
-#pragma unroll
-        for (int k = 0; k < len / 2; ++k) {
-          a[k] = sv::combine(a[2 * k], a[2 * k + 1]);
-          b[k] = sv::combine_nn(b[2 * k], b[2 * k + 1]);
-        }
-      ws.nd[out] = a[0];
-      ws.nq[out] = b[0];
-    }
-  }
-}
-
 // Tree over the nch chunk nodes of one slice (one workgroup per slice), the
-// chunk nodes padded with zeros to LS_MAX_CHUNKS.
-template <bool NN>
+// chunk nodes padded with zeros to 256 * K.
+template <bool NN, int K>
 __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t nch, Node *slots) {
-  constexpr int K = LS_TOP_PER_THREAD;
+  constexpr int KIND = NN ? sv::NODE_NN : sv::NODE_TWOSUM;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  Node sub[K / 8];
+  Node nd[K];
 #pragma unroll
-  for (int b = 0; b < K / 8; ++b) {
-    Node nd[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t idx = (int64_t)threadIdx.x * K + b * 8 + k;
-      nd[k] = idx < nch ? nodes[idx] : sv::zero_node();
-    }
-    if constexpr (NN) {
-#pragma unroll
-      for (int len = 8; len > 1; len >>= 1)
-#pragma unroll
-        for (int k = 0; k < len / 2; ++k) nd[k] = sv::combine_nn(nd[2 * k], nd[2 * k + 1]);
-      sub[b] = nd[0];
-    } else {
-      sub[b] = sv::node_tree<0, 8, 8>(nd);
-    }
+  for (int k = 0; k < K; ++k) {
+    const int64_t idx = (int64_t)threadIdx.x * K + k;
+    const Node t = nodes[idx < nch ? idx : nch - 1];  // unconditional: the loads overlap
+    nd[k] = idx < nch ? t : sv::zero_node();
   }
-  Node r;
-  if constexpr (NN) {
-#pragma unroll
-    for (int len = K / 8; len > 1; len >>= 1)
-#pragma unroll
-      for (int k = 0; k < len / 2; ++k) sub[k] = sv::combine_nn(sub[2 * k], sub[2 * k + 1]);
-    r = sub[0];
-  } else {
-    r = sv::node_tree<0, K / 8, K / 8>(sub);
-  }
-  r = sv::wave_tree<NN ? sv::NODE_NN : sv::NODE_TWOSUM>(r);
+  Node r = sv::node_tree<0, K, K, KIND>(nd);
+  r = sv::wave_tree<KIND>(r);
   return block_tree<4, NN>(r, slots, w, lane);
 }
 
 // PASS 0: m = Tree(y) / n.  PASS 1: the top trees of d and d^2 and step 4.
 // One 256-thread workgroup per slice; the slice's first value is at
 // x[s * sstride].
-template <int PASS>
+template <int PASS, int K>
 __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, int64_t n, int64_t sstride,
                                                   int64_t nch, int64_t ddof, LongWs ws, float *__restrict__ var_out,
                                                   float *__restrict__ mean_out) {
   __shared__ Node slots[2][4];
   const int64_t sl = blockIdx.x;
   if constexpr (PASS == 0) {
-    const Node ny = top_tree<false>(ws.ny + sl * nch, nch, slots[0]);
+    const Node ny = top_tree<false, K>(ws.ny + sl * nch, nch, slots[0]);
     if (threadIdx.x == 0) ws.m[sl] = sv::root_value(ny) / (float)n;
   } else {
-    const Node nd = top_tree<false>(ws.nd + sl * nch, nch, slots[0]);
-    const Node nq = top_tree<true>(ws.nq + sl * nch, nch, slots[1]);
+    const Node nd = top_tree<false, K>(ws.nd + sl * nch, nch, slots[0]);
+    const Node nq = top_tree<true, K>(ws.nq + sl * nch, nch, slots[1]);
     if (threadIdx.x == 0)
       finalize(nd, nq, x[sl * sstride], ws.m[sl], n, ddof, var_out + sl, mean_out ? mean_out + sl : nullptr);
   }
@@ -945,9 +1094,13 @@ struct Tuning {
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
   int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
-  int var_split = 4;          // waves sharing one row (1, 2, 4, 8) for 1024 < n <= 4096
+  int var_split = 2;          // waves per 4096 values of a row of 1025..16384 values (1, 2, 4, 8)
   int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
   int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
+  int var_cols_single_max = 1024;  // axis 0: rows up to which one workgroup holds a column tile (<= 1024)
+  int var_cols_waves = 16;    // axis 0, chunked: waves per workgroup (4, 8, 16); chunks of 16 * waves rows
+  int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
+  int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
 };
 Tuning g_tune;
 
@@ -972,6 +1125,72 @@ LongWs long_ws(void *workspace, int64_t nslices, int64_t nch) {
   const size_t nodes = (size_t)nslices * (size_t)nch * sizeof(Node);
   return {reinterpret_cast<Node *>(p), reinterpret_cast<Node *>(p + nodes), reinterpret_cast<Node *>(p + 2 * nodes),
           reinterpret_cast<float *>(p + 3 * nodes)};
+}
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Axis-0 chunked workspace: the three node arrays (room for the shortest
+// chunks, CC_E * CC_MIN_W rows) and m.  Independent of the launch knobs.
+struct ColsLayout {
+  size_t nodes, m, total;
+};
+
+ColsLayout cols_layout(int64_t R, int64_t C) {
+  const int64_t nch = (R + CC_E * CC_MIN_W - 1) / (CC_E * CC_MIN_W);
+  ColsLayout L;
+  L.nodes = round256((size_t)nch * (size_t)C * sizeof(Node));
+  L.m = round256((size_t)C * sizeof(float));
+  L.total = 3 * L.nodes + L.m;
+  return L;
+}
+
+ColsWs cols_ws(void *workspace, const ColsLayout &L) {
+  char *p = reinterpret_cast<char *>(workspace);
+  ColsWs ws;
+  ws.ny = reinterpret_cast<Node *>(p);
+  p += L.nodes;
+  ws.nd = reinterpret_cast<Node *>(p);
+  p += L.nodes;
+  ws.nq = reinterpret_cast<Node *>(p);
+  p += L.nodes;
+  ws.m = reinterpret_cast<float *>(p);
+  return ws;
+}
+
+template <int V, int W>
+void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var,
+                         float *mean, hipStream_t st) {
+  const int64_t nch = (R + CC_E * W - 1) / (CC_E * W);
+  const int64_t ncb = (C + 64 * V - 1) / (64 * V);
+  const dim3 grid((unsigned)(ncb * nch)), block(64 * W);
+  const dim3 per_col((unsigned)((C + 255) / 256));
+  k_cols_y<V, W><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  if (nch <= CC_GROUP) {
+    k_cols_dq<V, W, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  } else {
+    k_cols_m<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
+    k_cols_dq<V, W, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  }
+  k_cols_fin<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+}
+
+template <int V>
+void launch_cols_v(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var, float *mean,
+                   hipStream_t st) {
+  if (g_tune.var_cols_waves == 16) launch_cols_chunked<V, 16>(x, R, C, ddof, ws, var, mean, st);
+  else if (g_tune.var_cols_waves == 8) launch_cols_chunked<V, 8>(x, R, C, ddof, ws, var, mean, st);
+  else launch_cols_chunked<V, 4>(x, R, C, ddof, ws, var, mean, st);
+}
+
+// The top trees over nch <= LS_MAX_CHUNKS chunk nodes per slice: 256
+// threads of K nodes each, K the smallest of 1, 4, 32 that holds nch (the
+// zero padding beyond nch changes no bit).
+template <int PASS>
+void launch_long_top(const float *x, int64_t n, int64_t sstride, int64_t nch, int64_t ddof, const LongWs &ws,
+                     float *var, float *mean, dim3 grid, hipStream_t st) {
+  if (nch <= 256) k_long_top<PASS, 1><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  else if (nch <= 1024) k_long_top<PASS, 4><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  else k_long_top<PASS, LS_TOP_PER_THREAD><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
 }
 
 struct SumPlan {
@@ -1006,8 +1225,8 @@ template <int E, bool VEC, int LOADP, bool NT>
 void launch_sum_t(const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
                   hipStream_t st) {
   const dim3 grid((unsigned)p.blocks), block(64 * SUM_W);
-  if (g_tune.sum_depth == 4) k_tree_sum<E, SUM_W, VEC, LOADP, NT, 4><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
-  else k_tree_sum<E, SUM_W, VEC, LOADP, NT, 2><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
+  if (g_tune.sum_depth == 4) k_tree_sum<E, SUM_W, VEC, LOADP, NT, 4><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out, g_tune.sum_xcd);
+  else k_tree_sum<E, SUM_W, VEC, LOADP, NT, 2><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out, g_tune.sum_xcd);
 }
 
 // The double-word-carry sum in the default load configuration (coalesced
@@ -1016,8 +1235,8 @@ template <int E>
 void launch_sum_dw(bool vec, const float *x, int64_t n, const SumPlan &p, Node *part, unsigned *counter, float *out,
                    hipStream_t st) {
   const dim3 grid((unsigned)p.blocks), block(64 * SUM_W);
-  if (vec) k_tree_sum<E, SUM_W, true, 0, true, 2, sv::NODE_DW><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
-  else k_tree_sum<E, SUM_W, false, 0, true, 2, sv::NODE_DW><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out);
+  if (vec) k_tree_sum<E, SUM_W, true, 0, true, 2, sv::NODE_DW><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out, g_tune.sum_xcd);
+  else k_tree_sum<E, SUM_W, false, 0, true, 2, sv::NODE_DW><<<grid, block, 0, st>>>(x, n, p.log2_g, part, counter, out, g_tune.sum_xcd);
 }
 
 template <int E>
@@ -1041,7 +1260,7 @@ void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t 
                    hipStream_t st) {
   // var_lds_pad: unused dynamic LDS per workgroup, a cap on resident waves
   k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), (size_t)g_tune.var_lds_pad, st>>>(
-      x, n, ld, ddof, var, mean);
+      x, n, ld, ddof, var, mean, g_tune.var_xcd);
 }
 
 // A row shared by W waves of E values per lane; 16-byte loads follow
@@ -1079,6 +1298,34 @@ void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t l
     case 5: launch_rows_t<E, W, true, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
     case 6: launch_rows_t<E, W, true, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
     default: launch_rows_t<E, W, true, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
+  }
+}
+
+// Rows of 1025..16384 values: the row's power-of-two tile (2048 .. 16384
+// values) is shared by var_split waves per 4096 values, E = 64 / var_split
+// values per lane (a 2048-value tile takes at most 32 values per lane, a
+// 16384-value tile at most 16 waves).
+void launch_rows_tile(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
+                      float *mean, hipStream_t st) {
+  const int s = g_tune.var_split;
+  if (n <= 2048) {
+    if (s <= 2) launch_rows_split<32, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else if (s == 4) launch_rows_split<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else launch_rows_split<8, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
+  } else if (n <= 4096) {
+    if (s == 1) launch_rows_ew<64, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else if (s == 2) launch_rows_split<32, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else if (s == 4) launch_rows_split<16, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else launch_rows_split<8, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
+  } else if (n <= 8192) {
+    if (s == 1) launch_rows_split<64, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else if (s == 2) launch_rows_split<32, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else if (s == 4) launch_rows_split<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else launch_rows_split<8, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
+  } else {
+    if (s == 1) launch_rows_ew<64, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else if (s == 2) launch_rows_split<32, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
+    else launch_rows_split<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
   }
 }
 
@@ -1120,12 +1367,12 @@ void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t co
     const dim3 grid((unsigned)rows);
 #define SV_ROWS(E, W)                                                                                 \
   do {                                                                                                \
-    if (vec) k_var_rows<E, W, true, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean); \
-    else k_var_rows<E, W, false, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean);   \
+    if (vec) k_var_rows<E, W, true, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean, 0); \
+    else k_var_rows<E, W, false, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean, 0);   \
   } while (0)
     if (n <= 256) SV_ROWS(4, 1);
     else if (n <= 1024) SV_ROWS(16, 1);
-    else if (n <= 4096) SV_ROWS(16, 4);  // the default geometry of the main kernel
+    else if (n <= 4096) SV_ROWS(32, 2);  // the default geometry of the main kernel
     else SV_ROWS(64, 4);
 #undef SV_ROWS
   } else {
@@ -1223,8 +1470,9 @@ size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis) {
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t n = ax1 ? cols : rows;
   const int64_t nslices = ax1 ? rows : cols;
-  if (ax1 ? (n <= ROWS_MAX_N) : (n <= COLS_MAX_R)) return 0;
-  const int64_t nch = ax1 ? (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK : (n + LS_COL_CHUNK - 1) / LS_COL_CHUNK;
+  if (!ax1) return (n == 0 || nslices == 0) ? 0 : cols_layout(n, nslices).total;
+  if (n <= ROWS_MAX_N) return 0;
+  const int64_t nch = (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK;
   if (nch > LS_MAX_CHUNKS) return (size_t)-1;
   return long_ws_bytes(nslices, nch);
 }
@@ -1247,15 +1495,13 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
   if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: x is NULL");
   if (nslices > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: %lld slices exceed the grid", (long long)nslices);
-  const bool is_long = ax1 ? (n > ROWS_MAX_N) : (n > COLS_MAX_R);
-  const int64_t nch = !is_long ? 0
-                      : ax1    ? (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK
-                               : (n + LS_COL_CHUNK - 1) / LS_COL_CHUNK;
-  if (is_long) {
-    if (nch > LS_MAX_CHUNKS)
-      return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: slices of length %lld exceed %d chunks", (long long)n,
-                  LS_MAX_CHUNKS);
-    const size_t need = long_ws_bytes(nslices, nch);
+  const bool is_long = ax1 && n > ROWS_MAX_N;
+  const int64_t nch = is_long ? (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK : 0;
+  if (is_long && nch > LS_MAX_CHUNKS)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: slices of length %lld exceed %d chunks", (long long)n,
+                LS_MAX_CHUNKS);
+  if (is_long || (!ax1 && n > 0)) {
+    const size_t need = is_long ? long_ws_bytes(nslices, nch) : cols_layout(n, nslices).total;
     if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_f32: workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
       return fail(SV_ERR_WORKSPACE, "sv_variance_f32: workspace has %zu bytes, %zu needed", workspace_bytes, need);
@@ -1274,23 +1520,20 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
   }
   if (is_long) {
     const LongWs ws = long_ws(workspace, nslices, nch);
-    if (ax1) {
-      const bool vec = aligned16(x) && (cols % 4 == 0);
-      const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
-      if (vec) k_long_rows<0, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-      else k_long_rows<0, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-      k_long_top<0><<<top, 256, 0, st>>>(x, n, cols, nch, ddof, ws, var_out, mean_out);
-      if (vec) k_long_rows<1, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-      else k_long_rows<1, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-      k_long_top<1><<<top, 256, 0, st>>>(x, n, cols, nch, ddof, ws, var_out, mean_out);
-    } else {
-      const int64_t ncb = (cols + 63) / 64;
-      const dim3 grid((unsigned)(ncb * nch)), block(1024), top((unsigned)cols);
-      k_long_cols<0><<<grid, block, 0, st>>>(x, rows, cols, nch, ws);
-      k_long_top<0><<<top, 256, 0, st>>>(x, rows, 1, nch, ddof, ws, var_out, mean_out);
-      k_long_cols<1><<<grid, block, 0, st>>>(x, rows, cols, nch, ws);
-      k_long_top<1><<<top, 256, 0, st>>>(x, rows, 1, nch, ddof, ws, var_out, mean_out);
-    }
+    const bool vec = aligned16(x) && (cols % 4 == 0);
+    const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
+    if (vec) k_long_rows<0, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+    else k_long_rows<0, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+    launch_long_top<0>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
+    if (vec) k_long_rows<1, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+    else k_long_rows<1, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+    launch_long_top<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
+    return check_launch("sv_variance_f32");
+  }
+  if (!ax1 && n > g_tune.var_cols_single_max) {
+    const ColsWs ws = cols_ws(workspace, cols_layout(rows, cols));
+    if (aligned16(x) && cols % 4 == 0) launch_cols_v<4>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+    else launch_cols_v<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
     return check_launch("sv_variance_f32");
   }
   if (ax1) {
@@ -1304,17 +1547,14 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
       if (R == 2) k_var_rows_dma<2, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
       else if (R == 4) k_var_rows_dma<4, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
       else k_var_rows_dma<8, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
-    } else if (n <= 4096) {
+    } else if (n <= 4096 && g_tune.var_rows_per_wave > 1) {
       const int R = g_tune.var_rows_per_wave;
       if (R == 2) launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
       else if (R == 4) launch_pipe_r<4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else if (R == 8) launch_pipe_r<8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else if (g_tune.var_split == 2) launch_rows_split<32, 2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else if (g_tune.var_split == 4) launch_rows_split<16, 4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else if (g_tune.var_split == 8) launch_rows_split<8, 8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else launch_rows_ew<64, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      else launch_pipe_r<8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    } else {
+      launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     }
-    else launch_rows_ew<64, 4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
   } else {
     if (n <= 4) launch_cols_ew<4, 1>(x, rows, cols, ddof, var_out, mean_out, st);
     else if (n <= 16) launch_cols_ew<16, 1>(x, rows, cols, ddof, var_out, mean_out, st);
@@ -1370,7 +1610,6 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
   return check_launch("sv_variance_variant_f32");
 }
 
-static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis) {
   if (rows < 0 || cols < 0) return (size_t)-1;
@@ -1381,8 +1620,8 @@ size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis) {
   const size_t inner = ax1 ? sv_variance_f32_workspace_size(2 * rows, cols, 1)
                            : sv_variance_f32_workspace_size(rows, 2 * cols, 0);
   if (inner == (size_t)-1) return (size_t)-1;
-  size_t b = align256((size_t)2 * nslices * sizeof(float));  // per-component variances
-  if (ax1) b += align256((size_t)2 * rows * cols * sizeof(float));  // split rows
+  size_t b = round256((size_t)2 * nslices * sizeof(float));  // per-component variances
+  if (ax1) b += round256((size_t)2 * rows * cols * sizeof(float));  // split rows
   return b + inner;
 }
 
@@ -1414,11 +1653,11 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
   (void)hipGetLastError();
   char *wp = reinterpret_cast<char *>(workspace);
   float *vparts = reinterpret_cast<float *>(wp);
-  wp += align256((size_t)2 * nslices * sizeof(float));
+  wp += round256((size_t)2 * nslices * sizeof(float));
   sv_status rc;
   if (ax1) {
     float *split = reinterpret_cast<float *>(wp);
-    wp += align256((size_t)2 * rows * cols * sizeof(float));
+    wp += round256((size_t)2 * rows * cols * sizeof(float));
     const size_t inner = sv_variance_f32_workspace_size(2 * rows, cols, 1);
     if (rows * cols > 0) {
       const int64_t total = rows * cols;
@@ -1467,6 +1706,21 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_nt") == 0) return flag(&g_tune.var_nt);
+  if (strcmp(key, "var_cols_single_max") == 0) {
+    if (value < 0 || value > COLS_MAX_R)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_single_max must be in [0, %lld]",
+                  (long long)COLS_MAX_R);
+    g_tune.var_cols_single_max = (int)value;
+    return ok();
+  }
+  if (strcmp(key, "var_cols_waves") == 0) {
+    if (value != 4 && value != 8 && value != 16)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_waves must be 4, 8 or 16");
+    g_tune.var_cols_waves = (int)value;
+    return ok();
+  }
+  if (strcmp(key, "sum_xcd") == 0) return flag(&g_tune.sum_xcd);
+  if (strcmp(key, "var_xcd") == 0) return flag(&g_tune.var_xcd);
   if (strcmp(key, "var_lds_pad") == 0) {
     if (value < 0 || value > 65536) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_lds_pad must be in [0, 65536]");
     g_tune.var_lds_pad = (int)value;

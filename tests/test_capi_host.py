@@ -60,11 +60,18 @@ def test_workspace_sizes(L):
         assert L.sv_tree_sum_f32_workspace_size(n) == want
     assert L.sv_tree_sum_f32_workspace_size((1 << 36) + 1) == ctypes.c_size_t(-1).value
     assert L.sv_variance_f32_workspace_size(4096, 4096, 1) == 0
-    assert L.sv_variance_f32_workspace_size(1000, 64, 0) == 0
     assert L.sv_variance_f32_workspace_size(1, 64, 3) == ctypes.c_size_t(-1).value
-    # long slices: 24 bytes per chunk (16384 values on axis 1, 1024 on axis 0) + 4 per slice
+    # axis 0: three node arrays of 8 bytes per 64-row chunk per column and 4
+    # bytes of m per column, each rounded up to 256 bytes
+    r256 = lambda b: (b + 255) // 256 * 256
+    for R, C in ((1000, 64), (1025, 7), (4096, 4096), (1, 1), (64, 65), (65, 1000)):
+        want = 3 * r256(-(-R // 64) * C * 8) + r256(4 * C)
+        assert L.sv_variance_f32_workspace_size(R, C, 0) == want, (R, C)
+        assert L.sv_variance_f32_workspace_size(R, C, -2) == want, (R, C)
+    assert L.sv_variance_f32_workspace_size(0, 5, 0) == 0
+    assert L.sv_variance_f32_workspace_size(5, 0, 0) == 0
+    # long rows: 24 bytes per 16384-value chunk + 4 per row
     assert L.sv_variance_f32_workspace_size(3, 16385, 1) == 3 * 2 * 24 + 3 * 4
-    assert L.sv_variance_f32_workspace_size(1025, 7, 0) == 7 * 2 * 24 + 7 * 4
     assert L.sv_variance_f32_workspace_size(1, 8192 * 16384, 1) == 8192 * 24 + 4
     assert L.sv_variance_f32_workspace_size(1, 8192 * 16384 + 1, 1) == ctypes.c_size_t(-1).value
 
@@ -151,8 +158,9 @@ def test_f64_sizes_and_argument_errors(L):
 
 def test_complex_argument_errors_and_sizes(L):
     out = ctypes.c_void_p(0x2000)
-    # axis 0: per-component variances (2*cols floats) + the float view's own workspace (0 here)
-    assert L.sv_variance_c64_workspace_size(1000, 64, 0) == 512
+    # axis 0: per-component variances (2*cols floats) + the float view's own
+    # workspace ([1000, 128] along axis 0)
+    assert L.sv_variance_c64_workspace_size(1000, 64, 0) == 512 + L.sv_variance_f32_workspace_size(1000, 128, 0)
     # axis 1: per-component variances + split rows (8 bytes per value)
     assert L.sv_variance_c64_workspace_size(64, 1000, 1) == 512 + 64 * 1000 * 8
     assert L.sv_variance_c64_workspace_size(2, 3, 5) == ctypes.c_size_t(-1).value
@@ -170,7 +178,9 @@ def test_tuning_knob_validation(L):
     assert L.sv_set_tuning(b"nope", 0) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(None, 0) == SV_ERR_INVALID_ARGUMENT
     for key, good, bad in ((b"sum_load_path", 1, 2), (b"sum_nt", 0, -1), (b"var_load_path", 2, 5),
-                           (b"var_nt", 1, 2), (b"var_rows_per_wave", 4, 3), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0)):
+                           (b"var_nt", 1, 2), (b"var_rows_per_wave", 4, 3), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0),
+                           (b"sum_xcd", 1, 2), (b"var_xcd", 1, -1), (b"var_split", 8, 3), (b"var_dma_rows", 2, 1),
+                           (b"var_lds_pad", 65536, 65537)):
         assert L.sv_set_tuning(key, good) == 0, key
         assert L.sv_set_tuning(key, bad) == SV_ERR_INVALID_ARGUMENT, key
     assert L.sv_set_tuning(b"sum_blocks", 8193) == SV_ERR_INVALID_ARGUMENT

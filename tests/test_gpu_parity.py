@@ -37,6 +37,8 @@ SUM_GEOMETRIES = {
     "one_chunk_per_wave": {"sum_blocks": 8192, "sum_e": 16},
     "lane_loads_plain": {"sum_load_path": 1, "sum_nt": 0},
     "single_workgroup": {"sum_blocks": 1},
+    "xcd_contiguous": {"sum_xcd": 1},
+    "xcd_contiguous_few_blocks": {"sum_xcd": 1, "sum_blocks": 61},
 }
 VAR_GEOMETRIES = {
     "default": {},
@@ -44,11 +46,23 @@ VAR_GEOMETRIES = {
     "lds_transpose": {"var_load_path": 0, "var_nt": 0},
     "staged_transpose": {"var_load_path": 2},
     "split1": {"var_split": 1},
-    "split2": {"var_split": 2},
+    "split4": {"var_split": 4},
     "occupancy_capped": {"var_lds_pad": 20000},
     "split8": {"var_split": 8},
+    "xcd_contiguous": {"var_xcd": 1},
+    "xcd_contiguous_split1": {"var_xcd": 1, "var_split": 1},
     "pipelined_rows2": {"var_rows_per_wave": 2},
     "pipelined_rows8_lds": {"var_rows_per_wave": 8, "var_load_path": 0},
+}
+
+# Axis-0 paths: one workgroup per column tile (rows up to var_cols_single_max)
+# or row chunks of 16 * var_cols_waves rows in three launches.
+COL_GEOMETRIES = {
+    "default": {},
+    "chunked_w4": {"var_cols_single_max": 0},
+    "chunked_w8": {"var_cols_single_max": 0, "var_cols_waves": 8},
+    "chunked_w16": {"var_cols_single_max": 0, "var_cols_waves": 16},
+    "single_upto_64": {"var_cols_single_max": 64, "var_cols_waves": 8},
 }
 
 
@@ -65,6 +79,15 @@ def sum_geometry(request, torch_dev):
     import stable_variance_amd as sv
 
     _apply(SUM_GEOMETRIES[request.param])
+    yield request.param
+    sv.set_tuning("reset", 0)
+
+
+@pytest.fixture(params=list(COL_GEOMETRIES), ids=list(COL_GEOMETRIES))
+def col_geometry(request, torch_dev):
+    import stable_variance_amd as sv
+
+    _apply(COL_GEOMETRIES[request.param])
     yield request.param
     sv.set_tuning("reset", 0)
 
@@ -235,7 +258,8 @@ def test_variance_4096_square(torch_dev, var_geometry):
     assert oracle.max_rel_err(v, v64) <= 4 * U
 
 
-ROW_NS = [1, 2, 3, 5, 64, 255, 256, 257, 1000, 1023, 1024, 1025, 4095, 4096, 4097, 10000, 16384]
+ROW_NS = [1, 2, 3, 5, 64, 255, 256, 257, 1000, 1023, 1024, 1025, 1500, 2048, 2049, 4095, 4096, 4097, 6000, 8192,
+          8193, 10000, 16384]
 
 
 @pytest.mark.parametrize("n", ROW_NS)
@@ -276,7 +300,7 @@ def test_variance_specials_rows(torch_dev, var_geometry, n):
 
 
 @pytest.mark.parametrize("R", [3, 64, 1000, 1500])
-def test_variance_specials_cols(torch_dev, R):
+def test_variance_specials_cols(torch_dev, col_geometry, R):
     a = np.ascontiguousarray(special_rows(R, seed=R + 7).T)
     check_var(torch_dev, a, 0, 0)
 
@@ -285,7 +309,7 @@ COL_RS = [1, 2, 3, 4, 5, 16, 17, 64, 65, 100, 128, 129, 256, 257, 512, 513, 1000
 
 
 @pytest.mark.parametrize("R", COL_RS)
-def test_variance_cols_shapes(torch_dev, R):
+def test_variance_cols_shapes(torch_dev, col_geometry, R):
     rng = np.random.default_rng(R)
     for C in (1, 63, 64, 65, 200):
         a = rng.normal(-3e3, 2, (R, C)).astype(np.float32)
@@ -337,7 +361,7 @@ def test_variance_long_rows(torch_dev, n):
 
 
 @pytest.mark.parametrize("R", [1025, 2048, 3000, 5000])
-def test_variance_long_cols(torch_dev, R):
+def test_variance_long_cols(torch_dev, col_geometry, R):
     rng = np.random.default_rng(R)
     for C in (1, 64, 130):
         a = rng.normal(-7e3, 0.5, (R, C)).astype(np.float32)
@@ -345,6 +369,33 @@ def test_variance_long_cols(torch_dev, R):
         check_var(torch_dev, a, 0, 1)
     b = W.adversarial_values(R * 33, R).reshape(R, 33)
     check_var(torch_dev, b, 0, 0)
+
+
+@pytest.mark.parametrize("R,C", [(4096, 1000), (2000, 4100), (5000, 257), (300, 4096), (70000, 12), (1, 3000)])
+def test_variance_cols_wide(torch_dev, col_geometry, R, C):
+    # several column blocks with a ragged last block (16-byte loads of four
+    # columns when C % 4 == 0, one column per lane otherwise) and ragged chunks
+    rng = np.random.default_rng(R + C)
+    a = rng.normal(2.5e4, 4, (R, C)).astype(np.float32)
+    check_var(torch_dev, a, 0, 0)
+    check_var(torch_dev, a, 0, 5)
+    b = W.adversarial_values(R * C, R + 1).reshape(R, C)
+    check_var(torch_dev, b, 0, 0)
+
+
+def test_variance_4096_square_axis0(torch_dev, col_geometry):
+    a = W.c4_matrix()
+    v = check_var(torch_dev, a, 0)
+    assert oracle.max_rel_err(v, oracle.var_f64(a, axis=0)) <= 4 * U
+
+
+def test_variance_cols_datasets_and_constants(torch_dev, col_geometry):
+    for name, a, axis, _ in W.datasets_d1_d4():
+        check_var(torch_dev, a, axis)
+    for c in (1.0, 1e10, 1e38):
+        for R in (3, 1000, 3000):
+            v = check_var(torch_dev, np.full((R, 20), np.float32(c)), 0, 1)
+            assert np.all(v == 0.0)
 
 
 def test_variance_single_long_row(torch_dev):
@@ -478,7 +529,8 @@ def gpu_sum_dw(torch_dev, x, offset=0):
     return np.float32(r.item())
 
 
-DW_GEOMETRIES = {"default": {}, "e16_few_blocks": {"sum_e": 16, "sum_blocks": 64}, "single_workgroup": {"sum_blocks": 1}}
+DW_GEOMETRIES = {"default": {}, "e16_few_blocks": {"sum_e": 16, "sum_blocks": 64}, "single_workgroup": {"sum_blocks": 1},
+                 "xcd_contiguous": {"sum_xcd": 1, "sum_blocks": 1000}}
 
 
 @pytest.mark.parametrize("knobs", list(DW_GEOMETRIES.values()), ids=list(DW_GEOMETRIES))
