@@ -384,12 +384,12 @@ def main():
     sum64_ms = time_op(lambda i: check(L.sv_tree_sum_f64(c5d[i % 2].data_ptr(), SUM_N, out64.data_ptr(),
                                                         ws64.data_ptr(), need64, sh)), reps=30)
     var64_ms = time_op(lambda i: check(L.sv_variance_f64(c4d[i % 4].data_ptr(), VAR_ROWS, VAR_COLS, 1, 0,
-                                                        var64.data_ptr(), mean64.data_ptr(), sh)), reps=40)
+                                                        var64.data_ptr(), mean64.data_ptr(), None, 0, sh)), reps=40)
     read64_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c5d[i % 2].data_ptr(), 2 * SUM_N,
                                                                    probe_out.data_ptr(), sh)), reps=20)
     top = torch.full((1, 3), 1e307, dtype=torch.float64, device=dev)
     top_var = torch.empty(1, dtype=torch.float64, device=dev)
-    check(L.sv_variance_f64(top.data_ptr(), 1, 3, 1, 0, top_var.data_ptr(), None, sh))
+    check(L.sv_variance_f64(top.data_ptr(), 1, 3, 1, 0, top_var.data_ptr(), None, None, 0, sh))
     torch.cuda.synchronize()
     f64 = {"sum_1e8": {"avg_launch_ms": round(sum64_ms, 5), "gb_s": round(8 * SUM_N / (sum64_ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(8 * SUM_N / (sum64_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -400,7 +400,8 @@ def main():
            "variance_of_1e307_x3": float(top_var.item()), "bit_exact": None}
     if not args.no_cpu_baseline:
         check(L.sv_tree_sum_f64(c5d[0].data_ptr(), SUM_N, out64.data_ptr(), ws64.data_ptr(), need64, sh))
-        check(L.sv_variance_f64(c4d[0].data_ptr(), VAR_ROWS, VAR_COLS, 1, 0, var64.data_ptr(), mean64.data_ptr(), sh))
+        check(L.sv_variance_f64(c4d[0].data_ptr(), VAR_ROWS, VAR_COLS, 1, 0, var64.data_ptr(), mean64.data_ptr(), None, 0,
+                                sh))
         torch.cuda.synchronize()
         rows = np.random.default_rng(1).choice(VAR_ROWS, 16, replace=False)
         ov64, om64 = oracle.variance_f64(c4_host[rows].astype(np.float64), axis=1)

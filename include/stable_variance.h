@@ -209,17 +209,25 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
  *   out one device double; workspace of sv_tree_sum_f64_workspace_size(n)
  *   bytes, 256-byte aligned, whose first SV_TREE_SUM_COUNTER_BYTES bytes are
  *   ticket counters with the same rules as for sv_tree_sum_f32.
- * sv_variance_f64: x row-major [rows, cols] device doubles (8-byte aligned);
- *   slices of at most 8192 values on axis 1 and 1024 on axis 0 (else
- *   SV_ERR_UNSUPPORTED); var_out (and mean_out if not NULL) one double per
- *   slice; no workspace.
+ * sv_variance_f64: x row-major [rows, cols] device doubles (8-byte aligned),
+ *   rows * cols < 2^39; var_out (and mean_out if not NULL) one double per
+ *   slice; workspace of sv_variance_f64_workspace_size(rows, cols, axis)
+ *   bytes, 256-byte aligned scratch, NULL allowed when that size is 0.
+ * sv_variance_f64_workspace_size: 0 when every slice fits one workgroup
+ *   (axis 1: n <= 16384; axis 0: n <= 1024).  Longer slices are reduced in
+ *   chunks (8192 values of a row; 128 rows of a column), reading the input
+ *   twice: three arrays of 16 bytes per chunk per slice and 8 bytes per
+ *   slice, each rounded up to 256 bytes.  (size_t)-1 for an unsupported
+ *   shape (a bad axis, rows * cols >= 2^39, an axis-1 row of more than 8192
+ *   chunks, i.e. 67,108,864 values).
  * Errors and asynchrony as for the float32 entry points.
  */
 size_t sv_tree_sum_f64_workspace_size(int64_t n);
 sv_status sv_tree_sum_f64(const double *x, int64_t n, double *out, void *workspace, size_t workspace_bytes,
                           void *stream);
+size_t sv_variance_f64_workspace_size(int64_t rows, int64_t cols, int axis);
 sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, double *var_out,
-                          double *mean_out, void *stream);
+                          double *mean_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Ahrens-Demmel-Nguyen binned reproducible sum of float32 values, as the

@@ -81,7 +81,9 @@ def capi():
                 L.sv_tree_sum_f64.restype = ctypes.c_int
                 L.sv_tree_sum_f64.argtypes = [vp, i64, vp, vp, sz, vp]
                 L.sv_variance_f64.restype = ctypes.c_int
-                L.sv_variance_f64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp]
+                L.sv_variance_f64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
+                L.sv_variance_f64_workspace_size.restype = sz
+                L.sv_variance_f64_workspace_size.argtypes = [i64, i64, ctypes.c_int]
                 L.sv_tree_sum_dw_f32.restype = ctypes.c_int
                 L.sv_tree_sum_dw_f32.argtypes = [vp, i64, vp, vp, sz, vp]
                 L.sv_adn_sum_f32_workspace_size.restype = sz
@@ -226,9 +228,14 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
             stream = torch.cuda.current_stream(x.device).cuda_stream
             out = torch.empty(ns, dtype=torch.float64, device=x.device)
             mean = torch.empty(ns, dtype=torch.float64, device=x.device) if return_mean else None
+            need = L.sv_variance_f64_workspace_size(rows, cols, axis)
+            if need == ctypes.c_size_t(-1).value:
+                raise SvError(5, f"var: shape {tuple(x2.shape)} along dim {axis} is not supported")
+            ws = _workspace("var64", need, x.device, stream)
             _check(L.sv_variance_f64(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof),
                                      out.data_ptr() if ns else None,
-                                     mean.data_ptr() if (mean is not None and ns) else None, stream))
+                                     mean.data_ptr() if (mean is not None and ns) else None,
+                                     ws.data_ptr() if ws is not None else None, need, stream))
         if squeeze:
             out = out.reshape(())
             mean = mean.reshape(()) if mean is not None else None

@@ -471,6 +471,320 @@ __global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restric
   }
 }
 
+// ------------------------------------------------------------------ long slices
+
+// Slices longer than one workgroup holds, cut into aligned chunks (nodes of
+// the slice's tree), as in the float32 path:
+//   axis 1, rows of more than 16384 values: chunks of 8192 values (8 waves
+//     of 64 lanes of 16 doubles); a y node per chunk, a per-row top tree
+//     giving m, d and d^2 nodes per chunk, per-row top trees and step 4.
+//   axis 0, columns of more than 1024 values: chunks of 128 rows of a block
+//     of 64*V columns (lane L holds V adjacent columns, one 16-byte load per
+//     row when V = 2, for the 16 rows of its wave); a y node per (chunk,
+//     column), m per column, d and d^2 nodes per (chunk, column), per-column
+//     trees and step 4.
+// The input is read twice; the workspace is scratch.
+
+constexpr int L64_E = 16;                       // doubles per lane
+constexpr int L64_W = 8;                        // waves per workgroup (up to 256 VGPRs: no spills)
+constexpr int64_t L64_ROW_CHUNK = 64LL * L64_E * L64_W;  // 8192 doubles
+constexpr int L64_TOP_MAX_K = 32;               // chunk nodes per thread of a top tree
+constexpr int64_t L64_MAX_CHUNKS = 256LL * L64_TOP_MAX_K;
+constexpr int64_t C64_CHUNK = (int64_t)L64_E * L64_W;     // 128 rows
+constexpr int C64_GROUP = 32;                   // chunk nodes per group of a per-column tree
+
+struct SliceWsD {
+  NodeD *ny;  // y-tree node of every chunk of every slice
+  NodeD *nd;  // d-tree nodes
+  NodeD *nq;  // d^2-tree nodes
+  double *m;  // per slice
+};
+
+// The W wave nodes of a workgroup (every lane of wave w holds node w) ->
+// the workgroup's node, valid in thread 0 (and every thread after the
+// barrier reads of `slots`).
+template <int W, bool NN>
+__device__ __forceinline__ NodeD block_tree_d(NodeD n, NodeD *slots, int w, int lane) {
+  if (lane == 0) slots[w] = n;
+  __syncthreads();
+  NodeD t[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) t[i] = slots[i];
+  __syncthreads();
+  return node_tree_d<0, W, W, NN>(t);
+}
+
+template <int PASS, bool VEC>
+__global__ __launch_bounds__(64 * L64_W) void k_long_rows_d(const double *__restrict__ x, int64_t n, int64_t ld,
+                                                            int64_t nch, SliceWsD ws) {
+  constexpr int E = L64_E, W = L64_W;
+  __shared__ NodeD slots[2][W];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x / nch;
+  const int64_t c = (int64_t)blockIdx.x % nch;
+  const double *__restrict__ row = x + r * ld;
+  const int64_t base = c * L64_ROW_CHUNK + (int64_t)w * 64 * E;
+  const bool empty = base >= n;  // wave-uniform: only padding, nodes (+0, +0)
+  float vf[2 * E];
+  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(row + base), 2 * (n - base), nullptr, vf, lane);
+  double v[E];
+  floats_to_doubles<E>(vf, v);
+  const double x0 = row[0];
+  const bool full = base + 64 * E <= n;
+  const int64_t left = n - base - (int64_t)lane * E;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = (full || i < valid) ? v[i] - x0 : 0.0;
+  const int64_t out = r * nch + c;
+  if constexpr (PASS == 0) {
+    NodeD ny = {0.0, 0.0};
+    if (!empty) ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
+    ny = block_tree_d<W, false>(ny, slots[0], w, lane);
+    if (threadIdx.x == 0) ws.ny[out] = ny;
+  } else {
+    const double m = ws.m[r];
+    NodeD nd = {0.0, 0.0}, nq = {0.0, 0.0};
+    if (!empty) {
+      if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
+      else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
+      nd = wave_tree_d<false>(nd);
+      nq = wave_tree_d<true>(nq);
+    }
+    nd = block_tree_d<W, false>(nd, slots[0], w, lane);
+    nq = block_tree_d<W, true>(nq, slots[1], w, lane);
+    if (threadIdx.x == 0) {
+      ws.nd[out] = nd;
+      ws.nq[out] = nq;
+    }
+  }
+}
+
+// Tree over the nch chunk nodes of one row (256 threads of K nodes each,
+// padded with zero nodes to 256 * K: the padding changes no bit).
+template <bool NN, int K>
+__device__ __forceinline__ NodeD top_tree_d(const NodeD *__restrict__ nodes, int64_t nch, NodeD *slots) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  NodeD nd[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t idx = (int64_t)threadIdx.x * K + k;
+    const NodeD t = nodes[idx < nch ? idx : nch - 1];  // unconditional: the loads overlap
+    nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
+  }
+  NodeD r = wave_tree_d<NN>(node_tree_d<0, K, K, NN>(nd));
+  return block_tree_d<4, NN>(r, slots, w, lane);
+}
+
+template <int PASS, int K>
+__global__ __launch_bounds__(256) void k_long_top_d(const double *__restrict__ x, int64_t n, int64_t ld,
+                                                    int64_t nch, int64_t ddof, SliceWsD ws,
+                                                    double *__restrict__ var_out, double *__restrict__ mean_out) {
+  __shared__ NodeD slots[2][4];
+  const int64_t r = blockIdx.x;
+  if constexpr (PASS == 0) {
+    const NodeD ny = top_tree_d<false, K>(ws.ny + r * nch, nch, slots[0]);
+    if (threadIdx.x == 0) ws.m[r] = root_value_d(ny) / (double)n;
+  } else {
+    const NodeD nd = top_tree_d<false, K>(ws.nd + r * nch, nch, slots[0]);
+    const NodeD nq = top_tree_d<true, K>(ws.nq + r * nch, nch, slots[1]);
+    if (threadIdx.x == 0)
+      finalize_d(nd, nq, x[r * ld], ws.m[r], n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
+  }
+}
+
+// Axis 0: rows [r0, r0 + E) of the V columns starting at c0 (a multiple of
+// V); columns past C read the last in-range ones (never written), rows past
+// R read row R-1 (masked to +0 afterwards).
+template <int V, int E>
+__device__ __forceinline__ void load_cols_tile_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t c0,
+                                                 int64_t r0, bool full, double (&v)[V][E]) {
+  const int64_t cc = c0 < C ? c0 : C - V;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t r = full ? r0 + i : (r0 + i < R ? r0 + i : R - 1);
+    const double *p = x + r * C + cc;
+    if constexpr (V == 2) {
+      const double2 g = *reinterpret_cast<const double2 *>(p);
+      v[0][i] = g.x;
+      v[1][i] = g.y;
+    } else {
+      v[0][i] = p[0];
+    }
+  }
+}
+
+template <int V, int E>
+__device__ __forceinline__ void shift_cols_tile_d(double (&v)[V][E], const double (&x0)[V], bool full, int valid) {
+#pragma unroll
+  for (int k = 0; k < V; ++k)
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[k][i] = (full || i < valid) ? v[k][i] - x0[k] : 0.0;
+}
+
+// Tree over p[0], p[stride], ... p[(count-1)*stride], zero-padded to a power
+// of two: aligned groups of C64_GROUP nodes level by level, each group node
+// written back in place of the group's first.  One thread per column.
+template <bool NN>
+__device__ NodeD chunk_tree_d(NodeD *p, int64_t stride, int64_t count) {
+  while (true) {
+    const int64_t groups = (count + C64_GROUP - 1) / C64_GROUP;
+    NodeD last = {0.0, 0.0};
+    for (int64_t g = 0; g < groups; ++g) {
+      NodeD sub[C64_GROUP / 8];
+#pragma unroll
+      for (int b = 0; b < C64_GROUP / 8; ++b) {
+        NodeD nd[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int64_t idx = g * C64_GROUP + b * 8 + k;
+          const NodeD t = p[(idx < count ? idx : count - 1) * stride];
+          nd[k] = idx < count ? t : NodeD{0.0, 0.0};
+        }
+        sub[b] = node_tree_d<0, 8, 8, NN>(nd);
+      }
+      last = node_tree_d<0, C64_GROUP / 8, C64_GROUP / 8, NN>(sub);
+      if (groups > 1) p[g * stride] = last;
+    }
+    if (groups == 1) return last;
+    count = groups;
+  }
+}
+
+// The same over nch <= C64_GROUP nodes, nothing written back.
+__device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, int64_t nch) {
+  NodeD sub[C64_GROUP / 8];
+#pragma unroll
+  for (int b = 0; b < C64_GROUP / 8; ++b) {
+    NodeD nd[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t idx = b * 8 + k;
+      const NodeD t = p[(idx < nch ? idx : nch - 1) * stride];
+      nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
+    }
+    sub[b] = node_tree_d<0, 8, 8, false>(nd);
+  }
+  return node_tree_d<0, C64_GROUP / 8, C64_GROUP / 8, false>(sub);
+}
+
+template <int V>
+__global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restrict__ x, int64_t R, int64_t C,
+                                                         int64_t nch, SliceWsD ws) {
+  constexpr int E = L64_E, W = L64_W, NC = 64 * V;
+  __shared__ NodeD s[W][V][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t c0 = cb * NC + (int64_t)lane * V;
+  const int64_t r0 = j * C64_CHUNK + (int64_t)w * E;
+  const bool full = r0 + E <= R;
+  const int64_t left = R - r0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  double v[V][E];
+  load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
+  double x0[V];
+  const int64_t cc = c0 < C ? c0 : C - V;
+#pragma unroll
+  for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
+  shift_cols_tile_d<V, E>(v, x0, full, valid);
+#pragma unroll
+  for (int k = 0; k < V; ++k) s[w][k][lane] = lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k]);
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < NC) {
+    const int k = t >> 6, l = t & 63;  // thread t combines column V*l + k of the block
+    const int64_t col = cb * NC + (int64_t)l * V + k;
+    if (col < C) {
+      NodeD nn[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) nn[i] = s[i][k][l];
+      ws.ny[j * C + col] = node_tree_d<0, W, W, false>(nn);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cols_m_d(int64_t R, int64_t C, int64_t nch, SliceWsD ws) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= C) return;
+  ws.m[col] = root_value_d(chunk_tree_d<false>(ws.ny + col, C, nch)) / (double)R;
+}
+
+// MLOCAL: nch <= C64_GROUP, and every workgroup forms m for its own columns
+// (no k_cols_m_d launch); else m comes from k_cols_m_d.
+template <int V, bool MLOCAL>
+__global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restrict__ x, int64_t R, int64_t C,
+                                                          int64_t nch, SliceWsD ws) {
+  constexpr int E = L64_E, W = L64_W, NC = 64 * V;
+  __shared__ NodeD sd[W][V][64];
+  __shared__ NodeD sq[W][V][64];
+  __shared__ double sm[V][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t c0 = cb * NC + (int64_t)lane * V;
+  const int64_t r0 = j * C64_CHUNK + (int64_t)w * E;
+  const bool full = r0 + E <= R;
+  const int64_t left = R - r0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  double v[V][E];
+  load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
+  const int64_t cc = c0 < C ? c0 : C - V;
+  if constexpr (MLOCAL) {
+    const int t = threadIdx.x;
+    if (t < NC) {
+      const int k = t >> 6, l = t & 63;  // column V*l + k of the block, clamped like the loads
+      const int64_t col = cb * NC + (int64_t)l * V + k;
+      const int64_t ccol = col < C ? col : C - 1;
+      sm[k][l] = root_value_d(chunk_tree_1_d(ws.ny + ccol, C, nch)) / (double)R;
+    }
+    __syncthreads();
+  }
+  double x0[V], m[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    x0[k] = x[cc + k];
+    m[k] = MLOCAL ? sm[k][lane] : ws.m[cc + k];
+  }
+  shift_cols_tile_d<V, E>(v, x0, full, valid);
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    NodeD nd, nq;
+    if (full) lane_tree_dq_d<false, 0, E, E>(v[k], m[k], E, nd, nq);
+    else lane_tree_dq_d<true, 0, E, E>(v[k], m[k], valid, nd, nq);
+    sd[w][k][lane] = nd;
+    sq[w][k][lane] = nq;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < NC) {
+    const int k = t >> 6, l = t & 63;
+    const int64_t col = cb * NC + (int64_t)l * V + k;
+    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][l];  // for k_cols_fin_d
+    if (col < C) {
+      NodeD a[W], b[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        a[i] = sd[i][k][l];
+        b[i] = sq[i][k][l];
+      }
+      ws.nd[j * C + col] = node_tree_d<0, W, W, false>(a);
+      ws.nq[j * C + col] = node_tree_d<0, W, W, true>(b);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_cols_fin_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                    int64_t ddof, SliceWsD ws, double *__restrict__ var_out,
+                                                    double *__restrict__ mean_out) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= C) return;
+  const NodeD nd = chunk_tree_d<false>(ws.nd + col, C, nch);
+  const NodeD nq = chunk_tree_d<true>(ws.nq + col, C, nch);
+  finalize_d(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+}
+
 __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) {
@@ -479,8 +793,62 @@ __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int
   }
 }
 
-constexpr int64_t V64_ROWS_MAX_N = 8192;
-constexpr int64_t V64_COLS_MAX_R = 1024;
+constexpr int64_t V64_ROWS_MAX_N = 16384;  // one workgroup per row
+constexpr int64_t V64_COLS_MAX_R = 1024;   // one workgroup per 64-column tile
+constexpr int64_t V64_MAX_ELEMS = 1LL << 39;
+
+size_t round256_d(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of the long-slice paths: three node arrays of nodes_per_array
+// nodes and one double per slice, each part 256-byte aligned.
+size_t slice_ws_bytes(int64_t nodes_per_array, int64_t nslices) {
+  return 3 * round256_d((size_t)nodes_per_array * sizeof(NodeD)) + round256_d((size_t)nslices * sizeof(double));
+}
+
+SliceWsD slice_ws(void *workspace, int64_t nodes_per_array) {
+  char *p = reinterpret_cast<char *>(workspace);
+  const size_t a = round256_d((size_t)nodes_per_array * sizeof(NodeD));
+  return {reinterpret_cast<NodeD *>(p), reinterpret_cast<NodeD *>(p + a), reinterpret_cast<NodeD *>(p + 2 * a),
+          reinterpret_cast<double *>(p + 3 * a)};
+}
+
+// Workspace bytes (0: single-workgroup slices; -1: unsupported).
+size_t var64_ws(int64_t rows, int64_t cols, bool ax1) {
+  const int64_t n = ax1 ? cols : rows, nslices = ax1 ? rows : cols;
+  if (n == 0 || nslices == 0) return 0;
+  if (ax1) {
+    if (n <= V64_ROWS_MAX_N) return 0;
+    const int64_t nch = (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK;
+    if (nch > L64_MAX_CHUNKS) return (size_t)-1;
+    return slice_ws_bytes(rows * nch, rows);
+  }
+  if (n <= V64_COLS_MAX_R) return 0;
+  return slice_ws_bytes(((n + C64_CHUNK - 1) / C64_CHUNK) * cols, cols);
+}
+
+template <int PASS>
+void launch_long_top_d(const double *x, int64_t n, int64_t ld, int64_t nch, int64_t ddof, const SliceWsD &ws,
+                       double *var, double *mean, dim3 grid, hipStream_t st) {
+  if (nch <= 256) k_long_top_d<PASS, 1><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+  else if (nch <= 1024) k_long_top_d<PASS, 4><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+  else k_long_top_d<PASS, L64_TOP_MAX_K><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+}
+
+template <int V>
+void launch_cols_d(const double *x, int64_t R, int64_t C, int64_t ddof, const SliceWsD &ws, double *var,
+                   double *mean, hipStream_t st) {
+  const int64_t nch = (R + C64_CHUNK - 1) / C64_CHUNK;
+  const int64_t ncb = (C + 64 * V - 1) / (64 * V);
+  const dim3 grid((unsigned)(ncb * nch)), block(64 * L64_W), per_col((unsigned)((C + 255) / 256));
+  k_cols_y_d<V><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  if (nch <= C64_GROUP) {
+    k_cols_dq_d<V, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  } else {
+    k_cols_m_d<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
+    k_cols_dq_d<V, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  }
+  k_cols_fin_d<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+}
 
 }  // namespace
 
@@ -527,8 +895,15 @@ sv_status sv_tree_sum_f64(const double *x, int64_t n, double *out, void *workspa
   return check_launch("sv_tree_sum_f64");
 }
 
+size_t sv_variance_f64_workspace_size(int64_t rows, int64_t cols, int axis) {
+  if (rows < 0 || cols < 0) return (size_t)-1;
+  if (axis != 0 && axis != 1 && axis != -1 && axis != -2) return (size_t)-1;
+  if (cols > 0 && rows > V64_MAX_ELEMS / cols) return (size_t)-1;
+  return var64_ws(rows, cols, axis == 1 || axis == -1);
+}
+
 sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, double *var_out,
-                          double *mean_out, void *stream) {
+                          double *mean_out, void *workspace, size_t workspace_bytes, void *stream) {
   if (rows < 0 || cols < 0)
     return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: negative shape [%lld, %lld]", (long long)rows,
                 (long long)cols);
@@ -538,14 +913,24 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
   const int64_t n = ax1 ? cols : rows;
+  if (cols > 0 && rows > V64_MAX_ELEMS / cols)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: rows * cols above 2^39");
   if (nslices == 0) return ok();
   if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: var_out is NULL");
-  if (rows * cols > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is NULL");
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is NULL");
   if (reinterpret_cast<uintptr_t>(x) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is not 8-byte aligned");
-  if ((ax1 && n > V64_ROWS_MAX_N) || (!ax1 && n > V64_COLS_MAX_R) || nslices > (int64_t)UINT32_MAX)
-    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: slices of %lld values along axis %d are not supported "
-                "(at most %lld on axis 1, %lld on axis 0)", (long long)n, ax1 ? 1 : 0,
-                (long long)V64_ROWS_MAX_N, (long long)V64_COLS_MAX_R);
+  if (nslices > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: %lld slices exceed the grid", (long long)nslices);
+  const size_t need = var64_ws(rows, cols, ax1);
+  if (need == (size_t)-1)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: rows of %lld values exceed %lld chunks", (long long)n,
+                (long long)L64_MAX_CHUNKS);
+  if (need > 0) {
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_f64: workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(SV_ERR_WORKSPACE, "sv_variance_f64: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!svh::aligned256(workspace)) return fail(SV_ERR_WORKSPACE, "sv_variance_f64: workspace is not 256-byte aligned");
+  }
   const sv_status dev = check_device();
   if (dev != SV_OK) return dev;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -565,8 +950,24 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     if (n <= 256) SV_ROWS64(4, 1);
     else if (n <= 1024) SV_ROWS64(16, 1);
     else if (n <= 4096) SV_ROWS64(16, 4);
-    else SV_ROWS64(16, 8);
+    else if (n <= 8192) SV_ROWS64(16, 8);
+    else if (n <= V64_ROWS_MAX_N) SV_ROWS64(16, 16);
+    else {
+      const int64_t nch = (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK;
+      const SliceWsD ws = slice_ws(workspace, rows * nch);
+      const dim3 lgrid((unsigned)(rows * nch)), lblock(64 * L64_W);
+      if (vec) k_long_rows_d<0, true><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
+      else k_long_rows_d<0, false><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
+      launch_long_top_d<0>(x, n, cols, nch, ddof, ws, var_out, mean_out, grid, st);
+      if (vec) k_long_rows_d<1, true><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
+      else k_long_rows_d<1, false><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
+      launch_long_top_d<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, grid, st);
+    }
 #undef SV_ROWS64
+  } else if (n > V64_COLS_MAX_R) {
+    const SliceWsD ws = slice_ws(workspace, ((n + C64_CHUNK - 1) / C64_CHUNK) * cols);
+    if (svh::aligned16(x) && cols % 2 == 0) launch_cols_d<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+    else launch_cols_d<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
   } else {
     const dim3 grid((unsigned)((cols + 63) / 64));
 #define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)

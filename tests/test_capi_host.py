@@ -149,11 +149,29 @@ def test_f64_sizes_and_argument_errors(L):
     assert L.sv_tree_sum_f64(BAD, 10, BAD, None, 0, None) == SV_ERR_WORKSPACE
     assert L.sv_tree_sum_f64(BAD, (1 << 35) + 1, BAD, None, 0, None) == SV_ERR_UNSUPPORTED
     out = ctypes.c_void_p(0x2000)
-    assert L.sv_variance_f64(BAD, 4, 4, 3, 0, out, None, None) == SV_ERR_INVALID_ARGUMENT
-    assert L.sv_variance_f64(BAD, 4, 4, 1, -1, out, None, None) == SV_ERR_INVALID_ARGUMENT
-    assert L.sv_variance_f64(BAD, 2, 8193, 1, 0, out, None, None) == SV_ERR_UNSUPPORTED
-    assert L.sv_variance_f64(BAD, 1025, 2, 0, 0, out, None, None) == SV_ERR_UNSUPPORTED
-    assert L.sv_variance_f64(None, 0, 5, 1, 0, None, None, None) == 0
+    assert L.sv_variance_f64(BAD, 4, 4, 3, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f64(BAD, 4, 4, 1, -1, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_f64(ctypes.c_void_p(0x1004), 4, 4, 1, 0, out, None, None, 0, None) == \
+        SV_ERR_INVALID_ARGUMENT  # not 8-byte aligned
+    assert L.sv_variance_f64(None, 0, 5, 1, 0, None, None, None, 0, None) == 0
+    # workspace: none for single-workgroup slices; long slices three arrays
+    # of 16 bytes per chunk per slice and 8 bytes per slice, each rounded to 256
+    r256 = lambda b: (b + 255) // 256 * 256
+    ws = L.sv_variance_f64_workspace_size
+    assert ws(7, 16384, 1) == 0 and ws(1024, 9, 0) == 0 and ws(0, 5, 0) == 0
+    assert ws(3, 16385, 1) == 3 * r256(3 * 3 * 16) + r256(3 * 8)
+    assert ws(1025, 7, 0) == 3 * r256(9 * 7 * 16) + r256(7 * 8)
+    assert ws(4096, 4096, 0) == 3 * r256(32 * 4096 * 16) + r256(4096 * 8)
+    assert ws(1, 8192 * 8192, 1) == 3 * r256(8192 * 16) + r256(8)
+    assert ws(1, 8192 * 8192 + 1, 1) == ctypes.c_size_t(-1).value
+    assert ws((1 << 20) + 1, 1 << 19, 1) == ctypes.c_size_t(-1).value  # above 2^39 values
+    assert ws(2, 3, 4) == ctypes.c_size_t(-1).value
+    # long slices need it: missing, short and misaligned workspaces are refused
+    assert L.sv_variance_f64(BAD, 2, 20000, 1, 0, out, None, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_f64(BAD, 2000, 3, 0, 0, out, None, ctypes.c_void_p(0x100000), 8, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_f64(BAD, 2000, 3, 0, 0, out, None, ctypes.c_void_p(0x100040), 1 << 20, None) == \
+        SV_ERR_WORKSPACE
+    assert L.sv_variance_f64(BAD, 1, 8192 * 8192 + 1, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
 
 
 def test_complex_argument_errors_and_sizes(L):

@@ -90,7 +90,8 @@ def test_var64_page_datasets_and_square(torch_dev):
     check_var64(torch_dev, W.c4_matrix().astype(np.float64)[:1024], 1)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 64, 255, 256, 257, 1000, 1024, 1025, 4095, 4096, 4097, 8192])
+@pytest.mark.parametrize("n", [1, 2, 3, 64, 255, 256, 257, 1000, 1024, 1025, 4095, 4096, 4097, 8192, 8193, 16384,
+                               16385, 40000])
 def test_var64_rows(torch_dev, n):
     rng = np.random.default_rng(n)
     a = rng.normal(1e8, 3, (19, n))
@@ -100,13 +101,29 @@ def test_var64_rows(torch_dev, n):
     check_var64(torch_dev, b, 1)
 
 
-@pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 512, 513, 1000, 1024])
+@pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 512, 513, 1000, 1024, 1025, 3000, 8192, 9001])
 def test_var64_cols(torch_dev, R):
+    # above 1024 rows: 128-row chunks, two adjacent columns per lane (16-byte
+    # loads) when the width is even, one otherwise; more than 32 chunks per
+    # column take the separate m launch
     rng = np.random.default_rng(R)
     for C in (1, 63, 64, 65, 130):
         a = rng.normal(-5e3, 2, (R, C))
         check_var64(torch_dev, a, 0)
         check_var64(torch_dev, a, 0, 1)
+    if R > 1024:
+        b = W.adversarial_values(R * 300, R).astype(np.float64).reshape(R, 300) * 1e250
+        check_var64(torch_dev, b, 0)
+
+
+@pytest.mark.parametrize("shape,axis", [((3, 300_001), 1), ((1, 1 << 20), 1), ((70_000, 6), 0), ((4096, 4096), 0)])
+def test_var64_long_slices(torch_dev, shape, axis):
+    # chunked paths: long rows (8192-value chunks, per-row top trees) and
+    # tall columns (128-row chunks; 547 chunks per column for 70,000 rows)
+    rng = np.random.default_rng(shape[0] + shape[1])
+    a = rng.normal(3e9, 7, shape)
+    check_var64(torch_dev, a, axis)
+    check_var64(torch_dev, np.full(shape, 1e307), axis)
 
 
 def test_var64_top_of_range_and_specials(torch_dev):
