@@ -170,8 +170,11 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
  *   mean_out   complex64 (interleaved), one per slice, or NULL:
  *              (mean(re), mean(im))
  *   workspace  sv_variance_c64_workspace_size(rows, cols, axis) bytes,
- *              256-byte aligned, no initialisation (axis 1 stages the split
- *              parts: 8 bytes per input value)
+ *              256-byte aligned, no initialisation; NULL allowed when that
+ *              size is 0.  Axis 1 rows of up to 8192 values are read once
+ *              and need none; longer rows stage the split parts (8 bytes per
+ *              input value); axis 0 reads the interleaved array as float32
+ *              [rows, 2 * cols] columns
  * Errors and asynchrony as for sv_variance_f32.
  */
 size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis);

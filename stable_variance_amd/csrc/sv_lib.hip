@@ -386,6 +386,101 @@ __global__ __launch_bounds__(256) void k_split_rows(const float *__restrict__ z,
   }
 }
 
+// Axis 1 in one pass: a row of n complex values is read once (8 bytes per
+// value), each lane holding E consecutive values, split in registers into
+// its real and imaginary parts; the two float32 variances run side by side
+// with the same tree topology as k_var_rows, and var = fl(var(re) +
+// var(im)), mean = (mean(re), mean(im)).  W waves own consecutive 64*E
+// ranges; a wave wholly past the row skips its trees (its nodes are +0).
+template <int E, int W, bool VEC>
+__global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict__ z, int64_t n, int64_t ddof,
+                                                         float *__restrict__ var_out, float *__restrict__ mean_out) {
+  __shared__ Node slots[6][W];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
+  const float *__restrict__ p = z + 2 * row * n;
+  const int64_t base = (int64_t)w * 64 * E;  // first complex value of this wave
+  const bool empty = base >= n;
+  float f[2 * E];
+  sv::load_tile<2 * E, VEC, 1, false>(p + 2 * base, 2 * (n - base), nullptr, f, lane);
+  const float x0r = p[0], x0i = p[1];
+  const bool full = base + 64 * E <= n;
+  const int64_t left = n - base - (int64_t)lane * E;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  float re[E], im[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    re[i] = (full || i < valid) ? f[2 * i] - x0r : 0.0f;
+    im[i] = (full || i < valid) ? f[2 * i + 1] - x0i : 0.0f;
+  }
+  Node yr = sv::zero_node(), yi = sv::zero_node();
+  if (!empty) {
+    yr = sv::wave_tree<sv::NODE_TWOSUM>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(re));
+    yi = sv::wave_tree<sv::NODE_TWOSUM>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(im));
+  }
+  if constexpr (W > 1) {
+    if (lane == 0) {
+      slots[0][w] = yr;
+      slots[1][w] = yi;
+    }
+    __syncthreads();
+    Node a[W], b[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      a[i] = slots[0][i];
+      b[i] = slots[1][i];
+    }
+    yr = sv::node_tree<0, W, W>(a);
+    yi = sv::node_tree<0, W, W>(b);
+  }
+  const float mr = sv::root_value(yr) / (float)n;
+  const float mi = sv::root_value(yi) / (float)n;
+  Node dr = sv::zero_node(), qr = sv::zero_node(), di = sv::zero_node(), qi = sv::zero_node();
+  if (!empty) {
+    if (full) {
+      sv::lane_tree_dq<false, 0, E, E>(re, mr, E, dr, qr);
+      sv::lane_tree_dq<false, 0, E, E>(im, mi, E, di, qi);
+    } else {
+      sv::lane_tree_dq<true, 0, E, E>(re, mr, valid, dr, qr);
+      sv::lane_tree_dq<true, 0, E, E>(im, mi, valid, di, qi);
+    }
+    dr = sv::wave_tree<sv::NODE_TWOSUM>(dr);
+    qr = sv::wave_tree<sv::NODE_NN>(qr);
+    di = sv::wave_tree<sv::NODE_TWOSUM>(di);
+    qi = sv::wave_tree<sv::NODE_NN>(qi);
+  }
+  if constexpr (W > 1) {
+    if (lane == 0) {
+      slots[2][w] = dr;
+      slots[3][w] = qr;
+      slots[4][w] = di;
+      slots[5][w] = qi;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    Node t[4][W];
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k][i] = slots[2 + k][i];
+    dr = sv::node_tree<0, W, W>(t[0]);
+    qr = sv::node_tree<0, W, W, sv::NODE_NN>(t[1]);
+    di = sv::node_tree<0, W, W>(t[2]);
+    qi = sv::node_tree<0, W, W, sv::NODE_NN>(t[3]);
+  }
+  if (threadIdx.x == 0) {
+    float vr, vi, mean_r, mean_i;
+    finalize(dr, qr, x0r, mr, n, ddof, &vr, &mean_r);
+    finalize(di, qi, x0i, mi, n, ddof, &vi, &mean_i);
+    var_out[row] = vr + vi;
+    if (mean_out) {
+      mean_out[2 * row] = mean_r;
+      mean_out[2 * row + 1] = mean_i;
+    }
+  }
+}
+
 // var[j] = fl(v[2j] + v[2j+1]): the variance of the real part plus that of
 // the imaginary part.
 __global__ __launch_bounds__(256) void k_pair_add(const float *__restrict__ v, int64_t count, float *__restrict__ out) {
@@ -1084,6 +1179,8 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
 
 // ------------------------------------------------------------------ host side
 
+constexpr int64_t C64_FUSED_MAX_N = 8192;  // complex rows reduced in one pass (k_var_rows_c64)
+
 // Launch-geometry tuning (never changes a result bit).
 struct Tuning {
   int sum_load_path = 0;      // 0: coalesced loads + LDS transpose, 1: per-lane contiguous loads
@@ -1617,6 +1714,7 @@ size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis) {
   if (cols > 0 && rows > VAR_MAX_ELEMS / 2 / cols) return (size_t)-1;
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
+  if (ax1 && cols <= C64_FUSED_MAX_N) return 0;  // one pass, no staging
   const size_t inner = ax1 ? sv_variance_f32_workspace_size(2 * rows, cols, 1)
                            : sv_variance_f32_workspace_size(rows, 2 * cols, 0);
   if (inner == (size_t)-1) return (size_t)-1;
@@ -1635,22 +1733,48 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
   if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: ddof = %lld < 0", (long long)ddof);
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
-  if (nslices == 0) return ok();
-  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: var_out is NULL");
-  if (rows * cols > 0 && !z) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: z is NULL");
-  if (reinterpret_cast<uintptr_t>(z) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: z is not 8-byte aligned");
   const size_t need = sv_variance_c64_workspace_size(rows, cols, axis);
   if (need == (size_t)-1) return fail(SV_ERR_UNSUPPORTED, "sv_variance_c64: shape [%lld, %lld] not supported",
                                       (long long)rows, (long long)cols);
-  if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace is NULL (%zu bytes needed)", need);
-  if (workspace_bytes < need)
-    return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace is not 256-byte aligned");
+  if (nslices == 0) return ok();
+  if (nslices > 0x7fffffffLL)
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_c64: %lld slices exceed the grid", (long long)nslices);
+  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: var_out is NULL");
+  if (rows * cols > 0 && !z) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: z is NULL");
+  if (reinterpret_cast<uintptr_t>(z) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_c64: z is not 8-byte aligned");
+  if (need > 0) {
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(SV_ERR_WORKSPACE, "sv_variance_c64: workspace is not 256-byte aligned");
+  }
   const sv_status dev = check_device();
   if (dev != SV_OK) return dev;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (ax1 && cols <= C64_FUSED_MAX_N) {
+    if (cols == 0) {  // empty rows: var and both mean parts are NaN
+      k_fill<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, st>>>(var_out, rows, __builtin_nanf(""));
+      if (mean_out) k_fill<<<dim3((unsigned)((2 * rows + 255) / 256)), 256, 0, st>>>(mean_out, 2 * rows, __builtin_nanf(""));
+      return check_launch("sv_variance_c64");
+    }
+    // rows start 16-byte aligned when z is and cols is even
+    const bool vec = aligned16(z) && (cols % 2 == 0);
+    const dim3 grid((unsigned)rows);
+#define SV_ROWS_C64(E, W)                                                                                 \
+  do {                                                                                                    \
+    if (vec) k_var_rows_c64<E, W, true><<<grid, dim3(64 * W), 0, st>>>(z, cols, ddof, var_out, mean_out);  \
+    else k_var_rows_c64<E, W, false><<<grid, dim3(64 * W), 0, st>>>(z, cols, ddof, var_out, mean_out);     \
+  } while (0)
+    if (cols <= 256) SV_ROWS_C64(4, 1);
+    else if (cols <= 1024) SV_ROWS_C64(16, 1);
+    else if (cols <= 2048) SV_ROWS_C64(16, 2);
+    else if (cols <= 4096) SV_ROWS_C64(16, 4);
+    else SV_ROWS_C64(16, 8);
+#undef SV_ROWS_C64
+    return check_launch("sv_variance_c64");
+  }
   char *wp = reinterpret_cast<char *>(workspace);
   float *vparts = reinterpret_cast<float *>(wp);
   wp += round256((size_t)2 * nslices * sizeof(float));

@@ -441,7 +441,11 @@ def test_complex_printed_values(torch_dev):
     assert v[0] == float(g["identical_variance"])
 
 
-@pytest.mark.parametrize("shape", [(64, 1000), (3, 4096), (5, 20000), (1000, 64), (2000, 3), (1, 1), (7, 2)])
+# rows of up to 8192 values take the one-pass kernel (odd widths: per-lane
+# scalar loads); longer rows the staged split
+@pytest.mark.parametrize("shape", [(64, 1000), (3, 4096), (5, 20000), (1000, 64), (2000, 3), (1, 1), (7, 2),
+                                   (9, 257), (4, 1025), (6, 2047), (3, 5000), (2, 8191), (2, 8192), (2, 8193),
+                                   (11, 0)])
 @pytest.mark.parametrize("axis", [0, 1])
 def test_complex_shapes(torch_dev, shape, axis):
     rng = np.random.default_rng(shape[0] * 7 + shape[1])
@@ -450,6 +454,17 @@ def test_complex_shapes(torch_dev, shape, axis):
     z = (re + 1j * im).astype(np.complex64)
     check_var_c64(torch_dev, z, axis, 0)
     check_var_c64(torch_dev, z, axis, 1)
+
+
+def test_complex_rows_specials(torch_dev):
+    # NaN / Inf / overflow in one part only: the other part's variance is
+    # unaffected and the sum follows IEEE addition
+    a = special_rows(3000, seed=5)
+    b = np.random.default_rng(6).normal(0, 1, a.shape).astype(np.float32)
+    for re, im in ((a, b), (b, a)):
+        z = np.empty(a.shape, np.complex64)  # parts set directly: 1j * inf would be nan + inf j
+        z.real, z.imag = re, im
+        check_var_c64(torch_dev, z, 1)
 
 
 def test_complex_then_sum_share_nothing(torch_dev):
