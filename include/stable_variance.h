@@ -306,10 +306,12 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "var_dma_rows"   rows of 1025..4096 values per wave staged by direct
  *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
  *   "var_split"      rows of 1025..16384 values: waves per 4096 values of
- *                    the row's power-of-two tile, 1, 2 (default), 4 or 8
- *                    (64, 32, 16 or 8 values per lane; a 2048-value tile
- *                    takes at most 32 values per lane, a 16384-value tile at
- *                    most 16 waves)
+ *                    the row's power-of-two tile, 1, 2, 4 or 8 (64, 32, 16
+ *                    or 8 values per lane; a 2048-value tile takes at most 32
+ *                    values per lane, a 16384-value tile at most 16 waves), or
+ *                    0 (default): 32, 16 or 8 values per lane, whichever
+ *                    gives the least VALU work for the row length (32 for
+ *                    every power of two)
  *   "var_lds_pad"    unused dynamic LDS bytes per row workgroup, 0..65536
  *                    (default 0): a cap on resident waves, for measurements
  *   "var_cols_single_max"  axis 0: columns of up to this many rows are

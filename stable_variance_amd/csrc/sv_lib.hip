@@ -1191,7 +1191,7 @@ struct Tuning {
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
   int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
-  int var_split = 2;          // waves per 4096 values of a row of 1025..16384 values (1, 2, 4, 8)
+  int var_split = 0;          // waves per 4096 values of a row of 1025..16384 values (1, 2, 4, 8; 0 auto)
   int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
   int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
   int var_cols_single_max = 1024;  // axis 0: rows up to which one workgroup holds a column tile (<= 1024)
@@ -1402,9 +1402,28 @@ void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t l
 // values) is shared by var_split waves per 4096 values, E = 64 / var_split
 // values per lane (a 2048-value tile takes at most 32 values per lane, a
 // 16384-value tile at most 16 waves).
+// var_split 0 (auto): the values per lane E in {32, 16, 8} that minimise the
+// VALU work of a row, (values in the waves the row reaches) x (23 per value
+// for the method + about 144 / E for the cross-lane levels); ties go to the
+// larger E.  Waves wholly past the row cost nothing.
+int auto_split(int64_t n) {
+  int best = 2;
+  int64_t best_cost = INT64_MAX;
+  for (int e = 32; e >= 8; e /= 2) {
+    const int64_t wave = 64LL * e;
+    const int64_t reached = (n + wave - 1) / wave * wave;
+    const int64_t cost = reached * (23 * e + 144) / e;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = 64 / e;
+    }
+  }
+  return best;
+}
+
 void launch_rows_tile(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                       float *mean, hipStream_t st) {
-  const int s = g_tune.var_split;
+  const int s = g_tune.var_split != 0 ? g_tune.var_split : auto_split(n);
   if (n <= 2048) {
     if (s <= 2) launch_rows_split<32, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
     else if (s == 4) launch_rows_split<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
@@ -1851,8 +1870,8 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_split") == 0) {
-    if (value != 1 && value != 2 && value != 4 && value != 8)
-      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_split must be 1, 2, 4 or 8");
+    if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_split must be 0, 1, 2, 4 or 8");
     g_tune.var_split = (int)value;
     return ok();
   }

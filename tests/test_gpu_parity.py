@@ -46,6 +46,7 @@ VAR_GEOMETRIES = {
     "lds_transpose": {"var_load_path": 0, "var_nt": 0},
     "staged_transpose": {"var_load_path": 2},
     "split1": {"var_split": 1},
+    "split2": {"var_split": 2},
     "split4": {"var_split": 4},
     "occupancy_capped": {"var_lds_pad": 20000},
     "split8": {"var_split": 8},
