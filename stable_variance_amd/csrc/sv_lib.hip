@@ -1201,12 +1201,6 @@ struct Tuning {
 };
 Tuning g_tune;
 
-int ceil_log2(int64_t v) {
-  int l = 0;
-  while ((1LL << l) < v) ++l;
-  return l;
-}
-
 constexpr int64_t SUM_MAX_N = 1LL << 36;
 constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
 constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel
