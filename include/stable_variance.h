@@ -34,7 +34,10 @@
  *   - The call is asynchronous: it enqueues work on `stream` (a hipStream_t;
  *     NULL is the default stream) and returns.  Outputs are valid once the
  *     stream has been synchronised.  Inputs must stay valid until then.
- *   - Calls never throw and never allocate device memory.
+ *   - Calls never throw and never allocate device memory.  They make no
+ *     memset or copy calls and no host synchronisation, and every counter
+ *     they use is reset by the kernels, so a sequence of calls can be
+ *     captured once in a HIP graph and replayed.
  *   - Calls that share a workspace must be ordered (same stream); two
  *     concurrent calls need two workspaces.
  */
