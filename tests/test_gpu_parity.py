@@ -201,6 +201,33 @@ def test_sum_workspace_left_zero_and_deterministic(torch_dev):
     assert same_bits(r1.item(), r0)
 
 
+def test_concurrent_streams_own_workspaces(torch_dev):
+    # two default-priority streams, each with its own workspaces (the binding
+    # keeps one per stream), running sums and both variance paths at once
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    xs = [W.sum_cancelling_pairs(3_000_000, 0.01, seed=s) for s in (21, 22)]
+    cols = [np.random.default_rng(s).normal(7e3, 2, (2500, 300)).astype(np.float32) for s in (23, 24)]
+    rows = [np.random.default_rng(s).normal(-4e2, 1, (700, 3000)).astype(np.float32) for s in (25, 26)]
+    dx = [torch.from_numpy(a).to(dev) for a in xs]
+    dc = [torch.from_numpy(a).to(dev) for a in cols]
+    dr = [torch.from_numpy(a).to(dev) for a in rows]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    out = [[], []]
+    for rep in range(3):
+        for k, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                out[k].append((sv.tree_sum(dx[k]), sv.var(dc[k], dim=0), sv.var(dr[k], dim=1)))
+    torch.cuda.synchronize()
+    for k in range(2):
+        want = (oracle.tree_sum(xs[k]), oracle.variance(cols[k], axis=0)[0], oracle.variance(rows[k], axis=1)[0])
+        for s_, vc, vr in out[k]:
+            assert same_bits(np.float32(s_.item()), want[0])
+            assert same_bits(vc.cpu().numpy(), want[1]) and same_bits(vr.cpu().numpy(), want[2])
+
+
 def test_sum_full_size_1e8(torch_dev):
     # 10^8 values (400 MB): 99% N(0,1), 1% large cancelling pairs, seed 3,
     # in the benchmark's launch configuration and in two others.
