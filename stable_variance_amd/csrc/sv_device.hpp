@@ -578,6 +578,21 @@ struct Chunk {
     else return 64 * i + lane;
   }
 
+  // Loads of a chunk that lies wholly inside the data: no branch.
+  __device__ static __forceinline__ void issue_full(const float *__restrict__ p, int lane, float (&raw)[E]) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < J; ++k) {
+        const int e = (LOADP == 1) ? lane * E + 4 * k : 256 * k + 4 * lane;
+        const float4 g = ld4<NT>(p + e);
+        raw[4 * k] = g.x; raw[4 * k + 1] = g.y; raw[4 * k + 2] = g.z; raw[4 * k + 3] = g.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) raw[i] = ld1<NT>(p + raw_index(i, lane));
+    }
+  }
+
   __device__ static __forceinline__ void issue(const float *__restrict__ p, int64_t len, int lane, float (&raw)[E]) {
     const int lim = len <= 0 ? 0 : (len >= SIZE ? SIZE : (int)len);
     if (lim == SIZE) {

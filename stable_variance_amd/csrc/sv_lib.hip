@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
   __shared__ unsigned is_last;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches
   const int64_t G = 1LL << log2_g;
   const int nb = (int)gridDim.x;
   const int bid = xcd ? sv::xcd_contiguous((int)blockIdx.x, nb) : (int)blockIdx.x;  // logical workgroup
@@ -298,9 +298,47 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
       }
     }
   };
-  if (G >= D) stream(std::integral_constant<int, D>{});
-  else if (G >= 2) stream(std::integral_constant<int, 2>{});
-  else stream(std::integral_constant<int, 1>{});
+  // The same ring for a run whose chunks all lie inside the data (every
+  // wave but the last): the loads are issued without any branch around them
+  // (the steady loop, then a last block with no issue), so the compiler
+  // waits only for the chunk being reduced.  A load behind a branch makes it
+  // wait for every outstanding load, the prefetched chunks included.
+  auto stream_full = [&](auto depth) {
+    constexpr int DD = decltype(depth)::value;
+    float r[DD][E];
+    if (G == DD) {  // the whole run in flight at once
+#pragma unroll
+      for (int u = 0; u < DD; ++u) C::issue_full(chunk_ptr(c0 + u), lane, r[u]);
+#pragma unroll
+      for (int u = 0; u < DD; ++u) reduce_chunk(r[u], u);
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < DD - 1; ++u) C::issue_full(chunk_ptr(c0 + u), lane, r[u]);
+    int64_t j = 0;
+    for (; j + DD < G; j += DD) {
+#pragma unroll
+      for (int u = 0; u < DD; ++u) {
+        C::issue_full(chunk_ptr(c0 + j + u + DD - 1), lane, r[(u + DD - 1) % DD]);
+        reduce_chunk(r[u], j + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < DD; ++u) {
+      if (u == 0) C::issue_full(chunk_ptr(c0 + j + DD - 1), lane, r[DD - 1]);  // the run's last chunk
+      reduce_chunk(r[u], j + u);
+    }
+  };
+  const bool run_full = (c0 + G) * C::SIZE <= n;  // wave-uniform
+  if (run_full) {
+    if (G >= D) stream_full(std::integral_constant<int, D>{});
+    else if (G >= 2) stream_full(std::integral_constant<int, 2>{});
+    else stream_full(std::integral_constant<int, 1>{});
+  } else {
+    if (G >= D) stream(std::integral_constant<int, D>{});
+    else if (G >= 2) stream(std::integral_constant<int, 2>{});
+    else stream(std::integral_constant<int, 1>{});
+  }
   if (lane == 0) slots[w] = st[0];
   __syncthreads();
 
