@@ -385,8 +385,8 @@ constexpr int lds_floats_per_wave() { return 64 * (E + 4); }
 template <int E>
 constexpr int lds_floats_staged() { return 16 * (E + 4); }
 
-// Values p[lane*E + i], i < E, of a 64*E tile starting at p; elements at or
-// beyond `len` read as 0 (len may be <= 0).
+// Values p[lane*E + i], i < E, of a 64*E tile starting at p; in a ragged
+// tile, elements at or beyond `len` read as 0 (len may be <= 0, see below).
 //
 // LOADP 0: coalesced loads (each instruction covers 64 consecutive 16-byte
 //          chunks, or 64 consecutive floats when !VEC), transposed through
@@ -397,7 +397,9 @@ constexpr int lds_floats_staged() { return 16 * (E + 4); }
 // A wave whose tile lies entirely inside the data takes a branch-free path;
 // a ragged tile (the slice's last) loads at addresses clamped to [0, len)
 // (whole 16-byte groups when VEC, single floats otherwise); a tile entirely
-// beyond the data loads nothing.
+// beyond the data loads nothing and leaves v unwritten (every caller masks
+// the values past the slice, so zero-filling it would only cost one move per
+// value on every wave).
 typedef float sv_v4f __attribute__((ext_vector_type(4)));
 
 // 16-byte and 4-byte loads; NT marks them non-temporal (streamed data that
@@ -429,11 +431,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
   // ragged: number of valid values in [0, TILE], and a safe index for loads
   const int lim = len <= 0 ? 0 : (len >= TILE ? TILE : (int)len);
   const int last = lim > 0 ? lim - 1 : 0;
-  if (lim == 0) {  // the whole tile lies beyond the data: no load at all
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = 0.0f;
-    return;
-  }
+  if (lim == 0) return;  // the whole tile lies beyond the data: no load, v left as is
   if constexpr (LOADP == 2) {
     // Staged transpose: coalesced 16-byte loads (instruction k covers values
     // [256k, 256k + 256)), then four stages through a quarter-size LDS region:
