@@ -196,9 +196,11 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     """Variance of each slice of a 2-D (or 1-D) float32, float64 or complex64
     tensor along ``dim`` (float64: the method with every operation in double).
 
-    Returns a float32 tensor of the non-reduced length (and the mean, float32
-    or complex64, when ``return_mean``).  For complex64 data the variance is
-    var(re) + var(im), each part as for float32.
+    Returns a tensor of the non-reduced length (a 0-d tensor for 1-D input):
+    float32 for float32 and complex64 data, float64 for float64 data, and the
+    mean (same dtype as the data) when ``return_mean``.  For complex64 data
+    the variance is var(re) + var(im), each part as for float32.  Inputs that
+    are not contiguous are copied to a contiguous tensor first.
     """
     import torch
 
@@ -206,6 +208,8 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     is_complex = x.dtype == torch.complex64
     is_double = x.dtype == torch.float64
     if x.dim() == 1:
+        if dim not in (0, -1):
+            raise ValueError(f"dim {dim} out of range for a 1-D tensor")
         x2 = x.reshape(1, -1)
         axis = 1
         squeeze = True
