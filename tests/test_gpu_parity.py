@@ -532,7 +532,8 @@ def test_variants_against_oracle(torch_dev, name):
     rng = np.random.default_rng(code)
     cases += [(rng.normal(1e4, 1, (9, 4096)).astype(np.float32), 1), (rng.normal(0, 3, (5, 10000)).astype(np.float32), 1),
               (rng.normal(-5, 1, (700, 70)).astype(np.float32), 0), (W.adversarial_values(6 * 300, code).reshape(6, 300), 1),
-              (np.full((1, 3), np.float32(1e38)), 1), (W.constant(1e30), 0)]
+              (np.full((1, 3), np.float32(1e38)), 1), (W.constant(1e30), 0),
+              (rng.normal(7, 2, (4, 1500)).astype(np.float32), 1)]  # a wave wholly past the row
     for a, ax in cases:
         for ddof in (0, 1):
             t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
