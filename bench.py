@@ -279,6 +279,38 @@ def main():
     var_batches = batches(run_var)
     sum_batches = batches(run_sum)
     torch_var_ms = time_op(lambda i: torch.var(c4[i % N_VAR_COPIES], dim=1, correction=0))
+    # The step's two parts are independent: the VALU-bound variance and the
+    # HBM-bound sum on two default-priority streams at once, each with its
+    # own buffers.  Context only: `value` is the sequential step above.
+    s_var, s_sum = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    ws2 = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    var2 = [(a.data_ptr(), VAR_ROWS, VAR_COLS, 1, 0, var_out.data_ptr(), mean_out.data_ptr(), None, 0,
+             s_var.cuda_stream) for a in c4]
+    sum2 = [(b.data_ptr(), SUM_N, sum_out.data_ptr(), ws2.data_ptr(), ws_bytes, s_sum.cuda_stream) for b in c5]
+
+    def two_streams(k):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev_var, ev_sum = torch.cuda.Event(), torch.cuda.Event()
+        torch.cuda.synchronize()
+        start.record(stream)
+        s_var.wait_event(start)
+        s_sum.wait_event(start)
+        for i in range(k):
+            check(var_fn(*var2[i % N_VAR_COPIES]))
+            check(sum_fn(*sum2[i % N_SUM_COPIES]))
+        ev_var.record(s_var)
+        ev_sum.record(s_sum)
+        stream.wait_event(ev_var)
+        stream.wait_event(ev_sum)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / k
+
+    two_streams(5)
+    overlap_ms = min(two_streams(K) for _ in range(3))
+    overlap = {"ms_per_step": round(overlap_ms, 5),
+               "gelem_s": round((VAR_ROWS * VAR_COLS + SUM_N) / (overlap_ms * 1e-3) / 1e9, 2),
+               "over_sequential_step": round(overlap_ms / ((var_avg + sum_avg)), 3)}
     # the same buffers along axis 0 (4096 column slices of stride 4096: row
     # chunks, the input read twice, three launches)
     ws0 = torch.zeros(max(1, L.sv_variance_f32_workspace_size(VAR_ROWS, VAR_COLS, 0)), dtype=torch.uint8, device=dev)
@@ -456,6 +488,7 @@ def main():
         "sum_kernel": {"avg_launch_ms": round(sum_avg, 5), "gelem_s": round(SUM_N / (sum_avg * 1e-3) / 1e9, 2),
                        "batches": sum_batches},
         "context": {"torch_var_correction0_ms": round(torch_var_ms, 5),
+                    "step_on_two_streams": overlap,
                     "variance_axis0_4096x4096": axis0,
                     "kernel_over_torch_var": round(var_avg / torch_var_ms, 3),
                     "torch_sum_ms": round(torch_sum_ms, 5),
