@@ -317,6 +317,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    every power of two)
  *   "var_lds_pad"    unused dynamic LDS bytes per row workgroup, 0..65536
  *                    (default 0): a cap on resident waves, for measurements
+ *   "var_short_rows" rows of at most 512 values: 1 (default) = several rows
+ *                    per wave (a group of lanes per row), 0 = one workgroup
+ *                    per row
  *   "var_cols_single_max"  axis 0: columns of up to this many rows are
  *                    held by one workgroup and read once (0..1024, default
  *                    1024); longer columns are reduced in row chunks

@@ -272,6 +272,27 @@ __device__ __forceinline__ Node wave_tree(Node n) {
   return comb(p.a, p.b);
 }
 
+// The first log2(S) of those levels: afterwards every lane holds the node of
+// its aligned group of S lanes (S = 1, 2, 4, ..., 64).
+template <int KIND, int S>
+__device__ __forceinline__ Node seg_tree(Node n) {
+  static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "segment of a power-of-two lanes");
+  auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
+  if constexpr (S >= 2) n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
+  if constexpr (S >= 4) n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
+  if constexpr (S >= 8) n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
+  if constexpr (S >= 16) n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
+  if constexpr (S >= 32) {
+    const NodePair p = swap_node<16>(n);
+    n = comb(p.a, p.b);
+  }
+  if constexpr (S >= 64) {
+    const NodePair p = swap_node<32>(n);
+    n = comb(p.a, p.b);
+  }
+  return n;
+}
+
 // The same six levels when lane L holds the range of virtual lane
 // v(L) = 4*(L % 16) + L / 16 (the layout of the LDS-DMA row buffers below):
 // virtual bits 0 and 1 are lane bits 4 and 5, virtual bits 2..5 are lane bits

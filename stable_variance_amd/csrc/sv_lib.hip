@@ -646,6 +646,70 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   }
 }
 
+// Axis 1, short rows (n <= 512): a wave holds 64/S rows, row k on lanes
+// [k*S, (k+1)*S), each lane E consecutive values of its row, so that no lane
+// idles on a row much shorter than the wave.  The row's tree is the in-lane
+// levels and then the first log2(S) cross-lane levels (S*E is a power of two
+// >= n; the values past n are +0).  Four waves per workgroup, independent.
+template <int E, int S, int VW>
+__global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ x, int64_t rows, int64_t n,
+                                                      int64_t ld, int64_t ddof, float *__restrict__ var_out,
+                                                      float *__restrict__ mean_out) {
+  constexpr int RPW = 64 / S;  // rows per wave
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = lane % S;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / S;
+  const bool rowok = row < rows;
+  const float *__restrict__ p = x + (rowok ? row : rows - 1) * ld;  // past the last row: read it again
+  const bool full = (n == (int64_t)S * E);                           // uniform
+  const int64_t e0 = (int64_t)l * E;
+  const int64_t left = n - e0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+
+  // Loads of VW floats (16 or 8 bytes, or single floats): every one issued;
+  // an index past the row reads its last values (n is a multiple of VW, so
+  // a group is wholly inside the row or wholly past it).
+  float v[E];
+  if constexpr (VW == 4) {
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j) {
+      const int64_t e = e0 + 4 * j;
+      const float4 g = *reinterpret_cast<const float4 *>(p + (full || e < n ? e : n - 4));
+      v[4 * j] = g.x; v[4 * j + 1] = g.y; v[4 * j + 2] = g.z; v[4 * j + 3] = g.w;
+    }
+  } else if constexpr (VW == 2) {
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const int64_t e = e0 + 2 * j;
+      const float2 g = *reinterpret_cast<const float2 *>(p + (full || e < n ? e : n - 2));
+      v[2 * j] = g.x; v[2 * j + 1] = g.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t e = e0 + i;
+      v[i] = p[full || e < n ? e : n - 1];
+    }
+  }
+  const float x0 = p[0];
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+  }
+  Node ny = sv::seg_tree<sv::NODE_TWOSUM, S>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v));
+  const float m = sv::root_value(ny) / (float)n;
+  Node nd, nq;
+  if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+  else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
+  nd = sv::seg_tree<sv::NODE_TWOSUM, S>(nd);
+  nq = sv::seg_tree<sv::NODE_NN, S>(nq);
+  if (l == 0 && rowok) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+}
+
 // Axis 1, n <= 64*E: each wave owns R consecutive rows (one lane holds E
 // consecutive values of a row) and reduces row k while the loads of row k+1
 // are in flight, so HBM streaming and the three trees overlap.  The waves of
@@ -1234,6 +1298,7 @@ struct Tuning {
   int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
   int var_cols_single_max = 1024;  // axis 0: rows up to which one workgroup holds a column tile (<= 1024)
   int var_cols_waves = 16;    // axis 0, chunked: waves per workgroup (4, 8, 16); chunks of 16 * waves rows
+  int var_short_rows = 1;     // rows of <= 512 values share waves (0: one workgroup per row)
   int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
   int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
 };
@@ -1428,6 +1493,36 @@ void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t l
     case 6: launch_rows_t<E, W, true, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
     default: launch_rows_t<E, W, true, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
   }
+}
+
+constexpr int64_t SEG_MAX_N = 512;  // rows that share waves (k_var_rows_seg)
+
+// vw: 4 for 16-byte aligned rows of a multiple of 4 values, 2 for 8-byte
+// aligned rows of an even count, else 1.
+template <int E, int S>
+void launch_seg_t(int vw, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
+                  float *mean, hipStream_t st) {
+  constexpr int RPB = 4 * (64 / S);  // rows per workgroup
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
+  if (vw == 4) k_var_rows_seg<E, S, 4><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
+  else if (vw == 2) k_var_rows_seg<E, S, 2><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
+  else k_var_rows_seg<E, S, 1><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
+}
+
+// Short rows: E values per lane (4, 8 or 16) and S lanes per row with S*E
+// the row's power-of-two tile.
+void launch_rows_seg(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
+                     hipStream_t st) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(x);
+  const int vec = (a % 16 == 0 && ld % 4 == 0) ? 4 : (a % 8 == 0 && ld % 2 == 0) ? 2 : 1;
+  if (n <= 4) launch_seg_t<4, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else if (n <= 8) launch_seg_t<8, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else if (n <= 16) launch_seg_t<16, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else if (n <= 32) launch_seg_t<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else if (n <= 64) launch_seg_t<16, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else if (n <= 128) launch_seg_t<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else if (n <= 256) launch_seg_t<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
+  else launch_seg_t<16, 32>(vec, x, rows, n, ld, ddof, var, mean, st);
 }
 
 // Rows of 1025..16384 values: the row's power-of-two tile (2048 .. 16384
@@ -1686,7 +1781,8 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
   }
   if (ax1) {
     const bool vec = aligned16(x) && (cols % 4 == 0);
-    if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+    if (n <= SEG_MAX_N && g_tune.var_short_rows) launch_rows_seg(x, rows, n, cols, ddof, var_out, mean_out, st);
+    else if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     else if (n <= 1024) launch_rows_ew<16, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     else if (n <= 4096 && vec && g_tune.var_dma_rows > 0) {
       const int R = g_tune.var_dma_rows;
@@ -1894,6 +1990,7 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     g_tune.var_cols_waves = (int)value;
     return ok();
   }
+  if (strcmp(key, "var_short_rows") == 0) return flag(&g_tune.var_short_rows);
   if (strcmp(key, "sum_xcd") == 0) return flag(&g_tune.sum_xcd);
   if (strcmp(key, "var_xcd") == 0) return flag(&g_tune.var_xcd);
   if (strcmp(key, "var_lds_pad") == 0) {

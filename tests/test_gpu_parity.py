@@ -52,6 +52,7 @@ VAR_GEOMETRIES = {
     "split8": {"var_split": 8},
     "xcd_contiguous": {"var_xcd": 1},
     "xcd_contiguous_split1": {"var_xcd": 1, "var_split": 1},
+    "short_rows_one_per_workgroup": {"var_short_rows": 0},
     "pipelined_rows2": {"var_rows_per_wave": 2},
     "pipelined_rows8_lds": {"var_rows_per_wave": 8, "var_load_path": 0},
 }
@@ -298,6 +299,21 @@ def test_variance_rows_shapes(torch_dev, var_geometry, n):
     check_var(torch_dev, a, 1, 0)
     check_var(torch_dev, a, 1, 1)
     b = W.adversarial_values(rows * n, n).reshape(rows, n)
+    check_var(torch_dev, b, 1, 0)
+
+
+@pytest.mark.parametrize("shape", [(1000, 4), (4099, 1), (2050, 2), (513, 16), (777, 33), (3000, 100), (65, 500),
+                                   (4096, 512), (301, 7), (100, 129), (257, 255), (1000, 250), (300, 6),
+                                   (129, 18), (200, 130)])
+def test_variance_many_short_rows(torch_dev, var_geometry, shape):
+    # short rows share waves (a row per group of S lanes): partial last
+    # workgroups, odd widths (scalar loads), even widths (8-byte loads),
+    # widths below and above each tile
+    rng = np.random.default_rng(shape[0] + 17 * shape[1])
+    a = rng.normal(3e3, 1.5, shape).astype(np.float32)
+    check_var(torch_dev, a, 1, 0)
+    check_var(torch_dev, a, 1, 1)
+    b = W.adversarial_values(shape[0] * shape[1], shape[1]).reshape(shape)
     check_var(torch_dev, b, 1, 0)
 
 
