@@ -173,6 +173,19 @@ __device__ __forceinline__ NodeD wave_tree_d(NodeD n) {
   return swap_level_d<32, NN>(n);
 }
 
+// The first log2(S) of those levels: every lane ends with the node of its
+// aligned group of S lanes.
+template <bool NN, int S>
+__device__ __forceinline__ NodeD seg_tree_d(NodeD n) {
+  if constexpr (S >= 2) n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1>(n));
+  if constexpr (S >= 4) n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2>(n));
+  if constexpr (S >= 8) n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR>(n));
+  if constexpr (S >= 16) n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR>(n));
+  if constexpr (S >= 32) n = swap_level_d<16, NN>(n);
+  if constexpr (S >= 64) n = swap_level_d<32, NN>(n);
+  return n;
+}
+
 // E doubles from 2E floats held lane-contiguously (low word first).
 template <int E>
 __device__ __forceinline__ void floats_to_doubles(const float (&f)[2 * E], double (&d)[E]) {
@@ -407,6 +420,55 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
     nq = node_tree_d<0, W, W, true>(tq);
   }
   if (threadIdx.x == 0) finalize_d(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+}
+
+// Axis 1, short rows (n <= 512): a wave holds 64/S rows, row k on lanes
+// [k*S, (k+1)*S), each lane E consecutive doubles; the in-lane levels, then
+// the first log2(S) cross-lane levels (S*E a power of two >= n, values past
+// n are +0).  VW = 2: 16-byte loads of two doubles (16-byte aligned rows of
+// an even count), else single doubles; every load issued, clamped, masked.
+template <int E, int S, int VW>
+__global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict__ x, int64_t rows, int64_t n,
+                                                        int64_t ld, int64_t ddof, double *__restrict__ var_out,
+                                                        double *__restrict__ mean_out) {
+  constexpr int RPW = 64 / S;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = lane % S;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / S;
+  const bool rowok = row < rows;
+  const double *__restrict__ p = x + (rowok ? row : rows - 1) * ld;
+  const bool full = (n == (int64_t)S * E);
+  const int64_t e0 = (int64_t)l * E;
+  const int64_t left = n - e0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  double v[E];
+  if constexpr (VW == 2) {
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const int64_t e = e0 + 2 * j;
+      const double2 g = *reinterpret_cast<const double2 *>(p + (full || e < n ? e : n - 2));
+      v[2 * j] = g.x;
+      v[2 * j + 1] = g.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t e = e0 + i;
+      v[i] = p[full || e < n ? e : n - 1];
+    }
+  }
+  const double x0 = p[0];
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = (full || i < valid) ? v[i] - x0 : 0.0;
+  const NodeD ny = seg_tree_d<false, S>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
+  const double m = root_value_d(ny) / (double)n;
+  NodeD nd, nq;
+  if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
+  else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
+  nd = seg_tree_d<false, S>(nd);
+  nq = seg_tree_d<true, S>(nq);
+  if (l == 0 && rowok) finalize_d(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
 }
 
 // Axis 0: lanes own columns (a row of 64 consecutive doubles per load), the
@@ -947,7 +1009,24 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     if (vec) k_var_rows_f64<E, W, true><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var_out, mean_out); \
     else k_var_rows_f64<E, W, false><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var_out, mean_out);    \
   } while (0)
-    if (n <= 256) SV_ROWS64(4, 1);
+    if (n <= 512) {
+      const int vw = (svh::aligned16(x) && cols % 2 == 0) ? 2 : 1;
+#define SV_SEG64(E, S)                                                                                        \
+  do {                                                                                                        \
+    const dim3 sgrid((unsigned)((rows + 4 * (64 / S) - 1) / (4 * (64 / S))));                                 \
+    if (vw == 2) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out); \
+    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);   \
+  } while (0)
+      if (n <= 4) SV_SEG64(4, 1);
+      else if (n <= 8) SV_SEG64(8, 1);
+      else if (n <= 16) SV_SEG64(16, 1);
+      else if (n <= 32) SV_SEG64(16, 2);
+      else if (n <= 64) SV_SEG64(16, 4);
+      else if (n <= 128) SV_SEG64(16, 8);
+      else if (n <= 256) SV_SEG64(16, 16);
+      else SV_SEG64(16, 32);
+#undef SV_SEG64
+    }
     else if (n <= 1024) SV_ROWS64(16, 1);
     else if (n <= 4096) SV_ROWS64(16, 4);
     else if (n <= 8192) SV_ROWS64(16, 8);

@@ -519,6 +519,77 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
   }
 }
 
+// Short complex rows (n <= 512): 64/S rows per wave, row k on lanes
+// [k*S, (k+1)*S), each lane E consecutive complex values, split in registers
+// as in k_var_rows_c64; the in-lane levels and the first log2(S) cross-lane
+// levels per part.  VW2 = 2 complex values per 16-byte load (16-byte aligned
+// rows of an even count), else one (8 bytes); every load issued, clamped and
+// masked.
+template <int E, int S, int VW2>
+__global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restrict__ z, int64_t rows, int64_t n,
+                                                          int64_t ddof, float *__restrict__ var_out,
+                                                          float *__restrict__ mean_out) {
+  constexpr int RPW = 64 / S;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = lane % S;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / S;
+  const bool rowok = row < rows;
+  const float *__restrict__ p = z + 2 * (rowok ? row : rows - 1) * n;
+  const bool full = (n == (int64_t)S * E);
+  const int64_t e0 = (int64_t)l * E;
+  const int64_t left = n - e0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  float re[E], im[E];
+  if constexpr (VW2 == 2) {
+#pragma unroll
+    for (int j = 0; j < E / 2; ++j) {
+      const int64_t e = e0 + 2 * j;
+      const float4 g = *reinterpret_cast<const float4 *>(p + 2 * (full || e < n ? e : n - 2));
+      re[2 * j] = g.x; im[2 * j] = g.y; re[2 * j + 1] = g.z; im[2 * j + 1] = g.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t e = e0 + i;
+      const float2 g = *reinterpret_cast<const float2 *>(p + 2 * (full || e < n ? e : n - 1));
+      re[i] = g.x; im[i] = g.y;
+    }
+  }
+  const float x0r = p[0], x0i = p[1];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    re[i] = (full || i < valid) ? re[i] - x0r : 0.0f;
+    im[i] = (full || i < valid) ? im[i] - x0i : 0.0f;
+  }
+  const Node yr = sv::seg_tree<sv::NODE_TWOSUM, S>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(re));
+  const Node yi = sv::seg_tree<sv::NODE_TWOSUM, S>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(im));
+  const float mr = sv::root_value(yr) / (float)n;
+  const float mi = sv::root_value(yi) / (float)n;
+  Node dr, qr, di, qi;
+  if (full) {
+    sv::lane_tree_dq<false, 0, E, E>(re, mr, E, dr, qr);
+    sv::lane_tree_dq<false, 0, E, E>(im, mi, E, di, qi);
+  } else {
+    sv::lane_tree_dq<true, 0, E, E>(re, mr, valid, dr, qr);
+    sv::lane_tree_dq<true, 0, E, E>(im, mi, valid, di, qi);
+  }
+  dr = sv::seg_tree<sv::NODE_TWOSUM, S>(dr);
+  qr = sv::seg_tree<sv::NODE_NN, S>(qr);
+  di = sv::seg_tree<sv::NODE_TWOSUM, S>(di);
+  qi = sv::seg_tree<sv::NODE_NN, S>(qi);
+  if (l == 0 && rowok) {
+    float vr, vi, mean_r, mean_i;
+    finalize(dr, qr, x0r, mr, n, ddof, &vr, &mean_r);
+    finalize(di, qi, x0i, mi, n, ddof, &vi, &mean_i);
+    var_out[row] = vr + vi;
+    if (mean_out) {
+      mean_out[2 * row] = mean_r;
+      mean_out[2 * row + 1] = mean_i;
+    }
+  }
+}
+
 // var[j] = fl(v[2j] + v[2j+1]): the variance of the real part plus that of
 // the imaginary part.
 __global__ __launch_bounds__(256) void k_pair_add(const float *__restrict__ v, int64_t count, float *__restrict__ out) {
@@ -1914,7 +1985,24 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     if (vec) k_var_rows_c64<E, W, true><<<grid, dim3(64 * W), 0, st>>>(z, cols, ddof, var_out, mean_out);  \
     else k_var_rows_c64<E, W, false><<<grid, dim3(64 * W), 0, st>>>(z, cols, ddof, var_out, mean_out);     \
   } while (0)
-    if (cols <= 256) SV_ROWS_C64(4, 1);
+    if (cols <= SEG_MAX_N && g_tune.var_short_rows) {
+      const int vw2 = vec ? 2 : 1;
+#define SV_SEG_C64(E, S)                                                                                          \
+  do {                                                                                                            \
+    const dim3 sgrid((unsigned)((rows + 4 * (64 / S) - 1) / (4 * (64 / S))));                                     \
+    if (vw2 == 2) k_var_rows_c64_seg<E, S, 2><<<sgrid, dim3(256), 0, st>>>(z, rows, cols, ddof, var_out, mean_out); \
+    else k_var_rows_c64_seg<E, S, 1><<<sgrid, dim3(256), 0, st>>>(z, rows, cols, ddof, var_out, mean_out);       \
+  } while (0)
+      if (cols <= 4) SV_SEG_C64(4, 1);
+      else if (cols <= 8) SV_SEG_C64(8, 1);
+      else if (cols <= 16) SV_SEG_C64(16, 1);
+      else if (cols <= 32) SV_SEG_C64(16, 2);
+      else if (cols <= 64) SV_SEG_C64(16, 4);
+      else if (cols <= 128) SV_SEG_C64(16, 8);
+      else if (cols <= 256) SV_SEG_C64(16, 16);
+      else SV_SEG_C64(16, 32);
+#undef SV_SEG_C64
+    } else if (cols <= 256) SV_ROWS_C64(4, 1);
     else if (cols <= 1024) SV_ROWS_C64(16, 1);
     else if (cols <= 2048) SV_ROWS_C64(16, 2);
     else if (cols <= 4096) SV_ROWS_C64(16, 4);

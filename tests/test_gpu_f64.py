@@ -101,6 +101,18 @@ def test_var64_rows(torch_dev, n):
     check_var64(torch_dev, b, 1)
 
 
+@pytest.mark.parametrize("shape", [(5000, 4), (999, 7), (600, 16), (301, 33), (130, 100), (97, 255), (66, 512),
+                                   (1000, 6)])
+def test_var64_many_short_rows(torch_dev, shape):
+    # rows of at most 512 doubles share waves (a group of lanes per row)
+    rng = np.random.default_rng(shape[0] + shape[1])
+    a = rng.normal(-2e5, 3, shape)
+    check_var64(torch_dev, a, 1)
+    check_var64(torch_dev, a, 1, 1)
+    b = W.adversarial_values(shape[0] * shape[1], shape[1]).astype(np.float64).reshape(shape) * 1e200
+    check_var64(torch_dev, b, 1)
+
+
 @pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 512, 513, 1000, 1024, 1025, 3000, 8192, 9001])
 def test_var64_cols(torch_dev, R):
     # above 1024 rows: 128-row chunks, two adjacent columns per lane (16-byte

@@ -489,7 +489,7 @@ def test_complex_printed_values(torch_dev):
 # scalar loads); longer rows the staged split
 @pytest.mark.parametrize("shape", [(64, 1000), (3, 4096), (5, 20000), (1000, 64), (2000, 3), (1, 1), (7, 2),
                                    (9, 257), (4, 1025), (6, 2047), (3, 5000), (2, 8191), (2, 8192), (2, 8193),
-                                   (11, 0)])
+                                   (11, 0), (3000, 4), (777, 9), (500, 30), (260, 64), (129, 200), (70, 512)])
 @pytest.mark.parametrize("axis", [0, 1])
 def test_complex_shapes(torch_dev, shape, axis):
     rng = np.random.default_rng(shape[0] * 7 + shape[1])
