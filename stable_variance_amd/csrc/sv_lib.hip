@@ -1104,18 +1104,27 @@ __device__ Node chunk_tree(Node *p, int64_t stride, int64_t count) {
   }
 }
 
-template <int V, int W>
+// G row groups per wave: lane L = q*G + g holds the V adjacent columns of
+// column group q (Q = 64/G groups, V*Q columns per block) for the E rows
+// [g*E, (g+1)*E) of the wave's G*E rows; the wave's node of a column is the
+// in-lane levels and then the first log2(G) cross-lane levels (lanes of one
+// column group are adjacent).  G = 1 for blocks of 64*V columns; narrow
+// matrices take G up to 64 so that no lane idles.  Chunks of W*G*E rows.
+template <int V, int W, int G>
 __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
                                                    ColsWs ws) {
-  constexpr int E = CC_E, NC = 64 * V;
+  constexpr int E = CC_E, Q = 64 / G, NC = V * Q;
   static_assert(64 * W >= NC, "one thread per column of the block");
-  __shared__ Node s[W][V][64];
+  __shared__ Node s[W][V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane / G, g = lane % G;
   const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
-  const int64_t c0 = cb * NC + (int64_t)lane * V;
-  const int64_t r0 = j * (E * W) + (int64_t)w * E;
+  const int64_t c0 = cb * NC + (int64_t)q * V;
+  const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);  // the wave's first row
+  const int64_t r0 = rw + (int64_t)g * E;
   const bool full = r0 + E <= R;
+  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
 
@@ -1125,18 +1134,21 @@ __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, 
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
   for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
-  shift_cols_tile<V, E>(v, x0, full, valid);
+  shift_cols_tile<V, E>(v, x0, wave_full, valid);
 #pragma unroll
-  for (int k = 0; k < V; ++k) s[w][k][lane] = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k]);
+  for (int k = 0; k < V; ++k) {
+    const Node nd = sv::seg_tree<sv::NODE_TWOSUM, G>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k]));
+    if (g == 0) s[w][k][q] = nd;
+  }
   __syncthreads();
   const int t = threadIdx.x;
   if (t < NC) {
-    const int k = t >> 6, l = t & 63;  // thread t combines column V*l + k of the block
-    const int64_t col = cb * NC + (int64_t)l * V + k;
+    const int k = t / Q, qq = t % Q;  // thread t combines column V*qq + k of the block
+    const int64_t col = cb * NC + (int64_t)qq * V + k;
     if (col < C) {
       Node nn[W];
 #pragma unroll
-      for (int i = 0; i < W; ++i) nn[i] = s[i][k][l];
+      for (int i = 0; i < W; ++i) nn[i] = s[i][k][qq];
       ws.ny[j * C + col] = sv::node_tree<0, W, W>(nn);
     }
   }
@@ -1167,22 +1179,58 @@ __device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int6
   return sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8>(sub);
 }
 
+// The per-column trees over many chunk nodes with a wave per column (four
+// columns per workgroup): lane l takes nodes [l*K, (l+1)*K) (zero nodes past
+// nch), the in-lane levels and then the wave's six levels give the tree of
+// the column's chunks padded to 64*K nodes.  PASS 0: m; PASS 1: step 4.
+template <int PASS, int K>
+__global__ __launch_bounds__(256) void k_cols_top(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                  int64_t ddof, ColsWs ws, float *__restrict__ var_out,
+                                                  float *__restrict__ mean_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (col >= C) return;  // the whole wave
+  auto tree = [&](const Node *p, auto kind) {
+    constexpr int KIND = decltype(kind)::value;
+    Node nd[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t idx = (int64_t)lane * K + k;
+      const Node t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+      nd[k] = idx < nch ? t : sv::zero_node();
+    }
+    return sv::wave_tree<KIND>(sv::node_tree<0, K, K, KIND>(nd));
+  };
+  if constexpr (PASS == 0) {
+    const Node ny = tree(ws.ny + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
+    if (lane == 0) ws.m[col] = sv::root_value(ny) / (float)R;
+  } else {
+    const Node nd = tree(ws.nd + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
+    const Node nq = tree(ws.nq + col, std::integral_constant<int, sv::NODE_NN>{});
+    if (lane == 0) finalize(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+  }
+}
+
 // MLOCAL: nch <= CC_GROUP, and every workgroup forms m for its own columns
 // from their y chunk nodes (no k_cols_m launch); else m comes from k_cols_m.
-template <int V, int W, bool MLOCAL>
+// Tile layout as in k_cols_y.
+template <int V, int W, int G, bool MLOCAL>
 __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
                                                     ColsWs ws) {
-  constexpr int E = CC_E, NC = 64 * V;
+  constexpr int E = CC_E, Q = 64 / G, NC = V * Q;
   static_assert(64 * W >= NC, "one thread per column of the block");
-  __shared__ Node sd[W][V][64];
-  __shared__ Node sq[W][V][64];
-  __shared__ float sm[V][64];
+  __shared__ Node sd[W][V][Q];
+  __shared__ Node sq[W][V][Q];
+  __shared__ float sm[V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane / G, g = lane % G;
   const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
-  const int64_t c0 = cb * NC + (int64_t)lane * V;
-  const int64_t r0 = j * (E * W) + (int64_t)w * E;
+  const int64_t c0 = cb * NC + (int64_t)q * V;
+  const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);
+  const int64_t r0 = rw + (int64_t)g * E;
   const bool full = r0 + E <= R;
+  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
 
@@ -1193,39 +1241,43 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
   if constexpr (MLOCAL) {
     const int t = threadIdx.x;
     if (t < NC) {
-      const int k = t >> 6, l = t & 63;  // thread t: column V*l + k of the block (clamped like the loads)
-      const int64_t col = cb * NC + (int64_t)l * V + k;
+      const int k = t / Q, qq = t % Q;  // column V*qq + k of the block, clamped like the loads
+      const int64_t col = cb * NC + (int64_t)qq * V + k;
       const int64_t ccol = col < C ? col : C - 1;
-      sm[k][l] = sv::root_value(chunk_tree_1(ws.ny + ccol, C, nch)) / (float)R;
+      sm[k][qq] = sv::root_value(chunk_tree_1(ws.ny + ccol, C, nch)) / (float)R;
     }
     __syncthreads();
   }
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     x0[k] = x[cc + k];
-    m[k] = MLOCAL ? sm[k][lane] : ws.m[cc + k];
+    m[k] = MLOCAL ? sm[k][q] : ws.m[cc + k];
   }
-  shift_cols_tile<V, E>(v, x0, full, valid);
+  shift_cols_tile<V, E>(v, x0, wave_full, valid);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     Node nd, nq;
-    if (full) sv::lane_tree_dq<false, 0, E, E>(v[k], m[k], E, nd, nq);
+    if (wave_full) sv::lane_tree_dq<false, 0, E, E>(v[k], m[k], E, nd, nq);
     else sv::lane_tree_dq<true, 0, E, E>(v[k], m[k], valid, nd, nq);
-    sd[w][k][lane] = nd;
-    sq[w][k][lane] = nq;
+    nd = sv::seg_tree<sv::NODE_TWOSUM, G>(nd);
+    nq = sv::seg_tree<sv::NODE_NN, G>(nq);
+    if (g == 0) {
+      sd[w][k][q] = nd;
+      sq[w][k][q] = nq;
+    }
   }
   __syncthreads();
   const int t = threadIdx.x;
   if (t < NC) {
-    const int k = t >> 6, l = t & 63;  // thread t combines column V*l + k of the block
-    const int64_t col = cb * NC + (int64_t)l * V + k;
-    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][l];  // for k_cols_fin
+    const int k = t / Q, qq = t % Q;  // thread t combines column V*qq + k of the block
+    const int64_t col = cb * NC + (int64_t)qq * V + k;
+    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][qq];  // for k_cols_fin
     if (col < C) {
       Node a[W], b[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        a[i] = sd[i][k][l];
-        b[i] = sq[i][k][l];
+        a[i] = sd[i][k][qq];
+        b[i] = sq[i][k][qq];
       }
       ws.nd[j * C + col] = sv::node_tree<0, W, W>(a);
       ws.nq[j * C + col] = sv::node_tree<0, W, W, sv::NODE_NN>(b);
@@ -1422,29 +1474,57 @@ ColsWs cols_ws(void *workspace, const ColsLayout &L) {
   return ws;
 }
 
-template <int V, int W>
+template <int V, int W, int G>
 void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var,
                          float *mean, hipStream_t st) {
-  const int64_t nch = (R + CC_E * W - 1) / (CC_E * W);
-  const int64_t ncb = (C + 64 * V - 1) / (64 * V);
+  constexpr int64_t CH = (int64_t)CC_E * W * G;  // rows per chunk
+  constexpr int NC = V * (64 / G);                // columns per block
+  const int64_t nch = (R + CH - 1) / CH;
+  const int64_t ncb = (C + NC - 1) / NC;
   const dim3 grid((unsigned)(ncb * nch)), block(64 * W);
   const dim3 per_col((unsigned)((C + 255) / 256));
-  k_cols_y<V, W><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  k_cols_y<V, W, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
   if (nch <= CC_GROUP) {
-    k_cols_dq<V, W, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_dq<V, W, G, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_fin<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+  } else if (nch <= 64 * 16) {
+    // many chunks: a wave per column for m and for the final trees
+    const dim3 per_wave((unsigned)((C + 3) / 4));
+    if (nch <= 64 * 4) {
+      k_cols_top<0, 4><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+      k_cols_top<1, 4><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    } else {
+      k_cols_top<0, 16><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+      k_cols_top<1, 16><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    }
   } else {
     k_cols_m<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
-    k_cols_dq<V, W, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_fin<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
   }
-  k_cols_fin<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+}
+
+// Row groups per wave, so that lanes stay on columns: G = 1 (64 column
+// groups of V per block) for matrices of at least 64 groups, G = 4 (16 groups
+// per block) for 5 to 63, G = 16 (4 groups) for 2 to 4, G = 64 for one.
+template <int V, int W>
+void launch_cols_g(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var, float *mean,
+                   hipStream_t st) {
+  const int64_t groups = (C + V - 1) / V;
+  if (groups >= 64) launch_cols_chunked<V, W, 1>(x, R, C, ddof, ws, var, mean, st);
+  else if (groups > 4) launch_cols_chunked<V, W, 4>(x, R, C, ddof, ws, var, mean, st);
+  else if (groups > 1) launch_cols_chunked<V, W, 16>(x, R, C, ddof, ws, var, mean, st);
+  else launch_cols_chunked<V, W, 64>(x, R, C, ddof, ws, var, mean, st);
 }
 
 template <int V>
 void launch_cols_v(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var, float *mean,
                    hipStream_t st) {
-  if (g_tune.var_cols_waves == 16) launch_cols_chunked<V, 16>(x, R, C, ddof, ws, var, mean, st);
-  else if (g_tune.var_cols_waves == 8) launch_cols_chunked<V, 8>(x, R, C, ddof, ws, var, mean, st);
-  else launch_cols_chunked<V, 4>(x, R, C, ddof, ws, var, mean, st);
+  if (g_tune.var_cols_waves == 16) launch_cols_g<V, 16>(x, R, C, ddof, ws, var, mean, st);
+  else if (g_tune.var_cols_waves == 8) launch_cols_g<V, 8>(x, R, C, ddof, ws, var, mean, st);
+  else launch_cols_g<V, 4>(x, R, C, ddof, ws, var, mean, st);
 }
 
 // The top trees over nch <= LS_MAX_CHUNKS chunk nodes per slice: 256

@@ -415,7 +415,9 @@ def test_variance_long_cols(torch_dev, col_geometry, R):
     check_var(torch_dev, b, 0, 0)
 
 
-@pytest.mark.parametrize("R,C", [(4096, 1000), (2000, 4100), (5000, 257), (300, 4096), (70000, 12), (1, 3000)])
+@pytest.mark.parametrize("R,C", [(4096, 1000), (2000, 4100), (5000, 257), (300, 4096), (70000, 12), (1, 3000),
+                                 (100000, 4), (50000, 16), (20000, 7), (8193, 2), (30000, 1), (9000, 40),
+                                 (40000, 130), (70000, 65)])
 def test_variance_cols_wide(torch_dev, col_geometry, R, C):
     # several column blocks with a ragged last block (16-byte loads of four
     # columns when C % 4 == 0, one column per lane otherwise) and ragged chunks
