@@ -220,10 +220,11 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
  *   slice; workspace of sv_variance_f64_workspace_size(rows, cols, axis)
  *   bytes, 256-byte aligned scratch, NULL allowed when that size is 0.
  * sv_variance_f64_workspace_size: 0 when every slice fits one workgroup
- *   (axis 1: n <= 16384; axis 0: n <= 1024).  Longer slices are reduced in
- *   chunks (8192 values of a row; 128 rows of a column), reading the input
- *   twice: three arrays of 16 bytes per chunk per slice and 8 bytes per
- *   slice, each rounded up to 256 bytes.  (size_t)-1 for an unsupported
+ *   (axis 1: n <= 16384; axis 0: n <= 256).  Longer slices are reduced in
+ *   chunks (8192 values of a row; 128 rows of a column, or a multiple of 128
+ *   for narrow matrices), reading the input twice: three arrays of 16 bytes
+ *   per 128-value chunk per slice and 8 bytes per slice, each rounded up to
+ *   256 bytes.  (size_t)-1 for an unsupported
  *   shape (a bad axis, rows * cols >= 2^39, an axis-1 row of more than 8192
  *   chunks, i.e. 67,108,864 values).
  * Errors and asynchrony as for the float32 entry points.
@@ -305,7 +306,7 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "var_nt"         row variance: as sum_nt (default 0)
  *   "var_rows_per_wave"  rows of 1025..4096 values one wave pipelines (the
  *                    next row's loads in flight while one is reduced): 1
- *                    (default), 2, 4 or 8
+ *                    (default) or 2
  *   "var_dma_rows"   rows of 1025..4096 values per wave staged by direct
  *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
  *   "var_split"      rows of 1025..16384 values: waves per 4096 values of

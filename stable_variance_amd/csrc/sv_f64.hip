@@ -15,6 +15,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/stable_variance.h"
 #include "sv_device.hpp"
 #include "sv_host.hpp"
@@ -540,11 +542,12 @@ __global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restric
 //   axis 1, rows of more than 16384 values: chunks of 8192 values (8 waves
 //     of 64 lanes of 16 doubles); a y node per chunk, a per-row top tree
 //     giving m, d and d^2 nodes per chunk, per-row top trees and step 4.
-//   axis 0, columns of more than 1024 values: chunks of 128 rows of a block
-//     of 64*V columns (lane L holds V adjacent columns, one 16-byte load per
-//     row when V = 2, for the 16 rows of its wave); a y node per (chunk,
+//   axis 0, columns of more than 256 values: chunks of 128*G rows of a
+//     block of V*64/G columns (lane L = q*G + g holds the V adjacent columns
+//     of group q, one 16-byte load per row when V = 2, for 16 rows; G = 1
+//     for wide matrices, up to 64 for narrow ones); a y node per (chunk,
 //     column), m per column, d and d^2 nodes per (chunk, column), per-column
-//     trees and step 4.
+//     trees (a wave per column when there are many chunks) and step 4.
 // The input is read twice; the workspace is scratch.
 
 constexpr int L64_E = 16;                       // doubles per lane
@@ -731,17 +734,27 @@ __device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, 
   return node_tree_d<0, C64_GROUP / 8, C64_GROUP / 8, false>(sub);
 }
 
-template <int V>
+// G row groups per wave: lane L = q*G + g holds the V adjacent columns of
+// column group q (Q = 64/G groups, V*Q columns per block) for the E rows
+// [g*E, (g+1)*E) of the wave's G*E rows; the wave's node of a column is the
+// in-lane levels and then the first log2(G) cross-lane levels (the lanes of
+// a column group are adjacent).  G = 1 for blocks of 64*V columns; narrow
+// matrices take larger G so that lanes stay on columns.  Chunks of W*G*E
+// rows.
+template <int V, int G>
 __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                          int64_t nch, SliceWsD ws) {
-  constexpr int E = L64_E, W = L64_W, NC = 64 * V;
-  __shared__ NodeD s[W][V][64];
+  constexpr int E = L64_E, W = L64_W, Q = 64 / G, NC = V * Q;
+  __shared__ NodeD s[W][V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane / G, g = lane % G;
   const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
-  const int64_t c0 = cb * NC + (int64_t)lane * V;
-  const int64_t r0 = j * C64_CHUNK + (int64_t)w * E;
+  const int64_t c0 = cb * NC + (int64_t)q * V;
+  const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);  // the wave's first row
+  const int64_t r0 = rw + (int64_t)g * E;
   const bool full = r0 + E <= R;
+  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
   double v[V][E];
@@ -750,18 +763,21 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restric
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
   for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
-  shift_cols_tile_d<V, E>(v, x0, full, valid);
+  shift_cols_tile_d<V, E>(v, x0, wave_full, valid);
 #pragma unroll
-  for (int k = 0; k < V; ++k) s[w][k][lane] = lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k]);
+  for (int k = 0; k < V; ++k) {
+    const NodeD nd = seg_tree_d<false, G>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k]));
+    if (g == 0) s[w][k][q] = nd;
+  }
   __syncthreads();
   const int t = threadIdx.x;
   if (t < NC) {
-    const int k = t >> 6, l = t & 63;  // thread t combines column V*l + k of the block
-    const int64_t col = cb * NC + (int64_t)l * V + k;
+    const int k = t / Q, qq = t % Q;  // thread t combines column V*qq + k of the block
+    const int64_t col = cb * NC + (int64_t)qq * V + k;
     if (col < C) {
       NodeD nn[W];
 #pragma unroll
-      for (int i = 0; i < W; ++i) nn[i] = s[i][k][l];
+      for (int i = 0; i < W; ++i) nn[i] = s[i][k][qq];
       ws.ny[j * C + col] = node_tree_d<0, W, W, false>(nn);
     }
   }
@@ -773,63 +789,110 @@ __global__ __launch_bounds__(256) void k_cols_m_d(int64_t R, int64_t C, int64_t 
   ws.m[col] = root_value_d(chunk_tree_d<false>(ws.ny + col, C, nch)) / (double)R;
 }
 
+// The per-column trees over the chunk nodes with S lanes per column (64/S
+// columns per wave, four waves per workgroup): lane l of a column's group
+// takes nodes [l*K, (l+1)*K) (zero nodes past nch), the in-lane levels and
+// then the first log2(S) cross-lane levels give the tree of the column's
+// chunks padded to S*K nodes.  PASS 0: m; PASS 1: step 4.
+template <int PASS, int K, int S>
+__global__ __launch_bounds__(256) void k_cols_top_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t nch,
+                                                    int64_t ddof, SliceWsD ws, double *__restrict__ var_out,
+                                                    double *__restrict__ mean_out) {
+  constexpr int PW = 64 / S;
+  const int lane = threadIdx.x & 63;
+  const int64_t col0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PW;
+  if (col0 >= C) return;  // the whole wave
+  const int64_t col = col0 + lane / S;
+  const int sl = lane % S;
+  const bool colok = col < C;
+  const int64_t cc = colok ? col : C - 1;
+  auto tree = [&](const NodeD *p, auto nn) {
+    constexpr bool NN = decltype(nn)::value;
+    NodeD nd[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t idx = (int64_t)sl * K + k;
+      const NodeD t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+      nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
+    }
+    return seg_tree_d<NN, S>(node_tree_d<0, K, K, NN>(nd));
+  };
+  if constexpr (PASS == 0) {
+    const NodeD ny = tree(ws.ny + cc, std::false_type{});
+    if (sl == 0 && colok) ws.m[col] = root_value_d(ny) / (double)R;
+  } else {
+    const NodeD nd = tree(ws.nd + cc, std::false_type{});
+    const NodeD nq = tree(ws.nq + cc, std::true_type{});
+    if (sl == 0 && colok)
+      finalize_d(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+  }
+}
+
 // MLOCAL: nch <= C64_GROUP, and every workgroup forms m for its own columns
-// (no k_cols_m_d launch); else m comes from k_cols_m_d.
-template <int V, bool MLOCAL>
+// (no k_cols_m_d launch); else m comes from k_cols_m_d or k_cols_top_d.
+// Tile layout as in k_cols_y_d.
+template <int V, int G, bool MLOCAL>
 __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                           int64_t nch, SliceWsD ws) {
-  constexpr int E = L64_E, W = L64_W, NC = 64 * V;
-  __shared__ NodeD sd[W][V][64];
-  __shared__ NodeD sq[W][V][64];
-  __shared__ double sm[V][64];
+  constexpr int E = L64_E, W = L64_W, Q = 64 / G, NC = V * Q;
+  __shared__ NodeD sd[W][V][Q];
+  __shared__ NodeD sq[W][V][Q];
+  __shared__ double sm[V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane / G, g = lane % G;
   const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
-  const int64_t c0 = cb * NC + (int64_t)lane * V;
-  const int64_t r0 = j * C64_CHUNK + (int64_t)w * E;
+  const int64_t c0 = cb * NC + (int64_t)q * V;
+  const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);
+  const int64_t r0 = rw + (int64_t)g * E;
   const bool full = r0 + E <= R;
+  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
-  double v[V][E];
-  load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
   const int64_t cc = c0 < C ? c0 : C - V;
   if constexpr (MLOCAL) {
     const int t = threadIdx.x;
     if (t < NC) {
-      const int k = t >> 6, l = t & 63;  // column V*l + k of the block, clamped like the loads
-      const int64_t col = cb * NC + (int64_t)l * V + k;
+      const int k = t / Q, qq = t % Q;  // column V*qq + k of the block, clamped like the loads
+      const int64_t col = cb * NC + (int64_t)qq * V + k;
       const int64_t ccol = col < C ? col : C - 1;
-      sm[k][l] = root_value_d(chunk_tree_1_d(ws.ny + ccol, C, nch)) / (double)R;
+      sm[k][qq] = root_value_d(chunk_tree_1_d(ws.ny + ccol, C, nch)) / (double)R;
     }
     __syncthreads();
   }
+  double v[V][E];  // loaded after m, which holds fewer registers at once
+  load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
   double x0[V], m[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     x0[k] = x[cc + k];
-    m[k] = MLOCAL ? sm[k][lane] : ws.m[cc + k];
+    m[k] = MLOCAL ? sm[k][q] : ws.m[cc + k];
   }
-  shift_cols_tile_d<V, E>(v, x0, full, valid);
+  shift_cols_tile_d<V, E>(v, x0, wave_full, valid);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     NodeD nd, nq;
-    if (full) lane_tree_dq_d<false, 0, E, E>(v[k], m[k], E, nd, nq);
+    if (wave_full) lane_tree_dq_d<false, 0, E, E>(v[k], m[k], E, nd, nq);
     else lane_tree_dq_d<true, 0, E, E>(v[k], m[k], valid, nd, nq);
-    sd[w][k][lane] = nd;
-    sq[w][k][lane] = nq;
+    nd = seg_tree_d<false, G>(nd);
+    nq = seg_tree_d<true, G>(nq);
+    if (g == 0) {
+      sd[w][k][q] = nd;
+      sq[w][k][q] = nq;
+    }
   }
   __syncthreads();
   const int t = threadIdx.x;
   if (t < NC) {
-    const int k = t >> 6, l = t & 63;
-    const int64_t col = cb * NC + (int64_t)l * V + k;
-    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][l];  // for k_cols_fin_d
+    const int k = t / Q, qq = t % Q;  // thread t combines column V*qq + k of the block
+    const int64_t col = cb * NC + (int64_t)qq * V + k;
+    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][qq];  // for k_cols_fin_d
     if (col < C) {
       NodeD a[W], b[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        a[i] = sd[i][k][l];
-        b[i] = sq[i][k][l];
+        a[i] = sd[i][k][qq];
+        b[i] = sq[i][k][qq];
       }
       ws.nd[j * C + col] = node_tree_d<0, W, W, false>(a);
       ws.nq[j * C + col] = node_tree_d<0, W, W, true>(b);
@@ -856,7 +919,7 @@ __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int
 }
 
 constexpr int64_t V64_ROWS_MAX_N = 16384;  // one workgroup per row
-constexpr int64_t V64_COLS_MAX_R = 1024;   // one workgroup per 64-column tile
+constexpr int64_t V64_COLS_MAX_R = 256;    // one workgroup per 64-column tile
 constexpr int64_t V64_MAX_ELEMS = 1LL << 39;
 
 size_t round256_d(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -896,20 +959,55 @@ void launch_long_top_d(const double *x, int64_t n, int64_t ld, int64_t nch, int6
   else k_long_top_d<PASS, L64_TOP_MAX_K><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
 }
 
-template <int V>
+template <int V, int G>
 void launch_cols_d(const double *x, int64_t R, int64_t C, int64_t ddof, const SliceWsD &ws, double *var,
                    double *mean, hipStream_t st) {
-  const int64_t nch = (R + C64_CHUNK - 1) / C64_CHUNK;
-  const int64_t ncb = (C + 64 * V - 1) / (64 * V);
+  constexpr int64_t CH = C64_CHUNK * G;  // rows per chunk
+  constexpr int NC = V * (64 / G);       // columns per block
+  const int64_t nch = (R + CH - 1) / CH;
+  const int64_t ncb = (C + NC - 1) / NC;
   const dim3 grid((unsigned)(ncb * nch)), block(64 * L64_W), per_col((unsigned)((C + 255) / 256));
-  k_cols_y_d<V><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  k_cols_y_d<V, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  auto per_waves = [&](int per_wave) { return dim3((unsigned)((C + 4 * per_wave - 1) / (4 * per_wave))); };
   if (nch <= C64_GROUP) {
-    k_cols_dq_d<V, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_dq_d<V, G, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    // the final trees: a group of S >= nch lanes per column, one node each
+    if (nch <= 4) k_cols_top_d<1, 1, 4><<<per_waves(16), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    else if (nch <= 8) k_cols_top_d<1, 1, 8><<<per_waves(8), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    else if (nch <= 16) k_cols_top_d<1, 1, 16><<<per_waves(4), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    else k_cols_top_d<1, 1, 32><<<per_waves(2), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+  } else if (nch <= 64 * 16) {
+    // many chunks: a wave per column for m and for the final trees
+    const dim3 per_wave = per_waves(1);
+    if (nch <= 64 * 4) {
+      k_cols_top_d<0, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+      k_cols_top_d<1, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    } else {
+      k_cols_top_d<0, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+      k_cols_top_d<1, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    }
   } else {
     k_cols_m_d<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
-    k_cols_dq_d<V, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    k_cols_fin_d<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
   }
-  k_cols_fin_d<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+}
+
+// Row groups per wave, so that lanes stay on columns: with `groups` column
+// groups of V, G = 1 for at least 64 groups, 4 for 9 to 63 (16 groups per
+// block), 8 for 5 to 8, 16 for 3 and 4, 32 for 2 and 64 for one.
+template <int V>
+void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const SliceWsD &ws, double *var,
+                    double *mean, hipStream_t st) {
+  const int64_t groups = (C + V - 1) / V;
+  if (groups >= 64) launch_cols_d<V, 1>(x, R, C, ddof, ws, var, mean, st);
+  else if (groups > 8) launch_cols_d<V, 4>(x, R, C, ddof, ws, var, mean, st);
+  else if (groups > 4) launch_cols_d<V, 8>(x, R, C, ddof, ws, var, mean, st);
+  else if (groups > 2) launch_cols_d<V, 16>(x, R, C, ddof, ws, var, mean, st);
+  else if (groups > 1) launch_cols_d<V, 32>(x, R, C, ddof, ws, var, mean, st);
+  else launch_cols_d<V, 64>(x, R, C, ddof, ws, var, mean, st);
 }
 
 }  // namespace
@@ -1045,17 +1143,15 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
 #undef SV_ROWS64
   } else if (n > V64_COLS_MAX_R) {
     const SliceWsD ws = slice_ws(workspace, ((n + C64_CHUNK - 1) / C64_CHUNK) * cols);
-    if (svh::aligned16(x) && cols % 2 == 0) launch_cols_d<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
-    else launch_cols_d<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+    if (svh::aligned16(x) && cols % 2 == 0) launch_cols_gd<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+    else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
   } else {
     const dim3 grid((unsigned)((cols + 63) / 64));
 #define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)
     if (n <= 4) SV_COLS64(4, 1);
     else if (n <= 16) SV_COLS64(16, 1);
     else if (n <= 64) SV_COLS64(16, 4);
-    else if (n <= 256) SV_COLS64(16, 16);
-    else if (n <= 512) SV_COLS64(32, 16);
-    else SV_COLS64(64, 16);
+    else SV_COLS64(16, 16);  // n <= V64_COLS_MAX_R
 #undef SV_COLS64
   }
   return check_launch("sv_variance_f64");

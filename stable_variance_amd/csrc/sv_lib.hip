@@ -413,14 +413,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(SV_SUM_M
 // §2: the real and imaginary parts are split and their variances added).
 // Row r of a [rows, cols] complex64 array (interleaved re, im) becomes rows
 // 2r (re) and 2r+1 (im) of a [2*rows, cols] float32 array.
+// Rows stride by gridDim.y and columns by gridDim.x * 256 (no integer
+// division in the index arithmetic).
 __global__ __launch_bounds__(256) void k_split_rows(const float *__restrict__ z, int64_t rows, int64_t cols,
                                                     float *__restrict__ out) {
-  const int64_t total = rows * cols;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / cols, c = i % cols;
-    const float2 v = reinterpret_cast<const float2 *>(z)[i];
-    out[(2 * r) * cols + c] = v.x;
-    out[(2 * r + 1) * cols + c] = v.y;
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float2 *__restrict__ zr = reinterpret_cast<const float2 *>(z) + r * cols;
+    float *__restrict__ re = out + (2 * r) * cols;
+    float *__restrict__ im = re + cols;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < cols; c += (int64_t)gridDim.x * 256) {
+      const float2 v = zr[c];
+      re[c] = v.x;
+      im[c] = v.y;
+    }
   }
 }
 
@@ -1020,13 +1025,17 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 // chunk.  Three or four launches, ordered by the stream (each reads what the
 // previous ones wrote; the workspace is scratch):
 //   k_cols_y    the y-tree node of every (chunk, column)
-//   k_cols_m    per column m = Tree(y)/n, the tree over its chunk nodes (for
+//   m           per column m = Tree(y)/n, the tree over its chunk nodes: for
 //               at most 32 chunks per column each k_cols_dq workgroup forms
-//               the m of its own columns instead, and this launch is skipped)
+//               the m of its own columns (no launch); up to 1024 chunks a
+//               wave per column (k_cols_top); beyond, a thread per column
+//               (k_cols_m)
 //   k_cols_dq   the tile read again (mostly from the chip's last-level cache
 //               when the input fits in it): the d- and d^2-tree node of
 //               every (chunk, column)
-//   k_cols_fin  per column the trees over its d and d^2 chunk nodes, step 4
+//   step 4      per column the trees over its d and d^2 chunk nodes: a group
+//               of lanes (up to 32 chunks) or a wave (up to 1024) per column
+//               (k_cols_top), else a thread per column (k_cols_fin)
 
 constexpr int CC_E = 16;             // rows per lane in a chunk
 constexpr int CC_MIN_W = 4;          // the workspace is sized for the shortest chunk
@@ -1179,35 +1188,42 @@ __device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int6
   return sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8>(sub);
 }
 
-// The per-column trees over many chunk nodes with a wave per column (four
-// columns per workgroup): lane l takes nodes [l*K, (l+1)*K) (zero nodes past
-// nch), the in-lane levels and then the wave's six levels give the tree of
-// the column's chunks padded to 64*K nodes.  PASS 0: m; PASS 1: step 4.
-template <int PASS, int K>
+// The per-column trees over the chunk nodes with S lanes per column (64/S
+// columns per wave, four waves per workgroup): lane l of a column's group
+// takes nodes [l*K, (l+1)*K) (zero nodes past nch), the in-lane levels and
+// then the first log2(S) cross-lane levels give the tree of the column's
+// chunks padded to S*K nodes.  PASS 0: m; PASS 1: step 4.
+template <int PASS, int K, int S>
 __global__ __launch_bounds__(256) void k_cols_top(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
                                                   int64_t ddof, ColsWs ws, float *__restrict__ var_out,
                                                   float *__restrict__ mean_out) {
+  constexpr int PW = 64 / S;
   const int lane = threadIdx.x & 63;
-  const int64_t col = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (col >= C) return;  // the whole wave
+  const int64_t col0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PW;
+  if (col0 >= C) return;  // the whole wave
+  const int64_t col = col0 + lane / S;
+  const int sl = lane % S;
+  const bool colok = col < C;
+  const int64_t cc = colok ? col : C - 1;
   auto tree = [&](const Node *p, auto kind) {
     constexpr int KIND = decltype(kind)::value;
     Node nd[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int64_t idx = (int64_t)lane * K + k;
+      const int64_t idx = (int64_t)sl * K + k;
       const Node t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
       nd[k] = idx < nch ? t : sv::zero_node();
     }
-    return sv::wave_tree<KIND>(sv::node_tree<0, K, K, KIND>(nd));
+    return sv::seg_tree<KIND, S>(sv::node_tree<0, K, K, KIND>(nd));
   };
   if constexpr (PASS == 0) {
-    const Node ny = tree(ws.ny + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
-    if (lane == 0) ws.m[col] = sv::root_value(ny) / (float)R;
+    const Node ny = tree(ws.ny + cc, std::integral_constant<int, sv::NODE_TWOSUM>{});
+    if (sl == 0 && colok) ws.m[col] = sv::root_value(ny) / (float)R;
   } else {
-    const Node nd = tree(ws.nd + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
-    const Node nq = tree(ws.nq + col, std::integral_constant<int, sv::NODE_NN>{});
-    if (lane == 0) finalize(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+    const Node nd = tree(ws.nd + cc, std::integral_constant<int, sv::NODE_TWOSUM>{});
+    const Node nq = tree(ws.nq + cc, std::integral_constant<int, sv::NODE_NN>{});
+    if (sl == 0 && colok)
+      finalize(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
   }
 }
 
@@ -1234,8 +1250,6 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
 
-  float v[V][E];
-  load_cols_tile<V, E>(x, R, C, c0, r0, full, v);
   float x0[V], m[V];
   const int64_t cc = c0 < C ? c0 : C - V;
   if constexpr (MLOCAL) {
@@ -1248,6 +1262,10 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
     }
     __syncthreads();
   }
+  // the tile is loaded after m: the chunk nodes and the tile together do not
+  // fit in the registers of 16 waves
+  float v[V][E];
+  load_cols_tile<V, E>(x, R, C, c0, r0, full, v);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     x0[k] = x[cc + k];
@@ -1415,7 +1433,7 @@ struct Tuning {
   int64_t sum_blocks = 8192;  // target workgroup count of the tree sum
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
-  int var_rows_per_wave = 1;  // rows a wave pipelines (1, 2, 4, 8) for 1024 < n <= 4096
+  int var_rows_per_wave = 1;  // rows a wave pipelines (1 or 2) for 1024 < n <= 4096
   int var_split = 0;          // waves per 4096 values of a row of 1025..16384 values (1, 2, 4, 8; 0 auto)
   int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
   int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
@@ -1484,20 +1502,25 @@ void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, con
   const dim3 grid((unsigned)(ncb * nch)), block(64 * W);
   const dim3 per_col((unsigned)((C + 255) / 256));
   k_cols_y<V, W, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+  auto per_waves = [&](int per_wave) { return dim3((unsigned)((C + 4 * per_wave - 1) / (4 * per_wave))); };
   if (nch <= CC_GROUP) {
     k_cols_dq<V, W, G, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-    k_cols_fin<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    // the final trees: a group of S >= nch lanes per column, one node each
+    if (nch <= 4) k_cols_top<1, 1, 4><<<per_waves(16), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    else if (nch <= 8) k_cols_top<1, 1, 8><<<per_waves(8), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    else if (nch <= 16) k_cols_top<1, 1, 16><<<per_waves(4), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    else k_cols_top<1, 1, 32><<<per_waves(2), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
   } else if (nch <= 64 * 16) {
     // many chunks: a wave per column for m and for the final trees
-    const dim3 per_wave((unsigned)((C + 3) / 4));
+    const dim3 per_wave = per_waves(1);
     if (nch <= 64 * 4) {
-      k_cols_top<0, 4><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_top<0, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
       k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top<1, 4><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_top<1, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     } else {
-      k_cols_top<0, 16><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_top<0, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
       k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top<1, 16><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_top<1, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     }
   } else {
     k_cols_m<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
@@ -1943,10 +1966,7 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
       else if (R == 4) k_var_rows_dma<4, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
       else k_var_rows_dma<8, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
     } else if (n <= 4096 && g_tune.var_rows_per_wave > 1) {
-      const int R = g_tune.var_rows_per_wave;
-      if (R == 2) launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else if (R == 4) launch_pipe_r<4>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-      else launch_pipe_r<8>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
+      launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     } else {
       launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     }
@@ -2099,9 +2119,10 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     wp += round256((size_t)2 * rows * cols * sizeof(float));
     const size_t inner = sv_variance_f32_workspace_size(2 * rows, cols, 1);
     if (rows * cols > 0) {
-      const int64_t total = rows * cols;
-      const int64_t blocks = (total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536;
-      k_split_rows<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(z, rows, cols, split);
+      const int64_t bx = (cols + 255) / 256 < 65536 ? (cols + 255) / 256 : 65536;
+      const int64_t by_max = 65535 / bx > 1 ? 65535 / bx : 1;
+      const int64_t by = rows < by_max ? rows : by_max;
+      k_split_rows<<<dim3((unsigned)bx, (unsigned)by), dim3(256), 0, st>>>(z, rows, cols, split);
       rc = check_launch("sv_variance_c64");
       if (rc != SV_OK) return rc;
     }
@@ -2173,8 +2194,8 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_rows_per_wave") == 0) {
-    if (value != 1 && value != 2 && value != 4 && value != 8)
-      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_rows_per_wave must be 1, 2, 4 or 8");
+    if (value != 1 && value != 2)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_rows_per_wave must be 1 or 2");
     g_tune.var_rows_per_wave = (int)value;
     return ok();
   }

@@ -158,7 +158,9 @@ def test_f64_sizes_and_argument_errors(L):
     # of 16 bytes per chunk per slice and 8 bytes per slice, each rounded to 256
     r256 = lambda b: (b + 255) // 256 * 256
     ws = L.sv_variance_f64_workspace_size
-    assert ws(7, 16384, 1) == 0 and ws(1024, 9, 0) == 0 and ws(0, 5, 0) == 0
+    assert ws(7, 16384, 1) == 0 and ws(256, 9, 0) == 0 and ws(0, 5, 0) == 0
+    assert ws(257, 9, 0) == 3 * r256(3 * 9 * 16) + r256(9 * 8)
+    assert ws(1024, 9, 0) == 3 * r256(8 * 9 * 16) + r256(9 * 8)
     assert ws(3, 16385, 1) == 3 * r256(3 * 3 * 16) + r256(3 * 8)
     assert ws(1025, 7, 0) == 3 * r256(9 * 7 * 16) + r256(7 * 8)
     assert ws(4096, 4096, 0) == 3 * r256(32 * 4096 * 16) + r256(4096 * 8)
@@ -200,7 +202,7 @@ def test_tuning_knob_validation(L):
     assert L.sv_set_tuning(b"nope", 0) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_set_tuning(None, 0) == SV_ERR_INVALID_ARGUMENT
     for key, good, bad in ((b"sum_load_path", 1, 2), (b"sum_nt", 0, -1), (b"var_load_path", 2, 5),
-                           (b"var_nt", 1, 2), (b"var_rows_per_wave", 4, 3), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0),
+                           (b"var_nt", 1, 2), (b"var_rows_per_wave", 2, 4), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0),
                            (b"sum_xcd", 1, 2), (b"var_xcd", 1, -1), (b"var_split", 0, 3), (b"var_split", 8, 16), (b"var_dma_rows", 2, 1),
                            (b"var_lds_pad", 65536, 65537), (b"var_short_rows", 0, 2)):
         assert L.sv_set_tuning(key, good) == 0, key

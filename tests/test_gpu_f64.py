@@ -115,16 +115,33 @@ def test_var64_many_short_rows(torch_dev, shape):
 
 @pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 512, 513, 1000, 1024, 1025, 3000, 8192, 9001])
 def test_var64_cols(torch_dev, R):
-    # above 1024 rows: 128-row chunks, two adjacent columns per lane (16-byte
+    # above 256 rows: 128-row chunks, two adjacent columns per lane (16-byte
     # loads) when the width is even, one otherwise; more than 32 chunks per
-    # column take the separate m launch
+    # column take a separate m launch
     rng = np.random.default_rng(R)
     for C in (1, 63, 64, 65, 130):
         a = rng.normal(-5e3, 2, (R, C))
         check_var64(torch_dev, a, 0)
         check_var64(torch_dev, a, 0, 1)
-    if R > 1024:
+    if R > 256:
         b = W.adversarial_values(R * 300, R).astype(np.float64).reshape(R, 300) * 1e250
+        check_var64(torch_dev, b, 0)
+
+
+@pytest.mark.parametrize("R,C", [(30000, 1), (100000, 1), (300000, 1), (8_400_000, 1), (50000, 2), (20000, 3),
+                                 (70000, 4), (2_100_000, 4), (9000, 7), (5000, 10), (3000, 12), (40000, 17),
+                                 (8193, 40), (2000, 130), (257, 5), (600, 64)])
+def test_var64_cols_narrow(torch_dev, R, C):
+    # narrow matrices: G row groups per wave (chunks of 128*G rows, G from 1
+    # to 64 as the column groups number 65 down to 1); per-column trees by a
+    # lane group (up to 32 chunks), a wave (up to 1024) or a thread (beyond:
+    # 8,400,000 rows in 8192-row chunks)
+    rng = np.random.default_rng(R * 7 + C)
+    a = rng.normal(-3e5, 9, (R, C))
+    check_var64(torch_dev, a, 0)
+    check_var64(torch_dev, a, 0, 2)
+    if R * C <= 400_000:
+        b = W.adversarial_values(R * C, R + C).astype(np.float64).reshape(R, C) * 1e200
         check_var64(torch_dev, b, 0)
 
 

@@ -54,7 +54,7 @@ VAR_GEOMETRIES = {
     "xcd_contiguous_split1": {"var_xcd": 1, "var_split": 1},
     "short_rows_one_per_workgroup": {"var_short_rows": 0},
     "pipelined_rows2": {"var_rows_per_wave": 2},
-    "pipelined_rows8_lds": {"var_rows_per_wave": 8, "var_load_path": 0},
+    "pipelined_rows2_lds": {"var_rows_per_wave": 2, "var_load_path": 0},
 }
 
 # Axis-0 paths: one workgroup per column tile (rows up to var_cols_single_max)
