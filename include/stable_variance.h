@@ -321,6 +321,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "var_short_rows" rows of at most 512 values: 1 (default) = several rows
  *                    per wave (a group of lanes per row), 0 = one workgroup
  *                    per row
+ *   "var_cols_one"   axis 0, columns of 65 to var_cols_single_max rows
+ *                    with a 16-byte aligned base and a width divisible by 4:
+ *                    1 (default) = four columns per lane, 16-byte loads, G
+ *                    row groups per wave; 0 = one column per lane
  *   "var_cols_single_max"  axis 0: columns of up to this many rows are
  *                    held by one workgroup and read once (0..1024, default
  *                    1024); longer columns are reduced in row chunks

@@ -65,6 +65,7 @@ COL_GEOMETRIES = {
     "chunked_w8": {"var_cols_single_max": 0, "var_cols_waves": 8},
     "chunked_w16": {"var_cols_single_max": 0, "var_cols_waves": 16},
     "single_upto_64": {"var_cols_single_max": 64, "var_cols_waves": 8},
+    "single_lane_per_column": {"var_cols_one": 0},
 }
 
 
@@ -426,6 +427,19 @@ def test_variance_cols_wide(torch_dev, col_geometry, R, C):
     check_var(torch_dev, a, 0, 0)
     check_var(torch_dev, a, 0, 5)
     b = W.adversarial_values(R * C, R + 1).reshape(R, C)
+    check_var(torch_dev, b, 0, 0)
+
+
+@pytest.mark.parametrize("R,C", [(100, 140_000), (400, 40_000), (65, 140_000), (1000, 36_000), (77, 300_000),
+                                 (200, 40_000), (129, 4096), (1024, 64), (65, 8), (16, 140_000)])
+def test_variance_cols_one_launch(torch_dev, R, C):
+    # whole columns in one launch with 16-byte loads: every (G, W) choice,
+    # from 256 columns and 8 waves per workgroup to 16 columns and 4 waves
+    rng = np.random.default_rng(R * 3 + C)
+    a = rng.normal(8e3, 3, (R, C)).astype(np.float32)
+    check_var(torch_dev, a, 0, 0)
+    check_var(torch_dev, a, 0, 1)
+    b = W.adversarial_values(R * C, R + 5).reshape(R, C)
     check_var(torch_dev, b, 0, 0)
 
 
