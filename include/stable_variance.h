@@ -220,7 +220,7 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
  *   slice; workspace of sv_variance_f64_workspace_size(rows, cols, axis)
  *   bytes, 256-byte aligned scratch, NULL allowed when that size is 0.
  * sv_variance_f64_workspace_size: 0 when every slice fits one workgroup
- *   (axis 1: n <= 16384; axis 0: n <= 256).  Longer slices are reduced in
+ *   (axis 1: n <= 16384; axis 0: n <= 1024).  Longer slices are reduced in
  *   chunks (8192 values of a row; 128 rows of a column, or a multiple of 128
  *   for narrow matrices), reading the input twice: three arrays of 16 bytes
  *   per 128-value chunk per slice and 8 bytes per slice, each rounded up to

@@ -542,7 +542,7 @@ __global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restric
 //   axis 1, rows of more than 16384 values: chunks of 8192 values (8 waves
 //     of 64 lanes of 16 doubles); a y node per chunk, a per-row top tree
 //     giving m, d and d^2 nodes per chunk, per-row top trees and step 4.
-//   axis 0, columns of more than 256 values: chunks of 128*G rows of a
+//   axis 0, columns of more than 1024 values: chunks of 128*G rows of a
 //     block of V*64/G columns (lane L = q*G + g holds the V adjacent columns
 //     of group q, one 16-byte load per row when V = 2, for 16 rows; G = 1
 //     for wide matrices, up to 64 for narrow ones); a y node per (chunk,
@@ -900,6 +900,80 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
   }
 }
 
+// Whole columns in one workgroup (R <= 16*G*W rows): the tile layout of
+// k_cols_y_d with a single chunk, and y, m, d and d^2 in one launch, the tile
+// kept in registers between the two passes.  Waves wholly past the last row
+// load nothing (their values are the +0 padding).
+template <int V, int W, int G>
+__global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict__ x, int64_t R, int64_t C,
+                                                       int64_t ddof, double *__restrict__ var_out,
+                                                       double *__restrict__ mean_out) {
+  constexpr int E = L64_E, Q = 64 / G, NC = V * Q;
+  __shared__ NodeD sd[W][V][Q];
+  __shared__ NodeD sq[W][V][Q];
+  __shared__ double sm[V][Q];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane / G, g = lane % G;
+  const int64_t cb = blockIdx.x;
+  const int64_t c0 = cb * NC + (int64_t)q * V;
+  const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
+  const int64_t r0 = rw + (int64_t)g * E;
+  const bool full = r0 + E <= R;
+  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
+  const int64_t left = R - r0;
+  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  double v[V][E];
+  if (rw < R) load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
+  double x0[V];
+  const int64_t cc = c0 < C ? c0 : C - V;
+#pragma unroll
+  for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
+  shift_cols_tile_d<V, E>(v, x0, wave_full, valid);  // +0 past the last row
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const NodeD nd = seg_tree_d<false, G>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k]));
+    if (g == 0) sd[w][k][q] = nd;
+  }
+  __syncthreads();
+  // thread t forms m (then step 4) of column V*tq + tk of the block, t = tk*Q + tq
+  for (int t = threadIdx.x; t < NC; t += 64 * W) {
+    const int tk = t / Q, tq = t % Q;
+    NodeD nn[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) nn[i] = sd[i][tk][tq];
+    sm[tk][tq] = root_value_d(node_tree_d<0, W, W, false>(nn)) / (double)R;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    NodeD nd, nq;
+    if (wave_full) lane_tree_dq_d<false, 0, E, E>(v[k], sm[k][q], E, nd, nq);
+    else lane_tree_dq_d<true, 0, E, E>(v[k], sm[k][q], valid, nd, nq);
+    nd = seg_tree_d<false, G>(nd);
+    nq = seg_tree_d<true, G>(nq);
+    if (g == 0) {
+      sd[w][k][q] = nd;  // the y nodes were read before the barrier
+      sq[w][k][q] = nq;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < NC; t += 64 * W) {
+    const int tk = t / Q, tq = t % Q;
+    const int64_t col = cb * NC + (int64_t)tq * V + tk;
+    if (col < C) {
+      NodeD a[W], b[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        a[i] = sd[i][tk][tq];
+        b[i] = sq[i][tk][tq];
+      }
+      finalize_d(node_tree_d<0, W, W, false>(a), node_tree_d<0, W, W, true>(b), x[col], sm[tk][tq], R, ddof,
+                 var_out + col, mean_out ? mean_out + col : nullptr);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_cols_fin_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t nch,
                                                     int64_t ddof, SliceWsD ws, double *__restrict__ var_out,
                                                     double *__restrict__ mean_out) {
@@ -919,7 +993,7 @@ __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int
 }
 
 constexpr int64_t V64_ROWS_MAX_N = 16384;  // one workgroup per row
-constexpr int64_t V64_COLS_MAX_R = 256;    // one workgroup per 64-column tile
+constexpr int64_t V64_COLS_MAX_R = 1024;   // whole columns in one workgroup
 constexpr int64_t V64_MAX_ELEMS = 1LL << 39;
 
 size_t round256_d(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1008,6 +1082,35 @@ void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const S
   else if (groups > 2) launch_cols_d<V, 16>(x, R, C, ddof, ws, var, mean, st);
   else if (groups > 1) launch_cols_d<V, 32>(x, R, C, ddof, ws, var, mean, st);
   else launch_cols_d<V, 64>(x, R, C, ddof, ws, var, mean, st);
+}
+
+// Columns of 64 < R <= 1024 rows in one launch (V = 2 adjacent columns per
+// lane, or 1): 16*G*W = the power of two at or above R rows per workgroup,
+// V*64/G columns.  Of the (G, W) pairs that hold exactly that many rows (G
+// in 1, 4, 16; W in 1, 2, 4, 8), the smallest G that still gives 512
+// workgroups, else the largest.
+template <int V>
+void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, double *var, double *mean,
+                       hipStream_t st) {
+  int64_t cap = L64_E;
+  while (cap < R) cap *= 2;
+  const int gw = (int)(cap / L64_E);  // 8 .. 64
+  int g = gw >= 16 ? gw / 8 : 1;      // W <= 8
+  if (g == 2 || g == 8) g *= 2;       // G in 1, 4, 16
+  while (g < 16 && g * 4 <= gw && (C + V * 64 / g - 1) / (V * 64 / g) < 512) g *= 4;
+  const int w = gw / g;
+  const dim3 grid((unsigned)((C + V * 64 / g - 1) / (V * 64 / g)));
+#define SV_ONE64(G_, W_) k_cols_one_d<V, W_, G_><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
+  switch (g * 16 + w) {  // R > 64: 16*G*W >= 128
+    case 16 * 1 + 8: SV_ONE64(1, 8); break;
+    case 16 * 4 + 2: SV_ONE64(4, 2); break;
+    case 16 * 4 + 4: SV_ONE64(4, 4); break;
+    case 16 * 4 + 8: SV_ONE64(4, 8); break;
+    case 16 * 16 + 1: SV_ONE64(16, 1); break;
+    case 16 * 16 + 2: SV_ONE64(16, 2); break;
+    default: SV_ONE64(16, 4); break;  // gw = 64
+  }
+#undef SV_ONE64
 }
 
 }  // namespace
@@ -1145,13 +1248,15 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     const SliceWsD ws = slice_ws(workspace, ((n + C64_CHUNK - 1) / C64_CHUNK) * cols);
     if (svh::aligned16(x) && cols % 2 == 0) launch_cols_gd<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
     else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+  } else if (n > 64) {
+    if (svh::aligned16(x) && cols % 2 == 0) launch_cols_one_d<2>(x, rows, cols, ddof, var_out, mean_out, st);
+    else launch_cols_one_d<1>(x, rows, cols, ddof, var_out, mean_out, st);
   } else {
     const dim3 grid((unsigned)((cols + 63) / 64));
 #define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)
     if (n <= 4) SV_COLS64(4, 1);
     else if (n <= 16) SV_COLS64(16, 1);
-    else if (n <= 64) SV_COLS64(16, 4);
-    else SV_COLS64(16, 16);  // n <= V64_COLS_MAX_R
+    else SV_COLS64(16, 4);
 #undef SV_COLS64
   }
   return check_launch("sv_variance_f64");

@@ -158,9 +158,7 @@ def test_f64_sizes_and_argument_errors(L):
     # of 16 bytes per chunk per slice and 8 bytes per slice, each rounded to 256
     r256 = lambda b: (b + 255) // 256 * 256
     ws = L.sv_variance_f64_workspace_size
-    assert ws(7, 16384, 1) == 0 and ws(256, 9, 0) == 0 and ws(0, 5, 0) == 0
-    assert ws(257, 9, 0) == 3 * r256(3 * 9 * 16) + r256(9 * 8)
-    assert ws(1024, 9, 0) == 3 * r256(8 * 9 * 16) + r256(9 * 8)
+    assert ws(7, 16384, 1) == 0 and ws(1024, 9, 0) == 0 and ws(0, 5, 0) == 0
     assert ws(3, 16385, 1) == 3 * r256(3 * 3 * 16) + r256(3 * 8)
     assert ws(1025, 7, 0) == 3 * r256(9 * 7 * 16) + r256(7 * 8)
     assert ws(4096, 4096, 0) == 3 * r256(32 * 4096 * 16) + r256(4096 * 8)

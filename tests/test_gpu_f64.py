@@ -115,17 +115,32 @@ def test_var64_many_short_rows(torch_dev, shape):
 
 @pytest.mark.parametrize("R", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 512, 513, 1000, 1024, 1025, 3000, 8192, 9001])
 def test_var64_cols(torch_dev, R):
-    # above 256 rows: 128-row chunks, two adjacent columns per lane (16-byte
-    # loads) when the width is even, one otherwise; more than 32 chunks per
-    # column take a separate m launch
+    # 65 to 1024 rows: one launch, two adjacent columns per lane (16-byte
+    # loads) when the width is even, one otherwise; above 1024 rows: 128-row
+    # chunks in the same layout, more than 32 chunks per column take a
+    # separate m launch
     rng = np.random.default_rng(R)
     for C in (1, 63, 64, 65, 130):
         a = rng.normal(-5e3, 2, (R, C))
         check_var64(torch_dev, a, 0)
         check_var64(torch_dev, a, 0, 1)
-    if R > 256:
+    if R > 64:
         b = W.adversarial_values(R * 300, R).astype(np.float64).reshape(R, 300) * 1e250
         check_var64(torch_dev, b, 0)
+
+
+@pytest.mark.parametrize("R,C", [(100, 70_000), (400, 20_000), (65, 70_000), (1000, 18_000), (200, 20_000),
+                                 (129, 2048), (1024, 32), (65, 4), (300, 7), (777, 3001), (513, 1)])
+def test_var64_cols_one_launch(torch_dev, R, C):
+    # whole columns of 65..1024 rows in one launch: every (G, W) choice, two
+    # columns per lane (even widths) or one (odd widths)
+    rng = np.random.default_rng(R * 5 + C)
+    a = rng.normal(-6e4, 5, (R, C))
+    check_var64(torch_dev, a, 0)
+    check_var64(torch_dev, a, 0, 1)
+    check_var64(torch_dev, np.ascontiguousarray(a[:, 1:]) if C > 2 else a, 0)
+    b = W.adversarial_values(R * C, R + 9).astype(np.float64).reshape(R, C) * 1e100
+    check_var64(torch_dev, b, 0)
 
 
 @pytest.mark.parametrize("R,C", [(30000, 1), (100000, 1), (300000, 1), (8_400_000, 1), (50000, 2), (20000, 3),
