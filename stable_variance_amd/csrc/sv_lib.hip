@@ -1051,7 +1051,9 @@ struct ColsWs {
 // Loads rows [r0, r0 + E) of the V columns starting at c0 (c0 a multiple of
 // V).  Columns past C read the last in-range columns instead (their results
 // are never written); rows past R read row R-1 (masked to +0 afterwards).
-template <int V, int E>
+// VEC16: one 16-byte load per row when V = 4 (base and width allow it);
+// else V 4-byte loads, which read the same cache lines.
+template <int V, int E, bool VEC16 = true>
 __device__ __forceinline__ void load_cols_tile(const float *__restrict__ x, int64_t R, int64_t C, int64_t c0,
                                                int64_t r0, bool full, float (&v)[V][E]) {
   const int64_t cc = c0 < C ? c0 : C - V;
@@ -1059,7 +1061,7 @@ __device__ __forceinline__ void load_cols_tile(const float *__restrict__ x, int6
   for (int i = 0; i < E; ++i) {
     const int64_t r = full ? r0 + i : (r0 + i < R ? r0 + i : R - 1);
     const float *p = x + r * C + cc;
-    if constexpr (V == 4) {
+    if constexpr (V == 4 && VEC16) {
       const float4 g = *reinterpret_cast<const float4 *>(p);
       v[0][i] = g.x;
       v[1][i] = g.y;
@@ -1307,7 +1309,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
 // k_cols_y with a single chunk, and y, m, d and d^2 in one launch, the tile
 // kept in registers between the two passes.  Waves wholly past the last row
 // load nothing (their values are the +0 padding).
-template <int V, int W, int G>
+template <int V, int W, int G, bool VEC16>
 __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
   constexpr int E = CC_E, Q = 64 / G, NC = V * Q;
@@ -1327,7 +1329,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
 
   float v[V][E];
-  if (rw < R) load_cols_tile<V, E>(x, R, C, c0, r0, full, v);
+  if (rw < R) load_cols_tile<V, E, VEC16>(x, R, C, c0, r0, full, v);
   float x0[V];
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
@@ -1514,7 +1516,7 @@ struct Tuning {
   int var_cols_single_max = 1024;  // axis 0: rows up to which one workgroup holds a column tile (<= 1024)
   int var_cols_waves = 16;    // axis 0, chunked: waves per workgroup (4, 8, 16); chunks of 16 * waves rows
   int var_short_rows = 1;     // rows of <= 512 values share waves (0: one workgroup per row)
-  int var_cols_one = 1;       // axis 0, whole columns: 16-byte tiles when aligned (0: a lane per column)
+  int var_cols_one = 1;       // axis 0, 65..1024 rows: 1 auto, 2 four columns per lane, 3 one, 0 the lane kernel
   int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
   int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
 };
@@ -1625,10 +1627,13 @@ void launch_cols_v(const float *x, int64_t R, int64_t C, int64_t ddof, const Col
   else launch_cols_g<V, 4>(x, R, C, ddof, ws, var, mean, st);
 }
 
-// Columns of 64 < R <= 1024 rows in one launch: 16*G*W = the power of two at or
-// above R rows per workgroup, 4*64/G columns.  Of the (G, W) pairs that hold
-// exactly that many rows (G in 1, 4, 16; W in 1, 2, 4, 8), the smallest G
-// that still gives 512 workgroups, else the largest.
+// Columns of 64 < R <= 1024 rows in one launch (k_cols_one), four adjacent
+// columns per lane (one 16-byte load per row when VEC16, else four 4-byte
+// loads): 16*G*W
+// = the power of two at or above R rows per workgroup, 4*64/G columns.  Of
+// the (G, W) pairs that hold exactly that many rows (G in 1, 4, 16; W in 1,
+// 2, 4, 8), the smallest G that still gives 512 workgroups, else the largest.
+template <bool VEC16>
 void launch_cols_one(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
   int64_t cap = CC_E;
   while (cap < R) cap *= 2;
@@ -1638,7 +1643,7 @@ void launch_cols_one(const float *x, int64_t R, int64_t C, int64_t ddof, float *
   while (g < 16 && g * 4 <= gw && (C + 4 * 64 / g - 1) / (4 * 64 / g) < 512) g *= 4;
   const int w = gw / g;
   const dim3 grid((unsigned)((C + 4 * 64 / g - 1) / (4 * 64 / g)));
-#define SV_ONE(G_, W_) k_cols_one<4, W_, G_><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
+#define SV_ONE(G_, W_) k_cols_one<4, W_, G_, VEC16><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
   switch (g * 16 + w) {  // R > 64: 16*G*W >= 128
     case 16 * 1 + 8: SV_ONE(1, 8); break;
     case 16 * 4 + 2: SV_ONE(4, 2); break;
@@ -1647,6 +1652,28 @@ void launch_cols_one(const float *x, int64_t R, int64_t C, int64_t ddof, float *
     case 16 * 16 + 1: SV_ONE(16, 1); break;
     case 16 * 16 + 2: SV_ONE(16, 2); break;
     default: SV_ONE(16, 4); break;  // gw = 64
+  }
+#undef SV_ONE
+}
+
+// The same with one column per lane (16 values per lane: four times the
+// waves of four columns per lane): G in 1, 4 (row segments of at least 16
+// lanes, 64 bytes), W up to 16; G = 1 when that gives 512 workgroups.
+void launch_cols_one1(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
+  int64_t cap = CC_E;
+  while (cap < R) cap *= 2;
+  const int gw = (int)(cap / CC_E);  // 8 .. 64
+  const int g = (gw > 16 || (C + 63) / 64 < 512) && gw >= 8 ? 4 : 1;
+  const int w = gw / g;
+  const dim3 grid((unsigned)((C + 64 / g - 1) / (64 / g)));
+#define SV_ONE(G_, W_) k_cols_one<1, W_, G_, false><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
+  switch (g * 32 + w) {  // R > 64: 16*G*W >= 128
+    case 32 * 1 + 8: SV_ONE(1, 8); break;
+    case 32 * 1 + 16: SV_ONE(1, 16); break;
+    case 32 * 4 + 2: SV_ONE(4, 2); break;
+    case 32 * 4 + 4: SV_ONE(4, 4); break;
+    case 32 * 4 + 8: SV_ONE(4, 8); break;
+    default: SV_ONE(4, 16); break;  // gw = 64
   }
 #undef SV_ONE
 }
@@ -2072,11 +2099,20 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
       launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     }
   } else {
-    // columns of more than 64 rows: four columns per lane (16-byte loads); up
-    // to 64 rows the lane-per-column kernel, whose lanes hold exactly 4, 16
-    // or 64 rows, is as fast or faster ([4, 1000000]: 6.5 against 16 us)
-    if (g_tune.var_cols_one && n > 64 && aligned16(x) && cols % 4 == 0)
-      launch_cols_one(x, rows, cols, ddof, var_out, mean_out, st);
+    // columns of more than 64 rows (and at least 4 of them): one launch with
+    // four columns per lane; up to 64 rows the lane-per-column kernel, whose
+    // lanes hold exactly 4, 16 or 64 rows, is as fast or faster ([4, 1000000]:
+    // 6.5 against 16 us)
+    if (g_tune.var_cols_one && n > 64) {
+      // four columns per lane for long columns (513..1024 rows) of wide
+      // matrices, else one: [1000, 20000] 31.0 against 37.1 us, [300, 50000]
+      // 34.1 against 24.0, [512, 4096] 7.0 against 4.8
+      const int mode = g_tune.var_cols_one;
+      const bool four = cols >= 4 && (mode == 2 || (mode == 1 && n > 512 && cols >= 8192));
+      if (!four) launch_cols_one1(x, rows, cols, ddof, var_out, mean_out, st);
+      else if (aligned16(x) && cols % 4 == 0) launch_cols_one<true>(x, rows, cols, ddof, var_out, mean_out, st);
+      else launch_cols_one<false>(x, rows, cols, ddof, var_out, mean_out, st);
+    }
     else if (n <= 4) launch_cols_ew<4, 1>(x, rows, cols, ddof, var_out, mean_out, st);
     else if (n <= 16) launch_cols_ew<16, 1>(x, rows, cols, ddof, var_out, mean_out, st);
     else if (n <= 64) launch_cols_ew<64, 1>(x, rows, cols, ddof, var_out, mean_out, st);
@@ -2286,7 +2322,12 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_short_rows") == 0) return flag(&g_tune.var_short_rows);
-  if (strcmp(key, "var_cols_one") == 0) return flag(&g_tune.var_cols_one);
+  if (strcmp(key, "var_cols_one") == 0) {
+    if (value < 0 || value > 3)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_one must be 0, 1, 2 or 3");
+    g_tune.var_cols_one = (int)value;
+    return ok();
+  }
   if (strcmp(key, "sum_xcd") == 0) return flag(&g_tune.sum_xcd);
   if (strcmp(key, "var_xcd") == 0) return flag(&g_tune.var_xcd);
   if (strcmp(key, "var_lds_pad") == 0) {

@@ -66,6 +66,8 @@ COL_GEOMETRIES = {
     "chunked_w16": {"var_cols_single_max": 0, "var_cols_waves": 16},
     "single_upto_64": {"var_cols_single_max": 64, "var_cols_waves": 8},
     "single_lane_per_column": {"var_cols_one": 0},
+    "single_four_columns_per_lane": {"var_cols_one": 2},
+    "single_one_column_per_lane": {"var_cols_one": 3},
 }
 
 
@@ -431,10 +433,22 @@ def test_variance_cols_wide(torch_dev, col_geometry, R, C):
 
 
 @pytest.mark.parametrize("R,C", [(100, 140_000), (400, 40_000), (65, 140_000), (1000, 36_000), (77, 300_000),
-                                 (200, 40_000), (129, 4096), (1024, 64), (65, 8), (16, 140_000)])
-def test_variance_cols_one_launch(torch_dev, R, C):
-    # whole columns in one launch with 16-byte loads: every (G, W) choice,
-    # from 256 columns and 8 waves per workgroup to 16 columns and 4 waves
+                                 (200, 40_000), (129, 4096), (1024, 64), (65, 8), (16, 140_000), (600, 9001),
+                                 (900, 8193), (300, 3), (100, 140_001), (200, 40_001), (400, 40_001)])
+@pytest.mark.parametrize("mode", [1, 2, 3])
+def test_variance_cols_one_launch(torch_dev, R, C, mode):
+    # whole columns in one launch: every (G, W) choice of four columns per
+    # lane (16-byte loads, or four 4-byte loads for odd widths) and of one
+    import stable_variance_amd as sv
+
+    sv.set_tuning("var_cols_one", mode)
+    try:
+        _cols_one_cases(torch_dev, R, C)
+    finally:
+        sv.set_tuning("reset", 0)
+
+
+def _cols_one_cases(torch_dev, R, C):
     rng = np.random.default_rng(R * 3 + C)
     a = rng.normal(8e3, 3, (R, C)).astype(np.float32)
     check_var(torch_dev, a, 0, 0)
