@@ -1084,31 +1084,35 @@ void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const S
   else launch_cols_d<V, 64>(x, R, C, ddof, ws, var, mean, st);
 }
 
-// Columns of 64 < R <= 1024 rows in one launch (V = 2 adjacent columns per
-// lane, or 1): 16*G*W = the power of two at or above R rows per workgroup,
-// V*64/G columns.  Of the (G, W) pairs that hold exactly that many rows (G
-// in 1, 4, 16; W in 1, 2, 4, 8), the smallest G that still gives 512
-// workgroups, else the largest.
-template <int V>
-void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, double *var, double *mean,
+// Columns of 64 < R <= 1024 rows in one launch (k_cols_one_d), 16*G*W = the
+// power of two at or above R rows per workgroup:
+//   R <= 512: one column per lane (16 doubles per lane), G 1 or 4 (row
+//     segments of at least 16 lanes, 128 bytes), W up to 16, G = 1 when that
+//     still gives 512 workgroups;
+//   R > 512: two adjacent columns per lane (one 16-byte load per row) for an
+//     aligned base and an even width, else one; G = 16, W = 4.
+// Measured (us, one column per lane against two): [100, 140000] 26.5 / 39.6,
+// [512, 4096] 8.0 / 10.9; [1000, 20000] 65.2 / 52.5, [1000, 1000] 13.0 / 6.9.
+void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool vec, double *var, double *mean,
                        hipStream_t st) {
+  if (R > 512) {
+    if (vec) k_cols_one_d<2, 4, 16><<<dim3((unsigned)((C + 7) / 8)), dim3(256), 0, st>>>(x, R, C, ddof, var, mean);
+    else k_cols_one_d<1, 4, 16><<<dim3((unsigned)((C + 3) / 4)), dim3(256), 0, st>>>(x, R, C, ddof, var, mean);
+    return;
+  }
   int64_t cap = L64_E;
   while (cap < R) cap *= 2;
-  const int gw = (int)(cap / L64_E);  // 8 .. 64
-  int g = gw >= 16 ? gw / 8 : 1;      // W <= 8
-  if (g == 2 || g == 8) g *= 2;       // G in 1, 4, 16
-  while (g < 16 && g * 4 <= gw && (C + V * 64 / g - 1) / (V * 64 / g) < 512) g *= 4;
+  const int gw = (int)(cap / L64_E);  // 8 .. 32
+  const int g = (gw > 16 || (C + 63) / 64 < 512) ? 4 : 1;
   const int w = gw / g;
-  const dim3 grid((unsigned)((C + V * 64 / g - 1) / (V * 64 / g)));
-#define SV_ONE64(G_, W_) k_cols_one_d<V, W_, G_><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
-  switch (g * 16 + w) {  // R > 64: 16*G*W >= 128
-    case 16 * 1 + 8: SV_ONE64(1, 8); break;
-    case 16 * 4 + 2: SV_ONE64(4, 2); break;
-    case 16 * 4 + 4: SV_ONE64(4, 4); break;
-    case 16 * 4 + 8: SV_ONE64(4, 8); break;
-    case 16 * 16 + 1: SV_ONE64(16, 1); break;
-    case 16 * 16 + 2: SV_ONE64(16, 2); break;
-    default: SV_ONE64(16, 4); break;  // gw = 64
+  const dim3 grid((unsigned)((C + 64 / g - 1) / (64 / g)));
+#define SV_ONE64(G_, W_) k_cols_one_d<1, W_, G_><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
+  switch (g * 32 + w) {  // 64 < R <= 512: 128 <= 16*G*W <= 512
+    case 32 * 1 + 8: SV_ONE64(1, 8); break;
+    case 32 * 1 + 16: SV_ONE64(1, 16); break;
+    case 32 * 4 + 2: SV_ONE64(4, 2); break;
+    case 32 * 4 + 4: SV_ONE64(4, 4); break;
+    default: SV_ONE64(4, 8); break;  // gw = 32
   }
 #undef SV_ONE64
 }
@@ -1249,8 +1253,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     if (svh::aligned16(x) && cols % 2 == 0) launch_cols_gd<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
     else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
   } else if (n > 64) {
-    if (svh::aligned16(x) && cols % 2 == 0) launch_cols_one_d<2>(x, rows, cols, ddof, var_out, mean_out, st);
-    else launch_cols_one_d<1>(x, rows, cols, ddof, var_out, mean_out, st);
+    launch_cols_one_d(x, rows, cols, ddof, svh::aligned16(x) && cols % 2 == 0, var_out, mean_out, st);
   } else {
     const dim3 grid((unsigned)((cols + 63) / 64));
 #define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)

@@ -130,10 +130,11 @@ def test_var64_cols(torch_dev, R):
 
 
 @pytest.mark.parametrize("R,C", [(100, 70_000), (400, 20_000), (65, 70_000), (1000, 18_000), (200, 20_000),
-                                 (129, 2048), (1024, 32), (65, 4), (300, 7), (777, 3001), (513, 1)])
+                                 (200, 40_000), (129, 2048), (1024, 32), (65, 4), (300, 7), (777, 3001), (513, 1)])
 def test_var64_cols_one_launch(torch_dev, R, C):
-    # whole columns of 65..1024 rows in one launch: every (G, W) choice, two
-    # columns per lane (even widths) or one (odd widths)
+    # whole columns of 65..1024 rows in one launch: up to 512 rows one column
+    # per lane in every (G, W) choice; above, two columns per lane (even
+    # widths) or one (odd widths)
     rng = np.random.default_rng(R * 5 + C)
     a = rng.normal(-6e4, 5, (R, C))
     check_var64(torch_dev, a, 0)
