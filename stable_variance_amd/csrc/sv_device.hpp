@@ -441,9 +441,13 @@ __device__ __forceinline__ float ld1(const float *p) {
   else return *p;
 }
 
+// avail: floats readable from p (the rest of the matrix, at least len).  A
+// ragged tile with a whole tile readable (every row but the last few) loads
+// as a full one, one base address with immediate offsets, and masks the
+// values past len; otherwise each load's index is clamped to the data.
 template <int E, bool VEC, int LOADP, bool NT = false>
 __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t len, float *__restrict__ lds,
-                                          float (&v)[E], int lane) {
+                                          float (&v)[E], int lane, int64_t avail = 0) {
   static_assert(E >= 4 && (E & (E - 1)) == 0, "E must be a power of two >= 4");
   constexpr int J = E / 4;
   constexpr int STR = E + 4;
@@ -487,7 +491,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
   }
   if constexpr (LOADP == 1 || LOADP == 2) {
     const int e0 = lane * E;
-    if (full) {
+    if (full || avail >= TILE) {  // wave-uniform
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (VEC) {
@@ -497,6 +501,10 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
 #pragma unroll
           for (int t = 0; t < 4; ++t) v[4 * j + t] = ld1<NT>(p + e0 + 4 * j + t);
         }
+      }
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) v[i] = (e0 + i < lim) ? v[i] : 0.0f;
       }
     } else if constexpr (VEC) {
       // lim is a multiple of 4 (16-byte aligned rows of a multiple of 4

@@ -373,7 +373,9 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   const int64_t base = (int64_t)w * 64 * E;
 
   float vf[2 * E];
-  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(p + base), 2 * (n - base), nullptr, vf, lane);
+  const int64_t avail = 2 * (((int64_t)gridDim.x - 1 - row) * ld + (n - base));  // floats to the matrix's end
+  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(p + base), 2 * (n - base), nullptr, vf, lane,
+                                      avail);
   double v[E];
   floats_to_doubles<E>(vf, v);
   const double x0 = p[0];
@@ -592,7 +594,9 @@ __global__ __launch_bounds__(64 * L64_W) void k_long_rows_d(const double *__rest
   const int64_t base = c * L64_ROW_CHUNK + (int64_t)w * 64 * E;
   const bool empty = base >= n;  // wave-uniform: only padding, nodes (+0, +0)
   float vf[2 * E];
-  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(row + base), 2 * (n - base), nullptr, vf, lane);
+  const int64_t avail = 2 * (((int64_t)gridDim.x / nch - 1 - r) * ld + (n - base));  // floats to the matrix's end
+  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(row + base), 2 * (n - base), nullptr, vf, lane,
+                                      avail);
   double v[E];
   floats_to_doubles<E>(vf, v);
   const double x0 = row[0];

@@ -446,7 +446,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
   const int64_t base = (int64_t)w * 64 * E;  // first complex value of this wave
   const bool empty = base >= n;
   float f[2 * E];
-  sv::load_tile<2 * E, VEC, 1, false>(p + 2 * base, 2 * (n - base), nullptr, f, lane);
+  const int64_t avail = 2 * (((int64_t)gridDim.x - 1 - row) * n + (n - base));  // floats to the array's end
+  sv::load_tile<2 * E, VEC, 1, false>(p + 2 * base, 2 * (n - base), nullptr, f, lane, avail);
   const float x0r = p[0], x0i = p[1];
   const bool full = base + 64 * E <= n;
   const int64_t left = n - base - (int64_t)lane * E;
@@ -654,7 +655,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   // them (the branch is wave-uniform).
   const bool empty = base >= n;
   float v[E];
-  sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, vl);
+  const int64_t avail = ((int64_t)gridDim.x - 1 - row) * ld + (n - base);  // to the matrix's end
+  sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, vl, avail);
   const float x0 = p[0];
 
   // step 1: shift by the first element (padding stays +0)
@@ -1423,7 +1425,8 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
   const int64_t base = c * LS_ROW_CHUNK + (int64_t)w * 64 * E;
   float v[E];
   float dummy_lds[1];
-  sv::load_tile<E, VEC, 1, false>(row + base, n - base, dummy_lds, v, lane);
+  const int64_t avail = ((int64_t)gridDim.x / nch - 1 - r) * ld + (n - base);  // to the matrix's end
+  sv::load_tile<E, VEC, 1, false>(row + base, n - base, dummy_lds, v, lane, avail);
   const float x0 = row[0];
   const bool full = base + 64 * E <= n;
   const int64_t vl = n - base - (int64_t)lane * E;
