@@ -321,6 +321,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "var_short_rows" rows of at most 512 values: 1 (default) = several rows
  *                    per wave (a group of lanes per row), 0 = one workgroup
  *                    per row
+ *   "var_long_rows"  axis 1, rows of 16385..65536 values when there are at
+ *                    least 256 rows: 1 (default) = one workgroup of 16 waves
+ *                    per row, the row read once (the workspace is then not
+ *                    used); 0 = the chunked path
  *   "var_cols_one"   axis 0, columns of 65 to var_cols_single_max rows:
  *                    one launch of G row groups per wave with 2 = four
  *                    columns per lane (one 16-byte load per row for a 16-byte

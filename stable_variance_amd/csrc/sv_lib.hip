@@ -1520,6 +1520,7 @@ struct Tuning {
   int var_cols_waves = 16;    // axis 0, chunked: waves per workgroup (4, 8, 16); chunks of 16 * waves rows
   int var_short_rows = 1;     // rows of <= 512 values share waves (0: one workgroup per row)
   int var_cols_one = 1;       // axis 0, 65..1024 rows: 1 auto, 2 four columns per lane, 3 one, 0 the lane kernel
+  int var_long_rows = 1;      // rows of 16385..65536 values, 256+ rows: 1 one workgroup per row, 0 chunked
   int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
   int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
 };
@@ -1527,7 +1528,11 @@ Tuning g_tune;
 
 constexpr int64_t SUM_MAX_N = 1LL << 36;
 constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
-constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel
+constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel for any number of rows
+// Rows of up to 65536 values also take one workgroup per row (16 waves) when
+// there are enough rows to fill the chip; fewer rows take the chunked path.
+constexpr int64_t ROWS_ONE_MAX_N = 65536;
+constexpr int64_t ROWS_ONE_MIN_ROWS = 256;
 constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
 
 // Long-slice workspace: y, d and d^2 chunk nodes per slice, then m.
@@ -1870,10 +1875,16 @@ void launch_rows_tile(bool vec, const float *x, int64_t rows, int64_t n, int64_t
     else if (s == 2) launch_rows_split<32, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
     else if (s == 4) launch_rows_split<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
     else launch_rows_split<8, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
-  } else {
+  } else if (n <= ROWS_MAX_N) {
     if (s == 1) launch_rows_ew<64, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
     else if (s == 2) launch_rows_split<32, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
     else launch_rows_split<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
+  } else if (n <= 32768) {  // 16 waves of 32 values (per-lane loads)
+    if (vec) launch_rows_t<32, 16, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+    else launch_rows_t<32, 16, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+  } else {  // n <= ROWS_ONE_MAX_N: 16 waves of 64 values
+    if (vec) launch_rows_t<64, 16, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+    else launch_rows_t<64, 16, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
   }
 }
 
@@ -2066,7 +2077,7 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
     return check_launch("sv_variance_f32");
   }
-  if (is_long) {
+  if (is_long && !(g_tune.var_long_rows && n <= ROWS_ONE_MAX_N && rows >= ROWS_ONE_MIN_ROWS)) {
     const LongWs ws = long_ws(workspace, nslices, nch);
     const bool vec = aligned16(x) && (cols % 4 == 0);
     const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
@@ -2325,6 +2336,7 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_short_rows") == 0) return flag(&g_tune.var_short_rows);
+  if (strcmp(key, "var_long_rows") == 0) return flag(&g_tune.var_long_rows);
   if (strcmp(key, "var_cols_one") == 0) {
     if (value < 0 || value > 3)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_one must be 0, 1, 2 or 3");

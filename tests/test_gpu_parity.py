@@ -391,6 +391,24 @@ def test_variance_unsupported_shape_leaves_output(torch_dev):
     assert L.sv_variance_f32_workspace_size(1, big, 1) == ctypes.c_size_t(-1).value
 
 
+@pytest.mark.parametrize("n", [16385, 20001, 32768, 32769, 50002, 65536])
+@pytest.mark.parametrize("long_rows", [1, 0])
+def test_variance_long_rows_one_workgroup(torch_dev, n, long_rows):
+    # 256+ rows of 16385..65536 values: one workgroup of 16 waves per row
+    # (32 or 64 values per lane), or the chunked path; odd lengths load
+    # without 16-byte vectors
+    import stable_variance_amd as sv
+
+    sv.set_tuning("var_long_rows", long_rows)
+    try:
+        rng = np.random.default_rng(n + long_rows)
+        a = rng.normal(-2e4, 5, (300, n)).astype(np.float32)
+        check_var(torch_dev, a, 1, 0)
+        check_var(torch_dev, a, 1, 2)
+    finally:
+        sv.set_tuning("reset", 0)
+
+
 LONG_ROW_NS = [16385, 20000, 32768, 50001, 100003]
 
 
