@@ -325,6 +325,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    least 256 rows: 1 (default) = one workgroup of 16 waves
  *                    per row, the row read once (the workspace is then not
  *                    used); 0 = the chunked path
+ *   "var_cols_short" axis 0, columns of at most 15 rows with a 16-byte
+ *                    aligned base and a width divisible by 4: 1 (default) =
+ *                    four columns per lane, every tree in-lane; 0 = a lane
+ *                    per column
  *   "var_cols_one"   axis 0, columns of 65 to var_cols_single_max rows:
  *                    one launch of G row groups per wave with 2 = four
  *                    columns per lane (one 16-byte load per row for a 16-byte

@@ -1521,6 +1521,7 @@ struct Tuning {
   int var_short_rows = 1;     // rows of <= 512 values share waves (0: one workgroup per row)
   int var_cols_one = 1;       // axis 0, 65..1024 rows: 1 auto, 2 four columns per lane, 3 one, 0 the lane kernel
   int var_long_rows = 1;      // rows of 16385..65536 values, 256+ rows: 1 one workgroup per row, 0 chunked
+  int var_cols_short = 1;     // axis 0, columns of <= 15 rows: 1 four columns per lane, 0 the lane kernel
   int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
   int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
 };
@@ -1912,6 +1913,60 @@ void launch_pipe_r(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld
   }
 }
 
+// Axis 0, short columns (R <= E rows, E <= 16, R < 16): each lane owns four adjacent
+// columns (one 16-byte load per row, 16-byte aligned base and a width
+// divisible by 4) and all three trees are in-lane: no cross-lane levels, no
+// LDS, no barrier.  Rows past R are the +0 padding of the column's tree.
+template <int E>
+__global__ __launch_bounds__(256) void k_cols_short(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
+                                                    float *__restrict__ var_out, float *__restrict__ mean_out) {
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c0 >= C) return;
+  const float *__restrict__ p = x + c0;
+  float v[4][E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float4 g = *reinterpret_cast<const float4 *>(p + (i < R ? i : R - 1) * C);
+    v[0][i] = g.x;
+    v[1][i] = g.y;
+    v[2][i] = g.z;
+    v[3][i] = g.w;
+  }
+  const int valid = (int)R;  // R <= E
+  float var4[4], mean4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = v[k][0];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[k][i] = (i < valid) ? v[k][i] - x0 : 0.0f;
+    const float m = sv::root_value(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k])) / (float)R;
+    Node nd, nq;
+    sv::lane_tree_dq<true, 0, E, E>(v[k], m, valid, nd, nq);
+    finalize(nd, nq, x0, m, R, ddof, &var4[k], &mean4[k]);
+  }
+  // one 16-byte store per output (c0 is a multiple of 4, the outputs 16-byte
+  // aligned when they are; else four 4-byte stores)
+  auto store4 = [&](float *out, const float (&t)[4]) {
+    float *o = out + c0;
+    if ((reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+      *reinterpret_cast<float4 *>(o) = make_float4(t[0], t[1], t[2], t[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = t[k];
+    }
+  };
+  store4(var_out, var4);
+  if (mean_out) store4(mean_out, mean4);
+}
+
+void launch_cols_short(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
+  const dim3 grid((unsigned)((C / 4 + 255) / 256)), block(256);
+  if (R <= 2) k_cols_short<2><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+  else if (R <= 4) k_cols_short<4><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+  else if (R <= 8) k_cols_short<8><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+  else k_cols_short<16><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+}
+
 template <int E, int W>
 void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
   const dim3 grid((unsigned)((C + 63) / 64)), block(64 * W);
@@ -2113,11 +2168,15 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
       launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     }
   } else {
-    // columns of more than 64 rows (and at least 4 of them): one launch with
-    // four columns per lane; up to 64 rows the lane-per-column kernel, whose
-    // lanes hold exactly 4, 16 or 64 rows, is as fast or faster ([4, 1000000]:
-    // 6.5 against 16 us)
-    if (g_tune.var_cols_one && n > 64) {
+    // columns of at most 15 rows: four columns per lane, every tree in-lane
+    // (at 16 rows the lane kernel's lanes hold exactly 16: [16, 1000000] 12.7
+    // against 16.7 us);
+    // more than 64 rows: one launch of G row groups per wave; otherwise the
+    // lane-per-column kernel, whose lanes hold exactly 4, 16 or 64 rows
+    // (faster than G row groups there: [4, 1000000] 6.5 against 16 us)
+    if (n < 16 && g_tune.var_cols_short && aligned16(x) && cols % 4 == 0) {
+      launch_cols_short(x, rows, cols, ddof, var_out, mean_out, st);
+    } else if (g_tune.var_cols_one && n > 64) {
       // four columns per lane for long columns (513..1024 rows) of wide
       // matrices, else one: [1000, 20000] 31.0 against 37.1 us, [300, 50000]
       // 34.1 against 24.0, [512, 4096] 7.0 against 4.8
@@ -2337,6 +2396,7 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
   }
   if (strcmp(key, "var_short_rows") == 0) return flag(&g_tune.var_short_rows);
   if (strcmp(key, "var_long_rows") == 0) return flag(&g_tune.var_long_rows);
+  if (strcmp(key, "var_cols_short") == 0) return flag(&g_tune.var_cols_short);
   if (strcmp(key, "var_cols_one") == 0) {
     if (value < 0 || value > 3)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_one must be 0, 1, 2 or 3");

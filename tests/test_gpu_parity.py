@@ -65,7 +65,7 @@ COL_GEOMETRIES = {
     "chunked_w8": {"var_cols_single_max": 0, "var_cols_waves": 8},
     "chunked_w16": {"var_cols_single_max": 0, "var_cols_waves": 16},
     "single_upto_64": {"var_cols_single_max": 64, "var_cols_waves": 8},
-    "single_lane_per_column": {"var_cols_one": 0},
+    "single_lane_per_column": {"var_cols_one": 0, "var_cols_short": 0},
     "single_four_columns_per_lane": {"var_cols_one": 2},
     "single_one_column_per_lane": {"var_cols_one": 3},
 }
@@ -472,6 +472,20 @@ def _cols_one_cases(torch_dev, R, C):
     check_var(torch_dev, a, 0, 0)
     check_var(torch_dev, a, 0, 1)
     b = W.adversarial_values(R * C, R + 5).reshape(R, C)
+    check_var(torch_dev, b, 0, 0)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 9, 15, 16])
+def test_variance_short_cols_wide(torch_dev, R):
+    # columns of at most 15 rows, four per lane, every tree in-lane (16: the
+    # lane-per-column kernel)
+    rng = np.random.default_rng(R + 77)
+    for C in (4, 8, 1028, 250_000):
+        a = rng.normal(3e3, 2, (R, C)).astype(np.float32)
+        check_var(torch_dev, a, 0, 0)
+        check_var(torch_dev, a, 0, 1)
+        check_var(torch_dev, a, 0, 5)
+    b = W.adversarial_values(R * 4096, R + 3).reshape(R, 4096)
     check_var(torch_dev, b, 0, 0)
 
 
