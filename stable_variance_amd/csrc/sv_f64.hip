@@ -371,6 +371,9 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   const int64_t row = blockIdx.x;
   const double *__restrict__ p = x + row * ld;
   const int64_t base = (int64_t)w * 64 * E;
+  // a wave wholly past the row holds only padding: its nodes are (+0, +0),
+  // what its trees would compute, so it skips them (wave-uniform)
+  const bool empty = base >= n;
 
   float vf[2 * E];
   const int64_t avail = 2 * (((int64_t)gridDim.x - 1 - row) * ld + (n - base));  // floats to the matrix's end
@@ -391,7 +394,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
     for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0;
   }
 
-  NodeD ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
+  NodeD ny = {0.0, 0.0};
+  if (!empty) ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
@@ -402,11 +406,13 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   }
   const double m = root_value_d(ny) / (double)n;
 
-  NodeD nd, nq;
-  if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
-  else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
-  nd = wave_tree_d<false>(nd);
-  nq = wave_tree_d<true>(nq);
+  NodeD nd = {0.0, 0.0}, nq = {0.0, 0.0};
+  if (!empty) {
+    if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
+    else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
+    nd = wave_tree_d<false>(nd);
+    nq = wave_tree_d<true>(nq);
+  }
   if constexpr (W > 1) {
     if (lane == 0) {
       slots[1][w] = nd;
@@ -666,7 +672,9 @@ __global__ __launch_bounds__(256) void k_long_top_d(const double *__restrict__ x
 // Axis 0: rows [r0, r0 + E) of the V columns starting at c0 (a multiple of
 // V); columns past C read the last in-range ones (never written), rows past
 // R read row R-1 (masked to +0 afterwards).
-template <int V, int E>
+// VEC16: one 16-byte load per row when V = 2 (base and width allow it);
+// else V 8-byte loads, which read the same cache lines.
+template <int V, int E, bool VEC16 = true>
 __device__ __forceinline__ void load_cols_tile_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t c0,
                                                  int64_t r0, bool full, double (&v)[V][E]) {
   const int64_t cc = c0 < C ? c0 : C - V;
@@ -674,12 +682,13 @@ __device__ __forceinline__ void load_cols_tile_d(const double *__restrict__ x, i
   for (int i = 0; i < E; ++i) {
     const int64_t r = full ? r0 + i : (r0 + i < R ? r0 + i : R - 1);
     const double *p = x + r * C + cc;
-    if constexpr (V == 2) {
+    if constexpr (V == 2 && VEC16) {
       const double2 g = *reinterpret_cast<const double2 *>(p);
       v[0][i] = g.x;
       v[1][i] = g.y;
     } else {
-      v[0][i] = p[0];
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k][i] = p[k];
     }
   }
 }
@@ -908,7 +917,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
 // k_cols_y_d with a single chunk, and y, m, d and d^2 in one launch, the tile
 // kept in registers between the two passes.  Waves wholly past the last row
 // load nothing (their values are the +0 padding).
-template <int V, int W, int G>
+template <int V, int W, int G, bool VEC16 = true>
 __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                        int64_t ddof, double *__restrict__ var_out,
                                                        double *__restrict__ mean_out) {
@@ -928,7 +937,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
   double v[V][E];
-  if (rw < R) load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
+  if (rw < R) load_cols_tile_d<V, E, VEC16>(x, R, C, c0, r0, full, v);
   double x0[V];
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
@@ -976,6 +985,49 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
                  var_out + col, mean_out ? mean_out + col : nullptr);
     }
   }
+}
+
+// Axis 0, short columns (R <= E rows, E <= 16, R < 16): each lane owns two
+// adjacent columns (one 16-byte load per row, 16-byte aligned base and an
+// even width) and all three trees are in-lane: no cross-lane levels, no
+// LDS, no barrier.  Rows past R are the +0 padding of the column's tree.
+template <int E>
+__global__ __launch_bounds__(256) void k_cols_short_d(const double *__restrict__ x, int64_t R, int64_t C,
+                                                      int64_t ddof, double *__restrict__ var_out,
+                                                      double *__restrict__ mean_out) {
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+  if (c0 >= C) return;
+  const double *__restrict__ p = x + c0;
+  double v[2][E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const double2 g = *reinterpret_cast<const double2 *>(p + (i < R ? i : R - 1) * C);
+    v[0][i] = g.x;
+    v[1][i] = g.y;
+  }
+  const int valid = (int)R;  // R <= E
+  double var2[2], mean2[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const double x0 = v[k][0];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[k][i] = (i < valid) ? v[k][i] - x0 : 0.0;
+    const double m = root_value_d(lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k])) / (double)R;
+    NodeD nd, nq;
+    lane_tree_dq_d<true, 0, E, E>(v[k], m, valid, nd, nq);
+    finalize_d(nd, nq, x0, m, R, ddof, &var2[k], &mean2[k]);
+  }
+  auto store2 = [&](double *out, const double (&t)[2]) {
+    double *o = out + c0;
+    if ((reinterpret_cast<uintptr_t>(out) & 15u) == 0) {
+      *reinterpret_cast<double2 *>(o) = make_double2(t[0], t[1]);
+    } else {
+      o[0] = t[0];
+      o[1] = t[1];
+    }
+  };
+  store2(var_out, var2);
+  if (mean_out) store2(mean_out, mean2);
 }
 
 __global__ __launch_bounds__(256) void k_cols_fin_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t nch,
@@ -1093,15 +1145,18 @@ void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const S
 //   R <= 512: one column per lane (16 doubles per lane), G 1 or 4 (row
 //     segments of at least 16 lanes, 128 bytes), W up to 16, G = 1 when that
 //     still gives 512 workgroups;
-//   R > 512: two adjacent columns per lane (one 16-byte load per row) for an
-//     aligned base and an even width, else one; G = 16, W = 4.
+//   R > 512: two adjacent columns per lane (one 16-byte load per row for an
+//     aligned base and an even width, else two 8-byte loads; one column for
+//     a single column); G = 16, W = 4.
 // Measured (us, one column per lane against two): [100, 140000] 26.5 / 39.6,
 // [512, 4096] 8.0 / 10.9; [1000, 20000] 65.2 / 52.5, [1000, 1000] 13.0 / 6.9.
 void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool vec, double *var, double *mean,
                        hipStream_t st) {
   if (R > 512) {
-    if (vec) k_cols_one_d<2, 4, 16><<<dim3((unsigned)((C + 7) / 8)), dim3(256), 0, st>>>(x, R, C, ddof, var, mean);
-    else k_cols_one_d<1, 4, 16><<<dim3((unsigned)((C + 3) / 4)), dim3(256), 0, st>>>(x, R, C, ddof, var, mean);
+    const dim3 grid2((unsigned)((C + 7) / 8)), block(256);
+    if (vec) k_cols_one_d<2, 4, 16><<<grid2, block, 0, st>>>(x, R, C, ddof, var, mean);
+    else if (C >= 2) k_cols_one_d<2, 4, 16, false><<<grid2, block, 0, st>>>(x, R, C, ddof, var, mean);  // two 8-byte loads
+    else k_cols_one_d<1, 4, 16><<<dim3((unsigned)((C + 3) / 4)), block, 0, st>>>(x, R, C, ddof, var, mean);
     return;
   }
   int64_t cap = L64_E;
@@ -1237,6 +1292,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
 #undef SV_SEG64
     }
     else if (n <= 1024) SV_ROWS64(16, 1);
+    else if (n <= 2048) SV_ROWS64(16, 2);
     else if (n <= 4096) SV_ROWS64(16, 4);
     else if (n <= 8192) SV_ROWS64(16, 8);
     else if (n <= V64_ROWS_MAX_N) SV_ROWS64(16, 16);
@@ -1258,6 +1314,12 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
   } else if (n > 64) {
     launch_cols_one_d(x, rows, cols, ddof, svh::aligned16(x) && cols % 2 == 0, var_out, mean_out, st);
+  } else if (n < 16 && svh::aligned16(x) && cols % 2 == 0) {
+    const dim3 grid((unsigned)((cols / 2 + 255) / 256)), block(256);
+    if (n <= 2) k_cols_short_d<2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+    else if (n <= 4) k_cols_short_d<4><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+    else if (n <= 8) k_cols_short_d<8><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+    else k_cols_short_d<16><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
   } else {
     const dim3 grid((unsigned)((cols + 63) / 64));
 #define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)

@@ -90,7 +90,7 @@ def test_var64_page_datasets_and_square(torch_dev):
     check_var64(torch_dev, W.c4_matrix().astype(np.float64)[:1024], 1)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 64, 255, 256, 257, 1000, 1024, 1025, 4095, 4096, 4097, 8192, 8193, 16384,
+@pytest.mark.parametrize("n", [1, 2, 3, 64, 255, 256, 257, 1000, 1024, 1025, 1500, 2048, 4095, 4096, 4097, 8192, 8193, 16384,
                                16385, 40000])
 def test_var64_rows(torch_dev, n):
     rng = np.random.default_rng(n)
@@ -129,8 +129,23 @@ def test_var64_cols(torch_dev, R):
         check_var64(torch_dev, b, 0)
 
 
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 8, 9, 15, 16])
+def test_var64_short_cols(torch_dev, R):
+    # columns of at most 15 rows: two per lane, every tree in-lane (16 rows
+    # and odd widths: a lane per column)
+    rng = np.random.default_rng(R + 41)
+    for C in (2, 3, 1000, 100_000):
+        a = rng.normal(7e5, 3, (R, C))
+        check_var64(torch_dev, a, 0)
+        check_var64(torch_dev, a, 0, 1)
+        check_var64(torch_dev, a, 0, 4)
+    b = W.adversarial_values(R * 2048, R + 8).astype(np.float64).reshape(R, 2048) * 1e150
+    check_var64(torch_dev, b, 0)
+
+
 @pytest.mark.parametrize("R,C", [(100, 70_000), (400, 20_000), (65, 70_000), (1000, 18_000), (200, 20_000),
-                                 (200, 40_000), (129, 2048), (1024, 32), (65, 4), (300, 7), (777, 3001), (513, 1)])
+                                 (200, 40_000), (129, 2048), (1024, 32), (65, 4), (300, 7), (777, 3001), (513, 1),
+                                 (1000, 20_001), (600, 3)])
 def test_var64_cols_one_launch(torch_dev, R, C):
     # whole columns of 65..1024 rows in one launch: up to 512 rows one column
     # per lane in every (G, W) choice; above, two columns per lane (even
