@@ -1501,7 +1501,7 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
 
 // ------------------------------------------------------------------ host side
 
-constexpr int64_t C64_FUSED_MAX_N = 8192;  // complex rows reduced in one pass (k_var_rows_c64)
+constexpr int64_t C64_FUSED_MAX_N = 16384;  // complex rows reduced in one pass (k_var_rows_c64)
 
 // Launch-geometry tuning (never changes a result bit).
 struct Tuning {
@@ -2321,7 +2321,8 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     else if (cols <= 1024) SV_ROWS_C64(16, 1);
     else if (cols <= 2048) SV_ROWS_C64(16, 2);
     else if (cols <= 4096) SV_ROWS_C64(16, 4);
-    else SV_ROWS_C64(16, 8);
+    else if (cols <= 8192) SV_ROWS_C64(16, 8);
+    else SV_ROWS_C64(16, 16);
 #undef SV_ROWS_C64
     return check_launch("sv_variance_c64");
   }
