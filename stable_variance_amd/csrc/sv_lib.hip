@@ -679,12 +679,15 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
     ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
     ny = sv::wave_tree_p32<sv::NODE_TWOSUM>(ny);
   }
+  // The launch may hold fewer than W waves (the ones the row reaches); the
+  // tree's other wave nodes are (+0, +0).
+  const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
     Node t[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) t[i] = slots[0][i];
+    for (int i = 0; i < W; ++i) t[i] = i < nw ? slots[0][i] : sv::zero_node();
     ny = sv::node_tree<0, W, W>(t);
   }
   const float m = local_mean<V>(ny, n);
@@ -710,8 +713,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
     Node td[W], tq[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) {
-      td[i] = slots[1][i];
-      tq[i] = slots[2][i];
+      td[i] = i < nw ? slots[1][i] : sv::zero_node();
+      tq[i] = i < nw ? slots[2][i] : sv::zero_node();
     }
     nd = sv::node_tree<0, W, W>(td);
     nq = sv::node_tree<0, W, W, sv::NODE_NN>(tq);
@@ -1763,8 +1766,12 @@ void launch_sum_e(bool vec, const float *x, int64_t n, const SumPlan &p, Node *p
 template <int E, int W, bool VEC, int LOADP, bool NT>
 void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
                    hipStream_t st) {
-  // var_lds_pad: unused dynamic LDS per workgroup, a cap on resident waves
-  k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * W), (size_t)g_tune.var_lds_pad, st>>>(
+  // only the waves the row reaches (the tree pads the others with zero
+  // nodes); var_lds_pad: unused dynamic LDS per workgroup, a cap on resident
+  // waves
+  const int64_t reach = (n + 64 * E - 1) / (64 * E);
+  const int waves = reach < W ? (int)reach : W;
+  k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * waves), (size_t)g_tune.var_lds_pad, st>>>(
       x, n, ld, ddof, var, mean, g_tune.var_xcd);
 }
 
