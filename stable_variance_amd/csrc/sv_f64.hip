@@ -687,8 +687,10 @@ __device__ __forceinline__ void load_cols_tile_d(const double *__restrict__ x, i
       v[0][i] = g.x;
       v[1][i] = g.y;
     } else {
+      // columns past C (a partial last pair of an odd width) read the last
+      // column instead; their results are never written
 #pragma unroll
-      for (int k = 0; k < V; ++k) v[k][i] = p[k];
+      for (int k = 0; k < V; ++k) v[k][i] = x[r * C + (cc + k < C ? cc + k : C - 1)];
     }
   }
 }
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   double x0[V];
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
-  for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
+  for (int k = 0; k < V; ++k) x0[k] = x[cc + k < C ? cc + k : C - 1];
   shift_cols_tile_d<V, E>(v, x0, wave_full, valid);  // +0 past the last row
 #pragma unroll
   for (int k = 0; k < V; ++k) {

@@ -1073,8 +1073,10 @@ __device__ __forceinline__ void load_cols_tile(const float *__restrict__ x, int6
       v[2][i] = g.z;
       v[3][i] = g.w;
     } else {
+      // columns past C (a partial last group of an odd width) read the last
+      // column instead; their results are never written
 #pragma unroll
-      for (int k = 0; k < V; ++k) v[k][i] = p[k];
+      for (int k = 0; k < V; ++k) v[k][i] = x[r * C + (cc + k < C ? cc + k : C - 1)];
     }
   }
 }
@@ -1338,7 +1340,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   float x0[V];
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
-  for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
+  for (int k = 0; k < V; ++k) x0[k] = x[cc + k < C ? cc + k : C - 1];
   shift_cols_tile<V, E>(v, x0, wave_full, valid);  // +0 past the last row
 #pragma unroll
   for (int k = 0; k < V; ++k) {
