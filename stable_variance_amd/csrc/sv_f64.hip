@@ -1108,17 +1108,21 @@ void launch_cols_d(const double *x, int64_t R, int64_t C, int64_t ddof, const Sl
     else if (nch <= 8) k_cols_top_d<1, 1, 8><<<per_waves(8), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     else if (nch <= 16) k_cols_top_d<1, 1, 16><<<per_waves(4), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     else k_cols_top_d<1, 1, 32><<<per_waves(2), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-  } else if (nch <= 64 * 16) {
+  } else if (nch <= 64 * 64) {
     // many chunks: a wave per column for m and for the final trees
     const dim3 per_wave = per_waves(1);
     if (nch <= 64 * 4) {
       k_cols_top_d<0, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
       k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
       k_cols_top_d<1, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    } else {
+    } else if (nch <= 64 * 16) {
       k_cols_top_d<0, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
       k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
       k_cols_top_d<1, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    } else {
+      k_cols_top_d<0, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+      k_cols_top_d<1, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     }
   } else {
     k_cols_m_d<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);

@@ -1032,14 +1032,14 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 //   k_cols_y    the y-tree node of every (chunk, column)
 //   m           per column m = Tree(y)/n, the tree over its chunk nodes: for
 //               at most 32 chunks per column each k_cols_dq workgroup forms
-//               the m of its own columns (no launch); up to 1024 chunks a
+//               the m of its own columns (no launch); up to 4096 chunks a
 //               wave per column (k_cols_top); beyond, a thread per column
 //               (k_cols_m)
 //   k_cols_dq   the tile read again (mostly from the chip's last-level cache
 //               when the input fits in it): the d- and d^2-tree node of
 //               every (chunk, column)
 //   step 4      per column the trees over its d and d^2 chunk nodes: a group
-//               of lanes (up to 32 chunks) or a wave (up to 1024) per column
+//               of lanes (up to 32 chunks) or a wave (up to 4096) per column
 //               (k_cols_top), else a thread per column (k_cols_fin)
 
 constexpr int CC_E = 16;             // rows per lane in a chunk
@@ -1601,17 +1601,21 @@ void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, con
     else if (nch <= 8) k_cols_top<1, 1, 8><<<per_waves(8), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     else if (nch <= 16) k_cols_top<1, 1, 16><<<per_waves(4), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     else k_cols_top<1, 1, 32><<<per_waves(2), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-  } else if (nch <= 64 * 16) {
+  } else if (nch <= 64 * 64) {
     // many chunks: a wave per column for m and for the final trees
     const dim3 per_wave = per_waves(1);
     if (nch <= 64 * 4) {
       k_cols_top<0, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
       k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
       k_cols_top<1, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    } else {
+    } else if (nch <= 64 * 16) {
       k_cols_top<0, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
       k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
       k_cols_top<1, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    } else {
+      k_cols_top<0, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+      k_cols_top<1, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     }
   } else {
     k_cols_m<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);

@@ -176,6 +176,12 @@ def test_var64_cols_narrow(torch_dev, R, C):
         check_var64(torch_dev, b, 0)
 
 
+def test_var64_cols_many_chunks(torch_dev):
+    # 1563 chunks of 128 rows per column: a wave per column, 64 nodes per lane
+    a = np.random.default_rng(65).normal(4e4, 2, (200_000, 65))
+    check_var64(torch_dev, a, 0)
+
+
 @pytest.mark.parametrize("shape,axis", [((3, 300_001), 1), ((1, 1 << 20), 1), ((70_000, 6), 0), ((4096, 4096), 0)])
 def test_var64_long_slices(torch_dev, shape, axis):
     # chunked paths: long rows (8192-value chunks, per-row top trees) and

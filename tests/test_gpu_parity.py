@@ -489,6 +489,15 @@ def test_variance_short_cols_wide(torch_dev, R):
     check_var(torch_dev, b, 0, 0)
 
 
+@pytest.mark.parametrize("R,C", [(500_000, 129), (1_100_000, 7)])
+def test_variance_cols_many_chunks(torch_dev, R, C):
+    # 1025..4096 chunks per column: m and the final trees with 64 chunk nodes
+    # per lane of a wave per column
+    rng = np.random.default_rng(R + C)
+    a = rng.normal(-1e3, 3, (R, C)).astype(np.float32)
+    check_var(torch_dev, a, 0, 0)
+
+
 def test_variance_4096_square_axis0(torch_dev, col_geometry):
     a = W.c4_matrix()
     v = check_var(torch_dev, a, 0)
