@@ -564,7 +564,7 @@ constexpr int64_t L64_ROW_CHUNK = 64LL * L64_E * L64_W;  // 8192 doubles
 constexpr int L64_TOP_MAX_K = 32;               // chunk nodes per thread of a top tree
 constexpr int64_t L64_MAX_CHUNKS = 256LL * L64_TOP_MAX_K;
 constexpr int64_t C64_CHUNK = (int64_t)L64_E * L64_W;     // 128 rows
-constexpr int C64_GROUP = 32;                   // chunk nodes per group of a per-column tree
+constexpr int C64_GROUP = 32;                   // chunk nodes per column that k_cols_dq_d reduces for m itself
 
 struct SliceWsD {
   NodeD *ny;  // y-tree node of every chunk of every slice
@@ -703,36 +703,8 @@ __device__ __forceinline__ void shift_cols_tile_d(double (&v)[V][E], const doubl
     for (int i = 0; i < E; ++i) v[k][i] = (full || i < valid) ? v[k][i] - x0[k] : 0.0;
 }
 
-// Tree over p[0], p[stride], ... p[(count-1)*stride], zero-padded to a power
-// of two: aligned groups of C64_GROUP nodes level by level, each group node
-// written back in place of the group's first.  One thread per column.
-template <bool NN>
-__device__ NodeD chunk_tree_d(NodeD *p, int64_t stride, int64_t count) {
-  while (true) {
-    const int64_t groups = (count + C64_GROUP - 1) / C64_GROUP;
-    NodeD last = {0.0, 0.0};
-    for (int64_t g = 0; g < groups; ++g) {
-      NodeD sub[C64_GROUP / 8];
-#pragma unroll
-      for (int b = 0; b < C64_GROUP / 8; ++b) {
-        NodeD nd[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int64_t idx = g * C64_GROUP + b * 8 + k;
-          const NodeD t = p[(idx < count ? idx : count - 1) * stride];
-          nd[k] = idx < count ? t : NodeD{0.0, 0.0};
-        }
-        sub[b] = node_tree_d<0, 8, 8, NN>(nd);
-      }
-      last = node_tree_d<0, C64_GROUP / 8, C64_GROUP / 8, NN>(sub);
-      if (groups > 1) p[g * stride] = last;
-    }
-    if (groups == 1) return last;
-    count = groups;
-  }
-}
-
-// The same over nch <= C64_GROUP nodes, nothing written back.
+// Tree over the nch <= C64_GROUP chunk nodes p[0], p[stride], ..., padded
+// with zero nodes to C64_GROUP (the padding changes no bit).
 __device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, int64_t nch) {
   NodeD sub[C64_GROUP / 8];
 #pragma unroll
@@ -798,12 +770,6 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restric
   }
 }
 
-__global__ __launch_bounds__(256) void k_cols_m_d(int64_t R, int64_t C, int64_t nch, SliceWsD ws) {
-  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (col >= C) return;
-  ws.m[col] = root_value_d(chunk_tree_d<false>(ws.ny + col, C, nch)) / (double)R;
-}
-
 // The per-column trees over the chunk nodes with S lanes per column (64/S
 // columns per wave, four waves per workgroup): lane l of a column's group
 // takes nodes [l*K, (l+1)*K) (zero nodes past nch), the in-lane levels and
@@ -843,8 +809,67 @@ __global__ __launch_bounds__(256) void k_cols_top_d(const double *__restrict__ x
   }
 }
 
+// The per-column trees over more than 4096 chunk nodes, a wave per column:
+// lane l reduces the run of 64*P nodes [l*64*P, (l+1)*64*P) (P = 2^log2p,
+// zero nodes past nch) in batches of 64, merging the batch nodes in tree
+// order with a binary counter (wave-uniform loop, constant stack indices),
+// then the wave's six levels.  PASS 0: m; PASS 1: step 4.
+constexpr int TOP_BIG_LEVELS_D = 16;  // P up to 2^15
+template <int PASS>
+__global__ __launch_bounds__(256) void k_cols_top_big_d(const double *__restrict__ x, int64_t R, int64_t C,
+                                                        int64_t nch, int log2p, int64_t ddof, SliceWsD ws,
+                                                        double *__restrict__ var_out, double *__restrict__ mean_out) {
+  constexpr int K = 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (col >= C) return;  // the whole wave
+  const int64_t P = (int64_t)1 << log2p;
+  auto tree = [&](const NodeD *p, auto nn) {
+    constexpr bool NN = decltype(nn)::value;
+    NodeD st[TOP_BIG_LEVELS_D];
+#pragma unroll
+    for (int lv = 0; lv < TOP_BIG_LEVELS_D; ++lv) st[lv] = NodeD{0.0, 0.0};
+    for (int64_t b = 0; b < P; ++b) {
+      NodeD nd[K];
+      const int64_t i0 = ((int64_t)lane * P + b) * K;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t idx = i0 + k;
+        const NodeD t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+        nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
+      }
+      NodeD carry = node_tree_d<0, K, K, NN>(nd);
+      bool placed = false;
+#pragma unroll
+      for (int lv = 0; lv < TOP_BIG_LEVELS_D; ++lv) {
+        if (!placed) {
+          if ((b >> lv) & 1) {
+            carry = comb_d<NN>(st[lv], carry);
+          } else {
+            st[lv] = carry;
+            placed = true;
+          }
+        }
+      }
+    }
+    NodeD r = {0.0, 0.0};
+#pragma unroll
+    for (int lv = 0; lv < TOP_BIG_LEVELS_D; ++lv)
+      if (lv == log2p) r = st[lv];
+    return wave_tree_d<NN>(r);
+  };
+  if constexpr (PASS == 0) {
+    const NodeD ny = tree(ws.ny + col, std::false_type{});
+    if (lane == 0) ws.m[col] = root_value_d(ny) / (double)R;
+  } else {
+    const NodeD nd = tree(ws.nd + col, std::false_type{});
+    const NodeD nq = tree(ws.nq + col, std::true_type{});
+    if (lane == 0) finalize_d(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+  }
+}
+
 // MLOCAL: nch <= C64_GROUP, and every workgroup forms m for its own columns
-// (no k_cols_m_d launch); else m comes from k_cols_m_d or k_cols_top_d.
+// (no separate launch); else m comes from k_cols_top_d or k_cols_top_big_d.
 // Tile layout as in k_cols_y_d.
 template <int V, int G, bool MLOCAL>
 __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restrict__ x, int64_t R, int64_t C,
@@ -901,7 +926,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
   if (t < NC) {
     const int k = t / Q, qq = t % Q;  // thread t combines column V*qq + k of the block
     const int64_t col = cb * NC + (int64_t)qq * V + k;
-    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][qq];  // for k_cols_fin_d
+    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][qq];  // for step 4
     if (col < C) {
       NodeD a[W], b[W];
 #pragma unroll
@@ -1032,16 +1057,6 @@ __global__ __launch_bounds__(256) void k_cols_short_d(const double *__restrict__
   if (mean_out) store2(mean_out, mean2);
 }
 
-__global__ __launch_bounds__(256) void k_cols_fin_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t nch,
-                                                    int64_t ddof, SliceWsD ws, double *__restrict__ var_out,
-                                                    double *__restrict__ mean_out) {
-  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (col >= C) return;
-  const NodeD nd = chunk_tree_d<false>(ws.nd + col, C, nch);
-  const NodeD nq = chunk_tree_d<true>(ws.nq + col, C, nch);
-  finalize_d(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
-}
-
 __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) {
@@ -1098,7 +1113,7 @@ void launch_cols_d(const double *x, int64_t R, int64_t C, int64_t ddof, const Sl
   constexpr int NC = V * (64 / G);       // columns per block
   const int64_t nch = (R + CH - 1) / CH;
   const int64_t ncb = (C + NC - 1) / NC;
-  const dim3 grid((unsigned)(ncb * nch)), block(64 * L64_W), per_col((unsigned)((C + 255) / 256));
+  const dim3 grid((unsigned)(ncb * nch)), block(64 * L64_W);
   k_cols_y_d<V, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
   auto per_waves = [&](int per_wave) { return dim3((unsigned)((C + 4 * per_wave - 1) / (4 * per_wave))); };
   if (nch <= C64_GROUP) {
@@ -1125,9 +1140,12 @@ void launch_cols_d(const double *x, int64_t R, int64_t C, int64_t ddof, const Sl
       k_cols_top_d<1, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     }
   } else {
-    k_cols_m_d<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
+    int log2p = 0;  // runs of 64 * 2^log2p chunk nodes per lane
+    while (((int64_t)64 * 64 << log2p) < nch) ++log2p;
+    const dim3 per_wave = per_waves(1);
+    k_cols_top_big_d<0><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
     k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-    k_cols_fin_d<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    k_cols_top_big_d<1><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
   }
 }
 

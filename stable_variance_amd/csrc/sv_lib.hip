@@ -1032,19 +1032,18 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 //   k_cols_y    the y-tree node of every (chunk, column)
 //   m           per column m = Tree(y)/n, the tree over its chunk nodes: for
 //               at most 32 chunks per column each k_cols_dq workgroup forms
-//               the m of its own columns (no launch); up to 4096 chunks a
-//               wave per column (k_cols_top); beyond, a thread per column
-//               (k_cols_m)
+//               the m of its own columns (no launch); else a wave per column
+//               (k_cols_top up to 4096 chunks, k_cols_top_big beyond)
 //   k_cols_dq   the tile read again (mostly from the chip's last-level cache
 //               when the input fits in it): the d- and d^2-tree node of
 //               every (chunk, column)
 //   step 4      per column the trees over its d and d^2 chunk nodes: a group
-//               of lanes (up to 32 chunks) or a wave (up to 4096) per column
-//               (k_cols_top), else a thread per column (k_cols_fin)
+//               of lanes (up to 32 chunks) or a wave per column (k_cols_top,
+//               k_cols_top_big)
 
 constexpr int CC_E = 16;             // rows per lane in a chunk
 constexpr int CC_MIN_W = 4;          // the workspace is sized for the shortest chunk
-constexpr int CC_GROUP = 32;         // chunk nodes per group of the per-column trees
+constexpr int CC_GROUP = 32;         // chunk nodes per column that k_cols_dq reduces for m itself
 
 struct ColsWs {
   Node *ny;  // [nch][C] y-tree node of each chunk of each column
@@ -1088,38 +1087,6 @@ __device__ __forceinline__ void shift_cols_tile(float (&v)[V][E], const float (&
   for (int k = 0; k < V; ++k)
 #pragma unroll
     for (int i = 0; i < E; ++i) v[k][i] = (full || i < valid) ? v[k][i] - x0[k] : 0.0f;
-}
-
-// Tree over p[0], p[stride], ..., p[(count-1)*stride] padded with zero nodes
-// to a power of two: aligned groups of CC_GROUP nodes level by level, each
-// group node written back in place of the group's first node.  One thread
-// per column.
-template <int KIND>
-__device__ Node chunk_tree(Node *p, int64_t stride, int64_t count) {
-  while (true) {
-    const int64_t groups = (count + CC_GROUP - 1) / CC_GROUP;
-    Node last = sv::zero_node();
-    for (int64_t g = 0; g < groups; ++g) {
-      Node sub[CC_GROUP / 8];
-#pragma unroll
-      for (int b = 0; b < CC_GROUP / 8; ++b) {
-        Node nd[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // every load is issued (an index past the end reads the last node),
-          // so the group's loads are in flight together
-          const int64_t idx = g * CC_GROUP + b * 8 + k;
-          const Node t = p[(idx < count ? idx : count - 1) * stride];
-          nd[k] = idx < count ? t : sv::zero_node();
-        }
-        sub[b] = sv::node_tree<0, 8, 8, KIND>(nd);
-      }
-      last = sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8, KIND>(sub);
-      if (groups > 1) p[g * stride] = last;
-    }
-    if (groups == 1) return last;
-    count = groups;
-  }
 }
 
 // G row groups per wave: lane L = q*G + g holds the V adjacent columns of
@@ -1170,13 +1137,6 @@ __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, 
       ws.ny[j * C + col] = sv::node_tree<0, W, W>(nn);
     }
   }
-}
-
-__global__ __launch_bounds__(256) void k_cols_m(int64_t R, int64_t C, int64_t nch, ColsWs ws) {
-  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (col >= C) return;
-  const Node ny = chunk_tree<sv::NODE_TWOSUM>(ws.ny + col, C, nch);
-  ws.m[col] = sv::root_value(ny) / (float)R;
 }
 
 // Tree over the nch <= CC_GROUP chunk nodes p[0], p[stride], ... (one group,
@@ -1236,8 +1196,69 @@ __global__ __launch_bounds__(256) void k_cols_top(const float *__restrict__ x, i
   }
 }
 
+// The per-column trees over more than 4096 chunk nodes, a wave per column:
+// lane l reduces the run of 64*P nodes [l*64*P, (l+1)*64*P) (P = 2^log2p,
+// zero nodes past nch) in batches of 64, merging the batch nodes in tree
+// order with a binary counter (the loop is wave-uniform, so every stack
+// index is a constant), then the wave's six levels.  PASS 0: m; PASS 1:
+// step 4.
+constexpr int TOP_BIG_LEVELS = 16;  // P up to 2^15: 2^27 chunks per column
+template <int PASS>
+__global__ __launch_bounds__(256) void k_cols_top_big(const float *__restrict__ x, int64_t R, int64_t C,
+                                                      int64_t nch, int log2p, int64_t ddof, ColsWs ws,
+                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
+  constexpr int K = 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t col = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (col >= C) return;  // the whole wave
+  const int64_t P = (int64_t)1 << log2p;
+  auto tree = [&](const Node *p, auto kind) {
+    constexpr int KIND = decltype(kind)::value;
+    Node st[TOP_BIG_LEVELS];
+#pragma unroll
+    for (int lv = 0; lv < TOP_BIG_LEVELS; ++lv) st[lv] = sv::zero_node();
+    for (int64_t b = 0; b < P; ++b) {
+      Node nd[K];
+      const int64_t i0 = ((int64_t)lane * P + b) * K;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t idx = i0 + k;
+        const Node t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+        nd[k] = idx < nch ? t : sv::zero_node();
+      }
+      Node carry = sv::node_tree<0, K, K, KIND>(nd);
+      bool placed = false;
+#pragma unroll
+      for (int lv = 0; lv < TOP_BIG_LEVELS; ++lv) {
+        if (!placed) {
+          if ((b >> lv) & 1) {
+            carry = sv::combine_k<KIND>(st[lv], carry);
+          } else {
+            st[lv] = carry;
+            placed = true;
+          }
+        }
+      }
+    }
+    Node r = sv::zero_node();
+#pragma unroll
+    for (int lv = 0; lv < TOP_BIG_LEVELS; ++lv)
+      if (lv == log2p) r = st[lv];
+    return sv::wave_tree<KIND>(r);
+  };
+  if constexpr (PASS == 0) {
+    const Node ny = tree(ws.ny + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
+    if (lane == 0) ws.m[col] = sv::root_value(ny) / (float)R;
+  } else {
+    const Node nd = tree(ws.nd + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
+    const Node nq = tree(ws.nq + col, std::integral_constant<int, sv::NODE_NN>{});
+    if (lane == 0) finalize(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
+  }
+}
+
 // MLOCAL: nch <= CC_GROUP, and every workgroup forms m for its own columns
-// from their y chunk nodes (no k_cols_m launch); else m comes from k_cols_m.
+// from their y chunk nodes (no separate launch); else m comes from
+// k_cols_top or k_cols_top_big.
 // Tile layout as in k_cols_y.
 template <int V, int W, int G, bool MLOCAL>
 __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
@@ -1298,7 +1319,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
   if (t < NC) {
     const int k = t / Q, qq = t % Q;  // thread t combines column V*qq + k of the block
     const int64_t col = cb * NC + (int64_t)qq * V + k;
-    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][qq];  // for k_cols_fin
+    if (MLOCAL && j == 0 && col < C) ws.m[col] = sm[k][qq];  // for step 4
     if (col < C) {
       Node a[W], b[W];
 #pragma unroll
@@ -1384,16 +1405,6 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
                var_out + col, mean_out ? mean_out + col : nullptr);
     }
   }
-}
-
-__global__ __launch_bounds__(256) void k_cols_fin(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
-                                                  int64_t ddof, ColsWs ws, float *__restrict__ var_out,
-                                                  float *__restrict__ mean_out) {
-  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (col >= C) return;
-  const Node nd = chunk_tree<sv::NODE_TWOSUM>(ws.nd + col, C, nch);
-  const Node nq = chunk_tree<sv::NODE_NN>(ws.nq + col, C, nch);
-  finalize(nd, nq, x[col], ws.m[col], R, ddof, var_out + col, mean_out ? mean_out + col : nullptr);
 }
 
 // ------------------------------------------------------------------ long slices
@@ -1591,7 +1602,6 @@ void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, con
   const int64_t nch = (R + CH - 1) / CH;
   const int64_t ncb = (C + NC - 1) / NC;
   const dim3 grid((unsigned)(ncb * nch)), block(64 * W);
-  const dim3 per_col((unsigned)((C + 255) / 256));
   k_cols_y<V, W, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
   auto per_waves = [&](int per_wave) { return dim3((unsigned)((C + 4 * per_wave - 1) / (4 * per_wave))); };
   if (nch <= CC_GROUP) {
@@ -1618,9 +1628,12 @@ void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, con
       k_cols_top<1, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
     }
   } else {
-    k_cols_m<<<per_col, dim3(256), 0, st>>>(R, C, nch, ws);
+    int log2p = 0;  // runs of 64 * 2^log2p chunk nodes per lane
+    while (((int64_t)64 * 64 << log2p) < nch) ++log2p;
+    const dim3 per_wave = per_waves(1);
+    k_cols_top_big<0><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
     k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-    k_cols_fin<<<per_col, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    k_cols_top_big<1><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
   }
 }
 

@@ -176,9 +176,11 @@ def test_var64_cols_narrow(torch_dev, R, C):
         check_var64(torch_dev, b, 0)
 
 
-def test_var64_cols_many_chunks(torch_dev):
-    # 1563 chunks of 128 rows per column: a wave per column, 64 nodes per lane
-    a = np.random.default_rng(65).normal(4e4, 2, (200_000, 65))
+@pytest.mark.parametrize("R", [200_000, 600_000])
+def test_var64_cols_many_chunks(torch_dev, R):
+    # 1563 chunks of 128 rows per column: a wave per column, 64 nodes per
+    # lane; 4688 chunks: runs of 128 nodes per lane merged by a binary counter
+    a = np.random.default_rng(R).normal(4e4, 2, (R, 65))
     check_var64(torch_dev, a, 0)
 
 

@@ -489,13 +489,21 @@ def test_variance_short_cols_wide(torch_dev, R):
     check_var(torch_dev, b, 0, 0)
 
 
-@pytest.mark.parametrize("R,C", [(500_000, 129), (1_100_000, 7)])
-def test_variance_cols_many_chunks(torch_dev, R, C):
-    # 1025..4096 chunks per column: m and the final trees with 64 chunk nodes
-    # per lane of a wave per column
+@pytest.mark.parametrize("R,C,waves", [(500_000, 129, 16), (1_100_000, 7, 16), (1_050_000, 65, 16),
+                                       (600_000, 65, 4)])
+def test_variance_cols_many_chunks(torch_dev, R, C, waves):
+    # 1025..4096 chunks per column: 64 chunk nodes per lane of a wave per
+    # column; beyond (4102 chunks, and 9375 chunks of 64 rows at four
+    # waves): runs of 64*P nodes per lane merged by a binary counter
+    import stable_variance_amd as sv
+
     rng = np.random.default_rng(R + C)
     a = rng.normal(-1e3, 3, (R, C)).astype(np.float32)
-    check_var(torch_dev, a, 0, 0)
+    sv.set_tuning("var_cols_waves", waves)
+    try:
+        check_var(torch_dev, a, 0, 0)
+    finally:
+        sv.set_tuning("reset", 0)
 
 
 def test_variance_4096_square_axis0(torch_dev, col_geometry):
