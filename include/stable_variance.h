@@ -120,7 +120,10 @@ sv_status sv_tree_sum_dw_f32(const float *x, int64_t n, float *out, void *worksp
  * Bytes of workspace sv_variance_f32 needs.
  *   axis 1: 0 when every row fits one workgroup (n <= 16384 values), else 24
  *           bytes per 16384-value chunk of every row plus 4 bytes per row
- *           (long rows are reduced in chunks, reading the input twice).
+ *           (long rows are reduced in chunks, reading the input twice; with
+ *           256 or more rows of up to 65536 values each row takes one
+ *           workgroup instead and the workspace is not used, but the size
+ *           stays the chunked path's, independent of the tuning knobs).
  *   axis 0: whenever rows and cols are both nonzero: three arrays of 8
  *           bytes per 64-row chunk per column and 4 bytes per column, each
  *           rounded up to 256 bytes.  Columns longer than one workgroup holds
