@@ -117,3 +117,51 @@ def test_random_shape(torch_dev, case):
         m, want_m = m.view(np.float32), np.ascontiguousarray(want_m).view(np.float32)
     assert _same(v, want_v, check_dt), (CASES[case], np.flatnonzero(~np.isclose(v, want_v, equal_nan=True))[:5])
     assert _same(m, want_m, check_dt), CASES[case]
+
+
+# ------------------------------------------------------------------ sums
+
+def _draw_sum_cases():
+    rng = np.random.default_rng(31337)
+    cases = []
+    for _ in range(24):
+        n = int(np.exp(rng.uniform(0.0, np.log(6_000_000))))
+        kind = ("f32", "f32", "dw", "f64", "adn")[int(rng.integers(5))]
+        offset = int(rng.integers(4))
+        fold = int(rng.integers(2, 9))
+        seed = int(rng.integers(1 << 30))
+        cases.append((kind, n, offset, fold, seed))
+    return cases
+
+
+SUM_CASES = _draw_sum_cases()
+
+
+@pytest.mark.parametrize("case", range(len(SUM_CASES)),
+                         ids=[f"{k}-n{n}-off{o}" + (f"-K{f}" if k == "adn" else "") for k, n, o, f, _ in SUM_CASES])
+def test_random_sum(torch_dev, case):
+    # tree sums (plain and double-word carries, float32 and float64) and the
+    # ADN sum over random lengths, from bases 0..3 elements into a buffer
+    import stable_variance_amd as sv
+    from oracle import adn
+
+    torch, dev = torch_dev
+    kind, n, offset, fold, seed = SUM_CASES[case]
+    rng = np.random.default_rng(seed)
+    if rng.random() < 0.5:
+        x = W.sum_cancelling_pairs(n, 0.01, seed=seed)
+    else:
+        x = W.adversarial_values(n, seed) if rng.random() < 0.5 else rng.normal(0, 1, n).astype(np.float32)
+    if kind == "f64":
+        x = x.astype(np.float64) * 1e100
+    t = _device_view(torch, dev, x, offset)
+    if kind == "f32":
+        got, want, dt = sv.tree_sum(t), oracle.tree_sum(x), np.float32
+    elif kind == "dw":
+        got, want, dt = sv.tree_sum(t, carry="dw"), oracle.tree_sum_dw(x), np.float32
+    elif kind == "f64":
+        got, want, dt = sv.tree_sum(t), oracle.tree_sum_f64(x), np.float64
+    else:
+        got, want, dt = sv.adn_sum(t, fold=fold), adn.adn_sum(x, fold), np.float32
+    torch.cuda.synchronize()
+    assert _same(np.asarray(got.item(), dt), np.asarray(want, dt), dt), (SUM_CASES[case], got.item(), want)
