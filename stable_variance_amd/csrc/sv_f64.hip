@@ -1249,7 +1249,9 @@ size_t sv_variance_f64_workspace_size(int64_t rows, int64_t cols, int axis) {
   if (rows < 0 || cols < 0) return (size_t)-1;
   if (axis != 0 && axis != 1 && axis != -1 && axis != -2) return (size_t)-1;
   if (cols > 0 && rows > V64_MAX_ELEMS / cols) return (size_t)-1;
-  return var64_ws(rows, cols, axis == 1 || axis == -1);
+  const bool ax1 = (axis == 1 || axis == -1);
+  if (!ax1 && (rows + C64_CHUNK - 1) / C64_CHUNK > ((int64_t)64 * 64 << (TOP_BIG_LEVELS_D - 1))) return (size_t)-1;
+  return var64_ws(rows, cols, ax1);
 }
 
 sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, double *var_out,
@@ -1271,6 +1273,10 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
   if (reinterpret_cast<uintptr_t>(x) & 7u) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is not 8-byte aligned");
   if (nslices > 0x7fffffffLL)
     return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: %lld slices exceed the grid", (long long)nslices);
+  // axis 0: the per-column trees hold up to 64 * 64 * 2^(TOP_BIG_LEVELS_D - 1)
+  // chunk nodes; chunks are at least 128 rows
+  if (!ax1 && (n + C64_CHUNK - 1) / C64_CHUNK > ((int64_t)64 * 64 << (TOP_BIG_LEVELS_D - 1)))
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: columns of %lld rows exceed the chunk trees", (long long)n);
   const size_t need = var64_ws(rows, cols, ax1);
   if (need == (size_t)-1)
     return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: rows of %lld values exceed %lld chunks", (long long)n,

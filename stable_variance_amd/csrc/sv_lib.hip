@@ -2110,6 +2110,7 @@ size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis) {
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t n = ax1 ? cols : rows;
   const int64_t nslices = ax1 ? rows : cols;
+  if (!ax1 && (n + 63) / 64 > ((int64_t)64 * 64 << (TOP_BIG_LEVELS - 1))) return (size_t)-1;
   if (!ax1) return (n == 0 || nslices == 0) ? 0 : cols_layout(n, nslices).total;
   if (n <= ROWS_MAX_N) return 0;
   const int64_t nch = (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK;
@@ -2140,6 +2141,10 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
   if (is_long && nch > LS_MAX_CHUNKS)
     return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: slices of length %lld exceed %d chunks", (long long)n,
                 LS_MAX_CHUNKS);
+  // axis 0: the per-column trees hold up to 64 * 64 * 2^(TOP_BIG_LEVELS - 1)
+  // chunk nodes; chunks are at least 64 rows
+  if (!ax1 && (n + 63) / 64 > ((int64_t)64 * 64 << (TOP_BIG_LEVELS - 1)))
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: columns of %lld rows exceed the chunk trees", (long long)n);
   if (is_long || (!ax1 && n > 0)) {
     const size_t need = is_long ? long_ws_bytes(nslices, nch) : cols_layout(n, nslices).total;
     if (!workspace) return fail(SV_ERR_WORKSPACE, "sv_variance_f32: workspace is NULL (%zu bytes needed)", need);

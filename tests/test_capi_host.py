@@ -109,6 +109,10 @@ def test_variance_argument_errors(L):
     assert L.sv_variance_f32(BAD, 2, 20000, 1, 0, out, None, ctypes.c_void_p(0x100040), 4096, None) == \
         SV_ERR_WORKSPACE
     assert L.sv_variance_f32(BAD, 1, 8192 * 16384 + 1, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
+    # axis-0 columns beyond the per-column chunk trees (2^27 chunks of >= 64 rows)
+    assert L.sv_variance_f32_workspace_size(1 << 34, 2, 0) == ctypes.c_size_t(-1).value
+    assert L.sv_variance_f32_workspace_size(1 << 33, 2, 0) != ctypes.c_size_t(-1).value
+    assert L.sv_variance_f32(BAD, 1 << 34, 2, 0, 0, out, None, BAD, 1 << 40, None) == SV_ERR_UNSUPPORTED
 
 
 def test_adn_sizes_and_argument_errors(L):
@@ -172,6 +176,9 @@ def test_f64_sizes_and_argument_errors(L):
     assert L.sv_variance_f64(BAD, 2000, 3, 0, 0, out, None, ctypes.c_void_p(0x100040), 1 << 20, None) == \
         SV_ERR_WORKSPACE
     assert L.sv_variance_f64(BAD, 1, 8192 * 8192 + 1, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
+    # axis-0 columns beyond the per-column chunk trees (2^27 chunks of >= 128 rows)
+    assert ws(1 << 35, 2, 0) == ctypes.c_size_t(-1).value
+    assert L.sv_variance_f64(BAD, 1 << 35, 2, 0, 0, out, None, BAD, 1 << 40, None) == SV_ERR_UNSUPPORTED
 
 
 def test_complex_argument_errors_and_sizes(L):
