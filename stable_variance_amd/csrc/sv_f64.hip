@@ -1299,9 +1299,15 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     const bool vec = svh::aligned16(x) && (cols % 2 == 0);
     const dim3 grid((unsigned)rows);
 #define SV_ROWS64(E, W)                                                                                      \
-  do {                                                                                                       \
-    if (vec) k_var_rows_f64<E, W, true><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var_out, mean_out); \
-    else k_var_rows_f64<E, W, false><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var_out, mean_out);    \
+  do { /* rows in batches: a launch holds at most 2^32 - 1 work-items */                                   \
+    const int64_t batch = (int64_t)0xffffffffu / (64 * W);                                                   \
+    for (int64_t r0 = 0; r0 < rows; r0 += batch) {                                                           \
+      const int64_t nr = rows - r0 < batch ? rows - r0 : batch;                                              \
+      const double *xr = x + r0 * cols;                                                                      \
+      double *mr = mean_out ? mean_out + r0 : nullptr;                                                       \
+      if (vec) k_var_rows_f64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr); \
+      else k_var_rows_f64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr);   \
+    }                                                                                                        \
   } while (0)
     if (n <= 512) {
       const int vw = (svh::aligned16(x) && cols % 2 == 0) ? 2 : 1;

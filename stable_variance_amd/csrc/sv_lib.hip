@@ -1790,8 +1790,13 @@ void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t 
   // waves
   const int64_t reach = (n + 64 * E - 1) / (64 * E);
   const int waves = reach < W ? (int)reach : W;
-  k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)rows), dim3(64 * waves), (size_t)g_tune.var_lds_pad, st>>>(
-      x, n, ld, ddof, var, mean, g_tune.var_xcd);
+  // a launch holds at most 2^32 - 1 work-items: rows in batches
+  const int64_t batch = (int64_t)0xffffffffu / (64 * waves);
+  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+    k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)nr), dim3(64 * waves), (size_t)g_tune.var_lds_pad, st>>>(
+        x + r0 * ld, n, ld, ddof, var + r0, mean ? mean + r0 : nullptr, g_tune.var_xcd);
+  }
 }
 
 // A row shared by W waves of E values per lane; 16-byte loads follow
@@ -2327,9 +2332,15 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     const bool vec = aligned16(z) && (cols % 2 == 0);
     const dim3 grid((unsigned)rows);
 #define SV_ROWS_C64(E, W)                                                                                 \
-  do {                                                                                                    \
-    if (vec) k_var_rows_c64<E, W, true><<<grid, dim3(64 * W), 0, st>>>(z, cols, ddof, var_out, mean_out);  \
-    else k_var_rows_c64<E, W, false><<<grid, dim3(64 * W), 0, st>>>(z, cols, ddof, var_out, mean_out);     \
+  do { /* rows in batches: a launch holds at most 2^32 - 1 work-items */                              \
+    const int64_t batch = (int64_t)0xffffffffu / (64 * W);                                              \
+    for (int64_t r0 = 0; r0 < rows; r0 += batch) {                                                      \
+      const int64_t nr = rows - r0 < batch ? rows - r0 : batch;                                         \
+      const float *zr = z + 2 * r0 * cols;                                                              \
+      float *mr = mean_out ? mean_out + 2 * r0 : nullptr;                                               \
+      if (vec) k_var_rows_c64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr); \
+      else k_var_rows_c64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr);   \
+    }                                                                                                   \
   } while (0)
     if (cols <= SEG_MAX_N && g_tune.var_short_rows) {
       const int vw2 = vec ? 2 : 1;
