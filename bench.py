@@ -145,8 +145,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
-              f"(the method has no multi-GPU step here).", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported; the benchmark runs on one GPU "
+              f"(the method has no cross-GPU step).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()

@@ -59,7 +59,7 @@ typedef int sv_status;
 #define SV_ERR_WORKSPACE 2        /* workspace missing, too small or misaligned  */
 #define SV_ERR_NO_DEVICE 3        /* no usable HIP device                        */
 #define SV_ERR_HIP 4              /* a HIP runtime call or a launch failed       */
-#define SV_ERR_UNSUPPORTED 5      /* shape outside what this build supports      */
+#define SV_ERR_UNSUPPORTED 5      /* shape outside what the library supports     */
 
 /* Version of this ABI (SV_ABI_VERSION of the header the library was built with). */
 int sv_abi_version(void);
