@@ -177,7 +177,7 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
  *              (mean(re), mean(im))
  *   workspace  sv_variance_c64_workspace_size(rows, cols, axis) bytes,
  *              256-byte aligned, no initialisation; NULL allowed when that
- *              size is 0.  Axis 1 rows of up to 16384 values are read once
+ *              size is 0.  Axis 1 rows of up to 32768 values are read once
  *              and need none; longer rows stage the split parts (8 bytes per
  *              input value); axis 0 reads the interleaved array as float32
  *              [rows, 2 * cols] columns

@@ -463,20 +463,19 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
     yr = sv::wave_tree<sv::NODE_TWOSUM>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(re));
     yi = sv::wave_tree<sv::NODE_TWOSUM>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(im));
   }
+  // The tree over the waves' nodes: lane l < W takes wave l's real node,
+  // lane W + l its imaginary node, and the first log2(W) cross-lane levels
+  // pair them in tree order (one node per lane instead of all W in every
+  // lane's registers).
   if constexpr (W > 1) {
     if (lane == 0) {
       slots[0][w] = yr;
       slots[1][w] = yi;
     }
     __syncthreads();
-    Node a[W], b[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      a[i] = slots[0][i];
-      b[i] = slots[1][i];
-    }
-    yr = sv::node_tree<0, W, W>(a);
-    yi = sv::node_tree<0, W, W>(b);
+    const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 2 * W ? (&slots[0][0])[lane] : sv::zero_node());
+    yr = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
+    yi = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
   }
   const float mr = sv::root_value(yr) / (float)n;
   const float mi = sv::root_value(yi) / (float)n;
@@ -494,7 +493,12 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
     di = sv::wave_tree<sv::NODE_TWOSUM>(di);
     qi = sv::wave_tree<sv::NODE_NN>(qi);
   }
+  // Wave 0 alone: lanes [k*W, (k+1)*W) take the waves' nodes of tree k (d
+  // and d^2 of the real part, then of the imaginary part).  The d^2 trees
+  // take the TwoSum node here: on non-negative operands its error is the
+  // same exact value as the Fast2Sum form's.
   if constexpr (W > 1) {
+    static_assert(4 * W <= 64, "four trees of W nodes in one wave");
     if (lane == 0) {
       slots[2][w] = dr;
       slots[3][w] = qr;
@@ -502,16 +506,12 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
       slots[5][w] = qi;
     }
     __syncthreads();
-    if (threadIdx.x != 0) return;
-    Node t[4][W];
-#pragma unroll
-    for (int i = 0; i < W; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t[k][i] = slots[2 + k][i];
-    dr = sv::node_tree<0, W, W>(t[0]);
-    qr = sv::node_tree<0, W, W, sv::NODE_NN>(t[1]);
-    di = sv::node_tree<0, W, W>(t[2]);
-    qi = sv::node_tree<0, W, W, sv::NODE_NN>(t[3]);
+    if (w != 0) return;
+    const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 4 * W ? (&slots[2][0])[lane] : sv::zero_node());
+    dr = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
+    qr = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
+    di = {sv::readlane_f(t.s, 2 * W), sv::readlane_f(t.c, 2 * W)};
+    qi = {sv::readlane_f(t.s, 3 * W), sv::readlane_f(t.c, 3 * W)};
   }
   if (threadIdx.x == 0) {
     float vr, vi, mean_r, mean_i;
@@ -1517,7 +1517,7 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
 
 // ------------------------------------------------------------------ host side
 
-constexpr int64_t C64_FUSED_MAX_N = 16384;  // complex rows reduced in one pass (k_var_rows_c64)
+constexpr int64_t C64_FUSED_MAX_N = 32768;  // complex rows reduced in one pass (k_var_rows_c64)
 
 // Launch-geometry tuning (never changes a result bit).
 struct Tuning {
@@ -2364,7 +2364,8 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     else if (cols <= 2048) SV_ROWS_C64(16, 2);
     else if (cols <= 4096) SV_ROWS_C64(16, 4);
     else if (cols <= 8192) SV_ROWS_C64(16, 8);
-    else SV_ROWS_C64(16, 16);
+    else if (cols <= 16384) SV_ROWS_C64(16, 16);
+    else SV_ROWS_C64(32, 16);
 #undef SV_ROWS_C64
     return check_launch("sv_variance_c64");
   }

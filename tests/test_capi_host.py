@@ -186,20 +186,21 @@ def test_complex_argument_errors_and_sizes(L):
     # axis 0: per-component variances (2*cols floats) + the float view's own
     # workspace ([1000, 128] along axis 0)
     assert L.sv_variance_c64_workspace_size(1000, 64, 0) == 512 + L.sv_variance_f32_workspace_size(1000, 128, 0)
-    # axis 1: none up to 8192 values per row (one pass); above, the
+    # axis 1: none up to 32768 values per row (one pass); above, the
     # per-component variances + the split rows (8 bytes per value) + the
     # float view's own workspace
     assert L.sv_variance_c64_workspace_size(64, 1000, 1) == 0
-    assert L.sv_variance_c64_workspace_size(3, 16384, 1) == 0
-    assert L.sv_variance_c64_workspace_size(3, 16385, 1) == 256 + (3 * 16385 * 8 + 255) // 256 * 256 + \
-        L.sv_variance_f32_workspace_size(6, 16385, 1)
+    assert L.sv_variance_c64_workspace_size(3, 16385, 1) == 0
+    assert L.sv_variance_c64_workspace_size(3, 32768, 1) == 0
+    assert L.sv_variance_c64_workspace_size(3, 32769, 1) == 256 + (3 * 32769 * 8 + 255) // 256 * 256 + \
+        L.sv_variance_f32_workspace_size(6, 32769, 1)
     assert L.sv_variance_c64_workspace_size(2, 3, 5) == ctypes.c_size_t(-1).value
     assert L.sv_variance_c64(BAD, -1, 4, 1, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_variance_c64(BAD, 4, 4, 7, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_variance_c64(BAD, 4, 4, 1, -2, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_variance_c64(ctypes.c_void_p(0x1004), 4, 4, 1, 0, out, None, None, 0, None) == \
         SV_ERR_INVALID_ARGUMENT  # not 8-byte aligned
-    assert L.sv_variance_c64(BAD, 4, 20000, 1, 0, out, None, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_c64(BAD, 4, 40000, 1, 0, out, None, None, 0, None) == SV_ERR_WORKSPACE
     assert L.sv_variance_c64(None, 0, 4, 1, 0, None, None, None, 0, None) == 0
 
 

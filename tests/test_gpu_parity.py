@@ -564,11 +564,12 @@ def test_complex_printed_values(torch_dev):
     assert v[0] == float(g["identical_variance"])
 
 
-# rows of up to 16384 values take the one-pass kernel (odd widths: per-lane
-# scalar loads); longer rows the staged split
+# rows of up to 32768 values take the one-pass kernel (odd widths: per-lane
+# scalar loads; 16385 and up: 32 values per lane); longer rows the staged split
 @pytest.mark.parametrize("shape", [(64, 1000), (3, 4096), (5, 20000), (1000, 64), (2000, 3), (1, 1), (7, 2),
                                    (9, 257), (4, 1025), (6, 2047), (3, 5000), (2, 8191), (2, 8192), (2, 8193),
-                                   (3, 12001), (2, 16384), (2, 16385),
+                                   (3, 12001), (2, 16384), (2, 16385), (3, 20001), (40, 24576), (2, 32767),
+                                   (2, 32768), (2, 32769),
                                    (11, 0), (3000, 4), (777, 9), (500, 30), (260, 64), (129, 200), (70, 512)])
 @pytest.mark.parametrize("axis", [0, 1])
 def test_complex_shapes(torch_dev, shape, axis):
