@@ -681,14 +681,22 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   }
   // The launch may hold fewer than W waves (the ones the row reaches); the
   // tree's other wave nodes are (+0, +0).
+  // From four waves on, the tree over the wave nodes takes one node per lane
+  // (lane l < W wave l's) and the first log2(W) cross-lane levels, instead
+  // of all W nodes in every lane's registers.
   const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
-    Node t[W];
+    if constexpr (W >= 4) {
+      const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < nw ? slots[0][lane] : sv::zero_node());
+      ny = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
+    } else {
+      Node t[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) t[i] = i < nw ? slots[0][i] : sv::zero_node();
-    ny = sv::node_tree<0, W, W>(t);
+      for (int i = 0; i < W; ++i) t[i] = i < nw ? slots[0][i] : sv::zero_node();
+      ny = sv::node_tree<0, W, W>(t);
+    }
   }
   const float m = local_mean<V>(ny, n);
 
@@ -709,15 +717,26 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
       slots[2][w] = nq;
     }
     __syncthreads();
-    if (threadIdx.x != 0) return;
-    Node td[W], tq[W];
+    if constexpr (W >= 4) {
+      // wave 0: lanes [0, W) the d nodes, [W, 2W) the d^2 nodes; the d^2
+      // tree takes the TwoSum node, whose error on non-negative operands is
+      // the same exact value as the Fast2Sum form's
+      if (w != 0) return;
+      const int i = lane & (W - 1);
+      const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 2 * W && i < nw ? (&slots[1][0])[lane] : sv::zero_node());
+      nd = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
+      nq = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
+    } else {
+      if (threadIdx.x != 0) return;
+      Node td[W], tq[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-      td[i] = i < nw ? slots[1][i] : sv::zero_node();
-      tq[i] = i < nw ? slots[2][i] : sv::zero_node();
+      for (int i = 0; i < W; ++i) {
+        td[i] = i < nw ? slots[1][i] : sv::zero_node();
+        tq[i] = i < nw ? slots[2][i] : sv::zero_node();
+      }
+      nd = sv::node_tree<0, W, W>(td);
+      nq = sv::node_tree<0, W, W, sv::NODE_NN>(tq);
     }
-    nd = sv::node_tree<0, W, W>(td);
-    nq = sv::node_tree<0, W, W, sv::NODE_NN>(tq);
   }
 
   // step 4
