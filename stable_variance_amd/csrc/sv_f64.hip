@@ -188,6 +188,14 @@ __device__ __forceinline__ NodeD seg_tree_d(NodeD n) {
   return n;
 }
 
+// Lane l's double, as a wave-uniform value (both words read from lane l).
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), l);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
 // E doubles from 2E floats held lane-contiguously (low word first).
 template <int E>
 __device__ __forceinline__ void floats_to_doubles(const float (&f)[2 * E], double (&d)[E]) {
@@ -396,13 +404,20 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
 
   NodeD ny = {0.0, 0.0};
   if (!empty) ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
+  // From four waves on, the tree over the wave nodes takes one node per lane
+  // (lane l < W wave l's) and the first log2(W) cross-lane levels.
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
-    NodeD t[W];
+    if constexpr (W >= 4) {
+      const NodeD t = seg_tree_d<false, W>(lane < W ? slots[0][lane] : NodeD{0.0, 0.0});
+      ny = {readlane_d(t.s, 0), readlane_d(t.c, 0)};
+    } else {
+      NodeD t[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) t[i] = slots[0][i];
-    ny = node_tree_d<0, W, W, false>(t);
+      for (int i = 0; i < W; ++i) t[i] = slots[0][i];
+      ny = node_tree_d<0, W, W, false>(t);
+    }
   }
   const double m = root_value_d(ny) / (double)n;
 
@@ -419,15 +434,25 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
       slots[2][w] = nq;
     }
     __syncthreads();
-    if (threadIdx.x != 0) return;
-    NodeD td[W], tq[W];
+    if constexpr (W >= 4) {
+      // wave 0: lanes [0, W) the d nodes, [W, 2W) the d^2 nodes; the d^2
+      // tree takes the TwoSum node, whose error on non-negative operands is
+      // the same exact value as the Fast2Sum form's
+      if (w != 0) return;
+      const NodeD t = seg_tree_d<false, W>(lane < 2 * W ? (&slots[1][0])[lane] : NodeD{0.0, 0.0});
+      nd = {readlane_d(t.s, 0), readlane_d(t.c, 0)};
+      nq = {readlane_d(t.s, W), readlane_d(t.c, W)};
+    } else {
+      if (threadIdx.x != 0) return;
+      NodeD td[W], tq[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-      td[i] = slots[1][i];
-      tq[i] = slots[2][i];
+      for (int i = 0; i < W; ++i) {
+        td[i] = slots[1][i];
+        tq[i] = slots[2][i];
+      }
+      nd = node_tree_d<0, W, W, false>(td);
+      nq = node_tree_d<0, W, W, true>(tq);
     }
-    nd = node_tree_d<0, W, W, false>(td);
-    nq = node_tree_d<0, W, W, true>(tq);
   }
   if (threadIdx.x == 0) finalize_d(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
 }
