@@ -196,13 +196,14 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// E doubles from 2E floats held lane-contiguously (low word first).
+// E doubles from 2E floats held lane-contiguously (low word first).  Built
+// with the hi/lo intrinsic: the 64-bit shift-and-or form left, at 32 doubles
+// per lane, one private-memory slot per double (float stores, double loads).
 template <int E>
 __device__ __forceinline__ void floats_to_doubles(const float (&f)[2 * E], double (&d)[E]) {
 #pragma unroll
   for (int i = 0; i < E; ++i)
-    d[i] = __builtin_bit_cast(double, ((unsigned long long)__builtin_bit_cast(unsigned, f[2 * i + 1]) << 32) |
-                                          __builtin_bit_cast(unsigned, f[2 * i]));
+    d[i] = __hiloint2double(__builtin_bit_cast(int, f[2 * i + 1]), __builtin_bit_cast(int, f[2 * i]));
 }
 
 __device__ __forceinline__ void store_node_d(NodeD *dst, NodeD v) {
@@ -1091,6 +1092,12 @@ __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int
 }
 
 constexpr int64_t V64_ROWS_MAX_N = 16384;  // one workgroup per row
+// Rows of up to 32768 values take one workgroup of 32 values per lane when
+// there are enough rows to fill the chip (fewer take the chunked path, which
+// spreads a row over several workgroups); the workspace is sized for the
+// chunked path either way.
+constexpr int64_t V64_ROWS_ONE_MAX_N = 32768;
+constexpr int64_t V64_ROWS_ONE_MIN_ROWS = 256;
 constexpr int64_t V64_COLS_MAX_R = 1024;   // whole columns in one workgroup
 constexpr int64_t V64_MAX_ELEMS = 1LL << 39;
 
@@ -1357,6 +1364,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     else if (n <= 4096) SV_ROWS64(16, 4);
     else if (n <= 8192) SV_ROWS64(16, 8);
     else if (n <= V64_ROWS_MAX_N) SV_ROWS64(16, 16);
+    else if (n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS) SV_ROWS64(32, 16);
     else {
       const int64_t nch = (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK;
       const SliceWsD ws = slice_ws(workspace, rows * nch);

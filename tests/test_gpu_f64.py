@@ -212,3 +212,15 @@ def test_var64_top_of_range_and_specials(torch_dev):
     torch, dev = torch_dev
     v = sv.var(torch.zeros((3, 0), dtype=torch.float64, device=dev), dim=1)
     assert torch.isnan(v).all()
+
+
+# at least 256 rows of 16385..32768 values: one workgroup of 16 waves, 32
+# doubles per lane (odd widths: 8-byte loads); fewer rows keep the chunks
+@pytest.mark.parametrize("shape", [(256, 16385), (300, 20001), (256, 32768), (257, 24576), (255, 20000)])
+def test_var64_long_rows_one_workgroup(torch_dev, shape):
+    rng = np.random.default_rng(shape[0] + shape[1])
+    a = rng.normal(-3e7, 5, shape)
+    check_var64(torch_dev, a, 1)
+    check_var64(torch_dev, a, 1, 1)
+    b = W.adversarial_values(shape[0] * shape[1], shape[1]).astype(np.float64).reshape(shape) * 1e200
+    check_var64(torch_dev, b, 1)
