@@ -44,8 +44,12 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fno-unsafe-math-optimizations",
           "-fexcess-precision=standard", "-fPIC", "-shared", "-Wall", "-Wextra"]
 
+# The kernel of [VAR] §2.  READING of step 2: the local mean's sum of y is
+# the plain pairwise tree (METHOD_KERNEL); the compensated tree of step 3
+# sums the residuals d and d^2.  METHOD_KERNEL_COMP_SY is the other reading,
+# every sum of the slice on the compensated tree.
 METHOD_KERNEL = 0
-METHOD_KERNEL_PLAIN_SY = 1
+METHOD_KERNEL_COMP_SY = 1
 METHOD_REFERENCE = 2
 METHOD_NAIVE = 3
 # Ablation rows of the method page's §4 (one step changed at a time)
@@ -54,7 +58,7 @@ METHOD_SHIFT_PLAIN_2T = 5        # shift + centring + two-term, plain tree
 METHOD_NOSHIFT_COMP_2T = 6       # no shift, two-term, compensated tree
 METHOD_SHIFT_COMP_NO2T = 7       # shift + centring, compensated tree, no two-term
 METHOD_SHIFT_KAHAN_NO2T = 8      # shift + centring, sequential Kahan scan, no two-term
-METHOD_KERNEL_DW = 9             # the method with double-word carries in all three trees
+METHOD_KERNEL_DW = 9             # the method with double-word carries in its compensated trees
 
 _lib = None
 
@@ -213,8 +217,9 @@ def tree_sum_f64(x, pad_to: int = 0) -> np.float64:
 
 
 def variance_f64(x, axis: int = -1, ddof: int = 0, method: int = METHOD_KERNEL):
-    """The method (METHOD_KERNEL) or the two-term reference (METHOD_REFERENCE)
-    on a 2-D float64 array, every operation in binary64."""
+    """The method (METHOD_KERNEL, or METHOD_KERNEL_COMP_SY for the other
+    reading of step 2) or the two-term reference (METHOD_REFERENCE) on a
+    2-D float64 array, every operation in binary64."""
     a = np.ascontiguousarray(x, np.float64)
     if a.ndim == 1:
         a = a.reshape(1, -1)
@@ -255,9 +260,10 @@ def seq_neumaier(x) -> np.float32:
 def variance(x, axis: int = -1, ddof: int = 0, method: int = METHOD_KERNEL):
     """Variance and mean of a 2-D float32 array along ``axis``.
 
-    method: METHOD_KERNEL (the [VAR] §2 kernel, compensated Sy tree),
-    METHOD_KERNEL_PLAIN_SY (same with the plain Sy tree), METHOD_REFERENCE
-    (the two-term formula of [VAR] §1), METHOD_NAIVE.
+    method: METHOD_KERNEL (the [VAR] §2 kernel: plain tree of y for the
+    local mean, compensated trees of d and d^2), METHOD_KERNEL_COMP_SY (the
+    same with a compensated tree of y), METHOD_REFERENCE (the two-term
+    formula of [VAR] §1), METHOD_NAIVE, and the ablation rows 4..9.
     Returns (var, mean) as float32 arrays.
     """
     a = _f32c(x)

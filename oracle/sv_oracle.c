@@ -212,18 +212,23 @@ float orc_seq_naive_f32(const float *x, int64_t n) {
     return sum;
 }
 
-/* The Kahan recurrence in the blog's form: the stored correction is
- * subtracted from the next input, and the new correction is the difference
- * of the sums minus the adjusted input. */
+/* Kahan's compensated summation (W. Kahan, "Further remarks on reducing
+ * truncation errors", CACM 8(1), 1965; stated as Algorithm 4.2 in Higham,
+ * "Accuracy and Stability of Numerical Algorithms", 2nd ed., section 4.3).
+ * c holds the low-order part that the last addition to s dropped, with its
+ * sign reversed; it is taken off the next term before that term is added.
+ * Starting from s = c = 0, the first pass leaves s = x[0] and c = 0.  The
+ * [KAHAN] page prints what this recurrence gives on 10^6 copies of 0.001f
+ * (1000.00006), which pins it. */
 float orc_seq_kahan_f32(const float *x, int64_t n) {
-    float sum = 0.0f, corr = 0.0f;
+    float s = 0.0f, c = 0.0f;
     for (int64_t i = 0; i < n; ++i) {
-        float adj = x[i] - corr;
-        float t = sum + adj;
-        corr = (t - sum) - adj;
-        sum = t;
+        float y = x[i] - c;        /* the term, corrected by the lost part */
+        float t = s + y;           /* the new sum, rounded                 */
+        c = (t - s) - y;           /* what the rounding of t dropped       */
+        s = t;
     }
-    return sum;
+    return s;
 }
 
 /* Neumaier's variant ([ORD]): the branch on magnitudes picks which operand's
@@ -271,8 +276,11 @@ static void gather(const float *x, int64_t n, int64_t stride, float *out) {
  * The kernel of [VAR] §2, one slice.
  *   step 1  x0 = x[0]; y_i = fl(x_i - x0)
  *   step 2  m = fl(Sy / fl(n)); d_i = fl(y_i - m)
- *           READING: Sy is the compensated tree of y when comp_sy != 0 (the
- *           default), the plain tree of the same topology otherwise.
+ *           READING: Sy is the plain pairwise tree of y (comp_sy == 0, the
+ *           method): step 2 writes a plain sum(y), and step 3 describes the
+ *           compensated tree for the sums of the residuals only.  comp_sy != 0
+ *           is the other reading, every sum of the slice on the compensated
+ *           tree.
  *   step 3  S1 = Tree(d), S2 = Tree(q) with q_i = fl(d_i * d_i)
  *   step 4  v = max(fl(fl(S2/n) - fl(b*b)), 0) with b = fl(S1/n), then the
  *           ddof rescale; mean = fl(x0 + m).
@@ -304,12 +312,16 @@ static void var_kernel_slice(const float *x, int64_t n, int64_t stride, int64_t 
 }
 
 /*
- * Ablation variants of [VAR] §4, one step changed at a time.  Flags:
+ * Ablation variants of [VAR] §4, one step of the kernel changed at a time.
+ * Flags:
  *   shift    y = x - x0 (else y = x and mean = m)
- *   sum_kind 0 plain tree, 1 compensated tree, 2 sequential Kahan scan
- *            (the Kahan form of [KAHAN]), 3 compensated tree with
- *            double-word carries, for every sum of the slice
+ *   sum_kind how the sums of the residuals (S1 and S2, the sums that the
+ *            kernel takes on the compensated tree) are formed: 0 plain tree,
+ *            1 compensated tree, 2 sequential Kahan scan, 3 compensated tree
+ *            with double-word carries
  *   twoterm  v = max(S2/n - (S1/n)^2, 0) (else v = max(S2/n, 0))
+ * READING: the local mean keeps the kernel's plain tree of y in every row
+ * (no row of the table names the centring's sum as the step it changes).
  * READING: "no two-term" is v = max(S2/n, 0); the Kahan-scan row of the
  * table ("shift + centring, Kahan sequential scan") has no two-term step,
  * like the other rows whose label does not add one.
@@ -333,7 +345,7 @@ static void var_variant_slice(const float *x, int64_t n, int64_t stride, int64_t
     if (shift)
         for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - x0;             /* y */
     float fn = (float)n;
-    float m = slice_sum(buf, n, sum_kind) / fn;
+    float m = orc_tree_plain_f32(buf, n, 1, 0) / fn;
     for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;                  /* d */
     float s1 = twoterm ? slice_sum(buf, n, sum_kind) : 0.0f;
     for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] * buf[i];             /* q */
@@ -404,14 +416,14 @@ static void var_naive_slice(const float *x, int64_t n, int64_t stride, int64_t d
  * Batched entry points over a row-major [rows, cols] array.
  *   axis 1: rows slices of length cols (contiguous)
  *   axis 0: cols slices of length rows (stride cols)
- * method: 0 kernel (comp_sy 1), 1 kernel with a plain Sy tree, 2 two-term
- * reference, 3 naive, and the [VAR] §4 ablation rows:
+ * method: 0 the kernel (plain Sy tree), 1 the kernel with a compensated Sy
+ * tree, 2 two-term reference, 3 naive, and the [VAR] §4 ablation rows:
  *   4 shift + centring, plain tree, no two-term
  *   5 shift + centring + two-term, plain tree
  *   6 no shift, two-term, compensated tree
  *   7 shift + centring, compensated tree, no two-term
  *   8 shift + centring, sequential Kahan scan, no two-term
- *   9 the method with double-word carries in all three trees
+ *   9 the kernel with double-word carries in its compensated trees
  * mean may be NULL.  Returns 0, or -1 on bad arguments.
  */
 int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
@@ -429,8 +441,8 @@ int orc_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64
         const float *xs = x + s * sstride;
         float v, mu;
         switch (method) {
-        case 0: var_kernel_slice(xs, n, stride, ddof, 1, buf, &v, &mu); break;
-        case 1: var_kernel_slice(xs, n, stride, ddof, 0, buf, &v, &mu); break;
+        case 0: var_kernel_slice(xs, n, stride, ddof, 0, buf, &v, &mu); break;
+        case 1: var_kernel_slice(xs, n, stride, ddof, 1, buf, &v, &mu); break;
         case 2: var_reference_slice(xs, n, stride, ddof, buf, buf2, &v, &mu); break;
         case 3: var_naive_slice(xs, n, stride, ddof, buf, &v, &mu); break;
         case 4: var_variant_slice(xs, n, stride, ddof, 1, 0, 0, buf, &v, &mu); break;
@@ -520,9 +532,11 @@ static inline double ddof_scale_d(double v, int64_t n, int64_t ddof) {
     return v * f;
 }
 
-/* The kernel of [VAR] §2 on one slice, in double. */
-static void var_kernel_slice_d(const double *x, int64_t n, int64_t stride, int64_t ddof, double *buf,
-                               double *var, double *mean) {
+/* The kernel of [VAR] §2 on one slice, in double, with the same reading
+ * of step 2 as in float32: Sy is the plain tree (comp_sy == 0) or, in the
+ * other reading, the compensated tree. */
+static void var_kernel_slice_d(const double *x, int64_t n, int64_t stride, int64_t ddof, int comp_sy,
+                               double *buf, double *var, double *mean) {
     if (n <= 0) {
         *var = NAN;
         *mean = NAN;
@@ -532,7 +546,8 @@ static void var_kernel_slice_d(const double *x, int64_t n, int64_t stride, int64
     double x0 = buf[0];
     for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - x0;
     double fn = (double)n;
-    double m = orc_tree_sum_f64(buf, n, 1, 0) / fn;
+    double sy = comp_sy ? orc_tree_sum_f64(buf, n, 1, 0) : tree_plain_d(buf, n);
+    double m = sy / fn;
     for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] - m;
     double s1 = orc_tree_sum_f64(buf, n, 1, 0);
     for (int64_t i = 0; i < n; ++i) buf[i] = buf[i] * buf[i];
@@ -565,10 +580,11 @@ static void var_reference_slice_d(const double *x, int64_t n, int64_t stride, in
 }
 
 /* Variance of a row-major double [rows, cols] array; method 0 the kernel,
- * 2 the two-term reference.  Returns 0, or -1 on bad arguments. */
+ * 1 the kernel with a compensated Sy tree, 2 the two-term reference.
+ * Returns 0, or -1 on bad arguments. */
 int orc_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int method,
                      double *var, double *mean) {
-    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || (method != 0 && method != 2)) return -1;
+    if (rows < 0 || cols < 0 || ddof < 0 || (axis != 0 && axis != 1) || method < 0 || method > 2) return -1;
     int64_t nslices = axis == 1 ? rows : cols;
     int64_t n = axis == 1 ? cols : rows;
     int64_t stride = axis == 1 ? 1 : cols;
@@ -578,7 +594,7 @@ int orc_variance_f64(const double *x, int64_t rows, int64_t cols, int axis, int6
     if (!buf || !buf2) { free(buf); free(buf2); return -2; }
     for (int64_t s = 0; s < nslices; ++s) {
         double v, mu;
-        if (method == 0) var_kernel_slice_d(x + s * sstride, n, stride, ddof, buf, &v, &mu);
+        if (method != 2) var_kernel_slice_d(x + s * sstride, n, stride, ddof, method, buf, &v, &mu);
         else var_reference_slice_d(x + s * sstride, n, stride, ddof, buf, buf2, &v, &mu);
         var[s] = v;
         if (mean) mean[s] = mu;

@@ -253,7 +253,15 @@ def test_c_and_numpy_forms_agree():
 
 # ---------------------------------------------------------------- variance
 
-def test_identical_values_table():
+# The two readings of the method page's §2 step 2 (m = sum(y) / n): the
+# plain tree of y (the method) and the compensated tree of y.  Every pin of
+# the kernel below holds for both; test_local_mean_readings_hand_worked
+# tells them apart.
+KERNELS = [oracle.METHOD_KERNEL, oracle.METHOD_KERNEL_COMP_SY]
+
+
+@pytest.mark.parametrize("method", KERNELS)
+def test_identical_values_table(method):
     # Method page §3: variance of three identical float32 values.  The naive
     # and two-term columns fix the reading of mean() as tree * fl(1/n); the
     # kernel returns exactly 0 up to 1e38 thanks to the shift.
@@ -261,22 +269,44 @@ def test_identical_values_table():
         x = np.full((1, 3), np.float32(float(c)))
         vn = oracle.variance(x, axis=1, method=oracle.METHOD_NAIVE)[0][0]
         vr = oracle.variance(x, axis=1, method=oracle.METHOD_REFERENCE)[0][0]
-        vk, mk = oracle.variance(x, axis=1, method=oracle.METHOD_KERNEL)
+        vk, mk = oracle.variance(x, axis=1, method=method)
         assert "%g" % vn == naive and "%g" % vr == ref and "%g" % vk[0] == ker
         assert vk[0] == 0.0 and mk[0] == np.float32(float(c))
 
 
+@pytest.mark.parametrize("method", KERNELS)
 @pytest.mark.parametrize("c", [1.0, 1e10, 1e30, 1e38, -3.5e37, 7.5e10])
 @pytest.mark.parametrize("ddof", [0, 1])
-def test_constant_slices_zero(c, ddof):
+def test_constant_slices_zero(c, ddof, method):
     # Identical values give exactly 0.0 and mean == c (a missing shift
     # overflows to NaN at 1e38).
     x = W.constant(c)
-    v, m = oracle.variance(x, axis=0, ddof=ddof)
+    v, m = oracle.variance(x, axis=0, ddof=ddof, method=method)
     assert np.all(v == 0.0) and not np.any(np.signbit(v))
     assert np.all(m == np.float32(c))
-    v, m = oracle.variance(x.T.copy(), axis=1, ddof=ddof)
+    v, m = oracle.variance(x.T.copy(), axis=1, ddof=ddof, method=method)
     assert np.all(v == 0.0) and np.all(m == np.float32(c))
+
+
+def test_local_mean_readings_hand_worked():
+    # y = x - x0 = [0, 1, 2^24, 1] (x0 = 0).  The plain pairwise tree gives
+    # fl(0 + 1) = 1 and fl(2^24 + 1) = 2^24 (a tie, to even), then
+    # fl(1 + 2^24) = 2^24: m = 2^24 / 4 = 4194304.  The compensated tree
+    # carries the two lost ones and returns the exact 2^24 + 2: m = 4194304.5.
+    # mean = x0 + m shows which sum the local centring took.  Both readings
+    # then give the variance of the same four values within the bound (the
+    # two-term correction absorbs the error of m); the exact variance is
+    # computed with Fractions.
+    x = np.array([[0.0, 1.0, 2.0 ** 24, 1.0]], np.float32)
+    vp, mp = oracle.variance(x, axis=1, method=oracle.METHOD_KERNEL)
+    vc, mc = oracle.variance(x, axis=1, method=oracle.METHOD_KERNEL_COMP_SY)
+    assert mp[0] == np.float32(4194304.0)
+    assert mc[0] == np.float32(4194304.5)
+    vals = [Fraction(0), Fraction(1), Fraction(2 ** 24), Fraction(1)]
+    mu = sum(vals) / 4
+    exact = sum((v - mu) ** 2 for v in vals) / 4
+    for v in (vp[0], vc[0]):
+        assert abs(F(v) - exact) <= Fraction(TOL_VAR) * exact
 
 
 def test_sterbenz_shift_exact_d4():
@@ -290,43 +320,48 @@ def test_sterbenz_shift_exact_d4():
     assert np.mean(y.astype(np.float64) == exact) == float(g["equal_fraction"])
 
 
+@pytest.mark.parametrize("method", KERNELS)
 @pytest.mark.parametrize("n", [1000, 1024, 4096, 3])
-def test_arithmetic_progression_closed_form(n):
+def test_arithmetic_progression_closed_form(n, method):
     # x_i = 10000 + i: the shift, the centring and the squares are exact, so
     # var = fl32((n^2 - 1)/12) (ddof 0), mean = 10000 + (n-1)/2 exactly;
     # with ddof 1 the exact n(n+1)/12 is within 1 ulp.  A wrong sign in the
-    # two-term formula, a wrong centring or a wrong ddof factor fails.
+    # two-term formula, a wrong centring or a wrong ddof factor fails.  (Every
+    # partial sum of y is an integer below 2^24, so the plain and the
+    # compensated trees of y agree here.)
     x = (10000.0 + np.arange(n)).astype(np.float32)
-    v, m = oracle.variance(x[None, :], axis=1, ddof=0)
+    v, m = oracle.variance(x[None, :], axis=1, ddof=0, method=method)
     assert v[0] == oracle.round_f32(Fraction(n * n - 1, 12))
     assert m[0] == np.float32(10000 + (n - 1) / 2)
-    v1, _ = oracle.variance(x[:, None], axis=0, ddof=1)
+    v1, _ = oracle.variance(x[:, None], axis=0, ddof=1, method=method)
     exact = Fraction(n * (n + 1), 12)
     ulp = np.spacing(np.float32(float(exact)))
     assert abs(F(v1[0]) - exact) <= F(ulp)
 
 
-def test_ddof_edge_cases():
+@pytest.mark.parametrize("method", KERNELS)
+def test_ddof_edge_cases(method):
     x = np.array([[5.0]], np.float32)
-    v, m = oracle.variance(x, axis=1, ddof=0)
+    v, m = oracle.variance(x, axis=1, ddof=0, method=method)
     assert v[0] == 0.0 and m[0] == 5.0
-    v, _ = oracle.variance(x, axis=1, ddof=1)      # 0 * (1/0) = 0 * inf
+    v, _ = oracle.variance(x, axis=1, ddof=1, method=method)      # 0 * (1/0) = 0 * inf
     assert np.isnan(v[0])
     x = np.array([[1.0, 3.0]], np.float32)
-    v, _ = oracle.variance(x, axis=1, ddof=2)      # 1 * inf
+    v, _ = oracle.variance(x, axis=1, ddof=2, method=method)      # 1 * inf
     assert v[0] == np.inf
-    v, m = oracle.variance(np.zeros((3, 0), np.float32), axis=1)
+    v, m = oracle.variance(np.zeros((3, 0), np.float32), axis=1, method=method)
     assert np.all(np.isnan(v)) and np.all(np.isnan(m))
 
 
-def test_accuracy_d1_d4_and_no_worse_than_reference():
+@pytest.mark.parametrize("method", KERNELS)
+def test_accuracy_d1_d4_and_no_worse_than_reference(method):
     # Against the float64 variance of the same float32 values: within
     # 4 * 2^-24 and no worse than the two-term reference on these
     # well-conditioned datasets; same order of magnitude as the page's tables.
     table = {r[0]: [float(v) for v in r[1:]] for r in read_table("accuracy_tables.txt")}
     for name, a, ax, _ in W.datasets_d1_d4():
         v64 = oracle.var_f64(a, axis=ax)
-        ek = oracle.max_rel_err(oracle.variance(a, axis=ax)[0], v64)
+        ek = oracle.max_rel_err(oracle.variance(a, axis=ax, method=method)[0], v64)
         er = oracle.max_rel_err(oracle.variance(a, axis=ax, method=oracle.METHOD_REFERENCE)[0], v64)
         en = oracle.max_rel_err(oracle.variance(a, axis=ax, method=oracle.METHOD_NAIVE)[0], v64)
         naive_p, ref_p, ker_p = table[name][0], table[name][1], table[name][2]
@@ -355,15 +390,16 @@ def test_complex_check():
     assert v[0] == float(g["identical_variance"])
 
 
-def test_kernel_steps_numpy_cross_check():
+@pytest.mark.parametrize("method", KERNELS)
+def test_kernel_steps_numpy_cross_check(method):
     # The variance kernel rebuilt from the numpy tree levels, step by step,
     # agrees bit for bit with the C oracle (cross-check, not a pin).
     rng = np.random.default_rng(9)
     for rows, cols in [(7, 1000), (5, 4096), (3, 33), (2, 1)]:
         x = rng.normal(1e4, 1, (rows, cols)).astype(np.float32)
-        v, m = oracle.variance(x, axis=1)
+        v, m = oracle.variance(x, axis=1, method=method)
         y = (x - x[:, :1]).astype(np.float32)
-        sy = oracle.np_tree_sum(y)
+        sy = oracle.np_tree_plain(y) if method == oracle.METHOD_KERNEL else oracle.np_tree_sum(y)
         mm = (sy / np.float32(cols)).astype(np.float32)
         d = (y - mm[:, None]).astype(np.float32)
         q = (d * d).astype(np.float32)
@@ -390,6 +426,18 @@ def test_ablation_identical_1e38_column():
     for m in SHIFTED:
         assert oracle.variance(x, axis=1, method=m)[0][0] == 0.0, m
     assert np.isnan(oracle.variance(x, axis=1, method=oracle.METHOD_REFERENCE)[0][0])
+
+
+def test_ablation_rows_keep_the_plain_local_mean():
+    # Each ablation row changes one step of the kernel; none of them names the
+    # local centring's sum, so every shifted row keeps the kernel's plain tree
+    # of y: on y = [0, 1, 2^24, 1] its mean is 2^24 / 4 (see
+    # test_local_mean_readings_hand_worked), not the compensated 4194304.5.
+    x = np.array([[0.0, 1.0, 2.0 ** 24, 1.0]], np.float32)
+    for m in SHIFTED + [oracle.METHOD_KERNEL_DW]:
+        assert oracle.variance(x, axis=1, method=m)[1][0] == np.float32(4194304.0), m
+    # without the shift, y = x: the same plain tree of the same values
+    assert oracle.variance(x, axis=1, method=oracle.METHOD_NOSHIFT_COMP_2T)[1][0] == np.float32(4194304.0)
 
 
 def test_ablation_two_term_does_not_change_the_errors():
