@@ -353,7 +353,7 @@ def np_tree_plain(x, pad_to: int = 0) -> np.ndarray:
     with np.errstate(invalid="ignore", over="ignore"):
         while s.shape[-1] > 1:
             s = s[..., 0::2] + s[..., 1::2]
-    return s[..., 0]
+        return (s[..., 0] + np.float32(0.0)).astype(np.float32)  # root: fl(s + 0)
 
 
 # ---------------------------------------------------------------------------

@@ -185,7 +185,12 @@ int orc_tree_node_f32(const float *x, int64_t n, int64_t pad_to, float *s_out, f
     return 0;
 }
 
-/* Same topology without the error array: the plain pairwise tree. */
+/* Same topology without the error array: the plain pairwise tree.
+ * READING (the root of a plain tree, [VAR] §2 step 3: "the result is the
+ * final sum plus the final carry"): a plain tree's carry is zero, so its
+ * value is fl(s_0 + 0).  That differs from s_0 only when s_0 is -0 (every
+ * value -0), and it makes the result independent of how far the values are
+ * padded with +0, as for the compensated tree, whose carries are never -0. */
 float orc_tree_plain_f32(const float *x, int64_t n, int64_t stride, int64_t pad_to) {
     if (n <= 0) return 0.0f;
     int64_t P = pow2_ceil(n);
@@ -198,7 +203,7 @@ float orc_tree_plain_f32(const float *x, int64_t n, int64_t stride, int64_t pad_
     for (int64_t i = 0; i < P; ++i) s[i] = (i < n) ? x[i * stride] : 0.0f;
     for (int64_t len = P; len > 1; len >>= 1)
         for (int64_t k = 0; k < len / 2; ++k) s[k] = s[2 * k] + s[2 * k + 1];
-    float r = s[0];
+    float r = s[0] + 0.0f;
     free(s);
     return r;
 }
@@ -514,7 +519,7 @@ static double tree_plain_d(const double *x, int64_t n) {
     for (int64_t i = 0; i < P; ++i) s[i] = (i < n) ? x[i] : 0.0;
     for (int64_t len = P; len > 1; len >>= 1)
         for (int64_t k = 0; k < len / 2; ++k) s[k] = s[2 * k] + s[2 * k + 1];
-    double r = s[0];
+    double r = s[0] + 0.0;  /* the root rule of the float32 plain tree */
     free(s);
     return r;
 }
