@@ -11,8 +11,9 @@
  *   sv_variance_f32   the variance and the mean of each slice of a row-major
  *                     [rows, cols] array along an axis (same page, §2 steps
  *                     1-4): shift by the slice's first element, local
- *                     centring, compensated trees of d and d^2, two-term
- *                     correction and ddof rescale.
+ *                     centring by the plain tree of the shifted values,
+ *                     compensated trees of d and d^2, two-term correction
+ *                     and ddof rescale.
  *
  * Arithmetic: IEEE binary32, round to nearest even, every operation rounded
  * on its own (no FMA contraction, no reassociation, subnormals kept).
@@ -146,7 +147,10 @@ size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
  *                 cols); var_out/mean_out have cols entries
  * For each slice x[0..n) (Pennacchio, "Variance in float32 ...", §2):
  *   step 1  y_i = fl(x_i - x_0)
- *   step 2  m = fl(Tree(y) / fl(n)),  d_i = fl(y_i - m)
+ *   step 2  m = fl(Plain(y) / fl(n)),  d_i = fl(y_i - m), where Plain is
+ *           the same adjacent-pair tree without the error array (step 2
+ *           writes a plain sum; step 3 introduces the compensated tree for
+ *           the sums of the residuals)
  *   step 3  S1 = Tree(d),  S2 = Tree(fl(d_i * d_i))
  *   step 4  var = max(fl(fl(S2/n) - fl(b*b)), 0) with b = fl(S1/n), where a
  *           NaN stays NaN and any other value <= 0 gives +0; if ddof != 0
@@ -192,6 +196,8 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
  * float32 ...", §4: one step changed at a time) and the two formulae of its
  * §1, for accuracy and speed comparisons.  `variant`:
  *   0  the method (same result as sv_variance_f32)
+ *   1  the method with the compensated tree for the local mean too,
+ *      m = fl(Tree(y) / fl(n)) (the other reading of §2 step 2)
  *   2  two-term reference formula: m = mean(x), d = x - m,
  *      var = max(mean(d^2) - mean(d)^2, 0); mean() = plain tree * fl(1/n);
  *      no shift (the returned mean is m)
@@ -201,6 +207,8 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
  *   6  no shift, two-term, compensated trees (the returned mean is m)
  *   7  shift + centring, compensated trees, no two-term
  * "Plain tree" is the same adjacent-pair topology without the error array.
+ * Every variant but 1 takes the plain tree for the local mean, as the method
+ * does; "plain" and "compensated" name the trees of d and d^2.
  * Shapes: axis 1 with n <= 16384, axis 0 with n <= 1024 (else
  * SV_ERR_UNSUPPORTED).  No workspace; otherwise as sv_variance_f32.
  */
@@ -307,11 +315,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    coalesced loads transposed through LDS in four stages of
  *                    16 lanes each (a quarter of the LDS of path 0)
  *   "var_nt"         row variance: as sum_nt (default 0)
- *   "var_rows_per_wave"  rows of 1025..4096 values one wave pipelines (the
- *                    next row's loads in flight while one is reduced): 1
- *                    (default) or 2
- *   "var_dma_rows"   rows of 1025..4096 values per wave staged by direct
- *                    global-to-LDS loads: 0 (off, default), 2, 4 or 8
+ *   "var_full_rows"  rows that fill their power-of-two tile exactly and
+ *                    start 16-byte aligned: 1 (default) = the kernel without
+ *                    masks or clamped loads, 0 = the general row kernel
  *   "var_split"      rows of 1025..16384 values: waves per 4096 values of
  *                    the row's power-of-two tile, 1, 2, 4 or 8 (64, 32, 16
  *                    or 8 values per lane; a 2048-value tile takes at most 32
@@ -354,8 +360,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    (32 only with three folds; other counts use 16)
  *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)
  *   "reset"          any value: restore every default
- * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  Not thread
- * safe with concurrent calls.
+ * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  The settings
+ * belong to the calling host thread: they steer that thread's later calls
+ * only, and every other thread keeps its own (a new thread starts from the
+ * defaults).
  */
 sv_status sv_set_tuning(const char *key, int64_t value);
 

@@ -267,6 +267,7 @@ def var(x, dim: int = -1, ddof: int = 0, return_mean: bool = False):
 # Ablation variants of the method page's §4 (see sv_variance_variant_f32).
 VARIANTS = {
     "kernel": 0,
+    "kernel_comp_y": 1,
     "reference": 2,
     "naive": 3,
     "shift_plain_no2t": 4,

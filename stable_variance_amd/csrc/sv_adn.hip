@@ -547,7 +547,7 @@ struct AdnTuning {
   int e = 16;                  // values per lane in a chunk: 16 or 32
   int64_t blocks = 512;        // target number of workgroups (few: each merge is costly)
 };
-AdnTuning g_adn;
+thread_local AdnTuning g_adn;  // per host thread, like the other launch knobs
 
 template <int K, int E>
 void launch_k(bool vec, dim3 grid, const float *x, int64_t n, int64_t chunks, int64_t g, unsigned *recs,

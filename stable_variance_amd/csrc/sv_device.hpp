@@ -119,13 +119,19 @@ __device__ __forceinline__ Node combine_dw(Node l, Node r) { return renorm_dw(co
 
 __device__ __forceinline__ Node leaf_dw(float a, float b) { return renorm_dw(leaf_canon(a, b)); }
 
+// Plain pairwise node: fl(l.s + r.s) and no carry (c stays +0).  Its s part
+// is the same sum as the compensated node's s, so a plain tree is the s half
+// of a compensated tree of the same topology.
+__device__ __forceinline__ Node combine_plain(Node l, Node r) { return {l.s + r.s, 0.0f}; }
+
 // Node kinds of the cross-lane and node-array trees.
-enum NodeKind { NODE_TWOSUM = 0, NODE_NN = 1, NODE_DW = 2 };
+enum NodeKind { NODE_TWOSUM = 0, NODE_NN = 1, NODE_DW = 2, NODE_PLAIN = 3 };
 
 template <int KIND>
 __device__ __forceinline__ Node combine_k(Node l, Node r) {
   if constexpr (KIND == NODE_NN) return combine_nn(l, r);
   else if constexpr (KIND == NODE_DW) return combine_dw(l, r);
+  else if constexpr (KIND == NODE_PLAIN) return combine_plain(l, r);
   else return combine(l, r);
 }
 
@@ -134,11 +140,27 @@ __device__ __forceinline__ float root_value(Node n) {
   return __builtin_isfinite(n.s) ? n.s + n.c : n.s;
 }
 
+// Value at the root of a tree of the given kind.  A plain tree's carry is
+// zero, so its value is fl(s + 0): s itself, except that an all -0 sum gives
+// +0, whatever the +0 padding beyond the data (the compensated tree's
+// carries are never -0, so fl(s + c) has the same property).
+template <int KIND>
+__device__ __forceinline__ float root_value_k(Node n) {
+  if constexpr (KIND == NODE_PLAIN) return n.s + 0.0f;
+  else return root_value(n);
+}
+
 __device__ __forceinline__ Node zero_node() { return {0.0f, 0.0f}; }
 
 // ---------------------------------------------------------------- in-lane trees
 
-enum LeafKind { LEAF_CANON = 0, LEAF_FAST = 1, LEAF_NN = 2, LEAF_DW = 3 };
+enum LeafKind { LEAF_CANON = 0, LEAF_FAST = 1, LEAF_NN = 2, LEAF_DW = 3, LEAF_PLAIN = 4 };
+
+// The tree of the local mean, m = sum(y) / n (method page §2 step 2): the
+// plain pairwise tree, the s half of the compensated tree's topology.  The
+// sums of d and d^2 (step 3) take the compensated tree.
+constexpr int Y_KIND = NODE_PLAIN;
+constexpr int Y_LEAF = LEAF_PLAIN;
 
 // Subtrees of at least this many values are scheduled one after the other
 // (a scheduling barrier between siblings): the compiler then interleaves
@@ -157,14 +179,16 @@ __device__ __forceinline__ Node lane_tree(const float (&v)[E]) {
     if constexpr (LEAF == LEAF_CANON) return leaf_canon(v[OFF], v[OFF + 1]);
     else if constexpr (LEAF == LEAF_FAST) return leaf_fast(v[OFF], v[OFF + 1]);
     else if constexpr (LEAF == LEAF_DW) return leaf_dw(v[OFF], v[OFF + 1]);
+    else if constexpr (LEAF == LEAF_PLAIN) return {v[OFF] + v[OFF + 1], 0.0f};
     else return leaf_nn(v[OFF], v[OFF + 1]);
   } else {
     const Node l = lane_tree<LEAF, OFF, N / 2, E>(v);
-    if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (N / 2 >= SCHED_BLOCK && LEAF != LEAF_PLAIN) __builtin_amdgcn_sched_barrier(0);
     const Node r = lane_tree<LEAF, OFF + N / 2, N / 2, E>(v);
-    if constexpr (N / 2 >= SCHED_BLOCK) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (N / 2 >= SCHED_BLOCK && LEAF != LEAF_PLAIN) __builtin_amdgcn_sched_barrier(0);
     if constexpr (LEAF == LEAF_NN) return combine_nn(l, r);
     else if constexpr (LEAF == LEAF_DW) return combine_dw(l, r);
+    else if constexpr (LEAF == LEAF_PLAIN) return combine_plain(l, r);
     else return combine(l, r);
   }
 }
@@ -220,9 +244,12 @@ constexpr int DPP_QUAD_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8
 constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <- lane 15-i within 16
 
-template <int CTRL>
+// The neighbour's node; a plain tree moves only its sums (its carries are
+// +0 everywhere).
+template <int CTRL, int KIND = NODE_TWOSUM>
 __device__ __forceinline__ Node dpp_node(Node n) {
-  return {dpp<CTRL>(n.s), dpp<CTRL>(n.c)};
+  if constexpr (KIND == NODE_PLAIN) return {dpp<CTRL>(n.s), 0.0f};
+  else return {dpp<CTRL>(n.s), dpp<CTRL>(n.c)};
 }
 
 // Cross-row exchanges of gfx950 (one VALU instruction per register, no LDS):
@@ -247,11 +274,16 @@ __device__ __forceinline__ void swap_halves(float v, float &a, float &b) {
   b = __builtin_bit_cast(float, y);
 }
 
-template <int XOR>
+template <int XOR, int KIND = NODE_TWOSUM>
 __device__ __forceinline__ NodePair swap_node(Node n) {
   NodePair p;
   swap_halves<XOR>(n.s, p.a.s, p.b.s);
-  swap_halves<XOR>(n.c, p.a.c, p.b.c);
+  if constexpr (KIND == NODE_PLAIN) {
+    p.a.c = 0.0f;
+    p.b.c = 0.0f;
+  } else {
+    swap_halves<XOR>(n.c, p.a.c, p.b.c);
+  }
   return p;
 }
 
@@ -262,13 +294,13 @@ __device__ __forceinline__ NodePair swap_node(Node n) {
 template <int KIND>
 __device__ __forceinline__ Node wave_tree(Node n) {
   auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
-  n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
-  n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
-  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
-  n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
-  NodePair p = swap_node<16>(n);
+  n = comb(n, dpp_node<DPP_QUAD_XOR1, KIND>(n));
+  n = comb(n, dpp_node<DPP_QUAD_XOR2, KIND>(n));
+  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR, KIND>(n));
+  n = comb(n, dpp_node<DPP_ROW_MIRROR, KIND>(n));
+  NodePair p = swap_node<16, KIND>(n);
   n = comb(p.a, p.b);
-  p = swap_node<32>(n);
+  p = swap_node<32, KIND>(n);
   return comb(p.a, p.b);
 }
 
@@ -278,38 +310,18 @@ template <int KIND, int S>
 __device__ __forceinline__ Node seg_tree(Node n) {
   static_assert(S >= 1 && S <= 64 && (S & (S - 1)) == 0, "segment of a power-of-two lanes");
   auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
-  if constexpr (S >= 2) n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
-  if constexpr (S >= 4) n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
-  if constexpr (S >= 8) n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
-  if constexpr (S >= 16) n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
+  if constexpr (S >= 2) n = comb(n, dpp_node<DPP_QUAD_XOR1, KIND>(n));
+  if constexpr (S >= 4) n = comb(n, dpp_node<DPP_QUAD_XOR2, KIND>(n));
+  if constexpr (S >= 8) n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR, KIND>(n));
+  if constexpr (S >= 16) n = comb(n, dpp_node<DPP_ROW_MIRROR, KIND>(n));
   if constexpr (S >= 32) {
-    const NodePair p = swap_node<16>(n);
+    const NodePair p = swap_node<16, KIND>(n);
     n = comb(p.a, p.b);
   }
   if constexpr (S >= 64) {
-    const NodePair p = swap_node<32>(n);
+    const NodePair p = swap_node<32, KIND>(n);
     n = comb(p.a, p.b);
   }
-  return n;
-}
-
-// The same six levels when lane L holds the range of virtual lane
-// v(L) = 4*(L % 16) + L / 16 (the layout of the LDS-DMA row buffers below):
-// virtual bits 0 and 1 are lane bits 4 and 5, virtual bits 2..5 are lane bits
-// 0..3.  The first two levels need the exact partner (lane xor 16, xor 32);
-// after them the quad permutations are exact and the mirrors again reach the
-// sibling because the lower lanes already agree.
-template <int KIND>
-__device__ __forceinline__ Node wave_tree_vlane(Node n) {
-  auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
-  NodePair p = swap_node<16>(n);
-  n = comb(p.a, p.b);
-  p = swap_node<32>(n);
-  n = comb(p.a, p.b);
-  n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
-  n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
-  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
-  n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
   return n;
 }
 
@@ -339,13 +351,13 @@ __device__ __forceinline__ void swap32_two(float x, float y, float &a, float &b)
 template <int KIND>
 __device__ __forceinline__ Node wave_tree_p32(Node n) {
   auto comb = [](Node a, Node b) { return combine_k<KIND>(a, b); };
-  NodePair p = swap_node<32>(n);
+  NodePair p = swap_node<32, KIND>(n);
   n = comb(p.a, p.b);
-  n = comb(n, dpp_node<DPP_QUAD_XOR1>(n));
-  n = comb(n, dpp_node<DPP_QUAD_XOR2>(n));
-  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR>(n));
-  n = comb(n, dpp_node<DPP_ROW_MIRROR>(n));
-  p = swap_node<16>(n);
+  n = comb(n, dpp_node<DPP_QUAD_XOR1, KIND>(n));
+  n = comb(n, dpp_node<DPP_QUAD_XOR2, KIND>(n));
+  n = comb(n, dpp_node<DPP_ROW_HALF_MIRROR, KIND>(n));
+  n = comb(n, dpp_node<DPP_ROW_MIRROR, KIND>(n));
+  p = swap_node<16, KIND>(n);
   return comb(p.a, p.b);
 }
 

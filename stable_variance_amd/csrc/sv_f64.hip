@@ -76,28 +76,42 @@ __device__ __forceinline__ NodeD leaf_nn_d(double a, double b) {
 
 __device__ __forceinline__ double root_value_d(NodeD n) { return __builtin_isfinite(n.s) ? n.s + n.c : n.s; }
 
-template <bool NN>
+// Node kinds of the double trees: 0 (false) TwoSum, 1 (true) the
+// non-negative node, KD_PLAIN the plain pairwise node fl(l.s + r.s) with no
+// carry, the tree of the local mean (method page §2 step 2).
+constexpr int KD_PLAIN = 2;
+
+template <int NN>
 __device__ __forceinline__ NodeD comb_d(NodeD l, NodeD r) {
-  if constexpr (NN) return combine_nn_d(l, r);
+  if constexpr (NN == KD_PLAIN) return {l.s + r.s, 0.0};
+  else if constexpr (NN) return combine_nn_d(l, r);
   else return combine_d(l, r);
 }
 
-enum { LEAF_CANON_D = 0, LEAF_FAST_D = 1, LEAF_NN_D = 2 };
+// The value at the root of a tree of kind K (a plain tree: fl(s + 0)).
+template <int K>
+__device__ __forceinline__ double root_value_kd(NodeD n) {
+  if constexpr (K == KD_PLAIN) return n.s + 0.0;  // fl(s + 0): an all -0 sum gives +0
+  else return root_value_d(n);
+}
+
+enum { LEAF_CANON_D = 0, LEAF_FAST_D = 1, LEAF_NN_D = 2, LEAF_PLAIN_D = 3 };
 
 template <int LEAF, int OFF, int N, int E>
 __device__ __forceinline__ NodeD lane_tree_d(const double (&v)[E]) {
   if constexpr (N == 2) {
     if constexpr (LEAF == LEAF_CANON_D) return leaf_canon_d(v[OFF], v[OFF + 1]);
     else if constexpr (LEAF == LEAF_FAST_D) return leaf_fast_d(v[OFF], v[OFF + 1]);
+    else if constexpr (LEAF == LEAF_PLAIN_D) return {v[OFF] + v[OFF + 1], 0.0};
     else return leaf_nn_d(v[OFF], v[OFF + 1]);
   } else {
     const NodeD l = lane_tree_d<LEAF, OFF, N / 2, E>(v);
     const NodeD r = lane_tree_d<LEAF, OFF + N / 2, N / 2, E>(v);
-    return comb_d<LEAF == LEAF_NN_D>(l, r);
+    return comb_d<LEAF == LEAF_PLAIN_D ? KD_PLAIN : (LEAF == LEAF_NN_D ? 1 : 0)>(l, r);
   }
 }
 
-template <int OFF, int N, int K, bool NN>
+template <int OFF, int N, int K, int NN>
 __device__ __forceinline__ NodeD node_tree_d(const NodeD (&nd)[K]) {
   if constexpr (N == 1) return nd[OFF];
   else return comb_d<NN>(node_tree_d<OFF, N / 2, K, NN>(nd), node_tree_d<OFF + N / 2, N / 2, K, NN>(nd));
@@ -135,9 +149,10 @@ __device__ __forceinline__ double dpp_d(double v) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-template <int CTRL>
+template <int CTRL, int NN = 0>
 __device__ __forceinline__ NodeD dpp_node_d(NodeD n) {
-  return {dpp_d<CTRL>(n.s), dpp_d<CTRL>(n.c)};
+  if constexpr (NN == KD_PLAIN) return {dpp_d<CTRL>(n.s), 0.0};  // a plain tree's carries are +0
+  else return {dpp_d<CTRL>(n.s), dpp_d<CTRL>(n.c)};
 }
 
 // A lane's double and its partner's (lane ^ XOR): both words of each copy go
@@ -155,34 +170,39 @@ __device__ __forceinline__ void swap_d(double v, double &a, double &b) {
                                      __builtin_bit_cast(unsigned, lb));
 }
 
-template <int XOR, bool NN>
+template <int XOR, int NN>
 __device__ __forceinline__ NodeD swap_level_d(NodeD n) {
   NodeD a, b;
   swap_d<XOR>(n.s, a.s, b.s);
-  swap_d<XOR>(n.c, a.c, b.c);
+  if constexpr (NN == KD_PLAIN) {
+    a.c = 0.0;
+    b.c = 0.0;
+  } else {
+    swap_d<XOR>(n.c, a.c, b.c);
+  }
   return comb_d<NN>(a, b);
 }
 
 // The six cross-lane levels (lane k holds range k); every lane ends with the
 // wave's node.  The mirrors reach the sibling because the lower lanes agree.
-template <bool NN>
+template <int NN>
 __device__ __forceinline__ NodeD wave_tree_d(NodeD n) {
-  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1>(n));
-  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2>(n));
-  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR>(n));
-  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1, NN>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2, NN>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR, NN>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR, NN>(n));
   n = swap_level_d<16, NN>(n);
   return swap_level_d<32, NN>(n);
 }
 
 // The first log2(S) of those levels: every lane ends with the node of its
 // aligned group of S lanes.
-template <bool NN, int S>
+template <int NN, int S>
 __device__ __forceinline__ NodeD seg_tree_d(NodeD n) {
-  if constexpr (S >= 2) n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1>(n));
-  if constexpr (S >= 4) n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2>(n));
-  if constexpr (S >= 8) n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR>(n));
-  if constexpr (S >= 16) n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR>(n));
+  if constexpr (S >= 2) n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1, NN>(n));
+  if constexpr (S >= 4) n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2, NN>(n));
+  if constexpr (S >= 8) n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR, NN>(n));
+  if constexpr (S >= 16) n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR, NN>(n));
   if constexpr (S >= 32) n = swap_level_d<16, NN>(n);
   if constexpr (S >= 64) n = swap_level_d<32, NN>(n);
   return n;
@@ -404,23 +424,23 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   }
 
   NodeD ny = {0.0, 0.0};
-  if (!empty) ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
+  if (!empty) ny = wave_tree_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
   // From four waves on, the tree over the wave nodes takes one node per lane
   // (lane l < W wave l's) and the first log2(W) cross-lane levels.
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
     if constexpr (W >= 4) {
-      const NodeD t = seg_tree_d<false, W>(lane < W ? slots[0][lane] : NodeD{0.0, 0.0});
+      const NodeD t = seg_tree_d<KD_PLAIN, W>(lane < W ? slots[0][lane] : NodeD{0.0, 0.0});
       ny = {readlane_d(t.s, 0), readlane_d(t.c, 0)};
     } else {
       NodeD t[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) t[i] = slots[0][i];
-      ny = node_tree_d<0, W, W, false>(t);
+      ny = node_tree_d<0, W, W, KD_PLAIN>(t);
     }
   }
-  const double m = root_value_d(ny) / (double)n;
+  const double m = root_value_kd<KD_PLAIN>(ny) / (double)n;
 
   NodeD nd = {0.0, 0.0}, nq = {0.0, 0.0};
   if (!empty) {
@@ -497,8 +517,8 @@ __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict
   const double x0 = p[0];
 #pragma unroll
   for (int i = 0; i < E; ++i) v[i] = (full || i < valid) ? v[i] - x0 : 0.0;
-  const NodeD ny = seg_tree_d<false, S>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
-  const double m = root_value_d(ny) / (double)n;
+  const NodeD ny = seg_tree_d<KD_PLAIN, S>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
+  const double m = root_value_kd<KD_PLAIN>(ny) / (double)n;
   NodeD nd, nq;
   if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
   else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
@@ -541,16 +561,16 @@ __global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restric
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0;
   }
-  NodeD ny = lane_tree_d<LEAF_FAST_D, 0, E, E>(v);
+  NodeD ny = lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v);
   sy[w][lane] = ny;
   __syncthreads();
   {
     NodeD nn[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nn[i] = sy[i][lane];
-    ny = node_tree_d<0, W, W, false>(nn);
+    ny = node_tree_d<0, W, W, KD_PLAIN>(nn);
   }
-  const double m = root_value_d(ny) / (double)R;
+  const double m = root_value_kd<KD_PLAIN>(ny) / (double)R;
   NodeD nd, nq;
   if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
   else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
@@ -602,7 +622,7 @@ struct SliceWsD {
 // The W wave nodes of a workgroup (every lane of wave w holds node w) ->
 // the workgroup's node, valid in thread 0 (and every thread after the
 // barrier reads of `slots`).
-template <int W, bool NN>
+template <int W, int NN>
 __device__ __forceinline__ NodeD block_tree_d(NodeD n, NodeD *slots, int w, int lane) {
   if (lane == 0) slots[w] = n;
   __syncthreads();
@@ -640,8 +660,8 @@ __global__ __launch_bounds__(64 * L64_W) void k_long_rows_d(const double *__rest
   const int64_t out = r * nch + c;
   if constexpr (PASS == 0) {
     NodeD ny = {0.0, 0.0};
-    if (!empty) ny = wave_tree_d<false>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v));
-    ny = block_tree_d<W, false>(ny, slots[0], w, lane);
+    if (!empty) ny = wave_tree_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
+    ny = block_tree_d<W, KD_PLAIN>(ny, slots[0], w, lane);
     if (threadIdx.x == 0) ws.ny[out] = ny;
   } else {
     const double m = ws.m[r];
@@ -663,7 +683,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_long_rows_d(const double *__rest
 
 // Tree over the nch chunk nodes of one row (256 threads of K nodes each,
 // padded with zero nodes to 256 * K: the padding changes no bit).
-template <bool NN, int K>
+template <int NN, int K>
 __device__ __forceinline__ NodeD top_tree_d(const NodeD *__restrict__ nodes, int64_t nch, NodeD *slots) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -685,8 +705,8 @@ __global__ __launch_bounds__(256) void k_long_top_d(const double *__restrict__ x
   __shared__ NodeD slots[2][4];
   const int64_t r = blockIdx.x;
   if constexpr (PASS == 0) {
-    const NodeD ny = top_tree_d<false, K>(ws.ny + r * nch, nch, slots[0]);
-    if (threadIdx.x == 0) ws.m[r] = root_value_d(ny) / (double)n;
+    const NodeD ny = top_tree_d<KD_PLAIN, K>(ws.ny + r * nch, nch, slots[0]);
+    if (threadIdx.x == 0) ws.m[r] = root_value_kd<KD_PLAIN>(ny) / (double)n;
   } else {
     const NodeD nd = top_tree_d<false, K>(ws.nd + r * nch, nch, slots[0]);
     const NodeD nq = top_tree_d<true, K>(ws.nq + r * nch, nch, slots[1]);
@@ -729,8 +749,9 @@ __device__ __forceinline__ void shift_cols_tile_d(double (&v)[V][E], const doubl
     for (int i = 0; i < E; ++i) v[k][i] = (full || i < valid) ? v[k][i] - x0[k] : 0.0;
 }
 
-// Tree over the nch <= C64_GROUP chunk nodes p[0], p[stride], ..., padded
-// with zero nodes to C64_GROUP (the padding changes no bit).
+// Tree of the local mean over the nch <= C64_GROUP y chunk nodes p[0],
+// p[stride], ..., padded with zero nodes to C64_GROUP (the padding changes no
+// bit).
 __device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, int64_t nch) {
   NodeD sub[C64_GROUP / 8];
 #pragma unroll
@@ -742,9 +763,9 @@ __device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, 
       const NodeD t = p[(idx < nch ? idx : nch - 1) * stride];
       nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
     }
-    sub[b] = node_tree_d<0, 8, 8, false>(nd);
+    sub[b] = node_tree_d<0, 8, 8, KD_PLAIN>(nd);
   }
-  return node_tree_d<0, C64_GROUP / 8, C64_GROUP / 8, false>(sub);
+  return node_tree_d<0, C64_GROUP / 8, C64_GROUP / 8, KD_PLAIN>(sub);
 }
 
 // G row groups per wave: lane L = q*G + g holds the V adjacent columns of
@@ -779,7 +800,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restric
   shift_cols_tile_d<V, E>(v, x0, wave_full, valid);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const NodeD nd = seg_tree_d<false, G>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k]));
+    const NodeD nd = seg_tree_d<KD_PLAIN, G>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v[k]));
     if (g == 0) s[w][k][q] = nd;
   }
   __syncthreads();
@@ -791,7 +812,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restric
       NodeD nn[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) nn[i] = s[i][k][qq];
-      ws.ny[j * C + col] = node_tree_d<0, W, W, false>(nn);
+      ws.ny[j * C + col] = node_tree_d<0, W, W, KD_PLAIN>(nn);
     }
   }
 }
@@ -814,7 +835,7 @@ __global__ __launch_bounds__(256) void k_cols_top_d(const double *__restrict__ x
   const bool colok = col < C;
   const int64_t cc = colok ? col : C - 1;
   auto tree = [&](const NodeD *p, auto nn) {
-    constexpr bool NN = decltype(nn)::value;
+    constexpr int NN = decltype(nn)::value;
     NodeD nd[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -825,8 +846,8 @@ __global__ __launch_bounds__(256) void k_cols_top_d(const double *__restrict__ x
     return seg_tree_d<NN, S>(node_tree_d<0, K, K, NN>(nd));
   };
   if constexpr (PASS == 0) {
-    const NodeD ny = tree(ws.ny + cc, std::false_type{});
-    if (sl == 0 && colok) ws.m[col] = root_value_d(ny) / (double)R;
+    const NodeD ny = tree(ws.ny + cc, std::integral_constant<int, KD_PLAIN>{});
+    if (sl == 0 && colok) ws.m[col] = root_value_kd<KD_PLAIN>(ny) / (double)R;
   } else {
     const NodeD nd = tree(ws.nd + cc, std::false_type{});
     const NodeD nq = tree(ws.nq + cc, std::true_type{});
@@ -851,7 +872,7 @@ __global__ __launch_bounds__(256) void k_cols_top_big_d(const double *__restrict
   if (col >= C) return;  // the whole wave
   const int64_t P = (int64_t)1 << log2p;
   auto tree = [&](const NodeD *p, auto nn) {
-    constexpr bool NN = decltype(nn)::value;
+    constexpr int NN = decltype(nn)::value;
     NodeD st[TOP_BIG_LEVELS_D];
 #pragma unroll
     for (int lv = 0; lv < TOP_BIG_LEVELS_D; ++lv) st[lv] = NodeD{0.0, 0.0};
@@ -885,8 +906,8 @@ __global__ __launch_bounds__(256) void k_cols_top_big_d(const double *__restrict
     return wave_tree_d<NN>(r);
   };
   if constexpr (PASS == 0) {
-    const NodeD ny = tree(ws.ny + col, std::false_type{});
-    if (lane == 0) ws.m[col] = root_value_d(ny) / (double)R;
+    const NodeD ny = tree(ws.ny + col, std::integral_constant<int, KD_PLAIN>{});
+    if (lane == 0) ws.m[col] = root_value_kd<KD_PLAIN>(ny) / (double)R;
   } else {
     const NodeD nd = tree(ws.nd + col, std::false_type{});
     const NodeD nq = tree(ws.nq + col, std::true_type{});
@@ -922,7 +943,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
       const int k = t / Q, qq = t % Q;  // column V*qq + k of the block, clamped like the loads
       const int64_t col = cb * NC + (int64_t)qq * V + k;
       const int64_t ccol = col < C ? col : C - 1;
-      sm[k][qq] = root_value_d(chunk_tree_1_d(ws.ny + ccol, C, nch)) / (double)R;
+      sm[k][qq] = root_value_kd<KD_PLAIN>(chunk_tree_1_d(ws.ny + ccol, C, nch)) / (double)R;
     }
     __syncthreads();
   }
@@ -998,7 +1019,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   shift_cols_tile_d<V, E>(v, x0, wave_full, valid);  // +0 past the last row
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const NodeD nd = seg_tree_d<false, G>(lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k]));
+    const NodeD nd = seg_tree_d<KD_PLAIN, G>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v[k]));
     if (g == 0) sd[w][k][q] = nd;
   }
   __syncthreads();
@@ -1008,7 +1029,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
     NodeD nn[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nn[i] = sd[i][tk][tq];
-    sm[tk][tq] = root_value_d(node_tree_d<0, W, W, false>(nn)) / (double)R;
+    sm[tk][tq] = root_value_kd<KD_PLAIN>(node_tree_d<0, W, W, KD_PLAIN>(nn)) / (double)R;
   }
   __syncthreads();
 #pragma unroll
@@ -1065,7 +1086,7 @@ __global__ __launch_bounds__(256) void k_cols_short_d(const double *__restrict__
     const double x0 = v[k][0];
 #pragma unroll
     for (int i = 0; i < E; ++i) v[k][i] = (i < valid) ? v[k][i] - x0 : 0.0;
-    const double m = root_value_d(lane_tree_d<LEAF_FAST_D, 0, E, E>(v[k])) / (double)R;
+    const double m = root_value_kd<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v[k])) / (double)R;
     NodeD nd, nq;
     lane_tree_dq_d<true, 0, E, E>(v[k], m, valid, nd, nq);
     finalize_d(nd, nq, x0, m, R, ddof, &var2[k], &mean2[k]);
@@ -1331,24 +1352,22 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     const bool vec = svh::aligned16(x) && (cols % 2 == 0);
     const dim3 grid((unsigned)rows);
 #define SV_ROWS64(E, W)                                                                                      \
-  do { /* rows in batches: a launch holds at most 2^32 - 1 work-items */                                   \
-    const int64_t batch = (int64_t)0xffffffffu / (64 * W);                                                   \
-    for (int64_t r0 = 0; r0 < rows; r0 += batch) {                                                           \
-      const int64_t nr = rows - r0 < batch ? rows - r0 : batch;                                              \
-      const double *xr = x + r0 * cols;                                                                      \
-      double *mr = mean_out ? mean_out + r0 : nullptr;                                                       \
-      if (vec) k_var_rows_f64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr); \
-      else k_var_rows_f64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr);   \
-    }                                                                                                        \
-  } while (0)
+  svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {                                             \
+    const double *xr = x + r0 * cols;                                                                        \
+    double *mr = mean_out ? mean_out + r0 : nullptr;                                                         \
+    if (vec) k_var_rows_f64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr); \
+    else k_var_rows_f64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr);   \
+  })
     if (n <= 512) {
       const int vw = (svh::aligned16(x) && cols % 2 == 0) ? 2 : 1;
-#define SV_SEG64(E, S)                                                                                        \
-  do {                                                                                                        \
-    const dim3 sgrid((unsigned)((rows + 4 * (64 / S) - 1) / (4 * (64 / S))));                                 \
-    if (vw == 2) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out); \
-    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);   \
-  } while (0)
+#define SV_SEG64(E, S)                                                                                  \
+  svh::in_batches(rows, 4 * (64 / S), 256, [&](int64_t r0, int64_t nr) {                                \
+    const dim3 sgrid((unsigned)((nr + 4 * (64 / S) - 1) / (4 * (64 / S))));                             \
+    const double *xr = x + r0 * cols;                                                                   \
+    double *vr = var_out + r0, *mr = mean_out ? mean_out + r0 : nullptr;                                \
+    if (vw == 2) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr); \
+    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr);         \
+  })
       if (n <= 4) SV_SEG64(4, 1);
       else if (n <= 8) SV_SEG64(8, 1);
       else if (n <= 16) SV_SEG64(16, 1);

@@ -25,6 +25,16 @@ __attribute__((visibility("hidden"))) const char *last_error();
 __attribute__((visibility("hidden"))) sv_status adn_set_tuning(const char *key, int64_t value, bool *handled);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A launch holds at most 2^32 - 1 work-items.  in_batches(total, per_block,
+// threads, fn) calls fn(first, count) over [0, total) in runs of whole blocks
+// (per_block items of `threads` work-items each), every run within the limit,
+// so that a launcher can advance its pointers by `first` items.
+template <class Fn>
+inline void in_batches(int64_t total, int64_t per_block, int64_t threads, Fn &&fn) {
+  const int64_t batch = ((int64_t)0xffffffffu / threads) * per_block;
+  for (int64_t s0 = 0; s0 < total; s0 += batch) fn(s0, total - s0 < batch ? total - s0 : batch);
+}
 inline bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 }  // namespace svh

@@ -20,6 +20,7 @@
 //                cross-wave ones is in-lane.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -81,7 +82,7 @@ namespace {
 
 // Combine the wave nodes of the W waves of a workgroup (wave w covers the
 // w-th consecutive range).  Every thread returns the workgroup's node.
-template <int W, bool NN>
+template <int W, int KIND>
 __device__ __forceinline__ Node block_tree(Node n, Node *slots, int w, int lane) {
   if constexpr (W == 1) {
     return n;
@@ -92,26 +93,15 @@ __device__ __forceinline__ Node block_tree(Node n, Node *slots, int w, int lane)
 #pragma unroll
     for (int i = 0; i < W; ++i) nd[i] = slots[i];
     __syncthreads();
-    if constexpr (NN) {
-      // pairwise over W nodes with the non-negative node
-      Node t[W];
-#pragma unroll
-      for (int i = 0; i < W; ++i) t[i] = nd[i];
-#pragma unroll
-      for (int len = W; len > 1; len >>= 1)
-#pragma unroll
-        for (int k = 0; k < len / 2; ++k) t[k] = sv::combine_nn(t[2 * k], t[2 * k + 1]);
-      return t[0];
-    } else {
-      return sv::node_tree<0, W, W>(nd);
-    }
+    return sv::node_tree<0, W, W, KIND>(nd);
   }
 }
 
 // Variants of the slice computation (the ablation rows of the method page's
 // §4, numbered as the C ABI's `variant`).  V_KERNEL is the method.
 enum Variant {
-  V_KERNEL = 0,           // shift + centring + two-term, compensated trees
+  V_KERNEL = 0,           // shift + centring + two-term; plain tree of y, compensated trees of d and d^2
+  V_COMP_Y = 1,           // the same with a compensated tree of y (the other reading of step 2)
   V_REFERENCE = 2,        // two-term formula: means as plain tree * fl(1/n), no shift
   V_NAIVE = 3,            // mean((x - mean(x))^2), means as plain tree * fl(1/n)
   V_SHIFT_PLAIN_NO2T = 4,
@@ -121,18 +111,23 @@ enum Variant {
 };
 template <int V>
 struct VariantFlags {
-  static constexpr bool shift = V == V_KERNEL || V == V_SHIFT_PLAIN_NO2T || V == V_SHIFT_PLAIN_2T ||
+  static constexpr bool shift = V == V_KERNEL || V == V_COMP_Y || V == V_SHIFT_PLAIN_NO2T || V == V_SHIFT_PLAIN_2T ||
                                 V == V_SHIFT_COMP_NO2T;
-  static constexpr bool comp = V == V_KERNEL || V == V_NOSHIFT_COMP_2T || V == V_SHIFT_COMP_NO2T;
-  static constexpr bool twoterm = V == V_KERNEL || V == V_REFERENCE || V == V_SHIFT_PLAIN_2T || V == V_NOSHIFT_COMP_2T;
+  static constexpr bool comp = V == V_KERNEL || V == V_COMP_Y || V == V_NOSHIFT_COMP_2T || V == V_SHIFT_COMP_NO2T;
+  static constexpr bool comp_y = V == V_COMP_Y;  // every other row keeps the kernel's plain tree of y
+  static constexpr bool twoterm = V == V_KERNEL || V == V_COMP_Y || V == V_REFERENCE || V == V_SHIFT_PLAIN_2T ||
+                                  V == V_NOSHIFT_COMP_2T;
   static constexpr bool recip = V == V_REFERENCE || V == V_NAIVE;
+  static constexpr int ykind = comp_y ? sv::NODE_TWOSUM : sv::NODE_PLAIN;
+  static constexpr int yleaf = comp_y ? sv::LEAF_FAST : sv::LEAF_PLAIN;
 };
 
-// The value of a slice sum: the compensated tree's root, or the plain tree
-// (the s part of the same nodes: s is formed as in a plain pairwise tree).
+// The value of a slice sum: the compensated tree's root, or the plain tree's
+// (the s part of the same nodes, formed as in a plain pairwise tree, and its
+// root rule fl(s + 0)).
 template <bool COMP>
 __device__ __forceinline__ float tree_value(Node n) {
-  return COMP ? sv::root_value(n) : n.s;
+  return COMP ? sv::root_value(n) : sv::root_value_k<sv::NODE_PLAIN>(n);
 }
 
 // m from the slice sum of y: a division by fl(n), or the product with
@@ -140,7 +135,7 @@ __device__ __forceinline__ float tree_value(Node n) {
 template <int V>
 __device__ __forceinline__ float local_mean(Node ny, int64_t n) {
   using F = VariantFlags<V>;
-  const float sy = tree_value<F::comp>(ny);
+  const float sy = sv::root_value_k<F::ykind>(ny);
   const float fn = (float)n;
   if constexpr (F::recip) {
     const float inv = 1.0f / fn;
@@ -460,8 +455,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
   }
   Node yr = sv::zero_node(), yi = sv::zero_node();
   if (!empty) {
-    yr = sv::wave_tree<sv::NODE_TWOSUM>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(re));
-    yi = sv::wave_tree<sv::NODE_TWOSUM>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(im));
+    yr = sv::wave_tree<sv::Y_KIND>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(re));
+    yi = sv::wave_tree<sv::Y_KIND>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(im));
   }
   // The tree over the waves' nodes: lane l < W takes wave l's real node,
   // lane W + l its imaginary node, and the first log2(W) cross-lane levels
@@ -473,12 +468,12 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
       slots[1][w] = yi;
     }
     __syncthreads();
-    const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 2 * W ? (&slots[0][0])[lane] : sv::zero_node());
+    const Node t = sv::seg_tree<sv::Y_KIND, W>(lane < 2 * W ? (&slots[0][0])[lane] : sv::zero_node());
     yr = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
     yi = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
   }
-  const float mr = sv::root_value(yr) / (float)n;
-  const float mi = sv::root_value(yi) / (float)n;
+  const float mr = sv::root_value_k<sv::Y_KIND>(yr) / (float)n;
+  const float mi = sv::root_value_k<sv::Y_KIND>(yi) / (float)n;
   Node dr = sv::zero_node(), qr = sv::zero_node(), di = sv::zero_node(), qi = sv::zero_node();
   if (!empty) {
     if (full) {
@@ -568,10 +563,10 @@ __global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restric
     re[i] = (full || i < valid) ? re[i] - x0r : 0.0f;
     im[i] = (full || i < valid) ? im[i] - x0i : 0.0f;
   }
-  const Node yr = sv::seg_tree<sv::NODE_TWOSUM, S>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(re));
-  const Node yi = sv::seg_tree<sv::NODE_TWOSUM, S>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(im));
-  const float mr = sv::root_value(yr) / (float)n;
-  const float mi = sv::root_value(yi) / (float)n;
+  const Node yr = sv::seg_tree<sv::Y_KIND, S>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(re));
+  const Node yi = sv::seg_tree<sv::Y_KIND, S>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(im));
+  const float mr = sv::root_value_k<sv::Y_KIND>(yr) / (float)n;
+  const float mi = sv::root_value_k<sv::Y_KIND>(yi) / (float)n;
   Node dr, qr, di, qi;
   if (full) {
     sv::lane_tree_dq<false, 0, E, E>(re, mr, E, dr, qr);
@@ -634,6 +629,112 @@ __global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
 
 // ------------------------------------------------------------------ variance, axis 1
 
+// Per-call constants of step 2 and step 4, formed on the host.  When fl(n)
+// is a power of two, x / fl(n) and x * rn with rn = 1 / fl(n) (exact) are the
+// same rounding of the same real number, so the kernels multiply; dfac is
+// the ddof factor fl(fl(n) / fl(max(n - ddof, 0))), a correctly rounded
+// division on the host as it would be on the device.
+struct StepConsts {
+  float fn;    // fl(n)
+  float rn;    // 1 / fl(n) when fl(n) is a power of two, else 0 (divide)
+  float dfac;  // the ddof factor (unused when ddof == 0)
+  int ddof_on; // ddof != 0
+};
+
+__device__ __forceinline__ float div_n(float a, const StepConsts &k) { return k.rn != 0.0f ? a * k.rn : a / k.fn; }
+
+// Step 4 from the roots of the d and d^2 trees: the two-term correction,
+// the NaN-propagating max with 0, the ddof rescale and the mean x0 + m.
+__device__ __forceinline__ void finalize_k(Node nd, Node nq, float x0, float m, const StepConsts &k, float *var_out,
+                                           float *mean_out) {
+  const float a = div_n(sv::root_value(nq), k);
+  const float b = div_n(sv::root_value(nd), k);
+  const float bb = b * b;
+  float v = a - bb;
+  v = (v != v) ? v : ((v > 0.0f) ? v : 0.0f);
+  if (k.ddof_on) v = v * k.dfac;
+  *var_out = v;
+  if (mean_out) *mean_out = x0 + m;
+}
+
+// Axis 1, rows that fill their power-of-two tile exactly (n = 64*E*W) and
+// start 16 bytes aligned: every wave is full, so there are no masks, clamped
+// loads or empty waves.  Lane L holds the E consecutive values of virtual
+// lane 2 (L mod 32) + L / 32 of its wave's range (the order in which the d
+// and d^2 trees share their cross-lane levels); the row stays in registers
+// from the y pass to the d pass, so HBM is read once.
+template <int E, int W>
+__global__ __launch_bounds__(64 * W) void k_var_rows_full(const float *__restrict__ x, int64_t ld, StepConsts k,
+                                                          float *__restrict__ var_out, float *__restrict__ mean_out) {
+  static_assert(E % 4 == 0 && W >= 1 && W <= 16, "tile of whole 16-byte groups, at most 16 waves");
+  __shared__ float ys[W];
+  __shared__ Node dqs[2][W];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
+  const float *__restrict__ p = x + row * ld;
+  const float *__restrict__ src = p + w * (64 * E) + sv::vlane_pair32(lane) * E;
+  float v[E];
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j) {
+    const float4 g = *reinterpret_cast<const float4 *>(src + 4 * j);
+    v[4 * j] = g.x; v[4 * j + 1] = g.y; v[4 * j + 2] = g.z; v[4 * j + 3] = g.w;
+  }
+  const float x0 = p[0];
+
+  // step 1: y = x - x0
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
+
+  // step 2: the plain tree of y, m = Sy / n
+  float sy = sv::wave_tree_p32<sv::Y_KIND>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(v)).s;
+  if constexpr (W > 1) {
+    if (lane == 0) ys[w] = sy;
+    __syncthreads();
+    Node t[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) t[i] = {ys[i], 0.0f};
+    sy = sv::node_tree<0, W, W, sv::Y_KIND>(t).s;
+  }
+  const float m = div_n(sy, k);
+
+  // step 3: Tree(d), Tree(d^2); lanes 0..31 end with the wave's d node,
+  // lanes 32..63 with its d^2 node
+  Node nd, nq;
+  sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
+  const Node ndq = sv::wave_tree_dq(nd, nq);
+  nd = {sv::readlane_f(ndq.s, 0), sv::readlane_f(ndq.c, 0)};
+  nq = {sv::readlane_f(ndq.s, 32), sv::readlane_f(ndq.c, 32)};
+  if constexpr (W > 1) {
+    if (lane == 0) {
+      dqs[0][w] = nd;
+      dqs[1][w] = nq;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    if constexpr (W >= 4) {
+      // lanes [0, W) the d nodes, [W, 2W) the d^2 nodes, and the first
+      // log2(W) cross-lane levels (TwoSum nodes: on non-negative operands
+      // the same exact error as the Fast2Sum form)
+      const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 2 * W ? (&dqs[0][0])[lane] : sv::zero_node());
+      nd = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
+      nq = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
+    } else {
+      Node td[W], tq[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        td[i] = dqs[0][i];
+        tq[i] = dqs[1][i];
+      }
+      nd = sv::node_tree<0, W, W>(td);
+      nq = sv::node_tree<0, W, W, sv::NODE_NN>(tq);
+    }
+  }
+
+  // step 4
+  if (lane == 0) finalize_k(nd, nq, x0, m, k, var_out + row, mean_out ? mean_out + row : nullptr);
+}
+
 template <int E, int W, bool VEC, int LOADP, bool NT, int V = V_KERNEL>
 __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out,
@@ -676,8 +777,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   // step 2: m = Tree(y) / n
   Node ny = sv::zero_node();
   if (!empty) {
-    ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree_p32<sv::NODE_TWOSUM>(ny);
+    ny = sv::lane_tree<F::yleaf, 0, E, E>(v);
+    ny = sv::wave_tree_p32<F::ykind>(ny);
   }
   // The launch may hold fewer than W waves (the ones the row reaches); the
   // tree's other wave nodes are (+0, +0).
@@ -689,13 +790,13 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
     if constexpr (W >= 4) {
-      const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < nw ? slots[0][lane] : sv::zero_node());
+      const Node t = sv::seg_tree<F::ykind, W>(lane < nw ? slots[0][lane] : sv::zero_node());
       ny = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
     } else {
       Node t[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) t[i] = i < nw ? slots[0][i] : sv::zero_node();
-      ny = sv::node_tree<0, W, W>(t);
+      ny = sv::node_tree<0, W, W, F::ykind>(t);
     }
   }
   const float m = local_mean<V>(ny, n);
@@ -800,160 +901,14 @@ __global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ 
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
   }
-  Node ny = sv::seg_tree<sv::NODE_TWOSUM, S>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v));
-  const float m = sv::root_value(ny) / (float)n;
+  Node ny = sv::seg_tree<sv::Y_KIND, S>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(v));
+  const float m = sv::root_value_k<sv::Y_KIND>(ny) / (float)n;
   Node nd, nq;
   if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
   else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
   nd = sv::seg_tree<sv::NODE_TWOSUM, S>(nd);
   nq = sv::seg_tree<sv::NODE_NN, S>(nq);
   if (l == 0 && rowok) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
-}
-
-// Axis 1, n <= 64*E: each wave owns R consecutive rows (one lane holds E
-// consecutive values of a row) and reduces row k while the loads of row k+1
-// are in flight, so HBM streaming and the three trees overlap.  The waves of
-// a workgroup are independent (no barrier).
-template <int E, int R, bool VEC, int LOADP, bool NT, int MINW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MINW, 8))) void k_var_rows_pipe(
-    const float *__restrict__ x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *__restrict__ var_out,
-    float *__restrict__ mean_out) {
-  using C = sv::Chunk<E, VEC, LOADP, NT>;
-  constexpr int W = 4;
-  constexpr int LPW = (LOADP == 0) ? sv::lds_floats_per_wave<E>() : 1;
-  __shared__ float lds[W * LPW];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int64_t r0 = ((int64_t)blockIdx.x * W + w) * R;
-  float *const my_lds = lds + w * LPW;
-  const bool full = (n == 64 * E);
-  const int64_t vl = n - (int64_t)lane * E;
-  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
-
-  // the buffer holds the raw loads of row r on entry and is reused in place
-  auto process = [&](float (&v)[E], int64_t r) {
-    if (r >= rows) return;
-    if constexpr (LOADP == 0) C::finish(v, my_lds, lane, v);
-    const float x0 = x[r * ld];
-    if (full) {
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
-    } else {
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
-    }
-    Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree<sv::NODE_TWOSUM>(ny);
-    const float m = sv::root_value(ny) / (float)n;
-    Node nd, nq;
-    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
-    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
-    nq = sv::wave_tree<sv::NODE_NN>(nq);
-    if (lane == 0) finalize(nd, nq, x0, m, n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
-  };
-  auto issue_row = [&](int64_t r, float (&v)[E]) { C::issue(x + r * ld, r < rows ? n : (int64_t)0, lane, v); };
-
-  float ra[E], rb[E];
-  issue_row(r0, ra);
-  if constexpr (R == 1) {
-    process(ra, r0);
-  } else {
-    static_assert(R % 2 == 0, "R is 1 or even");
-#pragma unroll 1
-    for (int k = 0; k < R; k += 2) {
-      issue_row(r0 + k + 1, rb);
-      process(ra, r0 + k);
-      if (k + 2 < R) issue_row(r0 + k + 2, ra);
-      process(rb, r0 + k + 1);
-    }
-  }
-}
-
-// Axis 1, rows of n <= 4096 values with n % 4 == 0 and 16-byte aligned rows:
-// the row's loads go straight from HBM into LDS (global_load_lds, 16 bytes
-// per lane and 1 KiB per instruction) without passing through registers.  A
-// wave owns R consecutive rows: it waits for row k in its LDS buffer, copies
-// it into registers, starts the DMA of row k+1 into the same buffer and then
-// reduces row k, so the next row streams in while the three trees run.  The
-// waves of a workgroup are independent.
-//
-// LDS row buffer: 16 blocks of 1 KiB (one DMA instruction each), each block
-// followed by 16 bytes of padding (260 floats per block).  Lane L reads the 64
-// consecutive values of virtual lane v(L) = 4*(L % 16) + L/16, which lie in
-// block L % 16 at offset 64*(L/16): 16 consecutive lanes then hit 16 distinct
-// 4-bank groups.  The cross-lane tree follows the virtual lane order.
-constexpr int DMA_BLK_F = 260;              // floats per 1 KiB block + padding
-constexpr int DMA_ROW_F = 16 * DMA_BLK_F;   // one row buffer (16,640 bytes)
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-template <int R, int W>
-__global__ __launch_bounds__(64 * W) void k_var_rows_dma(const float *__restrict__ x, int64_t rows, int64_t n,
-                                                         int64_t ld, int64_t ddof, float *__restrict__ var_out,
-                                                         float *__restrict__ mean_out) {
-  constexpr int E = 64;
-  __shared__ float lds[W][DMA_ROW_F];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int64_t r0 = ((int64_t)blockIdx.x * W + w) * R;
-  const int vl = 4 * (lane % 16) + lane / 16;  // virtual lane
-  const bool full = (n == 64 * E);
-  const int64_t vv = n - (int64_t)vl * E;
-  const int valid = vv < 0 ? 0 : (vv > E ? E : (int)vv);
-  float *const buf = lds[w];
-
-  // Start the DMA of row r (lanes past n load nothing).
-  auto dma_row = [&](int64_t r) {
-    const float *src = x + r * ld + 4 * lane;
-    if (full) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        __builtin_amdgcn_global_load_lds((glb_void_t *)(src + 256 * k), (lds_void_t *)(buf + k * DMA_BLK_F), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (256 * k + 4 * lane < n)
-          __builtin_amdgcn_global_load_lds((glb_void_t *)(src + 256 * k), (lds_void_t *)(buf + k * DMA_BLK_F), 16, 0,
-                                           0);
-    }
-  };
-
-  if (r0 < rows) dma_row(r0);
-#pragma unroll 1
-  for (int k = 0; k < R; ++k) {
-    const int64_t r = r0 + k;
-    if (r >= rows) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): row k is in LDS
-    float v[E];
-    const float *src = buf + (lane % 16) * DMA_BLK_F + (lane / 16) * 64;
-#pragma unroll
-    for (int j = 0; j < E / 4; ++j) {
-      const float4 t = *reinterpret_cast<const float4 *>(src + 4 * j);
-      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): read out before the buffer is refilled
-    if (k + 1 < R && r + 1 < rows) dma_row(r + 1);
-
-    const float x0 = x[r * ld];
-    if (full) {
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
-    } else {
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
-    }
-    Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree_vlane<sv::NODE_TWOSUM>(ny);
-    const float m = sv::root_value(ny) / (float)n;
-    Node nd, nq;
-    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
-    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = sv::wave_tree_vlane<sv::NODE_TWOSUM>(nd);
-    nq = sv::wave_tree_vlane<sv::NODE_NN>(nq);
-    if (lane == 0) finalize(nd, nq, x0, m, n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
-  }
 }
 
 // ------------------------------------------------------------------ variance, axis 0
@@ -1003,14 +958,14 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
     }
   }
 
-  Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
+  Node ny = sv::lane_tree<F::yleaf, 0, E, E>(v);
   sy[w][lane] = ny;
   __syncthreads();
   {
     Node nn[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nn[i] = sy[i][lane];
-    ny = sv::node_tree<0, W, W>(nn);
+    ny = sv::node_tree<0, W, W, F::ykind>(nn);
   }
   const float m = local_mean<V>(ny, R);
 
@@ -1141,7 +1096,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, 
   shift_cols_tile<V, E>(v, x0, wave_full, valid);
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const Node nd = sv::seg_tree<sv::NODE_TWOSUM, G>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k]));
+    const Node nd = sv::seg_tree<sv::Y_KIND, G>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(v[k]));
     if (g == 0) s[w][k][q] = nd;
   }
   __syncthreads();
@@ -1153,13 +1108,13 @@ __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, 
       Node nn[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) nn[i] = s[i][k][qq];
-      ws.ny[j * C + col] = sv::node_tree<0, W, W>(nn);
+      ws.ny[j * C + col] = sv::node_tree<0, W, W, sv::Y_KIND>(nn);
     }
   }
 }
 
-// Tree over the nch <= CC_GROUP chunk nodes p[0], p[stride], ... (one group,
-// nothing written back).
+// Tree of the local mean over the nch <= CC_GROUP y chunk nodes p[0],
+// p[stride], ... (one group, nothing written back).
 __device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int64_t nch) {
   Node sub[CC_GROUP / 8];
 #pragma unroll
@@ -1171,9 +1126,9 @@ __device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int6
       const Node t = p[(idx < nch ? idx : nch - 1) * stride];
       nd[k] = idx < nch ? t : sv::zero_node();
     }
-    sub[b] = sv::node_tree<0, 8, 8>(nd);
+    sub[b] = sv::node_tree<0, 8, 8, sv::Y_KIND>(nd);
   }
-  return sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8>(sub);
+  return sv::node_tree<0, CC_GROUP / 8, CC_GROUP / 8, sv::Y_KIND>(sub);
 }
 
 // The per-column trees over the chunk nodes with S lanes per column (64/S
@@ -1205,8 +1160,8 @@ __global__ __launch_bounds__(256) void k_cols_top(const float *__restrict__ x, i
     return sv::seg_tree<KIND, S>(sv::node_tree<0, K, K, KIND>(nd));
   };
   if constexpr (PASS == 0) {
-    const Node ny = tree(ws.ny + cc, std::integral_constant<int, sv::NODE_TWOSUM>{});
-    if (sl == 0 && colok) ws.m[col] = sv::root_value(ny) / (float)R;
+    const Node ny = tree(ws.ny + cc, std::integral_constant<int, sv::Y_KIND>{});
+    if (sl == 0 && colok) ws.m[col] = sv::root_value_k<sv::Y_KIND>(ny) / (float)R;
   } else {
     const Node nd = tree(ws.nd + cc, std::integral_constant<int, sv::NODE_TWOSUM>{});
     const Node nq = tree(ws.nq + cc, std::integral_constant<int, sv::NODE_NN>{});
@@ -1266,8 +1221,8 @@ __global__ __launch_bounds__(256) void k_cols_top_big(const float *__restrict__ 
     return sv::wave_tree<KIND>(r);
   };
   if constexpr (PASS == 0) {
-    const Node ny = tree(ws.ny + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
-    if (lane == 0) ws.m[col] = sv::root_value(ny) / (float)R;
+    const Node ny = tree(ws.ny + col, std::integral_constant<int, sv::Y_KIND>{});
+    if (lane == 0) ws.m[col] = sv::root_value_k<sv::Y_KIND>(ny) / (float)R;
   } else {
     const Node nd = tree(ws.nd + col, std::integral_constant<int, sv::NODE_TWOSUM>{});
     const Node nq = tree(ws.nq + col, std::integral_constant<int, sv::NODE_NN>{});
@@ -1307,7 +1262,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
       const int k = t / Q, qq = t % Q;  // column V*qq + k of the block, clamped like the loads
       const int64_t col = cb * NC + (int64_t)qq * V + k;
       const int64_t ccol = col < C ? col : C - 1;
-      sm[k][qq] = sv::root_value(chunk_tree_1(ws.ny + ccol, C, nch)) / (float)R;
+      sm[k][qq] = sv::root_value_k<sv::Y_KIND>(chunk_tree_1(ws.ny + ccol, C, nch)) / (float)R;
     }
     __syncthreads();
   }
@@ -1384,7 +1339,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   shift_cols_tile<V, E>(v, x0, wave_full, valid);  // +0 past the last row
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    const Node nd = sv::seg_tree<sv::NODE_TWOSUM, G>(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k]));
+    const Node nd = sv::seg_tree<sv::Y_KIND, G>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(v[k]));
     if (g == 0) sd[w][k][q] = nd;
   }
   __syncthreads();
@@ -1394,7 +1349,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
     Node nn[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) nn[i] = sd[i][tk][tq];
-    sm[tk][tq] = sv::root_value(sv::node_tree<0, W, W>(nn)) / (float)R;
+    sm[tk][tq] = sv::root_value_k<sv::Y_KIND>(sv::node_tree<0, W, W, sv::Y_KIND>(nn)) / (float)R;
   }
   __syncthreads();
 #pragma unroll
@@ -1475,9 +1430,9 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
   }
   const int64_t out = r * nch + c;
   if constexpr (PASS == 0) {
-    Node ny = sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v);
-    ny = sv::wave_tree<sv::NODE_TWOSUM>(ny);
-    ny = block_tree<W, false>(ny, slots[0], w, lane);
+    Node ny = sv::lane_tree<sv::Y_LEAF, 0, E, E>(v);
+    ny = sv::wave_tree<sv::Y_KIND>(ny);
+    ny = block_tree<W, sv::Y_KIND>(ny, slots[0], w, lane);
     if (threadIdx.x == 0) ws.ny[out] = ny;
   } else {
     const float m = ws.m[r];
@@ -1486,8 +1441,8 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
     else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
     nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
     nq = sv::wave_tree<sv::NODE_NN>(nq);
-    nd = block_tree<W, false>(nd, slots[0], w, lane);
-    nq = block_tree<W, true>(nq, slots[1], w, lane);
+    nd = block_tree<W, sv::NODE_TWOSUM>(nd, slots[0], w, lane);
+    nq = block_tree<W, sv::NODE_NN>(nq, slots[1], w, lane);
     if (threadIdx.x == 0) {
       ws.nd[out] = nd;
       ws.nq[out] = nq;
@@ -1497,9 +1452,8 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
 
 // Tree over the nch chunk nodes of one slice (one workgroup per slice), the
 // chunk nodes padded with zeros to 256 * K.
-template <bool NN, int K>
+template <int KIND, int K>
 __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t nch, Node *slots) {
-  constexpr int KIND = NN ? sv::NODE_NN : sv::NODE_TWOSUM;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   Node nd[K];
@@ -1511,7 +1465,7 @@ __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t
   }
   Node r = sv::node_tree<0, K, K, KIND>(nd);
   r = sv::wave_tree<KIND>(r);
-  return block_tree<4, NN>(r, slots, w, lane);
+  return block_tree<4, KIND>(r, slots, w, lane);
 }
 
 // PASS 0: m = Tree(y) / n.  PASS 1: the top trees of d and d^2 and step 4.
@@ -1524,11 +1478,11 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
   __shared__ Node slots[2][4];
   const int64_t sl = blockIdx.x;
   if constexpr (PASS == 0) {
-    const Node ny = top_tree<false, K>(ws.ny + sl * nch, nch, slots[0]);
-    if (threadIdx.x == 0) ws.m[sl] = sv::root_value(ny) / (float)n;
+    const Node ny = top_tree<sv::Y_KIND, K>(ws.ny + sl * nch, nch, slots[0]);
+    if (threadIdx.x == 0) ws.m[sl] = sv::root_value_k<sv::Y_KIND>(ny) / (float)n;
   } else {
-    const Node nd = top_tree<false, K>(ws.nd + sl * nch, nch, slots[0]);
-    const Node nq = top_tree<true, K>(ws.nq + sl * nch, nch, slots[1]);
+    const Node nd = top_tree<sv::NODE_TWOSUM, K>(ws.nd + sl * nch, nch, slots[0]);
+    const Node nq = top_tree<sv::NODE_NN, K>(ws.nq + sl * nch, nch, slots[1]);
     if (threadIdx.x == 0)
       finalize(nd, nq, x[sl * sstride], ws.m[sl], n, ddof, var_out + sl, mean_out ? mean_out + sl : nullptr);
   }
@@ -1538,7 +1492,9 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
 
 constexpr int64_t C64_FUSED_MAX_N = 32768;  // complex rows reduced in one pass (k_var_rows_c64)
 
-// Launch-geometry tuning (never changes a result bit).
+// Launch-geometry tuning (never changes a result bit).  Each host thread has
+// its own settings: sv_set_tuning on one thread leaves the calls of every
+// other thread alone.
 struct Tuning {
   int sum_load_path = 0;      // 0: coalesced loads + LDS transpose, 1: per-lane contiguous loads
   int sum_nt = 1;             // non-temporal loads of the summed input
@@ -1547,9 +1503,7 @@ struct Tuning {
   int64_t sum_blocks = 8192;  // target workgroup count of the tree sum
   int var_load_path = 1;      // as sum_load_path, for the row-variance kernel
   int var_nt = 0;             // non-temporal loads in the row-variance kernel
-  int var_rows_per_wave = 1;  // rows a wave pipelines (1 or 2) for 1024 < n <= 4096
   int var_split = 0;          // waves per 4096 values of a row of 1025..16384 values (1, 2, 4, 8; 0 auto)
-  int var_dma_rows = 0;       // rows per wave of the LDS-DMA row kernel (0 = off, 2, 4, 8)
   int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
   int var_cols_single_max = 1024;  // axis 0: rows up to which one workgroup holds a column tile (<= 1024)
   int var_cols_waves = 16;    // axis 0, chunked: waves per workgroup (4, 8, 16); chunks of 16 * waves rows
@@ -1559,8 +1513,21 @@ struct Tuning {
   int var_cols_short = 1;     // axis 0, columns of <= 15 rows: 1 four columns per lane, 0 the lane kernel
   int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
   int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
+  int var_full_rows = 1;      // rows that fill their tile exactly take the kernel without masks (0: the general one)
 };
-Tuning g_tune;
+thread_local Tuning g_tune;
+
+// The per-call constants of steps 2 and 4 (see StepConsts).
+StepConsts step_consts(int64_t n, int64_t ddof) {
+  StepConsts k;
+  k.fn = (float)n;
+  int ex = 0;
+  k.rn = (n > 0 && frexpf(k.fn, &ex) == 0.5f) ? 1.0f / k.fn : 0.0f;
+  k.ddof_on = ddof != 0;
+  const int64_t den = n - ddof < 0 ? 0 : n - ddof;
+  k.dfac = ddof != 0 ? k.fn / (float)den : 1.0f;
+  return k;
+}
 
 constexpr int64_t SUM_MAX_N = 1LL << 36;
 constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
@@ -1804,18 +1771,26 @@ void launch_sum_e(bool vec, const float *x, int64_t n, const SumPlan &p, Node *p
 template <int E, int W, bool VEC, int LOADP, bool NT>
 void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
                    hipStream_t st) {
+  if constexpr (VEC && LOADP == 1 && !NT) {
+    // rows that fill the tile exactly: the kernel without masks
+    if (n == 64LL * E * W && g_tune.var_full_rows && !g_tune.var_lds_pad && !g_tune.var_xcd) {
+      const StepConsts k = step_consts(n, ddof);
+      svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {
+        k_var_rows_full<E, W><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(x + r0 * ld, ld, k, var + r0,
+                                                                           mean ? mean + r0 : nullptr);
+      });
+      return;
+    }
+  }
   // only the waves the row reaches (the tree pads the others with zero
   // nodes); var_lds_pad: unused dynamic LDS per workgroup, a cap on resident
   // waves
   const int64_t reach = (n + 64 * E - 1) / (64 * E);
   const int waves = reach < W ? (int)reach : W;
-  // a launch holds at most 2^32 - 1 work-items: rows in batches
-  const int64_t batch = (int64_t)0xffffffffu / (64 * waves);
-  for (int64_t r0 = 0; r0 < rows; r0 += batch) {
-    const int64_t nr = rows - r0 < batch ? rows - r0 : batch;
+  svh::in_batches(rows, 1, 64 * waves, [&](int64_t r0, int64_t nr) {
     k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)nr), dim3(64 * waves), (size_t)g_tune.var_lds_pad, st>>>(
         x + r0 * ld, n, ld, ddof, var + r0, mean ? mean + r0 : nullptr, g_tune.var_xcd);
-  }
+  });
 }
 
 // A row shared by W waves of E values per lane; 16-byte loads follow
@@ -1864,10 +1839,14 @@ template <int E, int S>
 void launch_seg_t(int vw, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                   float *mean, hipStream_t st) {
   constexpr int RPB = 4 * (64 / S);  // rows per workgroup
-  const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
-  if (vw == 4) k_var_rows_seg<E, S, 4><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
-  else if (vw == 2) k_var_rows_seg<E, S, 2><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
-  else k_var_rows_seg<E, S, 1><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
+  svh::in_batches(rows, RPB, 256, [&](int64_t r0, int64_t nr) {
+    const dim3 grid((unsigned)((nr + RPB - 1) / RPB)), block(256);
+    const float *xr = x + r0 * ld;
+    float *vr = var + r0, *mr = mean ? mean + r0 : nullptr;
+    if (vw == 4) k_var_rows_seg<E, S, 4><<<grid, block, 0, st>>>(xr, nr, n, ld, ddof, vr, mr);
+    else if (vw == 2) k_var_rows_seg<E, S, 2><<<grid, block, 0, st>>>(xr, nr, n, ld, ddof, vr, mr);
+    else k_var_rows_seg<E, S, 1><<<grid, block, 0, st>>>(xr, nr, n, ld, ddof, vr, mr);
+  });
 }
 
 // Short rows: E values per lane (4, 8 or 16) and S lanes per row with S*E
@@ -1939,30 +1918,6 @@ void launch_rows_tile(bool vec, const float *x, int64_t rows, int64_t n, int64_t
   }
 }
 
-template <int R, bool VEC, int LOADP, bool NT>
-void launch_pipe_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
-                   hipStream_t st) {
-  const int64_t waves = (rows + R - 1) / R;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  k_var_rows_pipe<64, R, VEC, LOADP, NT, 2><<<grid, block, 0, st>>>(x, rows, n, ld, ddof, var, mean);
-}
-
-template <int R>
-void launch_pipe_r(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
-                   float *mean, hipStream_t st) {
-  const int sel = (vec ? 4 : 0) + (g_tune.var_load_path != 0 ? 2 : 0) + (g_tune.var_nt ? 1 : 0);
-  switch (sel) {
-    case 0: launch_pipe_t<R, false, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
-    case 1: launch_pipe_t<R, false, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
-    case 2: launch_pipe_t<R, false, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
-    case 3: launch_pipe_t<R, false, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
-    case 4: launch_pipe_t<R, true, 0, false>(x, rows, n, ld, ddof, var, mean, st); break;
-    case 5: launch_pipe_t<R, true, 0, true>(x, rows, n, ld, ddof, var, mean, st); break;
-    case 6: launch_pipe_t<R, true, 1, false>(x, rows, n, ld, ddof, var, mean, st); break;
-    default: launch_pipe_t<R, true, 1, true>(x, rows, n, ld, ddof, var, mean, st); break;
-  }
-}
-
 // Axis 0, short columns (R <= E rows, E <= 16, R < 16): each lane owns four adjacent
 // columns (one 16-byte load per row, 16-byte aligned base and a width
 // divisible by 4) and all three trees are in-lane: no cross-lane levels, no
@@ -1989,7 +1944,7 @@ __global__ __launch_bounds__(256) void k_cols_short(const float *__restrict__ x,
     const float x0 = v[k][0];
 #pragma unroll
     for (int i = 0; i < E; ++i) v[k][i] = (i < valid) ? v[k][i] - x0 : 0.0f;
-    const float m = sv::root_value(sv::lane_tree<sv::LEAF_FAST, 0, E, E>(v[k])) / (float)R;
+    const float m = sv::root_value_k<sv::Y_KIND>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(v[k])) / (float)R;
     Node nd, nq;
     sv::lane_tree_dq<true, 0, E, E>(v[k], m, valid, nd, nq);
     finalize(nd, nq, x0, m, R, ddof, &var4[k], &mean4[k]);
@@ -2028,12 +1983,13 @@ void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t co
                     float *mean, hipStream_t st) {
   if (ax1) {
     const int64_t n = cols;
-    const dim3 grid((unsigned)rows);
-#define SV_ROWS(E, W)                                                                                 \
-  do {                                                                                                \
-    if (vec) k_var_rows<E, W, true, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean, 0); \
-    else k_var_rows<E, W, false, 1, false, V><<<grid, dim3(64 * W), 0, st>>>(x, n, cols, ddof, var, mean, 0);   \
-  } while (0)
+#define SV_ROWS(E, W)                                                                                   \
+  svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {                                        \
+    const float *xr = x + r0 * cols;                                                                    \
+    float *vr = var + r0, *mr = mean ? mean + r0 : nullptr;                                             \
+    if (vec) k_var_rows<E, W, true, 1, false, V><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, vr, mr, 0); \
+    else k_var_rows<E, W, false, 1, false, V><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, vr, mr, 0);   \
+  })
     if (n <= 256) SV_ROWS(4, 1);
     else if (n <= 1024) SV_ROWS(16, 1);
     else if (n <= 4096) SV_ROWS(32, 2);  // the default geometry of the main kernel
@@ -2210,18 +2166,7 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     if (n <= SEG_MAX_N && g_tune.var_short_rows) launch_rows_seg(x, rows, n, cols, ddof, var_out, mean_out, st);
     else if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
     else if (n <= 1024) launch_rows_ew<16, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    else if (n <= 4096 && vec && g_tune.var_dma_rows > 0) {
-      const int R = g_tune.var_dma_rows;
-      const int64_t waves = (rows + R - 1) / R;
-      const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-      if (R == 2) k_var_rows_dma<2, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
-      else if (R == 4) k_var_rows_dma<4, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
-      else k_var_rows_dma<8, 4><<<grid, block, 0, st>>>(x, rows, n, cols, ddof, var_out, mean_out);
-    } else if (n <= 4096 && g_tune.var_rows_per_wave > 1) {
-      launch_pipe_r<2>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    } else {
-      launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    }
+    else launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
   } else {
     // columns of at most 15 rows: four columns per lane, every tree in-lane
     // (at 16 rows the lane kernel's lanes hold exactly 16: [16, 1000000] 12.7
@@ -2260,8 +2205,9 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
   if (axis != 0 && axis != 1 && axis != -1 && axis != -2)
     return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: axis %d not in {0, 1, -1, -2}", axis);
   if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: ddof = %lld < 0", (long long)ddof);
-  if (variant != V_KERNEL && variant != V_REFERENCE && variant != V_NAIVE && variant != V_SHIFT_PLAIN_NO2T &&
-      variant != V_SHIFT_PLAIN_2T && variant != V_NOSHIFT_COMP_2T && variant != V_SHIFT_COMP_NO2T)
+  if (variant != V_KERNEL && variant != V_COMP_Y && variant != V_REFERENCE && variant != V_NAIVE &&
+      variant != V_SHIFT_PLAIN_NO2T && variant != V_SHIFT_PLAIN_2T && variant != V_NOSHIFT_COMP_2T &&
+      variant != V_SHIFT_COMP_NO2T)
     return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: unknown variant %d", variant);
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
@@ -2285,6 +2231,7 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
   const bool vec = aligned16(x) && (cols % 4 == 0);
   switch (variant) {
     case V_KERNEL: launch_variant<V_KERNEL>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_COMP_Y: launch_variant<V_COMP_Y>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
     case V_REFERENCE: launch_variant<V_REFERENCE>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
     case V_NAIVE: launch_variant<V_NAIVE>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
     case V_SHIFT_PLAIN_NO2T: launch_variant<V_SHIFT_PLAIN_NO2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
@@ -2349,26 +2296,23 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     }
     // rows start 16-byte aligned when z is and cols is even
     const bool vec = aligned16(z) && (cols % 2 == 0);
-    const dim3 grid((unsigned)rows);
 #define SV_ROWS_C64(E, W)                                                                                 \
-  do { /* rows in batches: a launch holds at most 2^32 - 1 work-items */                              \
-    const int64_t batch = (int64_t)0xffffffffu / (64 * W);                                              \
-    for (int64_t r0 = 0; r0 < rows; r0 += batch) {                                                      \
-      const int64_t nr = rows - r0 < batch ? rows - r0 : batch;                                         \
-      const float *zr = z + 2 * r0 * cols;                                                              \
-      float *mr = mean_out ? mean_out + 2 * r0 : nullptr;                                               \
-      if (vec) k_var_rows_c64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr); \
-      else k_var_rows_c64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr);   \
-    }                                                                                                   \
-  } while (0)
+  svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {                                        \
+    const float *zr = z + 2 * r0 * cols;                                                                \
+    float *mr = mean_out ? mean_out + 2 * r0 : nullptr;                                                 \
+    if (vec) k_var_rows_c64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr); \
+    else k_var_rows_c64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr);   \
+  })
     if (cols <= SEG_MAX_N && g_tune.var_short_rows) {
       const int vw2 = vec ? 2 : 1;
-#define SV_SEG_C64(E, S)                                                                                          \
-  do {                                                                                                            \
-    const dim3 sgrid((unsigned)((rows + 4 * (64 / S) - 1) / (4 * (64 / S))));                                     \
-    if (vw2 == 2) k_var_rows_c64_seg<E, S, 2><<<sgrid, dim3(256), 0, st>>>(z, rows, cols, ddof, var_out, mean_out); \
-    else k_var_rows_c64_seg<E, S, 1><<<sgrid, dim3(256), 0, st>>>(z, rows, cols, ddof, var_out, mean_out);       \
-  } while (0)
+#define SV_SEG_C64(E, S)                                                                                \
+  svh::in_batches(rows, 4 * (64 / S), 256, [&](int64_t r0, int64_t nr) {                                \
+    const dim3 sgrid((unsigned)((nr + 4 * (64 / S) - 1) / (4 * (64 / S))));                             \
+    const float *zr = z + 2 * r0 * cols;                                                                \
+    float *vr = var_out + r0, *mr = mean_out ? mean_out + 2 * r0 : nullptr;                             \
+    if (vw2 == 2) k_var_rows_c64_seg<E, S, 2><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, ddof, vr, mr); \
+    else k_var_rows_c64_seg<E, S, 1><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, ddof, vr, mr);         \
+  })
       if (cols <= 4) SV_SEG_C64(4, 1);
       else if (cols <= 8) SV_SEG_C64(8, 1);
       else if (cols <= 16) SV_SEG_C64(16, 1);
@@ -2467,6 +2411,7 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "sum_xcd") == 0) return flag(&g_tune.sum_xcd);
+  if (strcmp(key, "var_full_rows") == 0) return flag(&g_tune.var_full_rows);
   if (strcmp(key, "var_xcd") == 0) return flag(&g_tune.var_xcd);
   if (strcmp(key, "var_lds_pad") == 0) {
     if (value < 0 || value > 65536) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_lds_pad must be in [0, 65536]");
@@ -2477,18 +2422,6 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_split must be 0, 1, 2, 4 or 8");
     g_tune.var_split = (int)value;
-    return ok();
-  }
-  if (strcmp(key, "var_rows_per_wave") == 0) {
-    if (value != 1 && value != 2)
-      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_rows_per_wave must be 1 or 2");
-    g_tune.var_rows_per_wave = (int)value;
-    return ok();
-  }
-  if (strcmp(key, "var_dma_rows") == 0) {
-    if (value != 0 && value != 2 && value != 4 && value != 8)
-      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_dma_rows must be 0, 2, 4 or 8");
-    g_tune.var_dma_rows = (int)value;
     return ok();
   }
   if (strcmp(key, "sum_e") == 0) {

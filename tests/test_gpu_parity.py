@@ -53,8 +53,8 @@ VAR_GEOMETRIES = {
     "xcd_contiguous": {"var_xcd": 1},
     "xcd_contiguous_split1": {"var_xcd": 1, "var_split": 1},
     "short_rows_one_per_workgroup": {"var_short_rows": 0},
-    "pipelined_rows2": {"var_rows_per_wave": 2},
-    "pipelined_rows2_lds": {"var_rows_per_wave": 2, "var_load_path": 0},
+    "general_kernel_for_full_tiles": {"var_full_rows": 0},
+    "general_kernel_split1": {"var_full_rows": 0, "var_split": 1},
 }
 
 # Axis-0 paths: one workgroup per column tile (rows up to var_cols_single_max)
@@ -264,13 +264,14 @@ def check_var(torch_dev, a, axis, ddof=0):
     return v
 
 
-def test_variance_page_datasets(torch_dev, var_geometry):
+@pytest.mark.parametrize("ddof", [0, 1])
+def test_variance_page_datasets(torch_dev, var_geometry, ddof):
     for name, a, axis, _ in W.datasets_d1_d4():
-        v = check_var(torch_dev, a, axis)
-        v64 = oracle.var_f64(a, axis=axis)
-        er = oracle.max_rel_err(oracle.variance(a, axis=axis, method=oracle.METHOD_REFERENCE)[0], v64)
+        v = check_var(torch_dev, a, axis, ddof)
+        v64 = oracle.var_f64(a, axis=axis, ddof=ddof)
+        er = oracle.max_rel_err(oracle.variance(a, axis=axis, ddof=ddof, method=oracle.METHOD_REFERENCE)[0], v64)
         ek = oracle.max_rel_err(v, v64)
-        assert ek <= 4 * U and ek <= er, (name, ek, er)
+        assert ek <= 4 * U and ek <= er, (name, ddof, ek, er)
 
 
 @pytest.mark.parametrize("c", [1.0, 1e10, 1e30, 1e38])
@@ -284,10 +285,14 @@ def test_variance_constants_exact_zero(torch_dev, c, ddof):
 
 
 def test_variance_4096_square(torch_dev, var_geometry):
+    # the timing shape: bit-exact, within 4 * 2^-24 of the float64 variance
+    # and no worse than the two-term reference formula
     a = W.c4_matrix()
     v = check_var(torch_dev, a, 1)
     v64 = oracle.var_f64(a, axis=1)
-    assert oracle.max_rel_err(v, v64) <= 4 * U
+    ek = oracle.max_rel_err(v, v64)
+    er = oracle.max_rel_err(oracle.variance(a, axis=1, method=oracle.METHOD_REFERENCE)[0], v64)
+    assert ek <= 4 * U and ek <= er, (ek, er)
 
 
 ROW_NS = [1, 2, 3, 5, 64, 255, 256, 257, 1000, 1023, 1024, 1025, 1500, 2048, 2049, 4095, 4096, 4097, 6000, 8192,
@@ -531,6 +536,23 @@ def test_variance_single_long_row(torch_dev):
     assert v[0] == 0.0
 
 
+@pytest.mark.parametrize("n", [(1 << 24) + 1, (1 << 25) + 7])
+@pytest.mark.parametrize("axis", [1, 0])
+def test_variance_slices_beyond_2_24(torch_dev, n, axis):
+    # Step 2 divides by fl(n): above 2^24 it rounds (2^24 + 1 -> 2^24, and
+    # 2^25 + 7 -> 2^25 + 8).  The axis-1 slice of 2^25 + 7 values has 2049
+    # chunks, so its top trees take 32 chunk nodes per thread; the axis-0
+    # column takes the per-column chunk trees of one column.
+    assert float(np.float32(n)) != n
+    rng = np.random.default_rng(n % 1000)
+    a = rng.normal(3e3, 2, n).astype(np.float32)
+    a = a[None, :] if axis == 1 else a[:, None]
+    for ddof in (0, 1):
+        v = check_var(torch_dev, a, axis, ddof)
+        v64 = oracle.var_f64(a, axis=axis, ddof=ddof)
+        assert oracle.max_rel_err(v, v64) <= 4 * U
+
+
 # ------------------------------------------------------------------ complex64
 
 def gpu_var_c64(torch_dev, z, axis, ddof=0):
@@ -605,18 +627,8 @@ def test_complex_then_sum_share_nothing(torch_dev):
 
 # ------------------------------------------------------------------ ablation variants
 
-GPU_VARIANTS = {"kernel": 0, "reference": 2, "naive": 3, "shift_plain_no2t": 4, "shift_plain_2t": 5,
-                "noshift_comp_2t": 6, "shift_comp_no2t": 7}
-
-
-def same_bits_or_zero(a, b):
-    # the plain trees of unshifted data may differ in the sign of an exact
-    # zero (a larger zero padding turns -0 into +0); everything else is exact
-    a = np.asarray(a, np.float32).ravel()
-    b = np.asarray(b, np.float32).ravel()
-    both_zero = (a == 0) & (b == 0)
-    nan = np.isnan(a) & np.isnan(b)
-    return bool(np.all(nan | both_zero | (a.view(np.uint32) == b.view(np.uint32))))
+GPU_VARIANTS = {"kernel": 0, "kernel_comp_y": 1, "reference": 2, "naive": 3, "shift_plain_no2t": 4,
+                "shift_plain_2t": 5, "noshift_comp_2t": 6, "shift_comp_no2t": 7}
 
 
 @pytest.mark.parametrize("name", list(GPU_VARIANTS))
@@ -630,15 +642,17 @@ def test_variants_against_oracle(torch_dev, name):
     cases += [(rng.normal(1e4, 1, (9, 4096)).astype(np.float32), 1), (rng.normal(0, 3, (5, 10000)).astype(np.float32), 1),
               (rng.normal(-5, 1, (700, 70)).astype(np.float32), 0), (W.adversarial_values(6 * 300, code).reshape(6, 300), 1),
               (np.full((1, 3), np.float32(1e38)), 1), (W.constant(1e30), 0),
-              (rng.normal(7, 2, (4, 1500)).astype(np.float32), 1)]  # a wave wholly past the row
+              (rng.normal(7, 2, (4, 1500)).astype(np.float32), 1),  # a wave wholly past the row
+              (np.full((3, 5), np.float32(-0.0)), 1), (np.full((5, 3), np.float32(-0.0)), 0),  # all -0 slices
+              (np.array([[0.0, 1.0, 2.0 ** 24, 1.0]], np.float32), 1)]  # separates the two local means
     for a, ax in cases:
         for ddof in (0, 1):
             t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
             v, m = sv.var_variant(t, code, dim=ax, ddof=ddof, return_mean=True)
             torch.cuda.synchronize()
             ov, om = oracle.variance(a, axis=ax, ddof=ddof, method=code)
-            assert same_bits_or_zero(v.cpu().numpy(), ov), (name, a.shape, ax, ddof)
-            assert same_bits_or_zero(m.cpu().numpy(), om), (name, a.shape, ax, ddof)
+            assert same_bits(v.cpu().numpy(), ov), (name, a.shape, ax, ddof)
+            assert same_bits(m.cpu().numpy(), om), (name, a.shape, ax, ddof)
 
 
 def test_variant_zero_matches_the_main_entry_point(torch_dev):
