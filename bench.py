@@ -18,6 +18,10 @@ host as a reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --calibrate-copy     (a plain 400 MB copy, for counter scaling)
+       python bench.py --only KERNEL [--steps K] [--warmup W]
+                                            (K launches of one kernel on the same inputs,
+                                             for profiler runs: variance, variance_axis0,
+                                             sum, adn, read)
 """
 from __future__ import annotations
 
@@ -133,6 +137,70 @@ def cpu_oracle_all_cores(c4_host, c5_host):
             "sample": f"full workload x {reps} reps, {t_total:.1f} s, C oracle on {cores} threads"}
 
 
+def only(kernel, steps, warmup):
+    """K launches of one kernel on the benchmark's inputs (after W untimed
+    ones), nothing else: the command the committed profiles are taken with."""
+    import torch
+
+    import stable_variance_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    L = sv.capi()
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(L.sv_last_error_message().decode())
+
+    if kernel in ("variance", "variance_axis0"):
+        c4 = [torch.from_numpy(W.c4_matrix()).to(dev)]
+        for k in range(1, N_VAR_COPIES):
+            c4.append(torch.roll(c4[0], shifts=97 * k, dims=1).contiguous())
+        axis = 1 if kernel == "variance" else 0
+        nsl = VAR_ROWS if axis == 1 else VAR_COLS
+        ws_b = max(1, L.sv_variance_f32_workspace_size(VAR_ROWS, VAR_COLS, axis))
+        ws = torch.zeros(ws_b, dtype=torch.uint8, device=dev)
+        v = torch.empty(nsl, dtype=torch.float32, device=dev)
+        m = torch.empty(nsl, dtype=torch.float32, device=dev)
+        run = lambda i: check(L.sv_variance_f32(c4[i % N_VAR_COPIES].data_ptr(), VAR_ROWS, VAR_COLS, axis, 0,
+                                                v.data_ptr(), m.data_ptr(), ws.data_ptr(), ws_b, sh))
+        elems = VAR_ROWS * VAR_COLS
+    else:
+        c5 = [torch.from_numpy(W.sum_cancelling_pairs()).to(dev)]
+        for k in range(1, N_SUM_COPIES):
+            c5.append(torch.roll(c5[0], shifts=1_000_003 * k).contiguous())
+        out = torch.empty((), dtype=torch.float32, device=dev)
+        if kernel == "sum":
+            ws_b = L.sv_tree_sum_f32_workspace_size(SUM_N)
+            ws = torch.zeros(ws_b, dtype=torch.uint8, device=dev)
+            run = lambda i: check(L.sv_tree_sum_f32(c5[i % N_SUM_COPIES].data_ptr(), SUM_N, out.data_ptr(),
+                                                    ws.data_ptr(), ws_b, sh))
+        elif kernel == "adn":
+            ws_b = L.sv_adn_sum_f32_workspace_size(SUM_N)
+            ws = torch.zeros(ws_b, dtype=torch.uint8, device=dev)
+            run = lambda i: check(L.sv_adn_sum_f32(c5[i % N_SUM_COPIES].data_ptr(), SUM_N, ADN_FOLD, out.data_ptr(),
+                                                   ws.data_ptr(), ws_b, sh))
+        elif kernel == "read":
+            run = lambda i: check(L.sv_probe_read_bandwidth(c5[i % N_SUM_COPIES].data_ptr(), SUM_N, out.data_ptr(),
+                                                             sh))
+        else:
+            raise SystemExit(f"bench.py --only: unknown kernel {kernel!r}")
+        elems = SUM_N
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"only": kernel, "launches": steps, "warmup": warmup, "avg_ms": round(ms, 5),
+                      "gelem_s": round(elems / (ms * 1e-3) / 1e9, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +210,7 @@ def main():
                     help="untimed steps run back to back for this long before the warm-up steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--only", default=None, help="run one kernel only (see the usage above)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -150,6 +219,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.only:
+        only(args.only, args.steps, args.warmup)
         return
 
     import numpy as np

@@ -52,6 +52,10 @@ def capi():
                 if not os.path.exists(_LIB_PATH):
                     raise ImportError(
                         f"libstable_variance.so is not built ({_LIB_PATH}); run __graft_entry__.build()")
+                # torch first: its HIP runtime and the library's have the same
+                # soname, so whichever loads first serves both, and torch's
+                # allocations need its own
+                import torch  # noqa: F401
                 L = ctypes.CDLL(_LIB_PATH)
                 i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
                 L.sv_abi_version.restype = ctypes.c_int
