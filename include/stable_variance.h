@@ -118,6 +118,23 @@ sv_status sv_tree_sum_dw_f32(const float *x, int64_t n, float *out, void *worksp
                              void *stream);
 
 /*
+ * sv_tree_sum_f32 for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same result, arguments (without the workspace),
+ * errors and asynchrony as sv_tree_sum_f32, and n <= 2^36 (a larger n gives
+ * SV_ERR_UNSUPPORTED).  It allocates nothing: the workspace is a
+ * SV_TREE_SUM_NOALLOC_SCRATCH_BYTES-byte array inside the library, one per
+ * GPU, held until the process ends.  Its first call on a device looks the
+ * array up (with that device current) and clears its ticket counters on
+ * `stream` with a small kernel; every call leaves them zero again.  All calls
+ * on one GPU share that array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results, so order them, e.g.
+ * on one stream.
+ */
+#define SV_TREE_SUM_NOALLOC_SCRATCH_BYTES 99584
+sv_status sv_tree_sum_f32_noalloc(const float *x, int64_t n, float *out, void *stream);
+
+/*
  * Bytes of workspace sv_variance_f32 needs.
  *   axis 1: 0 when every row fits one workgroup (n <= 16384 values), else 24
  *           bytes per 16384-value chunk of every row plus 4 bytes per row

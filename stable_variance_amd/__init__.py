@@ -68,6 +68,8 @@ def capi():
                 L.sv_tree_sum_f32_workspace_size.argtypes = [i64]
                 L.sv_tree_sum_f32.restype = ctypes.c_int
                 L.sv_tree_sum_f32.argtypes = [vp, i64, vp, vp, sz, vp]
+                L.sv_tree_sum_f32_noalloc.restype = ctypes.c_int
+                L.sv_tree_sum_f32_noalloc.argtypes = [vp, i64, vp, vp]
                 L.sv_variance_f32_workspace_size.restype = sz
                 L.sv_variance_f32_workspace_size.argtypes = [i64, i64, ctypes.c_int]
                 L.sv_variance_f32.restype = ctypes.c_int

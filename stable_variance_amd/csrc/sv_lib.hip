@@ -26,6 +26,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/stable_variance.h"
@@ -2010,6 +2011,50 @@ void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t co
   }
 }
 
+// ------------------------------------------------------------------ tree sum, no workspace argument
+
+// The tree sum's workspace as a file-scope device array (ticket counters,
+// then partial nodes: the layout of a caller's workspace).  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol): it takes each device's address with hipGetSymbolAddress.
+constexpr size_t NOALLOC_BYTES = SUM_WS_HEADER + (size_t)(SUM_MAX_BLOCKS + SUM_MAX_BLOCKS / SUM_GROUP) * sizeof(Node);
+static_assert(NOALLOC_BYTES == SV_TREE_SUM_NOALLOC_SCRATCH_BYTES, "header constant");
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[NOALLOC_MAX_DEVICES];  // each device's address of `scratch`, once set up
+
+// The current device's address of `scratch`.  On the first call on a device
+// it is looked up (with that device current) and *first is set, so that the
+// caller clears the counters before their first use.
+sv_status scratch_address(const char *who, void **ptr, bool *first) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(SV_ERR_UNSUPPORTED, "%s: device %d beyond the %d devices set up", who, dev, NOALLOC_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  *first = false;
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SV_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", who, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+    *first = true;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -2081,6 +2126,33 @@ sv_status sv_tree_sum_f32(const float *x, int64_t n, float *out, void *workspace
 sv_status sv_tree_sum_dw_f32(const float *x, int64_t n, float *out, void *workspace, size_t workspace_bytes,
                              void *stream) {
   return tree_sum_impl("sv_tree_sum_dw_f32", true, x, n, out, workspace, workspace_bytes, stream);
+}
+
+sv_status sv_tree_sum_f32_noalloc(const float *x, int64_t n, float *out, void *stream) {
+  const char *who = "sv_tree_sum_f32_noalloc";
+  if (n < 0) return fail(SV_ERR_INVALID_ARGUMENT, "%s: n = %lld < 0", who, (long long)n);
+  if (n > SUM_MAX_N)
+    return fail(SV_ERR_UNSUPPORTED, "%s: n = %lld above 2^36, the most its %zu-byte scratch array serves", who,
+                (long long)n, NOALLOC_BYTES);
+  if (!out) return fail(SV_ERR_INVALID_ARGUMENT, "%s: out is NULL", who);
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "%s: x is NULL with n > 0", who);
+  const sv_status dev = check_device();
+  if (dev != SV_OK) return dev;
+  void *ptr = nullptr;
+  bool first = false;
+  const sv_status sc = scratch_address(who, &ptr, &first);
+  if (sc != SV_OK) return sc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (first) {
+    // the ticket counters start at zero (a fill kernel, no memset call);
+    // every sum leaves them zero again
+    k_fill<<<dim3((unsigned)(SUM_WS_HEADER / 4 + 255) / 256), 256, 0, st>>>(reinterpret_cast<float *>(ptr),
+                                                                          (int64_t)(SUM_WS_HEADER / 4), 0.0f);
+    const sv_status rc = check_launch(who);
+    if (rc != SV_OK) return rc;
+  }
+  return tree_sum_impl(who, false, x, n, out, ptr, NOALLOC_BYTES, stream);
 }
 
 size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis) {
