@@ -339,9 +339,8 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    the row's power-of-two tile, 1, 2, 4 or 8 (64, 32, 16
  *                    or 8 values per lane; a 2048-value tile takes at most 32
  *                    values per lane, a 16384-value tile at most 16 waves), or
- *                    0 (default): 32, 16 or 8 values per lane, whichever
- *                    gives the least VALU work for the row length (32 for
- *                    every power of two)
+ *                    0 (default): four waves per row for tiles of up to 4096
+ *                    values, eight above
  *   "var_lds_pad"    unused dynamic LDS bytes per row workgroup, 0..65536
  *                    (default 0): a cap on resident waves, for measurements
  *   "var_short_rows" rows of at most 512 values: 1 (default) = several rows
