@@ -223,11 +223,18 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
  *   5  shift + centring + two-term, plain trees
  *   6  no shift, two-term, compensated trees (the returned mean is m)
  *   7  shift + centring, compensated trees, no two-term
+ *   8  shift + centring, sequential Kahan scan, no two-term: m from the plain
+ *      tree of y as in the method, then S2 = Kahan's compensated recurrence
+ *      over q_i = (y_i - m)^2 in index order (s = c = 0; for each q:
+ *      t = s + (q - c), c = (t - s) - (q - c), s = t), var = max(S2/n, 0)
+ *      and the ddof rescale.  A serial chain per slice (a lane per slice),
+ *      so it runs far below the other variants' speed, as on the page
  * "Plain tree" is the same adjacent-pair topology without the error array.
  * Every variant but 1 takes the plain tree for the local mean, as the method
  * does; "plain" and "compensated" name the trees of d and d^2.
- * Shapes: axis 1 with n <= 16384, axis 0 with n <= 1024 (else
- * SV_ERR_UNSUPPORTED).  No workspace; otherwise as sv_variance_f32.
+ * Shapes: axis 1 with n <= 16384, axis 0 with n <= 1024; variant 8 any
+ * axis with n <= 4194304 (else SV_ERR_UNSUPPORTED).  No workspace; otherwise
+ * as sv_variance_f32.
  */
 sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int variant,
                                   float *var_out, float *mean_out, void *stream);

@@ -280,12 +280,15 @@ VARIANTS = {
     "shift_plain_2t": 5,
     "noshift_comp_2t": 6,
     "shift_comp_no2t": 7,
+    "shift_kahan_no2t": 8,
 }
 
 
 def var_variant(x, variant, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     """One of the ablation variants (a name of VARIANTS or its number) on a
-    2-D float32 tensor; single-workgroup shapes only."""
+    2-D float32 tensor.  The tree variants take one workgroup per slice (rows
+    of up to 16384 values, columns of up to 1024); the Kahan scan takes slices
+    of up to 2^22 values."""
     import torch
 
     _check_tensor(x)

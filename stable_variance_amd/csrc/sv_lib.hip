@@ -109,6 +109,7 @@ enum Variant {
   V_SHIFT_PLAIN_2T = 5,
   V_NOSHIFT_COMP_2T = 6,
   V_SHIFT_COMP_NO2T = 7,
+  V_SHIFT_KAHAN_NO2T = 8,  // shift + centring, Kahan sequential scan, no two-term (k_var_kahan)
 };
 template <int V>
 struct VariantFlags {
@@ -1975,6 +1976,168 @@ void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *v
   k_var_cols<E, W><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
 }
 
+// The ablation row "shift + centring, Kahan sequential scan" of the method
+// page's §4: the local mean from the plain tree of y (as in the method),
+// then S2 summed by Kahan's compensated recurrence in index order, one value
+// after the other, and var = max(S2 / n, 0) with the ddof rescale (no
+// two-term step).  The scan is serial per slice, so a lane owns a slice and
+// a wave 64 slices.  Axis 1 rows reach the lanes through LDS tiles of 64 rows
+// by 64 values (loaded 1 KiB per instruction, written and read back 16 bytes
+// per lane, rows 68 floats apart);
+// axis 0 columns are read directly, one row of the wave's 64 columns per
+// load.  Two passes over the data: the plain tree of y (64-value chunks in
+// registers, the chunk nodes merged in tree order by a binary counter whose
+// state is the same in every lane), then the scan.
+constexpr int KS_T = 64;                 // values per chunk (tile width)
+constexpr int KS_LD = KS_T + 4;          // LDS tile row stride: 16-byte aligned rows, 16 lanes per bank cycle
+constexpr int KS_LEVELS = 16;            // chunk-tree levels: 2^16 chunks
+template <bool AX1, bool VEC>
+__global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, int64_t nsl, int64_t n, int64_t ld,
+                                                  int64_t ddof, float *__restrict__ var_out,
+                                                  float *__restrict__ mean_out) {
+  __shared__ float4 tile4[AX1 ? KS_T * KS_LD / 4 : 1];
+  float *const tile = reinterpret_cast<float *>(tile4);
+  const int lane = threadIdx.x;
+  const int64_t s0 = (int64_t)blockIdx.x * 64;
+  const int64_t sl = s0 + lane;
+  const bool real = sl < nsl;
+  const int64_t slc = real ? sl : nsl - 1;  // lanes past the last slice read it again
+  const int64_t nch = (n + KS_T - 1) / KS_T;
+
+  // A chunk is loaded in two steps, so that the next chunk's loads are in
+  // flight while the current one is reduced: issue() fills raw registers
+  // (every load issued, at indices clamped to the data), lanes() turns them
+  // into this lane's values v[k] = slice[c*64 + k] (through the LDS tile on
+  // axis 1).  Values past n are masked by the callers.
+  auto issue = [&](int64_t c, float(&raw)[KS_T]) {
+    c = c < nch ? c : nch - 1;
+    if constexpr (AX1) {
+      // lane L loads values 4 (L mod 16) .. +3 of the chunk in row 4j + L/16
+      // of the wave's 64 rows: 16 bytes at once when the group lies inside
+      // the row and rows are 16-byte aligned (VEC), else one by one
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        const int64_t row = s0 + r < nsl ? s0 + r : nsl - 1;
+        const int64_t col = c * KS_T + 4 * (lane & 15);
+        const float *__restrict__ q = x + row * ld;
+        float4 g;
+        if (VEC && col + 3 < n) {
+          g = *reinterpret_cast<const float4 *>(q + col);
+        } else {
+          g = make_float4(q[col < n ? col : n - 1], q[col + 1 < n ? col + 1 : n - 1],
+                          q[col + 2 < n ? col + 2 : n - 1], q[col + 3 < n ? col + 3 : n - 1]);
+        }
+        raw[4 * j] = g.x; raw[4 * j + 1] = g.y; raw[4 * j + 2] = g.z; raw[4 * j + 3] = g.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS_T; ++k) {
+        const int64_t i = c * KS_T + k;
+        raw[k] = x[(i < n ? i : n - 1) * ld + slc];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto lanes = [&](const float(&raw)[KS_T], float(&v)[KS_T]) {
+    if constexpr (AX1) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        *reinterpret_cast<float4 *>(tile + (4 * j + (lane >> 4)) * KS_LD + 4 * (lane & 15)) =
+            make_float4(raw[4 * j], raw[4 * j + 1], raw[4 * j + 2], raw[4 * j + 3]);
+      sv::wave_lds_sync();
+#pragma unroll
+      for (int k = 0; k < KS_T / 4; ++k) {
+        const float4 t = *reinterpret_cast<const float4 *>(tile + lane * KS_LD + 4 * k);
+        v[4 * k] = t.x; v[4 * k + 1] = t.y; v[4 * k + 2] = t.z; v[4 * k + 3] = t.w;
+      }
+      sv::wave_lds_sync();
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS_T; ++k) v[k] = raw[k];
+    }
+  };
+  // every chunk c < nch through `body`, two register sets alternating
+  auto stream = [&](auto &&body) {
+    float ra[KS_T], rb[KS_T], v[KS_T];
+    issue(0, ra);
+    for (int64_t c = 0; c < nch; c += 2) {
+      issue(c + 1, rb);
+      lanes(ra, v);
+      body(c, v);
+      issue(c + 2, ra);
+      if (c + 1 < nch) {  // uniform
+        lanes(rb, v);
+        body(c + 1, v);
+      }
+    }
+  };
+  const float x0 = AX1 ? x[slc * ld] : x[slc];
+
+  // pass 1: the plain tree of y
+  float st[KS_LEVELS];
+#pragma unroll
+  for (int lv = 0; lv < KS_LEVELS; ++lv) st[lv] = 0.0f;
+  stream([&](int64_t c, float(&v)[KS_T]) {
+#pragma unroll
+    for (int k = 0; k < KS_T; ++k) v[k] = (c * KS_T + k < n) ? v[k] - x0 : 0.0f;
+    float carry = sv::lane_tree<sv::LEAF_PLAIN, 0, KS_T, KS_T>(v).s;
+    bool placed = false;
+#pragma unroll
+    for (int lv = 0; lv < KS_LEVELS; ++lv) {
+      if (!placed) {
+        if ((c >> lv) & 1) {
+          carry = st[lv] + carry;
+        } else {
+          st[lv] = carry;
+          placed = true;
+        }
+      }
+    }
+  });
+  // the pending left nodes, combined in tree order (their right siblings
+  // beyond the data are zero subtrees), then the plain tree's root rule
+  float sy = 0.0f;
+  bool any = false;
+#pragma unroll
+  for (int lv = 0; lv < KS_LEVELS; ++lv) {
+    if ((nch >> lv) & 1) {
+      sy = any ? st[lv] + sy : st[lv];
+      any = true;
+    }
+  }
+  sy = sy + 0.0f;
+  const float fn = (float)n;
+  const float m = sy / fn;
+
+  // pass 2: Kahan's recurrence over q_i = (y_i - m)^2 in index order
+  float sum = 0.0f, corr = 0.0f;
+  stream([&](int64_t c, float(&v)[KS_T]) {
+#pragma unroll
+    for (int k = 0; k < KS_T; ++k) {
+      if (c * KS_T + k < n) {  // uniform
+        const float d = (v[k] - x0) - m;
+        const float q = d * d;
+        const float yk = q - corr;
+        const float t = sum + yk;
+        corr = (t - sum) - yk;
+        sum = t;
+      }
+    }
+  });
+  if (real) {
+    const float a = sum / fn;
+    float var = (a != a) ? a : ((a > 0.0f) ? a : 0.0f);
+    if (ddof != 0) {
+      int64_t den = n - ddof;
+      if (den < 0) den = 0;
+      var = var * (fn / (float)den);
+    }
+    var_out[sl] = var;
+    if (mean_out) mean_out[sl] = x0 + m;
+  }
+}
+
 template <int V>
 void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t cols, int64_t ddof, float *var,
                     float *mean, hipStream_t st) {
@@ -2275,7 +2438,7 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
   if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: ddof = %lld < 0", (long long)ddof);
   if (variant != V_KERNEL && variant != V_COMP_Y && variant != V_REFERENCE && variant != V_NAIVE &&
       variant != V_SHIFT_PLAIN_NO2T && variant != V_SHIFT_PLAIN_2T && variant != V_NOSHIFT_COMP_2T &&
-      variant != V_SHIFT_COMP_NO2T)
+      variant != V_SHIFT_COMP_NO2T && variant != V_SHIFT_KAHAN_NO2T)
     return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: unknown variant %d", variant);
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
@@ -2283,7 +2446,12 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
   if (nslices == 0) return ok();
   if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: var_out is NULL");
   if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: x is NULL");
-  if (nslices > 0x7fffffffLL || (ax1 ? n > ROWS_MAX_N : n > COLS_MAX_R))
+  // the tree variants take one workgroup per slice (rows of up to 16384
+  // values, columns of up to 1024); the Kahan scan takes a lane per slice and
+  // slices of up to 2^16 chunks of 64 values
+  const bool kahan = variant == V_SHIFT_KAHAN_NO2T;
+  if (nslices > 0x7fffffffLL ||
+      (kahan ? n > ((int64_t)KS_T << KS_LEVELS) : (ax1 ? n > ROWS_MAX_N : n > COLS_MAX_R)))
     return fail(SV_ERR_UNSUPPORTED, "sv_variance_variant_f32: shape [%lld, %lld] along axis %d not supported",
                 (long long)rows, (long long)cols, axis);
   const sv_status dev = check_device();
@@ -2297,6 +2465,13 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
     return check_launch("sv_variance_variant_f32");
   }
   const bool vec = aligned16(x) && (cols % 4 == 0);
+  if (variant == V_SHIFT_KAHAN_NO2T) {
+    const dim3 grid((unsigned)((nslices + 63) / 64)), block(64);
+    if (!ax1) k_var_kahan<false, false><<<grid, block, 0, st>>>(x, nslices, n, cols, ddof, var_out, mean_out);
+    else if (vec) k_var_kahan<true, true><<<grid, block, 0, st>>>(x, nslices, n, cols, ddof, var_out, mean_out);
+    else k_var_kahan<true, false><<<grid, block, 0, st>>>(x, nslices, n, cols, ddof, var_out, mean_out);
+    return check_launch("sv_variance_variant_f32");
+  }
   switch (variant) {
     case V_KERNEL: launch_variant<V_KERNEL>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
     case V_COMP_Y: launch_variant<V_COMP_Y>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;

@@ -628,7 +628,7 @@ def test_complex_then_sum_share_nothing(torch_dev):
 # ------------------------------------------------------------------ ablation variants
 
 GPU_VARIANTS = {"kernel": 0, "kernel_comp_y": 1, "reference": 2, "naive": 3, "shift_plain_no2t": 4,
-                "shift_plain_2t": 5, "noshift_comp_2t": 6, "shift_comp_no2t": 7}
+                "shift_plain_2t": 5, "noshift_comp_2t": 6, "shift_comp_no2t": 7, "shift_kahan_no2t": 8}
 
 
 @pytest.mark.parametrize("name", list(GPU_VARIANTS))
@@ -653,6 +653,29 @@ def test_variants_against_oracle(torch_dev, name):
             ov, om = oracle.variance(a, axis=ax, ddof=ddof, method=code)
             assert same_bits(v.cpu().numpy(), ov), (name, a.shape, ax, ddof)
             assert same_bits(m.cpu().numpy(), om), (name, a.shape, ax, ddof)
+
+
+@pytest.mark.parametrize("shape,axis", [((3, 70000), 1), ((2, 5001), 1), ((130, 4097), 1), ((3000, 70), 0),
+                                        ((1, 64), 1), ((65, 1), 0), ((4096, 4096), 1)])
+def test_kahan_scan_variant_long_and_ragged_slices(torch_dev, shape, axis):
+    # The Kahan-scan row has no one-workgroup limit: slices beyond 16384
+    # values, widths that are not a multiple of 4 (per-value loads), a partial
+    # last wave of 64 slices, the chunk counter past 64 chunks, and the
+    # timing shape.  Bit for bit against the oracle's loop.
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    a = rng.normal(5e3, 3, shape).astype(np.float32)
+    if shape == (4096, 4096):
+        a = W.c4_matrix()
+    t = torch.from_numpy(a).to(dev)
+    for ddof in (0, 1):
+        v, m = sv.var_variant(t, "shift_kahan_no2t", dim=axis, ddof=ddof, return_mean=True)
+        torch.cuda.synchronize()
+        ov, om = oracle.variance(a, axis=axis, ddof=ddof, method=oracle.METHOD_SHIFT_KAHAN_NO2T)
+        assert same_bits(v.cpu().numpy(), ov), (shape, axis, ddof)
+        assert same_bits(m.cpu().numpy(), om), (shape, axis, ddof)
 
 
 def test_variant_zero_matches_the_main_entry_point(torch_dev):
