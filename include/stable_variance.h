@@ -144,10 +144,10 @@ sv_status sv_tree_sum_f32_noalloc(const float *x, int64_t n, float *out, void *s
  *           stays the chunked path's, independent of the tuning knobs).
  *   axis 0: whenever rows and cols are both nonzero: three arrays of 8
  *           bytes per 64-row chunk per column and 4 bytes per column, each
- *           rounded up to 256 bytes.  Columns longer than one workgroup holds
- *           (by default more than 1024 rows) are reduced in row chunks,
- *           reading the input twice; the size does not depend on the tuning
- *           knobs.
+ *           rounded up to 256 bytes.  Columns of up to 4096 rows are reduced
+ *           in one launch that reads the input once (whole columns per
+ *           workgroup); longer columns in row chunks, reading the input
+ *           twice.  The size does not depend on the tuning knobs.
  * (size_t)-1 for an unsupported shape (an axis-1 row of more than 8192
  * chunks, a bad axis, rows * cols >= 2^40).  The workspace must be 256-byte
  * aligned; it is scratch (no initialisation, nothing kept between calls), so
@@ -374,6 +374,12 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    1024); longer columns are reduced in row chunks
  *   "var_cols_waves" axis 0, chunked: waves per workgroup, 4, 8 or 16
  *                    (default): chunks of 64, 128 or 256 rows
+ *   "var_cols_once"  axis 0, columns of 1025..4096 rows: 1 (default) = 16
+ *                    whole columns per workgroup of up to 16 waves, one
+ *                    column per lane, the input read once, when that grid
+ *                    fills at least three quarters of the chip's last round
+ *                    of workgroups, else the row-chunk launches; 0 = always
+ *                    the row-chunk launches; 2 = always the one-read launch
  *   "sum_xcd"        tree sum: 1 = renumber the workgroups so that each of the
  *                    eight dies (XCDs) streams one contiguous region; 0 =
  *                    dispatch order, consecutive regions spread over the dies

@@ -1309,31 +1309,42 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
   }
 }
 
-// Whole columns in one workgroup (R <= 16*G*W rows): the tile layout of
+// Whole columns in one workgroup (R <= E*G*W rows): the tile layout of
 // k_cols_y with a single chunk, and y, m, d and d^2 in one launch, the tile
 // kept in registers between the two passes.  Waves wholly past the last row
 // load nothing (their values are the +0 padding).
-template <int V, int W, int G, bool VEC16>
+// E rows per lane (16; 32 or 64 for one column per lane and columns of up
+// to 2048 or 4096 rows in one workgroup of 16 waves).  MODE 0 branches per
+// wave between full and ragged row ranges; MODE 1 is for R = E*G*W (no
+// masks), MODE 2 masks every wave (one code path: with 64 rows per lane the
+// two paths of MODE 0 would keep two copies of the shifted tile).
+template <int V, int W, int G, bool VEC16, int E = CC_E, int MODE = 0>
 __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
-  constexpr int E = CC_E, Q = 64 / G, NC = V * Q;
+  constexpr int Q = 64 / G, NC = V * Q;
   __shared__ Node sd[W][V][Q];
   __shared__ Node sq[W][V][Q];
   __shared__ float sm[V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // MODE 2 launches only the waves that reach row R; the others' nodes are
+  // the zero nodes of the padding
+  const int nw = MODE == 2 ? __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6)) : W;
   const int q = lane / G, g = lane % G;
   const int64_t cb = blockIdx.x;
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
-  const bool full = r0 + E <= R;
-  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
+  const bool full = MODE == 1 || r0 + E <= R;
+  const bool wave_full = MODE == 1 || (MODE == 0 && rw + (int64_t)E * G <= R);  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
 
   float v[V][E];
-  if (rw < R) load_cols_tile<V, E, VEC16>(x, R, C, c0, r0, full, v);
+  // MODE 0 skips the loads of a wave wholly past R; MODE 2 issues them at
+  // rows clamped to R - 1, so that no branch makes the first use of a
+  // value wait for all of them
+  if (MODE != 0 || rw < R) load_cols_tile<V, E, VEC16>(x, R, C, c0, r0, full, v);
   float x0[V];
   const int64_t cc = c0 < C ? c0 : C - V;
 #pragma unroll
@@ -1346,11 +1357,11 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   }
   __syncthreads();
   // thread t forms m (then step 4) of columns V*tq + tk of the block, t = tk*Q + tq
-  for (int t = threadIdx.x; t < NC; t += 64 * W) {
+  for (int t = threadIdx.x; t < NC; t += blockDim.x) {
     const int tk = t / Q, tq = t % Q;
     Node nn[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) nn[i] = sd[i][tk][tq];
+    for (int i = 0; i < W; ++i) nn[i] = i < nw ? sd[i][tk][tq] : sv::zero_node();
     sm[tk][tq] = sv::root_value_k<sv::Y_KIND>(sv::node_tree<0, W, W, sv::Y_KIND>(nn)) / (float)R;
   }
   __syncthreads();
@@ -1367,15 +1378,15 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < NC; t += 64 * W) {
+  for (int t = threadIdx.x; t < NC; t += blockDim.x) {
     const int tk = t / Q, tq = t % Q;
     const int64_t col = cb * NC + (int64_t)tq * V + tk;
     if (col < C) {
       Node a[W], b[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        a[i] = sd[i][tk][tq];
-        b[i] = sq[i][tk][tq];
+        a[i] = i < nw ? sd[i][tk][tq] : sv::zero_node();
+        b[i] = i < nw ? sq[i][tk][tq] : sv::zero_node();
       }
       finalize(sv::node_tree<0, W, W>(a), sv::node_tree<0, W, W, sv::NODE_NN>(b), x[col], sm[tk][tq], R, ddof,
                var_out + col, mean_out ? mean_out + col : nullptr);
@@ -1516,6 +1527,8 @@ struct Tuning {
   int sum_xcd = 0;            // tree sum: each die (XCD) streams one contiguous region
   int var_xcd = 0;            // row variance: each die (XCD) takes one contiguous run of rows
   int var_full_rows = 1;      // rows that fill their tile exactly take the kernel without masks (0: the general one)
+  int var_cols_once = 1;      // axis 0, 1025..4096 rows: one workgroup per 16 columns, one read, when the
+                             // grid fills the chip (0: row chunks; 2: one read whatever the fill)
 };
 thread_local Tuning g_tune;
 
@@ -1539,6 +1552,7 @@ constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel for any number 
 constexpr int64_t ROWS_ONE_MAX_N = 65536;
 constexpr int64_t ROWS_ONE_MIN_ROWS = 256;
 constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
+constexpr int64_t COLS_ONE_LONG_MAX_R = 4096;  // one column per lane, 64 rows per lane, 16 waves
 
 // Long-slice workspace: y, d and d^2 chunk nodes per slice, then m.
 size_t long_ws_bytes(int64_t nslices, int64_t nch) {
@@ -2386,6 +2400,35 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     launch_long_top<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
     return check_launch("sv_variance_f32");
   }
+  if (!ax1 && n > COLS_MAX_R && n <= COLS_ONE_LONG_MAX_R && g_tune.var_cols_once &&
+      g_tune.var_cols_single_max == COLS_MAX_R) {
+    // columns of 1025..4096 rows: sixteen whole columns per workgroup of up
+    // to 16 waves (four row groups of E rows per wave; a shorter column
+    // launches only the waves its rows reach), read once -- unless the grid
+    // would leave the chip's last round of workgroups mostly empty (each
+    // workgroup holds 256 KB in registers, so one or two fit a CU)
+    const int e = n <= 2048 ? 32 : 64;
+    const int waves = (int)((n + 4 * e - 1) / (4 * e));
+    const int64_t nwg = (cols + 15) / 16;
+    const void *kern = n == 2048   ? reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 32, 1>)
+                       : n < 2048  ? reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 32, 2>)
+                       : n == 4096 ? reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 64, 1>)
+                                   : reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 64, 2>);
+    int per_cu = 0, cus = 0, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * waves, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0) {
+      const int64_t cap = (int64_t)per_cu * cus, rounds = (nwg + cap - 1) / cap;
+      if (g_tune.var_cols_once == 2 || 4 * nwg >= 3 * rounds * cap) {
+        const dim3 grid((unsigned)nwg), block(64 * (unsigned)waves);
+        if (n == 2048) k_cols_one<1, 16, 4, false, 32, 1><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+        else if (n < 2048) k_cols_one<1, 16, 4, false, 32, 2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+        else if (n == 4096) k_cols_one<1, 16, 4, false, 64, 1><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+        else k_cols_one<1, 16, 4, false, 64, 2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+        return check_launch("sv_variance_f32");
+      }
+    }
+  }
   if (!ax1 && n > g_tune.var_cols_single_max) {
     const ColsWs ws = cols_ws(workspace, cols_layout(rows, cols));
     if (aligned16(x) && cols % 4 == 0) launch_cols_v<4>(x, rows, cols, ddof, ws, var_out, mean_out, st);
@@ -2655,6 +2698,12 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
   }
   if (strcmp(key, "sum_xcd") == 0) return flag(&g_tune.sum_xcd);
   if (strcmp(key, "var_full_rows") == 0) return flag(&g_tune.var_full_rows);
+  if (strcmp(key, "var_cols_once") == 0) {
+    if (value < 0 || value > 2)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_once must be 0, 1 or 2");
+    g_tune.var_cols_once = (int)value;
+    return ok();
+  }
   if (strcmp(key, "var_xcd") == 0) return flag(&g_tune.var_xcd);
   if (strcmp(key, "var_lds_pad") == 0) {
     if (value < 0 || value > 65536) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_lds_pad must be in [0, 65536]");

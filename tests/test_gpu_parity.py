@@ -68,6 +68,8 @@ COL_GEOMETRIES = {
     "single_lane_per_column": {"var_cols_one": 0, "var_cols_short": 0},
     "single_four_columns_per_lane": {"var_cols_one": 2},
     "single_one_column_per_lane": {"var_cols_one": 3},
+    "row_chunk_launches": {"var_cols_once": 0},
+    "one_read_whatever_the_fill": {"var_cols_once": 2},
 }
 
 
@@ -507,6 +509,29 @@ def test_variance_cols_many_chunks(torch_dev, R, C, waves):
     sv.set_tuning("var_cols_waves", waves)
     try:
         check_var(torch_dev, a, 0, 0)
+    finally:
+        sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("R,C", [(4096, 4096), (1025, 256), (3000, 4100), (4095, 260), (2048, 8192), (1088, 4),
+                                 (4096, 1000), (2000, 10), (2049, 17), (1025, 1), (3999, 33)])
+@pytest.mark.parametrize("once", [1, 2])
+def test_variance_cols_one_read(torch_dev, R, C, once):
+    # Columns of 1025..4096 rows in one launch that reads the input once
+    # (once=2 forces it; once=1 lets the grid's fill choose): 2048 and 4096
+    # rows (every wave full), ragged lengths (only the reached waves, a
+    # partial last one), a partial last block of 16 columns, one-lane and
+    # narrow widths, and widths that are not a multiple of 4.
+    rng = np.random.default_rng(R + C)
+    a = rng.normal(-2e3, 5, (R, C)).astype(np.float32)
+    import stable_variance_amd as sv
+
+    sv.set_tuning("var_cols_once", once)
+    try:
+        for ddof in (0, 1):
+            check_var(torch_dev, a, 0, ddof)
+        v = check_var(torch_dev, np.full((R, C), np.float32(1e38)), 0, 0)
+        assert np.all(v == 0.0)
     finally:
         sv.set_tuning("reset", 0)
 
