@@ -45,11 +45,17 @@ N_VAR_COPIES, N_SUM_COPIES = 6, 2
 # Algorithmic bytes per launch: every input value read once, outputs written once.
 VAR_BYTES = VAR_ROWS * VAR_COLS * 4 + 2 * VAR_ROWS * 4
 SUM_BYTES = SUM_N * 4 + 4
-# Plain FP32 VALU operations the method needs per variance element (see the design notes):
-# shift 1, Tree(y) 7, centre 1, square 1, Tree(d) 7, Tree(d^2) 6.
-VAR_OPS_PER_ELEM = 23
+# Plain FP32 VALU operations the method needs per variance element, one tree
+# node per element: shift 1, plain tree of y 1, centre 1, square 1,
+# compensated tree of d 7 (TwoSum 6 + carry 1), of d^2 6 (Fast2Sum on
+# non-negative operands 4 + carry 2).
+VAR_OPS_PER_ELEM = 17
+VAR_KERNEL = "k_var_rows_full<16, 4>"
+VAR0_KERNEL = "k_cols_one<1, 16, 4, false, 64, 1>"
 SUM_COUNTERS = os.path.join(ROOT, "profiles", "k_tree_sum_1e8_counters.txt")
-VAR_COUNTERS = os.path.join(ROOT, "profiles", "k_var_rows_4096x4096_counters.txt")
+VAR_COUNTERS = os.path.join(ROOT, "profiles", "k_var_rows_full_4096x4096_counters.txt")
+VAR_VALU = os.path.join(ROOT, "profiles", "k_var_rows_full_4096x4096_valu.txt")
+VAR0_COUNTERS = os.path.join(ROOT, "profiles", "k_cols_one_4096x4096_axis0_counters.txt")
 ADN_COUNTERS = os.path.join(ROOT, "profiles", "k_adn_sum_1e8_counters.txt")
 ADN_FOLD = 3
 # float-sum throughput printed on the ADN page ("Scalar-sum throughput", GElements/s)
@@ -66,10 +72,9 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_counter_traffic(path):
-    """HBM bytes per launch from a committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), or None
-    when absent or taken on other kernel source."""
+def read_summary(path, key):
+    """One figure from a committed rocprofv3 counter summary, or None when
+    the summary is absent or was taken on other kernel source."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -81,9 +86,15 @@ def read_counter_traffic(path):
     if kv.get("source_digest") != source_digest():
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_counter_traffic(path):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled by a plain copy
+    of known size) from a committed counter summary, or None."""
+    return read_summary(path, "traffic_bytes_per_launch")
 
 
 def calibrate_copy():
@@ -383,8 +394,8 @@ def main():
     overlap = {"ms_per_step": round(overlap_ms, 5),
                "gelem_s": round((VAR_ROWS * VAR_COLS + SUM_N) / (overlap_ms * 1e-3) / 1e9, 2),
                "over_sequential_step": round(overlap_ms / ((var_avg + sum_avg)), 3)}
-    # the same buffers along axis 0 (4096 column slices of stride 4096: row
-    # chunks, the input read twice, three launches)
+    # the same buffers along axis 0 (4096 column slices of stride 4096: one
+    # launch, sixteen whole columns per workgroup, the input read once)
     ws0 = torch.zeros(max(1, L.sv_variance_f32_workspace_size(VAR_ROWS, VAR_COLS, 0)), dtype=torch.uint8, device=dev)
     v0 = torch.empty(VAR_COLS, dtype=torch.float32, device=dev)
     m0 = torch.empty(VAR_COLS, dtype=torch.float32, device=dev)
@@ -392,7 +403,9 @@ def main():
                                                  v0.data_ptr(), m0.data_ptr(), ws0.data_ptr(), ws0.numel(), sh))
     var0_ms = time_op(run_var0, reps=50)
     torch_var0_ms = time_op(lambda i: torch.var(c4[i % N_VAR_COPIES], dim=0, correction=0))
-    axis0 = {"avg_ms": round(var0_ms, 5), "gb_s": round(VAR_BYTES / (var0_ms * 1e-3) / 1e9, 1),
+    var0_gbs = VAR_BYTES / (var0_ms * 1e-3) / 1e9
+    axis0 = {"kernel": VAR0_KERNEL, "avg_ms": round(var0_ms, 5), "gb_s": round(var0_gbs, 1),
+             "hbm_frac": round(var0_gbs / HBM_PEAK_GBS, 4), "traffic": read_counter_traffic(VAR0_COUNTERS),
              "torch_var_dim0_ms": round(torch_var0_ms, 5)}
     if parity is not None:
         run_var0(0)
@@ -522,6 +535,8 @@ def main():
     var_tops = VAR_ROWS * VAR_COLS * VAR_OPS_PER_ELEM / (var_avg * 1e-3) / 1e12
     traffic = read_counter_traffic(SUM_COUNTERS)
     var_traffic = read_counter_traffic(VAR_COUNTERS)
+    var_valu = read_summary(VAR_VALU, "valu_instructions_issued_per_element")
+    sum_frac, var_frac = sum_gbs / HBM_PEAK_GBS, var_gbs / HBM_PEAK_GBS
 
     out = {
         "metric": METRIC,
@@ -546,8 +561,12 @@ def main():
                      "traffic": traffic, "avg_launch_ms": round(sum_avg, 5),
                      "algorithmic_bytes_per_launch": SUM_BYTES,
                      "read_ceiling_gbs": round(read_sum_gbs, 1),
-                     "frac_of_read_ceiling": round(sum_gbs / read_sum_gbs, 4)},
-        "variance_kernel": {"kernel": "k_var_rows<32, 2> (4096x4096, axis 1, two waves per row)", "avg_launch_ms": round(var_avg, 5),
+                     "frac_of_read_ceiling": round(sum_gbs / read_sum_gbs, 4),
+                     # both kernels of the step against the same HBM peak
+                     "step_kernels": {"k_tree_sum": round(sum_frac, 4), VAR_KERNEL: round(var_frac, 4)},
+                     "min_frac": round(min(sum_frac, var_frac), 4)},
+        "variance_kernel": {"kernel": f"{VAR_KERNEL} (4096x4096, axis 1, four waves per row)",
+                            "avg_launch_ms": round(var_avg, 5),
                             "gelem_s": round(VAR_ROWS * VAR_COLS / (var_avg * 1e-3) / 1e9, 2),
                             "hbm": {"achieved": round(var_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(var_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": VAR_BYTES,
@@ -555,7 +574,8 @@ def main():
                                     "frac_of_read_ceiling": round(var_gbs / read_var_gbs, 4)},
                             "alu": {"achieved": round(var_tops, 2), "peak": VALU_PEAK_TOPS, "unit": "Tops/s",
                                     "frac": round(var_tops / VALU_PEAK_TOPS, 4),
-                                    "ops_per_element": VAR_OPS_PER_ELEM},
+                                    "ops_per_element": VAR_OPS_PER_ELEM,
+                                    "valu_instructions_issued_per_element": var_valu},
                             "batches": var_batches},
         "sum_kernel": {"avg_launch_ms": round(sum_avg, 5), "gelem_s": round(SUM_N / (sum_avg * 1e-3) / 1e9, 2),
                        "batches": sum_batches},

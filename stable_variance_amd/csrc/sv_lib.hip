@@ -1331,7 +1331,17 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   // the zero nodes of the padding
   const int nw = MODE == 2 ? __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6)) : W;
   const int q = lane / G, g = lane % G;
-  const int64_t cb = blockIdx.x;
+  // Blocks narrower than a 128-byte cache line (NC < 32 columns) share each
+  // line with the next P - 1 blocks.  The dispatcher deals workgroups round
+  // robin to the eight dies, each with its own L2, so block b would run on
+  // die b % 8 and P dies would fetch the same line.  Within each full group
+  // of 8P workgroups, the P on one die take P adjacent blocks instead.
+  int64_t cb = blockIdx.x;
+  if constexpr (NC < 32) {
+    constexpr int P = 32 / NC;
+    const int64_t grp = cb / (8 * P), r = cb % (8 * P);
+    if ((grp + 1) * (8 * P) <= (int64_t)gridDim.x) cb = grp * (8 * P) + P * (r % 8) + r / 8;
+  }
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
@@ -2407,24 +2417,22 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     // launches only the waves its rows reach), read once -- unless the grid
     // would leave the chip's last round of workgroups mostly empty (each
     // workgroup holds 256 KB in registers, so one or two fit a CU)
-    const int e = n <= 2048 ? 32 : 64;
+    const int e = n <= 2048 ? 32 : 64;  // rows per lane over all blocks
     const int waves = (int)((n + 4 * e - 1) / (4 * e));
     const int64_t nwg = (cols + 15) / 16;
-    const void *kern = n == 2048   ? reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 32, 1>)
-                       : n < 2048  ? reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 32, 2>)
-                       : n == 4096 ? reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 64, 1>)
-                                   : reinterpret_cast<const void *>(k_cols_one<1, 16, 4, false, 64, 2>);
+    // MODE 1 when every wave is full (2048 or 4096 rows), else MODE 2
+    const bool exact = n == 2048 || n == 4096, big = n > 2048;
+    using KFn = void (*)(const float *, int64_t, int64_t, int64_t, float *, float *);
+    const KFn kern = big ? (exact ? k_cols_one<1, 16, 4, false, 64, 1> : k_cols_one<1, 16, 4, false, 64, 2>)
+                         : (exact ? k_cols_one<1, 16, 4, false, 32, 1> : k_cols_one<1, 16, 4, false, 32, 2>);
     int per_cu = 0, cus = 0, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * waves, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), 64 * waves, 0) ==
+            hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0) {
       const int64_t cap = (int64_t)per_cu * cus, rounds = (nwg + cap - 1) / cap;
       if (g_tune.var_cols_once == 2 || 4 * nwg >= 3 * rounds * cap) {
-        const dim3 grid((unsigned)nwg), block(64 * (unsigned)waves);
-        if (n == 2048) k_cols_one<1, 16, 4, false, 32, 1><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-        else if (n < 2048) k_cols_one<1, 16, 4, false, 32, 2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-        else if (n == 4096) k_cols_one<1, 16, 4, false, 64, 1><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-        else k_cols_one<1, 16, 4, false, 64, 2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
+        kern<<<dim3((unsigned)nwg), dim3(64 * (unsigned)waves), 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
         return check_launch("sv_variance_f32");
       }
     }
