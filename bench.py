@@ -401,7 +401,7 @@ def main():
     m0 = torch.empty(VAR_COLS, dtype=torch.float32, device=dev)
     run_var0 = lambda i: check(L.sv_variance_f32(c4[i % N_VAR_COPIES].data_ptr(), VAR_ROWS, VAR_COLS, 0, 0,
                                                  v0.data_ptr(), m0.data_ptr(), ws0.data_ptr(), ws0.numel(), sh))
-    var0_ms = time_op(run_var0, reps=50)
+    var0_ms = time_op(run_var0, reps=400)  # about 10 ms of work: clocks at their steady state
     torch_var0_ms = time_op(lambda i: torch.var(c4[i % N_VAR_COPIES], dim=0, correction=0))
     var0_gbs = VAR_BYTES / (var0_ms * 1e-3) / 1e9
     axis0 = {"kernel": VAR0_KERNEL, "avg_ms": round(var0_ms, 5), "gb_s": round(var0_gbs, 1),

@@ -149,7 +149,7 @@ sv_status sv_tree_sum_f32_noalloc(const float *x, int64_t n, float *out, void *s
  *           workgroup); longer columns in row chunks, reading the input
  *           twice.  The size does not depend on the tuning knobs.
  * (size_t)-1 for an unsupported shape (an axis-1 row of more than 8192
- * chunks, a bad axis, rows * cols >= 2^40).  The workspace must be 256-byte
+ * chunks, a bad axis, rows * cols > 2^36).  The workspace must be 256-byte
  * aligned; it is scratch (no initialisation, nothing kept between calls), so
  * calls that share one must be ordered on one stream.
  */
@@ -178,8 +178,10 @@ size_t sv_variance_f32_workspace_size(int64_t rows, int64_t cols, int axis);
  *   mean_out   may be NULL (the mean is then not written)
  *   workspace  device buffer of sv_variance_f32_workspace_size(...) bytes;
  *              may be NULL when that size is 0
- * rows and cols must be >= 0 with rows * cols < 2^40; an axis-1 row may hold
- * at most 8192 chunks (134,217,728 values).
+ * rows and cols must be >= 0 with rows * cols <= 2^36 (256 GiB of float32,
+ * about the most one 288 GB GPU holds: every launch then stays within HIP's
+ * 2^32 - 1 work-items per grid); an axis-1 row may hold at most 8192 chunks
+ * (134,217,728 values).
  */
 sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
                           float *var_out, float *mean_out, void *workspace, size_t workspace_bytes,

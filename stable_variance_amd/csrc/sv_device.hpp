@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sv_index.hpp"
+
 #if defined(__FAST_MATH__)
 #error "stable_variance must be built without fast-math (TwoSum needs exact IEEE rounding)"
 #endif
@@ -44,10 +46,7 @@ struct Node {
 // indices (die x takes the x-th run, the first nb mod 8 runs one longer), so
 // a die streams one region of the buffer.  A bijection of [0, nb): results
 // depend only on logical indices, so the renumbering changes no bit.
-__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
-  const int q = nb >> 3, r = nb & 7, die = b & 7, i = b >> 3;
-  return (die < r ? die * (q + 1) : r * (q + 1) + (die - r) * q) + i;
-}
+using svx::xcd_contiguous;
 
 // ---------------------------------------------------------------- nodes
 
@@ -330,7 +329,7 @@ __device__ __forceinline__ Node seg_tree(Node n) {
 // Lane L holding the range of virtual lane v(L) = 2 (L mod 32) + L / 32: the
 // tree's first cross-lane level then pairs lanes L and L ^ 32, virtual bits
 // 1..5 are lane bits 0..4, and the level order below follows.
-__device__ __forceinline__ int vlane_pair32(int lane) { return 2 * (lane & 31) + (lane >> 5); }
+using svx::vlane_pair32;
 
 // Lane l's value of v, as a wave-uniform (scalar) value.
 __device__ __forceinline__ float readlane_f(float v, int l) {
@@ -465,9 +464,8 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
   constexpr int STR = E + 4;
   constexpr int TILE = 64 * E;
   const bool full = len >= TILE;  // wave-uniform
-  // ragged: number of valid values in [0, TILE], and a safe index for loads
-  const int lim = len <= 0 ? 0 : (len >= TILE ? TILE : (int)len);
-  const int last = lim > 0 ? lim - 1 : 0;
+  // ragged: number of valid values in [0, TILE]
+  const int lim = svx::tile_lim(len, TILE);
   if (lim == 0) return;  // the whole tile lies beyond the data: no load, v left as is
   if constexpr (LOADP == 2) {
     // Staged transpose: coalesced 16-byte loads (instruction k covers values
@@ -478,7 +476,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
     if (full && VEC) {
       float4 g[J];
 #pragma unroll
-      for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + 256 * k + 4 * lane);
+      for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + svx::tile_index(false, true, E, lane, k));
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -507,11 +505,11 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         if constexpr (VEC) {
-          const float4 g = ld4<NT>(p + e0 + 4 * j);
+          const float4 g = ld4<NT>(p + svx::tile_index(true, true, E, lane, j));
           v[4 * j] = g.x; v[4 * j + 1] = g.y; v[4 * j + 2] = g.z; v[4 * j + 3] = g.w;
         } else {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[4 * j + t] = ld1<NT>(p + e0 + 4 * j + t);
+          for (int t = 0; t < 4; ++t) v[4 * j + t] = ld1<NT>(p + svx::tile_index(true, false, E, lane, 4 * j + t));
         }
       }
       if (!full) {
@@ -524,8 +522,8 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
       // data: clamped 16-byte loads, every one issued
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int e = e0 + 4 * j;
-        const float4 g = ld4<NT>(p + (e < lim ? e : lim - 4));
+        const int e = svx::tile_index(true, true, E, lane, j);
+        const float4 g = ld4<NT>(p + svx::clamp_group(e, lim, 4));
         const bool in = e < lim;
         v[4 * j] = in ? g.x : 0.0f; v[4 * j + 1] = in ? g.y : 0.0f;
         v[4 * j + 2] = in ? g.z : 0.0f; v[4 * j + 3] = in ? g.w : 0.0f;
@@ -533,8 +531,8 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
     } else {
 #pragma unroll
       for (int i = 0; i < E; ++i) {
-        const int e = e0 + i;
-        const float g = p[e < last ? e : last];
+        const int e = svx::tile_index(true, false, E, lane, i);
+        const float g = p[svx::clamp_group(e, lim, 1)];
         v[i] = (e < lim) ? g : 0.0f;
       }
     }
@@ -544,8 +542,8 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
       float4 g[J];
 #pragma unroll
       for (int k = 0; k < J; ++k) {
-        const int e = 256 * k + 4 * lane;
-        const float4 t = ld4<NT>(p + (e < lim ? e : lim - 4));
+        const int e = svx::tile_index(false, true, E, lane, k);
+        const float4 t = ld4<NT>(p + svx::clamp_group(e, lim, 4));
         const bool in = e < lim;
         g[k] = make_float4(in ? t.x : 0.0f, in ? t.y : 0.0f, in ? t.z : 0.0f, in ? t.w : 0.0f);
       }
@@ -557,7 +555,7 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
     } else if (full && VEC) {
       float4 g[J];
 #pragma unroll
-      for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + 256 * k + 4 * lane);
+      for (int k = 0; k < J; ++k) g[k] = ld4<NT>(p + svx::tile_index(false, true, E, lane, k));
 #pragma unroll
       for (int k = 0; k < J; ++k) {
         const int e = 256 * k + 4 * lane;
@@ -567,11 +565,11 @@ __device__ __forceinline__ void load_tile(const float *__restrict__ p, int64_t l
       float g[E];
 #pragma unroll
       for (int k = 0; k < E; ++k) {
-        const int e = 64 * k + lane;
+        const int e = svx::tile_index(false, false, E, lane, k);
         if (full) {
           g[k] = ld1<NT>(p + e);
         } else {
-          const float t = p[e < last ? e : last];
+          const float t = p[svx::clamp_group(e, lim, 1)];
           g[k] = (e < lim) ? t : 0.0f;
         }
       }
@@ -612,9 +610,9 @@ struct Chunk {
   static constexpr int SIZE = 64 * E;
 
   __device__ static __forceinline__ int raw_index(int i, int lane) {
-    if constexpr (LOADP == 1) return lane * E + i;
-    else if constexpr (VEC) return 256 * (i / 4) + 4 * lane + (i % 4);
-    else return 64 * i + lane;
+    if constexpr (LOADP == 1) return svx::tile_index(true, false, E, lane, i);
+    else if constexpr (VEC) return svx::tile_index(false, true, E, lane, i / 4) + (i % 4);
+    else return svx::tile_index(false, false, E, lane, i);
   }
 
   // Loads of a chunk that lies wholly inside the data: no branch.
@@ -622,7 +620,7 @@ struct Chunk {
     if constexpr (VEC) {
 #pragma unroll
       for (int k = 0; k < J; ++k) {
-        const int e = (LOADP == 1) ? lane * E + 4 * k : 256 * k + 4 * lane;
+        const int e = svx::tile_index(LOADP == 1, true, E, lane, k);
         const float4 g = ld4<NT>(p + e);
         raw[4 * k] = g.x; raw[4 * k + 1] = g.y; raw[4 * k + 2] = g.z; raw[4 * k + 3] = g.w;
       }
@@ -633,12 +631,12 @@ struct Chunk {
   }
 
   __device__ static __forceinline__ void issue(const float *__restrict__ p, int64_t len, int lane, float (&raw)[E]) {
-    const int lim = len <= 0 ? 0 : (len >= SIZE ? SIZE : (int)len);
+    const int lim = svx::tile_lim(len, SIZE);
     if (lim == SIZE) {
       if constexpr (VEC) {
 #pragma unroll
         for (int k = 0; k < J; ++k) {
-          const int e = (LOADP == 1) ? lane * E + 4 * k : 256 * k + 4 * lane;
+          const int e = svx::tile_index(LOADP == 1, true, E, lane, k);
           const float4 g = ld4<NT>(p + e);
           raw[4 * k] = g.x; raw[4 * k + 1] = g.y; raw[4 * k + 2] = g.z; raw[4 * k + 3] = g.w;
         }
@@ -650,11 +648,10 @@ struct Chunk {
 #pragma unroll
       for (int i = 0; i < E; ++i) raw[i] = 0.0f;
     } else {
-      const int last = lim - 1;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const int e = raw_index(i, lane);
-        const float t = p[e < last ? e : last];
+        const float t = p[svx::clamp_group(e, lim, 1)];
         raw[i] = (e < lim) ? t : 0.0f;
       }
     }

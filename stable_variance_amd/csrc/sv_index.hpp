@@ -1,0 +1,326 @@
+// Index arithmetic and launch geometry of the library's kernels, as constexpr
+// functions: the kernels compute their global load indices with them and the
+// launchers their grids, and a host-only test evaluates the same functions
+// over whole planned launches (every workgroup, lane and load) to check that
+// each index lies inside the data and each launch within the dispatch
+// limits.  Plain C++17, no device code: constexpr functions are callable from
+// kernels as they are.  Indices count elements (floats, or doubles in the
+// float64 path) from the start of the array a kernel reads.
+#pragma once
+
+#include <stdint.h>
+
+namespace svx {
+
+// ---------------------------------------------------------------- limits and geometry constants
+
+constexpr int64_t SUM_MAX_N = 1LL << 36;        // tree sum: values per call
+constexpr int SUM_W = 4;                        // tree sum: waves per workgroup
+constexpr int SUM_MAX_BLOCKS = 8192;            // tree sum: workgroups of one launch
+constexpr int SUM_MAX_LOG2_GROUP = 16;          // tree sum: chunks per wave <= 2^16
+constexpr int64_t VAR_MAX_ELEMS = 1LL << 36;    // variance: rows * cols per call
+constexpr int64_t SEG_MAX_N = 512;              // rows that share waves
+constexpr int64_t ROWS_MAX_N = 16384;           // rows of one tile, any number of rows
+constexpr int64_t ROWS_ONE_MAX_N = 65536;       // rows of one workgroup when there are enough rows
+constexpr int64_t ROWS_ONE_MIN_ROWS = 256;
+constexpr int64_t LS_ROW_CHUNK = 64LL * 64 * 4; // long rows: 16384-value chunks (4 waves x 64 lanes x 64)
+constexpr int LS_TOP_PER_THREAD = 32;           // long rows: chunk nodes per thread of the top tree
+constexpr int LS_MAX_CHUNKS = 256 * LS_TOP_PER_THREAD;
+constexpr int CC_E = 16;                        // axis 0: rows per lane in a chunk
+constexpr int CC_MIN_W = 4;                     // axis 0: the workspace is sized for the shortest chunk
+constexpr int CC_GROUP = 32;                    // axis 0: chunk nodes per column k_cols_dq reduces for m itself
+constexpr int TOP_BIG_LEVELS = 16;              // axis 0: 64 * 64 * 2^15 chunk nodes per column
+constexpr int64_t COLS_MAX_R = 1024;            // axis 0: single-tile column kernels
+constexpr int64_t COLS_ONE_LONG_MAX_R = 4096;   // axis 0: columns read once
+constexpr int64_t C64_FUSED_MAX_N = 32768;      // complex rows reduced in one pass
+constexpr int KS_T = 64;                        // Kahan scan: values per chunk
+constexpr int KS_LEVELS = 16;                   // Kahan scan: 2^16 chunks
+
+// ---------------------------------------------------------------- clamps
+
+// A clamped load of w consecutive elements: e when the group starts inside
+// [0, lim), else the last whole group lim - w.  With lim a positive multiple
+// of w every group is wholly inside or wholly past the data.  (I: int for
+// indices inside one tile, which keeps them in 32-bit registers; int64_t
+// for indices into a whole array.)
+template <class I>
+constexpr I clamp_group(I e, I lim, int w) { return e < lim ? e : lim - w; }
+
+// An index clamped to the last of count (count >= 1).
+template <class I>
+constexpr I clamp_last(I i, I count) { return i < count ? i : count - 1; }
+
+// ---------------------------------------------------------------- row tiles
+
+// Data values of a tile of `tile` values whose data run has len values left.
+constexpr int tile_lim(int64_t len, int tile) { return len <= 0 ? 0 : (len >= tile ? tile : (int)len); }
+
+// Index in a tile of 64*E values of load k of `lane`: per-lane ranges (lane
+// owns [lane*E, lane*E + E)) or coalesced (16-byte load k covers the 256
+// values [256k, 256k + 256), 4-byte load k the 64 values [64k, 64k + 64)).
+// vec: 16-byte loads, k < E/4; else 4-byte loads, k < E.
+constexpr int tile_index(bool per_lane, bool vec, int E, int lane, int k) {
+  return per_lane ? lane * E + (vec ? 4 * k : k) : (vec ? 256 * k + 4 * lane : 64 * k + lane);
+}
+
+// Elements readable from the tile at `base` of row `row` to the end of the
+// last row of the launch: rows [row, nrows) of stride ld, the last n long.
+constexpr int64_t rows_avail(int64_t nrows, int64_t row, int64_t ld, int64_t n, int64_t base) {
+  return (nrows - 1 - row) * ld + (n - base);
+}
+
+// The range of virtual lane 2 (L mod 32) + L / 32 held by lane L (the order
+// in which the d and d^2 trees share their cross-lane levels).
+constexpr int vlane_pair32(int lane) { return 2 * (lane & 31) + (lane >> 5); }
+
+// Workgroup b of nb runs on die b mod 8; the renumbering that gives each die
+// one contiguous run of logical indices (die x takes the x-th run, the first
+// nb mod 8 runs one longer).  A bijection of [0, nb).
+constexpr int xcd_contiguous(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, die = b & 7, i = b >> 3;
+  return (die < r ? die * (q + 1) : r * (q + 1) + (die - r) * q) + i;
+}
+
+// Short rows sharing waves: the row of `lane` in wave w of workgroup b, S
+// lanes per row, 64/S rows per wave, four waves per workgroup.
+constexpr int64_t seg_row(int64_t b, int w, int lane, int S) { return (b * 4 + w) * (64 / S) + lane / S; }
+
+// ---------------------------------------------------------------- column tiles
+
+// First of the V adjacent columns a lane loads: c0, or the last V columns
+// when c0 lies past the matrix (C >= V).
+constexpr int64_t cols_first(int64_t c0, int64_t C, int V) { return c0 < C ? c0 : C - V; }
+
+// Column block of workgroup b of nb when blocks of nc < 32 columns share a
+// 128-byte line with the next P - 1 blocks (P = 32 / nc): within each full
+// group of 8P workgroups, the P that run on one die (b mod 8) take P adjacent
+// blocks.  A bijection of [0, nb).
+template <class I>
+constexpr I line_on_one_die(I b, I nb, int nc) {
+  if (nc >= 32) return b;
+  const I P = 32 / nc, grp = b / (8 * P), r = b % (8 * P);
+  return (grp + 1) * (8 * P) <= nb ? grp * (8 * P) + P * (r % 8) + r / 8 : b;
+}
+
+// ---------------------------------------------------------------- launch plans
+
+// Work-items of one launch: at most 2^32 - 1.
+constexpr int64_t MAX_LAUNCH_ITEMS = 0xffffffffLL;
+
+// Rows per launch of a launcher that gives each workgroup per_block rows and
+// `threads` work-items (the batch of in_batches).
+constexpr int64_t batch_rows(int64_t per_block, int64_t threads) {
+  return (MAX_LAUNCH_ITEMS / threads) * per_block;
+}
+
+// The tree sum: chunks of 64*e values, SUM_W-wave workgroups, each wave
+// streaming 2^log2_g consecutive chunks; log2_g is the smallest value that
+// keeps the workgroup count at or below target_blocks (clamped to
+// [1, max_blocks]), capped at max_log2_g.
+struct SumPlan {
+  int e;
+  int log2_g;
+  int64_t blocks;
+};
+constexpr SumPlan plan_sum(int64_t n, int e, int64_t target_blocks, int sum_w, int64_t max_blocks, int max_log2_g) {
+  const int64_t chunk = 64LL * e;
+  const int64_t chunks = (n + chunk - 1) / chunk;
+  const int64_t waves = (chunks + sum_w - 1) / sum_w;
+  if (target_blocks > max_blocks) target_blocks = max_blocks;
+  if (target_blocks < 1) target_blocks = 1;
+  int g = 0;
+  while (g < max_log2_g && ((waves + (1LL << g) - 1) >> g) > target_blocks) ++g;
+  return {e, g, (waves + (1LL << g) - 1) >> g};
+}
+
+// Waves per 4096 values of a row of 1025..16384 values when var_split is 0:
+// four waves per row for tiles of up to 4096 values and eight above.
+constexpr int auto_split(int64_t n) {
+  int64_t tile = 2048;
+  while (tile < n) tile *= 2;
+  const int64_t w = tile <= 4096 ? 4 : 8;
+  return (int)(64 * 64 * w / tile);
+}
+
+// Axis 1, one workgroup per row (rows of 257..65536 values not on the
+// short-row path): E values per lane, W waves.  split: var_split (0 auto).
+struct RowsPlan {
+  int E, W;
+};
+constexpr RowsPlan rows_plan(int64_t n, int split) {
+  if (n <= 256) return {4, 1};
+  if (n <= 1024) return {16, 1};
+  const int s = split != 0 ? split : auto_split(n);
+  if (n <= 2048) return s <= 2 ? RowsPlan{32, 1} : s == 4 ? RowsPlan{16, 2} : RowsPlan{8, 4};
+  if (n <= 4096)
+    return s == 1 ? RowsPlan{64, 1} : s == 2 ? RowsPlan{32, 2} : s == 4 ? RowsPlan{16, 4} : RowsPlan{8, 8};
+  if (n <= 8192)
+    return s == 1 ? RowsPlan{64, 2} : s == 2 ? RowsPlan{32, 4} : s == 4 ? RowsPlan{16, 8} : RowsPlan{8, 16};
+  if (n <= 16384) return s == 1 ? RowsPlan{64, 4} : s == 2 ? RowsPlan{32, 8} : RowsPlan{16, 16};
+  if (n <= 32768) return {32, 16};
+  return {64, 16};
+}
+
+// Waves a row of n values reaches in a plan of W waves of 64*E values.
+constexpr int rows_waves(int64_t n, int E, int W) {
+  const int64_t reach = (n + 64 * E - 1) / (64 * E);
+  return reach < W ? (int)reach : W;
+}
+
+// The ablation variants' rows (up to 16384 values, one workgroup per row).
+constexpr RowsPlan variant_rows_plan(int64_t n) {
+  if (n <= 256) return {4, 1};
+  if (n <= 1024) return {16, 1};
+  if (n <= 4096) return {32, 2};
+  return {64, 4};
+}
+
+// Short rows (n <= 512): E values per lane and S lanes per row, S*E the
+// row's power-of-two tile.
+struct SegPlan {
+  int E, S;
+};
+constexpr SegPlan seg_plan(int64_t n) {
+  if (n <= 4) return {4, 1};
+  if (n <= 8) return {8, 1};
+  if (n <= 16) return {16, 1};
+  if (n <= 32) return {16, 2};
+  if (n <= 64) return {16, 4};
+  if (n <= 128) return {16, 8};
+  if (n <= 256) return {16, 16};
+  return {16, 32};
+}
+
+// Load width of the short-row kernel: 4 floats for 16-byte aligned rows of
+// a multiple of 4 values, 2 for 8-byte aligned rows of an even count, else 1.
+constexpr int seg_vw(uint64_t addr, int64_t ld) {
+  return (addr % 16 == 0 && ld % 4 == 0) ? 4 : (addr % 8 == 0 && ld % 2 == 0) ? 2 : 1;
+}
+
+// Complex rows of up to 32768 values in one pass: E values per lane, W waves.
+constexpr RowsPlan c64_rows_plan(int64_t n) {
+  if (n <= 256) return {4, 1};
+  if (n <= 1024) return {16, 1};
+  if (n <= 2048) return {16, 2};
+  if (n <= 4096) return {16, 4};
+  if (n <= 8192) return {16, 8};
+  if (n <= 16384) return {16, 16};
+  return {32, 16};
+}
+
+// Axis 0, lane per column (k_var_cols): E rows per lane, W waves, 64 columns
+// per workgroup.
+constexpr RowsPlan cols_lane_plan(int64_t R) {
+  if (R <= 4) return {4, 1};
+  if (R <= 16) return {16, 1};
+  if (R <= 64) return {64, 1};
+  if (R <= 128) return {64, 2};
+  if (R <= 256) return {64, 4};
+  if (R <= 512) return {64, 8};
+  return {64, 16};
+}
+
+// Axis 0, columns of fewer than 16 rows: E rows per lane (the power of two
+// at or above R, at least 2), four columns per lane.
+constexpr int cols_short_e(int64_t R) { return R <= 2 ? 2 : R <= 4 ? 4 : R <= 8 ? 8 : 16; }
+
+// Axis 0, 65..1024 rows in one launch (k_cols_one): G row groups per wave,
+// W waves, 16 rows per lane, V adjacent columns per lane; 16*G*W is the power
+// of two at or above R and V*64/G columns per workgroup.
+struct ColsOnePlan {
+  int G, W;
+  int64_t blocks;
+};
+// Four columns per lane: of the (G, W) pairs that hold exactly that many
+// rows (G in 1, 4, 16; W up to 8), the smallest G that still gives 512
+// workgroups, else the largest.
+constexpr ColsOnePlan cols_one4_plan(int64_t R, int64_t C) {
+  int64_t cap = 16;
+  while (cap < R) cap *= 2;
+  const int gw = (int)(cap / 16);
+  int g = gw >= 16 ? gw / 8 : 1;
+  if (g == 2 || g == 8) g *= 2;
+  while (g < 16 && g * 4 <= gw && (C + 4 * 64 / g - 1) / (4 * 64 / g) < 512) g *= 4;
+  return {g, gw / g, (C + 4 * 64 / g - 1) / (4 * 64 / g)};
+}
+// One column per lane: G in 1, 4 (row segments of at least 16 lanes), W up
+// to 16; G = 1 when that gives 512 workgroups.
+constexpr ColsOnePlan cols_one1_plan(int64_t R, int64_t C) {
+  int64_t cap = 16;
+  while (cap < R) cap *= 2;
+  const int gw = (int)(cap / 16);
+  const int g = (gw > 16 || (C + 63) / 64 < 512) && gw >= 8 ? 4 : 1;
+  return {g, gw / g, (C + 64 / g - 1) / (64 / g)};
+}
+
+// Axis 0, 1025..4096 rows read once: sixteen columns per workgroup, E rows
+// per lane (32 up to 2048 rows, else 64), four row groups per wave, the waves
+// the column's rows reach; mode 1 when every wave is full, else 2.
+struct ColsLongPlan {
+  int E, waves, mode;
+  int64_t blocks;
+};
+constexpr ColsLongPlan cols_long_plan(int64_t R, int64_t C) {
+  const int e = R <= 2048 ? 32 : 64;
+  return {e, (int)((R + 4 * e - 1) / (4 * e)), (R == 2048 || R == 4096) ? 1 : 2, (C + 15) / 16};
+}
+
+// Axis 0 in row chunks: G row groups per wave (lanes stay on columns: G = 1
+// for at least 64 groups of V columns, 4 for 5..63, 16 for 2..4, 64 for
+// one), chunks of 16*W*G rows, V*64/G columns per block.
+struct ColsChunkPlan {
+  int G;
+  int64_t nch, ncb;
+};
+constexpr ColsChunkPlan cols_chunk_plan(int V, int W, int64_t R, int64_t C) {
+  const int64_t groups = (C + V - 1) / V;
+  const int g = groups >= 64 ? 1 : groups > 4 ? 4 : groups > 1 ? 16 : 64;
+  const int64_t ch = 16LL * W * g;
+  const int nc = V * (64 / g);
+  return {g, (R + ch - 1) / ch, (C + nc - 1) / nc};
+}
+
+// ---------------------------------------------------------------- float32 variance routes
+
+// The launch path of a float32 variance of a [rows, cols] matrix (n > 0
+// values per slice), given the launch knobs and, for columns of 1025..4096
+// rows, whether the one-read grid fills the chip (one_read_fills).
+enum class Route {
+  LONG_ROWS_CHUNKED,  // axis 1, rows longer than one tile: chunk launches
+  ROWS_SEG,           // axis 1, short rows sharing waves
+  ROWS_TILE,          // axis 1, one workgroup per row (rows_plan)
+  COLS_ONE_READ,      // axis 0, 1025..4096 rows read once (cols_long_plan)
+  COLS_CHUNKED,       // axis 0, row chunks (cols_chunk_plan)
+  COLS_SHORT,         // axis 0, fewer than 16 rows, four columns per lane
+  COLS_ONE4,          // axis 0, 65..1024 rows, four columns per lane (cols_one4_plan)
+  COLS_ONE1,          // axis 0, 65..1024 rows, one column per lane (cols_one1_plan)
+  COLS_LANE,          // axis 0, a lane per column (cols_lane_plan)
+};
+struct RouteKnobs {
+  int var_long_rows, var_cols_once, var_cols_single_max, var_short_rows, var_cols_short, var_cols_one;
+};
+// Columns that are candidates for the one-read launch.
+constexpr bool cols_one_read_candidate(bool ax1, int64_t n, const RouteKnobs &k) {
+  return !ax1 && n > COLS_MAX_R && n <= COLS_ONE_LONG_MAX_R && k.var_cols_once != 0 &&
+         k.var_cols_single_max == COLS_MAX_R;
+}
+// vec16: the matrix starts 16-byte aligned and cols is a multiple of 4.
+constexpr Route f32_route(int64_t rows, int64_t cols, bool ax1, bool vec16, const RouteKnobs &k,
+                          bool one_read_fills) {
+  const int64_t n = ax1 ? cols : rows;
+  if (ax1 && n > ROWS_MAX_N && !(k.var_long_rows && n <= ROWS_ONE_MAX_N && rows >= ROWS_ONE_MIN_ROWS))
+    return Route::LONG_ROWS_CHUNKED;
+  if (cols_one_read_candidate(ax1, n, k) && (k.var_cols_once == 2 || one_read_fills)) return Route::COLS_ONE_READ;
+  if (!ax1 && n > k.var_cols_single_max) return Route::COLS_CHUNKED;
+  if (ax1) return n <= SEG_MAX_N && k.var_short_rows ? Route::ROWS_SEG : Route::ROWS_TILE;
+  if (n < 16 && k.var_cols_short && vec16) return Route::COLS_SHORT;
+  if (k.var_cols_one && n > 64) {
+    // four columns per lane for long columns (513..1024 rows) of wide
+    // matrices, else one
+    const bool four = cols >= 4 && (k.var_cols_one == 2 || (k.var_cols_one == 1 && n > 512 && cols >= 8192));
+    return four ? Route::COLS_ONE4 : Route::COLS_ONE1;
+  }
+  return Route::COLS_LANE;
+}
+
+}  // namespace svx

@@ -227,9 +227,9 @@ __device__ __forceinline__ Node load_node_agent(const Node *src) {
 
 // ------------------------------------------------------------------ tree sum
 
-constexpr int SUM_W = 4;                            // waves per workgroup
-constexpr int SUM_MAX_BLOCKS = 8192;                // workgroups of one tree-sum launch
-constexpr int SUM_MAX_LOG2_GROUP = 16;              // chunks per wave <= 2^16
+using svx::SUM_W;                // waves per workgroup
+using svx::SUM_MAX_BLOCKS;       // workgroups of one tree-sum launch
+using svx::SUM_MAX_LOG2_GROUP;   // chunks per wave <= 2^16
 constexpr int SUM_GROUP = 64;                       // workgroups per first-level ticket
 static_assert(SV_TREE_SUM_COUNTER_BYTES == 256 * (1 + SUM_MAX_BLOCKS / SUM_GROUP), "header constant");
 constexpr int SUM_COUNTER_STRIDE = 64;              // counters 256 bytes apart
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
   const int64_t base = (int64_t)w * 64 * E;  // first complex value of this wave
   const bool empty = base >= n;
   float f[2 * E];
-  const int64_t avail = 2 * (((int64_t)gridDim.x - 1 - row) * n + (n - base));  // floats to the array's end
+  const int64_t avail = 2 * svx::rows_avail(gridDim.x, row, n, n, base);  // floats to the launch's last row
   sv::load_tile<2 * E, VEC, 1, false>(p + 2 * base, 2 * (n - base), nullptr, f, lane, avail);
   const float x0r = p[0], x0i = p[1];
   const bool full = base + 64 * E <= n;
@@ -532,13 +532,12 @@ template <int E, int S, int VW2>
 __global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restrict__ z, int64_t rows, int64_t n,
                                                           int64_t ddof, float *__restrict__ var_out,
                                                           float *__restrict__ mean_out) {
-  constexpr int RPW = 64 / S;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane % S;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / S;
+  const int64_t row = svx::seg_row(blockIdx.x, w, lane, S);
   const bool rowok = row < rows;
-  const float *__restrict__ p = z + 2 * (rowok ? row : rows - 1) * n;
+  const float *__restrict__ p = z + 2 * svx::clamp_last(row, rows) * n;
   const bool full = (n == (int64_t)S * E);
   const int64_t e0 = (int64_t)l * E;
   const int64_t left = n - e0;
@@ -548,14 +547,14 @@ __global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restric
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
       const int64_t e = e0 + 2 * j;
-      const float4 g = *reinterpret_cast<const float4 *>(p + 2 * (full || e < n ? e : n - 2));
+      const float4 g = *reinterpret_cast<const float4 *>(p + 2 * (full ? e : svx::clamp_group(e, n, 2)));
       re[2 * j] = g.x; im[2 * j] = g.y; re[2 * j + 1] = g.z; im[2 * j + 1] = g.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int64_t e = e0 + i;
-      const float2 g = *reinterpret_cast<const float2 *>(p + 2 * (full || e < n ? e : n - 1));
+      const float2 g = *reinterpret_cast<const float2 *>(p + 2 * (full ? e : svx::clamp_group(e, n, 1)));
       re[i] = g.x; im[i] = g.y;
     }
   }
@@ -758,7 +757,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
   // them (the branch is wave-uniform).
   const bool empty = base >= n;
   float v[E];
-  const int64_t avail = ((int64_t)gridDim.x - 1 - row) * ld + (n - base);  // to the matrix's end
+  const int64_t avail = svx::rows_avail(gridDim.x, row, ld, n, base);  // to the launch's last row
   sv::load_tile<E, VEC, LOADP, NT>(p + base, n - base, lds + w * LPW, v, vl, avail);
   const float x0 = p[0];
 
@@ -858,13 +857,12 @@ template <int E, int S, int VW>
 __global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ x, int64_t rows, int64_t n,
                                                       int64_t ld, int64_t ddof, float *__restrict__ var_out,
                                                       float *__restrict__ mean_out) {
-  constexpr int RPW = 64 / S;  // rows per wave
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane % S;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / S;
+  const int64_t row = svx::seg_row(blockIdx.x, w, lane, S);  // 64/S rows per wave
   const bool rowok = row < rows;
-  const float *__restrict__ p = x + (rowok ? row : rows - 1) * ld;  // past the last row: read it again
+  const float *__restrict__ p = x + svx::clamp_last(row, rows) * ld;  // past the last row: read it again
   const bool full = (n == (int64_t)S * E);                           // uniform
   const int64_t e0 = (int64_t)l * E;
   const int64_t left = n - e0;
@@ -878,21 +876,21 @@ __global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ 
 #pragma unroll
     for (int j = 0; j < E / 4; ++j) {
       const int64_t e = e0 + 4 * j;
-      const float4 g = *reinterpret_cast<const float4 *>(p + (full || e < n ? e : n - 4));
+      const float4 g = *reinterpret_cast<const float4 *>(p + (full ? e : svx::clamp_group(e, n, 4)));
       v[4 * j] = g.x; v[4 * j + 1] = g.y; v[4 * j + 2] = g.z; v[4 * j + 3] = g.w;
     }
   } else if constexpr (VW == 2) {
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
       const int64_t e = e0 + 2 * j;
-      const float2 g = *reinterpret_cast<const float2 *>(p + (full || e < n ? e : n - 2));
+      const float2 g = *reinterpret_cast<const float2 *>(p + (full ? e : svx::clamp_group(e, n, 2)));
       v[2 * j] = g.x; v[2 * j + 1] = g.y;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int64_t e = e0 + i;
-      v[i] = p[full || e < n ? e : n - 1];
+      v[i] = p[full ? e : svx::clamp_group(e, n, 1)];
     }
   }
   const float x0 = p[0];
@@ -917,7 +915,8 @@ __global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ 
 
 template <int E, int W, int V = V_KERNEL>
 __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
-                                                     float *__restrict__ var_out, float *__restrict__ mean_out) {
+                                                     float *__restrict__ var_out, float *__restrict__ mean_out,
+                                                     int64_t b0) {
   using F = VariantFlags<V>;
   __shared__ Node sy[W][64];
   __shared__ Node sd[W][64];
@@ -925,15 +924,16 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t blk = b0 + blockIdx.x;  // launches of at most 2^32 - 1 work-items
+  const int64_t col = blk * 64 + lane;
   const bool colok = col < C;
   const int64_t r0 = (int64_t)w * E;
 
   // Loads: for a fixed row the 64 lanes read 64 consecutive floats.  Out of
   // range rows/columns read a clamped in-range address and are replaced by 0.
   const bool full = r0 + E <= R;
-  const bool allcols = (int64_t)blockIdx.x * 64 + 64 <= C;
-  const int64_t ccol = colok ? col : C - 1;
+  const bool allcols = blk * 64 + 64 <= C;
+  const int64_t ccol = svx::clamp_last(col, C);
   float v[E];
   if (full && allcols) {
 #pragma unroll
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int64_t r = r0 + i;
-      const float t = x[(r < R ? r : R - 1) * C + ccol];
+      const float t = x[svx::clamp_last(r, R) * C + ccol];
       v[i] = (colok && r < R) ? t : 0.0f;
     }
   }
@@ -1017,9 +1017,9 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 //               of lanes (up to 32 chunks) or a wave per column (k_cols_top,
 //               k_cols_top_big)
 
-constexpr int CC_E = 16;             // rows per lane in a chunk
-constexpr int CC_MIN_W = 4;          // the workspace is sized for the shortest chunk
-constexpr int CC_GROUP = 32;         // chunk nodes per column that k_cols_dq reduces for m itself
+using svx::CC_E;                     // rows per lane in a chunk
+using svx::CC_MIN_W;                 // the workspace is sized for the shortest chunk
+using svx::CC_GROUP;                 // chunk nodes per column that k_cols_dq reduces for m itself
 
 struct ColsWs {
   Node *ny;  // [nch][C] y-tree node of each chunk of each column
@@ -1036,10 +1036,10 @@ struct ColsWs {
 template <int V, int E, bool VEC16 = true>
 __device__ __forceinline__ void load_cols_tile(const float *__restrict__ x, int64_t R, int64_t C, int64_t c0,
                                                int64_t r0, bool full, float (&v)[V][E]) {
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const int64_t r = full ? r0 + i : (r0 + i < R ? r0 + i : R - 1);
+    const int64_t r = full ? r0 + i : svx::clamp_last(r0 + i, R);
     const float *p = x + r * C + cc;
     if constexpr (V == 4 && VEC16) {
       const float4 g = *reinterpret_cast<const float4 *>(p);
@@ -1051,7 +1051,7 @@ __device__ __forceinline__ void load_cols_tile(const float *__restrict__ x, int6
       // columns past C (a partial last group of an odd width) read the last
       // column instead; their results are never written
 #pragma unroll
-      for (int k = 0; k < V; ++k) v[k][i] = x[r * C + (cc + k < C ? cc + k : C - 1)];
+      for (int k = 0; k < V; ++k) v[k][i] = x[r * C + svx::clamp_last(cc + k, C)];
     }
   }
 }
@@ -1073,14 +1073,15 @@ __device__ __forceinline__ void shift_cols_tile(float (&v)[V][E], const float (&
 // matrices take G up to 64 so that no lane idles.  Chunks of W*G*E rows.
 template <int V, int W, int G>
 __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
-                                                   ColsWs ws) {
+                                                   ColsWs ws, int64_t b0) {
   constexpr int E = CC_E, Q = 64 / G, NC = V * Q;
   static_assert(64 * W >= NC, "one thread per column of the block");
   __shared__ Node s[W][V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t blk = b0 + blockIdx.x;  // launches of at most 2^32 - 1 work-items
+  const int64_t cb = blk / nch, j = blk % nch;
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
@@ -1092,7 +1093,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_y(const float *__restrict__ x, 
   float v[V][E];
   load_cols_tile<V, E>(x, R, C, c0, r0, full, v);
   float x0[V];
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
 #pragma unroll
   for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
   shift_cols_tile<V, E>(v, x0, wave_full, valid);
@@ -1125,7 +1126,7 @@ __device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int6
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int64_t idx = b * 8 + k;
-      const Node t = p[(idx < nch ? idx : nch - 1) * stride];
+      const Node t = p[svx::clamp_last(idx, nch) * stride];
       nd[k] = idx < nch ? t : sv::zero_node();
     }
     sub[b] = sv::node_tree<0, 8, 8, sv::Y_KIND>(nd);
@@ -1141,22 +1142,22 @@ __device__ __forceinline__ Node chunk_tree_1(const Node *p, int64_t stride, int6
 template <int PASS, int K, int S>
 __global__ __launch_bounds__(256) void k_cols_top(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
                                                   int64_t ddof, ColsWs ws, float *__restrict__ var_out,
-                                                  float *__restrict__ mean_out) {
+                                                  float *__restrict__ mean_out, int64_t b0) {
   constexpr int PW = 64 / S;
   const int lane = threadIdx.x & 63;
-  const int64_t col0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PW;
+  const int64_t col0 = ((b0 + blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PW;
   if (col0 >= C) return;  // the whole wave
   const int64_t col = col0 + lane / S;
   const int sl = lane % S;
   const bool colok = col < C;
-  const int64_t cc = colok ? col : C - 1;
+  const int64_t cc = svx::clamp_last(col, C);
   auto tree = [&](const Node *p, auto kind) {
     constexpr int KIND = decltype(kind)::value;
     Node nd[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t idx = (int64_t)sl * K + k;
-      const Node t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+      const Node t = p[svx::clamp_last(idx, nch) * C];  // every load issued
       nd[k] = idx < nch ? t : sv::zero_node();
     }
     return sv::seg_tree<KIND, S>(sv::node_tree<0, K, K, KIND>(nd));
@@ -1178,14 +1179,15 @@ __global__ __launch_bounds__(256) void k_cols_top(const float *__restrict__ x, i
 // order with a binary counter (the loop is wave-uniform, so every stack
 // index is a constant), then the wave's six levels.  PASS 0: m; PASS 1:
 // step 4.
-constexpr int TOP_BIG_LEVELS = 16;  // P up to 2^15: 2^27 chunks per column
+using svx::TOP_BIG_LEVELS;  // P up to 2^15: 2^27 chunks per column
 template <int PASS>
 __global__ __launch_bounds__(256) void k_cols_top_big(const float *__restrict__ x, int64_t R, int64_t C,
                                                       int64_t nch, int log2p, int64_t ddof, ColsWs ws,
-                                                      float *__restrict__ var_out, float *__restrict__ mean_out) {
+                                                      float *__restrict__ var_out, float *__restrict__ mean_out,
+                                                      int64_t b0) {
   constexpr int K = 64;
   const int lane = threadIdx.x & 63;
-  const int64_t col = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t col = (b0 + blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (col >= C) return;  // the whole wave
   const int64_t P = (int64_t)1 << log2p;
   auto tree = [&](const Node *p, auto kind) {
@@ -1199,7 +1201,7 @@ __global__ __launch_bounds__(256) void k_cols_top_big(const float *__restrict__ 
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int64_t idx = i0 + k;
-        const Node t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+        const Node t = p[svx::clamp_last(idx, nch) * C];  // every load issued
         nd[k] = idx < nch ? t : sv::zero_node();
       }
       Node carry = sv::node_tree<0, K, K, KIND>(nd);
@@ -1238,7 +1240,7 @@ __global__ __launch_bounds__(256) void k_cols_top_big(const float *__restrict__ 
 // Tile layout as in k_cols_y.
 template <int V, int W, int G, bool MLOCAL>
 __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x, int64_t R, int64_t C, int64_t nch,
-                                                    ColsWs ws) {
+                                                    ColsWs ws, int64_t b0) {
   constexpr int E = CC_E, Q = 64 / G, NC = V * Q;
   static_assert(64 * W >= NC, "one thread per column of the block");
   __shared__ Node sd[W][V][Q];
@@ -1247,7 +1249,8 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t blk = b0 + blockIdx.x;  // launches of at most 2^32 - 1 work-items
+  const int64_t cb = blk / nch, j = blk % nch;
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);
   const int64_t r0 = rw + (int64_t)g * E;
@@ -1257,13 +1260,13 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
 
   float x0[V], m[V];
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
   if constexpr (MLOCAL) {
     const int t = threadIdx.x;
     if (t < NC) {
       const int k = t / Q, qq = t % Q;  // column V*qq + k of the block, clamped like the loads
       const int64_t col = cb * NC + (int64_t)qq * V + k;
-      const int64_t ccol = col < C ? col : C - 1;
+      const int64_t ccol = svx::clamp_last(col, C);
       sm[k][qq] = sv::root_value_k<sv::Y_KIND>(chunk_tree_1(ws.ny + ccol, C, nch)) / (float)R;
     }
     __syncthreads();
@@ -1320,7 +1323,8 @@ __global__ __launch_bounds__(64 * W) void k_cols_dq(const float *__restrict__ x,
 // two paths of MODE 0 would keep two copies of the shifted tile).
 template <int V, int W, int G, bool VEC16, int E = CC_E, int MODE = 0>
 __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
-                                                     float *__restrict__ var_out, float *__restrict__ mean_out) {
+                                                     float *__restrict__ var_out, float *__restrict__ mean_out,
+                                                     int b0) {
   constexpr int Q = 64 / G, NC = V * Q;
   __shared__ Node sd[W][V][Q];
   __shared__ Node sq[W][V][Q];
@@ -1336,12 +1340,9 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   // robin to the eight dies, each with its own L2, so block b would run on
   // die b % 8 and P dies would fetch the same line.  Within each full group
   // of 8P workgroups, the P on one die take P adjacent blocks instead.
-  int64_t cb = blockIdx.x;
-  if constexpr (NC < 32) {
-    constexpr int P = 32 / NC;
-    const int64_t grp = cb / (8 * P), r = cb % (8 * P);
-    if ((grp + 1) * (8 * P) <= (int64_t)gridDim.x) cb = grp * (8 * P) + P * (r % 8) + r / 8;
-  }
+  // b0: the launch's first workgroup (launches of at most 2^32 - 1
+  // work-items; fewer than 2^31 workgroups in all)
+  const int64_t cb = svx::line_on_one_die<int>(b0 + (int)blockIdx.x, (int)((C + NC - 1) / NC), NC);
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
@@ -1356,9 +1357,9 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
   // value wait for all of them
   if (MODE != 0 || rw < R) load_cols_tile<V, E, VEC16>(x, R, C, c0, r0, full, v);
   float x0[V];
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
 #pragma unroll
-  for (int k = 0; k < V; ++k) x0[k] = x[cc + k < C ? cc + k : C - 1];
+  for (int k = 0; k < V; ++k) x0[k] = x[svx::clamp_last(cc + k, C)];
   shift_cols_tile<V, E>(v, x0, wave_full, valid);  // +0 past the last row
 #pragma unroll
   for (int k = 0; k < V; ++k) {
@@ -1375,11 +1376,17 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
     sm[tk][tq] = sv::root_value_k<sv::Y_KIND>(sv::node_tree<0, W, W, sv::Y_KIND>(nn)) / (float)R;
   }
   __syncthreads();
+  // The step-3 masks are compared afresh from an opaque copy of `valid`:
+  // with E = 64 rows per lane, keeping the step-1 masks (one 64-bit scalar
+  // pair per row) alive across the barrier would overflow the scalar
+  // registers into vector ones and spill.
+  int valid_dq = valid;
+  if constexpr (MODE == 2) asm volatile("" : "+v"(valid_dq));
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     Node nd, nq;
     if (wave_full) sv::lane_tree_dq<false, 0, E, E>(v[k], sm[k][q], E, nd, nq);
-    else sv::lane_tree_dq<true, 0, E, E>(v[k], sm[k][q], valid, nd, nq);
+    else sv::lane_tree_dq<true, 0, E, E>(v[k], sm[k][q], valid_dq, nd, nq);
     nd = sv::seg_tree<sv::NODE_TWOSUM, G>(nd);
     nq = sv::seg_tree<sv::NODE_NN, G>(nq);
     if (g == 0) {
@@ -1413,9 +1420,9 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
 // read twice.  Workspace per row: nchunks y nodes, 2*nchunks d/d^2 nodes and
 // m.
 
-constexpr int LS_TOP_PER_THREAD = 32;                      // chunk nodes per thread at the top
-constexpr int LS_MAX_CHUNKS = 256 * LS_TOP_PER_THREAD;     // 8192 chunks per slice
-constexpr int64_t LS_ROW_CHUNK = 64LL * 64 * 4;            // axis 1: 16384 values (4 waves x 64 lanes x 64)
+using svx::LS_TOP_PER_THREAD;  // chunk nodes per thread at the top
+using svx::LS_MAX_CHUNKS;      // 8192 chunks per slice
+using svx::LS_ROW_CHUNK;       // axis 1: 16384 values (4 waves x 64 lanes x 64)
 
 struct LongWs {
   Node *ny;   // [nslices][nch]
@@ -1438,7 +1445,7 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
   const int64_t base = c * LS_ROW_CHUNK + (int64_t)w * 64 * E;
   float v[E];
   float dummy_lds[1];
-  const int64_t avail = ((int64_t)gridDim.x / nch - 1 - r) * ld + (n - base);  // to the matrix's end
+  const int64_t avail = svx::rows_avail(gridDim.x / nch, r, ld, n, base);  // to the launch's last row
   sv::load_tile<E, VEC, 1, false>(row + base, n - base, dummy_lds, v, lane, avail);
   const float x0 = row[0];
   const bool full = base + 64 * E <= n;
@@ -1483,7 +1490,7 @@ __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t idx = (int64_t)threadIdx.x * K + k;
-    const Node t = nodes[idx < nch ? idx : nch - 1];  // unconditional: the loads overlap
+    const Node t = nodes[svx::clamp_last(idx, nch)];  // unconditional: the loads overlap
     nd[k] = idx < nch ? t : sv::zero_node();
   }
   Node r = sv::node_tree<0, K, K, KIND>(nd);
@@ -1513,7 +1520,7 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
 
 // ------------------------------------------------------------------ host side
 
-constexpr int64_t C64_FUSED_MAX_N = 32768;  // complex rows reduced in one pass (k_var_rows_c64)
+using svx::C64_FUSED_MAX_N;  // complex rows reduced in one pass (k_var_rows_c64)
 
 // Launch-geometry tuning (never changes a result bit).  Each host thread has
 // its own settings: sv_set_tuning on one thread leaves the calls of every
@@ -1554,15 +1561,15 @@ StepConsts step_consts(int64_t n, int64_t ddof) {
   return k;
 }
 
-constexpr int64_t SUM_MAX_N = 1LL << 36;
-constexpr int64_t VAR_MAX_ELEMS = 1LL << 40;
-constexpr int64_t ROWS_MAX_N = 16384;  // single-tile row kernel for any number of rows
+using svx::SUM_MAX_N;
+using svx::VAR_MAX_ELEMS;
+using svx::ROWS_MAX_N;  // single-tile row kernel for any number of rows
 // Rows of up to 65536 values also take one workgroup per row (16 waves) when
 // there are enough rows to fill the chip; fewer rows take the chunked path.
-constexpr int64_t ROWS_ONE_MAX_N = 65536;
-constexpr int64_t ROWS_ONE_MIN_ROWS = 256;
-constexpr int64_t COLS_MAX_R = 1024;   // single-tile column kernel
-constexpr int64_t COLS_ONE_LONG_MAX_R = 4096;  // one column per lane, 64 rows per lane, 16 waves
+using svx::ROWS_ONE_MAX_N;
+using svx::ROWS_ONE_MIN_ROWS;
+using svx::COLS_MAX_R;           // single-tile column kernel
+using svx::COLS_ONE_LONG_MAX_R;  // one column per lane, 64 rows per lane, 16 waves
 
 // Long-slice workspace: y, d and d^2 chunk nodes per slice, then m.
 size_t long_ws_bytes(int64_t nslices, int64_t nch) {
@@ -1609,44 +1616,62 @@ ColsWs cols_ws(void *workspace, const ColsLayout &L) {
 template <int V, int W, int G>
 void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var,
                          float *mean, hipStream_t st) {
-  constexpr int64_t CH = (int64_t)CC_E * W * G;  // rows per chunk
-  constexpr int NC = V * (64 / G);                // columns per block
-  const int64_t nch = (R + CH - 1) / CH;
-  const int64_t ncb = (C + NC - 1) / NC;
-  const dim3 grid((unsigned)(ncb * nch)), block(64 * W);
-  k_cols_y<V, W, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-  auto per_waves = [&](int per_wave) { return dim3((unsigned)((C + 4 * per_wave - 1) / (4 * per_wave))); };
+  const svx::ColsChunkPlan p = svx::cols_chunk_plan(V, W, R, C);  // G = p.G
+  const int64_t nch = p.nch, ncb = p.ncb;
+  const dim3 block(64 * W);
+  // workgroup b = cb * nch + j takes chunk j of column block cb
+  svh::in_batches(ncb * nch, 1, 64 * W, [&](int64_t b0, int64_t nb) {
+    k_cols_y<V, W, G><<<dim3((unsigned)nb), block, 0, st>>>(x, R, C, nch, ws, b0);
+  });
+  auto dq = [&](auto mlocal) {
+    svh::in_batches(ncb * nch, 1, 64 * W, [&](int64_t b0, int64_t nb) {
+      k_cols_dq<V, W, G, decltype(mlocal)::value><<<dim3((unsigned)nb), block, 0, st>>>(x, R, C, nch, ws, b0);
+    });
+  };
+  // the top kernels: four waves of per_wave columns each per workgroup,
+  // launches of at most 2^32 - 1 work-items
+  auto top = [&](int per_wave, auto &&launch) {
+    svh::in_batches((C + 4 * per_wave - 1) / (4 * per_wave), 1, 256,
+                    [&](int64_t b0, int64_t nb) { launch(dim3((unsigned)nb), b0); });
+  };
   if (nch <= CC_GROUP) {
-    k_cols_dq<V, W, G, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    dq(std::true_type{});
     // the final trees: a group of S >= nch lanes per column, one node each
-    if (nch <= 4) k_cols_top<1, 1, 4><<<per_waves(16), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    else if (nch <= 8) k_cols_top<1, 1, 8><<<per_waves(8), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    else if (nch <= 16) k_cols_top<1, 1, 16><<<per_waves(4), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    else k_cols_top<1, 1, 32><<<per_waves(2), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+#define SV_TOP(PASS, K, S, PW)                                                                           \
+  top(PW, [&](dim3 g, int64_t b0) {                                                                      \
+    k_cols_top<PASS, K, S><<<g, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean, b0);              \
+  })
+    if (nch <= 4) SV_TOP(1, 1, 4, 16);
+    else if (nch <= 8) SV_TOP(1, 1, 8, 8);
+    else if (nch <= 16) SV_TOP(1, 1, 16, 4);
+    else SV_TOP(1, 1, 32, 2);
   } else if (nch <= 64 * 64) {
     // many chunks: a wave per column for m and for the final trees
-    const dim3 per_wave = per_waves(1);
     if (nch <= 64 * 4) {
-      k_cols_top<0, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-      k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top<1, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      SV_TOP(0, 4, 64, 1);
+      dq(std::false_type{});
+      SV_TOP(1, 4, 64, 1);
     } else if (nch <= 64 * 16) {
-      k_cols_top<0, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-      k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top<1, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      SV_TOP(0, 16, 64, 1);
+      dq(std::false_type{});
+      SV_TOP(1, 16, 64, 1);
     } else {
-      k_cols_top<0, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-      k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top<1, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      SV_TOP(0, 64, 64, 1);
+      dq(std::false_type{});
+      SV_TOP(1, 64, 64, 1);
     }
   } else {
     int log2p = 0;  // runs of 64 * 2^log2p chunk nodes per lane
     while (((int64_t)64 * 64 << log2p) < nch) ++log2p;
-    const dim3 per_wave = per_waves(1);
-    k_cols_top_big<0><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
-    k_cols_dq<V, W, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-    k_cols_top_big<1><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
+    top(1, [&](dim3 g, int64_t b0) {
+      k_cols_top_big<0><<<g, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean, b0);
+    });
+    dq(std::false_type{});
+    top(1, [&](dim3 g, int64_t b0) {
+      k_cols_top_big<1><<<g, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean, b0);
+    });
   }
+#undef SV_TOP
 }
 
 // Row groups per wave, so that lanes stay on columns: G = 1 (64 column
@@ -1655,11 +1680,12 @@ void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, con
 template <int V, int W>
 void launch_cols_g(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var, float *mean,
                    hipStream_t st) {
-  const int64_t groups = (C + V - 1) / V;
-  if (groups >= 64) launch_cols_chunked<V, W, 1>(x, R, C, ddof, ws, var, mean, st);
-  else if (groups > 4) launch_cols_chunked<V, W, 4>(x, R, C, ddof, ws, var, mean, st);
-  else if (groups > 1) launch_cols_chunked<V, W, 16>(x, R, C, ddof, ws, var, mean, st);
-  else launch_cols_chunked<V, W, 64>(x, R, C, ddof, ws, var, mean, st);
+  switch (svx::cols_chunk_plan(V, W, R, C).G) {
+    case 1: launch_cols_chunked<V, W, 1>(x, R, C, ddof, ws, var, mean, st); break;
+    case 4: launch_cols_chunked<V, W, 4>(x, R, C, ddof, ws, var, mean, st); break;
+    case 16: launch_cols_chunked<V, W, 16>(x, R, C, ddof, ws, var, mean, st); break;
+    default: launch_cols_chunked<V, W, 64>(x, R, C, ddof, ws, var, mean, st); break;
+  }
 }
 
 template <int V>
@@ -1678,15 +1704,12 @@ void launch_cols_v(const float *x, int64_t R, int64_t C, int64_t ddof, const Col
 // 2, 4, 8), the smallest G that still gives 512 workgroups, else the largest.
 template <bool VEC16>
 void launch_cols_one(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
-  int64_t cap = CC_E;
-  while (cap < R) cap *= 2;
-  const int gw = (int)(cap / CC_E);  // 8 .. 64
-  int g = gw >= 16 ? gw / 8 : 1;     // W <= 8
-  if (g == 2 || g == 8) g *= 2;      // G in 1, 4, 16
-  while (g < 16 && g * 4 <= gw && (C + 4 * 64 / g - 1) / (4 * 64 / g) < 512) g *= 4;
-  const int w = gw / g;
-  const dim3 grid((unsigned)((C + 4 * 64 / g - 1) / (4 * 64 / g)));
-#define SV_ONE(G_, W_) k_cols_one<4, W_, G_, VEC16><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
+  const svx::ColsOnePlan p = svx::cols_one4_plan(R, C);
+  const int g = p.G, w = p.W;
+#define SV_ONE(G_, W_)                                                                                   \
+  svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                    \
+    k_cols_one<4, W_, G_, VEC16><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean, (int)b0); \
+  })
   switch (g * 16 + w) {  // R > 64: 16*G*W >= 128
     case 16 * 1 + 8: SV_ONE(1, 8); break;
     case 16 * 4 + 2: SV_ONE(4, 2); break;
@@ -1703,13 +1726,12 @@ void launch_cols_one(const float *x, int64_t R, int64_t C, int64_t ddof, float *
 // waves of four columns per lane): G in 1, 4 (row segments of at least 16
 // lanes, 64 bytes), W up to 16; G = 1 when that gives 512 workgroups.
 void launch_cols_one1(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
-  int64_t cap = CC_E;
-  while (cap < R) cap *= 2;
-  const int gw = (int)(cap / CC_E);  // 8 .. 64
-  const int g = (gw > 16 || (C + 63) / 64 < 512) && gw >= 8 ? 4 : 1;
-  const int w = gw / g;
-  const dim3 grid((unsigned)((C + 64 / g - 1) / (64 / g)));
-#define SV_ONE(G_, W_) k_cols_one<1, W_, G_, false><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
+  const svx::ColsOnePlan p = svx::cols_one1_plan(R, C);
+  const int g = p.G, w = p.W;
+#define SV_ONE(G_, W_)                                                                                   \
+  svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                    \
+    k_cols_one<1, W_, G_, false><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean, (int)b0); \
+  })
   switch (g * 32 + w) {  // R > 64: 16*G*W >= 128
     case 32 * 1 + 8: SV_ONE(1, 8); break;
     case 32 * 1 + 16: SV_ONE(1, 16); break;
@@ -1732,25 +1754,14 @@ void launch_long_top(const float *x, int64_t n, int64_t sstride, int64_t nch, in
   else k_long_top<PASS, LS_TOP_PER_THREAD><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
 }
 
-struct SumPlan {
-  int e;
-  int log2_g;      // chunks per wave = 2^log2_g
-  int64_t blocks;  // workgroups (<= SUM_MAX_BLOCKS)
-};
-
-// Chunks of 64*e values; each wave of a SUM_W-wave workgroup streams 2^g of
-// them.  g is the smallest value that keeps the workgroup count at or below
-// `target_blocks`; with g capped at SUM_MAX_LOG2_GROUP the count stays at or
-// below SUM_MAX_BLOCKS for every n <= SUM_MAX_N.
+// The tree sum's plan: chunks of 64*e values, each wave of a SUM_W-wave
+// workgroup streaming 2^log2_g of them, log2_g the smallest value that keeps
+// the workgroup count at or below `target_blocks`; with log2_g capped at
+// SUM_MAX_LOG2_GROUP the count stays at or below SUM_MAX_BLOCKS for every
+// n <= SUM_MAX_N.
+using svx::SumPlan;
 SumPlan plan_sum(int64_t n, int e, int64_t target_blocks) {
-  const int64_t chunk = 64LL * e;
-  const int64_t chunks = (n + chunk - 1) / chunk;
-  const int64_t waves = (chunks + SUM_W - 1) / SUM_W;
-  if (target_blocks > SUM_MAX_BLOCKS) target_blocks = SUM_MAX_BLOCKS;
-  if (target_blocks < 1) target_blocks = 1;
-  int g = 0;
-  while (g < SUM_MAX_LOG2_GROUP && ((waves + (1LL << g) - 1) >> g) > target_blocks) ++g;
-  return {e, g, (waves + (1LL << g) - 1) >> g};
+  return svx::plan_sum(n, e, target_blocks, SUM_W, SUM_MAX_BLOCKS, SUM_MAX_LOG2_GROUP);
 }
 
 size_t sum_workspace_bytes(int64_t n) {
@@ -1811,8 +1822,7 @@ void launch_rows_t(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t 
   // only the waves the row reaches (the tree pads the others with zero
   // nodes); var_lds_pad: unused dynamic LDS per workgroup, a cap on resident
   // waves
-  const int64_t reach = (n + 64 * E - 1) / (64 * E);
-  const int waves = reach < W ? (int)reach : W;
+  const int waves = svx::rows_waves(n, E, W);
   svh::in_batches(rows, 1, 64 * waves, [&](int64_t r0, int64_t nr) {
     k_var_rows<E, W, VEC, LOADP, NT><<<dim3((unsigned)nr), dim3(64 * waves), (size_t)g_tune.var_lds_pad, st>>>(
         x + r0 * ld, n, ld, ddof, var + r0, mean ? mean + r0 : nullptr, g_tune.var_xcd);
@@ -1857,7 +1867,7 @@ void launch_rows_ew(bool vec, const float *x, int64_t rows, int64_t n, int64_t l
   }
 }
 
-constexpr int64_t SEG_MAX_N = 512;  // rows that share waves (k_var_rows_seg)
+using svx::SEG_MAX_N;  // rows that share waves (k_var_rows_seg)
 
 // vw: 4 for 16-byte aligned rows of a multiple of 4 values, 2 for 8-byte
 // aligned rows of an even count, else 1.
@@ -1879,16 +1889,18 @@ void launch_seg_t(int vw, const float *x, int64_t rows, int64_t n, int64_t ld, i
 // the row's power-of-two tile.
 void launch_rows_seg(const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var, float *mean,
                      hipStream_t st) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(x);
-  const int vec = (a % 16 == 0 && ld % 4 == 0) ? 4 : (a % 8 == 0 && ld % 2 == 0) ? 2 : 1;
-  if (n <= 4) launch_seg_t<4, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else if (n <= 8) launch_seg_t<8, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else if (n <= 16) launch_seg_t<16, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else if (n <= 32) launch_seg_t<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else if (n <= 64) launch_seg_t<16, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else if (n <= 128) launch_seg_t<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else if (n <= 256) launch_seg_t<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
-  else launch_seg_t<16, 32>(vec, x, rows, n, ld, ddof, var, mean, st);
+  const int vec = svx::seg_vw(reinterpret_cast<uintptr_t>(x), ld);
+  const svx::SegPlan p = svx::seg_plan(n);
+  switch (p.E * 100 + p.S) {
+    case 401: launch_seg_t<4, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 801: launch_seg_t<8, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1601: launch_seg_t<16, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1602: launch_seg_t<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1604: launch_seg_t<16, 4>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1608: launch_seg_t<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1616: launch_seg_t<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    default: launch_seg_t<16, 32>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+  }
 }
 
 // Rows of 1025..16384 values: the row's power-of-two tile (2048 .. 16384
@@ -1903,40 +1915,34 @@ void launch_rows_seg(const float *x, int64_t rows, int64_t n, int64_t ld, int64_
 // (E 16) against 14.3 (E 32) and 13.7 (E 8); [2048, 8192] 12.3 against 13.0
 // (E 32); [8192, 2048] 12.1 (E 8) against 13.3 (E 32); [1024, 16384] 13.0
 // (E 32) against 14.7 (E 16).
-int auto_split(int64_t n) {
-  int64_t tile = 2048;
-  while (tile < n) tile *= 2;
-  const int64_t w = tile <= 4096 ? 4 : 8;
-  return (int)(64 * 64 * w / tile);  // 64 / E with E = tile / (64 w)
-}
-
 void launch_rows_tile(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                       float *mean, hipStream_t st) {
-  const int s = g_tune.var_split != 0 ? g_tune.var_split : auto_split(n);
-  if (n <= 2048) {
-    if (s <= 2) launch_rows_split<32, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else if (s == 4) launch_rows_split<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else launch_rows_split<8, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
-  } else if (n <= 4096) {
-    if (s == 1) launch_rows_ew<64, 1>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else if (s == 2) launch_rows_split<32, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else if (s == 4) launch_rows_split<16, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else launch_rows_split<8, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
-  } else if (n <= 8192) {
-    if (s == 1) launch_rows_split<64, 2>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else if (s == 2) launch_rows_split<32, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else if (s == 4) launch_rows_split<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else launch_rows_split<8, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
-  } else if (n <= ROWS_MAX_N) {
-    if (s == 1) launch_rows_ew<64, 4>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else if (s == 2) launch_rows_split<32, 8>(vec, x, rows, n, ld, ddof, var, mean, st);
-    else launch_rows_split<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st);
-  } else if (n <= 32768) {  // 16 waves of 32 values (per-lane loads)
-    if (vec) launch_rows_t<32, 16, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
-    else launch_rows_t<32, 16, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
-  } else {  // n <= ROWS_ONE_MAX_N: 16 waves of 64 values
-    if (vec) launch_rows_t<64, 16, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
-    else launch_rows_t<64, 16, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+  const svx::RowsPlan p = svx::rows_plan(n, g_tune.var_split);
+  switch (p.E * 100 + p.W) {
+    case 401: launch_rows_ew<4, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1601: launch_rows_ew<16, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 3201: launch_rows_split<32, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1602: launch_rows_split<16, 2>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 804: launch_rows_split<8, 4>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 6401: launch_rows_ew<64, 1>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 3202: launch_rows_split<32, 2>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1604: launch_rows_split<16, 4>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 808: launch_rows_split<8, 8>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 6402: launch_rows_split<64, 2>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 3204: launch_rows_split<32, 4>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1608: launch_rows_split<16, 8>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 816: launch_rows_split<8, 16>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 6404: launch_rows_ew<64, 4>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 3208: launch_rows_split<32, 8>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 1616: launch_rows_split<16, 16>(vec, x, rows, n, ld, ddof, var, mean, st); break;
+    case 3216:  // 16 waves of 32 values (per-lane loads)
+      if (vec) launch_rows_t<32, 16, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+      else launch_rows_t<32, 16, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+      break;
+    default:  // 16 waves of 64 values
+      if (vec) launch_rows_t<64, 16, true, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+      else launch_rows_t<64, 16, false, 1, false>(x, rows, n, ld, ddof, var, mean, st);
+      break;
   }
 }
 
@@ -1946,14 +1952,15 @@ void launch_rows_tile(bool vec, const float *x, int64_t rows, int64_t n, int64_t
 // LDS, no barrier.  Rows past R are the +0 padding of the column's tree.
 template <int E>
 __global__ __launch_bounds__(256) void k_cols_short(const float *__restrict__ x, int64_t R, int64_t C, int64_t ddof,
-                                                    float *__restrict__ var_out, float *__restrict__ mean_out) {
-  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+                                                    float *__restrict__ var_out, float *__restrict__ mean_out,
+                                                    int64_t b0) {
+  const int64_t c0 = ((b0 + blockIdx.x) * 256 + threadIdx.x) * 4;
   if (c0 >= C) return;
   const float *__restrict__ p = x + c0;
   float v[4][E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const float4 g = *reinterpret_cast<const float4 *>(p + (i < R ? i : R - 1) * C);
+    const float4 g = *reinterpret_cast<const float4 *>(p + svx::clamp_last<int64_t>(i, R) * C);
     v[0][i] = g.x;
     v[1][i] = g.y;
     v[2][i] = g.z;
@@ -1987,17 +1994,37 @@ __global__ __launch_bounds__(256) void k_cols_short(const float *__restrict__ x,
 }
 
 void launch_cols_short(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
-  const dim3 grid((unsigned)((C / 4 + 255) / 256)), block(256);
-  if (R <= 2) k_cols_short<2><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
-  else if (R <= 4) k_cols_short<4><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
-  else if (R <= 8) k_cols_short<8><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
-  else k_cols_short<16><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+  const int e = svx::cols_short_e(R);
+  svh::in_batches((C / 4 + 255) / 256, 1, 256, [&](int64_t b0, int64_t nb) {
+    const dim3 grid((unsigned)nb), block(256);
+    switch (e) {
+      case 2: k_cols_short<2><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean, b0); break;
+      case 4: k_cols_short<4><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean, b0); break;
+      case 8: k_cols_short<8><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean, b0); break;
+      default: k_cols_short<16><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean, b0); break;
+    }
+  });
 }
 
-template <int E, int W>
-void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
-  const dim3 grid((unsigned)((C + 63) / 64)), block(64 * W);
-  k_var_cols<E, W><<<grid, block, 0, st>>>(x, R, C, ddof, var, mean);
+// Lane per column (k_var_cols): E rows per lane, W waves, 64 columns per
+// workgroup.
+template <int V>
+void launch_cols_lane(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
+  const svx::RowsPlan p = svx::cols_lane_plan(R);
+#define SV_COLS(E, W)                                                                                    \
+  svh::in_batches((C + 63) / 64, 1, 64 * W, [&](int64_t b0, int64_t nb) {                                \
+    k_var_cols<E, W, V><<<dim3((unsigned)nb), dim3(64 * W), 0, st>>>(x, R, C, ddof, var, mean, b0);      \
+  })
+  switch (p.E * 100 + p.W) {
+    case 401: SV_COLS(4, 1); break;
+    case 1601: SV_COLS(16, 1); break;
+    case 6401: SV_COLS(64, 1); break;
+    case 6402: SV_COLS(64, 2); break;
+    case 6404: SV_COLS(64, 4); break;
+    case 6408: SV_COLS(64, 8); break;
+    default: SV_COLS(64, 16); break;
+  }
+#undef SV_COLS
 }
 
 // The ablation row "shift + centring, Kahan sequential scan" of the method
@@ -2012,9 +2039,9 @@ void launch_cols_ew(const float *x, int64_t R, int64_t C, int64_t ddof, float *v
 // load.  Two passes over the data: the plain tree of y (64-value chunks in
 // registers, the chunk nodes merged in tree order by a binary counter whose
 // state is the same in every lane), then the scan.
-constexpr int KS_T = 64;                 // values per chunk (tile width)
+using svx::KS_T;                         // values per chunk (tile width)
 constexpr int KS_LD = KS_T + 4;          // LDS tile row stride: 16-byte aligned rows, 16 lanes per bank cycle
-constexpr int KS_LEVELS = 16;            // chunk-tree levels: 2^16 chunks
+using svx::KS_LEVELS;                    // chunk-tree levels: 2^16 chunks
 template <bool AX1, bool VEC>
 __global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, int64_t nsl, int64_t n, int64_t ld,
                                                   int64_t ddof, float *__restrict__ var_out,
@@ -2025,7 +2052,7 @@ __global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, i
   const int64_t s0 = (int64_t)blockIdx.x * 64;
   const int64_t sl = s0 + lane;
   const bool real = sl < nsl;
-  const int64_t slc = real ? sl : nsl - 1;  // lanes past the last slice read it again
+  const int64_t slc = svx::clamp_last(sl, nsl);  // lanes past the last slice read it again
   const int64_t nch = (n + KS_T - 1) / KS_T;
 
   // A chunk is loaded in two steps, so that the next chunk's loads are in
@@ -2034,7 +2061,7 @@ __global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, i
   // into this lane's values v[k] = slice[c*64 + k] (through the LDS tile on
   // axis 1).  Values past n are masked by the callers.
   auto issue = [&](int64_t c, float(&raw)[KS_T]) {
-    c = c < nch ? c : nch - 1;
+    c = svx::clamp_last(c, nch);
     if constexpr (AX1) {
       // lane L loads values 4 (L mod 16) .. +3 of the chunk in row 4j + L/16
       // of the wave's 64 rows: 16 bytes at once when the group lies inside
@@ -2042,15 +2069,15 @@ __global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, i
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = 4 * j + (lane >> 4);
-        const int64_t row = s0 + r < nsl ? s0 + r : nsl - 1;
+        const int64_t row = svx::clamp_last(s0 + r, nsl);
         const int64_t col = c * KS_T + 4 * (lane & 15);
         const float *__restrict__ q = x + row * ld;
         float4 g;
         if (VEC && col + 3 < n) {
           g = *reinterpret_cast<const float4 *>(q + col);
         } else {
-          g = make_float4(q[col < n ? col : n - 1], q[col + 1 < n ? col + 1 : n - 1],
-                          q[col + 2 < n ? col + 2 : n - 1], q[col + 3 < n ? col + 3 : n - 1]);
+          g = make_float4(q[svx::clamp_last(col, n)], q[svx::clamp_last(col + 1, n)],
+                          q[svx::clamp_last(col + 2, n)], q[svx::clamp_last(col + 3, n)]);
         }
         raw[4 * j] = g.x; raw[4 * j + 1] = g.y; raw[4 * j + 2] = g.z; raw[4 * j + 3] = g.w;
       }
@@ -2058,7 +2085,7 @@ __global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, i
 #pragma unroll
       for (int k = 0; k < KS_T; ++k) {
         const int64_t i = c * KS_T + k;
-        raw[k] = x[(i < n ? i : n - 1) * ld + slc];
+        raw[k] = x[svx::clamp_last(i, n) * ld + slc];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -2174,23 +2201,16 @@ void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t co
     if (vec) k_var_rows<E, W, true, 1, false, V><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, vr, mr, 0); \
     else k_var_rows<E, W, false, 1, false, V><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, vr, mr, 0);   \
   })
-    if (n <= 256) SV_ROWS(4, 1);
-    else if (n <= 1024) SV_ROWS(16, 1);
-    else if (n <= 4096) SV_ROWS(32, 2);  // the default geometry of the main kernel
-    else SV_ROWS(64, 4);
+    const svx::RowsPlan p = svx::variant_rows_plan(n);
+    switch (p.E * 100 + p.W) {
+      case 401: SV_ROWS(4, 1); break;
+      case 1601: SV_ROWS(16, 1); break;
+      case 3202: SV_ROWS(32, 2); break;
+      default: SV_ROWS(64, 4); break;
+    }
 #undef SV_ROWS
   } else {
-    const int64_t n = rows;
-    const dim3 grid((unsigned)((cols + 63) / 64));
-#define SV_COLS(E, W) k_var_cols<E, W, V><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var, mean)
-    if (n <= 4) SV_COLS(4, 1);
-    else if (n <= 16) SV_COLS(16, 1);
-    else if (n <= 64) SV_COLS(64, 1);
-    else if (n <= 128) SV_COLS(64, 2);
-    else if (n <= 256) SV_COLS(64, 4);
-    else if (n <= 512) SV_COLS(64, 8);
-    else SV_COLS(64, 16);
-#undef SV_COLS
+    launch_cols_lane<V>(x, rows, cols, ddof, var, mean, st);
   }
 }
 
@@ -2362,7 +2382,7 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: axis %d not in {0, 1, -1, -2}", axis);
   if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f32: ddof = %lld < 0", (long long)ddof);
   if (cols > 0 && rows > VAR_MAX_ELEMS / cols)
-    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: rows * cols above 2^40");
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f32: rows * cols above 2^36");
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
   const int64_t n = ax1 ? cols : rows;
@@ -2398,83 +2418,76 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
     return check_launch("sv_variance_f32");
   }
-  if (is_long && !(g_tune.var_long_rows && n <= ROWS_ONE_MAX_N && rows >= ROWS_ONE_MIN_ROWS)) {
-    const LongWs ws = long_ws(workspace, nslices, nch);
-    const bool vec = aligned16(x) && (cols % 4 == 0);
-    const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
-    if (vec) k_long_rows<0, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-    else k_long_rows<0, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-    launch_long_top<0>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
-    if (vec) k_long_rows<1, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-    else k_long_rows<1, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
-    launch_long_top<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
-    return check_launch("sv_variance_f32");
-  }
-  if (!ax1 && n > COLS_MAX_R && n <= COLS_ONE_LONG_MAX_R && g_tune.var_cols_once &&
-      g_tune.var_cols_single_max == COLS_MAX_R) {
-    // columns of 1025..4096 rows: sixteen whole columns per workgroup of up
-    // to 16 waves (four row groups of E rows per wave; a shorter column
-    // launches only the waves its rows reach), read once -- unless the grid
-    // would leave the chip's last round of workgroups mostly empty (each
-    // workgroup holds 256 KB in registers, so one or two fit a CU)
-    const int e = n <= 2048 ? 32 : 64;  // rows per lane over all blocks
-    const int waves = (int)((n + 4 * e - 1) / (4 * e));
-    const int64_t nwg = (cols + 15) / 16;
-    // MODE 1 when every wave is full (2048 or 4096 rows), else MODE 2
-    const bool exact = n == 2048 || n == 4096, big = n > 2048;
-    using KFn = void (*)(const float *, int64_t, int64_t, int64_t, float *, float *);
-    const KFn kern = big ? (exact ? k_cols_one<1, 16, 4, false, 64, 1> : k_cols_one<1, 16, 4, false, 64, 2>)
-                         : (exact ? k_cols_one<1, 16, 4, false, 32, 1> : k_cols_one<1, 16, 4, false, 32, 2>);
+  const svx::RouteKnobs knobs{g_tune.var_long_rows, g_tune.var_cols_once, g_tune.var_cols_single_max,
+                              g_tune.var_short_rows, g_tune.var_cols_short, g_tune.var_cols_one};
+  const bool vec16 = aligned16(x) && cols % 4 == 0;
+  // Columns of 1025..4096 rows: sixteen whole columns per workgroup of up to
+  // 16 waves (four row groups of E rows per wave; a shorter column launches
+  // only the waves its rows reach), read once -- unless the grid would leave
+  // the chip's last round of workgroups mostly empty (each workgroup holds
+  // 256 KB in registers, so one or two fit a CU).  MODE 1 when every wave is
+  // full (2048 or 4096 rows), else MODE 2.
+  using ColsOneFn = void (*)(const float *, int64_t, int64_t, int64_t, float *, float *, int);
+  ColsOneFn one_read = nullptr;
+  svx::ColsLongPlan one_plan{};
+  bool fills = false;
+  if (svx::cols_one_read_candidate(ax1, n, knobs)) {
+    one_plan = svx::cols_long_plan(n, cols);
+    const bool exact = one_plan.mode == 1, big = one_plan.E == 64;
+    one_read = big ? (exact ? k_cols_one<1, 16, 4, false, 64, 1> : k_cols_one<1, 16, 4, false, 64, 2>)
+                   : (exact ? k_cols_one<1, 16, 4, false, 32, 1> : k_cols_one<1, 16, 4, false, 32, 2>);
     int per_cu = 0, cus = 0, dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern), 64 * waves, 0) ==
-            hipSuccess &&
+    if (g_tune.var_cols_once != 2 && hipGetDevice(&dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(one_read),
+                                                     64 * one_plan.waves, 0) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0) {
-      const int64_t cap = (int64_t)per_cu * cus, rounds = (nwg + cap - 1) / cap;
-      if (g_tune.var_cols_once == 2 || 4 * nwg >= 3 * rounds * cap) {
-        kern<<<dim3((unsigned)nwg), dim3(64 * (unsigned)waves), 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-        return check_launch("sv_variance_f32");
-      }
+      const int64_t cap = (int64_t)per_cu * cus, rounds = (one_plan.blocks + cap - 1) / cap;
+      fills = 4 * one_plan.blocks >= 3 * rounds * cap;
     }
   }
-  if (!ax1 && n > g_tune.var_cols_single_max) {
-    const ColsWs ws = cols_ws(workspace, cols_layout(rows, cols));
-    if (aligned16(x) && cols % 4 == 0) launch_cols_v<4>(x, rows, cols, ddof, ws, var_out, mean_out, st);
-    else launch_cols_v<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
-    return check_launch("sv_variance_f32");
-  }
-  if (ax1) {
-    const bool vec = aligned16(x) && (cols % 4 == 0);
-    if (n <= SEG_MAX_N && g_tune.var_short_rows) launch_rows_seg(x, rows, n, cols, ddof, var_out, mean_out, st);
-    else if (n <= 256) launch_rows_ew<4, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    else if (n <= 1024) launch_rows_ew<16, 1>(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-    else launch_rows_tile(vec, x, rows, n, cols, ddof, var_out, mean_out, st);
-  } else {
+  switch (svx::f32_route(rows, cols, ax1, vec16, knobs, fills)) {
+    case svx::Route::LONG_ROWS_CHUNKED: {
+      const LongWs ws = long_ws(workspace, nslices, nch);
+      const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
+      if (vec16) k_long_rows<0, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      else k_long_rows<0, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      launch_long_top<0>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
+      if (vec16) k_long_rows<1, true><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      else k_long_rows<1, false><<<grid, block, 0, st>>>(x, n, cols, nch, ws);
+      launch_long_top<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
+      break;
+    }
+    case svx::Route::COLS_ONE_READ:
+      svh::in_batches(one_plan.blocks, 1, 64 * one_plan.waves, [&](int64_t b0, int64_t nb) {
+        one_read<<<dim3((unsigned)nb), dim3(64 * (unsigned)one_plan.waves), 0, st>>>(x, rows, cols, ddof, var_out,
+                                                                                  mean_out, (int)b0);
+      });
+      break;
+    case svx::Route::COLS_CHUNKED: {
+      const ColsWs ws = cols_ws(workspace, cols_layout(rows, cols));
+      if (vec16) launch_cols_v<4>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+      else launch_cols_v<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+      break;
+    }
+    case svx::Route::ROWS_SEG: launch_rows_seg(x, rows, n, cols, ddof, var_out, mean_out, st); break;
+    case svx::Route::ROWS_TILE: launch_rows_tile(vec16, x, rows, n, cols, ddof, var_out, mean_out, st); break;
     // columns of at most 15 rows: four columns per lane, every tree in-lane
     // (at 16 rows the lane kernel's lanes hold exactly 16: [16, 1000000] 12.7
     // against 16.7 us);
-    // more than 64 rows: one launch of G row groups per wave; otherwise the
-    // lane-per-column kernel, whose lanes hold exactly 4, 16 or 64 rows
-    // (faster than G row groups there: [4, 1000000] 6.5 against 16 us)
-    if (n < 16 && g_tune.var_cols_short && aligned16(x) && cols % 4 == 0) {
-      launch_cols_short(x, rows, cols, ddof, var_out, mean_out, st);
-    } else if (g_tune.var_cols_one && n > 64) {
-      // four columns per lane for long columns (513..1024 rows) of wide
-      // matrices, else one: [1000, 20000] 31.0 against 37.1 us, [300, 50000]
-      // 34.1 against 24.0, [512, 4096] 7.0 against 4.8
-      const int mode = g_tune.var_cols_one;
-      const bool four = cols >= 4 && (mode == 2 || (mode == 1 && n > 512 && cols >= 8192));
-      if (!four) launch_cols_one1(x, rows, cols, ddof, var_out, mean_out, st);
-      else if (aligned16(x) && cols % 4 == 0) launch_cols_one<true>(x, rows, cols, ddof, var_out, mean_out, st);
+    case svx::Route::COLS_SHORT: launch_cols_short(x, rows, cols, ddof, var_out, mean_out, st); break;
+    // more than 64 rows: one launch of G row groups per wave, four columns
+    // per lane for long columns (513..1024 rows) of wide matrices, else one:
+    // [1000, 20000] 31.0 against 37.1 us, [300, 50000] 34.1 against 24.0,
+    // [512, 4096] 7.0 against 4.8
+    case svx::Route::COLS_ONE4:
+      if (vec16) launch_cols_one<true>(x, rows, cols, ddof, var_out, mean_out, st);
       else launch_cols_one<false>(x, rows, cols, ddof, var_out, mean_out, st);
-    }
-    else if (n <= 4) launch_cols_ew<4, 1>(x, rows, cols, ddof, var_out, mean_out, st);
-    else if (n <= 16) launch_cols_ew<16, 1>(x, rows, cols, ddof, var_out, mean_out, st);
-    else if (n <= 64) launch_cols_ew<64, 1>(x, rows, cols, ddof, var_out, mean_out, st);
-    else if (n <= 128) launch_cols_ew<64, 2>(x, rows, cols, ddof, var_out, mean_out, st);
-    else if (n <= 256) launch_cols_ew<64, 4>(x, rows, cols, ddof, var_out, mean_out, st);
-    else if (n <= 512) launch_cols_ew<64, 8>(x, rows, cols, ddof, var_out, mean_out, st);
-    else launch_cols_ew<64, 16>(x, rows, cols, ddof, var_out, mean_out, st);
+      break;
+    case svx::Route::COLS_ONE1: launch_cols_one1(x, rows, cols, ddof, var_out, mean_out, st); break;
+    // otherwise the lane-per-column kernel, whose lanes hold exactly 4, 16
+    // or 64 rows (faster than G row groups there: [4, 1000000] 6.5 against
+    // 16 us)
+    case svx::Route::COLS_LANE: launch_cols_lane<V_KERNEL>(x, rows, cols, ddof, var_out, mean_out, st); break;
   }
   return check_launch("sv_variance_f32");
 }
@@ -2607,22 +2620,30 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     if (vw2 == 2) k_var_rows_c64_seg<E, S, 2><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, ddof, vr, mr); \
     else k_var_rows_c64_seg<E, S, 1><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, ddof, vr, mr);         \
   })
-      if (cols <= 4) SV_SEG_C64(4, 1);
-      else if (cols <= 8) SV_SEG_C64(8, 1);
-      else if (cols <= 16) SV_SEG_C64(16, 1);
-      else if (cols <= 32) SV_SEG_C64(16, 2);
-      else if (cols <= 64) SV_SEG_C64(16, 4);
-      else if (cols <= 128) SV_SEG_C64(16, 8);
-      else if (cols <= 256) SV_SEG_C64(16, 16);
-      else SV_SEG_C64(16, 32);
+      const svx::SegPlan sp = svx::seg_plan(cols);
+      switch (sp.E * 100 + sp.S) {
+        case 401: SV_SEG_C64(4, 1); break;
+        case 801: SV_SEG_C64(8, 1); break;
+        case 1601: SV_SEG_C64(16, 1); break;
+        case 1602: SV_SEG_C64(16, 2); break;
+        case 1604: SV_SEG_C64(16, 4); break;
+        case 1608: SV_SEG_C64(16, 8); break;
+        case 1616: SV_SEG_C64(16, 16); break;
+        default: SV_SEG_C64(16, 32); break;
+      }
 #undef SV_SEG_C64
-    } else if (cols <= 256) SV_ROWS_C64(4, 1);
-    else if (cols <= 1024) SV_ROWS_C64(16, 1);
-    else if (cols <= 2048) SV_ROWS_C64(16, 2);
-    else if (cols <= 4096) SV_ROWS_C64(16, 4);
-    else if (cols <= 8192) SV_ROWS_C64(16, 8);
-    else if (cols <= 16384) SV_ROWS_C64(16, 16);
-    else SV_ROWS_C64(32, 16);
+    } else {
+      const svx::RowsPlan rp = svx::c64_rows_plan(cols);
+      switch (rp.E * 100 + rp.W) {
+        case 401: SV_ROWS_C64(4, 1); break;
+        case 1601: SV_ROWS_C64(16, 1); break;
+        case 1602: SV_ROWS_C64(16, 2); break;
+        case 1604: SV_ROWS_C64(16, 4); break;
+        case 1608: SV_ROWS_C64(16, 8); break;
+        case 1616: SV_ROWS_C64(16, 16); break;
+        default: SV_ROWS_C64(32, 16); break;
+      }
+    }
 #undef SV_ROWS_C64
     return check_launch("sv_variance_c64");
   }

@@ -1,0 +1,562 @@
+// Host-only check of the float32 library's global load indices and launch
+// plans.  The launch geometry (svx::f32_route and the *_plan functions) and
+// the index arithmetic of every load (svx::clamp_*, tile_index, rows_avail,
+// seg_row, cols_first, line_on_one_die, ...) are the functions the kernels
+// and launchers call; this program walks each planned launch the way the
+// kernel walks its data (workgroups, waves, lanes, loads) and checks that
+// every element a load touches lies inside the array, and that every launch
+// stays within the dispatch limits (at most 2^32 - 1 work-items, 2^31 - 1
+// workgroups).  Large grids are sampled: their first and last workgroups
+// and an even spread between.
+//
+// Build: g++ -std=c++17 -O2 index_check.cpp -o index_check; run: ./index_check
+// (prints one line per failure, at most 40, and a summary; exit 1 on any).
+#include <stdint.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "../stable_variance_amd/csrc/sv_index.hpp"
+
+using namespace svx;
+
+namespace {
+
+int64_t g_checks = 0, g_launches = 0, g_fail = 0;
+std::set<std::string> g_seen;  // one line per (path, shape, kind of failure)
+
+struct Where {
+  const char *path;
+  int64_t rows, cols;
+  int64_t total;  // elements of the array the loads read
+};
+
+void report(const Where &c, const char *what, int64_t a, int64_t b, int64_t block, int lane) {
+  ++g_fail;
+  char key[160];
+  snprintf(key, sizeof key, "%s %lld %lld %s", c.path, (long long)c.rows, (long long)c.cols, what);
+  if (g_seen.insert(key).second && g_seen.size() <= 40)
+    printf("FAIL %s [%lld, %lld] %s: %lld %lld (workgroup %lld lane %d)\n", c.path, (long long)c.rows,
+           (long long)c.cols, what, (long long)a, (long long)b, (long long)block, lane);
+}
+
+// A load of w elements at idx.
+inline void load(const Where &c, int64_t idx, int w, int64_t block, int lane) {
+  ++g_checks;
+  if (idx < 0 || idx + w > c.total) report(c, "load index, width", idx, w, block, lane);
+}
+
+// HIP's dispatch limits: a grid dimension of at most 2^32 - 1 work-items
+// and 2^31 - 1 workgroups (stated here, not taken from the header).
+void launch(const Where &c, int64_t blocks, int64_t threads) {
+  ++g_launches;
+  if (blocks < 1 || blocks > 0x7fffffffLL || blocks * threads > 0xffffffffLL)
+    report(c, "launch blocks, threads", blocks, threads, -1, -1);
+}
+
+// Workgroups of a grid of nb to walk: all of a small grid, else the first
+// and last 12 and 8 spread between.
+std::vector<int64_t> visit(int64_t nb) {
+  std::vector<int64_t> v;
+  if (nb <= 32) {
+    for (int64_t b = 0; b < nb; ++b) v.push_back(b);
+    return v;
+  }
+  for (int64_t b = 0; b < 12; ++b) v.push_back(b);
+  for (int64_t b = nb - 12; b < nb; ++b) v.push_back(b);
+  for (int64_t i = 1; i <= 8; ++i) v.push_back(12 + (nb - 24) * i / 9);
+  std::sort(v.begin(), v.end());
+  v.erase(std::unique(v.begin(), v.end()), v.end());
+  return v;
+}
+
+// ------------------------------------------------------------------ tiles
+
+// The loads of load_tile<E, VEC, LOADP> for one lane (`lane` is the lane
+// argument the kernel passes), as offsets from the tile's start.
+template <class F>
+void tile_loads(int E, bool vec, int loadp, int64_t len, int64_t avail, int lane, F &&f) {
+  const int TILE = 64 * E, J = E / 4;
+  const bool full = len >= TILE;
+  const int lim = tile_lim(len, TILE);
+  if (lim == 0) return;
+  if (loadp == 2 && full && vec) {
+    for (int k = 0; k < J; ++k) f(tile_index(false, true, E, lane, k), 4);
+    return;
+  }
+  if (loadp == 1 || loadp == 2) {
+    if (full || avail >= TILE) {
+      for (int j = 0; j < J; ++j) {
+        if (vec) f(tile_index(true, true, E, lane, j), 4);
+        else
+          for (int t = 0; t < 4; ++t) f(tile_index(true, false, E, lane, 4 * j + t), 1);
+      }
+    } else if (vec) {
+      for (int j = 0; j < J; ++j) f(clamp_group(tile_index(true, true, E, lane, j), lim, 4), 4);
+    } else {
+      for (int i = 0; i < E; ++i) f(clamp_group(tile_index(true, false, E, lane, i), lim, 1), 1);
+    }
+  } else {
+    if (vec && !full) {
+      for (int k = 0; k < J; ++k) f(clamp_group(tile_index(false, true, E, lane, k), lim, 4), 4);
+    } else if (full && vec) {
+      for (int k = 0; k < J; ++k) f(tile_index(false, true, E, lane, k), 4);
+    } else {
+      for (int k = 0; k < E; ++k) {
+        const int e = tile_index(false, false, E, lane, k);
+        f(full ? e : clamp_group(e, lim, 1), 1);
+      }
+    }
+  }
+}
+
+// k_var_rows (and its ablation variants): one launch over rows [r0, r0+nr).
+void rows_launch(const Where &c, int64_t r0, int64_t nr, int64_t n, int64_t ld, int E, int W, bool vec, int loadp) {
+  const int waves = rows_waves(n, E, W);
+  launch(c, nr, 64 * waves);
+  for (int64_t b : visit(nr)) {
+    const int64_t row = b;  // also every permutation of the rows (xcd_contiguous)
+    const int64_t p = (r0 + row) * ld;
+    for (int w = 0; w < waves; ++w) {
+      const int64_t base = (int64_t)w * 64 * E;
+      for (int lane = 0; lane < 64; ++lane) {
+        tile_loads(E, vec, loadp, n - base, rows_avail(nr, row, ld, n, base), vlane_pair32(lane),
+                   [&](int64_t i, int wd) { load(c, p + base + i, wd, b, lane); });
+        load(c, p, 1, b, lane);  // x0
+      }
+    }
+  }
+}
+
+// k_var_rows_full: rows of exactly 64*E*W values.
+void rows_full_launch(const Where &c, int64_t r0, int64_t nr, int64_t ld, int E, int W) {
+  launch(c, nr, 64 * W);
+  for (int64_t b : visit(nr)) {
+    const int64_t p = (r0 + b) * ld;
+    for (int w = 0; w < W; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        for (int j = 0; j < E / 4; ++j) load(c, p + (int64_t)w * 64 * E + vlane_pair32(lane) * E + 4 * j, 4, b, lane);
+        load(c, p, 1, b, lane);
+      }
+  }
+}
+
+// Rows in batches of at most 2^32 - 1 work-items (svh::in_batches).
+template <class F>
+void batches(int64_t total, int64_t per_block, int64_t threads, F &&f) {
+  const int64_t batch = batch_rows(per_block, threads);
+  for (int64_t s0 = 0; s0 < total; s0 += batch) f(s0, std::min(batch, total - s0));
+}
+
+// The load path the row launchers pick for a plan (E, W) and var_load_path
+// (0 coalesced + LDS transpose, 1 per lane, 2 coalesced + staged transpose):
+// (E, W) of launch_rows_ew, the two 16-wave plans (per lane), or the rest
+// (launch_rows_split).
+int rows_loadp(int E, int W, bool vec, int vlp) {
+  const bool ew = (E == 4 && W == 1) || (E == 16 && W == 1) || (E == 64 && W == 1) || (E == 64 && W == 4);
+  if (ew) {
+    if (E % 16 == 0 && vlp == 2) return vec ? 2 : 1;
+    return vlp != 0 ? 1 : 0;
+  }
+  if (W == 16 && (E == 32 || E == 64)) return 1;
+  if (!vec) return 1;
+  if (vlp == 0) return 0;
+  return vlp == 2 && E % 16 == 0 ? 2 : 1;
+}
+
+void rows_tile(const Where &c, int64_t rows, int64_t n, bool vec, int split, int vlp, bool full_rows) {
+  const RowsPlan p = rows_plan(n, split);
+  const int loadp = rows_loadp(p.E, p.W, vec, vlp);
+  const bool full_kernel = vec && loadp == 1 && full_rows && n == 64LL * p.E * p.W;
+  const int waves = full_kernel ? p.W : rows_waves(n, p.E, p.W);
+  batches(rows, 1, 64 * waves, [&](int64_t r0, int64_t nr) {
+    if (full_kernel) rows_full_launch(c, r0, nr, n, p.E, p.W);
+    else rows_launch(c, r0, nr, n, n, p.E, p.W, vec, loadp);
+  });
+}
+
+// k_var_rows_seg (cplx = 1) and k_var_rows_c64_seg (cplx = 2: complex values
+// of two floats, loads of vw complex values).
+void rows_seg(const Where &c, int64_t rows, int64_t n, int vw, int cplx) {
+  const SegPlan sp = seg_plan(n);
+  const int rpb = 4 * (64 / sp.S);
+  batches(rows, rpb, 256, [&](int64_t r0, int64_t nr) {
+    const int64_t nb = (nr + rpb - 1) / rpb;
+    launch(c, nb, 256);
+    const bool full = n == (int64_t)sp.S * sp.E;
+    for (int64_t b : visit(nb))
+      for (int w = 0; w < 4; ++w)
+        for (int lane = 0; lane < 64; ++lane) {
+          const int64_t row = seg_row(b, w, lane, sp.S);
+          const int64_t p = cplx * (r0 + clamp_last(row, nr)) * n;
+          const int64_t e0 = (int64_t)(lane % sp.S) * sp.E;
+          for (int j = 0; j < sp.E / vw; ++j) {
+            const int64_t e = e0 + (int64_t)vw * j;
+            load(c, p + cplx * (full ? e : clamp_group(e, n, vw)), cplx * vw, b, lane);
+          }
+          load(c, p, cplx, b, lane);  // x0
+        }
+  });
+}
+
+// k_var_rows_c64: rows of n complex values, load_tile over 2*E floats.
+void rows_c64(const Where &c, int64_t rows, int64_t n, bool vec) {
+  const RowsPlan p = c64_rows_plan(n);
+  batches(rows, 1, 64 * p.W, [&](int64_t r0, int64_t nr) {
+    launch(c, nr, 64 * p.W);
+    for (int64_t b : visit(nr)) {
+      const int64_t pr = 2 * (r0 + b) * n;
+      for (int w = 0; w < p.W; ++w) {
+        const int64_t base = (int64_t)w * 64 * p.E;
+        for (int lane = 0; lane < 64; ++lane) {
+          tile_loads(2 * p.E, vec, 1, 2 * (n - base), 2 * rows_avail(nr, b, n, n, base), lane,
+                     [&](int64_t i, int wd) { load(c, pr + 2 * base + i, wd, b, lane); });
+          load(c, pr, 2, b, lane);
+        }
+      }
+    }
+  });
+}
+
+// k_long_rows (both passes) and k_long_top.
+void long_rows(const Where &c, int64_t rows, int64_t n, bool vec) {
+  const int64_t nch = (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK;
+  const int64_t nb = rows * nch;
+  launch(c, nb, 256);
+  launch(c, rows, 256);
+  for (int64_t b : visit(nb)) {
+    const int64_t r = b / nch, ch = b % nch;
+    for (int w = 0; w < 4; ++w) {
+      const int64_t base = ch * LS_ROW_CHUNK + (int64_t)w * 64 * 64;
+      for (int lane = 0; lane < 64; ++lane) {
+        tile_loads(64, vec, 1, n - base, rows_avail(nb / nch, r, n, n, base), lane,
+                   [&](int64_t i, int wd) { load(c, r * n + base + i, wd, b, lane); });
+        load(c, r * n, 1, b, lane);
+      }
+    }
+  }
+  for (int64_t sl : visit(rows)) load(c, sl * n, 1, sl, 0);  // finalize's x0
+}
+
+// ------------------------------------------------------------------ axis 0
+
+// The V adjacent columns x rows of load_cols_tile<V, E, VEC16> and the x0
+// loads of the column kernels (clamped: k_cols_one; not: k_cols_y, k_cols_dq).
+void cols_tile(const Where &c, int64_t R, int64_t C, int64_t c0, int64_t r0, bool full, int V, int E, bool vec16,
+               int64_t b, int lane) {
+  const int64_t cc = cols_first(c0, C, V);
+  for (int i = 0; i < E; ++i) {
+    const int64_t r = full ? r0 + i : clamp_last(r0 + i, R);
+    if (V == 4 && vec16) load(c, r * C + cc, 4, b, lane);
+    else
+      for (int k = 0; k < V; ++k) load(c, r * C + clamp_last(cc + k, C), 1, b, lane);
+  }
+}
+
+// k_cols_one<V, W, G, VEC16, E, MODE> over `waves` waves.
+void cols_one(const Where &c, int64_t R, int64_t C, int V, int W, int G, bool vec16, int E, int mode, int64_t blocks,
+              int waves) {
+  batches(blocks, 1, 64 * waves, [&](int64_t, int64_t cnt) { launch(c, cnt, 64 * waves); });
+  const int nc = V * (64 / G);
+  if ((C + nc - 1) / nc != blocks) report(c, "column blocks", blocks, nc, -1, -1);
+  for (int64_t b : visit(blocks)) {
+    const int64_t cb = line_on_one_die<int>((int)b, (int)((C + nc - 1) / nc), nc);
+    if (cb < 0 || cb >= blocks) report(c, "column block", cb, blocks, b, -1);
+    for (int w = 0; w < waves; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int q = lane / G, g = lane % G;
+        const int64_t c0 = cb * nc + (int64_t)q * V;
+        const int64_t rw = (int64_t)w * E * G, r0 = rw + (int64_t)g * E;
+        const bool full = mode == 1 || r0 + E <= R;
+        if (mode != 0 || rw < R) cols_tile(c, R, C, c0, r0, full, V, E, vec16, b, lane);
+        const int64_t cc = cols_first(c0, C, V);
+        for (int k = 0; k < V; ++k) load(c, clamp_last(cc + k, C), 1, b, lane);
+      }
+  }
+  (void)W;
+}
+
+// k_cols_y and k_cols_dq (the chunked path; the workspace reads are clamped
+// to the nch chunk nodes the workspace holds).
+void cols_chunked(const Where &c, int64_t R, int64_t C, int V, int W) {
+  const ColsChunkPlan p = cols_chunk_plan(V, W, R, C);
+  const int nc = V * (64 / p.G);
+  const int64_t nb = p.ncb * p.nch;
+  batches(nb, 1, 64 * W, [&](int64_t, int64_t cnt) {
+    launch(c, cnt, 64 * W);  // k_cols_y
+    launch(c, cnt, 64 * W);  // k_cols_dq
+  });
+  // the top trees: 64/S columns per wave (S lanes per column) for at most
+  // CC_GROUP chunks, else a wave per column
+  const int pw = p.nch <= 4 ? 16 : p.nch <= 8 ? 8 : p.nch <= 16 ? 4 : p.nch <= CC_GROUP ? 2 : 1;
+  batches((C + 4 * pw - 1) / (4 * pw), 1, 256, [&](int64_t, int64_t cnt) { launch(c, cnt, 256); });
+  if (p.nch > (R + CC_E * CC_MIN_W - 1) / (CC_E * CC_MIN_W)) report(c, "chunks beyond the workspace", p.nch, R, -1, -1);
+  for (int64_t b : visit(nb)) {
+    const int64_t cb = b / p.nch, j = b % p.nch;
+    for (int w = 0; w < W; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int q = lane / p.G, g = lane % p.G;
+        const int64_t c0 = cb * nc + (int64_t)q * V;
+        const int64_t rw = j * ((int64_t)CC_E * p.G * W) + (int64_t)w * (CC_E * p.G), r0 = rw + (int64_t)g * CC_E;
+        cols_tile(c, R, C, c0, r0, r0 + CC_E <= R, V, CC_E, true, b, lane);
+        const int64_t cc = cols_first(c0, C, V);
+        for (int k = 0; k < V; ++k) load(c, cc + k, 1, b, lane);
+      }
+  }
+}
+
+// k_var_cols: a lane per column.
+void cols_lane(const Where &c, int64_t R, int64_t C) {
+  const RowsPlan p = cols_lane_plan(R);
+  const int64_t nb = (C + 63) / 64;
+  batches(nb, 1, 64 * p.W, [&](int64_t, int64_t cnt) { launch(c, cnt, 64 * p.W); });
+  for (int64_t b : visit(nb))
+    for (int w = 0; w < p.W; ++w)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int64_t col = b * 64 + lane, r0 = (int64_t)w * p.E;
+        const bool full = r0 + p.E <= R, allcols = b * 64 + 64 <= C;
+        for (int i = 0; i < p.E; ++i) {
+          if (full && allcols) load(c, (r0 + i) * C + col, 1, b, lane);
+          else load(c, clamp_last(r0 + i, R) * C + clamp_last(col, C), 1, b, lane);
+        }
+        load(c, clamp_last(col, C), 1, b, lane);
+      }
+}
+
+// k_cols_short: four columns per lane, R < 16 rows.
+void cols_short(const Where &c, int64_t R, int64_t C) {
+  const int E = cols_short_e(R);
+  const int64_t nb = (C / 4 + 255) / 256;
+  batches(nb, 1, 256, [&](int64_t, int64_t cnt) { launch(c, cnt, 256); });
+  for (int64_t b : visit(nb))
+    for (int t = 0; t < 256; ++t) {
+      const int64_t c0 = (b * 256 + t) * 4;
+      if (c0 >= C) continue;
+      for (int i = 0; i < E; ++i) load(c, clamp_last<int64_t>(i, R) * C + c0, 4, b, t);
+    }
+}
+
+// ------------------------------------------------------------------ routes
+
+struct Knobs {
+  RouteKnobs r;
+  int split, loadp, full_rows;
+  int cols_waves;
+};
+
+// off: the matrix's address modulo 16 bytes (0, 8 or 4).
+void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k, bool fills) {
+  const bool ax1 = axis == 1;
+  const int64_t n = ax1 ? cols : rows;
+  if (rows == 0 || cols == 0) return;
+  const bool vec16 = off == 0 && cols % 4 == 0;
+  const Route route = f32_route(rows, cols, ax1, vec16, k.r, fills);
+  char name[64];
+  snprintf(name, sizeof name, "f32 axis %d route %d", axis, (int)route);
+  const Where c{name, rows, cols, rows * cols};
+  switch (route) {
+    case Route::LONG_ROWS_CHUNKED: long_rows(c, rows, n, vec16); break;
+    case Route::ROWS_SEG: rows_seg(c, rows, n, seg_vw(off, cols), 1); break;
+    case Route::ROWS_TILE: rows_tile(c, rows, n, vec16, k.split, k.loadp, k.full_rows); break;
+    case Route::COLS_ONE_READ: {
+      const ColsLongPlan p = cols_long_plan(rows, cols);
+      cols_one(c, rows, cols, 1, 16, 4, false, p.E, p.mode, p.blocks, p.waves);
+      break;
+    }
+    case Route::COLS_CHUNKED: cols_chunked(c, rows, cols, vec16 ? 4 : 1, k.cols_waves); break;
+    case Route::COLS_SHORT: cols_short(c, rows, cols); break;
+    case Route::COLS_ONE4: {
+      const ColsOnePlan p = cols_one4_plan(rows, cols);
+      cols_one(c, rows, cols, 4, p.W, p.G, vec16, CC_E, 0, p.blocks, p.W);
+      break;
+    }
+    case Route::COLS_ONE1: {
+      const ColsOnePlan p = cols_one1_plan(rows, cols);
+      cols_one(c, rows, cols, 1, p.W, p.G, false, CC_E, 0, p.blocks, p.W);
+      break;
+    }
+    case Route::COLS_LANE: cols_lane(c, rows, cols); break;
+  }
+}
+
+void variance_c64(int64_t rows, int64_t cols, int off, int short_rows) {
+  if (rows == 0 || cols == 0 || cols > C64_FUSED_MAX_N) return;
+  const Where c{"c64 axis 1", rows, cols, 2 * rows * cols};
+  const bool vec = off == 0 && cols % 2 == 0;
+  if (cols <= SEG_MAX_N && short_rows) rows_seg(c, rows, cols, vec ? 2 : 1, 2);
+  else rows_c64(c, rows, cols, vec);
+}
+
+void variant_f32(int64_t rows, int64_t cols, int axis, int off) {
+  const Where c{"variant", rows, cols, rows * cols};
+  if (axis == 1) {
+    const RowsPlan p = variant_rows_plan(cols);
+    const bool vec = off == 0 && cols % 4 == 0;
+    batches(rows, 1, 64 * p.W, [&](int64_t r0, int64_t nr) { rows_launch(c, r0, nr, cols, cols, p.E, p.W, vec, 1); });
+  } else {
+    cols_lane(c, rows, cols);
+  }
+}
+
+// k_var_kahan: a lane per slice, chunks of 64 values.
+void kahan(int64_t rows, int64_t cols, int axis, int off) {
+  const bool ax1 = axis == 1;
+  const int64_t nsl = ax1 ? rows : cols, n = ax1 ? cols : rows, ld = cols;
+  const bool vec = ax1 && off == 0 && cols % 4 == 0;
+  const Where c{"kahan", rows, cols, rows * cols};
+  const int64_t nb = (nsl + 63) / 64, nch = (n + KS_T - 1) / KS_T;
+  launch(c, nb, 64);
+  for (int64_t b : visit(nb)) {
+    const int64_t s0 = b * 64;
+    for (int lane = 0; lane < 64; ++lane) {
+      const int64_t slc = clamp_last(s0 + lane, nsl);
+      load(c, ax1 ? slc * ld : slc, 1, b, lane);
+      for (int64_t ch0 = 0; ch0 < nch + 2; ++ch0) {
+        const int64_t ch = clamp_last(ch0, nch);
+        if (ax1) {
+          for (int j = 0; j < 16; ++j) {
+            const int64_t row = clamp_last(s0 + 4 * j + (lane >> 4), nsl);
+            const int64_t col = ch * KS_T + 4 * (lane & 15);
+            if (vec && col + 3 < n) load(c, row * ld + col, 4, b, lane);
+            else
+              for (int t = 0; t < 4; ++t) load(c, row * ld + clamp_last(col + t, n), 1, b, lane);
+          }
+        } else {
+          for (int kk = 0; kk < KS_T; ++kk) load(c, clamp_last(ch * KS_T + kk, n) * ld + slc, 1, b, lane);
+        }
+        if (nch > 8 && ch0 == 2) ch0 = nch - 3;  // long slices: the first and last chunks
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ tree sum
+
+void tree_sum(int64_t n, int e, int64_t target, bool vec, int loadp, bool xcd) {
+  if (n == 0) return;
+  const SumPlan p = plan_sum(n, e, target, SUM_W, SUM_MAX_BLOCKS, SUM_MAX_LOG2_GROUP);
+  const Where c{"tree sum", 1, n, n};
+  launch(c, p.blocks, 64 * SUM_W);
+  if (p.blocks > SUM_MAX_BLOCKS) report(c, "blocks above the workspace", p.blocks, SUM_MAX_BLOCKS, -1, -1);
+  const int64_t size = 64LL * e, G = 1LL << p.log2_g;
+  for (int64_t b : visit(p.blocks)) {
+    const int64_t bid = xcd ? xcd_contiguous((int)b, (int)p.blocks) : b;
+    for (int w = 0; w < SUM_W; ++w) {
+      const int64_t c0 = (bid * SUM_W + w) * G;
+      const bool run_full = (c0 + G) * size <= n;
+      for (int64_t j = 0; j < G; ++j) {
+        if (G > 8 && j == 4) j = G - 4;  // long runs: the first and last chunks
+        const int64_t ch = c0 + j, len = n - ch * size;
+        const int lim = tile_lim(len, (int)size);
+        for (int lane = 0; lane < 64; ++lane) {
+          if (run_full || lim == size) {
+            if (vec)
+              for (int k = 0; k < e / 4; ++k) load(c, ch * size + tile_index(loadp == 1, true, e, lane, k), 4, b, lane);
+            else
+              for (int i = 0; i < e; ++i) {
+                const int idx = loadp == 1 ? tile_index(true, false, e, lane, i) : tile_index(false, false, e, lane, i);
+                load(c, ch * size + idx, 1, b, lane);
+              }
+          } else if (lim > 0) {
+            for (int i = 0; i < e; ++i) {
+              const int raw = loadp == 1 ? tile_index(true, false, e, lane, i)
+                              : vec      ? tile_index(false, true, e, lane, i / 4) + (i % 4)
+                                         : tile_index(false, false, e, lane, i);
+              load(c, ch * size + clamp_group(raw, lim, 1), 1, b, lane);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int main() {
+  // shapes: boundaries of every plan, ragged tails, odd widths
+  const int64_t sizes[] = {1,    2,    3,    4,    5,    7,    8,    15,   16,   17,   31,   33,   63,    64,
+                           65,   100,  127,  128,  129,  255,  256,  257,  300,  511,  512,  513,  777,   1000,
+                           1023, 1024, 1025, 1500, 2047, 2048, 2049, 3000, 4095, 4096, 4097, 6000, 8191,  8192,
+                           8193, 12345, 16383, 16384, 16385, 20000, 32768, 32769, 65535, 65536, 65537, 100003};
+  const RouteKnobs dflt{1, 1, 1024, 1, 1, 1};
+  std::vector<Knobs> knobs;
+  knobs.push_back({dflt, 0, 1, 1, 16});
+  for (int split : {1, 2, 4, 8}) knobs.push_back({dflt, split, 1, 1, 16});
+  for (int lp : {0, 2}) knobs.push_back({dflt, 0, lp, 1, 16});
+  knobs.push_back({dflt, 0, 1, 0, 16});
+  for (int cw : {4, 8}) knobs.push_back({{1, 0, 1024, 1, 1, 1}, 0, 1, 1, cw});
+  knobs.push_back({{0, 1, 1024, 0, 0, 0}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 1024, 1, 1, 2}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 1024, 1, 1, 3}, 0, 1, 1, 16});
+  knobs.push_back({{1, 2, 1024, 1, 1, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 512, 1, 1, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 0, 1, 1, 1}, 0, 1, 1, 16});
+
+  // every shape in the default knobs, the knob variants on a subset
+  const int64_t some[] = {1, 3, 16, 17, 64, 65, 257, 513, 1000, 1025, 2048, 3000, 4096, 4097, 16385, 65537};
+  auto in_some = [&](int64_t v) { return std::find(std::begin(some), std::end(some), v) != std::end(some); };
+  // The address offset (mod 16 bytes) only decides the load width: 16-byte
+  // loads need 0, the short rows' 8-byte loads 8; 4 stands for the rest.
+  for (int64_t R : sizes)
+    for (int64_t C : sizes) {
+      if (R * C > (1LL << 24)) continue;
+      for (int axis : {0, 1}) {
+        const int64_t n = axis == 1 ? C : R;
+        if (axis == 1 && n > ROWS_MAX_N && (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK > LS_MAX_CHUNKS) continue;
+        const bool cand = cols_one_read_candidate(axis == 1, n, dflt);
+        const bool seg = axis == 1 && n <= SEG_MAX_N;
+        const size_t nk = in_some(R) && in_some(C) ? knobs.size() : 1;
+        for (int off : {0, 8, 4}) {
+          if (off == 8 && !seg) continue;
+          for (size_t i = 0; i < nk; ++i)
+            for (bool fills : {true, false})
+              if (fills || cand || i > 0) variance_f32(R, C, axis, off, knobs[i], fills);
+          if (off == 8 || (axis == 0 && off != 0)) continue;
+          if ((axis == 1 ? C <= ROWS_MAX_N : R <= COLS_MAX_R)) variant_f32(R, C, axis, off);
+          if (n <= ((int64_t)KS_T << KS_LEVELS)) kahan(R, C, axis, off);
+        }
+      }
+      for (int off : {0, 4})
+        for (int sr : {0, 1}) variance_c64(R, C, off, sr);
+    }
+  for (int64_t n : {1LL, 5LL, 2047LL, 2048LL, 2049LL, 100000000LL, 100000003LL})
+    for (int e : {16, 32})
+      for (int64_t target : {1LL, 64LL, 8192LL})
+        for (bool vec : {true, false})
+          for (int lp : {0, 1})
+            for (bool xcd : {false, true}) tree_sum(n, e, target, vec, lp, xcd);
+
+  // launch limits at the largest accepted shapes (no loads walked beyond the
+  // sampled workgroups)
+  for (int64_t C : sizes) {
+    const int64_t R = VAR_MAX_ELEMS / C;
+    if (R > 0x7fffffffLL && C > 0) continue;  // more slices than a grid holds: refused
+    for (int axis : {0, 1}) {
+      const int64_t n = axis == 1 ? C : R, nsl = axis == 1 ? R : C;
+      if (nsl > 0x7fffffffLL) continue;
+      if (axis == 1 && n > ROWS_MAX_N && (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK > LS_MAX_CHUNKS) continue;
+      if (axis == 0 && (n + 63) / 64 > ((int64_t)64 * 64 << (TOP_BIG_LEVELS - 1))) continue;
+      for (const Knobs &k : knobs)
+        for (bool fills : {true, false}) variance_f32(R, C, axis, 0, k, fills);
+    }
+  }
+  for (int64_t R : sizes) {
+    const int64_t C = VAR_MAX_ELEMS / R;
+    for (int axis : {0, 1}) {
+      const int64_t n = axis == 1 ? C : R, nsl = axis == 1 ? R : C;
+      if (nsl > 0x7fffffffLL) continue;
+      if (axis == 1 && n > ROWS_MAX_N && (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK > LS_MAX_CHUNKS) continue;
+      for (const Knobs &k : knobs)
+        for (bool fills : {true, false}) variance_f32(R, C, axis, 0, k, fills);
+    }
+  }
+  for (int e : {16, 32}) tree_sum(SUM_MAX_N, e, 8192, true, 0, false);
+
+  printf("%lld loads and %lld launches checked, %lld failures\n", (long long)g_checks, (long long)g_launches,
+         (long long)g_fail);
+  return g_fail ? 1 : 0;
+}

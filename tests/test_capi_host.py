@@ -101,6 +101,10 @@ def test_variance_argument_errors(L):
     assert L.sv_variance_f32(BAD, 4, 4, 1, 0, None, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_variance_f32(None, 4, 4, 1, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_variance_f32(BAD, 1 << 21, 1 << 20, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
+    # at most 2^36 values (every launch within 2^32 - 1 work-items)
+    assert L.sv_variance_f32(BAD, (1 << 18) + 1, 1 << 18, 1, 0, out, None, None, 0, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_variance_f32_workspace_size((1 << 18) + 1, 1 << 18, 0) == ctypes.c_size_t(-1).value
+    assert L.sv_variance_f32_workspace_size(1 << 18, 1 << 18, 0) != ctypes.c_size_t(-1).value
     # an empty set of slices is a successful no-op
     assert L.sv_variance_f32(None, 0, 5, 1, 0, None, None, None, 0, None) == 0
     # long slices need a workspace of the advertised size, 256-byte aligned
