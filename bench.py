@@ -66,7 +66,8 @@ ADN_PAGE_FLOAT_GELEMS = {"NVIDIA GB10": 55.4, "NVIDIA RTX PRO 4500 Blackwell": 1
 def source_digest() -> str:
     h = hashlib.sha256()
     for rel in ("stable_variance_amd/csrc/sv_lib.hip", "stable_variance_amd/csrc/sv_adn.hip",
-                "stable_variance_amd/csrc/sv_f64.hip", "stable_variance_amd/csrc/sv_device.hpp"):
+                "stable_variance_amd/csrc/sv_f64.hip", "stable_variance_amd/csrc/sv_device.hpp",
+                "stable_variance_amd/csrc/sv_index.hpp"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -418,11 +419,13 @@ def main():
     torch_sum_ms = time_op(lambda i: torch.sum(c5[i % N_SUM_COPIES]))
     # practical HBM read ceiling: a plain non-temporal read of the same buffers
     probe_out = torch.empty(1, dtype=torch.float32, device=dev)
-    read_sum_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c5[i % N_SUM_COPIES].data_ptr(), SUM_N,
-                                                                     probe_out.data_ptr(), sh)))
-    read_var_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c4[i % N_VAR_COPIES].data_ptr(),
+    # (the median of 7 batches, like the kernels' own batches: a single short
+    # batch after the context measurements can run at unsettled clocks)
+    read_sum_ms = batches(lambda i: check(L.sv_probe_read_bandwidth(c5[i % N_SUM_COPIES].data_ptr(), SUM_N,
+                                                                     probe_out.data_ptr(), sh)))["median_ms"]
+    read_var_ms = batches(lambda i: check(L.sv_probe_read_bandwidth(c4[i % N_VAR_COPIES].data_ptr(),
                                                                      VAR_ROWS * VAR_COLS, probe_out.data_ptr(), sh)),
-                          reps=60)
+                          reps=60)["median_ms"]
     read_sum_gbs = SUM_N * 4 / (read_sum_ms * 1e-3) / 1e9
     read_var_gbs = VAR_ROWS * VAR_COLS * 4 / (read_var_ms * 1e-3) / 1e9
 
