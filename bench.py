@@ -87,8 +87,8 @@ def read_summary(path, key):
     if kv.get("source_digest") != source_digest():
         return None
     try:
-        return float(kv[key])
-    except (KeyError, ValueError):
+        return float(kv[key].split()[0])  # the figure, before any note
+    except (KeyError, ValueError, IndexError):
         return None
 
 
