@@ -253,8 +253,9 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
  *   bytes, 256-byte aligned, whose first SV_TREE_SUM_COUNTER_BYTES bytes are
  *   ticket counters with the same rules as for sv_tree_sum_f32.
  * sv_variance_f64: x row-major [rows, cols] device doubles (8-byte aligned),
- *   rows * cols < 2^39; var_out (and mean_out if not NULL) one double per
- *   slice; workspace of sv_variance_f64_workspace_size(rows, cols, axis)
+ *   rows * cols <= 2^35 (256 GiB of float64; every launch then stays
+ *   within HIP's 2^32 - 1 work-items per grid); var_out (and mean_out if
+ *   not NULL) one double per slice; workspace of sv_variance_f64_workspace_size(rows, cols, axis)
  *   bytes, 256-byte aligned scratch, NULL allowed when that size is 0.
  * sv_variance_f64_workspace_size: 0 when every slice fits one workgroup
  *   (axis 1: n <= 16384; axis 0: n <= 1024).  Longer slices are reduced in
@@ -262,7 +263,7 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
  *   for narrow matrices), reading the input twice: three arrays of 16 bytes
  *   per 128-value chunk per slice and 8 bytes per slice, each rounded up to
  *   256 bytes.  (size_t)-1 for an unsupported
- *   shape (a bad axis, rows * cols >= 2^39, an axis-1 row of more than 8192
+ *   shape (a bad axis, rows * cols > 2^35, an axis-1 row of more than 8192
  *   chunks, i.e. 67,108,864 values).
  * Errors and asynchrony as for the float32 entry points.
  */

@@ -245,16 +245,16 @@ __device__ __forceinline__ NodeD load_node_d(const NodeD *src) {
 
 // ------------------------------------------------------------------ tree sum
 
-constexpr int S64_W = 4;                 // waves per workgroup
-constexpr int S64_EF = 32;               // floats per lane per chunk (16 doubles)
+using svx::S64_W;                        // waves per workgroup
+using svx::S64_EF;                       // floats per lane per chunk (16 doubles)
 constexpr int S64_E = S64_EF / 2;
 constexpr int S64_CHUNK = 64 * S64_E;    // doubles per chunk
-constexpr int S64_MAX_BLOCKS = 8192;
+using svx::S64_MAX_BLOCKS;
 constexpr int S64_GROUP = 64;
 constexpr int S64_COUNTER_STRIDE = 64;
-constexpr int S64_MAX_LOG2_G = 16;
+using svx::S64_MAX_LOG2_G;
 constexpr size_t S64_WS_HEADER = 256 * (1 + S64_MAX_BLOCKS / S64_GROUP);
-constexpr int64_t S64_MAX_N = 1LL << 35;
+using svx::S64_MAX_N;
 static_assert(S64_WS_HEADER == SV_TREE_SUM_COUNTER_BYTES, "same counter layout as the float32 sum");
 
 // Each wave reduces a power-of-two run of chunks of 1024 doubles in tree
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   const bool empty = base >= n;
 
   float vf[2 * E];
-  const int64_t avail = 2 * (((int64_t)gridDim.x - 1 - row) * ld + (n - base));  // floats to the matrix's end
+  const int64_t avail = 2 * svx::rows_avail(gridDim.x, row, ld, n, base);  // floats to the launch's last row
   sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(p + base), 2 * (n - base), nullptr, vf, lane,
                                       avail);
   double v[E];
@@ -487,13 +487,12 @@ template <int E, int S, int VW>
 __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict__ x, int64_t rows, int64_t n,
                                                         int64_t ld, int64_t ddof, double *__restrict__ var_out,
                                                         double *__restrict__ mean_out) {
-  constexpr int RPW = 64 / S;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane % S;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * RPW + lane / S;
+  const int64_t row = svx::seg_row(blockIdx.x, w, lane, S);  // 64/S rows per wave
   const bool rowok = row < rows;
-  const double *__restrict__ p = x + (rowok ? row : rows - 1) * ld;
+  const double *__restrict__ p = x + svx::clamp_last(row, rows) * ld;
   const bool full = (n == (int64_t)S * E);
   const int64_t e0 = (int64_t)l * E;
   const int64_t left = n - e0;
@@ -503,7 +502,7 @@ __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict
 #pragma unroll
     for (int j = 0; j < E / 2; ++j) {
       const int64_t e = e0 + 2 * j;
-      const double2 g = *reinterpret_cast<const double2 *>(p + (full || e < n ? e : n - 2));
+      const double2 g = *reinterpret_cast<const double2 *>(p + (full ? e : svx::clamp_group(e, n, 2)));
       v[2 * j] = g.x;
       v[2 * j + 1] = g.y;
     }
@@ -511,7 +510,7 @@ __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int64_t e = e0 + i;
-      v[i] = p[full || e < n ? e : n - 1];
+      v[i] = p[full ? e : svx::clamp_group(e, n, 1)];
     }
   }
   const double x0 = p[0];
@@ -533,22 +532,22 @@ __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict
 template <int E, int W>
 __global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restrict__ x, int64_t R, int64_t C,
                                                          int64_t ddof, double *__restrict__ var_out,
-                                                         double *__restrict__ mean_out) {
+                                                         double *__restrict__ mean_out, int64_t b0) {
   __shared__ NodeD sy[W][64];
   __shared__ NodeD sd[W][64];
   __shared__ NodeD sq[W][64];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t col = (b0 + blockIdx.x) * 64 + lane;  // b0: launches of at most 2^32 - 1 work-items
   const bool colok = col < C;
   const int64_t r0 = (int64_t)w * E;
   const bool full = r0 + E <= R;
-  const int64_t ccol = colok ? col : C - 1;
+  const int64_t ccol = svx::clamp_last(col, C);
   double v[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int64_t r = r0 + i;
-    const double t = x[(r < R ? r : R - 1) * C + ccol];
+    const double t = x[svx::clamp_last(r, R) * C + ccol];
     v[i] = (colok && r < R) ? t : 0.0;
   }
   const double x0 = x[ccol];
@@ -604,13 +603,13 @@ __global__ __launch_bounds__(64 * W) void k_var_cols_f64(const double *__restric
 //     trees (a wave per column when there are many chunks) and step 4.
 // The input is read twice; the workspace is scratch.
 
-constexpr int L64_E = 16;                       // doubles per lane
-constexpr int L64_W = 8;                        // waves per workgroup (up to 256 VGPRs: no spills)
-constexpr int64_t L64_ROW_CHUNK = 64LL * L64_E * L64_W;  // 8192 doubles
-constexpr int L64_TOP_MAX_K = 32;               // chunk nodes per thread of a top tree
-constexpr int64_t L64_MAX_CHUNKS = 256LL * L64_TOP_MAX_K;
-constexpr int64_t C64_CHUNK = (int64_t)L64_E * L64_W;     // 128 rows
-constexpr int C64_GROUP = 32;                   // chunk nodes per column that k_cols_dq_d reduces for m itself
+using svx::L64_E;           // doubles per lane
+using svx::L64_W;           // waves per workgroup (up to 256 VGPRs: no spills)
+using svx::L64_ROW_CHUNK;   // 8192 doubles
+using svx::L64_TOP_MAX_K;   // chunk nodes per thread of a top tree
+using svx::L64_MAX_CHUNKS;
+using svx::C64_CHUNK;       // 128 rows
+using svx::C64_GROUP;       // chunk nodes per column that k_cols_dq_d reduces for m itself
 
 struct SliceWsD {
   NodeD *ny;  // y-tree node of every chunk of every slice
@@ -646,7 +645,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_long_rows_d(const double *__rest
   const int64_t base = c * L64_ROW_CHUNK + (int64_t)w * 64 * E;
   const bool empty = base >= n;  // wave-uniform: only padding, nodes (+0, +0)
   float vf[2 * E];
-  const int64_t avail = 2 * (((int64_t)gridDim.x / nch - 1 - r) * ld + (n - base));  // floats to the matrix's end
+  const int64_t avail = 2 * svx::rows_avail(gridDim.x / nch, r, ld, n, base);  // floats to the launch's last row
   sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(row + base), 2 * (n - base), nullptr, vf, lane,
                                       avail);
   double v[E];
@@ -691,7 +690,7 @@ __device__ __forceinline__ NodeD top_tree_d(const NodeD *__restrict__ nodes, int
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t idx = (int64_t)threadIdx.x * K + k;
-    const NodeD t = nodes[idx < nch ? idx : nch - 1];  // unconditional: the loads overlap
+    const NodeD t = nodes[svx::clamp_last(idx, nch)];  // unconditional: the loads overlap
     nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
   }
   NodeD r = wave_tree_d<NN>(node_tree_d<0, K, K, NN>(nd));
@@ -723,10 +722,10 @@ __global__ __launch_bounds__(256) void k_long_top_d(const double *__restrict__ x
 template <int V, int E, bool VEC16 = true>
 __device__ __forceinline__ void load_cols_tile_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t c0,
                                                  int64_t r0, bool full, double (&v)[V][E]) {
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const int64_t r = full ? r0 + i : (r0 + i < R ? r0 + i : R - 1);
+    const int64_t r = full ? r0 + i : svx::clamp_last(r0 + i, R);
     const double *p = x + r * C + cc;
     if constexpr (V == 2 && VEC16) {
       const double2 g = *reinterpret_cast<const double2 *>(p);
@@ -736,7 +735,7 @@ __device__ __forceinline__ void load_cols_tile_d(const double *__restrict__ x, i
       // columns past C (a partial last pair of an odd width) read the last
       // column instead; their results are never written
 #pragma unroll
-      for (int k = 0; k < V; ++k) v[k][i] = x[r * C + (cc + k < C ? cc + k : C - 1)];
+      for (int k = 0; k < V; ++k) v[k][i] = x[r * C + svx::clamp_last(cc + k, C)];
     }
   }
 }
@@ -760,7 +759,7 @@ __device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, 
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int64_t idx = b * 8 + k;
-      const NodeD t = p[(idx < nch ? idx : nch - 1) * stride];
+      const NodeD t = p[svx::clamp_last(idx, nch) * stride];
       nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
     }
     sub[b] = node_tree_d<0, 8, 8, KD_PLAIN>(nd);
@@ -777,13 +776,14 @@ __device__ __forceinline__ NodeD chunk_tree_1_d(const NodeD *p, int64_t stride, 
 // rows.
 template <int V, int G>
 __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restrict__ x, int64_t R, int64_t C,
-                                                         int64_t nch, SliceWsD ws) {
+                                                         int64_t nch, SliceWsD ws, int64_t b0) {
   constexpr int E = L64_E, W = L64_W, Q = 64 / G, NC = V * Q;
   __shared__ NodeD s[W][V][Q];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t blk = b0 + blockIdx.x;  // launches of at most 2^32 - 1 work-items
+  const int64_t cb = blk / nch, j = blk % nch;
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
@@ -794,7 +794,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restric
   double v[V][E];
   load_cols_tile_d<V, E>(x, R, C, c0, r0, full, v);
   double x0[V];
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
 #pragma unroll
   for (int k = 0; k < V; ++k) x0[k] = x[cc + k];
   shift_cols_tile_d<V, E>(v, x0, wave_full, valid);
@@ -825,22 +825,22 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_y_d(const double *__restric
 template <int PASS, int K, int S>
 __global__ __launch_bounds__(256) void k_cols_top_d(const double *__restrict__ x, int64_t R, int64_t C, int64_t nch,
                                                     int64_t ddof, SliceWsD ws, double *__restrict__ var_out,
-                                                    double *__restrict__ mean_out) {
+                                                    double *__restrict__ mean_out, int64_t b0) {
   constexpr int PW = 64 / S;
   const int lane = threadIdx.x & 63;
-  const int64_t col0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PW;
+  const int64_t col0 = ((b0 + blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * PW;
   if (col0 >= C) return;  // the whole wave
   const int64_t col = col0 + lane / S;
   const int sl = lane % S;
   const bool colok = col < C;
-  const int64_t cc = colok ? col : C - 1;
+  const int64_t cc = svx::clamp_last(col, C);
   auto tree = [&](const NodeD *p, auto nn) {
     constexpr int NN = decltype(nn)::value;
     NodeD nd[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int64_t idx = (int64_t)sl * K + k;
-      const NodeD t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+      const NodeD t = p[svx::clamp_last(idx, nch) * C];  // every load issued
       nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
     }
     return seg_tree_d<NN, S>(node_tree_d<0, K, K, NN>(nd));
@@ -861,14 +861,15 @@ __global__ __launch_bounds__(256) void k_cols_top_d(const double *__restrict__ x
 // zero nodes past nch) in batches of 64, merging the batch nodes in tree
 // order with a binary counter (wave-uniform loop, constant stack indices),
 // then the wave's six levels.  PASS 0: m; PASS 1: step 4.
-constexpr int TOP_BIG_LEVELS_D = 16;  // P up to 2^15
+using svx::TOP_BIG_LEVELS_D;  // P up to 2^15
 template <int PASS>
 __global__ __launch_bounds__(256) void k_cols_top_big_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                         int64_t nch, int log2p, int64_t ddof, SliceWsD ws,
-                                                        double *__restrict__ var_out, double *__restrict__ mean_out) {
+                                                        double *__restrict__ var_out, double *__restrict__ mean_out,
+                                                        int64_t b0) {
   constexpr int K = 64;
   const int lane = threadIdx.x & 63;
-  const int64_t col = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t col = (b0 + blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (col >= C) return;  // the whole wave
   const int64_t P = (int64_t)1 << log2p;
   auto tree = [&](const NodeD *p, auto nn) {
@@ -882,7 +883,7 @@ __global__ __launch_bounds__(256) void k_cols_top_big_d(const double *__restrict
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         const int64_t idx = i0 + k;
-        const NodeD t = p[(idx < nch ? idx : nch - 1) * C];  // every load issued
+        const NodeD t = p[svx::clamp_last(idx, nch) * C];  // every load issued
         nd[k] = idx < nch ? t : NodeD{0.0, 0.0};
       }
       NodeD carry = node_tree_d<0, K, K, NN>(nd);
@@ -920,7 +921,7 @@ __global__ __launch_bounds__(256) void k_cols_top_big_d(const double *__restrict
 // Tile layout as in k_cols_y_d.
 template <int V, int G, bool MLOCAL>
 __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restrict__ x, int64_t R, int64_t C,
-                                                          int64_t nch, SliceWsD ws) {
+                                                          int64_t nch, SliceWsD ws, int64_t b0) {
   constexpr int E = L64_E, W = L64_W, Q = 64 / G, NC = V * Q;
   __shared__ NodeD sd[W][V][Q];
   __shared__ NodeD sq[W][V][Q];
@@ -928,7 +929,8 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int64_t cb = blockIdx.x / nch, j = blockIdx.x % nch;
+  const int64_t blk = b0 + blockIdx.x;  // launches of at most 2^32 - 1 work-items
+  const int64_t cb = blk / nch, j = blk % nch;
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = j * ((int64_t)E * G * W) + (int64_t)w * (E * G);
   const int64_t r0 = rw + (int64_t)g * E;
@@ -936,13 +938,13 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
   const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
   if constexpr (MLOCAL) {
     const int t = threadIdx.x;
     if (t < NC) {
       const int k = t / Q, qq = t % Q;  // column V*qq + k of the block, clamped like the loads
       const int64_t col = cb * NC + (int64_t)qq * V + k;
-      const int64_t ccol = col < C ? col : C - 1;
+      const int64_t ccol = svx::clamp_last(col, C);
       sm[k][qq] = root_value_kd<KD_PLAIN>(chunk_tree_1_d(ws.ny + ccol, C, nch)) / (double)R;
     }
     __syncthreads();
@@ -994,7 +996,7 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
 template <int V, int W, int G, bool VEC16 = true>
 __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                        int64_t ddof, double *__restrict__ var_out,
-                                                       double *__restrict__ mean_out) {
+                                                       double *__restrict__ mean_out, int b0) {
   constexpr int E = L64_E, Q = 64 / G, NC = V * Q;
   __shared__ NodeD sd[W][V][Q];
   __shared__ NodeD sq[W][V][Q];
@@ -1002,7 +1004,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int64_t cb = blockIdx.x;
+  const int64_t cb = b0 + (int)blockIdx.x;  // b0: launches of at most 2^32 - 1 work-items
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
@@ -1013,9 +1015,9 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   double v[V][E];
   if (rw < R) load_cols_tile_d<V, E, VEC16>(x, R, C, c0, r0, full, v);
   double x0[V];
-  const int64_t cc = c0 < C ? c0 : C - V;
+  const int64_t cc = svx::cols_first(c0, C, V);
 #pragma unroll
-  for (int k = 0; k < V; ++k) x0[k] = x[cc + k < C ? cc + k : C - 1];
+  for (int k = 0; k < V; ++k) x0[k] = x[svx::clamp_last(cc + k, C)];
   shift_cols_tile_d<V, E>(v, x0, wave_full, valid);  // +0 past the last row
 #pragma unroll
   for (int k = 0; k < V; ++k) {
@@ -1068,14 +1070,14 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
 template <int E>
 __global__ __launch_bounds__(256) void k_cols_short_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                       int64_t ddof, double *__restrict__ var_out,
-                                                      double *__restrict__ mean_out) {
-  const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+                                                      double *__restrict__ mean_out, int64_t b0) {
+  const int64_t c0 = ((b0 + blockIdx.x) * 256 + threadIdx.x) * 2;
   if (c0 >= C) return;
   const double *__restrict__ p = x + c0;
   double v[2][E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const double2 g = *reinterpret_cast<const double2 *>(p + (i < R ? i : R - 1) * C);
+    const double2 g = *reinterpret_cast<const double2 *>(p + svx::clamp_last<int64_t>(i, R) * C);
     v[0][i] = g.x;
     v[1][i] = g.y;
   }
@@ -1112,15 +1114,15 @@ __global__ void k_fill_nan_d(double *__restrict__ a, double *__restrict__ b, int
   }
 }
 
-constexpr int64_t V64_ROWS_MAX_N = 16384;  // one workgroup per row
+using svx::V64_ROWS_MAX_N;  // one workgroup per row
 // Rows of up to 32768 values take one workgroup of 32 values per lane when
 // there are enough rows to fill the chip (fewer take the chunked path, which
 // spreads a row over several workgroups); the workspace is sized for the
 // chunked path either way.
-constexpr int64_t V64_ROWS_ONE_MAX_N = 32768;
-constexpr int64_t V64_ROWS_ONE_MIN_ROWS = 256;
-constexpr int64_t V64_COLS_MAX_R = 1024;   // whole columns in one workgroup
-constexpr int64_t V64_MAX_ELEMS = 1LL << 39;
+using svx::V64_ROWS_ONE_MAX_N;
+using svx::V64_ROWS_ONE_MIN_ROWS;
+using svx::V64_COLS_MAX_R;  // whole columns in one workgroup
+using svx::V64_MAX_ELEMS;   // 2^35 doubles: every launch within 2^32 - 1 work-items
 
 size_t round256_d(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -1162,59 +1164,79 @@ void launch_long_top_d(const double *x, int64_t n, int64_t ld, int64_t nch, int6
 template <int V, int G>
 void launch_cols_d(const double *x, int64_t R, int64_t C, int64_t ddof, const SliceWsD &ws, double *var,
                    double *mean, hipStream_t st) {
-  constexpr int64_t CH = C64_CHUNK * G;  // rows per chunk
-  constexpr int NC = V * (64 / G);       // columns per block
-  const int64_t nch = (R + CH - 1) / CH;
-  const int64_t ncb = (C + NC - 1) / NC;
-  const dim3 grid((unsigned)(ncb * nch)), block(64 * L64_W);
-  k_cols_y_d<V, G><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-  auto per_waves = [&](int per_wave) { return dim3((unsigned)((C + 4 * per_wave - 1) / (4 * per_wave))); };
+  const svx::ColsChunkPlan p = svx::cols_chunk64_plan(V, R, C);  // G = p.G
+  const int64_t nch = p.nch, ncb = p.ncb;
+  const dim3 block(64 * L64_W);
+  // workgroup b = cb * nch + j takes chunk j of column block cb; launches of
+  // at most 2^32 - 1 work-items
+  svh::in_batches(ncb * nch, 1, 64 * L64_W, [&](int64_t b0, int64_t nb) {
+    k_cols_y_d<V, G><<<dim3((unsigned)nb), block, 0, st>>>(x, R, C, nch, ws, b0);
+  });
+  auto dq = [&](auto mlocal) {
+    svh::in_batches(ncb * nch, 1, 64 * L64_W, [&](int64_t b0, int64_t nb) {
+      k_cols_dq_d<V, G, decltype(mlocal)::value><<<dim3((unsigned)nb), block, 0, st>>>(x, R, C, nch, ws, b0);
+    });
+  };
+  // the top kernels: four waves of per_wave columns each per workgroup
+  auto top = [&](int per_wave, auto &&launch) {
+    svh::in_batches((C + 4 * per_wave - 1) / (4 * per_wave), 1, 256,
+                    [&](int64_t b0, int64_t nb) { launch(dim3((unsigned)nb), b0); });
+  };
+#define SV_TOP64(PASS, K, S, PW)                                                                          \
+  top(PW, [&](dim3 g, int64_t b0) {                                                                      \
+    k_cols_top_d<PASS, K, S><<<g, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean, b0);            \
+  })
   if (nch <= C64_GROUP) {
-    k_cols_dq_d<V, G, true><<<grid, block, 0, st>>>(x, R, C, nch, ws);
+    dq(std::true_type{});
     // the final trees: a group of S >= nch lanes per column, one node each
-    if (nch <= 4) k_cols_top_d<1, 1, 4><<<per_waves(16), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    else if (nch <= 8) k_cols_top_d<1, 1, 8><<<per_waves(8), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    else if (nch <= 16) k_cols_top_d<1, 1, 16><<<per_waves(4), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-    else k_cols_top_d<1, 1, 32><<<per_waves(2), dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+    if (nch <= 4) SV_TOP64(1, 1, 4, 16);
+    else if (nch <= 8) SV_TOP64(1, 1, 8, 8);
+    else if (nch <= 16) SV_TOP64(1, 1, 16, 4);
+    else SV_TOP64(1, 1, 32, 2);
   } else if (nch <= 64 * 64) {
     // many chunks: a wave per column for m and for the final trees
-    const dim3 per_wave = per_waves(1);
     if (nch <= 64 * 4) {
-      k_cols_top_d<0, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-      k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top_d<1, 4, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      SV_TOP64(0, 4, 64, 1);
+      dq(std::false_type{});
+      SV_TOP64(1, 4, 64, 1);
     } else if (nch <= 64 * 16) {
-      k_cols_top_d<0, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-      k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top_d<1, 16, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      SV_TOP64(0, 16, 64, 1);
+      dq(std::false_type{});
+      SV_TOP64(1, 16, 64, 1);
     } else {
-      k_cols_top_d<0, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
-      k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-      k_cols_top_d<1, 64, 64><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, ddof, ws, var, mean);
+      SV_TOP64(0, 64, 64, 1);
+      dq(std::false_type{});
+      SV_TOP64(1, 64, 64, 1);
     }
   } else {
     int log2p = 0;  // runs of 64 * 2^log2p chunk nodes per lane
     while (((int64_t)64 * 64 << log2p) < nch) ++log2p;
-    const dim3 per_wave = per_waves(1);
-    k_cols_top_big_d<0><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
-    k_cols_dq_d<V, G, false><<<grid, block, 0, st>>>(x, R, C, nch, ws);
-    k_cols_top_big_d<1><<<per_wave, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean);
+    top(1, [&](dim3 g, int64_t b0) {
+      k_cols_top_big_d<0><<<g, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean, b0);
+    });
+    dq(std::false_type{});
+    top(1, [&](dim3 g, int64_t b0) {
+      k_cols_top_big_d<1><<<g, dim3(256), 0, st>>>(x, R, C, nch, log2p, ddof, ws, var, mean, b0);
+    });
   }
+#undef SV_TOP64
 }
 
-// Row groups per wave, so that lanes stay on columns: with `groups` column
-// groups of V, G = 1 for at least 64 groups, 4 for 9 to 63 (16 groups per
-// block), 8 for 5 to 8, 16 for 3 and 4, 32 for 2 and 64 for one.
+// Row groups per wave, so that lanes stay on columns (svx::cols_chunk64_plan):
+// with `groups` column groups of V, G = 1 for at least 64 groups, 4 for 9 to
+// 63 (16 groups per block), 8 for 5 to 8, 16 for 3 and 4, 32 for 2 and 64
+// for one.
 template <int V>
 void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const SliceWsD &ws, double *var,
                     double *mean, hipStream_t st) {
-  const int64_t groups = (C + V - 1) / V;
-  if (groups >= 64) launch_cols_d<V, 1>(x, R, C, ddof, ws, var, mean, st);
-  else if (groups > 8) launch_cols_d<V, 4>(x, R, C, ddof, ws, var, mean, st);
-  else if (groups > 4) launch_cols_d<V, 8>(x, R, C, ddof, ws, var, mean, st);
-  else if (groups > 2) launch_cols_d<V, 16>(x, R, C, ddof, ws, var, mean, st);
-  else if (groups > 1) launch_cols_d<V, 32>(x, R, C, ddof, ws, var, mean, st);
-  else launch_cols_d<V, 64>(x, R, C, ddof, ws, var, mean, st);
+  switch (svx::cols_chunk64_plan(V, R, C).G) {
+    case 1: launch_cols_d<V, 1>(x, R, C, ddof, ws, var, mean, st); break;
+    case 4: launch_cols_d<V, 4>(x, R, C, ddof, ws, var, mean, st); break;
+    case 8: launch_cols_d<V, 8>(x, R, C, ddof, ws, var, mean, st); break;
+    case 16: launch_cols_d<V, 16>(x, R, C, ddof, ws, var, mean, st); break;
+    case 32: launch_cols_d<V, 32>(x, R, C, ddof, ws, var, mean, st); break;
+    default: launch_cols_d<V, 64>(x, R, C, ddof, ws, var, mean, st); break;
+  }
 }
 
 // Columns of 64 < R <= 1024 rows in one launch (k_cols_one_d), 16*G*W = the
@@ -1229,26 +1251,25 @@ void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const S
 // [512, 4096] 8.0 / 10.9; [1000, 20000] 65.2 / 52.5, [1000, 1000] 13.0 / 6.9.
 void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool vec, double *var, double *mean,
                        hipStream_t st) {
-  if (R > 512) {
-    const dim3 grid2((unsigned)((C + 7) / 8)), block(256);
-    if (vec) k_cols_one_d<2, 4, 16><<<grid2, block, 0, st>>>(x, R, C, ddof, var, mean);
-    else if (C >= 2) k_cols_one_d<2, 4, 16, false><<<grid2, block, 0, st>>>(x, R, C, ddof, var, mean);  // two 8-byte loads
-    else k_cols_one_d<1, 4, 16><<<dim3((unsigned)((C + 3) / 4)), block, 0, st>>>(x, R, C, ddof, var, mean);
-    return;
-  }
-  int64_t cap = L64_E;
-  while (cap < R) cap *= 2;
-  const int gw = (int)(cap / L64_E);  // 8 .. 32
-  const int g = (gw > 16 || (C + 63) / 64 < 512) ? 4 : 1;
-  const int w = gw / g;
-  const dim3 grid((unsigned)((C + 64 / g - 1) / (64 / g)));
-#define SV_ONE64(G_, W_) k_cols_one_d<1, W_, G_><<<grid, dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean)
-  switch (g * 32 + w) {  // 64 < R <= 512: 128 <= 16*G*W <= 512
-    case 32 * 1 + 8: SV_ONE64(1, 8); break;
-    case 32 * 1 + 16: SV_ONE64(1, 16); break;
-    case 32 * 4 + 2: SV_ONE64(4, 2); break;
-    case 32 * 4 + 4: SV_ONE64(4, 4); break;
-    default: SV_ONE64(4, 8); break;  // gw = 32
+  const svx::ColsOne64Plan p = svx::cols_one64_plan(R, C, vec);
+#define SV_ONE64(V_, W_, G_, ...)                                                                         \
+  svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                    \
+    k_cols_one_d<V_, W_, G_, ##__VA_ARGS__><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, \
+                                                                                         mean, (int)b0);  \
+  })
+  if (p.V == 2) {
+    if (vec) SV_ONE64(2, 4, 16);
+    else SV_ONE64(2, 4, 16, false);  // two 8-byte loads
+  } else if (p.G == 16) {
+    SV_ONE64(1, 4, 16);  // a single column of 513..1024 rows
+  } else {
+    switch (p.G * 32 + p.W) {  // 64 < R <= 512: 128 <= 16*G*W <= 512
+      case 32 * 1 + 8: SV_ONE64(1, 8, 1); break;
+      case 32 * 1 + 16: SV_ONE64(1, 16, 1); break;
+      case 32 * 4 + 2: SV_ONE64(1, 2, 4); break;
+      case 32 * 4 + 4: SV_ONE64(1, 4, 4); break;
+      default: SV_ONE64(1, 8, 4); break;  // gw = 32
+    }
   }
 #undef SV_ONE64
 }
@@ -1285,11 +1306,11 @@ sv_status sv_tree_sum_f64(const double *x, int64_t n, double *out, void *workspa
     k_zero_d<<<1, 1, 0, st>>>(out);
     return check_launch("sv_tree_sum_f64");
   }
-  const int64_t chunks = (n + S64_CHUNK - 1) / S64_CHUNK;
-  const int64_t wgs = (chunks + S64_W - 1) / S64_W;
-  int g = 0;
-  while (g < S64_MAX_LOG2_G && ((wgs + (1LL << g) - 1) >> g) > S64_MAX_BLOCKS) ++g;
-  const int64_t blocks = (wgs + (1LL << g) - 1) >> g;
+  // chunks of 64 * 16 doubles, each wave streaming 2^g of them, g the
+  // smallest value that keeps the workgroup count at or below S64_MAX_BLOCKS
+  const svx::SumPlan plan = svx::plan_sum(n, S64_EF / 2, S64_MAX_BLOCKS, S64_W, S64_MAX_BLOCKS, S64_MAX_LOG2_G);
+  const int g = plan.log2_g;
+  const int64_t blocks = plan.blocks;
   unsigned *counter = reinterpret_cast<unsigned *>(workspace);
   NodeD *part = reinterpret_cast<NodeD *>(reinterpret_cast<char *>(workspace) + S64_WS_HEADER);
   const dim3 grid((unsigned)blocks), block(64 * S64_W);
@@ -1319,7 +1340,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
   const int64_t nslices = ax1 ? rows : cols;
   const int64_t n = ax1 ? cols : rows;
   if (cols > 0 && rows > V64_MAX_ELEMS / cols)
-    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: rows * cols above 2^39");
+    return fail(SV_ERR_UNSUPPORTED, "sv_variance_f64: rows * cols above 2^35");
   if (nslices == 0) return ok();
   if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: var_out is NULL");
   if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_f64: x is NULL");
@@ -1348,9 +1369,34 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     k_fill_nan_d<<<dim3((unsigned)((nslices + 255) / 256)), dim3(256), 0, st>>>(var_out, mean_out, nslices);
     return check_launch("sv_variance_f64");
   }
-  if (ax1) {
-    const bool vec = svh::aligned16(x) && (cols % 2 == 0);
-    const dim3 grid((unsigned)rows);
+  const bool vec = svh::aligned16(x) && (cols % 2 == 0);
+  switch (svx::f64_route(rows, cols, ax1, vec)) {
+    case svx::Route64::ROWS_SEG: {
+      // rows of up to 512 doubles sharing waves: 16-byte loads of two
+      // doubles for aligned rows of an even count, else single doubles
+#define SV_SEG64(E, S)                                                                                  \
+  svh::in_batches(rows, 4 * (64 / S), 256, [&](int64_t r0, int64_t nr) {                                \
+    const dim3 sgrid((unsigned)((nr + 4 * (64 / S) - 1) / (4 * (64 / S))));                             \
+    const double *xr = x + r0 * cols;                                                                   \
+    double *vr = var_out + r0, *mr = mean_out ? mean_out + r0 : nullptr;                                \
+    if (vec) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr);     \
+    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr);         \
+  })
+      const svx::SegPlan sp = svx::seg_plan(n);
+      switch (sp.E * 100 + sp.S) {
+        case 401: SV_SEG64(4, 1); break;
+        case 801: SV_SEG64(8, 1); break;
+        case 1601: SV_SEG64(16, 1); break;
+        case 1602: SV_SEG64(16, 2); break;
+        case 1604: SV_SEG64(16, 4); break;
+        case 1608: SV_SEG64(16, 8); break;
+        case 1616: SV_SEG64(16, 16); break;
+        default: SV_SEG64(16, 32); break;
+      }
+#undef SV_SEG64
+      break;
+    }
+    case svx::Route64::ROWS_TILE: {
 #define SV_ROWS64(E, W)                                                                                      \
   svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {                                             \
     const double *xr = x + r0 * cols;                                                                        \
@@ -1358,63 +1404,64 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     if (vec) k_var_rows_f64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr); \
     else k_var_rows_f64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr);   \
   })
-    if (n <= 512) {
-      const int vw = (svh::aligned16(x) && cols % 2 == 0) ? 2 : 1;
-#define SV_SEG64(E, S)                                                                                  \
-  svh::in_batches(rows, 4 * (64 / S), 256, [&](int64_t r0, int64_t nr) {                                \
-    const dim3 sgrid((unsigned)((nr + 4 * (64 / S) - 1) / (4 * (64 / S))));                             \
-    const double *xr = x + r0 * cols;                                                                   \
-    double *vr = var_out + r0, *mr = mean_out ? mean_out + r0 : nullptr;                                \
-    if (vw == 2) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr); \
-    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr);         \
-  })
-      if (n <= 4) SV_SEG64(4, 1);
-      else if (n <= 8) SV_SEG64(8, 1);
-      else if (n <= 16) SV_SEG64(16, 1);
-      else if (n <= 32) SV_SEG64(16, 2);
-      else if (n <= 64) SV_SEG64(16, 4);
-      else if (n <= 128) SV_SEG64(16, 8);
-      else if (n <= 256) SV_SEG64(16, 16);
-      else SV_SEG64(16, 32);
-#undef SV_SEG64
+      const svx::RowsPlan rp = svx::rows64_plan(n);
+      switch (rp.E * 100 + rp.W) {
+        case 1601: SV_ROWS64(16, 1); break;
+        case 1602: SV_ROWS64(16, 2); break;
+        case 1604: SV_ROWS64(16, 4); break;
+        case 1608: SV_ROWS64(16, 8); break;
+        case 1616: SV_ROWS64(16, 16); break;
+        default: SV_ROWS64(32, 16); break;
+      }
+#undef SV_ROWS64
+      break;
     }
-    else if (n <= 1024) SV_ROWS64(16, 1);
-    else if (n <= 2048) SV_ROWS64(16, 2);
-    else if (n <= 4096) SV_ROWS64(16, 4);
-    else if (n <= 8192) SV_ROWS64(16, 8);
-    else if (n <= V64_ROWS_MAX_N) SV_ROWS64(16, 16);
-    else if (n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS) SV_ROWS64(32, 16);
-    else {
+    case svx::Route64::LONG_ROWS_CHUNKED: {
       const int64_t nch = (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK;
       const SliceWsD ws = slice_ws(workspace, rows * nch);
-      const dim3 lgrid((unsigned)(rows * nch)), lblock(64 * L64_W);
+      const dim3 lgrid((unsigned)(rows * nch)), lblock(64 * L64_W), grid((unsigned)rows);
       if (vec) k_long_rows_d<0, true><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
       else k_long_rows_d<0, false><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
       launch_long_top_d<0>(x, n, cols, nch, ddof, ws, var_out, mean_out, grid, st);
       if (vec) k_long_rows_d<1, true><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
       else k_long_rows_d<1, false><<<lgrid, lblock, 0, st>>>(x, n, cols, nch, ws);
       launch_long_top_d<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, grid, st);
+      break;
     }
-#undef SV_ROWS64
-  } else if (n > V64_COLS_MAX_R) {
-    const SliceWsD ws = slice_ws(workspace, ((n + C64_CHUNK - 1) / C64_CHUNK) * cols);
-    if (svh::aligned16(x) && cols % 2 == 0) launch_cols_gd<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
-    else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
-  } else if (n > 64) {
-    launch_cols_one_d(x, rows, cols, ddof, svh::aligned16(x) && cols % 2 == 0, var_out, mean_out, st);
-  } else if (n < 16 && svh::aligned16(x) && cols % 2 == 0) {
-    const dim3 grid((unsigned)((cols / 2 + 255) / 256)), block(256);
-    if (n <= 2) k_cols_short_d<2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-    else if (n <= 4) k_cols_short_d<4><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-    else if (n <= 8) k_cols_short_d<8><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-    else k_cols_short_d<16><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out);
-  } else {
-    const dim3 grid((unsigned)((cols + 63) / 64));
-#define SV_COLS64(E, W) k_var_cols_f64<E, W><<<grid, dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out)
-    if (n <= 4) SV_COLS64(4, 1);
-    else if (n <= 16) SV_COLS64(16, 1);
-    else SV_COLS64(16, 4);
+    case svx::Route64::COLS_CHUNKED: {
+      const SliceWsD ws = slice_ws(workspace, ((n + C64_CHUNK - 1) / C64_CHUNK) * cols);
+      if (vec) launch_cols_gd<2>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+      else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
+      break;
+    }
+    case svx::Route64::COLS_ONE: launch_cols_one_d(x, rows, cols, ddof, vec, var_out, mean_out, st); break;
+    case svx::Route64::COLS_SHORT: {
+      const int e = svx::cols_short_e(n);
+      svh::in_batches((cols / 2 + 255) / 256, 1, 256, [&](int64_t b0, int64_t nb) {
+        const dim3 grid((unsigned)nb), block(256);
+        switch (e) {
+          case 2: k_cols_short_d<2><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out, b0); break;
+          case 4: k_cols_short_d<4><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out, b0); break;
+          case 8: k_cols_short_d<8><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out, b0); break;
+          default: k_cols_short_d<16><<<grid, block, 0, st>>>(x, rows, cols, ddof, var_out, mean_out, b0); break;
+        }
+      });
+      break;
+    }
+    case svx::Route64::COLS_LANE: {
+      const svx::RowsPlan lp = svx::cols_lane64_plan(n);
+#define SV_COLS64(E, W)                                                                                  \
+  svh::in_batches((cols + 63) / 64, 1, 64 * W, [&](int64_t b0, int64_t nb) {                             \
+    k_var_cols_f64<E, W><<<dim3((unsigned)nb), dim3(64 * W), 0, st>>>(x, rows, cols, ddof, var_out, mean_out, b0); \
+  })
+      switch (lp.E * 100 + lp.W) {
+        case 401: SV_COLS64(4, 1); break;
+        case 1601: SV_COLS64(16, 1); break;
+        default: SV_COLS64(16, 4); break;
+      }
 #undef SV_COLS64
+      break;
+    }
   }
   return check_launch("sv_variance_f64");
 }

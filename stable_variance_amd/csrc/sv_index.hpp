@@ -323,4 +323,89 @@ constexpr Route f32_route(int64_t rows, int64_t cols, bool ax1, bool vec16, cons
   return Route::COLS_LANE;
 }
 
+// ---------------------------------------------------------------- float64 path
+
+constexpr int64_t S64_MAX_N = 1LL << 35;         // float64 tree sum: values per call
+constexpr int S64_W = 4;                         // float64 tree sum: waves per workgroup
+constexpr int S64_EF = 32;                       // floats per lane per chunk (16 doubles)
+constexpr int S64_MAX_BLOCKS = 8192;
+constexpr int S64_MAX_LOG2_G = 16;
+constexpr int64_t V64_MAX_ELEMS = 1LL << 35;     // float64 variance: rows * cols per call (256 GiB)
+constexpr int64_t V64_ROWS_MAX_N = 16384;        // one workgroup per row
+constexpr int64_t V64_ROWS_ONE_MAX_N = 32768;    // ... with at least V64_ROWS_ONE_MIN_ROWS rows
+constexpr int64_t V64_ROWS_ONE_MIN_ROWS = 256;
+constexpr int64_t V64_COLS_MAX_R = 1024;         // whole columns in one workgroup
+constexpr int L64_E = 16;                        // doubles per lane (long slices)
+constexpr int L64_W = 8;                         // waves per workgroup (long slices)
+constexpr int64_t L64_ROW_CHUNK = 64LL * L64_E * L64_W;  // 8192 doubles
+constexpr int L64_TOP_MAX_K = 32;
+constexpr int64_t L64_MAX_CHUNKS = 256LL * L64_TOP_MAX_K;
+constexpr int64_t C64_CHUNK = (int64_t)L64_E * L64_W;   // 128 rows
+constexpr int C64_GROUP = 32;
+constexpr int TOP_BIG_LEVELS_D = 16;
+
+enum class Route64 {
+  LONG_ROWS_CHUNKED,  // axis 1, rows longer than one workgroup holds
+  ROWS_SEG,           // axis 1, up to 512 values, rows sharing waves (seg_plan)
+  ROWS_TILE,          // axis 1, one workgroup per row (rows64_plan)
+  COLS_CHUNKED,       // axis 0, more than 1024 rows (cols_chunk64_plan)
+  COLS_ONE,           // axis 0, 65..1024 rows (cols_one64_plan)
+  COLS_SHORT,         // axis 0, fewer than 16 rows, two columns per lane
+  COLS_LANE,          // axis 0, a lane per column (cols_lane64_plan)
+};
+// vec16: the matrix starts 16-byte aligned and cols is even.
+constexpr Route64 f64_route(int64_t rows, int64_t cols, bool ax1, bool vec16) {
+  const int64_t n = ax1 ? cols : rows;
+  if (ax1) {
+    if (n <= 512) return Route64::ROWS_SEG;
+    if (n <= V64_ROWS_MAX_N || (n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS)) return Route64::ROWS_TILE;
+    return Route64::LONG_ROWS_CHUNKED;
+  }
+  if (n > V64_COLS_MAX_R) return Route64::COLS_CHUNKED;
+  if (n > 64) return Route64::COLS_ONE;
+  if (n < 16 && vec16) return Route64::COLS_SHORT;
+  return Route64::COLS_LANE;
+}
+// Axis-1 rows of 513..32768 doubles: 16 doubles per lane and the waves of the
+// power-of-two tile, 32 per lane and 16 waves above 16384.
+constexpr RowsPlan rows64_plan(int64_t n) {
+  if (n <= 1024) return {16, 1};
+  if (n <= 2048) return {16, 2};
+  if (n <= 4096) return {16, 4};
+  if (n <= 8192) return {16, 8};
+  if (n <= V64_ROWS_MAX_N) return {16, 16};
+  return {32, 16};
+}
+// Axis 0, 65..1024 rows in one launch: V adjacent columns per lane (two above
+// 512 rows, one below or for a single column), G row groups, W waves of 16
+// rows per lane, `blocks` workgroups of V*64/G columns.
+struct ColsOne64Plan {
+  int V, G, W;
+  int64_t blocks;
+};
+constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16) {
+  if (R > 512) return (vec16 || C >= 2) ? ColsOne64Plan{2, 16, 4, (C + 7) / 8} : ColsOne64Plan{1, 16, 4, (C + 3) / 4};
+  int64_t cap = L64_E;
+  while (cap < R) cap *= 2;
+  const int gw = (int)(cap / L64_E);
+  const int g = (gw > 16 || (C + 63) / 64 < 512) ? 4 : 1;
+  return {1, g, gw / g, (C + 64 / g - 1) / (64 / g)};
+}
+// Axis 0, a lane per column (up to 64 rows).
+constexpr RowsPlan cols_lane64_plan(int64_t R) {
+  if (R <= 4) return {4, 1};
+  if (R <= 16) return {16, 1};
+  return {16, 4};
+}
+// Axis 0 in chunks of 128*G rows of a block of V*64/G columns: G = 1 for at
+// least 64 column groups of V, 4 for 9..63, 8 for 5..8, 16 for 3..4, 32 for
+// 2, 64 for one.
+constexpr ColsChunkPlan cols_chunk64_plan(int V, int64_t R, int64_t C) {
+  const int64_t groups = (C + V - 1) / V;
+  const int g = groups >= 64 ? 1 : groups > 8 ? 4 : groups > 4 ? 8 : groups > 2 ? 16 : groups > 1 ? 32 : 64;
+  const int64_t ch = C64_CHUNK * g;
+  const int nc = V * (64 / g);
+  return {g, (R + ch - 1) / ch, (C + nc - 1) / nc};
+}
+
 }  // namespace svx

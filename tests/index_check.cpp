@@ -250,20 +250,21 @@ void cols_tile(const Where &c, int64_t R, int64_t C, int64_t c0, int64_t r0, boo
   const int64_t cc = cols_first(c0, C, V);
   for (int i = 0; i < E; ++i) {
     const int64_t r = full ? r0 + i : clamp_last(r0 + i, R);
-    if (V == 4 && vec16) load(c, r * C + cc, 4, b, lane);
+    if (V > 1 && vec16) load(c, r * C + cc, V, b, lane);  // 16 bytes: four floats or two doubles
     else
       for (int k = 0; k < V; ++k) load(c, r * C + clamp_last(cc + k, C), 1, b, lane);
   }
 }
 
 // k_cols_one<V, W, G, VEC16, E, MODE> over `waves` waves.
+// pair_lines: the float32 kernel's die pairing of blocks narrower than a line.
 void cols_one(const Where &c, int64_t R, int64_t C, int V, int W, int G, bool vec16, int E, int mode, int64_t blocks,
-              int waves) {
+              int waves, bool pair_lines = true) {
   batches(blocks, 1, 64 * waves, [&](int64_t, int64_t cnt) { launch(c, cnt, 64 * waves); });
   const int nc = V * (64 / G);
   if ((C + nc - 1) / nc != blocks) report(c, "column blocks", blocks, nc, -1, -1);
   for (int64_t b : visit(blocks)) {
-    const int64_t cb = line_on_one_die<int>((int)b, (int)((C + nc - 1) / nc), nc);
+    const int64_t cb = pair_lines ? line_on_one_die<int>((int)b, (int)((C + nc - 1) / nc), nc) : b;
     if (cb < 0 || cb >= blocks) report(c, "column block", cb, blocks, b, -1);
     for (int w = 0; w < waves; ++w)
       for (int lane = 0; lane < 64; ++lane) {
@@ -281,8 +282,8 @@ void cols_one(const Where &c, int64_t R, int64_t C, int V, int W, int G, bool ve
 
 // k_cols_y and k_cols_dq (the chunked path; the workspace reads are clamped
 // to the nch chunk nodes the workspace holds).
-void cols_chunked(const Where &c, int64_t R, int64_t C, int V, int W) {
-  const ColsChunkPlan p = cols_chunk_plan(V, W, R, C);
+void cols_chunked(const Where &c, int64_t R, int64_t C, int V, int W, const ColsChunkPlan &p, int64_t ws_chunks,
+                  int group) {
   const int nc = V * (64 / p.G);
   const int64_t nb = p.ncb * p.nch;
   batches(nb, 1, 64 * W, [&](int64_t, int64_t cnt) {
@@ -291,9 +292,9 @@ void cols_chunked(const Where &c, int64_t R, int64_t C, int V, int W) {
   });
   // the top trees: 64/S columns per wave (S lanes per column) for at most
   // CC_GROUP chunks, else a wave per column
-  const int pw = p.nch <= 4 ? 16 : p.nch <= 8 ? 8 : p.nch <= 16 ? 4 : p.nch <= CC_GROUP ? 2 : 1;
+  const int pw = p.nch <= 4 ? 16 : p.nch <= 8 ? 8 : p.nch <= 16 ? 4 : p.nch <= group ? 2 : 1;
   batches((C + 4 * pw - 1) / (4 * pw), 1, 256, [&](int64_t, int64_t cnt) { launch(c, cnt, 256); });
-  if (p.nch > (R + CC_E * CC_MIN_W - 1) / (CC_E * CC_MIN_W)) report(c, "chunks beyond the workspace", p.nch, R, -1, -1);
+  if (p.nch > ws_chunks) report(c, "chunks beyond the workspace", p.nch, ws_chunks, -1, -1);
   for (int64_t b : visit(nb)) {
     const int64_t cb = b / p.nch, j = b % p.nch;
     for (int w = 0; w < W; ++w)
@@ -301,7 +302,7 @@ void cols_chunked(const Where &c, int64_t R, int64_t C, int V, int W) {
         const int q = lane / p.G, g = lane % p.G;
         const int64_t c0 = cb * nc + (int64_t)q * V;
         const int64_t rw = j * ((int64_t)CC_E * p.G * W) + (int64_t)w * (CC_E * p.G), r0 = rw + (int64_t)g * CC_E;
-        cols_tile(c, R, C, c0, r0, r0 + CC_E <= R, V, CC_E, true, b, lane);
+        cols_tile(c, R, C, c0, r0, r0 + CC_E <= R, V, CC_E, V > 1, b, lane);
         const int64_t cc = cols_first(c0, C, V);
         for (int k = 0; k < V; ++k) load(c, cc + k, 1, b, lane);
       }
@@ -309,8 +310,7 @@ void cols_chunked(const Where &c, int64_t R, int64_t C, int V, int W) {
 }
 
 // k_var_cols: a lane per column.
-void cols_lane(const Where &c, int64_t R, int64_t C) {
-  const RowsPlan p = cols_lane_plan(R);
+void cols_lane(const Where &c, int64_t R, int64_t C, const RowsPlan &p) {
   const int64_t nb = (C + 63) / 64;
   batches(nb, 1, 64 * p.W, [&](int64_t, int64_t cnt) { launch(c, cnt, 64 * p.W); });
   for (int64_t b : visit(nb))
@@ -326,16 +326,17 @@ void cols_lane(const Where &c, int64_t R, int64_t C) {
       }
 }
 
-// k_cols_short: four columns per lane, R < 16 rows.
-void cols_short(const Where &c, int64_t R, int64_t C) {
+// k_cols_short(_d): V columns per lane (four floats or two doubles, 16
+// bytes), R < 16 rows.
+void cols_short(const Where &c, int64_t R, int64_t C, int V) {
   const int E = cols_short_e(R);
-  const int64_t nb = (C / 4 + 255) / 256;
+  const int64_t nb = (C / V + 255) / 256;
   batches(nb, 1, 256, [&](int64_t, int64_t cnt) { launch(c, cnt, 256); });
   for (int64_t b : visit(nb))
     for (int t = 0; t < 256; ++t) {
-      const int64_t c0 = (b * 256 + t) * 4;
+      const int64_t c0 = (b * 256 + t) * V;
       if (c0 >= C) continue;
-      for (int i = 0; i < E; ++i) load(c, clamp_last<int64_t>(i, R) * C + c0, 4, b, t);
+      for (int i = 0; i < E; ++i) load(c, clamp_last<int64_t>(i, R) * C + c0, V, b, t);
     }
 }
 
@@ -366,8 +367,13 @@ void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k,
       cols_one(c, rows, cols, 1, 16, 4, false, p.E, p.mode, p.blocks, p.waves);
       break;
     }
-    case Route::COLS_CHUNKED: cols_chunked(c, rows, cols, vec16 ? 4 : 1, k.cols_waves); break;
-    case Route::COLS_SHORT: cols_short(c, rows, cols); break;
+    case Route::COLS_CHUNKED: {
+      const int V = vec16 ? 4 : 1;
+      cols_chunked(c, rows, cols, V, k.cols_waves, cols_chunk_plan(V, k.cols_waves, rows, cols),
+                   (rows + CC_E * CC_MIN_W - 1) / (CC_E * CC_MIN_W), CC_GROUP);
+      break;
+    }
+    case Route::COLS_SHORT: cols_short(c, rows, cols, 4); break;
     case Route::COLS_ONE4: {
       const ColsOnePlan p = cols_one4_plan(rows, cols);
       cols_one(c, rows, cols, 4, p.W, p.G, vec16, CC_E, 0, p.blocks, p.W);
@@ -378,7 +384,7 @@ void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k,
       cols_one(c, rows, cols, 1, p.W, p.G, false, CC_E, 0, p.blocks, p.W);
       break;
     }
-    case Route::COLS_LANE: cols_lane(c, rows, cols); break;
+    case Route::COLS_LANE: cols_lane(c, rows, cols, cols_lane_plan(rows)); break;
   }
 }
 
@@ -397,7 +403,72 @@ void variant_f32(int64_t rows, int64_t cols, int axis, int off) {
     const bool vec = off == 0 && cols % 4 == 0;
     batches(rows, 1, 64 * p.W, [&](int64_t r0, int64_t nr) { rows_launch(c, r0, nr, cols, cols, p.E, p.W, vec, 1); });
   } else {
-    cols_lane(c, rows, cols);
+    cols_lane(c, rows, cols, cols_lane_plan(rows));
+  }
+}
+
+// The float64 variance (indices in doubles; the row tiles load floats, two
+// per double).  off: the matrix's address modulo 16 bytes (0 or 8).
+void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
+  const bool ax1 = axis == 1;
+  const int64_t n = ax1 ? cols : rows;
+  if (rows == 0 || cols == 0) return;
+  const bool vec = off == 0 && cols % 2 == 0;
+  const Route64 route = f64_route(rows, cols, ax1, vec);
+  char name[64];
+  snprintf(name, sizeof name, "f64 axis %d route %d", axis, (int)route);
+  const Where c{name, rows, cols, rows * cols};
+  const Where cf{name, rows, cols, 2 * rows * cols};  // the same array in floats
+  switch (route) {
+    case Route64::ROWS_SEG: rows_seg(c, rows, n, vec ? 2 : 1, 1); break;
+    case Route64::ROWS_TILE: {
+      const RowsPlan p = rows64_plan(n);
+      batches(rows, 1, 64 * p.W, [&](int64_t r0, int64_t nr) {
+        launch(c, nr, 64 * p.W);
+        for (int64_t b : visit(nr)) {
+          const int64_t pr = (r0 + b) * cols;
+          for (int w = 0; w < p.W; ++w) {
+            const int64_t base = (int64_t)w * 64 * p.E;
+            for (int lane = 0; lane < 64; ++lane) {
+              tile_loads(2 * p.E, vec, 1, 2 * (n - base), 2 * rows_avail(nr, b, cols, n, base), lane,
+                         [&](int64_t i, int wd) { load(cf, 2 * (pr + base) + i, wd, b, lane); });
+              load(c, pr, 1, b, lane);
+            }
+          }
+        }
+      });
+      break;
+    }
+    case Route64::LONG_ROWS_CHUNKED: {
+      const int64_t nch = (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK, nb = rows * nch;
+      launch(c, nb, 64 * L64_W);
+      launch(c, rows, 256);
+      for (int64_t b : visit(nb)) {
+        const int64_t r = b / nch, ch = b % nch;
+        for (int w = 0; w < L64_W; ++w) {
+          const int64_t base = ch * L64_ROW_CHUNK + (int64_t)w * 64 * L64_E;
+          for (int lane = 0; lane < 64; ++lane) {
+            tile_loads(2 * L64_E, vec, 1, 2 * (n - base), 2 * rows_avail(nb / nch, r, cols, n, base), lane,
+                       [&](int64_t i, int wd) { load(cf, 2 * (r * cols + base) + i, wd, b, lane); });
+            load(c, r * cols, 1, b, lane);
+          }
+        }
+      }
+      break;
+    }
+    case Route64::COLS_CHUNKED: {
+      const int V = vec ? 2 : 1;
+      cols_chunked(c, rows, cols, V, L64_W, cols_chunk64_plan(V, rows, cols), (rows + C64_CHUNK - 1) / C64_CHUNK,
+                   C64_GROUP);
+      break;
+    }
+    case Route64::COLS_ONE: {
+      const ColsOne64Plan p = cols_one64_plan(rows, cols, vec);
+      cols_one(c, rows, cols, p.V, p.W, p.G, vec, L64_E, 0, p.blocks, p.W, false);
+      break;
+    }
+    case Route64::COLS_SHORT: cols_short(c, rows, cols, 2); break;
+    case Route64::COLS_LANE: cols_lane(c, rows, cols, cols_lane64_plan(rows)); break;
   }
 }
 
@@ -522,6 +593,11 @@ int main() {
       }
       for (int off : {0, 4})
         for (int sr : {0, 1}) variance_c64(R, C, off, sr);
+      for (int axis : {0, 1}) {
+        const int64_t n = axis == 1 ? C : R;
+        if (axis == 1 && n > V64_ROWS_ONE_MAX_N && (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK > L64_MAX_CHUNKS) continue;
+        for (int off : {0, 8}) variance_f64(R, C, axis, off);
+      }
     }
   for (int64_t n : {1LL, 5LL, 2047LL, 2048LL, 2049LL, 100000000LL, 100000003LL})
     for (int e : {16, 32})
@@ -555,6 +631,26 @@ int main() {
     }
   }
   for (int e : {16, 32}) tree_sum(SUM_MAX_N, e, 8192, true, 0, false);
+  for (int64_t C : sizes) {
+    for (int64_t R : {V64_MAX_ELEMS / C, C > 0 ? V64_MAX_ELEMS / C : 0}) {
+      for (int axis : {0, 1}) {
+        const int64_t n = axis == 1 ? C : R, nsl = axis == 1 ? R : C;
+        if (nsl > 0x7fffffffLL || R == 0) continue;
+        if (axis == 1 && n > V64_ROWS_ONE_MAX_N && (n + L64_ROW_CHUNK - 1) / L64_ROW_CHUNK > L64_MAX_CHUNKS) continue;
+        if (axis == 0 && (n + C64_CHUNK - 1) / C64_CHUNK > ((int64_t)64 * 64 << (TOP_BIG_LEVELS_D - 1))) continue;
+        variance_f64(R, C, axis, 0);
+        variance_f64(C, R, axis, 0);
+      }
+    }
+  }
+  // the float64 sum: chunks of 1024 doubles, i.e. the float chunks of 2048
+  // of Chunk<32> over the same bytes (the same plan, in floats)
+  for (int64_t n : {(int64_t)1, (int64_t)1023, (int64_t)1025, (int64_t)50000000, S64_MAX_N}) {
+    const SumPlan pd = plan_sum(n, S64_EF / 2, S64_MAX_BLOCKS, S64_W, S64_MAX_BLOCKS, S64_MAX_LOG2_G);
+    const SumPlan pf = plan_sum(2 * n, S64_EF, S64_MAX_BLOCKS, SUM_W, SUM_MAX_BLOCKS, SUM_MAX_LOG2_GROUP);
+    if (pd.blocks != pf.blocks || pd.log2_g != pf.log2_g) printf("FAIL f64 sum plan %lld\n", (long long)n), ++g_fail;
+    for (bool vec : {true, false}) tree_sum(2 * n, S64_EF, S64_MAX_BLOCKS, vec, 0, false);
+  }
 
   printf("%lld loads and %lld launches checked, %lld failures\n", (long long)g_checks, (long long)g_launches,
          (long long)g_fail);

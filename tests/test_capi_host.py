@@ -172,7 +172,9 @@ def test_f64_sizes_and_argument_errors(L):
     assert ws(4096, 4096, 0) == 3 * r256(32 * 4096 * 16) + r256(4096 * 8)
     assert ws(1, 8192 * 8192, 1) == 3 * r256(8192 * 16) + r256(8)
     assert ws(1, 8192 * 8192 + 1, 1) == ctypes.c_size_t(-1).value
-    assert ws((1 << 20) + 1, 1 << 19, 1) == ctypes.c_size_t(-1).value  # above 2^39 values
+    assert ws((1 << 20) + 1, 1 << 19, 1) == ctypes.c_size_t(-1).value
+    assert ws((1 << 18) + 1, 1 << 17, 0) == ctypes.c_size_t(-1).value  # above 2^35 values
+    assert ws(1 << 18, 1 << 17, 0) != ctypes.c_size_t(-1).value
     assert ws(2, 3, 4) == ctypes.c_size_t(-1).value
     # long slices need it: missing, short and misaligned workspaces are refused
     assert L.sv_variance_f64(BAD, 2, 20000, 1, 0, out, None, None, 0, None) == SV_ERR_WORKSPACE
