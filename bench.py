@@ -67,7 +67,8 @@ def source_digest() -> str:
     h = hashlib.sha256()
     for rel in ("stable_variance_amd/csrc/sv_lib.hip", "stable_variance_amd/csrc/sv_adn.hip",
                 "stable_variance_amd/csrc/sv_f64.hip", "stable_variance_amd/csrc/sv_device.hpp",
-                "stable_variance_amd/csrc/sv_index.hpp"):
+                "stable_variance_amd/csrc/sv_index.hpp", "stable_variance_amd/csrc/sv_adn_kernel.hpp",
+                "stable_variance_amd/csrc/sv_adn_folds_9_14.hip", "stable_variance_amd/csrc/sv_adn_folds_15_21.hip"):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -299,8 +299,10 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
  *     beyond the float range gives +-Inf.
  *
  * x: n device floats (any alignment; 16-byte alignment takes vector loads).
- * fold: 2 .. SV_ADN_MAX_FOLD (the page allows up to 21: 9..21 return
- *   SV_ERR_UNSUPPORTED here; outside 2..21 SV_ERR_INVALID_ARGUMENT).
+ * fold: 2 .. SV_ADN_MAX_FOLD = 21, every fold count the page allows for
+ *   float (outside 2..21 SV_ERR_INVALID_ARGUMENT).  From 21 folds, and from
+ *   any index in the two coarsest bins, the deposits take the kernel's
+ *   general path (slower, same bits).
  * n: 0 .. SV_ADN_MAX_COUNT (the page's capacity for float; above it
  *   SV_ERR_UNSUPPORTED before anything else is touched).
  * out: one device float.
@@ -310,7 +312,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
  *   call leaves zero; calls sharing a workspace must be ordered on one
  *   stream.  Errors and asynchrony as for sv_tree_sum_f32.
  */
-#define SV_ADN_MAX_FOLD 8
+#define SV_ADN_MAX_FOLD 21
 #define SV_ADN_MAX_COUNT 4294966784LL
 #define SV_ADN_SUM_COUNTER_BYTES 33024
 size_t sv_adn_sum_f32_workspace_size(int64_t n);

@@ -7,9 +7,10 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "sv_lib.hip")
-SRCS = [SRC, os.path.join(HERE, "csrc", "sv_adn.hip"), os.path.join(HERE, "csrc", "sv_f64.hip")]
+SRCS = [SRC, os.path.join(HERE, "csrc", "sv_adn.hip"), os.path.join(HERE, "csrc", "sv_adn_folds_9_14.hip"),
+        os.path.join(HERE, "csrc", "sv_adn_folds_15_21.hip"), os.path.join(HERE, "csrc", "sv_f64.hip")]
 DEPS = SRCS + [os.path.join(HERE, "csrc", "sv_device.hpp"), os.path.join(HERE, "csrc", "sv_host.hpp"),
-               os.path.join(HERE, "csrc", "sv_index.hpp"),
+               os.path.join(HERE, "csrc", "sv_index.hpp"), os.path.join(HERE, "csrc", "sv_adn_kernel.hpp"),
                os.path.join(ROOT, "include", "stable_variance.h")]
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libstable_variance.so")

@@ -120,9 +120,9 @@ def test_variance_argument_errors(L):
 
 
 def test_adn_sizes_and_argument_errors(L):
-    # counters (33024 bytes), then an 80-byte record per workgroup (up to
-    # 8192) and per group of 64 workgroups
-    want = 33024 + 80 * (8192 + 128)
+    # counters (33024 bytes), then a 176-byte record (room for 21 folds) per
+    # workgroup (up to 8192) and per group of 64 workgroups
+    want = 33024 + 176 * (8192 + 128)
     assert L.sv_adn_sum_f32_workspace_size(0) == 0
     for n in (1, 4097, 10 ** 8, 4_294_966_784):
         assert L.sv_adn_sum_f32_workspace_size(n) == want
@@ -132,8 +132,6 @@ def test_adn_sizes_and_argument_errors(L):
     assert L.sv_adn_sum_f32(BAD, -1, 3, BAD, ws, want, None) == SV_ERR_INVALID_ARGUMENT
     for fold in (0, 1, 22):
         assert L.sv_adn_sum_f32(BAD, 10, fold, BAD, ws, want, None) == SV_ERR_INVALID_ARGUMENT
-    for fold in (9, 21):
-        assert L.sv_adn_sum_f32(BAD, 10, fold, BAD, ws, want, None) == SV_ERR_UNSUPPORTED
     assert L.sv_adn_sum_f32(BAD, 4_294_966_785, 3, BAD, ws, want, None) == SV_ERR_UNSUPPORTED
     assert b"capacity" in L.sv_last_error_message()
     assert L.sv_adn_sum_f32(BAD, 10, 3, None, ws, want, None) == SV_ERR_INVALID_ARGUMENT
@@ -232,7 +230,7 @@ def test_no_device_is_reported(L):
     ws = ctypes.c_void_p(0x100000)
     assert L.sv_tree_sum_f32(BAD, 10, BAD, ws, 1 << 20, None) == SV_ERR_NO_DEVICE
     assert L.sv_variance_f32(BAD, 4, 4, 1, 0, BAD, None, None, 0, None) == SV_ERR_NO_DEVICE
-    assert L.sv_adn_sum_f32(BAD, 10, 3, BAD, ws, 1 << 20, None) == SV_ERR_NO_DEVICE
+    assert L.sv_adn_sum_f32(BAD, 10, 3, BAD, ws, 1 << 21, None) == SV_ERR_NO_DEVICE
 
 
 def test_python_binding_rejects_bad_tensors():

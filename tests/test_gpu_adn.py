@@ -65,8 +65,10 @@ def gpu_adn(torch_dev, x, fold=3, offset=0):
     return np.float32(r.item())
 
 
-@pytest.mark.parametrize("fold", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("fold", list(range(2, 22)))
 def test_mixed_sets_every_fold(torch_dev, fold):
+    # every fold count the page allows for float (2..21); from 21 folds the
+    # index always reaches the scaled coarsest bins (the general path)
     for seed in range(2):
         for name, x in W.sum_mixed_sets(seed, scale=20):
             want = adn.adn_sum(x, fold)
@@ -99,6 +101,20 @@ def test_quick_start_and_empty(torch_dev):
     assert gpu_adn(torch_dev, x, 5) == 10000.0
     assert bits(gpu_adn(torch_dev, np.zeros(0, np.float32))) == 0
     assert bits(gpu_adn(torch_dev, np.full(5000, -0.0, np.float32))) == 0
+
+
+@pytest.mark.parametrize("fold", [9, 16, 21])
+def test_high_folds_sizes_alignment_and_specials(torch_dev, fold):
+    rng = np.random.default_rng(14 + fold)
+    for n in (1, 2049, 65537, 300_003):
+        x = (rng.standard_normal(n) * np.exp2(rng.integers(-60, 60, n))).astype(np.float32)
+        want = adn.adn_sum(x, fold)
+        assert bits(gpu_adn(torch_dev, x, fold)) == bits(want), (fold, n)
+        assert bits(gpu_adn(torch_dev, x, fold, offset=1)) == bits(want), (fold, n, "unaligned")
+    big = np.array([3e38, -3e38, 1e30, 1.0, -2.5e-40], np.float32)
+    assert bits(gpu_adn(torch_dev, big, fold)) == bits(adn.adn_sum(big, fold))
+    assert bits(gpu_adn(torch_dev, np.array([1.0, np.inf], np.float32), fold)) == bits(np.float32(np.inf))
+    assert bits(gpu_adn(torch_dev, np.array([np.nan, 1.0], np.float32), fold)) == 0x7FC00000
 
 
 def test_specials(torch_dev):

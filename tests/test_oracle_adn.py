@@ -28,7 +28,7 @@ def datasets(seed):
     return W.sum_mixed_sets(seed)
 
 
-@pytest.mark.parametrize("fold", [2, 3, 4, 6])
+@pytest.mark.parametrize("fold", [2, 3, 4, 6, 13, 21])
 def test_closed_form_equals_the_float32_steps(fold):
     # The float32 deposit algorithm (sticky bit, renormalisation, merges) and
     # the closed form of its result must agree bit for bit, in any order and
