@@ -128,6 +128,24 @@ def test_tree_pairing_hand_worked():
     assert oracle.tree_sum(z) == 2.0 ** 25 + 2.0
 
 
+def test_compensated_tree_pairing_hand_worked():
+    # The compensated tree's result depends on its pairing too.  Worked by
+    # hand, x = [7*2^23, 3*2^-25, 2.5, -0.5] (ulp(7*2^23) = 4):
+    # adjacent pairs (the reading): fl(7*2^23 + 3*2^-25) = 7*2^23 with
+    #   e = 3*2^-25; fl(2.5 - 0.5) = 2, e = 0.  Root: fl(7*2^23 + 2) is a tie,
+    #   to even: 7*2^23, e = 2; carry fl(fl(3*2^-25 + 0) + 2) = 2 (3*2^-25 is
+    #   under half an ulp of 2); result fl(7*2^23 + 2) = 7*2^23 = 58720256.
+    # (k, k + P/2) pairs: fl(7*2^23 + 2.5) = 7*2^23 + 4, e = -1.5;
+    #   fl(3*2^-25 - 0.5) exact, e = 0; root fl(7*2^23 + 4 - 0.5 + 3*2^-25) =
+    #   7*2^23 + 4, e = -0.5 + 3*2^-25; carry fl(-1.5 + e) = -2 + 2^-23
+    #   (the float nearest -2 + 3*2^-25); result fl(7*2^23 + 2 + 2^-23) =
+    #   7*2^23 + 4 = 58720260 (above the tie).  The pairings differ in the
+    #   last bit.
+    x = np.array([7 * 2.0 ** 23, 3 * 2.0 ** -25, 2.5, -0.5], np.float32)
+    assert oracle.tree_sum(x) == np.float32(58720256.0)
+    assert oracle.tree_sum(x[[0, 2, 1, 3]]) == np.float32(58720260.0)  # the other pairing, by reordering
+
+
 @pytest.mark.parametrize("n", [2, 3, 5, 7, 8, 13, 64, 100, 1000, 4097])
 def test_tree_exact_on_integer_data(n):
     # Big multiples of 2^24 that cancel in pairs, mixed with small integers.
