@@ -393,6 +393,11 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "adn_e"         values per lane in an ADN-sum chunk: 16 (default) or 32
  *                    (32 only with three folds; other counts use 16)
  *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)
+ *   "launch_items"   work-items per launch before a grid is cut into
+ *                    batches (each batch one launch with a first-workgroup
+ *                    offset): 1024 .. 2^32 - 1 (default 2^32 - 1, HIP's
+ *                    limit; lower values run the batched launches on small
+ *                    inputs, for tests)
  *   "reset"          any value: restore every default
  * Returns SV_ERR_INVALID_ARGUMENT for an unknown key or value.  The settings
  * belong to the calling host thread: they steer that thread's later calls

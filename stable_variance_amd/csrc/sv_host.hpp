@@ -26,13 +26,18 @@ __attribute__((visibility("hidden"))) sv_status adn_set_tuning(const char *key, 
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// A launch holds at most 2^32 - 1 work-items.  in_batches(total, per_block,
-// threads, fn) calls fn(first, count) over [0, total) in runs of whole blocks
-// (per_block items of `threads` work-items each), every run within the limit,
-// so that a launcher can advance its pointers by `first` items.
+// The work-items one launch may hold: 2^32 - 1 (HIP's limit), or fewer when
+// sv_set_tuning("launch_items") lowers it (at least 1024) so that tests run
+// the batched launches on small inputs.  Per host thread.
+__attribute__((visibility("hidden"))) int64_t launch_items();
+
+// in_batches(total, per_block, threads, fn) calls fn(first, count) over
+// [0, total) in runs of whole blocks (per_block items of `threads`
+// work-items each), every run within launch_items(), so that a launcher can
+// advance its pointers (or its first workgroup) by `first` items.
 template <class Fn>
 inline void in_batches(int64_t total, int64_t per_block, int64_t threads, Fn &&fn) {
-  const int64_t batch = ((int64_t)0xffffffffu / threads) * per_block;
+  const int64_t batch = (launch_items() / threads) * per_block;
   for (int64_t s0 = 0; s0 < total; s0 += batch) fn(s0, total - s0 < batch ? total - s0 : batch);
 }
 inline bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }

@@ -107,12 +107,6 @@ constexpr I line_on_one_die(I b, I nb, int nc) {
 // Work-items of one launch: at most 2^32 - 1.
 constexpr int64_t MAX_LAUNCH_ITEMS = 0xffffffffLL;
 
-// Rows per launch of a launcher that gives each workgroup per_block rows and
-// `threads` work-items (the batch of in_batches).
-constexpr int64_t batch_rows(int64_t per_block, int64_t threads) {
-  return (MAX_LAUNCH_ITEMS / threads) * per_block;
-}
-
 // The tree sum: chunks of 64*e values, SUM_W-wave workgroups, each wave
 // streaming 2^log2_g consecutive chunks; log2_g is the smallest value that
 // keeps the workgroup count at or below target_blocks (clamped to

@@ -1546,8 +1546,15 @@ struct Tuning {
   int var_full_rows = 1;      // rows that fill their tile exactly take the kernel without masks (0: the general one)
   int var_cols_once = 1;      // axis 0, 1025..4096 rows: one workgroup per 16 columns, one read, when the
                              // grid fills the chip (0: row chunks; 2: one read whatever the fill)
+  int64_t launch_items = svx::MAX_LAUNCH_ITEMS;  // work-items per launch before a grid is cut into batches
 };
 thread_local Tuning g_tune;
+
+}  // namespace
+
+int64_t svh::launch_items() { return g_tune.launch_items; }
+
+namespace {
 
 // The per-call constants of steps 2 and 4 (see StepConsts).
 StepConsts step_consts(int64_t n, int64_t ddof) {
@@ -2759,6 +2766,12 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     if (value < 1 || value > SUM_MAX_BLOCKS)
       return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: sum_blocks must be in [1, %d]", SUM_MAX_BLOCKS);
     g_tune.sum_blocks = value;
+    return ok();
+  }
+  if (strcmp(key, "launch_items") == 0) {
+    if (value < 1024 || value > svx::MAX_LAUNCH_ITEMS)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: launch_items must be in [1024, 2^32 - 1]");
+    g_tune.launch_items = value;
     return ok();
   }
   bool handled = false;

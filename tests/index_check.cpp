@@ -144,10 +144,12 @@ void rows_full_launch(const Where &c, int64_t r0, int64_t nr, int64_t ld, int E,
   }
 }
 
-// Rows in batches of at most 2^32 - 1 work-items (svh::in_batches).
+// Rows in batches of at most g_items work-items (svh::in_batches; 2^32 - 1
+// by default, lowered by the launch_items knob).
+int64_t g_items = MAX_LAUNCH_ITEMS;
 template <class F>
 void batches(int64_t total, int64_t per_block, int64_t threads, F &&f) {
-  const int64_t batch = batch_rows(per_block, threads);
+  const int64_t batch = (g_items / threads) * per_block;
   for (int64_t s0 = 0; s0 < total; s0 += batch) f(s0, std::min(batch, total - s0));
 }
 
@@ -605,6 +607,19 @@ int main() {
         for (bool vec : {true, false})
           for (int lp : {0, 1})
             for (bool xcd : {false, true}) tree_sum(n, e, target, vec, lp, xcd);
+
+  // the batched launches at the smallest launch_items knob (1024 work-items)
+  g_items = 1024;
+  for (int64_t R : {(int64_t)3, (int64_t)70, (int64_t)700, (int64_t)1500, (int64_t)2049, (int64_t)5000})
+    for (int64_t C : {(int64_t)3, (int64_t)33, (int64_t)300, (int64_t)1030, (int64_t)17000})
+      for (int axis : {0, 1}) {
+        for (int off : {0, 8, 4})
+          for (bool fills : {true, false}) variance_f32(R, C, axis, off, knobs[0], fills);
+        if (axis == 1 ? C <= ROWS_MAX_N : R <= COLS_MAX_R) variant_f32(R, C, axis, 0);
+        for (int off : {0, 8}) variance_f64(R, C, axis, off);
+        for (int off : {0, 4}) variance_c64(R, C, off, 1);
+      }
+  g_items = MAX_LAUNCH_ITEMS;
 
   // launch limits at the largest accepted shapes (no loads walked beyond the
   // sampled workgroups)

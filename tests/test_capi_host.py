@@ -215,7 +215,8 @@ def test_tuning_knob_validation(L):
     for key, good, bad in ((b"sum_load_path", 1, 2), (b"sum_nt", 0, -1), (b"var_load_path", 2, 5),
                            (b"var_nt", 1, 2), (b"var_full_rows", 0, 2), (b"var_cols_once", 2, 3), (b"var_cols_once", 0, -1), (b"sum_e", 16, 64), (b"sum_depth", 4, 3), (b"sum_blocks", 8192, 0),
                            (b"sum_xcd", 1, 2), (b"var_xcd", 1, -1), (b"var_split", 0, 3), (b"var_split", 8, 16),
-                           (b"var_lds_pad", 65536, 65537), (b"var_short_rows", 0, 2), (b"var_cols_one", 3, 4), (b"var_cols_one", 0, -1), (b"var_long_rows", 0, 2), (b"var_cols_short", 0, 3)):
+                           (b"var_lds_pad", 65536, 65537), (b"var_short_rows", 0, 2), (b"var_cols_one", 3, 4), (b"var_cols_one", 0, -1), (b"var_long_rows", 0, 2), (b"var_cols_short", 0, 3),
+                           (b"launch_items", 1024, 1023), (b"launch_items", 0xffffffff, 1 << 32)):
         assert L.sv_set_tuning(key, good) == 0, key
         assert L.sv_set_tuning(key, bad) == SV_ERR_INVALID_ARGUMENT, key
     assert L.sv_set_tuning(b"sum_blocks", 8193) == SV_ERR_INVALID_ARGUMENT

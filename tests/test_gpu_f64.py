@@ -224,3 +224,21 @@ def test_var64_long_rows_one_workgroup(torch_dev, shape):
     check_var64(torch_dev, a, 1, 1)
     b = W.adversarial_values(shape[0] * shape[1], shape[1]).astype(np.float64).reshape(shape) * 1e200
     check_var64(torch_dev, b, 1)
+
+
+@pytest.mark.parametrize("items", [1024, 4096])
+def test_var64_batched_launches(torch_dev, items):
+    # every float64 shape class with each grid cut into launches of at most
+    # `items` work-items (first-workgroup offsets), bit for bit
+    import stable_variance_amd as sv
+
+    rng = np.random.default_rng(items + 64)
+    sv.set_tuning("launch_items", items)
+    try:
+        for shape, axis in (((3000, 5), 1), ((800, 700), 1), ((300, 20000), 1), ((260, 17000), 1),
+                            ((6, 3000), 0), ((40, 900), 0), ((300, 900), 0), ((700, 901), 0), ((1100, 300), 0),
+                            ((3000, 7), 0)):
+            a = rng.normal(-4e3, 9, shape)
+            check_var64(torch_dev, a, axis, 1)
+    finally:
+        sv.set_tuning("reset", 0)

@@ -762,3 +762,55 @@ def test_sum_dw_cancelling_sets_and_full_workload(torch_dev):
     want = oracle.tree_sum_dw(x)
     assert same_bits(gpu_sum_dw(torch_dev, x), want)
     assert want == oracle.round_f32(oracle.exact_sum(x))   # 3735.104, correctly rounded
+
+
+# ---------------------------------------------------------------- batched launches
+
+# Every shape class with each grid cut into launches of at most 1024 or 4096
+# work-items (sv_set_tuning "launch_items"): the batched launches, with their
+# first-workgroup offsets, that only the largest inputs take at the default
+# limit of 2^32 - 1, here on small inputs and bit for bit against the oracle.
+BATCH_F32 = [((2000, 3), 1), ((3000, 300), 1), ((300, 3000), 1), ((260, 17000), 1), ((3, 20000), 1),
+             ((3, 2000), 0), ((40, 700), 0), ((700, 70), 0), ((700, 1030), 0), ((1500, 300), 0), ((3000, 40), 0),
+             ((5000, 33), 0), ((2049, 300), 0)]
+
+
+@pytest.mark.parametrize("items", [1024, 4096])
+@pytest.mark.parametrize("shape,axis", BATCH_F32)
+def test_variance_batched_launches(torch_dev, shape, axis, items):
+    import stable_variance_amd as sv
+
+    rng = np.random.default_rng(shape[0] * 7 + shape[1] + items)
+    a = rng.normal(-3e3, 11, shape).astype(np.float32)
+    once = [1, 2] if axis == 0 and 1024 < shape[0] <= 4096 else [1]
+    for o in once:
+        sv.set_tuning("reset", 0)
+        sv.set_tuning("launch_items", items)
+        sv.set_tuning("var_cols_once", o)
+        try:
+            check_var(torch_dev, a, axis, 1)
+        finally:
+            sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("items", [1024, 4096])
+def test_complex_and_variants_batched_launches(torch_dev, items):
+    import stable_variance_amd as sv
+
+    rng = np.random.default_rng(items)
+    sv.set_tuning("launch_items", items)
+    try:
+        for shape in ((3000, 5), (900, 700), (300, 2000)):
+            z = (rng.normal(size=shape) + 1j * rng.normal(size=shape)).astype(np.complex64) + (50 + 20j)
+            for axis in (0, 1):
+                check_var_c64(torch_dev, z, axis)
+        torch, dev = torch_dev
+        a = rng.normal(7e2, 3, (1100, 900)).astype(np.float32)
+        for code in (0, 2, 4, 6):  # the variant codes are the oracle's method numbers
+            for axis in (0, 1):
+                b = a if axis == 1 else np.ascontiguousarray(a[:1000])
+                v = sv.var_variant(torch.from_numpy(b).to(dev), code, dim=axis)
+                torch.cuda.synchronize()
+                assert same_bits(v.cpu().numpy(), oracle.variance(b, axis=axis, method=code)[0]), (code, axis, items)
+    finally:
+        sv.set_tuning("reset", 0)
