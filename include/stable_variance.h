@@ -201,9 +201,12 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
  *   workspace  sv_variance_c64_workspace_size(rows, cols, axis) bytes,
  *              256-byte aligned, no initialisation; NULL allowed when that
  *              size is 0.  Axis 1 rows of up to 32768 values are read once
- *              and need none; longer rows stage the split parts (8 bytes per
- *              input value); axis 0 reads the interleaved array as float32
- *              [rows, 2 * cols] columns
+ *              and need none; longer rows (up to 8192 chunks of 8192
+ *              values) are read twice in chunks, the parts split in
+ *              registers (8 bytes per row and 24 per chunk per part); rows
+ *              beyond that stage the split parts (8 bytes per input value);
+ *              axis 0 reads the interleaved array as float32 [rows, 2 * cols]
+ *              columns
  * Errors and asynchrony as for sv_variance_f32.
  */
 size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis);
@@ -390,6 +393,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    dispatch order, consecutive regions spread over the dies
  *                    (default, faster on MI355X)
  *   "var_xcd"        row variance: as sum_xcd, over rows (default 0)
+ *   "var_cols_pairs" axis 0, two columns of more than 4096 rows: 1 (default)
+ *                    = one row of pairs in chunks (wide loads), 0 = the
+ *                    column chunks
  *   "adn_e"         values per lane in an ADN-sum chunk: 16 (default) or 32
  *                    (32 only with three folds; other counts use 16)
  *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)

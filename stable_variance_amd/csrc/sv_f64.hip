@@ -1369,6 +1369,13 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     k_fill_nan_d<<<dim3((unsigned)((nslices + 255) / 256)), dim3(256), 0, st>>>(var_out, mean_out, nslices);
     return check_launch("sv_variance_f64");
   }
+  if (!ax1 && cols == 1 && rows <= L64_MAX_CHUNKS * L64_ROW_CHUNK) {
+    // A single column is one contiguous slice, as is the single row
+    // [1, rows]: the same values in the same order, hence the same tree and
+    // bits; the row form reads it with wide loads and needs less workspace
+    // than the column form, which the caller sized.
+    return sv_variance_f64(x, 1, rows, 1, ddof, var_out, mean_out, workspace, workspace_bytes, stream);
+  }
   const bool vec = svh::aligned16(x) && (cols % 2 == 0);
   switch (svx::f64_route(rows, cols, ax1, vec)) {
     case svx::Route64::ROWS_SEG: {

@@ -283,6 +283,7 @@ enum class Route {
   LONG_ROWS_CHUNKED,  // axis 1, rows longer than one tile: chunk launches
   ROWS_SEG,           // axis 1, short rows sharing waves
   ROWS_TILE,          // axis 1, one workgroup per row (rows_plan)
+  COLS_PAIRS,         // axis 0, two columns of more than 4096 rows: one row of pairs in chunks
   COLS_ONE_READ,      // axis 0, 1025..4096 rows read once (cols_long_plan)
   COLS_CHUNKED,       // axis 0, row chunks (cols_chunk_plan)
   COLS_SHORT,         // axis 0, fewer than 16 rows, four columns per lane
@@ -291,7 +292,8 @@ enum class Route {
   COLS_LANE,          // axis 0, a lane per column (cols_lane_plan)
 };
 struct RouteKnobs {
-  int var_long_rows, var_cols_once, var_cols_single_max, var_short_rows, var_cols_short, var_cols_one;
+  int var_long_rows, var_cols_once, var_cols_single_max, var_short_rows, var_cols_short, var_cols_one,
+      var_cols_pairs;
 };
 // Columns that are candidates for the one-read launch.
 constexpr bool cols_one_read_candidate(bool ax1, int64_t n, const RouteKnobs &k) {
@@ -304,6 +306,9 @@ constexpr Route f32_route(int64_t rows, int64_t cols, bool ax1, bool vec16, cons
   const int64_t n = ax1 ? cols : rows;
   if (ax1 && n > ROWS_MAX_N && !(k.var_long_rows && n <= ROWS_ONE_MAX_N && rows >= ROWS_ONE_MIN_ROWS))
     return Route::LONG_ROWS_CHUNKED;
+  if (!ax1 && cols == 2 && n > COLS_ONE_LONG_MAX_R && k.var_cols_pairs &&
+      (n + LS_ROW_CHUNK / 2 - 1) / (LS_ROW_CHUNK / 2) <= LS_MAX_CHUNKS)
+    return Route::COLS_PAIRS;
   if (cols_one_read_candidate(ax1, n, k) && (k.var_cols_once == 2 || one_read_fills)) return Route::COLS_ONE_READ;
   if (!ax1 && n > k.var_cols_single_max) return Route::COLS_CHUNKED;
   if (ax1) return n <= SEG_MAX_N && k.var_short_rows ? Route::ROWS_SEG : Route::ROWS_TILE;

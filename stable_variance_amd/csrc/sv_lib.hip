@@ -775,7 +775,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
     }
   }
 
-  // step 2: m = Tree(y) / n
+  // step 2: m = (the tree of y) / n: the plain tree (the compensated one in V_COMP_Y)
   Node ny = sv::zero_node();
   if (!empty) {
     ny = sv::lane_tree<F::yleaf, 0, E, E>(v);
@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(64 * W) void k_var_cols(const float *__restrict__ x
 // chunk.  Three or four launches, ordered by the stream (each reads what the
 // previous ones wrote; the workspace is scratch):
 //   k_cols_y    the y-tree node of every (chunk, column)
-//   m           per column m = Tree(y)/n, the tree over its chunk nodes: for
+//   m           per column m = Plain(y)/n, the tree over its chunk nodes: for
 //               at most 32 chunks per column each k_cols_dq workgroup forms
 //               the m of its own columns (no launch); else a wave per column
 //               (k_cols_top up to 4096 chunks, k_cols_top_big beyond)
@@ -1415,7 +1415,7 @@ __global__ __launch_bounds__(64 * W) void k_cols_one(const float *__restrict__ x
 
 // Rows longer than one workgroup's registers hold (axis 1, n > 16384) are
 // cut into aligned chunks (a chunk is a node of the row's tree) and reduced
-// in four launches: y-tree node per chunk -> per row m = Tree(y)/n -> d- and
+// in four launches: y-tree node per chunk -> per row m = Plain(y)/n -> d- and
 // d^2-tree nodes per chunk -> per row top trees and step 4.  The input is
 // read twice.  Workspace per row: nchunks y nodes, 2*nchunks d/d^2 nodes and
 // m.
@@ -1432,50 +1432,59 @@ struct LongWs {
 };
 
 // Axis 1, pass 0 or 1 over chunk c of row r (block index = r * nch + c).
-template <int PASS, bool VEC>
+// P = 2: each row holds n pairs (2n floats) of two interleaved slices (the
+// real and imaginary parts of complex values, or the two columns of a
+// [n, 2] matrix), slices 2r and 2r + 1 of the launch: a lane holds E/2
+// consecutive pairs (E floats, one per-lane load of 4 values at a time) and
+// splits them in registers; the chunk covers LS_ROW_CHUNK / 2 pairs, and
+// both slices' nodes go to the workspace.
+template <int PASS, bool VEC, int P = 1>
 __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t nch,
                                                    LongWs ws) {
-  constexpr int E = 64, W = 4;
-  __shared__ Node slots[2][W];
+  constexpr int E = 64, W = 4, EP = E / P;  // EP values of each slice per lane
+  constexpr int64_t CHUNK = LS_ROW_CHUNK / P;
+  __shared__ Node slots[2 * P][W];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x / nch;
   const int64_t c = (int64_t)blockIdx.x % nch;
   const float *__restrict__ row = x + r * ld;
-  const int64_t base = c * LS_ROW_CHUNK + (int64_t)w * 64 * E;
-  float v[E];
+  const int64_t base = c * CHUNK + (int64_t)w * 64 * EP;  // first value of this wave, of each slice
+  float f[E];
   float dummy_lds[1];
-  const int64_t avail = svx::rows_avail(gridDim.x / nch, r, ld, n, base);  // to the launch's last row
-  sv::load_tile<E, VEC, 1, false>(row + base, n - base, dummy_lds, v, lane, avail);
-  const float x0 = row[0];
-  const bool full = base + 64 * E <= n;
-  const int64_t vl = n - base - (int64_t)lane * E;
-  const int valid = vl < 0 ? 0 : (vl > E ? E : (int)vl);
-  if (full) {
+  const int64_t avail = P * svx::rows_avail(gridDim.x / nch, r, ld / P, n, base);  // floats to the launch's last row
+  sv::load_tile<E, VEC, 1, false>(row + P * base, P * (n - base), dummy_lds, f, lane, avail);
+  const bool full = base + 64 * EP <= n;
+  const int64_t vl = n - base - (int64_t)lane * EP;
+  const int valid = vl < 0 ? 0 : (vl > EP ? EP : (int)vl);
+  float v[P][EP];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
-  } else {
+  for (int j = 0; j < P; ++j) {
+    const float x0 = row[j];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
+    for (int i = 0; i < EP; ++i) v[j][i] = (full || i < valid) ? f[P * i + j] - x0 : 0.0f;
   }
-  const int64_t out = r * nch + c;
-  if constexpr (PASS == 0) {
-    Node ny = sv::lane_tree<sv::Y_LEAF, 0, E, E>(v);
-    ny = sv::wave_tree<sv::Y_KIND>(ny);
-    ny = block_tree<W, sv::Y_KIND>(ny, slots[0], w, lane);
-    if (threadIdx.x == 0) ws.ny[out] = ny;
-  } else {
-    const float m = ws.m[r];
-    Node nd, nq;
-    if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
-    else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
-    nq = sv::wave_tree<sv::NODE_NN>(nq);
-    nd = block_tree<W, sv::NODE_TWOSUM>(nd, slots[0], w, lane);
-    nq = block_tree<W, sv::NODE_NN>(nq, slots[1], w, lane);
-    if (threadIdx.x == 0) {
-      ws.nd[out] = nd;
-      ws.nq[out] = nq;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int64_t out = (P * r + j) * nch + c;
+    if constexpr (PASS == 0) {
+      Node ny = sv::lane_tree<sv::Y_LEAF, 0, EP, EP>(v[j]);
+      ny = sv::wave_tree<sv::Y_KIND>(ny);
+      ny = block_tree<W, sv::Y_KIND>(ny, slots[2 * j], w, lane);
+      if (threadIdx.x == 0) ws.ny[out] = ny;
+    } else {
+      const float m = ws.m[P * r + j];
+      Node nd, nq;
+      if (full) sv::lane_tree_dq<false, 0, EP, EP>(v[j], m, EP, nd, nq);
+      else sv::lane_tree_dq<true, 0, EP, EP>(v[j], m, valid, nd, nq);
+      nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
+      nq = sv::wave_tree<sv::NODE_NN>(nq);
+      nd = block_tree<W, sv::NODE_TWOSUM>(nd, slots[2 * j], w, lane);
+      nq = block_tree<W, sv::NODE_NN>(nq, slots[2 * j + 1], w, lane);
+      if (threadIdx.x == 0) {
+        ws.nd[out] = nd;
+        ws.nq[out] = nq;
+      }
     }
   }
 }
@@ -1498,10 +1507,10 @@ __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t
   return block_tree<4, KIND>(r, slots, w, lane);
 }
 
-// PASS 0: m = Tree(y) / n.  PASS 1: the top trees of d and d^2 and step 4.
-// One 256-thread workgroup per slice; the slice's first value is at
-// x[s * sstride].
-template <int PASS, int K>
+// PASS 0: m = Plain(y) / n.  PASS 1: the top trees of d and d^2 and step 4.
+// One 256-thread workgroup per slice; slice s's first value is at
+// x[(s / P) * sstride + s % P] (P interleaved slices per row).
+template <int PASS, int K, int P = 1>
 __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, int64_t n, int64_t sstride,
                                                   int64_t nch, int64_t ddof, LongWs ws, float *__restrict__ var_out,
                                                   float *__restrict__ mean_out) {
@@ -1514,7 +1523,8 @@ __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, i
     const Node nd = top_tree<sv::NODE_TWOSUM, K>(ws.nd + sl * nch, nch, slots[0]);
     const Node nq = top_tree<sv::NODE_NN, K>(ws.nq + sl * nch, nch, slots[1]);
     if (threadIdx.x == 0)
-      finalize(nd, nq, x[sl * sstride], ws.m[sl], n, ddof, var_out + sl, mean_out ? mean_out + sl : nullptr);
+      finalize(nd, nq, x[(sl / P) * sstride + sl % P], ws.m[sl], n, ddof, var_out + sl,
+               mean_out ? mean_out + sl : nullptr);
   }
 }
 
@@ -1547,6 +1557,7 @@ struct Tuning {
   int var_cols_once = 1;      // axis 0, 1025..4096 rows: one workgroup per 16 columns, one read, when the
                              // grid fills the chip (0: row chunks; 2: one read whatever the fill)
   int64_t launch_items = svx::MAX_LAUNCH_ITEMS;  // work-items per launch before a grid is cut into batches
+  int var_cols_pairs = 1;     // axis 0, two columns of 4097+ rows: one row of pairs in chunks (0: column chunks)
 };
 thread_local Tuning g_tune;
 
@@ -1753,12 +1764,29 @@ void launch_cols_one1(const float *x, int64_t R, int64_t C, int64_t ddof, float 
 // The top trees over nch <= LS_MAX_CHUNKS chunk nodes per slice: 256
 // threads of K nodes each, K the smallest of 1, 4, 32 that holds nch (the
 // zero padding beyond nch changes no bit).
-template <int PASS>
+template <int PASS, int P = 1>
 void launch_long_top(const float *x, int64_t n, int64_t sstride, int64_t nch, int64_t ddof, const LongWs &ws,
                      float *var, float *mean, dim3 grid, hipStream_t st) {
-  if (nch <= 256) k_long_top<PASS, 1><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
-  else if (nch <= 1024) k_long_top<PASS, 4><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
-  else k_long_top<PASS, LS_TOP_PER_THREAD><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  if (nch <= 256) k_long_top<PASS, 1, P><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  else if (nch <= 1024) k_long_top<PASS, 4, P><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  else k_long_top<PASS, LS_TOP_PER_THREAD, P><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+}
+
+// Rows of n pairs (two interleaved slices per row, row stride ld floats) in
+// chunks: slices 2r and 2r + 1 of row r; var and mean get 2 * rows entries
+// (slice order).  Workspace: long_ws of 2 * rows slices of
+// ceil(n / (LS_ROW_CHUNK / 2)) chunks.
+void launch_long_pairs(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, void *workspace,
+                       float *var, float *mean, hipStream_t st) {
+  const int64_t nch = (n + LS_ROW_CHUNK / 2 - 1) / (LS_ROW_CHUNK / 2);
+  const LongWs ws = long_ws(workspace, 2 * rows, nch);
+  const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)(2 * rows));
+  if (vec) k_long_rows<0, true, 2><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  else k_long_rows<0, false, 2><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  launch_long_top<0, 2>(x, n, ld, nch, ddof, ws, var, mean, top, st);
+  if (vec) k_long_rows<1, true, 2><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  else k_long_rows<1, false, 2><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  launch_long_top<1, 2>(x, n, ld, nch, ddof, ws, var, mean, top, st);
 }
 
 // The tree sum's plan: chunks of 64*e values, each wave of a SUM_W-wave
@@ -2425,8 +2453,17 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
     if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
     return check_launch("sv_variance_f32");
   }
-  const svx::RouteKnobs knobs{g_tune.var_long_rows, g_tune.var_cols_once, g_tune.var_cols_single_max,
-                              g_tune.var_short_rows, g_tune.var_cols_short, g_tune.var_cols_one};
+  if (!ax1 && cols == 1 && rows <= (int64_t)LS_MAX_CHUNKS * LS_ROW_CHUNK) {
+    // A single column [rows, 1] is one contiguous slice, as is the single row
+    // [1, rows]: the same values in the same order, hence the same tree and
+    // the same bits.  The row form reads it with wide loads; its workspace
+    // (none, or 24 bytes per 16384-value chunk) is smaller than the column
+    // form's, which the caller sized.
+    return sv_variance_f32(x, 1, rows, 1, ddof, var_out, mean_out, workspace, workspace_bytes, stream);
+  }
+  const svx::RouteKnobs knobs{g_tune.var_long_rows,  g_tune.var_cols_once,  g_tune.var_cols_single_max,
+                              g_tune.var_short_rows, g_tune.var_cols_short, g_tune.var_cols_one,
+                              g_tune.var_cols_pairs};
   const bool vec16 = aligned16(x) && cols % 4 == 0;
   // Columns of 1025..4096 rows: sixteen whole columns per workgroup of up to
   // 16 waves (four row groups of E rows per wave; a shorter column launches
@@ -2464,6 +2501,13 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
       launch_long_top<1>(x, n, cols, nch, ddof, ws, var_out, mean_out, top, st);
       break;
     }
+    case svx::Route::COLS_PAIRS:
+      // two columns: the matrix is one row of `rows` pairs (two interleaved
+      // slices, the same values in the same order per column), in chunks of
+      // LS_ROW_CHUNK / 2 rows read with wide per-lane loads; its workspace is
+      // smaller than the column chunks' that the caller sized
+      launch_long_pairs(aligned16(x) && rows % 2 == 0, x, 1, rows, 2 * rows, ddof, workspace, var_out, mean_out, st);
+      break;
     case svx::Route::COLS_ONE_READ:
       svh::in_batches(one_plan.blocks, 1, 64 * one_plan.waves, [&](int64_t b0, int64_t nb) {
         one_read<<<dim3((unsigned)nb), dim3(64 * (unsigned)one_plan.waves), 0, st>>>(x, rows, cols, ddof, var_out,
@@ -2564,6 +2608,9 @@ size_t sv_variance_c64_workspace_size(int64_t rows, int64_t cols, int axis) {
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
   if (ax1 && cols <= C64_FUSED_MAX_N) return 0;  // one pass, no staging
+  const int64_t pair_chunks = (cols + LS_ROW_CHUNK / 2 - 1) / (LS_ROW_CHUNK / 2);
+  if (ax1 && pair_chunks <= LS_MAX_CHUNKS)  // per-part variances, then the pair chunks' nodes
+    return round256((size_t)2 * rows * sizeof(float)) + long_ws_bytes(2 * rows, pair_chunks);
   const size_t inner = ax1 ? sv_variance_f32_workspace_size(2 * rows, cols, 1)
                            : sv_variance_f32_workspace_size(rows, 2 * cols, 0);
   if (inner == (size_t)-1) return (size_t)-1;
@@ -2658,7 +2705,16 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
   float *vparts = reinterpret_cast<float *>(wp);
   wp += round256((size_t)2 * nslices * sizeof(float));
   sv_status rc;
-  if (ax1) {
+  const int64_t pair_chunks = (cols + LS_ROW_CHUNK / 2 - 1) / (LS_ROW_CHUNK / 2);
+  if (ax1 && pair_chunks <= LS_MAX_CHUNKS) {
+    // Rows of more than 32768 values: chunks of LS_ROW_CHUNK / 2 complex
+    // values read once, the parts split in registers (two interleaved
+    // slices per row, the same values in the same order as the split rows),
+    // then the pair add.
+    launch_long_pairs(aligned16(z) && cols % 2 == 0, z, rows, cols, 2 * cols, ddof, wp, vparts, mean_out, st);
+    rc = check_launch("sv_variance_c64");
+  } else if (ax1) {
+    // rows of more than 8192 chunks of pairs: the parts staged as float rows
     float *split = reinterpret_cast<float *>(wp);
     wp += round256((size_t)2 * rows * cols * sizeof(float));
     const size_t inner = sv_variance_f32_workspace_size(2 * rows, cols, 1);
@@ -2741,6 +2797,7 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_xcd") == 0) return flag(&g_tune.var_xcd);
+  if (strcmp(key, "var_cols_pairs") == 0) return flag(&g_tune.var_cols_pairs);
   if (strcmp(key, "var_lds_pad") == 0) {
     if (value < 0 || value > 65536) return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_lds_pad must be in [0, 65536]");
     g_tune.var_lds_pad = (int)value;

@@ -243,6 +243,27 @@ void long_rows(const Where &c, int64_t rows, int64_t n, bool vec) {
   for (int64_t sl : visit(rows)) load(c, sl * n, 1, sl, 0);  // finalize's x0
 }
 
+// k_long_rows<PASS, VEC, 2> and k_long_top<PASS, K, 2>: rows of n pairs (two
+// interleaved slices per row, row stride ld floats).
+void long_pairs(const Where &c, int64_t rows, int64_t n, int64_t ld, bool vec) {
+  const int64_t chunk = LS_ROW_CHUNK / 2, nch = (n + chunk - 1) / chunk;
+  const int64_t nb = rows * nch;
+  launch(c, nb, 256);
+  launch(c, 2 * rows, 256);
+  for (int64_t b : visit(nb)) {
+    const int64_t r = b / nch, ch = b % nch;
+    for (int w = 0; w < 4; ++w) {
+      const int64_t base = ch * chunk + (int64_t)w * 64 * 32;
+      for (int lane = 0; lane < 64; ++lane) {
+        tile_loads(64, vec, 1, 2 * (n - base), 2 * rows_avail(nb / nch, r, ld / 2, n, base), lane,
+                   [&](int64_t i, int wd) { load(c, r * ld + 2 * base + i, wd, b, lane); });
+        load(c, r * ld, 2, b, lane);  // x0 of both slices
+      }
+    }
+  }
+  for (int64_t sl : visit(2 * rows)) load(c, (sl / 2) * ld + sl % 2, 1, sl, 0);  // finalize's x0
+}
+
 // ------------------------------------------------------------------ axis 0
 
 // The V adjacent columns x rows of load_cols_tile<V, E, VEC16> and the x0
@@ -364,6 +385,7 @@ void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k,
     case Route::LONG_ROWS_CHUNKED: long_rows(c, rows, n, vec16); break;
     case Route::ROWS_SEG: rows_seg(c, rows, n, seg_vw(off, cols), 1); break;
     case Route::ROWS_TILE: rows_tile(c, rows, n, vec16, k.split, k.loadp, k.full_rows); break;
+    case Route::COLS_PAIRS: long_pairs(c, 1, rows, 2 * rows, off == 0 && rows % 2 == 0); break;
     case Route::COLS_ONE_READ: {
       const ColsLongPlan p = cols_long_plan(rows, cols);
       cols_one(c, rows, cols, 1, 16, 4, false, p.E, p.mode, p.blocks, p.waves);
@@ -391,9 +413,13 @@ void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k,
 }
 
 void variance_c64(int64_t rows, int64_t cols, int off, int short_rows) {
-  if (rows == 0 || cols == 0 || cols > C64_FUSED_MAX_N) return;
+  if (rows == 0 || cols == 0) return;
   const Where c{"c64 axis 1", rows, cols, 2 * rows * cols};
   const bool vec = off == 0 && cols % 2 == 0;
+  if (cols > C64_FUSED_MAX_N) {
+    if ((cols + LS_ROW_CHUNK / 2 - 1) / (LS_ROW_CHUNK / 2) <= LS_MAX_CHUNKS) long_pairs(c, rows, cols, 2 * cols, vec);
+    return;
+  }
   if (cols <= SEG_MAX_N && short_rows) rows_seg(c, rows, cols, vec ? 2 : 1, 2);
   else rows_c64(c, rows, cols, vec);
 }
@@ -555,19 +581,19 @@ int main() {
                            65,   100,  127,  128,  129,  255,  256,  257,  300,  511,  512,  513,  777,   1000,
                            1023, 1024, 1025, 1500, 2047, 2048, 2049, 3000, 4095, 4096, 4097, 6000, 8191,  8192,
                            8193, 12345, 16383, 16384, 16385, 20000, 32768, 32769, 65535, 65536, 65537, 100003};
-  const RouteKnobs dflt{1, 1, 1024, 1, 1, 1};
+  const RouteKnobs dflt{1, 1, 1024, 1, 1, 1, 1};
   std::vector<Knobs> knobs;
   knobs.push_back({dflt, 0, 1, 1, 16});
   for (int split : {1, 2, 4, 8}) knobs.push_back({dflt, split, 1, 1, 16});
   for (int lp : {0, 2}) knobs.push_back({dflt, 0, lp, 1, 16});
   knobs.push_back({dflt, 0, 1, 0, 16});
-  for (int cw : {4, 8}) knobs.push_back({{1, 0, 1024, 1, 1, 1}, 0, 1, 1, cw});
-  knobs.push_back({{0, 1, 1024, 0, 0, 0}, 0, 1, 1, 16});
-  knobs.push_back({{1, 1, 1024, 1, 1, 2}, 0, 1, 1, 16});
-  knobs.push_back({{1, 1, 1024, 1, 1, 3}, 0, 1, 1, 16});
-  knobs.push_back({{1, 2, 1024, 1, 1, 1}, 0, 1, 1, 16});
-  knobs.push_back({{1, 1, 512, 1, 1, 1}, 0, 1, 1, 16});
-  knobs.push_back({{1, 1, 0, 1, 1, 1}, 0, 1, 1, 16});
+  for (int cw : {4, 8}) knobs.push_back({{1, 0, 1024, 1, 1, 1, 0}, 0, 1, 1, cw});
+  knobs.push_back({{0, 1, 1024, 0, 0, 0, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 1024, 1, 1, 2, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 1024, 1, 1, 3, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 2, 1024, 1, 1, 1, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 512, 1, 1, 1, 1}, 0, 1, 1, 16});
+  knobs.push_back({{1, 1, 0, 1, 1, 1, 1}, 0, 1, 1, 16});
 
   // every shape in the default knobs, the knob variants on a subset
   const int64_t some[] = {1, 3, 16, 17, 64, 65, 257, 513, 1000, 1025, 2048, 3000, 4096, 4097, 16385, 65537};

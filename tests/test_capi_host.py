@@ -191,13 +191,16 @@ def test_complex_argument_errors_and_sizes(L):
     # workspace ([1000, 128] along axis 0)
     assert L.sv_variance_c64_workspace_size(1000, 64, 0) == 512 + L.sv_variance_f32_workspace_size(1000, 128, 0)
     # axis 1: none up to 32768 values per row (one pass); above, the
-    # per-component variances + the split rows (8 bytes per value) + the
-    # float view's own workspace
+    # per-component variances + the pair chunks' nodes (three 8-byte nodes
+    # per 8192-value chunk per part, and 4 bytes per part); beyond 8192 such
+    # chunks the split rows (8 bytes per value) + the float view's workspace
     assert L.sv_variance_c64_workspace_size(64, 1000, 1) == 0
     assert L.sv_variance_c64_workspace_size(3, 16385, 1) == 0
     assert L.sv_variance_c64_workspace_size(3, 32768, 1) == 0
-    assert L.sv_variance_c64_workspace_size(3, 32769, 1) == 256 + (3 * 32769 * 8 + 255) // 256 * 256 + \
-        L.sv_variance_f32_workspace_size(6, 32769, 1)
+    assert L.sv_variance_c64_workspace_size(3, 32769, 1) == 256 + 6 * 5 * 24 + 6 * 4
+    n = 8192 * 8192 + 1
+    assert L.sv_variance_c64_workspace_size(1, n, 1) == 256 + (n * 8 + 255) // 256 * 256 + \
+        L.sv_variance_f32_workspace_size(2, n, 1)
     assert L.sv_variance_c64_workspace_size(2, 3, 5) == ctypes.c_size_t(-1).value
     assert L.sv_variance_c64(BAD, -1, 4, 1, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
     assert L.sv_variance_c64(BAD, 4, 4, 7, 0, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT

@@ -242,3 +242,12 @@ def test_var64_batched_launches(torch_dev, items):
             check_var64(torch_dev, a, axis, 1)
     finally:
         sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("R", [3, 1000, 20000, 1 << 20])
+def test_var64_single_column_as_a_row(torch_dev, R):
+    rng = np.random.default_rng(R + 64)
+    a = rng.normal(-3e3, 5, (R, 1))
+    for ddof in (0, 2):
+        v = check_var64(torch_dev, a, 0, ddof)
+        assert same_bits64(v, check_var64(torch_dev, np.ascontiguousarray(a.T), 1, ddof))

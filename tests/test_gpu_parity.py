@@ -814,3 +814,48 @@ def test_complex_and_variants_batched_launches(torch_dev, items):
                 assert same_bits(v.cpu().numpy(), oracle.variance(b, axis=axis, method=code)[0]), (code, axis, items)
     finally:
         sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("R", [1, 5, 64, 1000, 16385, 70000, 1 << 21])
+def test_variance_single_column_as_a_row(torch_dev, R):
+    # a [R, 1] column is read as the row [1, R] (the same values in the same
+    # order): bit for bit the oracle's column, and the row's
+    rng = np.random.default_rng(R)
+    a = rng.normal(3e3, 7, (R, 1)).astype(np.float32)
+    for ddof in (0, 1):
+        v = check_var(torch_dev, a, 0, ddof)
+        assert same_bits(v, check_var(torch_dev, np.ascontiguousarray(a.T), 1, ddof))
+
+
+@pytest.mark.parametrize("R", [4097, 8192, 8193, 50001, 1 << 20, 3_000_001])
+@pytest.mark.parametrize("pairs", [1, 0])
+def test_variance_two_columns(torch_dev, R, pairs):
+    # [R, 2] along axis 0: one row of R pairs in chunks (two interleaved
+    # slices), or the column chunks; aligned even, odd and misaligned
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    rng = np.random.default_rng(R + pairs)
+    a = rng.normal(-6e3, 13, (R, 2)).astype(np.float32)
+    sv.set_tuning("var_cols_pairs", pairs)
+    try:
+        for ddof in (0, 1):
+            check_var(torch_dev, a, 0, ddof)
+        buf = torch.zeros(2 * R + 1, dtype=torch.float32, device=dev)
+        buf[1:] = torch.from_numpy(a.reshape(-1)).to(dev)
+        v = sv.var(buf[1:].view(R, 2), dim=0)
+        torch.cuda.synchronize()
+        assert same_bits(v.cpu().numpy(), oracle.variance(a, axis=0)[0])
+    finally:
+        sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("shape,axis", [((3, 32769), 1), ((2, 100_001), 1), ((1, 1 << 21), 1), ((70, 40_000), 1),
+                                        ((1 << 20, 1), 0), ((50001, 1), 0)])
+def test_complex_long_rows_and_single_column(torch_dev, shape, axis):
+    # complex rows beyond 32768 values take the pair chunks (parts split in
+    # registers); a single complex column is a [R, 2] float matrix along axis 0
+    rng = np.random.default_rng(shape[0] + shape[1])
+    z = (rng.normal(3, 2, shape) + 1j * rng.normal(-1, 5, shape)).astype(np.complex64) + (4e3 - 2e3j)
+    for ddof in (0, 1):
+        check_var_c64(torch_dev, z, axis, ddof)
