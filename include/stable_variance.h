@@ -387,7 +387,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    column per lane, the input read once, when that grid
  *                    fills at least three quarters of the chip's last round
  *                    of workgroups, else the row-chunk launches; 0 = always
- *                    the row-chunk launches; 2 = always the one-read launch
+ *                    the row-chunk launches; 2 = always the one-read launch.
+ *                    The same setting picks the float64 launch of columns of
+ *                    1025..4096 rows (at least two columns): eight or four
+ *                    whole columns per workgroup of 8 waves, read once
  *   "sum_xcd"        tree sum: 1 = renumber the workgroups so that each of the
  *                    eight dies (XCDs) streams one contiguous region; 0 =
  *                    dispatch order, consecutive regions spread over the dies

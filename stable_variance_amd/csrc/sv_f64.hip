@@ -1004,7 +1004,10 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int64_t cb = b0 + (int)blockIdx.x;  // b0: launches of at most 2^32 - 1 work-items
+  // b0: launches of at most 2^32 - 1 work-items.  Blocks of fewer than 16
+  // doubles share a 128-byte line with the next block: the blocks of one
+  // line run on one die (svx::line_on_one_die, in 4-byte units).
+  const int64_t cb = svx::line_on_one_die<int>(b0 + (int)blockIdx.x, (int)((C + NC - 1) / NC), 2 * NC);
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
@@ -1239,14 +1242,18 @@ void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const S
   }
 }
 
-// Columns of 64 < R <= 1024 rows in one launch (k_cols_one_d), 16*G*W = the
+// Columns of 64 < R <= 4096 rows in one launch (k_cols_one_d), 16*G*W = the
 // power of two at or above R rows per workgroup:
 //   R <= 512: one column per lane (16 doubles per lane), G 1 or 4 (row
 //     segments of at least 16 lanes, 128 bytes), W up to 16, G = 1 when that
 //     still gives 512 workgroups;
 //   R > 512: two adjacent columns per lane (one 16-byte load per row for an
 //     aligned base and an even width, else two 8-byte loads; one column for
-//     a single column); G = 16, W = 4.
+//     a single column); G = 16, W = 4;
+//   R > 1024 (at least two columns): as above with W = 8 (512 work-items
+//     holding 32 doubles each), and G = 32 above 2048 rows (four columns
+//     per workgroup).  At 16 waves the 128 registers a lane may then use
+//     hold too little: the tile spills.
 // Measured (us, one column per lane against two): [100, 140000] 26.5 / 39.6,
 // [512, 4096] 8.0 / 10.9; [1000, 20000] 65.2 / 52.5, [1000, 1000] 13.0 / 6.9.
 void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool vec, double *var, double *mean,
@@ -1257,7 +1264,13 @@ void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool
     k_cols_one_d<V_, W_, G_, ##__VA_ARGS__><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, \
                                                                                          mean, (int)b0);  \
   })
-  if (p.V == 2) {
+  if (p.V == 2 && p.G == 32) {
+    if (vec) SV_ONE64(2, 8, 32);
+    else SV_ONE64(2, 8, 32, false);
+  } else if (p.V == 2 && p.W == 8) {
+    if (vec) SV_ONE64(2, 8, 16);
+    else SV_ONE64(2, 8, 16, false);
+  } else if (p.V == 2) {
     if (vec) SV_ONE64(2, 4, 16);
     else SV_ONE64(2, 4, 16, false);  // two 8-byte loads
   } else if (p.G == 16) {
@@ -1377,7 +1390,26 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     return sv_variance_f64(x, 1, rows, 1, ddof, var_out, mean_out, workspace, workspace_bytes, stream);
   }
   const bool vec = svh::aligned16(x) && (cols % 2 == 0);
-  switch (svx::f64_route(rows, cols, ax1, vec)) {
+  // Columns of 1025..4096 rows: read once by workgroups of eight or four
+  // whole columns (32 doubles per lane) unless that grid leaves the chip's
+  // last round of workgroups mostly empty.
+  bool one_read = false;
+  if (svx::cols_one_read64_candidate(ax1, rows, cols, svh::cols_once())) {
+    const svx::ColsOne64Plan p = svx::cols_one64_plan(rows, cols, vec);
+    one_read = svh::cols_once() == 2;
+    const void *fn = p.G == 32 ? (vec ? reinterpret_cast<const void *>(k_cols_one_d<2, 8, 32>)
+                                      : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 32, false>))
+                               : (vec ? reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16>)
+                                      : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16, false>));
+    int per_cu = 0, cus = 0, dev = 0;
+    if (!one_read && hipGetDevice(&dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * p.W, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0) {
+      const int64_t cap = (int64_t)per_cu * cus, rounds = (p.blocks + cap - 1) / cap;
+      one_read = 4 * p.blocks >= 3 * rounds * cap;
+    }
+  }
+  switch (svx::f64_route(rows, cols, ax1, vec, one_read)) {
     case svx::Route64::ROWS_SEG: {
       // rows of up to 512 doubles sharing waves: 16-byte loads of two
       // doubles for aligned rows of an even count, else single doubles

@@ -91,10 +91,11 @@ constexpr int64_t seg_row(int64_t b, int w, int lane, int S) { return (b * 4 + w
 // when c0 lies past the matrix (C >= V).
 constexpr int64_t cols_first(int64_t c0, int64_t C, int V) { return c0 < C ? c0 : C - V; }
 
-// Column block of workgroup b of nb when blocks of nc < 32 columns share a
-// 128-byte line with the next P - 1 blocks (P = 32 / nc): within each full
-// group of 8P workgroups, the P that run on one die (b mod 8) take P adjacent
-// blocks.  A bijection of [0, nb).
+// Column block of workgroup b of nb when blocks of nc < 32 four-byte words
+// (columns of float32, or half as many of float64) share a 128-byte line
+// with the next P - 1 blocks (P = 32 / nc): within each full group of 8P
+// workgroups, the P that run on one die (b mod 8) take P adjacent blocks.
+// A bijection of [0, nb).
 template <class I>
 constexpr I line_on_one_die(I b, I nb, int nc) {
   if (nc >= 32) return b;
@@ -334,6 +335,7 @@ constexpr int64_t V64_ROWS_MAX_N = 16384;        // one workgroup per row
 constexpr int64_t V64_ROWS_ONE_MAX_N = 32768;    // ... with at least V64_ROWS_ONE_MIN_ROWS rows
 constexpr int64_t V64_ROWS_ONE_MIN_ROWS = 256;
 constexpr int64_t V64_COLS_MAX_R = 1024;         // whole columns in one workgroup
+constexpr int64_t V64_COLS_ONE_MAX_R = 4096;     // ... or up to this many, read once, when the grid fills
 constexpr int L64_E = 16;                        // doubles per lane (long slices)
 constexpr int L64_W = 8;                         // waves per workgroup (long slices)
 constexpr int64_t L64_ROW_CHUNK = 64LL * L64_E * L64_W;  // 8192 doubles
@@ -348,19 +350,26 @@ enum class Route64 {
   ROWS_SEG,           // axis 1, up to 512 values, rows sharing waves (seg_plan)
   ROWS_TILE,          // axis 1, one workgroup per row (rows64_plan)
   COLS_CHUNKED,       // axis 0, more than 1024 rows (cols_chunk64_plan)
-  COLS_ONE,           // axis 0, 65..1024 rows (cols_one64_plan)
+  COLS_ONE,           // axis 0, 65..1024 rows, or 1025..4096 read once (cols_one64_plan)
   COLS_SHORT,         // axis 0, fewer than 16 rows, two columns per lane
   COLS_LANE,          // axis 0, a lane per column (cols_lane64_plan)
 };
-// vec16: the matrix starts 16-byte aligned and cols is even.
-constexpr Route64 f64_route(int64_t rows, int64_t cols, bool ax1, bool vec16) {
+// Columns that are candidates for the one-read launch of 1025..4096 rows
+// (var_cols_once: the float32 knob, 0 never, 1 when the grid fills, 2 always).
+constexpr bool cols_one_read64_candidate(bool ax1, int64_t rows, int64_t cols, int var_cols_once) {
+  return !ax1 && rows > V64_COLS_MAX_R && rows <= V64_COLS_ONE_MAX_R && cols >= 2 && var_cols_once != 0;
+}
+// vec16: the matrix starts 16-byte aligned and cols is even.  one_read: the
+// one-read launch is chosen for a candidate (above).
+constexpr Route64 f64_route(int64_t rows, int64_t cols, bool ax1, bool vec16, bool one_read = false) {
   const int64_t n = ax1 ? cols : rows;
   if (ax1) {
     if (n <= 512) return Route64::ROWS_SEG;
     if (n <= V64_ROWS_MAX_N || (n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS)) return Route64::ROWS_TILE;
     return Route64::LONG_ROWS_CHUNKED;
   }
-  if (n > V64_COLS_MAX_R) return Route64::COLS_CHUNKED;
+  if (n > V64_COLS_MAX_R) return (one_read && n <= V64_COLS_ONE_MAX_R && cols >= 2) ? Route64::COLS_ONE
+                                                                                    : Route64::COLS_CHUNKED;
   if (n > 64) return Route64::COLS_ONE;
   if (n < 16 && vec16) return Route64::COLS_SHORT;
   return Route64::COLS_LANE;
@@ -375,14 +384,17 @@ constexpr RowsPlan rows64_plan(int64_t n) {
   if (n <= V64_ROWS_MAX_N) return {16, 16};
   return {32, 16};
 }
-// Axis 0, 65..1024 rows in one launch: V adjacent columns per lane (two above
+// Axis 0, 65..4096 rows in one launch: V adjacent columns per lane (two above
 // 512 rows, one below or for a single column), G row groups, W waves of 16
-// rows per lane, `blocks` workgroups of V*64/G columns.
+// rows per lane (above 1024 rows: at least two columns, 8 waves, and 32 row
+// groups above 2048), `blocks` workgroups of V*64/G columns.
 struct ColsOne64Plan {
   int V, G, W;
   int64_t blocks;
 };
 constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16) {
+  if (R > 2048) return {2, 32, 8, (C + 3) / 4};
+  if (R > V64_COLS_MAX_R) return {2, 16, 8, (C + 7) / 8};
   if (R > 512) return (vec16 || C >= 2) ? ColsOne64Plan{2, 16, 4, (C + 7) / 8} : ColsOne64Plan{1, 16, 4, (C + 3) / 4};
   int64_t cap = L64_E;
   while (cap < R) cap *= 2;

@@ -1564,6 +1564,7 @@ thread_local Tuning g_tune;
 }  // namespace
 
 int64_t svh::launch_items() { return g_tune.launch_items; }
+int svh::cols_once() { return g_tune.var_cols_once; }
 
 namespace {
 

@@ -280,14 +280,15 @@ void cols_tile(const Where &c, int64_t R, int64_t C, int64_t c0, int64_t r0, boo
 }
 
 // k_cols_one<V, W, G, VEC16, E, MODE> over `waves` waves.
-// pair_lines: the float32 kernel's die pairing of blocks narrower than a line.
+// words: 4-byte words per element (the die pairing counts a block's width in
+// words: 1 for float32, 2 for float64).
 void cols_one(const Where &c, int64_t R, int64_t C, int V, int W, int G, bool vec16, int E, int mode, int64_t blocks,
-              int waves, bool pair_lines = true) {
+              int waves, int words = 1) {
   batches(blocks, 1, 64 * waves, [&](int64_t, int64_t cnt) { launch(c, cnt, 64 * waves); });
   const int nc = V * (64 / G);
   if ((C + nc - 1) / nc != blocks) report(c, "column blocks", blocks, nc, -1, -1);
   for (int64_t b : visit(blocks)) {
-    const int64_t cb = pair_lines ? line_on_one_die<int>((int)b, (int)((C + nc - 1) / nc), nc) : b;
+    const int64_t cb = line_on_one_die<int>((int)b, (int)((C + nc - 1) / nc), words * nc);
     if (cb < 0 || cb >= blocks) report(c, "column block", cb, blocks, b, -1);
     for (int w = 0; w < waves; ++w)
       for (int lane = 0; lane < 64; ++lane) {
@@ -437,12 +438,12 @@ void variant_f32(int64_t rows, int64_t cols, int axis, int off) {
 
 // The float64 variance (indices in doubles; the row tiles load floats, two
 // per double).  off: the matrix's address modulo 16 bytes (0 or 8).
-void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
+void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_read) {
   const bool ax1 = axis == 1;
   const int64_t n = ax1 ? cols : rows;
   if (rows == 0 || cols == 0) return;
   const bool vec = off == 0 && cols % 2 == 0;
-  const Route64 route = f64_route(rows, cols, ax1, vec);
+  const Route64 route = f64_route(rows, cols, ax1, vec, one_read);
   char name[64];
   snprintf(name, sizeof name, "f64 axis %d route %d", axis, (int)route);
   const Where c{name, rows, cols, rows * cols};
@@ -492,12 +493,18 @@ void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
     }
     case Route64::COLS_ONE: {
       const ColsOne64Plan p = cols_one64_plan(rows, cols, vec);
-      cols_one(c, rows, cols, p.V, p.W, p.G, vec, L64_E, 0, p.blocks, p.W, false);
+      cols_one(c, rows, cols, p.V, p.W, p.G, vec, L64_E, 0, p.blocks, p.W, 2);
       break;
     }
     case Route64::COLS_SHORT: cols_short(c, rows, cols, 2); break;
     case Route64::COLS_LANE: cols_lane(c, rows, cols, cols_lane64_plan(rows)); break;
   }
+}
+
+// Both launch choices of a candidate for the one-read columns.
+void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
+  variance_f64_route(rows, cols, axis, off, false);
+  if (cols_one_read64_candidate(axis == 1, rows, cols, 1)) variance_f64_route(rows, cols, axis, off, true);
 }
 
 // k_var_kahan: a lane per slice, chunks of 64 values.

@@ -251,3 +251,27 @@ def test_var64_single_column_as_a_row(torch_dev, R):
     for ddof in (0, 2):
         v = check_var64(torch_dev, a, 0, ddof)
         assert same_bits64(v, check_var64(torch_dev, np.ascontiguousarray(a.T), 1, ddof))
+
+
+@pytest.mark.parametrize("once", [2, 0])
+@pytest.mark.parametrize("R,C", [(1025, 2), (1025, 3), (2048, 9), (2049, 4), (3000, 33), (4096, 64), (4096, 7),
+                                 (1500, 1030)])
+def test_var64_cols_one_read(torch_dev, once, R, C):
+    # columns of 1025..4096 rows: read once by workgroups of whole columns
+    # (8 waves; 16 row groups per wave up to 2048 rows, 32 above) -- forced
+    # on (2) and off (0, the 128-row chunks) whatever the grid's fill
+    import stable_variance_amd as sv
+
+    rng = np.random.default_rng(R * 3 + C + once)
+    sv.set_tuning("var_cols_once", once)
+    try:
+        a = rng.normal(2e6, 3, (R, C))
+        check_var64(torch_dev, a, 0)
+        check_var64(torch_dev, a, 0, 1)
+        check_var64(torch_dev, np.ascontiguousarray(a[:, 1:]), 0)
+        b = W.adversarial_values(R * C, R + 5).astype(np.float64).reshape(R, C) * 1e200
+        check_var64(torch_dev, b, 0)
+        sv.set_tuning("launch_items", 1024)
+        check_var64(torch_dev, a, 0, 2)
+    finally:
+        sv.set_tuning("reset", 0)
