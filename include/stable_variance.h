@@ -398,7 +398,7 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "var_xcd"        row variance: as sum_xcd, over rows (default 0)
  *   "var_cols_pairs" axis 0, two columns of more than 4096 rows: 1 (default)
  *                    = one row of pairs in chunks (wide loads), 0 = the
- *                    column chunks
+ *                    column chunks; float32 and float64
  *   "adn_e"         values per lane in an ADN-sum chunk: 16 (default) or 32
  *                    (32 only with three folds; other counts use 16)
  *   "adn_blocks"     target number of ADN-sum workgroups, 1..8192 (default 512)

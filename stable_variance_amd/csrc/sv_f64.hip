@@ -632,50 +632,63 @@ __device__ __forceinline__ NodeD block_tree_d(NodeD n, NodeD *slots, int w, int 
   return node_tree_d<0, W, W, NN>(t);
 }
 
-template <int PASS, bool VEC>
+// P interleaved slices per row (P = 2: a matrix of two columns read as one
+// row of pairs): each slice's chunks hold 8192 / P values, EP = 16 / P per
+// lane, taken apart from the lane's 16 loaded doubles; slice j of row r is
+// slice P*r + j.
+template <int PASS, bool VEC, int P = 1>
 __global__ __launch_bounds__(64 * L64_W) void k_long_rows_d(const double *__restrict__ x, int64_t n, int64_t ld,
                                                             int64_t nch, SliceWsD ws) {
-  constexpr int E = L64_E, W = L64_W;
-  __shared__ NodeD slots[2][W];
+  constexpr int E = L64_E, W = L64_W, EP = E / P;
+  constexpr int64_t CHUNK = L64_ROW_CHUNK / P;
+  __shared__ NodeD slots[2 * P][W];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t r = (int64_t)blockIdx.x / nch;
   const int64_t c = (int64_t)blockIdx.x % nch;
   const double *__restrict__ row = x + r * ld;
-  const int64_t base = c * L64_ROW_CHUNK + (int64_t)w * 64 * E;
+  const int64_t base = c * CHUNK + (int64_t)w * 64 * EP;  // first value of this wave, of each slice
   const bool empty = base >= n;  // wave-uniform: only padding, nodes (+0, +0)
   float vf[2 * E];
-  const int64_t avail = 2 * svx::rows_avail(gridDim.x / nch, r, ld, n, base);  // floats to the launch's last row
-  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(row + base), 2 * (n - base), nullptr, vf, lane,
-                                      avail);
-  double v[E];
-  floats_to_doubles<E>(vf, v);
-  const double x0 = row[0];
-  const bool full = base + 64 * E <= n;
-  const int64_t left = n - base - (int64_t)lane * E;
-  const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
+  // floats to the launch's last row
+  const int64_t avail = 2 * P * svx::rows_avail(gridDim.x / nch, r, ld / P, n, base);
+  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(row + P * base), 2 * P * (n - base), nullptr,
+                                      vf, lane, avail);
+  double f[E];
+  floats_to_doubles<E>(vf, f);
+  const bool full = base + 64 * EP <= n;
+  const int64_t left = n - base - (int64_t)lane * EP;
+  const int valid = left < 0 ? 0 : (left > EP ? EP : (int)left);
+  double v[P][EP];
 #pragma unroll
-  for (int i = 0; i < E; ++i) v[i] = (full || i < valid) ? v[i] - x0 : 0.0;
-  const int64_t out = r * nch + c;
-  if constexpr (PASS == 0) {
-    NodeD ny = {0.0, 0.0};
-    if (!empty) ny = wave_tree_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
-    ny = block_tree_d<W, KD_PLAIN>(ny, slots[0], w, lane);
-    if (threadIdx.x == 0) ws.ny[out] = ny;
-  } else {
-    const double m = ws.m[r];
-    NodeD nd = {0.0, 0.0}, nq = {0.0, 0.0};
-    if (!empty) {
-      if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
-      else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
-      nd = wave_tree_d<false>(nd);
-      nq = wave_tree_d<true>(nq);
-    }
-    nd = block_tree_d<W, false>(nd, slots[0], w, lane);
-    nq = block_tree_d<W, true>(nq, slots[1], w, lane);
-    if (threadIdx.x == 0) {
-      ws.nd[out] = nd;
-      ws.nq[out] = nq;
+  for (int j = 0; j < P; ++j) {
+    const double x0 = row[j];
+#pragma unroll
+    for (int i = 0; i < EP; ++i) v[j][i] = (full || i < valid) ? f[P * i + j] - x0 : 0.0;
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int64_t out = (P * r + j) * nch + c;
+    if constexpr (PASS == 0) {
+      NodeD ny = {0.0, 0.0};
+      if (!empty) ny = wave_tree_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, EP, EP>(v[j]));
+      ny = block_tree_d<W, KD_PLAIN>(ny, slots[2 * j], w, lane);
+      if (threadIdx.x == 0) ws.ny[out] = ny;
+    } else {
+      const double m = ws.m[P * r + j];
+      NodeD nd = {0.0, 0.0}, nq = {0.0, 0.0};
+      if (!empty) {
+        if (full) lane_tree_dq_d<false, 0, EP, EP>(v[j], m, EP, nd, nq);
+        else lane_tree_dq_d<true, 0, EP, EP>(v[j], m, valid, nd, nq);
+        nd = wave_tree_d<false>(nd);
+        nq = wave_tree_d<true>(nq);
+      }
+      nd = block_tree_d<W, false>(nd, slots[2 * j], w, lane);
+      nq = block_tree_d<W, true>(nq, slots[2 * j + 1], w, lane);
+      if (threadIdx.x == 0) {
+        ws.nd[out] = nd;
+        ws.nq[out] = nq;
+      }
     }
   }
 }
@@ -697,7 +710,9 @@ __device__ __forceinline__ NodeD top_tree_d(const NodeD *__restrict__ nodes, int
   return block_tree_d<4, NN>(r, slots, w, lane);
 }
 
-template <int PASS, int K>
+// One workgroup per slice; slice s's first value is at
+// x[(s / P) * ld + s % P] (P interleaved slices per row).
+template <int PASS, int K, int P = 1>
 __global__ __launch_bounds__(256) void k_long_top_d(const double *__restrict__ x, int64_t n, int64_t ld,
                                                     int64_t nch, int64_t ddof, SliceWsD ws,
                                                     double *__restrict__ var_out, double *__restrict__ mean_out) {
@@ -710,7 +725,7 @@ __global__ __launch_bounds__(256) void k_long_top_d(const double *__restrict__ x
     const NodeD nd = top_tree_d<false, K>(ws.nd + r * nch, nch, slots[0]);
     const NodeD nq = top_tree_d<true, K>(ws.nq + r * nch, nch, slots[1]);
     if (threadIdx.x == 0)
-      finalize_d(nd, nq, x[r * ld], ws.m[r], n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
+      finalize_d(nd, nq, x[(r / P) * ld + r % P], ws.m[r], n, ddof, var_out + r, mean_out ? mean_out + r : nullptr);
   }
 }
 
@@ -1156,12 +1171,29 @@ size_t var64_ws(int64_t rows, int64_t cols, bool ax1) {
   return slice_ws_bytes(((n + C64_CHUNK - 1) / C64_CHUNK) * cols, cols);
 }
 
-template <int PASS>
+template <int PASS, int P = 1>
 void launch_long_top_d(const double *x, int64_t n, int64_t ld, int64_t nch, int64_t ddof, const SliceWsD &ws,
                        double *var, double *mean, dim3 grid, hipStream_t st) {
-  if (nch <= 256) k_long_top_d<PASS, 1><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
-  else if (nch <= 1024) k_long_top_d<PASS, 4><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
-  else k_long_top_d<PASS, L64_TOP_MAX_K><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+  if (nch <= 256) k_long_top_d<PASS, 1, P><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+  else if (nch <= 1024) k_long_top_d<PASS, 4, P><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+  else k_long_top_d<PASS, L64_TOP_MAX_K, P><<<grid, 256, 0, st>>>(x, n, ld, nch, ddof, ws, var, mean);
+}
+
+// A matrix of two columns along axis 0 as one row of n pairs: the chunk
+// launches of k_long_rows_d over both interleaved slices at once (16-byte
+// loads of whole rows), chunks of 4096 rows.  The workspace holds the node
+// arrays of 2 * nch chunk nodes.
+void launch_long_pairs_d(bool vec, const double *x, int64_t n, int64_t ddof, void *workspace, double *var,
+                         double *mean, hipStream_t st) {
+  const int64_t nch = (n + L64_ROW_CHUNK / 2 - 1) / (L64_ROW_CHUNK / 2);
+  const SliceWsD ws = slice_ws(workspace, 2 * nch);
+  const dim3 grid((unsigned)nch), block(64 * L64_W), top(2);
+  if (vec) k_long_rows_d<0, true, 2><<<grid, block, 0, st>>>(x, n, 2 * n, nch, ws);
+  else k_long_rows_d<0, false, 2><<<grid, block, 0, st>>>(x, n, 2 * n, nch, ws);
+  launch_long_top_d<0, 2>(x, n, 2 * n, nch, ddof, ws, var, mean, top, st);
+  if (vec) k_long_rows_d<1, true, 2><<<grid, block, 0, st>>>(x, n, 2 * n, nch, ws);
+  else k_long_rows_d<1, false, 2><<<grid, block, 0, st>>>(x, n, 2 * n, nch, ws);
+  launch_long_top_d<1, 2>(x, n, 2 * n, nch, ddof, ws, var, mean, top, st);
 }
 
 template <int V, int G>
@@ -1409,7 +1441,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
       one_read = 4 * p.blocks >= 3 * rounds * cap;
     }
   }
-  switch (svx::f64_route(rows, cols, ax1, vec, one_read)) {
+  switch (svx::f64_route(rows, cols, ax1, vec, one_read, svh::cols_pairs())) {
     case svx::Route64::ROWS_SEG: {
       // rows of up to 512 doubles sharing waves: 16-byte loads of two
       // doubles for aligned rows of an even count, else single doubles
@@ -1474,6 +1506,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
       break;
     }
     case svx::Route64::COLS_ONE: launch_cols_one_d(x, rows, cols, ddof, vec, var_out, mean_out, st); break;
+    case svx::Route64::COLS_PAIRS: launch_long_pairs_d(vec, x, rows, ddof, workspace, var_out, mean_out, st); break;
     case svx::Route64::COLS_SHORT: {
       const int e = svx::cols_short_e(n);
       svh::in_batches((cols / 2 + 255) / 256, 1, 256, [&](int64_t b0, int64_t nb) {

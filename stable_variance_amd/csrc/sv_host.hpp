@@ -32,6 +32,8 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 __attribute__((visibility("hidden"))) int64_t launch_items();
 // sv_set_tuning("var_cols_once") of this host thread: 0, 1 (default) or 2.
 __attribute__((visibility("hidden"))) int cols_once();
+// sv_set_tuning("var_cols_pairs") of this host thread: 0 or 1 (default).
+__attribute__((visibility("hidden"))) int cols_pairs();
 
 // in_batches(total, per_block, threads, fn) calls fn(first, count) over
 // [0, total) in runs of whole blocks (per_block items of `threads`

@@ -349,6 +349,7 @@ enum class Route64 {
   LONG_ROWS_CHUNKED,  // axis 1, rows longer than one workgroup holds
   ROWS_SEG,           // axis 1, up to 512 values, rows sharing waves (seg_plan)
   ROWS_TILE,          // axis 1, one workgroup per row (rows64_plan)
+  COLS_PAIRS,         // axis 0, two columns of more than 4096 rows: one row of pairs in chunks
   COLS_CHUNKED,       // axis 0, more than 1024 rows (cols_chunk64_plan)
   COLS_ONE,           // axis 0, 65..1024 rows, or 1025..4096 read once (cols_one64_plan)
   COLS_SHORT,         // axis 0, fewer than 16 rows, two columns per lane
@@ -360,14 +361,19 @@ constexpr bool cols_one_read64_candidate(bool ax1, int64_t rows, int64_t cols, i
   return !ax1 && rows > V64_COLS_MAX_R && rows <= V64_COLS_ONE_MAX_R && cols >= 2 && var_cols_once != 0;
 }
 // vec16: the matrix starts 16-byte aligned and cols is even.  one_read: the
-// one-read launch is chosen for a candidate (above).
-constexpr Route64 f64_route(int64_t rows, int64_t cols, bool ax1, bool vec16, bool one_read = false) {
+// one-read launch is chosen for a candidate (above).  pairs: the float32 knob
+// var_cols_pairs.
+constexpr Route64 f64_route(int64_t rows, int64_t cols, bool ax1, bool vec16, bool one_read = false,
+                            bool pairs = true) {
   const int64_t n = ax1 ? cols : rows;
   if (ax1) {
     if (n <= 512) return Route64::ROWS_SEG;
     if (n <= V64_ROWS_MAX_N || (n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS)) return Route64::ROWS_TILE;
     return Route64::LONG_ROWS_CHUNKED;
   }
+  if (cols == 2 && n > V64_COLS_ONE_MAX_R && pairs &&
+      (n + L64_ROW_CHUNK / 2 - 1) / (L64_ROW_CHUNK / 2) <= L64_MAX_CHUNKS)
+    return Route64::COLS_PAIRS;
   if (n > V64_COLS_MAX_R) return (one_read && n <= V64_COLS_ONE_MAX_R && cols >= 2) ? Route64::COLS_ONE
                                                                                     : Route64::COLS_CHUNKED;
   if (n > 64) return Route64::COLS_ONE;

@@ -436,14 +436,32 @@ void variant_f32(int64_t rows, int64_t cols, int axis, int off) {
   }
 }
 
+// k_long_rows_d<PASS, VEC, 2> and k_long_top_d<PASS, K, 2>: one row of n
+// pairs of doubles (c in doubles, cf the same array in floats).
+void long_pairs_d(const Where &c, const Where &cf, int64_t n, bool vec) {
+  const int64_t chunk = L64_ROW_CHUNK / 2, nch = (n + chunk - 1) / chunk;
+  launch(c, nch, 64 * L64_W);
+  launch(c, 2, 256);
+  for (int64_t b : visit(nch))
+    for (int w = 0; w < L64_W; ++w) {
+      const int64_t base = b * chunk + (int64_t)w * 64 * (L64_E / 2);
+      for (int lane = 0; lane < 64; ++lane) {
+        tile_loads(2 * L64_E, vec, 1, 4 * (n - base), 4 * rows_avail(1, 0, n, n, base), lane,
+                   [&](int64_t i, int wd) { load(cf, 4 * base + i, wd, b, lane); });
+        load(c, 0, 2, b, lane);  // x0 of both slices
+      }
+    }
+  for (int64_t sl = 0; sl < 2; ++sl) load(c, sl, 1, sl, 0);  // finalize's x0
+}
+
 // The float64 variance (indices in doubles; the row tiles load floats, two
 // per double).  off: the matrix's address modulo 16 bytes (0 or 8).
-void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_read) {
+void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_read, bool pairs) {
   const bool ax1 = axis == 1;
   const int64_t n = ax1 ? cols : rows;
   if (rows == 0 || cols == 0) return;
   const bool vec = off == 0 && cols % 2 == 0;
-  const Route64 route = f64_route(rows, cols, ax1, vec, one_read);
+  const Route64 route = f64_route(rows, cols, ax1, vec, one_read, pairs);
   char name[64];
   snprintf(name, sizeof name, "f64 axis %d route %d", axis, (int)route);
   const Where c{name, rows, cols, rows * cols};
@@ -485,6 +503,7 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
       }
       break;
     }
+    case Route64::COLS_PAIRS: long_pairs_d(c, cf, rows, vec); break;
     case Route64::COLS_CHUNKED: {
       const int V = vec ? 2 : 1;
       cols_chunked(c, rows, cols, V, L64_W, cols_chunk64_plan(V, rows, cols), (rows + C64_CHUNK - 1) / C64_CHUNK,
@@ -501,10 +520,12 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
   }
 }
 
-// Both launch choices of a candidate for the one-read columns.
+// Both launch choices of a candidate for the one-read columns, and of two
+// columns (pairs or column chunks).
 void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
-  variance_f64_route(rows, cols, axis, off, false);
-  if (cols_one_read64_candidate(axis == 1, rows, cols, 1)) variance_f64_route(rows, cols, axis, off, true);
+  variance_f64_route(rows, cols, axis, off, false, true);
+  if (cols_one_read64_candidate(axis == 1, rows, cols, 1)) variance_f64_route(rows, cols, axis, off, true, true);
+  if (axis == 0 && cols == 2) variance_f64_route(rows, cols, axis, off, false, false);
 }
 
 // k_var_kahan: a lane per slice, chunks of 64 values.

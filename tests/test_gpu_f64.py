@@ -275,3 +275,29 @@ def test_var64_cols_one_read(torch_dev, once, R, C):
         check_var64(torch_dev, a, 0, 2)
     finally:
         sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("pairs", [1, 0])
+@pytest.mark.parametrize("R", [4097, 4096 * 3, 100_003, 1 << 20])
+def test_var64_two_columns(torch_dev, R, pairs):
+    # [R, 2] doubles along axis 0 beyond 4096 rows: one row of R pairs in
+    # 4096-row chunks (two interleaved slices), or the column chunks; an
+    # aligned and a misaligned (8-byte) base
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    rng = np.random.default_rng(R + pairs + 64)
+    a = rng.normal(-6e5, 13, (R, 2))
+    sv.set_tuning("var_cols_pairs", pairs)
+    try:
+        for ddof in (0, 1):
+            check_var64(torch_dev, a, 0, ddof)
+        buf = torch.zeros(2 * R + 1, dtype=torch.float64, device=dev)
+        buf[1:] = torch.from_numpy(a.reshape(-1)).to(dev)
+        v = sv.var(buf[1:].view(R, 2), dim=0)
+        torch.cuda.synchronize()
+        assert same_bits64(v.cpu().numpy(), oracle.variance_f64(a, axis=0)[0])
+        b = W.adversarial_values(2 * R, R + 3).astype(np.float64).reshape(R, 2) * 1e200
+        check_var64(torch_dev, b, 0)
+    finally:
+        sv.set_tuning("reset", 0)
