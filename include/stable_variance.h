@@ -374,9 +374,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    columns per lane (one 16-byte load per row for a 16-byte
  *                    aligned base and a width divisible by 4, else four
  *                    4-byte loads; widths below 4 take one), 3 = one column
- *                    per lane, 1 (default) = four for 513 rows or more and
- *                    8192 columns or more, else one; 0 = 64 columns per
- *                    workgroup, a lane per column, not one launch per tile
+ *                    per lane, 1 (default) = four for 513 rows or more,
+ *                    8192 columns or more and 16-byte loads, else one;
+ *                    0 = 64 columns per workgroup, a lane per column, not one launch per tile
  *   "var_cols_single_max"  axis 0: columns of up to this many rows are
  *                    held by one workgroup and read once (0..1024, default
  *                    1024); longer columns are reduced in row chunks

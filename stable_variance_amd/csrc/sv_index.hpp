@@ -316,8 +316,10 @@ constexpr Route f32_route(int64_t rows, int64_t cols, bool ax1, bool vec16, cons
   if (n < 16 && k.var_cols_short && vec16) return Route::COLS_SHORT;
   if (k.var_cols_one && n > 64) {
     // four columns per lane for long columns (513..1024 rows) of wide
-    // matrices, else one
-    const bool four = cols >= 4 && (k.var_cols_one == 2 || (k.var_cols_one == 1 && n > 512 && cols >= 8192));
+    // matrices that take 16-byte loads, else one (four 4-byte loads per row
+    // measured slower than one column per lane)
+    const bool four =
+        cols >= 4 && (k.var_cols_one == 2 || (k.var_cols_one == 1 && n > 512 && cols >= 8192 && vec16));
     return four ? Route::COLS_ONE4 : Route::COLS_ONE1;
   }
   return Route::COLS_LANE;
