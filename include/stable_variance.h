@@ -238,11 +238,34 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
  * Every variant but 1 takes the plain tree for the local mean, as the method
  * does; "plain" and "compensated" name the trees of d and d^2.
  * Shapes: axis 1 with n <= 16384, axis 0 with n <= 1024; variant 8 any
- * axis with n <= 4194304 (else SV_ERR_UNSUPPORTED).  No workspace; otherwise
+ * axis with n <= 4194304 (else SV_ERR_UNSUPPORTED; longer slices of
+ * variants 0-7 take sv_variance_variant_ws_f32).  No workspace; otherwise
  * as sv_variance_f32.
  */
 sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int variant,
                                   float *var_out, float *mean_out, void *stream);
+
+/*
+ * The same variants with a caller-provided device workspace, for slices
+ * longer than one workgroup holds (same page, §4; the slice computation of
+ * §2 with one step changed).  Rows of more than 16384 values are reduced in
+ * chunks of 16384 (aligned nodes of the slice's tree, so the same bits as
+ * one workgroup would give); columns of more than 1024 rows are first
+ * transposed into the workspace (a copy: the same values in the same order,
+ * hence the same trees), then reduced as rows.  Slices of up to 8192 chunks
+ * (2^27 values); rows * cols <= 2^36.
+ * workspace: device memory, 256-byte aligned, at least
+ * sv_variance_variant_f32_workspace_size(rows, cols, axis, variant) bytes
+ * (0 for the shapes sv_variance_variant_f32 takes, and then it may be NULL);
+ * scratch, contents on entry ignored; SV_ERR_WORKSPACE when it is missing,
+ * short or misaligned.  The size function returns (size_t)-1 for an
+ * invalid argument or a shape beyond these limits.  Everything else as
+ * sv_variance_variant_f32.
+ */
+size_t sv_variance_variant_f32_workspace_size(int64_t rows, int64_t cols, int axis, int variant);
+sv_status sv_variance_variant_ws_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
+                                     int variant, float *var_out, float *mean_out, void *workspace,
+                                     size_t workspace_bytes, void *stream);
 
 /*
  * The method in binary64 (the float64 path): the compensated tree sum and

@@ -82,6 +82,11 @@ def capi():
                 L.sv_variance_c64.argtypes = [vp, i64, i64, ctypes.c_int, i64, vp, vp, vp, sz, vp]
                 L.sv_variance_variant_f32.restype = ctypes.c_int
                 L.sv_variance_variant_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
+                L.sv_variance_variant_f32_workspace_size.restype = sz
+                L.sv_variance_variant_f32_workspace_size.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int]
+                L.sv_variance_variant_ws_f32.restype = ctypes.c_int
+                L.sv_variance_variant_ws_f32.argtypes = [vp, i64, i64, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp,
+                                                         sz, vp]
                 L.sv_tree_sum_f64_workspace_size.restype = sz
                 L.sv_tree_sum_f64_workspace_size.argtypes = [i64]
                 L.sv_tree_sum_f64.restype = ctypes.c_int
@@ -287,8 +292,9 @@ VARIANTS = {
 def var_variant(x, variant, dim: int = -1, ddof: int = 0, return_mean: bool = False):
     """One of the ablation variants (a name of VARIANTS or its number) on a
     2-D float32 tensor.  The tree variants take one workgroup per slice (rows
-    of up to 16384 values, columns of up to 1024); the Kahan scan takes slices
-    of up to 2^22 values."""
+    of up to 16384 values, columns of up to 1024) or, beyond, the long-slice
+    launches with a workspace (slices of up to 2^27 values); the Kahan scan
+    takes slices of up to 2^22 values."""
     import torch
 
     _check_tensor(x)
@@ -303,7 +309,11 @@ def var_variant(x, variant, dim: int = -1, ddof: int = 0, return_mean: bool = Fa
         stream = torch.cuda.current_stream(x.device).cuda_stream
         out = torch.empty(ns, dtype=torch.float32, device=x.device)
         mean = torch.empty(ns, dtype=torch.float32, device=x.device) if return_mean else None
-        _check(L.sv_variance_variant_f32(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof), code,
-                                         out.data_ptr() if ns else None,
-                                         mean.data_ptr() if (mean is not None and ns) else None, stream))
+        need = L.sv_variance_variant_f32_workspace_size(rows, cols, axis, code)
+        need = 0 if need == ctypes.c_size_t(-1).value else need  # the call reports the error
+        ws = _workspace("variant", need, x.device, stream)
+        _check(L.sv_variance_variant_ws_f32(x2.data_ptr() if x2.numel() else None, rows, cols, axis, int(ddof), code,
+                                            out.data_ptr() if ns else None,
+                                            mean.data_ptr() if (mean is not None and ns) else None,
+                                            ws.data_ptr() if ws is not None else None, need, stream))
     return (out, mean) if return_mean else out

@@ -1438,9 +1438,12 @@ struct LongWs {
 // consecutive pairs (E floats, one per-lane load of 4 values at a time) and
 // splits them in registers; the chunk covers LS_ROW_CHUNK / 2 pairs, and
 // both slices' nodes go to the workspace.
-template <int PASS, bool VEC, int P = 1>
+// V: an ablation variant (its shift and tree of y; the d and d^2 trees are
+// the compensated ones, whose s parts are the plain trees).
+template <int PASS, bool VEC, int P = 1, int V = V_KERNEL>
 __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, int64_t n, int64_t ld, int64_t nch,
                                                    LongWs ws) {
+  using F = VariantFlags<V>;
   constexpr int E = 64, W = 4, EP = E / P;  // EP values of each slice per lane
   constexpr int64_t CHUNK = LS_ROW_CHUNK / P;
   __shared__ Node slots[2 * P][W];
@@ -1462,15 +1465,15 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
   for (int j = 0; j < P; ++j) {
     const float x0 = row[j];
 #pragma unroll
-    for (int i = 0; i < EP; ++i) v[j][i] = (full || i < valid) ? f[P * i + j] - x0 : 0.0f;
+    for (int i = 0; i < EP; ++i) v[j][i] = (full || i < valid) ? (F::shift ? f[P * i + j] - x0 : f[P * i + j]) : 0.0f;
   }
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int64_t out = (P * r + j) * nch + c;
     if constexpr (PASS == 0) {
-      Node ny = sv::lane_tree<sv::Y_LEAF, 0, EP, EP>(v[j]);
-      ny = sv::wave_tree<sv::Y_KIND>(ny);
-      ny = block_tree<W, sv::Y_KIND>(ny, slots[2 * j], w, lane);
+      Node ny = sv::lane_tree<F::yleaf, 0, EP, EP>(v[j]);
+      ny = sv::wave_tree<F::ykind>(ny);
+      ny = block_tree<W, F::ykind>(ny, slots[2 * j], w, lane);
       if (threadIdx.x == 0) ws.ny[out] = ny;
     } else {
       const float m = ws.m[P * r + j];
@@ -1509,22 +1512,27 @@ __device__ __forceinline__ Node top_tree(const Node *__restrict__ nodes, int64_t
 
 // PASS 0: m = Plain(y) / n.  PASS 1: the top trees of d and d^2 and step 4.
 // One 256-thread workgroup per slice; slice s's first value is at
-// x[(s / P) * sstride + s % P] (P interleaved slices per row).
-template <int PASS, int K, int P = 1>
+// x[(s / P) * sstride + s % P] (P interleaved slices per row).  V: an
+// ablation variant (its tree of y, local mean and step 4).
+template <int PASS, int K, int P = 1, int V = V_KERNEL>
 __global__ __launch_bounds__(256) void k_long_top(const float *__restrict__ x, int64_t n, int64_t sstride,
                                                   int64_t nch, int64_t ddof, LongWs ws, float *__restrict__ var_out,
                                                   float *__restrict__ mean_out) {
+  using F = VariantFlags<V>;
   __shared__ Node slots[2][4];
   const int64_t sl = blockIdx.x;
   if constexpr (PASS == 0) {
-    const Node ny = top_tree<sv::Y_KIND, K>(ws.ny + sl * nch, nch, slots[0]);
-    if (threadIdx.x == 0) ws.m[sl] = sv::root_value_k<sv::Y_KIND>(ny) / (float)n;
+    const Node ny = top_tree<F::ykind, K>(ws.ny + sl * nch, nch, slots[0]);
+    if (threadIdx.x == 0) ws.m[sl] = local_mean<V>(ny, n);
   } else {
     const Node nd = top_tree<sv::NODE_TWOSUM, K>(ws.nd + sl * nch, nch, slots[0]);
     const Node nq = top_tree<sv::NODE_NN, K>(ws.nq + sl * nch, nch, slots[1]);
-    if (threadIdx.x == 0)
-      finalize(nd, nq, x[(sl / P) * sstride + sl % P], ws.m[sl], n, ddof, var_out + sl,
-               mean_out ? mean_out + sl : nullptr);
+    if (threadIdx.x == 0) {
+      const float x0 = x[(sl / P) * sstride + sl % P];
+      float *mo = mean_out ? mean_out + sl : nullptr;
+      if constexpr (V == V_KERNEL) finalize(nd, nq, x0, ws.m[sl], n, ddof, var_out + sl, mo);
+      else finalize_v<V>(nd, nq, x0, ws.m[sl], n, ddof, var_out + sl, mo);
+    }
   }
 }
 
@@ -1766,12 +1774,12 @@ void launch_cols_one1(const float *x, int64_t R, int64_t C, int64_t ddof, float 
 // The top trees over nch <= LS_MAX_CHUNKS chunk nodes per slice: 256
 // threads of K nodes each, K the smallest of 1, 4, 32 that holds nch (the
 // zero padding beyond nch changes no bit).
-template <int PASS, int P = 1>
+template <int PASS, int P = 1, int V = V_KERNEL>
 void launch_long_top(const float *x, int64_t n, int64_t sstride, int64_t nch, int64_t ddof, const LongWs &ws,
                      float *var, float *mean, dim3 grid, hipStream_t st) {
-  if (nch <= 256) k_long_top<PASS, 1, P><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
-  else if (nch <= 1024) k_long_top<PASS, 4, P><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
-  else k_long_top<PASS, LS_TOP_PER_THREAD, P><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  if (nch <= 256) k_long_top<PASS, 1, P, V><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  else if (nch <= 1024) k_long_top<PASS, 4, P, V><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
+  else k_long_top<PASS, LS_TOP_PER_THREAD, P, V><<<grid, 256, 0, st>>>(x, n, sstride, nch, ddof, ws, var, mean);
 }
 
 // Rows of n pairs (two interleaved slices per row, row stride ld floats) in
@@ -2226,6 +2234,46 @@ __global__ __launch_bounds__(64) void k_var_kahan(const float *__restrict__ x, i
   }
 }
 
+// A variant over rows of more than 16384 values: the method's long-row chunk
+// launches (k_long_rows, k_long_top) with the variant's shift, tree of y,
+// local mean and step 4.  Workspace: long_ws of `rows` slices.
+template <int V>
+void launch_long_variant(bool vec, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof,
+                         void *workspace, float *var, float *mean, hipStream_t st) {
+  const int64_t nch = (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK;
+  const LongWs ws = long_ws(workspace, rows, nch);
+  const dim3 grid((unsigned)(rows * nch)), block(256), top((unsigned)rows);
+  if (vec) k_long_rows<0, true, 1, V><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  else k_long_rows<0, false, 1, V><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  launch_long_top<0, 1, V>(x, n, ld, nch, ddof, ws, var, mean, top, st);
+  if (vec) k_long_rows<1, true, 1, V><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  else k_long_rows<1, false, 1, V><<<grid, block, 0, st>>>(x, n, ld, nch, ws);
+  launch_long_top<1, 1, V>(x, n, ld, nch, ddof, ws, var, mean, top, st);
+}
+
+// xt = the transpose of x ([R, C] -> [C, R], both row-major): 32 x 32 tiles
+// through LDS, coalesced on both sides; workgroup b0 + blockIdx.x takes tile
+// (b / ceil(C/32), b mod ceil(C/32)).  A copy: the values keep their bits.
+__global__ __launch_bounds__(256) void k_transpose(const float *__restrict__ x, int64_t R, int64_t C,
+                                                   float *__restrict__ xt, int64_t b0) {
+  __shared__ float t[32][33];
+  const int64_t tiles_c = (C + 31) / 32;
+  const int64_t b = b0 + blockIdx.x;
+  const int64_t r0 = (b / tiles_c) * 32, c0 = (b % tiles_c) * 32;
+  const int lx = threadIdx.x & 31, ly = threadIdx.x >> 5;  // 32 x 8 threads
+#pragma unroll
+  for (int k = 0; k < 32; k += 8) {
+    const int64_t r = r0 + ly + k, c = c0 + lx;
+    if (r < R && c < C) t[ly + k][lx] = x[r * C + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 32; k += 8) {
+    const int64_t c = c0 + ly + k, r = r0 + lx;
+    if (r < R && c < C) xt[c * R + r] = t[lx][ly + k];
+  }
+}
+
 template <int V>
 void launch_variant(bool ax1, bool vec, const float *x, int64_t rows, int64_t cols, int64_t ddof, float *var,
                     float *mean, hipStream_t st) {
@@ -2545,32 +2593,65 @@ sv_status sv_variance_f32(const float *x, int64_t rows, int64_t cols, int axis, 
   return check_launch("sv_variance_f32");
 }
 
-sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int variant,
-                                  float *var_out, float *mean_out, void *stream) {
+size_t sv_variance_variant_f32_workspace_size(int64_t rows, int64_t cols, int axis, int variant) {
+  if (rows < 0 || cols < 0 || (axis != 0 && axis != 1 && axis != -1 && axis != -2)) return (size_t)-1;
+  if (variant < V_KERNEL || variant > V_SHIFT_KAHAN_NO2T) return (size_t)-1;
+  if (cols > 0 && rows > VAR_MAX_ELEMS / cols) return (size_t)-1;
+  const bool ax1 = (axis == 1 || axis == -1);
+  const int64_t n = ax1 ? cols : rows, nsl = ax1 ? rows : cols;
+  if (variant == V_SHIFT_KAHAN_NO2T) return n > ((int64_t)KS_T << KS_LEVELS) ? (size_t)-1 : 0;
+  if (n == 0 || nsl == 0 || (ax1 ? n <= ROWS_MAX_N : n <= COLS_MAX_R)) return 0;
+  const int64_t nch = (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK;
+  if (n > ROWS_MAX_N && nch > LS_MAX_CHUNKS) return (size_t)-1;
+  // axis 0: the transposed matrix, then (columns of more than 16384 rows)
+  // the chunk nodes of its rows
+  size_t b = ax1 ? 0 : round256((size_t)rows * (size_t)cols * sizeof(float));
+  if (n > ROWS_MAX_N) b += long_ws_bytes(nsl, nch);
+  return b;
+}
+
+}  // extern "C"
+
+namespace {
+
+sv_status variant_f32(const char *who, const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
+                      int variant, float *var_out, float *mean_out, void *workspace, size_t workspace_bytes,
+                      bool has_ws, void *stream) {
   if (rows < 0 || cols < 0)
-    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: negative shape [%lld, %lld]", (long long)rows,
-                (long long)cols);
+    return fail(SV_ERR_INVALID_ARGUMENT, "%s: negative shape [%lld, %lld]", who, (long long)rows, (long long)cols);
   if (axis != 0 && axis != 1 && axis != -1 && axis != -2)
-    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: axis %d not in {0, 1, -1, -2}", axis);
-  if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: ddof = %lld < 0", (long long)ddof);
+    return fail(SV_ERR_INVALID_ARGUMENT, "%s: axis %d not in {0, 1, -1, -2}", who, axis);
+  if (ddof < 0) return fail(SV_ERR_INVALID_ARGUMENT, "%s: ddof = %lld < 0", who, (long long)ddof);
   if (variant != V_KERNEL && variant != V_COMP_Y && variant != V_REFERENCE && variant != V_NAIVE &&
       variant != V_SHIFT_PLAIN_NO2T && variant != V_SHIFT_PLAIN_2T && variant != V_NOSHIFT_COMP_2T &&
       variant != V_SHIFT_COMP_NO2T && variant != V_SHIFT_KAHAN_NO2T)
-    return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: unknown variant %d", variant);
+    return fail(SV_ERR_INVALID_ARGUMENT, "%s: unknown variant %d", who, variant);
   const bool ax1 = (axis == 1 || axis == -1);
   const int64_t nslices = ax1 ? rows : cols;
   const int64_t n = ax1 ? cols : rows;
+  if (cols > 0 && rows > VAR_MAX_ELEMS / cols) return fail(SV_ERR_UNSUPPORTED, "%s: rows * cols above 2^36", who);
   if (nslices == 0) return ok();
-  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: var_out is NULL");
-  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "sv_variance_variant_f32: x is NULL");
+  if (!var_out) return fail(SV_ERR_INVALID_ARGUMENT, "%s: var_out is NULL", who);
+  if (n > 0 && !x) return fail(SV_ERR_INVALID_ARGUMENT, "%s: x is NULL", who);
   // the tree variants take one workgroup per slice (rows of up to 16384
-  // values, columns of up to 1024); the Kahan scan takes a lane per slice and
-  // slices of up to 2^16 chunks of 64 values
+  // values, columns of up to 1024) or, with a workspace, the long-slice
+  // launches; the Kahan scan takes a lane per slice and slices of up to 2^16
+  // chunks of 64 values
   const bool kahan = variant == V_SHIFT_KAHAN_NO2T;
-  if (nslices > 0x7fffffffLL ||
-      (kahan ? n > ((int64_t)KS_T << KS_LEVELS) : (ax1 ? n > ROWS_MAX_N : n > COLS_MAX_R)))
-    return fail(SV_ERR_UNSUPPORTED, "sv_variance_variant_f32: shape [%lld, %lld] along axis %d not supported",
-                (long long)rows, (long long)cols, axis);
+  const bool single = ax1 ? n <= ROWS_MAX_N : n <= COLS_MAX_R;
+  const int64_t nch = (n + LS_ROW_CHUNK - 1) / LS_ROW_CHUNK;
+  if (nslices > 0x7fffffffLL || (kahan ? n > ((int64_t)KS_T << KS_LEVELS)
+                                       : (!single && (!has_ws || (n > ROWS_MAX_N && nch > LS_MAX_CHUNKS)))))
+    return fail(SV_ERR_UNSUPPORTED, "%s: shape [%lld, %lld] along axis %d not supported%s", who, (long long)rows,
+                (long long)cols, axis,
+                (!kahan && !single && !has_ws) ? " (longer slices: sv_variance_variant_ws_f32)" : "");
+  const size_t need = kahan || single ? 0 : sv_variance_variant_f32_workspace_size(rows, cols, axis, variant);
+  if (need > 0) {
+    if (!workspace) return fail(SV_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", who, need);
+    if (workspace_bytes < need)
+      return fail(SV_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", who, workspace_bytes, need);
+    if (!svh::aligned256(workspace)) return fail(SV_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", who);
+  }
   const sv_status dev = check_device();
   if (dev != SV_OK) return dev;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -2579,7 +2660,7 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
     const unsigned blocks = (unsigned)((nslices + 255) / 256);
     k_fill<<<blocks, 256, 0, st>>>(var_out, nslices, __builtin_nanf(""));
     if (mean_out) k_fill<<<blocks, 256, 0, st>>>(mean_out, nslices, __builtin_nanf(""));
-    return check_launch("sv_variance_variant_f32");
+    return check_launch(who);
   }
   const bool vec = aligned16(x) && (cols % 4 == 0);
   if (variant == V_SHIFT_KAHAN_NO2T) {
@@ -2587,19 +2668,58 @@ sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, in
     if (!ax1) k_var_kahan<false, false><<<grid, block, 0, st>>>(x, nslices, n, cols, ddof, var_out, mean_out);
     else if (vec) k_var_kahan<true, true><<<grid, block, 0, st>>>(x, nslices, n, cols, ddof, var_out, mean_out);
     else k_var_kahan<true, false><<<grid, block, 0, st>>>(x, nslices, n, cols, ddof, var_out, mean_out);
-    return check_launch("sv_variance_variant_f32");
+    return check_launch(who);
   }
+  // Slices longer than one workgroup: columns are transposed into the
+  // workspace first (the same values in the same order, so the same trees),
+  // then rows of more than 16384 values take the chunk launches.
+  const float *xs = x;
+  int64_t srows = rows, scols = cols;
+  bool svec = vec, sax1 = ax1;
+  char *wp = reinterpret_cast<char *>(workspace);
+  if (!single && !ax1) {
+    float *xt = reinterpret_cast<float *>(wp);
+    const int64_t tiles = ((rows + 31) / 32) * ((cols + 31) / 32);
+    svh::in_batches(tiles, 1, 256, [&](int64_t b0, int64_t nb) {
+      k_transpose<<<dim3((unsigned)nb), dim3(256), 0, st>>>(x, rows, cols, xt, b0);
+    });
+    wp += round256((size_t)rows * (size_t)cols * sizeof(float));
+    xs = xt;
+    srows = cols;
+    scols = rows;
+    svec = scols % 4 == 0;  // the workspace is 256-byte aligned
+    sax1 = true;
+  }
+#define SV_VARIANT(V_)                                                                                           do {                                                                                                             if (sax1 && scols > ROWS_MAX_N)                                                                                   launch_long_variant<V_>(svec, xs, srows, scols, scols, ddof, wp, var_out, mean_out, st);                     else                                                                                                             launch_variant<V_>(sax1, svec, xs, srows, scols, ddof, var_out, mean_out, st);                             } while (0)
   switch (variant) {
-    case V_KERNEL: launch_variant<V_KERNEL>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    case V_COMP_Y: launch_variant<V_COMP_Y>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    case V_REFERENCE: launch_variant<V_REFERENCE>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    case V_NAIVE: launch_variant<V_NAIVE>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    case V_SHIFT_PLAIN_NO2T: launch_variant<V_SHIFT_PLAIN_NO2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    case V_SHIFT_PLAIN_2T: launch_variant<V_SHIFT_PLAIN_2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    case V_NOSHIFT_COMP_2T: launch_variant<V_NOSHIFT_COMP_2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
-    default: launch_variant<V_SHIFT_COMP_NO2T>(ax1, vec, x, rows, cols, ddof, var_out, mean_out, st); break;
+    case V_KERNEL: SV_VARIANT(V_KERNEL); break;
+    case V_COMP_Y: SV_VARIANT(V_COMP_Y); break;
+    case V_REFERENCE: SV_VARIANT(V_REFERENCE); break;
+    case V_NAIVE: SV_VARIANT(V_NAIVE); break;
+    case V_SHIFT_PLAIN_NO2T: SV_VARIANT(V_SHIFT_PLAIN_NO2T); break;
+    case V_SHIFT_PLAIN_2T: SV_VARIANT(V_SHIFT_PLAIN_2T); break;
+    case V_NOSHIFT_COMP_2T: SV_VARIANT(V_NOSHIFT_COMP_2T); break;
+    default: SV_VARIANT(V_SHIFT_COMP_NO2T); break;
   }
-  return check_launch("sv_variance_variant_f32");
+#undef SV_VARIANT
+  return check_launch(who);
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_variance_variant_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof, int variant,
+                                  float *var_out, float *mean_out, void *stream) {
+  return variant_f32("sv_variance_variant_f32", x, rows, cols, axis, ddof, variant, var_out, mean_out, nullptr, 0,
+                     false, stream);
+}
+
+sv_status sv_variance_variant_ws_f32(const float *x, int64_t rows, int64_t cols, int axis, int64_t ddof,
+                                     int variant, float *var_out, float *mean_out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  return variant_f32("sv_variance_variant_ws_f32", x, rows, cols, axis, ddof, variant, var_out, mean_out, workspace,
+                     workspace_bytes, true, stream);
 }
 
 

@@ -425,8 +425,29 @@ void variance_c64(int64_t rows, int64_t cols, int off, int short_rows) {
   else rows_c64(c, rows, cols, vec);
 }
 
+// Rows of more than 16384 values take the long-row chunks; columns of more
+// than 1024 rows are transposed (k_transpose: 32 x 32 tiles, 256 threads)
+// into a 256-byte aligned workspace and reduced as rows.
 void variant_f32(int64_t rows, int64_t cols, int axis, int off) {
   const Where c{"variant", rows, cols, rows * cols};
+  if (axis == 1 && cols > ROWS_MAX_N) {
+    long_rows(c, rows, cols, off == 0 && cols % 4 == 0);
+    return;
+  }
+  if (axis == 0 && rows > COLS_MAX_R) {
+    const int64_t tc = (cols + 31) / 32, tiles = ((rows + 31) / 32) * tc;
+    batches(tiles, 1, 256, [&](int64_t b0, int64_t nb) {
+      launch(c, nb, 256);
+      for (int64_t b : visit(nb))
+        for (int t = 0; t < 256; ++t)
+          for (int k = 0; k < 32; k += 8) {
+            const int64_t r = ((b0 + b) / tc) * 32 + (t >> 5) + k, col = ((b0 + b) % tc) * 32 + (t & 31);
+            if (r < rows && col < cols) load(c, r * cols + col, 1, b, t);
+          }
+    });
+    variant_f32(cols, rows, 1, 0);
+    return;
+  }
   if (axis == 1) {
     const RowsPlan p = variant_rows_plan(cols);
     const bool vec = off == 0 && cols % 4 == 0;
@@ -643,7 +664,7 @@ int main() {
             for (bool fills : {true, false})
               if (fills || cand || i > 0) variance_f32(R, C, axis, off, knobs[i], fills);
           if (off == 8 || (axis == 0 && off != 0)) continue;
-          if ((axis == 1 ? C <= ROWS_MAX_N : R <= COLS_MAX_R)) variant_f32(R, C, axis, off);
+          if (n <= LS_MAX_CHUNKS * LS_ROW_CHUNK) variant_f32(R, C, axis, off);
           if (n <= ((int64_t)KS_T << KS_LEVELS)) kahan(R, C, axis, off);
         }
       }
@@ -669,7 +690,7 @@ int main() {
       for (int axis : {0, 1}) {
         for (int off : {0, 8, 4})
           for (bool fills : {true, false}) variance_f32(R, C, axis, off, knobs[0], fills);
-        if (axis == 1 ? C <= ROWS_MAX_N : R <= COLS_MAX_R) variant_f32(R, C, axis, 0);
+        variant_f32(R, C, axis, 0);
         for (int off : {0, 8}) variance_f64(R, C, axis, off);
         for (int off : {0, 4}) variance_c64(R, C, off, 1);
       }

@@ -257,3 +257,30 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "sv_oracle" not in text, f
+
+
+def test_variant_workspace_sizes_and_errors(L):
+    # the variants beyond one workgroup: long rows take the chunk nodes of
+    # the long-row path (24 bytes per chunk per row, 4 per row), long
+    # columns the transposed matrix (256-byte rounded) first
+    ws = L.sv_variance_variant_f32_workspace_size
+    big = ctypes.c_size_t(-1).value
+    assert ws(4, 16384, 1, 0) == 0 and ws(1024, 9, 0, 3) == 0 and ws(0, 70000, 1, 0) == 0
+    assert ws(3, 20001, 1, 2) == 3 * 2 * 24 + 3 * 4
+    assert ws(1025, 3, 0, 0) == 12544
+    assert ws(20001, 3, 0, 5) == 240128 + 3 * 2 * 24 + 3 * 4
+    assert ws(1, 8192 * 16384, 1, 1) == 8192 * 24 + 4
+    assert ws(1, 8192 * 16384 + 1, 1, 1) == big
+    assert ws(3, 5000, 1, 8) == 0 and ws(3, (1 << 22) + 1, 1, 8) == big  # the Kahan scan: no workspace
+    assert ws(3, 5, 1, 9) == big and ws(3, 5, 2, 0) == big and ws(-1, 5, 1, 0) == big
+    out = ctypes.c_void_p(0x2000)
+    # the form without a workspace refuses the long slices; the other asks
+    # for the workspace it lacks (both before any device call)
+    assert L.sv_variance_variant_f32(BAD, 3, 20001, 1, 0, 2, out, None, None) == SV_ERR_UNSUPPORTED
+    assert L.sv_variance_variant_ws_f32(BAD, 3, 20001, 1, 0, 2, out, None, None, 0, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_variant_ws_f32(BAD, 2000, 5, 0, 0, 2, out, None, BAD, 100, None) == SV_ERR_WORKSPACE
+    assert L.sv_variance_variant_ws_f32(BAD, 2000, 5, 0, 0, 2, out, None, ctypes.c_void_p(0x1010), 1 << 20,
+                                        None) == SV_ERR_WORKSPACE  # misaligned
+    assert L.sv_variance_variant_ws_f32(BAD, 3, 5, 1, 0, 9, out, None, None, 0, None) == SV_ERR_INVALID_ARGUMENT
+    assert L.sv_variance_variant_ws_f32(BAD, 1, 8192 * 16384 + 1, 1, 0, 0, out, None, BAD, 1 << 30,
+                                        None) == SV_ERR_UNSUPPORTED

@@ -680,6 +680,42 @@ def test_variants_against_oracle(torch_dev, name):
             assert same_bits(m.cpu().numpy(), om), (name, a.shape, ax, ddof)
 
 
+@pytest.mark.parametrize("name", [n for n in GPU_VARIANTS if n != "shift_kahan_no2t"])
+def test_variants_on_long_slices(torch_dev, name):
+    # slices longer than one workgroup holds: rows of more than 16384 values
+    # in 16384-value chunks (aligned nodes of the tree), columns of more than
+    # 1024 rows transposed into the workspace and reduced as rows (in one
+    # workgroup up to 16384 rows, in chunks beyond); aligned, odd and
+    # misaligned widths; bit for bit against the oracle's variant
+    import stable_variance_amd as sv
+
+    torch, dev = torch_dev
+    code = GPU_VARIANTS[name]
+    rng = np.random.default_rng(code + 100)
+    cases = [(rng.normal(1e4, 1, (3, 20001)).astype(np.float32), 1), (rng.normal(-7, 2, (2, 40000)).astype(np.float32), 1),
+             (rng.normal(3e3, 5, (1, 70003)).astype(np.float32), 1), (rng.normal(5, 1, (1500, 7)).astype(np.float32), 0),
+             (rng.normal(-2e4, 3, (2000, 64)).astype(np.float32), 0), (rng.normal(9, 4, (20001, 3)).astype(np.float32), 0),
+             (W.adversarial_values(2 * 33000, code + 7).reshape(2, 33000), 1),
+             (W.adversarial_values(1100 * 5, code + 8).reshape(1100, 5), 0)]
+    for a, ax in cases:
+        for ddof in (0, 1):
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            v, m = sv.var_variant(t, code, dim=ax, ddof=ddof, return_mean=True)
+            torch.cuda.synchronize()
+            ov, om = oracle.variance(a, axis=ax, ddof=ddof, method=code)
+            assert same_bits(v.cpu().numpy(), ov), (name, a.shape, ax, ddof)
+            assert same_bits(m.cpu().numpy(), om), (name, a.shape, ax, ddof)
+        if ax == 1 and a.shape[1] % 4 == 0:  # a misaligned base: per-value loads
+            buf = torch.zeros(a.size + 1, dtype=torch.float32, device=dev)
+            buf[1:] = torch.from_numpy(a.reshape(-1)).to(dev)
+            v = sv.var_variant(buf[1:].view(a.shape), code, dim=ax)
+            torch.cuda.synchronize()
+            assert same_bits(v.cpu().numpy(), oracle.variance(a, axis=ax, method=code)[0]), (name, a.shape)
+    if code == 0:  # variant 0 is the method: the main entry point's bits
+        a = torch.from_numpy(cases[0][0]).to(dev)
+        assert torch.equal(sv.var_variant(a, 0, dim=1).view(torch.int32), sv.var(a, dim=1).view(torch.int32))
+
+
 @pytest.mark.parametrize("shape,axis", [((3, 70000), 1), ((2, 5001), 1), ((130, 4097), 1), ((3000, 70), 0),
                                         ((1, 64), 1), ((65, 1), 0), ((4096, 4096), 1)])
 def test_kahan_scan_variant_long_and_ragged_slices(torch_dev, shape, axis):
