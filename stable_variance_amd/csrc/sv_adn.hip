@@ -126,12 +126,8 @@ sv_status sv_adn_sum_f32(const float *x, int64_t n, int fold, float *out, void *
   (void)hipGetLastError();
 
   const int e = (g_adn.e == 32 && fold == 3) ? 32 : 16;
-  const int64_t csize = 64LL * e;
-  const int64_t chunks = (n + csize - 1) / csize;
-  const int64_t waves_target = ADN_WAVES * g_adn.blocks;
-  const int64_t g = (chunks + waves_target - 1) / waves_target;  // chunks per wave
-  const int64_t waves = (chunks + g - 1) / g;
-  const int64_t blocks = (waves + ADN_WAVES - 1) / ADN_WAVES;     // <= g_adn.blocks
+  const svx::AdnPlan plan = svx::adn_plan(n, e, g_adn.blocks);  // blocks <= g_adn.blocks
+  const int64_t chunks = plan.chunks, g = plan.g, blocks = plan.blocks;
   unsigned *counter = reinterpret_cast<unsigned *>(workspace);
   unsigned *recs = reinterpret_cast<unsigned *>(reinterpret_cast<char *>(workspace) + ADN_WS_HEADER);
   const bool vec = svh::aligned16(x);

@@ -11,6 +11,7 @@
 
 #include "../../include/stable_variance.h"
 #include "sv_device.hpp"
+#include "sv_index.hpp"
 
 namespace {
 
@@ -19,12 +20,12 @@ constexpr int ADN_GRID0 = -146;             // log2 of bin 0's unit
 constexpr int ADN_SCALE_FROM = 20;          // bins whose primary 1.5*2^q overflows a float ...
 constexpr int ADN_SCALE_SHIFT = 40;         // ... are stored scaled by 2^-40
 constexpr int ADN_RENORM = 512;             // 2^(24 - 13 - 2) deposits between renormalisations
-constexpr int ADN_REC = 44;                 // 32-bit words per accumulator record (2K + 2 <= 44)
-constexpr int ADN_WAVES = 4;                // waves per workgroup
-constexpr int ADN_MAX_BLOCKS = 8192;
-constexpr int ADN_GROUP = 64;               // workgroups per first-level ticket
-constexpr int ADN_COUNTER_STRIDE = 64;      // counters 256 bytes apart
-constexpr size_t ADN_WS_HEADER = 256 * (1 + ADN_MAX_BLOCKS / ADN_GROUP);
+using svx::ADN_REC;             // 32-bit words per accumulator record
+using svx::ADN_WAVES;           // waves per workgroup
+using svx::ADN_MAX_BLOCKS;
+using svx::ADN_GROUP;           // workgroups per first-level ticket
+using svx::ADN_COUNTER_STRIDE;  // counters 256 bytes apart
+constexpr size_t ADN_WS_HEADER = (size_t)svx::ADN_WS_HEADER;
 static_assert(ADN_WS_HEADER == SV_ADN_SUM_COUNTER_BYTES, "header constant");
 static_assert(2 * SV_ADN_MAX_FOLD + 2 <= ADN_REC, "record size");
 static_assert(ADN_MAX_BLOCKS / ADN_GROUP == 128, "two group records per lane");
@@ -324,14 +325,14 @@ __device__ __forceinline__ void adn_load(const float *__restrict__ x, int64_t n,
   if (base + 64 * E <= n) {  // wave-uniform: the whole chunk is inside, no per-lane checks
 #pragma unroll
     for (int j = 0; j < (VEC ? E / 4 : 0); ++j) {
-      const float4 g = sv::ld4<true>(x + base + 4 * (lane + 64 * j));
+      const float4 g = sv::ld4<true>(x + svx::adn_index(base, lane, j, 0, true));
       v[4 * j] = g.x;
       v[4 * j + 1] = g.y;
       v[4 * j + 2] = g.z;
       v[4 * j + 3] = g.w;
     }
 #pragma unroll
-    for (int i = 0; i < (VEC ? 0 : E); ++i) v[i] = sv::ld1<true>(x + base + lane + 64 * i);
+    for (int i = 0; i < (VEC ? 0 : E); ++i) v[i] = sv::ld1<true>(x + svx::adn_index(base, lane, i / 4, i % 4, false));
     return;
   }
   // the last, ragged chunk: element by element, zeros past n
@@ -339,7 +340,7 @@ __device__ __forceinline__ void adn_load(const float *__restrict__ x, int64_t n,
   for (int j = 0; j < E / 4; ++j) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int64_t i = VEC ? base + 4 * (lane + 64 * j) + t : base + lane + 64 * (4 * j + t);
+      const int64_t i = svx::adn_index(base, lane, j, t, VEC);
       v[4 * j + t] = i < n ? x[i] : 0.0f;
     }
   }

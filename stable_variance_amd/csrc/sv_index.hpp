@@ -427,4 +427,35 @@ constexpr ColsChunkPlan cols_chunk64_plan(int V, int64_t R, int64_t C) {
   return {g, (R + ch - 1) / ch, (C + nc - 1) / nc};
 }
 
+// ---------------------------------------------------------------- ADN sum
+
+constexpr int ADN_REC = 44;              // 32-bit words per accumulator record (2K + 2 <= 44)
+constexpr int ADN_WAVES = 4;             // waves per workgroup
+constexpr int ADN_MAX_BLOCKS = 8192;
+constexpr int ADN_GROUP = 64;            // workgroups per first-level ticket
+constexpr int ADN_COUNTER_STRIDE = 64;   // counters 256 bytes apart (32-bit words)
+// The counter header (the top counter, then one per group of ADN_GROUP
+// workgroups), then ADN_MAX_BLOCKS workgroup records and one record per group.
+constexpr int64_t ADN_WS_HEADER = 256 * (1 + ADN_MAX_BLOCKS / ADN_GROUP);
+
+// The ADN sum's launch over n values: chunks of 64*e values, g consecutive
+// chunks per wave, `blocks` workgroups of ADN_WAVES waves, at most
+// target_blocks (<= ADN_MAX_BLOCKS).
+struct AdnPlan {
+  int64_t chunks, g, blocks;
+};
+constexpr AdnPlan adn_plan(int64_t n, int e, int64_t target_blocks) {
+  const int64_t chunks = (n + 64LL * e - 1) / (64LL * e);
+  const int64_t waves_target = ADN_WAVES * target_blocks;
+  const int64_t g = (chunks + waves_target - 1) / waves_target;
+  const int64_t waves = (chunks + g - 1) / g;
+  return {chunks, g, (waves + ADN_WAVES - 1) / ADN_WAVES};
+}
+// Value t (0..3) of group j of a lane's E values in the chunk at `base`:
+// 16-byte loads (vec) give lane l the values 4(l + 64j) .. 4(l + 64j) + 3,
+// single loads the values l + 64(4j + t).
+constexpr int64_t adn_index(int64_t base, int lane, int j, int t, bool vec) {
+  return vec ? base + 4 * (lane + 64 * j) + t : base + lane + 64 * (4 * j + t);
+}
+
 }  // namespace svx

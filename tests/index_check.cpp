@@ -19,6 +19,7 @@
 #include <string>
 #include <vector>
 
+#include "../include/stable_variance.h"
 #include "../stable_variance_amd/csrc/sv_index.hpp"
 
 using namespace svx;
@@ -622,6 +623,60 @@ void tree_sum(int64_t n, int e, int64_t target, bool vec, int loadp, bool xcd) {
   }
 }
 
+// ------------------------------------------------------------------ ADN sum
+
+// k_adn_sum<K, E, VEC>: wave w of workgroup b streams chunks [c0, c1) of
+// 64*e values (a whole chunk with e/4 16-byte loads or e single loads per
+// lane, the ragged last one value by value below n); then the workgroup's
+// record, its group's counter and record, and the top counter, all inside
+// the workspace the size function gives (in 32-bit words).
+void adn_sum(int64_t n, int e, int64_t target, bool vec) {
+  if (n == 0) return;
+  const AdnPlan p = adn_plan(n, e, target);
+  const Where c{"adn sum", 1, n, n};
+  launch(c, p.blocks, 64 * ADN_WAVES);
+  if (p.blocks > target || p.blocks > ADN_MAX_BLOCKS) report(c, "blocks above the target", p.blocks, target, -1, -1);
+  const int64_t ngroups = (p.blocks + ADN_GROUP - 1) / ADN_GROUP;
+  if (ngroups > 128) report(c, "group records beyond two per lane", ngroups, 128, -1, -1);
+  const int64_t header_words = ADN_WS_HEADER / 4, rec_words = (int64_t)ADN_MAX_BLOCKS * ADN_REC;
+  const Where ws{"adn workspace", 1, header_words + rec_words + (ADN_MAX_BLOCKS / ADN_GROUP) * ADN_REC,
+                 header_words + rec_words + (ADN_MAX_BLOCKS / ADN_GROUP) * ADN_REC};
+  const int64_t size = 64LL * e;
+  for (int64_t b : visit(p.blocks)) {
+    const int64_t grp = b / ADN_GROUP;
+    load(ws, header_words + b * ADN_REC, ADN_REC, b, 0);                        // the workgroup's record
+    load(ws, (int64_t)ADN_COUNTER_STRIDE * (1 + grp), 1, b, 0);                 // its group's counter
+    if (ADN_COUNTER_STRIDE * (1 + grp) >= header_words) report(ws, "group counter past the header", grp, 0, b, 0);
+    load(ws, header_words + rec_words + grp * ADN_REC, ADN_REC, b, 0);          // its group's record
+    for (int lane = 0; lane < 64; ++lane) {
+      const int64_t idx = grp * ADN_GROUP + lane;  // the group's last workgroup reads these records
+      if (idx < p.blocks) load(ws, header_words + idx * ADN_REC, ADN_REC, b, lane);
+      for (int k = 0; k < 2; ++k)
+        if (2 * lane + k < ngroups) load(ws, header_words + rec_words + (2 * lane + k) * ADN_REC, ADN_REC, b, lane);
+    }
+    for (int w = 0; w < ADN_WAVES; ++w) {
+      const int64_t c0 = (b * ADN_WAVES + w) * p.g, c1 = std::min(c0 + p.g, p.chunks);
+      for (int64_t ch = c0; ch < c1; ++ch) {
+        if (c1 - c0 > 8 && ch == c0 + 4) ch = c1 - 4;  // long runs: the first and last chunks
+        const int64_t base = ch * size;
+        const bool whole = base + size <= n;
+        for (int lane = 0; lane < 64; ++lane)
+          for (int j = 0; j < e / 4; ++j) {
+            if (whole && vec) {
+              load(c, adn_index(base, lane, j, 0, true), 4, b, lane);
+              continue;
+            }
+            for (int t = 0; t < 4; ++t) {
+              const int64_t i = adn_index(base, lane, j, t, vec);
+              if (whole || i < n) load(c, i, 1, b, lane);
+            }
+          }
+      }
+    }
+  }
+  load(ws, 0, 1, -1, 0);  // the top counter
+}
+
 }  // namespace
 
 int main() {
@@ -733,6 +788,14 @@ int main() {
       }
     }
   }
+  // the ADN sum: the default and extreme workgroup targets, both load forms,
+  // sizes around a chunk and up to the accumulator's capacity
+  for (int64_t n : {(int64_t)1, (int64_t)1023, (int64_t)1024, (int64_t)1025, (int64_t)2049, (int64_t)100000000,
+                    (int64_t)100000003, (int64_t)SV_ADN_MAX_COUNT})
+    for (int e : {16, 32})
+      for (int64_t target : {(int64_t)1, (int64_t)7, (int64_t)512, (int64_t)ADN_MAX_BLOCKS})
+        for (bool vec : {true, false}) adn_sum(n, e, target, vec);
+
   // the float64 sum: chunks of 1024 doubles, i.e. the float chunks of 2048
   // of Chunk<32> over the same bytes (the same plan, in floats)
   for (int64_t n : {(int64_t)1, (int64_t)1023, (int64_t)1025, (int64_t)50000000, S64_MAX_N}) {
