@@ -390,6 +390,8 @@ __device__ __forceinline__ void finalize_d(NodeD nd, NodeD nq, double x0, double
 
 // Axis 1: one workgroup per row, W waves own consecutive 64*E ranges, each
 // lane E consecutive doubles; the row stays in registers between passes.
+// The launch holds only the waves the row reaches (svx::rows_waves); the
+// tree's other wave nodes are (+0, +0).
 template <int E, int W, bool VEC>
 __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restrict__ x, int64_t n, int64_t ld,
                                                          int64_t ddof, double *__restrict__ var_out,
@@ -425,18 +427,19 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
 
   NodeD ny = {0.0, 0.0};
   if (!empty) ny = wave_tree_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
+  const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));  // the waves launched
   // From four waves on, the tree over the wave nodes takes one node per lane
   // (lane l < W wave l's) and the first log2(W) cross-lane levels.
   if constexpr (W > 1) {
     if (lane == 0) slots[0][w] = ny;
     __syncthreads();
     if constexpr (W >= 4) {
-      const NodeD t = seg_tree_d<KD_PLAIN, W>(lane < W ? slots[0][lane] : NodeD{0.0, 0.0});
+      const NodeD t = seg_tree_d<KD_PLAIN, W>(lane < nw ? slots[0][lane] : NodeD{0.0, 0.0});
       ny = {readlane_d(t.s, 0), readlane_d(t.c, 0)};
     } else {
       NodeD t[W];
 #pragma unroll
-      for (int i = 0; i < W; ++i) t[i] = slots[0][i];
+      for (int i = 0; i < W; ++i) t[i] = i < nw ? slots[0][i] : NodeD{0.0, 0.0};
       ny = node_tree_d<0, W, W, KD_PLAIN>(t);
     }
   }
@@ -460,7 +463,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
       // tree takes the TwoSum node, whose error on non-negative operands is
       // the same exact value as the Fast2Sum form's
       if (w != 0) return;
-      const NodeD t = seg_tree_d<false, W>(lane < 2 * W ? (&slots[1][0])[lane] : NodeD{0.0, 0.0});
+      const NodeD t =
+          seg_tree_d<false, W>(lane < 2 * W && (lane & (W - 1)) < nw ? (&slots[1][0])[lane] : NodeD{0.0, 0.0});
       nd = {readlane_d(t.s, 0), readlane_d(t.c, 0)};
       nq = {readlane_d(t.s, W), readlane_d(t.c, W)};
     } else {
@@ -468,8 +472,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
       NodeD td[W], tq[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        td[i] = slots[1][i];
-        tq[i] = slots[2][i];
+        td[i] = i < nw ? slots[1][i] : NodeD{0.0, 0.0};
+        tq[i] = i < nw ? slots[2][i] : NodeD{0.0, 0.0};
       }
       nd = node_tree_d<0, W, W, false>(td);
       nq = node_tree_d<0, W, W, true>(tq);
@@ -1469,11 +1473,12 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     }
     case svx::Route64::ROWS_TILE: {
 #define SV_ROWS64(E, W)                                                                                      \
-  svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {                                             \
+  svh::in_batches(rows, 1, 64 * svx::rows_waves(n, E, W), [&](int64_t r0, int64_t nr) {                     \
     const double *xr = x + r0 * cols;                                                                        \
     double *mr = mean_out ? mean_out + r0 : nullptr;                                                         \
-    if (vec) k_var_rows_f64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr); \
-    else k_var_rows_f64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(xr, n, cols, ddof, var_out + r0, mr);   \
+    const dim3 block(64 * svx::rows_waves(n, E, W));  /* only the waves the row reaches */                  \
+    if (vec) k_var_rows_f64<E, W, true><<<dim3((unsigned)nr), block, 0, st>>>(xr, n, cols, ddof, var_out + r0, mr); \
+    else k_var_rows_f64<E, W, false><<<dim3((unsigned)nr), block, 0, st>>>(xr, n, cols, ddof, var_out + r0, mr);   \
   })
       const svx::RowsPlan rp = svx::rows64_plan(n);
       switch (rp.E * 100 + rp.W) {

@@ -431,7 +431,8 @@ __global__ __launch_bounds__(256) void k_split_rows(const float *__restrict__ z,
 // its real and imaginary parts; the two float32 variances run side by side
 // with the same tree topology as k_var_rows, and var = fl(var(re) +
 // var(im)), mean = (mean(re), mean(im)).  W waves own consecutive 64*E
-// ranges; a wave wholly past the row skips its trees (its nodes are +0).
+// ranges; the launch holds only the waves the row reaches (svx::rows_waves),
+// the tree's other wave nodes are +0.
 template <int E, int W, bool VEC>
 __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict__ z, int64_t n, int64_t ddof,
                                                          float *__restrict__ var_out, float *__restrict__ mean_out) {
@@ -463,14 +464,16 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
   // The tree over the waves' nodes: lane l < W takes wave l's real node,
   // lane W + l its imaginary node, and the first log2(W) cross-lane levels
   // pair them in tree order (one node per lane instead of all W in every
-  // lane's registers).
+  // lane's registers); waves not launched give zero nodes.
+  const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
+  const bool launched = (lane & (W - 1)) < nw;
   if constexpr (W > 1) {
     if (lane == 0) {
       slots[0][w] = yr;
       slots[1][w] = yi;
     }
     __syncthreads();
-    const Node t = sv::seg_tree<sv::Y_KIND, W>(lane < 2 * W ? (&slots[0][0])[lane] : sv::zero_node());
+    const Node t = sv::seg_tree<sv::Y_KIND, W>(lane < 2 * W && launched ? (&slots[0][0])[lane] : sv::zero_node());
     yr = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
     yi = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
   }
@@ -504,7 +507,8 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
     }
     __syncthreads();
     if (w != 0) return;
-    const Node t = sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 4 * W ? (&slots[2][0])[lane] : sv::zero_node());
+    const Node t =
+        sv::seg_tree<sv::NODE_TWOSUM, W>(lane < 4 * W && launched ? (&slots[2][0])[lane] : sv::zero_node());
     dr = {sv::readlane_f(t.s, 0), sv::readlane_f(t.c, 0)};
     qr = {sv::readlane_f(t.s, W), sv::readlane_f(t.c, W)};
     di = {sv::readlane_f(t.s, 2 * W), sv::readlane_f(t.c, 2 * W)};
@@ -2780,11 +2784,12 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
     // rows start 16-byte aligned when z is and cols is even
     const bool vec = aligned16(z) && (cols % 2 == 0);
 #define SV_ROWS_C64(E, W)                                                                                 \
-  svh::in_batches(rows, 1, 64 * W, [&](int64_t r0, int64_t nr) {                                        \
+  svh::in_batches(rows, 1, 64 * svx::rows_waves(cols, E, W), [&](int64_t r0, int64_t nr) {             \
     const float *zr = z + 2 * r0 * cols;                                                                \
     float *mr = mean_out ? mean_out + 2 * r0 : nullptr;                                                 \
-    if (vec) k_var_rows_c64<E, W, true><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr); \
-    else k_var_rows_c64<E, W, false><<<dim3((unsigned)nr), dim3(64 * W), 0, st>>>(zr, cols, ddof, var_out + r0, mr);   \
+    const dim3 block(64 * svx::rows_waves(cols, E, W));  /* only the waves the row reaches */          \
+    if (vec) k_var_rows_c64<E, W, true><<<dim3((unsigned)nr), block, 0, st>>>(zr, cols, ddof, var_out + r0, mr); \
+    else k_var_rows_c64<E, W, false><<<dim3((unsigned)nr), block, 0, st>>>(zr, cols, ddof, var_out + r0, mr);   \
   })
     if (cols <= SEG_MAX_N && g_tune.var_short_rows) {
       const int vw2 = vec ? 2 : 1;

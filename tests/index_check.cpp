@@ -208,11 +208,12 @@ void rows_seg(const Where &c, int64_t rows, int64_t n, int vw, int cplx) {
 // k_var_rows_c64: rows of n complex values, load_tile over 2*E floats.
 void rows_c64(const Where &c, int64_t rows, int64_t n, bool vec) {
   const RowsPlan p = c64_rows_plan(n);
-  batches(rows, 1, 64 * p.W, [&](int64_t r0, int64_t nr) {
-    launch(c, nr, 64 * p.W);
+  const int waves = rows_waves(n, p.E, p.W);  // only the waves the row reaches
+  batches(rows, 1, 64 * waves, [&](int64_t r0, int64_t nr) {
+    launch(c, nr, 64 * waves);
     for (int64_t b : visit(nr)) {
       const int64_t pr = 2 * (r0 + b) * n;
-      for (int w = 0; w < p.W; ++w) {
+      for (int w = 0; w < waves; ++w) {
         const int64_t base = (int64_t)w * 64 * p.E;
         for (int lane = 0; lane < 64; ++lane) {
           tile_loads(2 * p.E, vec, 1, 2 * (n - base), 2 * rows_avail(nr, b, n, n, base), lane,
@@ -492,11 +493,12 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
     case Route64::ROWS_SEG: rows_seg(c, rows, n, vec ? 2 : 1, 1); break;
     case Route64::ROWS_TILE: {
       const RowsPlan p = rows64_plan(n);
-      batches(rows, 1, 64 * p.W, [&](int64_t r0, int64_t nr) {
-        launch(c, nr, 64 * p.W);
+      const int waves = rows_waves(n, p.E, p.W);  // only the waves the row reaches
+      batches(rows, 1, 64 * waves, [&](int64_t r0, int64_t nr) {
+        launch(c, nr, 64 * waves);
         for (int64_t b : visit(nr)) {
           const int64_t pr = (r0 + b) * cols;
-          for (int w = 0; w < p.W; ++w) {
+          for (int w = 0; w < waves; ++w) {
             const int64_t base = (int64_t)w * 64 * p.E;
             for (int lane = 0; lane < 64; ++lane) {
               tile_loads(2 * p.E, vec, 1, 2 * (n - base), 2 * rows_avail(nr, b, cols, n, base), lane,
