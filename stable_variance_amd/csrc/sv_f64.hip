@@ -388,6 +388,40 @@ __device__ __forceinline__ void finalize_d(NodeD nd, NodeD nq, double x0, double
   if (mean_out) *mean_out = x0 + m;
 }
 
+// Per-call constants of the divisions by fl(n) and the ddof factor, formed
+// on the host: when fl(n) is a power of two, x / fl(n) and x * rn with
+// rn = 1 / fl(n) (exact) are the same rounding of the same real number.
+struct StepConstsD {
+  double fn;    // fl(n)
+  double rn;    // 1 / fl(n) when fl(n) is a power of two, else 0 (divide)
+  double dfac;  // fl(n) / fl(max(n - ddof, 0)), correctly rounded (unused when ddof == 0)
+  int ddof_on;
+};
+
+StepConstsD step_consts_d(int64_t n, int64_t ddof) {
+  StepConstsD k;
+  k.fn = (double)n;
+  int ex = 0;
+  k.rn = (n > 0 && frexp(k.fn, &ex) == 0.5) ? 1.0 / k.fn : 0.0;
+  k.ddof_on = ddof != 0;
+  const int64_t den = n - ddof < 0 ? 0 : n - ddof;
+  k.dfac = ddof != 0 ? k.fn / (double)den : 1.0;
+  return k;
+}
+
+__device__ __forceinline__ double div_n_d(double a, const StepConstsD &k) { return k.rn != 0.0 ? a * k.rn : a / k.fn; }
+
+// finalize_d with the per-call constants (the same results).
+__device__ __forceinline__ void finalize_dk(NodeD nd, NodeD nq, double x0, double m, const StepConstsD &k,
+                                            double *var_out, double *mean_out) {
+  const double a = div_n_d(root_value_d(nq), k);
+  const double b = div_n_d(root_value_d(nd), k);
+  double v = max0_nan_d(a - b * b);
+  if (k.ddof_on) v = v * k.dfac;
+  *var_out = v;
+  if (mean_out) *mean_out = x0 + m;
+}
+
 // Axis 1: one workgroup per row, W waves own consecutive 64*E ranges, each
 // lane E consecutive doubles; the row stays in registers between passes.
 // The launch holds only the waves the row reaches (svx::rows_waves); the
@@ -489,7 +523,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
 // an even count), else single doubles; every load issued, clamped, masked.
 template <int E, int S, int VW>
 __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict__ x, int64_t rows, int64_t n,
-                                                        int64_t ld, int64_t ddof, double *__restrict__ var_out,
+                                                        int64_t ld, StepConstsD k, double *__restrict__ var_out,
                                                         double *__restrict__ mean_out) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -521,13 +555,13 @@ __global__ __launch_bounds__(256) void k_var_rows_seg_d(const double *__restrict
 #pragma unroll
   for (int i = 0; i < E; ++i) v[i] = (full || i < valid) ? v[i] - x0 : 0.0;
   const NodeD ny = seg_tree_d<KD_PLAIN, S>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
-  const double m = root_value_kd<KD_PLAIN>(ny) / (double)n;
+  const double m = div_n_d(root_value_kd<KD_PLAIN>(ny), k);
   NodeD nd, nq;
   if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
   else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
   nd = seg_tree_d<false, S>(nd);
   nq = seg_tree_d<true, S>(nq);
-  if (l == 0 && rowok) finalize_d(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+  if (l == 0 && rowok) finalize_dk(nd, nq, x0, m, k, var_out + row, mean_out ? mean_out + row : nullptr);
 }
 
 // Axis 0: lanes own columns (a row of 64 consecutive doubles per load), the
@@ -1449,13 +1483,14 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
     case svx::Route64::ROWS_SEG: {
       // rows of up to 512 doubles sharing waves: 16-byte loads of two
       // doubles for aligned rows of an even count, else single doubles
+      const StepConstsD sk = step_consts_d(n, ddof);
 #define SV_SEG64(E, S)                                                                                  \
   svh::in_batches(rows, 4 * (64 / S), 256, [&](int64_t r0, int64_t nr) {                                \
     const dim3 sgrid((unsigned)((nr + 4 * (64 / S) - 1) / (4 * (64 / S))));                             \
     const double *xr = x + r0 * cols;                                                                   \
     double *vr = var_out + r0, *mr = mean_out ? mean_out + r0 : nullptr;                                \
-    if (vec) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr);     \
-    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, ddof, vr, mr);         \
+    if (vec) k_var_rows_seg_d<E, S, 2><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, sk, vr, mr);       \
+    else k_var_rows_seg_d<E, S, 1><<<sgrid, dim3(256), 0, st>>>(xr, nr, n, cols, sk, vr, mr);           \
   })
       const svx::SegPlan sp = svx::seg_plan(n);
       switch (sp.E * 100 + sp.S) {

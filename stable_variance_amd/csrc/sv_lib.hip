@@ -212,6 +212,35 @@ __device__ __forceinline__ void finalize(Node nd, Node nq, float x0, float m, in
   if (mean_out) *mean_out = x0 + m;
 }
 
+// Per-call constants of step 2 and step 4, formed on the host.  When fl(n)
+// is a power of two, x / fl(n) and x * rn with rn = 1 / fl(n) (exact) are the
+// same rounding of the same real number, so the kernels multiply; dfac is
+// the ddof factor fl(fl(n) / fl(max(n - ddof, 0))), a correctly rounded
+// division on the host as it would be on the device.
+struct StepConsts {
+  float fn;    // fl(n)
+  float rn;    // 1 / fl(n) when fl(n) is a power of two, else 0 (divide)
+  float dfac;  // the ddof factor (unused when ddof == 0)
+  int ddof_on; // ddof != 0
+};
+
+__device__ __forceinline__ float div_n(float a, const StepConsts &k) { return k.rn != 0.0f ? a * k.rn : a / k.fn; }
+
+// Step 4 from the roots of the d and d^2 trees: the two-term correction,
+// the NaN-propagating max with 0, the ddof rescale and the mean x0 + m.
+__device__ __forceinline__ void finalize_k(Node nd, Node nq, float x0, float m, const StepConsts &k, float *var_out,
+                                           float *mean_out) {
+  const float a = div_n(sv::root_value(nq), k);
+  const float b = div_n(sv::root_value(nd), k);
+  const float bb = b * b;
+  float v = a - bb;
+  v = (v != v) ? v : ((v > 0.0f) ? v : 0.0f);
+  if (k.ddof_on) v = v * k.dfac;
+  *var_out = v;
+  if (mean_out) *mean_out = x0 + m;
+}
+
+
 __device__ __forceinline__ void store_node_agent(Node *dst, Node v) {
   sv::store_u32_agent(reinterpret_cast<unsigned *>(&dst->s), __builtin_bit_cast(unsigned, v.s));
   sv::store_u32_agent(reinterpret_cast<unsigned *>(&dst->c), __builtin_bit_cast(unsigned, v.c));
@@ -534,7 +563,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_c64(const float *__restrict
 // masked.
 template <int E, int S, int VW2>
 __global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restrict__ z, int64_t rows, int64_t n,
-                                                          int64_t ddof, float *__restrict__ var_out,
+                                                          StepConsts k, float *__restrict__ var_out,
                                                           float *__restrict__ mean_out) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -570,8 +599,8 @@ __global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restric
   }
   const Node yr = sv::seg_tree<sv::Y_KIND, S>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(re));
   const Node yi = sv::seg_tree<sv::Y_KIND, S>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(im));
-  const float mr = sv::root_value_k<sv::Y_KIND>(yr) / (float)n;
-  const float mi = sv::root_value_k<sv::Y_KIND>(yi) / (float)n;
+  const float mr = div_n(sv::root_value_k<sv::Y_KIND>(yr), k);
+  const float mi = div_n(sv::root_value_k<sv::Y_KIND>(yi), k);
   Node dr, qr, di, qi;
   if (full) {
     sv::lane_tree_dq<false, 0, E, E>(re, mr, E, dr, qr);
@@ -586,8 +615,8 @@ __global__ __launch_bounds__(256) void k_var_rows_c64_seg(const float *__restric
   qi = sv::seg_tree<sv::NODE_NN, S>(qi);
   if (l == 0 && rowok) {
     float vr, vi, mean_r, mean_i;
-    finalize(dr, qr, x0r, mr, n, ddof, &vr, &mean_r);
-    finalize(di, qi, x0i, mi, n, ddof, &vi, &mean_i);
+    finalize_k(dr, qr, x0r, mr, k, &vr, &mean_r);
+    finalize_k(di, qi, x0i, mi, k, &vi, &mean_i);
     var_out[row] = vr + vi;
     if (mean_out) {
       mean_out[2 * row] = mean_r;
@@ -633,34 +662,6 @@ __global__ void k_fill(float *__restrict__ out, int64_t count, float value) {
 }
 
 // ------------------------------------------------------------------ variance, axis 1
-
-// Per-call constants of step 2 and step 4, formed on the host.  When fl(n)
-// is a power of two, x / fl(n) and x * rn with rn = 1 / fl(n) (exact) are the
-// same rounding of the same real number, so the kernels multiply; dfac is
-// the ddof factor fl(fl(n) / fl(max(n - ddof, 0))), a correctly rounded
-// division on the host as it would be on the device.
-struct StepConsts {
-  float fn;    // fl(n)
-  float rn;    // 1 / fl(n) when fl(n) is a power of two, else 0 (divide)
-  float dfac;  // the ddof factor (unused when ddof == 0)
-  int ddof_on; // ddof != 0
-};
-
-__device__ __forceinline__ float div_n(float a, const StepConsts &k) { return k.rn != 0.0f ? a * k.rn : a / k.fn; }
-
-// Step 4 from the roots of the d and d^2 trees: the two-term correction,
-// the NaN-propagating max with 0, the ddof rescale and the mean x0 + m.
-__device__ __forceinline__ void finalize_k(Node nd, Node nq, float x0, float m, const StepConsts &k, float *var_out,
-                                           float *mean_out) {
-  const float a = div_n(sv::root_value(nq), k);
-  const float b = div_n(sv::root_value(nd), k);
-  const float bb = b * b;
-  float v = a - bb;
-  v = (v != v) ? v : ((v > 0.0f) ? v : 0.0f);
-  if (k.ddof_on) v = v * k.dfac;
-  *var_out = v;
-  if (mean_out) *mean_out = x0 + m;
-}
 
 // Axis 1, rows that fill their power-of-two tile exactly (n = 64*E*W) and
 // start 16 bytes aligned: every wave is full, so there are no masks, clamped
@@ -857,9 +858,13 @@ __global__ __launch_bounds__(64 * W) void k_var_rows(const float *__restrict__ x
 // idles on a row much shorter than the wave.  The row's tree is the in-lane
 // levels and then the first log2(S) cross-lane levels (S*E is a power of two
 // >= n; the values past n are +0).  Four waves per workgroup, independent.
+// The divisions by fl(n) and the ddof factor come from the per-call
+// constants (k): multiplies by the exact reciprocal when fl(n) is a power of
+// two, where a row of a few values would otherwise spend most of its
+// instructions in division sequences.
 template <int E, int S, int VW>
 __global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ x, int64_t rows, int64_t n,
-                                                      int64_t ld, int64_t ddof, float *__restrict__ var_out,
+                                                      int64_t ld, StepConsts k, float *__restrict__ var_out,
                                                       float *__restrict__ mean_out) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -906,13 +911,13 @@ __global__ __launch_bounds__(256) void k_var_rows_seg(const float *__restrict__ 
     for (int i = 0; i < E; ++i) v[i] = (i < valid) ? v[i] - x0 : 0.0f;
   }
   Node ny = sv::seg_tree<sv::Y_KIND, S>(sv::lane_tree<sv::Y_LEAF, 0, E, E>(v));
-  const float m = sv::root_value_k<sv::Y_KIND>(ny) / (float)n;
+  const float m = div_n(sv::root_value_k<sv::Y_KIND>(ny), k);
   Node nd, nq;
   if (full) sv::lane_tree_dq<false, 0, E, E>(v, m, E, nd, nq);
   else sv::lane_tree_dq<true, 0, E, E>(v, m, valid, nd, nq);
   nd = sv::seg_tree<sv::NODE_TWOSUM, S>(nd);
   nq = sv::seg_tree<sv::NODE_NN, S>(nq);
-  if (l == 0 && rowok) finalize(nd, nq, x0, m, n, ddof, var_out + row, mean_out ? mean_out + row : nullptr);
+  if (l == 0 && rowok) finalize_k(nd, nq, x0, m, k, var_out + row, mean_out ? mean_out + row : nullptr);
 }
 
 // ------------------------------------------------------------------ variance, axis 0
@@ -1924,13 +1929,14 @@ template <int E, int S>
 void launch_seg_t(int vw, const float *x, int64_t rows, int64_t n, int64_t ld, int64_t ddof, float *var,
                   float *mean, hipStream_t st) {
   constexpr int RPB = 4 * (64 / S);  // rows per workgroup
+  const StepConsts k = step_consts(n, ddof);
   svh::in_batches(rows, RPB, 256, [&](int64_t r0, int64_t nr) {
     const dim3 grid((unsigned)((nr + RPB - 1) / RPB)), block(256);
     const float *xr = x + r0 * ld;
     float *vr = var + r0, *mr = mean ? mean + r0 : nullptr;
-    if (vw == 4) k_var_rows_seg<E, S, 4><<<grid, block, 0, st>>>(xr, nr, n, ld, ddof, vr, mr);
-    else if (vw == 2) k_var_rows_seg<E, S, 2><<<grid, block, 0, st>>>(xr, nr, n, ld, ddof, vr, mr);
-    else k_var_rows_seg<E, S, 1><<<grid, block, 0, st>>>(xr, nr, n, ld, ddof, vr, mr);
+    if (vw == 4) k_var_rows_seg<E, S, 4><<<grid, block, 0, st>>>(xr, nr, n, ld, k, vr, mr);
+    else if (vw == 2) k_var_rows_seg<E, S, 2><<<grid, block, 0, st>>>(xr, nr, n, ld, k, vr, mr);
+    else k_var_rows_seg<E, S, 1><<<grid, block, 0, st>>>(xr, nr, n, ld, k, vr, mr);
   });
 }
 
@@ -2793,13 +2799,14 @@ sv_status sv_variance_c64(const float *z, int64_t rows, int64_t cols, int axis, 
   })
     if (cols <= SEG_MAX_N && g_tune.var_short_rows) {
       const int vw2 = vec ? 2 : 1;
+      const StepConsts sk = step_consts(cols, ddof);
 #define SV_SEG_C64(E, S)                                                                                \
   svh::in_batches(rows, 4 * (64 / S), 256, [&](int64_t r0, int64_t nr) {                                \
     const dim3 sgrid((unsigned)((nr + 4 * (64 / S) - 1) / (4 * (64 / S))));                             \
     const float *zr = z + 2 * r0 * cols;                                                                \
     float *vr = var_out + r0, *mr = mean_out ? mean_out + 2 * r0 : nullptr;                             \
-    if (vw2 == 2) k_var_rows_c64_seg<E, S, 2><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, ddof, vr, mr); \
-    else k_var_rows_c64_seg<E, S, 1><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, ddof, vr, mr);         \
+    if (vw2 == 2) k_var_rows_c64_seg<E, S, 2><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, sk, vr, mr);   \
+    else k_var_rows_c64_seg<E, S, 1><<<sgrid, dim3(256), 0, st>>>(zr, nr, cols, sk, vr, mr);           \
   })
       const svx::SegPlan sp = svx::seg_plan(cols);
       switch (sp.E * 100 + sp.S) {
