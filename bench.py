@@ -508,6 +508,13 @@ def main():
                                                         var64.data_ptr(), mean64.data_ptr(), None, 0, sh)), reps=40)
     read64_ms = time_op(lambda i: check(L.sv_probe_read_bandwidth(c5d[i % 2].data_ptr(), 2 * SUM_N,
                                                                    probe_out.data_ptr(), sh)), reps=20)
+    # along axis 0: columns of 4096 doubles read once
+    var64c = torch.empty(VAR_COLS, dtype=torch.float64, device=dev)
+    ws64c_n = max(1, L.sv_variance_f64_workspace_size(VAR_ROWS, VAR_COLS, 0))
+    ws64c = torch.zeros(ws64c_n, dtype=torch.uint8, device=dev)
+    var64c_ms = time_op(lambda i: check(L.sv_variance_f64(c4d[i % 4].data_ptr(), VAR_ROWS, VAR_COLS, 0, 0,
+                                                         var64c.data_ptr(), None, ws64c.data_ptr(), ws64c_n, sh)),
+                        reps=40)
     top = torch.full((1, 3), 1e307, dtype=torch.float64, device=dev)
     top_var = torch.empty(1, dtype=torch.float64, device=dev)
     check(L.sv_variance_f64(top.data_ptr(), 1, 3, 1, 0, top_var.data_ptr(), None, None, 0, sh))
@@ -518,6 +525,10 @@ def main():
            "variance_4096x4096": {"avg_launch_ms": round(var64_ms, 5),
                                   "gb_s": round(8 * VAR_ROWS * VAR_COLS / (var64_ms * 1e-3) / 1e9, 1),
                                   "hbm_frac": round(8 * VAR_ROWS * VAR_COLS / (var64_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "variance_4096x4096_axis0": {"avg_launch_ms": round(var64c_ms, 5),
+                                        "gb_s": round(8 * VAR_ROWS * VAR_COLS / (var64c_ms * 1e-3) / 1e9, 1),
+                                        "hbm_frac": round(8 * VAR_ROWS * VAR_COLS / (var64c_ms * 1e-3) / 1e9 /
+                                                          HBM_PEAK_GBS, 4)},
            "variance_of_1e307_x3": float(top_var.item()), "bit_exact": None}
     if not args.no_cpu_baseline:
         check(L.sv_tree_sum_f64(c5d[0].data_ptr(), SUM_N, out64.data_ptr(), ws64.data_ptr(), need64, sh))
@@ -531,6 +542,39 @@ def main():
                 np.array_equal(mean64.cpu().numpy()[rows].view(np.uint64), om64.view(np.uint64)))
         f64["bit_exact"] = bool(ok64)
     del c5d, c4d
+
+    # complex64: pairs of the [4096, 4096] float32 buffers as (re, im), two
+    # 134 MB copies, along axis 1 (one pass, parts split in registers) and
+    # axis 0 (the interleaved array as float32 [4096, 8192], then the pair add)
+    zs = [torch.complex(c4[2 * k], c4[2 * k + 1]).contiguous() for k in range(2)]
+    zvar = torch.empty(VAR_COLS, dtype=torch.float32, device=dev)
+    zmean = torch.empty(2 * VAR_COLS, dtype=torch.float32, device=dev)
+    zws = {ax: max(1, L.sv_variance_c64_workspace_size(VAR_ROWS, VAR_COLS, ax)) for ax in (0, 1)}
+    zbuf = {ax: torch.zeros(zws[ax], dtype=torch.uint8, device=dev) for ax in (0, 1)}
+
+    def run_c64(i, ax):
+        check(L.sv_variance_c64(zs[i % 2].data_ptr(), VAR_ROWS, VAR_COLS, ax, 0, zvar.data_ptr(), zmean.data_ptr(),
+                                zbuf[ax].data_ptr(), zws[ax], sh))
+
+    c64 = {}
+    for ax in (1, 0):
+        ms = time_op(lambda i: run_c64(i, ax), reps=40)
+        gbs = 8 * VAR_ROWS * VAR_COLS / (ms * 1e-3) / 1e9
+        torch_ms = time_op(lambda i: torch.var(zs[i % 2], dim=ax, correction=0))
+        c64[f"variance_4096x4096_axis{ax}"] = {"avg_launch_ms": round(ms, 5), "gb_s": round(gbs, 1),
+                                               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                               "torch_var_ms": round(torch_ms, 5)}
+    c64["bit_exact_16_rows"] = None
+    if parity is not None:
+        run_c64(0, 1)
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(2).choice(VAR_ROWS, 16, replace=False)
+        z_host = zs[0][rows].cpu().numpy()
+        ovz, omz = oracle.variance_complex(z_host, axis=1)
+        got_m = zmean.cpu().numpy().view(np.complex64)[rows]
+        c64["bit_exact_16_rows"] = bool(np.array_equal(zvar.cpu().numpy()[rows].view(np.uint32), ovz.view(np.uint32))
+                                        and np.array_equal(got_m.view(np.uint64), omz.view(np.uint64)))
+    del zs
 
     elems = VAR_ROWS * VAR_COLS + SUM_N
     value = elems * K / wall / 1e9
@@ -594,6 +638,7 @@ def main():
                     "ablation_4096x4096": variants},
         "tree_sum_dw_carry": dw,
         "float64_path": f64,
+        "complex64_path": c64,
         "adn_sum": adn,
         "parity": parity,
     }
