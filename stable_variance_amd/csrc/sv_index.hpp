@@ -359,8 +359,13 @@ enum class Route64 {
 };
 // Columns that are candidates for the one-read launch of 1025..4096 rows
 // (var_cols_once: the float32 knob, 0 never, 1 when the grid fills, 2 always).
+// Under knob 1 the column also fills at least 5/8 of its tile (2048 or 4096
+// rows): a tile half padding ([1025, 16384]: 72 against 62 us for the row
+// chunks) holds a CU for half the data.
 constexpr bool cols_one_read64_candidate(bool ax1, int64_t rows, int64_t cols, int var_cols_once) {
-  return !ax1 && rows > V64_COLS_MAX_R && rows <= V64_COLS_ONE_MAX_R && cols >= 2 && var_cols_once != 0;
+  const int64_t tile = rows > 2048 ? 4096 : 2048;
+  return !ax1 && rows > V64_COLS_MAX_R && rows <= V64_COLS_ONE_MAX_R && cols >= 2 && var_cols_once != 0 &&
+         (var_cols_once == 2 || 8 * rows >= 5 * tile);
 }
 // vec16: the matrix starts 16-byte aligned and cols is even.  one_read: the
 // one-read launch is chosen for a candidate (above).  pairs: the float32 knob

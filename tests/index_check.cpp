@@ -548,7 +548,7 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
 // columns (pairs or column chunks).
 void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
   variance_f64_route(rows, cols, axis, off, false, true);
-  if (cols_one_read64_candidate(axis == 1, rows, cols, 1)) variance_f64_route(rows, cols, axis, off, true, true);
+  if (cols_one_read64_candidate(axis == 1, rows, cols, 2)) variance_f64_route(rows, cols, axis, off, true, true);
   if (axis == 0 && cols == 2) variance_f64_route(rows, cols, axis, off, false, false);
 }
 
