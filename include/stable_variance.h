@@ -413,7 +413,9 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    the row-chunk launches; 2 = always the one-read launch.
  *                    The same setting picks the float64 launch of columns of
  *                    1025..4096 rows (at least two columns): eight or four
- *                    whole columns per workgroup of 8 waves, read once
+ *                    whole columns per workgroup of 8 waves, read once (under
+ *                    1, only columns of at least 1280 or 2560 rows, 5/8 of
+ *                    their 2048- or 4096-row tile)
  *   "sum_xcd"        tree sum: 1 = renumber the workgroups so that each of the
  *                    eight dies (XCDs) streams one contiguous region; 0 =
  *                    dispatch order, consecutive regions spread over the dies
