@@ -1044,9 +1044,8 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
 
 // Whole columns in one workgroup (R <= 16*G*W rows): the tile layout of
 // k_cols_y_d with a single chunk, and y, m, d and d^2 in one launch, the tile
-// kept in registers between the two passes.  The launch holds only the waves
-// the column reaches (svx::cols_waves64); the tree's other wave nodes are
-// the +0 padding.
+// kept in registers between the two passes.  Waves wholly past the last row
+// load nothing (their values are the +0 padding).
 template <int V, int W, int G, bool VEC16 = true>
 __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                        int64_t ddof, double *__restrict__ var_out,
@@ -1058,7 +1057,6 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane / G, g = lane % G;
-  const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));  // the waves launched
   // b0: launches of at most 2^32 - 1 work-items.  Blocks of fewer than 16
   // doubles share a 128-byte line with the next block: the blocks of one
   // line run on one die (svx::line_on_one_die, in 4-byte units).
@@ -1084,11 +1082,11 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   }
   __syncthreads();
   // thread t forms m (then step 4) of column V*tq + tk of the block, t = tk*Q + tq
-  for (int t = threadIdx.x; t < NC; t += blockDim.x) {
+  for (int t = threadIdx.x; t < NC; t += 64 * W) {
     const int tk = t / Q, tq = t % Q;
     NodeD nn[W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) nn[i] = i < nw ? sd[i][tk][tq] : NodeD{0.0, 0.0};
+    for (int i = 0; i < W; ++i) nn[i] = sd[i][tk][tq];
     sm[tk][tq] = root_value_kd<KD_PLAIN>(node_tree_d<0, W, W, KD_PLAIN>(nn)) / (double)R;
   }
   __syncthreads();
@@ -1105,15 +1103,15 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
     }
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < NC; t += blockDim.x) {
+  for (int t = threadIdx.x; t < NC; t += 64 * W) {
     const int tk = t / Q, tq = t % Q;
     const int64_t col = cb * NC + (int64_t)tq * V + tk;
     if (col < C) {
       NodeD a[W], b[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
-        a[i] = i < nw ? sd[i][tk][tq] : NodeD{0.0, 0.0};
-        b[i] = i < nw ? sq[i][tk][tq] : NodeD{0.0, 0.0};
+        a[i] = sd[i][tk][tq];
+        b[i] = sq[i][tk][tq];
       }
       finalize_d(node_tree_d<0, W, W, false>(a), node_tree_d<0, W, W, true>(b), x[col], sm[tk][tq], R, ddof,
                  var_out + col, mean_out ? mean_out + col : nullptr);
@@ -1332,9 +1330,9 @@ void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool
                        hipStream_t st) {
   const svx::ColsOne64Plan p = svx::cols_one64_plan(R, C, vec);
 #define SV_ONE64(V_, W_, G_, ...)                                                                         \
-  svh::in_batches(p.blocks, 1, 64 * svx::cols_waves64(R, G_, W_), [&](int64_t b0, int64_t nb) {          \
-    k_cols_one_d<V_, W_, G_, ##__VA_ARGS__><<<dim3((unsigned)nb), dim3(64 * svx::cols_waves64(R, G_, W_)), 0, \
-                                              st>>>(x, R, C, ddof, var, mean, (int)b0);                   \
+  svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                    \
+    k_cols_one_d<V_, W_, G_, ##__VA_ARGS__><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, \
+                                                                                         mean, (int)b0);  \
   })
   if (p.V == 2 && p.G == 32) {
     if (vec) SV_ONE64(2, 8, 32);
@@ -1475,8 +1473,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
                                       : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16, false>));
     int per_cu = 0, cus = 0, dev = 0;
     if (!one_read && hipGetDevice(&dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * svx::cols_waves64(rows, p.G, p.W), 0) ==
-            hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * p.W, 0) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0) {
       const int64_t cap = (int64_t)per_cu * cus, rounds = (p.blocks + cap - 1) / cap;
       one_read = 4 * p.blocks >= 3 * rounds * cap;

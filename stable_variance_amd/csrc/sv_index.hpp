@@ -415,12 +415,6 @@ constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16) {
   const int g = (gw > 16 || (C + 63) / 64 < 512) ? 4 : 1;
   return {1, g, gw / g, (C + 64 / g - 1) / (64 / g)};
 }
-// Waves of a k_cols_one_d launch that R rows reach (L64_E rows per lane, G
-// row groups per wave, at most W waves).
-constexpr int cols_waves64(int64_t R, int G, int W) {
-  const int64_t reach = (R + (int64_t)L64_E * G - 1) / ((int64_t)L64_E * G);
-  return reach < W ? (int)reach : W;
-}
 // Axis 0, a lane per column (up to 64 rows).
 constexpr RowsPlan cols_lane64_plan(int64_t R) {
   if (R <= 4) return {4, 1};

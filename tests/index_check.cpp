@@ -536,7 +536,7 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
     }
     case Route64::COLS_ONE: {
       const ColsOne64Plan p = cols_one64_plan(rows, cols, vec);
-      cols_one(c, rows, cols, p.V, p.W, p.G, vec, L64_E, 0, p.blocks, cols_waves64(rows, p.G, p.W), 2);
+      cols_one(c, rows, cols, p.V, p.W, p.G, vec, L64_E, 0, p.blocks, p.W, 2);
       break;
     }
     case Route64::COLS_SHORT: cols_short(c, rows, cols, 2); break;
