@@ -1486,9 +1486,13 @@ __global__ __launch_bounds__(256) void k_long_rows(const float *__restrict__ x, 
       if (threadIdx.x == 0) ws.ny[out] = ny;
     } else {
       const float m = ws.m[P * r + j];
+      // the step-3 masks are compared afresh from an opaque copy of `valid`:
+      // kept from step 1 (a 64-bit scalar pair per value) they spilled
+      int valid_dq = valid;
+      asm volatile("" : "+v"(valid_dq));
       Node nd, nq;
       if (full) sv::lane_tree_dq<false, 0, EP, EP>(v[j], m, EP, nd, nq);
-      else sv::lane_tree_dq<true, 0, EP, EP>(v[j], m, valid, nd, nq);
+      else sv::lane_tree_dq<true, 0, EP, EP>(v[j], m, valid_dq, nd, nq);
       nd = sv::wave_tree<sv::NODE_TWOSUM>(nd);
       nq = sv::wave_tree<sv::NODE_NN>(nq);
       nd = block_tree<W, sv::NODE_TWOSUM>(nd, slots[2 * j], w, lane);
