@@ -681,7 +681,73 @@ void adn_sum(int64_t n, int e, int64_t target, bool vec) {
 
 }  // namespace
 
+// The route the dispatchers take for shapes whose choice was decided by
+// measurement (the launch geometry, never the result bits, depends on it).
+void route_expectations() {
+  const RouteKnobs k{1, 1, 1024, 1, 1, 1, 1};
+  struct F32 {
+    int64_t R, C;
+    bool ax1, vec16, fills;
+    Route want;
+    const char *why;
+  };
+  const F32 f32[] = {
+      {4096, 4096, true, true, false, Route::ROWS_TILE, "the headline rows"},
+      {300, 50000, true, true, false, Route::ROWS_TILE, "long rows, 256+ of them: one workgroup each"},
+      {100, 200000, true, true, false, Route::LONG_ROWS_CHUNKED, "rows above 65536 values"},
+      {200, 20000, true, true, false, Route::LONG_ROWS_CHUNKED, "long rows, fewer than 256"},
+      {100, 300, true, true, false, Route::ROWS_SEG, "short rows share waves"},
+      {4096, 4096, false, true, true, Route::COLS_ONE_READ, "4096-row columns, the grid fills"},
+      {3000, 4100, false, true, false, Route::COLS_CHUNKED, "the one-read grid would leave the chip idle"},
+      {8000000, 2, false, true, false, Route::COLS_PAIRS, "two long columns: one row of pairs"},
+      {1000, 20000, false, true, false, Route::COLS_ONE4, "16-byte loads, long columns of a wide matrix"},
+      {1000, 20001, false, false, false, Route::COLS_ONE1, "odd width: one column per lane"},
+      {300, 700, false, true, false, Route::COLS_ONE1, "short columns: one column per lane"},
+      {10, 100000, false, true, false, Route::COLS_SHORT, "at most 15 rows"},
+      {40, 1000, false, true, false, Route::COLS_LANE, "16..64 rows: a lane per column"},
+  };
+  for (const F32 &e : f32) {
+    const Route got = f32_route(e.R, e.C, e.ax1, e.vec16, k, e.fills);
+    if (got != e.want) {
+      printf("FAIL route f32 [%lld, %lld] axis %d: %d, want %d (%s)\n", (long long)e.R, (long long)e.C, e.ax1 ? 1 : 0,
+             (int)got, (int)e.want, e.why);
+      ++g_fail;
+    }
+  }
+  struct F64 {
+    int64_t R, C;
+    bool ax1, vec16, candidate;
+    Route64 want;
+    const char *why;
+  };
+  const F64 f64[] = {
+      {4096, 4096, true, true, false, Route64::ROWS_TILE, "rows of up to 16384 doubles"},
+      {300, 50000, true, true, false, Route64::LONG_ROWS_CHUNKED, "rows above 32768 doubles"},
+      {4096, 4096, false, true, true, Route64::COLS_ONE, "4096-row columns read once (when the grid fills)"},
+      {1025, 16384, false, true, false, Route64::COLS_CHUNKED, "1025 rows: the tile half padding"},
+      {2560, 5000, false, true, true, Route64::COLS_ONE, "5/8 of a 4096-row tile"},
+      {8000000, 2, false, true, false, Route64::COLS_PAIRS, "two long columns: one row of pairs"},
+      {1000, 3001, false, false, false, Route64::COLS_ONE, "65..1024 rows: one launch"},
+      {10, 100000, false, true, false, Route64::COLS_SHORT, "at most 15 rows"},
+  };
+  for (const F64 &e : f64) {
+    const bool cand = cols_one_read64_candidate(e.ax1, e.R, e.C, 1);
+    if (cand != e.candidate) {
+      printf("FAIL one-read candidate f64 [%lld, %lld]: %d, want %d (%s)\n", (long long)e.R, (long long)e.C, cand,
+             e.candidate, e.why);
+      ++g_fail;
+    }
+    const Route64 got = f64_route(e.R, e.C, e.ax1, e.vec16, cand, true);
+    if (got != e.want) {
+      printf("FAIL route f64 [%lld, %lld] axis %d: %d, want %d (%s)\n", (long long)e.R, (long long)e.C, e.ax1 ? 1 : 0,
+             (int)got, (int)e.want, e.why);
+      ++g_fail;
+    }
+  }
+}
+
 int main() {
+  route_expectations();
   // shapes: boundaries of every plan, ragged tails, odd widths
   const int64_t sizes[] = {1,    2,    3,    4,    5,    7,    8,    15,   16,   17,   31,   33,   63,    64,
                            65,   100,  127,  128,  129,  255,  256,  257,  300,  511,  512,  513,  777,   1000,
