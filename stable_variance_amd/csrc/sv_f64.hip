@@ -195,6 +195,54 @@ __device__ __forceinline__ NodeD wave_tree_d(NodeD n) {
   return swap_level_d<32, NN>(n);
 }
 
+// The permuted lane order of the float32 row kernels: lane L holds the range
+// of virtual lane 2 (L mod 32) + L / 32 (svx::vlane_pair32), so the first
+// cross-lane level pairs L and L ^ 32, then xor 1, xor 2, the two mirrors
+// and xor 16.  Every lane ends with the wave's node.
+template <int NN>
+__device__ __forceinline__ NodeD wave_tree_p32_d(NodeD n) {
+  n = swap_level_d<32, NN>(n);
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR1, NN>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_QUAD_XOR2, NN>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR, NN>(n));
+  n = comb_d<NN>(n, dpp_node_d<sv::DPP_ROW_MIRROR, NN>(n));
+  return swap_level_d<16, NN>(n);
+}
+
+// The words of two doubles through one v_permlane32_swap each (the float
+// helper): lanes 0..31 end with x of their own lane and of lane + 32, lanes
+// 32..63 with y of lane - 32 and of their own.
+__device__ __forceinline__ void swap32_two_d(double x, double y, double &a, double &b) {
+  const unsigned long long ux = __builtin_bit_cast(unsigned long long, x);
+  const unsigned long long uy = __builtin_bit_cast(unsigned long long, y);
+  float al, bl, ah, bh;
+  sv::swap32_two(__builtin_bit_cast(float, (unsigned)ux), __builtin_bit_cast(float, (unsigned)uy), al, bl);
+  sv::swap32_two(__builtin_bit_cast(float, (unsigned)(ux >> 32)), __builtin_bit_cast(float, (unsigned)(uy >> 32)), ah,
+                 bh);
+  a = __builtin_bit_cast(double, ((unsigned long long)__builtin_bit_cast(unsigned, ah) << 32) |
+                                     __builtin_bit_cast(unsigned, al));
+  b = __builtin_bit_cast(double, ((unsigned long long)__builtin_bit_cast(unsigned, bh) << 32) |
+                                     __builtin_bit_cast(unsigned, bl));
+}
+
+// The d and d^2 trees of a wave together, in the permuted lane order: one
+// swap gives lanes 0..31 the pairs of the d tree and lanes 32..63 those of
+// the d^2 tree, and the other five levels run once for both.  Lanes 0..31
+// return the wave's d node, lanes 32..63 its d^2 node.  The d^2 levels take
+// the TwoSum node: on non-negative operands its error is the same exact
+// value, with the same sign of zero, as the Fast2Sum form's.
+__device__ __forceinline__ NodeD wave_tree_dq_d(NodeD nd, NodeD nq) {
+  NodeD a, b;
+  swap32_two_d(nd.s, nq.s, a.s, b.s);
+  swap32_two_d(nd.c, nq.c, a.c, b.c);
+  NodeD n = comb_d<0>(a, b);
+  n = comb_d<0>(n, dpp_node_d<sv::DPP_QUAD_XOR1, 0>(n));
+  n = comb_d<0>(n, dpp_node_d<sv::DPP_QUAD_XOR2, 0>(n));
+  n = comb_d<0>(n, dpp_node_d<sv::DPP_ROW_HALF_MIRROR, 0>(n));
+  n = comb_d<0>(n, dpp_node_d<sv::DPP_ROW_MIRROR, 0>(n));
+  return swap_level_d<16, 0>(n);
+}
+
 // The first log2(S) of those levels: every lane ends with the node of its
 // aligned group of S lanes.
 template <int NN, int S>
@@ -423,7 +471,9 @@ __device__ __forceinline__ void finalize_dk(NodeD nd, NodeD nq, double x0, doubl
 }
 
 // Axis 1: one workgroup per row, W waves own consecutive 64*E ranges, each
-// lane E consecutive doubles; the row stays in registers between passes.
+// lane E consecutive doubles (lane L those of virtual lane
+// svx::vlane_pair32(L), the order in which the d and d^2 trees share their
+// cross-lane levels); the row stays in registers between passes.
 // The launch holds only the waves the row reaches (svx::rows_waves); the
 // tree's other wave nodes are (+0, +0).
 template <int E, int W, bool VEC>
@@ -439,17 +489,18 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   // a wave wholly past the row holds only padding: its nodes are (+0, +0),
   // what its trees would compute, so it skips them (wave-uniform)
   const bool empty = base >= n;
+  const int vl = svx::vlane_pair32(lane);  // this lane holds the range of virtual lane vl
 
   float vf[2 * E];
   const int64_t avail = 2 * svx::rows_avail(gridDim.x, row, ld, n, base);  // floats to the launch's last row
-  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(p + base), 2 * (n - base), nullptr, vf, lane,
+  sv::load_tile<2 * E, VEC, 1, false>(reinterpret_cast<const float *>(p + base), 2 * (n - base), nullptr, vf, vl,
                                       avail);
   double v[E];
   floats_to_doubles<E>(vf, v);
   const double x0 = p[0];
 
   const bool full = base + 64 * E <= n;
-  const int64_t left = n - base - (int64_t)lane * E;
+  const int64_t left = n - base - (int64_t)vl * E;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
   if (full) {
 #pragma unroll
@@ -460,7 +511,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   }
 
   NodeD ny = {0.0, 0.0};
-  if (!empty) ny = wave_tree_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
+  if (!empty) ny = wave_tree_p32_d<KD_PLAIN>(lane_tree_d<LEAF_PLAIN_D, 0, E, E>(v));
   const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));  // the waves launched
   // From four waves on, the tree over the wave nodes takes one node per lane
   // (lane l < W wave l's) and the first log2(W) cross-lane levels.
@@ -483,8 +534,9 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   if (!empty) {
     if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
     else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
-    nd = wave_tree_d<false>(nd);
-    nq = wave_tree_d<true>(nq);
+    const NodeD ndq = wave_tree_dq_d(nd, nq);  // lanes 0..31: d, 32..63: d^2
+    nd = {readlane_d(ndq.s, 0), readlane_d(ndq.c, 0)};
+    nq = {readlane_d(ndq.s, 32), readlane_d(ndq.c, 32)};
   }
   if constexpr (W > 1) {
     if (lane == 0) {

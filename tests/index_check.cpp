@@ -501,7 +501,7 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
           for (int w = 0; w < waves; ++w) {
             const int64_t base = (int64_t)w * 64 * p.E;
             for (int lane = 0; lane < 64; ++lane) {
-              tile_loads(2 * p.E, vec, 1, 2 * (n - base), 2 * rows_avail(nr, b, cols, n, base), lane,
+              tile_loads(2 * p.E, vec, 1, 2 * (n - base), 2 * rows_avail(nr, b, cols, n, base), vlane_pair32(lane),
                          [&](int64_t i, int wd) { load(cf, 2 * (pr + base) + i, wd, b, lane); });
               load(c, pr, 1, b, lane);
             }
