@@ -384,10 +384,10 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *   "var_short_rows" rows of at most 512 values: 1 (default) = several rows
  *                    per wave (a group of lanes per row), 0 = one workgroup
  *                    per row
- *   "var_long_rows"  axis 1, rows of 16385..65536 values when there are at
- *                    least 256 rows: 1 (default) = one workgroup of 16 waves
- *                    per row, the row read once (the workspace is then not
- *                    used); 0 = the chunked path
+ *   "var_long_rows"  axis 1, rows of 16385..65536 floats (16385..32768
+ *                    doubles) when there are at least 256 rows: 1 (default)
+ *                    = one workgroup of 16 waves per row, the row read once
+ *                    (the workspace is then not used); 0 = the chunked path
  *   "var_cols_short" axis 0, columns of at most 15 rows with a 16-byte
  *                    aligned base and a width divisible by 4: 1 (default) =
  *                    four columns per lane, every tree in-lane; 0 = a lane

@@ -1531,7 +1531,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
       one_read = 4 * p.blocks >= 3 * rounds * cap;
     }
   }
-  switch (svx::f64_route(rows, cols, ax1, vec, one_read, svh::cols_pairs())) {
+  switch (svx::f64_route(rows, cols, ax1, vec, one_read, svh::cols_pairs(), svh::long_rows() != 0)) {
     case svx::Route64::ROWS_SEG: {
       // rows of up to 512 doubles sharing waves: 16-byte loads of two
       // doubles for aligned rows of an even count, else single doubles

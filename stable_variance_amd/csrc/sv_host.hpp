@@ -34,6 +34,8 @@ __attribute__((visibility("hidden"))) int64_t launch_items();
 __attribute__((visibility("hidden"))) int cols_once();
 // sv_set_tuning("var_cols_pairs") of this host thread: 0 or 1 (default).
 __attribute__((visibility("hidden"))) int cols_pairs();
+// sv_set_tuning("var_long_rows") of this host thread: 0 or 1 (default).
+__attribute__((visibility("hidden"))) int long_rows();
 
 // in_batches(total, per_block, threads, fn) calls fn(first, count) over
 // [0, total) in runs of whole blocks (per_block items of `threads`

@@ -369,13 +369,15 @@ constexpr bool cols_one_read64_candidate(bool ax1, int64_t rows, int64_t cols, i
 }
 // vec16: the matrix starts 16-byte aligned and cols is even.  one_read: the
 // one-read launch is chosen for a candidate (above).  pairs: the float32 knob
-// var_cols_pairs.
+// var_cols_pairs.  long_rows: the float32 knob var_long_rows (0: rows of
+// 16385..32768 values take the chunks whatever the row count).
 constexpr Route64 f64_route(int64_t rows, int64_t cols, bool ax1, bool vec16, bool one_read = false,
-                            bool pairs = true) {
+                            bool pairs = true, bool long_rows = true) {
   const int64_t n = ax1 ? cols : rows;
   if (ax1) {
     if (n <= 512) return Route64::ROWS_SEG;
-    if (n <= V64_ROWS_MAX_N || (n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS)) return Route64::ROWS_TILE;
+    if (n <= V64_ROWS_MAX_N || (long_rows && n <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS))
+      return Route64::ROWS_TILE;
     return Route64::LONG_ROWS_CHUNKED;
   }
   if (cols == 2 && n > V64_COLS_ONE_MAX_R && pairs &&

@@ -1587,6 +1587,7 @@ thread_local Tuning g_tune;
 int64_t svh::launch_items() { return g_tune.launch_items; }
 int svh::cols_once() { return g_tune.var_cols_once; }
 int svh::cols_pairs() { return g_tune.var_cols_pairs; }
+int svh::long_rows() { return g_tune.var_long_rows; }
 
 namespace {
 

@@ -215,15 +215,23 @@ def test_var64_top_of_range_and_specials(torch_dev):
 
 
 # at least 256 rows of 16385..32768 values: one workgroup of 16 waves, 32
-# doubles per lane (odd widths: 8-byte loads); fewer rows keep the chunks
+# doubles per lane (odd widths: 8-byte loads), or the chunks under
+# var_long_rows 0; fewer rows keep the chunks
 @pytest.mark.parametrize("shape", [(256, 16385), (300, 20001), (256, 32768), (257, 24576), (255, 20000)])
-def test_var64_long_rows_one_workgroup(torch_dev, shape):
-    rng = np.random.default_rng(shape[0] + shape[1])
-    a = rng.normal(-3e7, 5, shape)
-    check_var64(torch_dev, a, 1)
-    check_var64(torch_dev, a, 1, 1)
-    b = W.adversarial_values(shape[0] * shape[1], shape[1]).astype(np.float64).reshape(shape) * 1e200
-    check_var64(torch_dev, b, 1)
+@pytest.mark.parametrize("long_rows", [1, 0])
+def test_var64_long_rows_one_workgroup(torch_dev, shape, long_rows):
+    import stable_variance_amd as sv
+
+    sv.set_tuning("var_long_rows", long_rows)
+    try:
+        rng = np.random.default_rng(shape[0] + shape[1])
+        a = rng.normal(-3e7, 5, shape)
+        check_var64(torch_dev, a, 1)
+        check_var64(torch_dev, a, 1, 1)
+        b = W.adversarial_values(shape[0] * shape[1], shape[1]).astype(np.float64).reshape(shape) * 1e200
+        check_var64(torch_dev, b, 1)
+    finally:
+        sv.set_tuning("reset", 0)
 
 
 @pytest.mark.parametrize("items", [1024, 4096])
