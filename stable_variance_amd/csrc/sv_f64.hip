@@ -1097,8 +1097,11 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
 // Whole columns in one workgroup (R <= 16*G*W rows): the tile layout of
 // k_cols_y_d with a single chunk, and y, m, d and d^2 in one launch, the tile
 // kept in registers between the two passes.  Waves wholly past the last row
-// load nothing (their values are the +0 padding).
-template <int V, int W, int G, bool VEC16 = true>
+// load nothing (their values are the +0 padding).  EXACT: R = 16*G*W, so no
+// lane holds padding and the masked code paths are not compiled (with them,
+// the 8-wave tile of 32 doubles per lane took 164 VGPRs and one workgroup per
+// CU; without, 102, and two).
+template <int V, int W, int G, bool VEC16 = true, bool EXACT = false>
 __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                        int64_t ddof, double *__restrict__ var_out,
                                                        double *__restrict__ mean_out, int b0) {
@@ -1116,8 +1119,8 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
-  const bool full = r0 + E <= R;
-  const bool wave_full = rw + (int64_t)E * G <= R;  // uniform
+  const bool full = EXACT || r0 + E <= R;
+  const bool wave_full = EXACT || rw + (int64_t)E * G <= R;  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
   double v[V][E];
@@ -1375,22 +1378,34 @@ void launch_cols_gd(const double *x, int64_t R, int64_t C, int64_t ddof, const S
 //   R > 1024 (at least two columns): as above with W = 8 (512 work-items
 //     holding 32 doubles each), and G = 32 above 2048 rows (four columns
 //     per workgroup).  At 16 waves the 128 registers a lane may then use
-//     hold too little: the tile spills.
+//     hold too little for the masked kernel: the tile spills.  At exactly
+//     2048 or 4096 rows the mask-free instance runs instead, and with
+//     `wide` (16-byte loads, a grid that fills the chip) 16 waves with G = 8
+//     or 16: sixteen or eight columns, 128- or 64-byte row segments.
 // Measured (us, one column per lane against two): [100, 140000] 26.5 / 39.6,
 // [512, 4096] 8.0 / 10.9; [1000, 20000] 65.2 / 52.5, [1000, 1000] 13.0 / 6.9.
-void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool vec, double *var, double *mean,
-                       hipStream_t st) {
-  const svx::ColsOne64Plan p = svx::cols_one64_plan(R, C, vec);
+void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool vec, bool wide, double *var,
+                       double *mean, hipStream_t st) {
+  const svx::ColsOne64Plan p = svx::cols_one64_plan(R, C, vec, wide);
 #define SV_ONE64(V_, W_, G_, ...)                                                                         \
   svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                    \
     k_cols_one_d<V_, W_, G_, ##__VA_ARGS__><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, \
                                                                                          mean, (int)b0);  \
   })
-  if (p.V == 2 && p.G == 32) {
-    if (vec) SV_ONE64(2, 8, 32);
+  if (p.W == 16 && p.V == 2) {  // the wide tiles (exactly 2048 or 4096 rows, 16-byte loads)
+    if (p.G == 16) SV_ONE64(2, 16, 16, true, true);
+    else SV_ONE64(2, 16, 8, true, true);
+  } else if (p.V == 2 && p.G == 32) {
+    if (R == 4096) {
+      if (vec) SV_ONE64(2, 8, 32, true, true);
+      else SV_ONE64(2, 8, 32, false, true);
+    } else if (vec) SV_ONE64(2, 8, 32);
     else SV_ONE64(2, 8, 32, false);
   } else if (p.V == 2 && p.W == 8) {
-    if (vec) SV_ONE64(2, 8, 16);
+    if (R == 2048) {
+      if (vec) SV_ONE64(2, 8, 16, true, true);
+      else SV_ONE64(2, 8, 16, false, true);
+    } else if (vec) SV_ONE64(2, 8, 16);
     else SV_ONE64(2, 8, 16, false);
   } else if (p.V == 2) {
     if (vec) SV_ONE64(2, 4, 16);
@@ -1514,21 +1529,38 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
   const bool vec = svh::aligned16(x) && (cols % 2 == 0);
   // Columns of 1025..4096 rows: read once by workgroups of eight or four
   // whole columns (32 doubles per lane) unless that grid leaves the chip's
-  // last round of workgroups mostly empty.
-  bool one_read = false;
+  // last round of workgroups mostly empty (judged with the masked kernel's
+  // occupancy, one workgroup per CU, also where the mask-free instance runs
+  // two).  Columns of exactly 2048 or 4096 rows with 16-byte loads take the
+  // wide 16-wave tile when its own grid fills the chip.  var_cols_once 2
+  // takes the one read, and the wide tile where it applies, whatever the fill.
+  bool one_read = false, wide = false;
   if (svx::cols_one_read64_candidate(ax1, rows, cols, svh::cols_once())) {
+    const bool forced = svh::cols_once() == 2;
+    int cus = 0, dev = 0;
+    const bool have_cus = !forced && hipGetDevice(&dev) == hipSuccess &&
+                          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                          cus > 0;
+    auto fills = [&](const void *fn, int waves, int64_t blocks) {
+      int per_cu = 0;
+      if (!have_cus || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * waves, 0) != hipSuccess ||
+          per_cu <= 0)
+        return false;
+      const int64_t cap = (int64_t)per_cu * cus, rounds = (blocks + cap - 1) / cap;
+      return 4 * blocks >= 3 * rounds * cap;
+    };
     const svx::ColsOne64Plan p = svx::cols_one64_plan(rows, cols, vec);
-    one_read = svh::cols_once() == 2;
     const void *fn = p.G == 32 ? (vec ? reinterpret_cast<const void *>(k_cols_one_d<2, 8, 32>)
                                       : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 32, false>))
                                : (vec ? reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16>)
                                       : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16, false>));
-    int per_cu = 0, cus = 0, dev = 0;
-    if (!one_read && hipGetDevice(&dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * p.W, 0) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0) {
-      const int64_t cap = (int64_t)per_cu * cus, rounds = (p.blocks + cap - 1) / cap;
-      one_read = 4 * p.blocks >= 3 * rounds * cap;
+    one_read = forced || fills(fn, p.W, p.blocks);
+    if (svx::cols_one64_wide_ok(rows, vec)) {
+      const svx::ColsOne64Plan pw = svx::cols_one64_plan(rows, cols, vec, true);
+      const void *fw = rows == 4096 ? reinterpret_cast<const void *>(k_cols_one_d<2, 16, 16, true, true>)
+                                    : reinterpret_cast<const void *>(k_cols_one_d<2, 16, 8, true, true>);
+      wide = forced || fills(fw, pw.W, pw.blocks);
+      one_read = one_read || wide;
     }
   }
   switch (svx::f64_route(rows, cols, ax1, vec, one_read, svh::cols_pairs(), svh::long_rows() != 0)) {
@@ -1597,7 +1629,7 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
       else launch_cols_gd<1>(x, rows, cols, ddof, ws, var_out, mean_out, st);
       break;
     }
-    case svx::Route64::COLS_ONE: launch_cols_one_d(x, rows, cols, ddof, vec, var_out, mean_out, st); break;
+    case svx::Route64::COLS_ONE: launch_cols_one_d(x, rows, cols, ddof, vec, wide, var_out, mean_out, st); break;
     case svx::Route64::COLS_PAIRS: launch_long_pairs_d(vec, x, rows, ddof, workspace, var_out, mean_out, st); break;
     case svx::Route64::COLS_SHORT: {
       const int e = svx::cols_short_e(n);

@@ -402,12 +402,17 @@ constexpr RowsPlan rows64_plan(int64_t n) {
 // Axis 0, 65..4096 rows in one launch: V adjacent columns per lane (two above
 // 512 rows, one below or for a single column), G row groups, W waves of 16
 // rows per lane (above 1024 rows: at least two columns, 8 waves, and 32 row
-// groups above 2048), `blocks` workgroups of V*64/G columns.
+// groups above 2048), `blocks` workgroups of V*64/G columns.  wide: columns
+// of exactly 2048 or 4096 rows with 16-byte loads take 16 waves instead, and
+// 8 or 16 row groups (sixteen or eight columns per workgroup).
 struct ColsOne64Plan {
   int V, G, W;
   int64_t blocks;
 };
-constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16) {
+constexpr bool cols_one64_wide_ok(int64_t R, bool vec16) { return vec16 && (R == 2048 || R == 4096); }
+constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16, bool wide = false) {
+  if (wide && cols_one64_wide_ok(R, vec16))
+    return R == 4096 ? ColsOne64Plan{2, 16, 16, (C + 7) / 8} : ColsOne64Plan{2, 8, 16, (C + 15) / 16};
   if (R > 2048) return {2, 32, 8, (C + 3) / 4};
   if (R > V64_COLS_MAX_R) return {2, 16, 8, (C + 7) / 8};
   if (R > 512) return (vec16 || C >= 2) ? ColsOne64Plan{2, 16, 4, (C + 7) / 8} : ColsOne64Plan{1, 16, 4, (C + 3) / 4};

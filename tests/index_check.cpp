@@ -480,7 +480,7 @@ void long_pairs_d(const Where &c, const Where &cf, int64_t n, bool vec) {
 // The float64 variance (indices in doubles; the row tiles load floats, two
 // per double).  off: the matrix's address modulo 16 bytes (0 or 8).
 void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_read, bool pairs,
-                        bool long_rows = true) {
+                        bool long_rows = true, bool wide = false) {
   const bool ax1 = axis == 1;
   const int64_t n = ax1 ? cols : rows;
   if (rows == 0 || cols == 0) return;
@@ -536,7 +536,7 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
       break;
     }
     case Route64::COLS_ONE: {
-      const ColsOne64Plan p = cols_one64_plan(rows, cols, vec);
+      const ColsOne64Plan p = cols_one64_plan(rows, cols, vec, wide);
       cols_one(c, rows, cols, p.V, p.W, p.G, vec, L64_E, 0, p.blocks, p.W, 2);
       break;
     }
@@ -545,12 +545,17 @@ void variance_f64_route(int64_t rows, int64_t cols, int axis, int off, bool one_
   }
 }
 
-// Both launch choices of a candidate for the one-read columns, of two
-// columns (pairs or column chunks) and of rows of 16385..32768 doubles with
-// 256 or more rows (one workgroup per row or chunks).
+// Both launch choices of a candidate for the one-read columns (and the wide
+// tile where it applies), of two columns (pairs or column chunks) and of
+// rows of 16385..32768 doubles with 256 or more rows (one workgroup per row
+// or chunks).
 void variance_f64(int64_t rows, int64_t cols, int axis, int off) {
   variance_f64_route(rows, cols, axis, off, false, true);
-  if (cols_one_read64_candidate(axis == 1, rows, cols, 2)) variance_f64_route(rows, cols, axis, off, true, true);
+  if (cols_one_read64_candidate(axis == 1, rows, cols, 2)) {
+    variance_f64_route(rows, cols, axis, off, true, true);
+    if (cols_one64_wide_ok(rows, off == 0 && cols % 2 == 0))
+      variance_f64_route(rows, cols, axis, off, true, true, true, true);
+  }
   if (axis == 0 && cols == 2) variance_f64_route(rows, cols, axis, off, false, false);
   if (axis == 1 && cols > V64_ROWS_MAX_N && cols <= V64_ROWS_ONE_MAX_N && rows >= V64_ROWS_ONE_MIN_ROWS)
     variance_f64_route(rows, cols, axis, off, false, true, false);

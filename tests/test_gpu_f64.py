@@ -263,11 +263,13 @@ def test_var64_single_column_as_a_row(torch_dev, R):
 
 @pytest.mark.parametrize("once", [2, 0])
 @pytest.mark.parametrize("R,C", [(1025, 2), (1025, 3), (2048, 9), (2049, 4), (3000, 33), (4096, 64), (4096, 7),
-                                 (1500, 1030)])
+                                 (1500, 1030), (2048, 40), (4096, 34)])
 def test_var64_cols_one_read(torch_dev, once, R, C):
     # columns of 1025..4096 rows: read once by workgroups of whole columns
-    # (8 waves; 16 row groups per wave up to 2048 rows, 32 above) -- forced
-    # on (2) and off (0, the 128-row chunks) whatever the grid's fill
+    # (8 waves; 16 row groups per wave up to 2048 rows, 32 above; the
+    # mask-free instance at exactly 2048 or 4096 rows, and there the 16-wave
+    # tile for even widths) -- forced on (2) and off (0, the 128-row chunks)
+    # whatever the grid's fill
     import stable_variance_amd as sv
 
     rng = np.random.default_rng(R * 3 + C + once)
@@ -283,6 +285,18 @@ def test_var64_cols_one_read(torch_dev, once, R, C):
         check_var64(torch_dev, a, 0, 2)
     finally:
         sv.set_tuning("reset", 0)
+
+
+@pytest.mark.parametrize("R,C", [(4096, 2048), (2048, 4096), (4096, 2046), (4096, 1024)])
+def test_var64_cols_wide_tiles(torch_dev, R, C):
+    # the default choice at sizes whose grid fills the chip: the 16-wave
+    # tiles of 4096 and 2048 rows (eight and sixteen columns per workgroup;
+    # [4096, 2046] ends in a partial block), and the mask-free 8-wave tile
+    # where the wide grid would not fill ([4096, 1024])
+    rng = np.random.default_rng(R + C + 640)
+    a = rng.normal(7e4, 2, (R, C))
+    check_var64(torch_dev, a, 0)
+    check_var64(torch_dev, a, 0, 1)
 
 
 @pytest.mark.parametrize("pairs", [1, 0])
