@@ -1097,11 +1097,12 @@ __global__ __launch_bounds__(64 * L64_W) void k_cols_dq_d(const double *__restri
 // Whole columns in one workgroup (R <= 16*G*W rows): the tile layout of
 // k_cols_y_d with a single chunk, and y, m, d and d^2 in one launch, the tile
 // kept in registers between the two passes.  Waves wholly past the last row
-// load nothing (their values are the +0 padding).  EXACT: R = 16*G*W, so no
-// lane holds padding and the masked code paths are not compiled (with them,
-// the 8-wave tile of 32 doubles per lane took 164 VGPRs and one workgroup per
-// CU; without, 102, and two).
-template <int V, int W, int G, bool VEC16 = true, bool EXACT = false>
+// load nothing (their values are the +0 padding).  MODE 0 branches per wave
+// between the full and the masked code paths; MODE 1 is for R = 16*G*W (no
+// lane holds padding: no masks); MODE 2 masks every wave (one code path).
+// Both paths together took the 8-wave tile of 32 doubles per lane to 164
+// VGPRs and one workgroup per CU; one path takes 102-116, and two.
+template <int V, int W, int G, bool VEC16 = true, int MODE = 0>
 __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict__ x, int64_t R, int64_t C,
                                                        int64_t ddof, double *__restrict__ var_out,
                                                        double *__restrict__ mean_out, int b0) {
@@ -1119,8 +1120,8 @@ __global__ __launch_bounds__(64 * W) void k_cols_one_d(const double *__restrict_
   const int64_t c0 = cb * NC + (int64_t)q * V;
   const int64_t rw = (int64_t)w * (E * G);  // the wave's first row
   const int64_t r0 = rw + (int64_t)g * E;
-  const bool full = EXACT || r0 + E <= R;
-  const bool wave_full = EXACT || rw + (int64_t)E * G <= R;  // uniform
+  const bool full = MODE == 1 || r0 + E <= R;
+  const bool wave_full = MODE == 1 || (MODE == 0 && rw + (int64_t)E * G <= R);  // uniform
   const int64_t left = R - r0;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
   double v[V][E];
@@ -1393,20 +1394,20 @@ void launch_cols_one_d(const double *x, int64_t R, int64_t C, int64_t ddof, bool
                                                                                          mean, (int)b0);  \
   })
   if (p.W == 16 && p.V == 2) {  // the wide tiles (exactly 2048 or 4096 rows, 16-byte loads)
-    if (p.G == 16) SV_ONE64(2, 16, 16, true, true);
-    else SV_ONE64(2, 16, 8, true, true);
+    if (p.G == 16) SV_ONE64(2, 16, 16, true, 1);
+    else SV_ONE64(2, 16, 8, true, 1);
   } else if (p.V == 2 && p.G == 32) {
     if (R == 4096) {
-      if (vec) SV_ONE64(2, 8, 32, true, true);
-      else SV_ONE64(2, 8, 32, false, true);
-    } else if (vec) SV_ONE64(2, 8, 32);
-    else SV_ONE64(2, 8, 32, false);
+      if (vec) SV_ONE64(2, 8, 32, true, 1);
+      else SV_ONE64(2, 8, 32, false, 1);
+    } else if (vec) SV_ONE64(2, 8, 32, true, 2);
+    else SV_ONE64(2, 8, 32, false, 2);
   } else if (p.V == 2 && p.W == 8) {
     if (R == 2048) {
-      if (vec) SV_ONE64(2, 8, 16, true, true);
-      else SV_ONE64(2, 8, 16, false, true);
-    } else if (vec) SV_ONE64(2, 8, 16);
-    else SV_ONE64(2, 8, 16, false);
+      if (vec) SV_ONE64(2, 8, 16, true, 1);
+      else SV_ONE64(2, 8, 16, false, 1);
+    } else if (vec) SV_ONE64(2, 8, 16, true, 2);
+    else SV_ONE64(2, 8, 16, false, 2);
   } else if (p.V == 2) {
     if (vec) SV_ONE64(2, 4, 16);
     else SV_ONE64(2, 4, 16, false);  // two 8-byte loads
@@ -1529,37 +1530,21 @@ sv_status sv_variance_f64(const double *x, int64_t rows, int64_t cols, int axis,
   const bool vec = svh::aligned16(x) && (cols % 2 == 0);
   // Columns of 1025..4096 rows: read once by workgroups of eight or four
   // whole columns (32 doubles per lane) unless that grid leaves the chip's
-  // last round of workgroups mostly empty (judged with the masked kernel's
-  // occupancy, one workgroup per CU, also where the mask-free instance runs
-  // two).  Columns of exactly 2048 or 4096 rows with 16-byte loads take the
-  // wide 16-wave tile when its own grid fills the chip.  var_cols_once 2
+  // last round mostly empty, a round being one workgroup per CU.  Columns of
+  // exactly 2048 or 4096 rows with 16-byte loads take the wide 16-wave tile
+  // when its own grid fills the chip by the same rule.  var_cols_once 2
   // takes the one read, and the wide tile where it applies, whatever the fill.
   bool one_read = false, wide = false;
   if (svx::cols_one_read64_candidate(ax1, rows, cols, svh::cols_once())) {
     const bool forced = svh::cols_once() == 2;
     int cus = 0, dev = 0;
-    const bool have_cus = !forced && hipGetDevice(&dev) == hipSuccess &&
-                          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                          cus > 0;
-    auto fills = [&](const void *fn, int waves, int64_t blocks) {
-      int per_cu = 0;
-      if (!have_cus || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * waves, 0) != hipSuccess ||
-          per_cu <= 0)
-        return false;
-      const int64_t cap = (int64_t)per_cu * cus, rounds = (blocks + cap - 1) / cap;
-      return 4 * blocks >= 3 * rounds * cap;
-    };
+    if (!forced && (hipGetDevice(&dev) != hipSuccess ||
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess))
+      cus = 0;
     const svx::ColsOne64Plan p = svx::cols_one64_plan(rows, cols, vec);
-    const void *fn = p.G == 32 ? (vec ? reinterpret_cast<const void *>(k_cols_one_d<2, 8, 32>)
-                                      : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 32, false>))
-                               : (vec ? reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16>)
-                                      : reinterpret_cast<const void *>(k_cols_one_d<2, 8, 16, false>));
-    one_read = forced || fills(fn, p.W, p.blocks);
+    one_read = forced || svx::one_round_fill(p.blocks, cus);
     if (svx::cols_one64_wide_ok(rows, vec)) {
-      const svx::ColsOne64Plan pw = svx::cols_one64_plan(rows, cols, vec, true);
-      const void *fw = rows == 4096 ? reinterpret_cast<const void *>(k_cols_one_d<2, 16, 16, true, true>)
-                                    : reinterpret_cast<const void *>(k_cols_one_d<2, 16, 8, true, true>);
-      wide = forced || fills(fw, pw.W, pw.blocks);
+      wide = forced || svx::one_round_fill(svx::cols_one64_plan(rows, cols, vec, true).blocks, cus);
       one_read = one_read || wide;
     }
   }

@@ -410,6 +410,13 @@ struct ColsOne64Plan {
   int64_t blocks;
 };
 constexpr bool cols_one64_wide_ok(int64_t R, bool vec16) { return vec16 && (R == 2048 || R == 4096); }
+// A grid of `blocks` workgroups, one per CU at a time on `cus` CUs, fills
+// at least three quarters of its last round (false without a CU count).
+constexpr bool one_round_fill(int64_t blocks, int64_t cus) {
+  if (cus <= 0) return false;
+  const int64_t rounds = (blocks + cus - 1) / cus;
+  return 4 * blocks >= 3 * rounds * cus;
+}
 constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16, bool wide = false) {
   if (wide && cols_one64_wide_ok(R, vec16))
     return R == 4096 ? ColsOne64Plan{2, 16, 16, (C + 7) / 8} : ColsOne64Plan{2, 8, 16, (C + 15) / 16};

@@ -753,6 +753,31 @@ void route_expectations() {
       ++g_fail;
     }
   }
+  // float64 columns of 1025..4096 rows on 256 CUs: the one read when its
+  // grid fills, and the wide 16-wave tile when its own grid does
+  struct Fill64 {
+    int64_t R, C;
+    bool one_read, wide;
+    const char *why;
+  };
+  const Fill64 fill64[] = {
+      {4096, 4096, true, true, "two full rounds of 16-wave tiles"},
+      {4096, 3000, true, false, "375 wide tiles: the second round half empty"},
+      {4096, 1024, true, false, "128 wide tiles: half the CUs"},
+      {2048, 8192, true, true, "512 tiles of sixteen columns"},
+      {2048, 2002, true, false, "126 wide tiles"},
+      {3000, 4100, true, false, "not a whole tile: no wide tile"},
+      {4096, 2050, false, false, "513 and 257 tiles: the last round nearly empty"},
+  };
+  for (const Fill64 &e : fill64) {
+    const bool wide = cols_one64_wide_ok(e.R, true) && one_round_fill(cols_one64_plan(e.R, e.C, true, true).blocks, 256);
+    const bool one = one_round_fill(cols_one64_plan(e.R, e.C, true).blocks, 256) || wide;
+    if (one != e.one_read || wide != e.wide) {
+      printf("FAIL fill f64 [%lld, %lld]: one read %d wide %d, want %d %d (%s)\n", (long long)e.R, (long long)e.C, one,
+             wide, e.one_read, e.wide, e.why);
+      ++g_fail;
+    }
+  }
 }
 
 int main() {
