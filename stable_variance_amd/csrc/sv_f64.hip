@@ -475,9 +475,12 @@ __device__ __forceinline__ void finalize_dk(NodeD nd, NodeD nq, double x0, doubl
 // svx::vlane_pair32(L), the order in which the d and d^2 trees share their
 // cross-lane levels); the row stays in registers between passes.
 // The launch holds only the waves the row reaches (svx::rows_waves); the
-// tree's other wave nodes are (+0, +0).
+// tree's other wave nodes are (+0, +0).  At 32 doubles per lane every wave
+// takes the masked code path (one path instead of two: 93-95 VGPRs instead
+// of 118) and the kernel asks for five waves per SIMD, so two workgroups of
+// up to ten waves (rows of up to 20480 doubles) share a CU.
 template <int E, int W, bool VEC>
-__global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restrict__ x, int64_t n, int64_t ld,
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(E == 32 ? 5 : 1, 8))) void k_var_rows_f64(const double *__restrict__ x, int64_t n, int64_t ld,
                                                          int64_t ddof, double *__restrict__ var_out,
                                                          double *__restrict__ mean_out) {
   __shared__ NodeD slots[3][W];
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
   const bool full = base + 64 * E <= n;
   const int64_t left = n - base - (int64_t)vl * E;
   const int valid = left < 0 ? 0 : (left > E ? E : (int)left);
-  if (full) {
+  if (full && E != 32) {
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = v[i] - x0;
   } else {
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(64 * W) void k_var_rows_f64(const double *__restric
 
   NodeD nd = {0.0, 0.0}, nq = {0.0, 0.0};
   if (!empty) {
-    if (full) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
+    if (full && E != 32) lane_tree_dq_d<false, 0, E, E>(v, m, E, nd, nq);
     else lane_tree_dq_d<true, 0, E, E>(v, m, valid, nd, nq);
     const NodeD ndq = wave_tree_dq_d(nd, nq);  // lanes 0..31: d, 32..63: d^2
     nd = {readlane_d(ndq.s, 0), readlane_d(ndq.c, 0)};
