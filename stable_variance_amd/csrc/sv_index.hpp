@@ -238,6 +238,9 @@ constexpr ColsOnePlan cols_one4_plan(int64_t R, int64_t C) {
   while (g < 16 && g * 4 <= gw && (C + 4 * 64 / g - 1) / (4 * 64 / g) < 512) g *= 4;
   return {g, gw / g, (C + 4 * 64 / g - 1) / (4 * 64 / g)};
 }
+// Four columns per lane, columns that fill at most 5/8 of the plan's tile of
+// 16*G*W rows: every wave masked (one code path), only the waves row R reaches.
+constexpr bool cols_one4_masked(int64_t R, const ColsOnePlan &p) { return 8 * R <= 5 * 16LL * p.G * p.W; }
 // One column per lane: G in 1, 4 (row segments of at least 16 lanes), W up
 // to 16; G = 1 when that gives 512 workgroups.
 constexpr ColsOnePlan cols_one1_plan(int64_t R, int64_t C) {

@@ -1744,14 +1744,27 @@ void launch_cols_v(const float *x, int64_t R, int64_t C, int64_t ddof, const Col
 // = the power of two at or above R rows per workgroup, 4*64/G columns.  Of
 // the (G, W) pairs that hold exactly that many rows (G in 1, 4, 16; W in 1,
 // 2, 4, 8), the smallest G that still gives 512 workgroups, else the largest.
+// A column that fills at most 5/8 of its tile takes MODE 2 (one masked
+// code path: 91-106 VGPRs against 140-150, and only the waves row R reaches);
+// fuller tiles keep MODE 0, whose full waves skip the masks (µs, MODE 0 /
+// MODE 2: [520, 65536] 53.0 / 48.5, [513, 30000] 26.7 / 25.0, [800, 10000]
+// 15.3 / 16.5, [1000, 8192] 14.5 / 15.9).
 template <bool VEC16>
 void launch_cols_one(const float *x, int64_t R, int64_t C, int64_t ddof, float *var, float *mean, hipStream_t st) {
   const svx::ColsOnePlan p = svx::cols_one4_plan(R, C);
   const int g = p.G, w = p.W;
-#define SV_ONE(G_, W_)                                                                                   \
-  svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                    \
-    k_cols_one<4, W_, G_, VEC16><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean, (int)b0); \
-  })
+  const bool sparse = svx::cols_one4_masked(R, p);
+  const int reached = (int)((R + 16LL * g - 1) / (16LL * g));  // the waves row R reaches
+#define SV_ONE(G_, W_)                                                                                        \
+  if (!sparse)                                                                                                \
+    svh::in_batches(p.blocks, 1, 64 * W_, [&](int64_t b0, int64_t nb) {                                       \
+      k_cols_one<4, W_, G_, VEC16><<<dim3((unsigned)nb), dim3(64 * W_), 0, st>>>(x, R, C, ddof, var, mean, (int)b0); \
+    });                                                                                                       \
+  else                                                                                                        \
+    svh::in_batches(p.blocks, 1, 64 * reached, [&](int64_t b0, int64_t nb) {                                  \
+      k_cols_one<4, W_, G_, VEC16, CC_E, 2><<<dim3((unsigned)nb), dim3(64 * (unsigned)reached), 0, st>>>(      \
+          x, R, C, ddof, var, mean, (int)b0);                                                                 \
+    })
   switch (g * 16 + w) {  // R > 64: 16*G*W >= 128
     case 16 * 1 + 8: SV_ONE(1, 8); break;
     case 16 * 4 + 2: SV_ONE(4, 2); break;

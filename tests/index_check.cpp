@@ -402,8 +402,12 @@ void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k,
     }
     case Route::COLS_SHORT: cols_short(c, rows, cols, 4); break;
     case Route::COLS_ONE4: {
+      // mode 2 over the waves row R reaches (clamped loads in every wave)
+      // for columns that fill at most 5/8 of the tile, else mode 0
       const ColsOnePlan p = cols_one4_plan(rows, cols);
-      cols_one(c, rows, cols, 4, p.W, p.G, vec16, CC_E, 0, p.blocks, p.W);
+      const bool sparse = cols_one4_masked(rows, p);
+      const int reached = (int)((rows + (int64_t)CC_E * p.G - 1) / ((int64_t)CC_E * p.G));
+      cols_one(c, rows, cols, 4, p.W, p.G, vec16, CC_E, sparse ? 2 : 0, p.blocks, sparse ? reached : p.W);
       break;
     }
     case Route::COLS_ONE1: {
