@@ -264,15 +264,17 @@ constexpr ColsLongPlan cols_long_plan(int64_t R, int64_t C) {
 }
 
 // Axis 0 in row chunks: G row groups per wave (lanes stay on columns: G = 1
-// for at least 64 groups of V columns, 4 for 5..63, 16 for 2..4, 64 for
-// one), chunks of 16*W*G rows, V*64/G columns per block.
+// for at least 64 groups of V columns, 4 for 9..63, 8 for 5..8, 16 for 3..4,
+// 32 for two, 64 for one, so that at most 64/G groups of lanes hold more
+// than half the matrix's columns), chunks of 16*W*G rows, V*64/G columns per
+// block.
 struct ColsChunkPlan {
   int G;
   int64_t nch, ncb;
 };
 constexpr ColsChunkPlan cols_chunk_plan(int V, int W, int64_t R, int64_t C) {
   const int64_t groups = (C + V - 1) / V;
-  const int g = groups >= 64 ? 1 : groups > 4 ? 4 : groups > 1 ? 16 : 64;
+  const int g = groups >= 64 ? 1 : groups > 8 ? 4 : groups > 4 ? 8 : groups > 2 ? 16 : groups > 1 ? 32 : 64;
   const int64_t ch = 16LL * W * g;
   const int nc = V * (64 / g);
   return {g, (R + ch - 1) / ch, (C + nc - 1) / nc};

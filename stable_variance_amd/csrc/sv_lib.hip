@@ -1718,14 +1718,17 @@ void launch_cols_chunked(const float *x, int64_t R, int64_t C, int64_t ddof, con
 
 // Row groups per wave, so that lanes stay on columns: G = 1 (64 column
 // groups of V per block) for matrices of at least 64 groups, G = 4 (16 groups
-// per block) for 5 to 63, G = 16 (4 groups) for 2 to 4, G = 64 for one.
+// per block) for 9 to 63, G = 8 (8 groups) for 5 to 8, G = 16 (4 groups) for
+// 3 and 4, G = 32 (2 groups) for two, G = 64 for one.
 template <int V, int W>
 void launch_cols_g(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var, float *mean,
                    hipStream_t st) {
   switch (svx::cols_chunk_plan(V, W, R, C).G) {
     case 1: launch_cols_chunked<V, W, 1>(x, R, C, ddof, ws, var, mean, st); break;
     case 4: launch_cols_chunked<V, W, 4>(x, R, C, ddof, ws, var, mean, st); break;
+    case 8: launch_cols_chunked<V, W, 8>(x, R, C, ddof, ws, var, mean, st); break;
     case 16: launch_cols_chunked<V, W, 16>(x, R, C, ddof, ws, var, mean, st); break;
+    case 32: launch_cols_chunked<V, W, 32>(x, R, C, ddof, ws, var, mean, st); break;
     default: launch_cols_chunked<V, W, 64>(x, R, C, ddof, ws, var, mean, st); break;
   }
 }
