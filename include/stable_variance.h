@@ -415,7 +415,13 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    1025..4096 rows (at least two columns): eight or four
  *                    whole columns per workgroup of 8 waves, read once (under
  *                    1, only columns of at least 1280 or 2560 rows, 5/8 of
- *                    their 2048- or 4096-row tile)
+ *                    their 2048- or 4096-row tile, and when that grid fills
+ *                    three quarters of its last round of one workgroup per
+ *                    CU); columns of exactly 2048 or 4096 rows with a 16-byte
+ *                    aligned base and an even width take sixteen or eight
+ *                    whole columns per workgroup of 16 waves instead when
+ *                    that grid fills the chip by the same rule (under 2,
+ *                    always)
  *   "sum_xcd"        tree sum: 1 = renumber the workgroups so that each of the
  *                    eight dies (XCDs) streams one contiguous region; 0 =
  *                    dispatch order, consecutive regions spread over the dies
