@@ -445,10 +445,14 @@ def test_variance_long_cols(torch_dev, col_geometry, R):
 
 @pytest.mark.parametrize("R,C", [(4096, 1000), (2000, 4100), (5000, 257), (300, 4096), (70000, 12), (1, 3000),
                                  (100000, 4), (50000, 16), (20000, 7), (8193, 2), (30000, 1), (9000, 40),
-                                 (40000, 130), (70000, 65)])
+                                 (40000, 130), (70000, 65), (20000, 8), (300000, 8), (33000, 20), (70000, 24),
+                                 (9000, 32)])
 def test_variance_cols_wide(torch_dev, col_geometry, R, C):
     # several column blocks with a ragged last block (16-byte loads of four
-    # columns when C % 4 == 0, one column per lane otherwise) and ragged chunks
+    # columns when C % 4 == 0, one column per lane otherwise) and ragged chunks;
+    # narrow matrices take 8 or 32 row groups per wave in the chunks (20..32
+    # and 8 columns; 35-37 chunks at [70000, 24] and [300000, 8], beyond the
+    # chunk count whose m each workgroup forms itself)
     rng = np.random.default_rng(R + C)
     a = rng.normal(2.5e4, 4, (R, C)).astype(np.float32)
     check_var(torch_dev, a, 0, 0)
