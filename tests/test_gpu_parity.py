@@ -812,7 +812,7 @@ def test_sum_dw_cancelling_sets_and_full_workload(torch_dev):
 # limit of 2^32 - 1, here on small inputs and bit for bit against the oracle.
 BATCH_F32 = [((2000, 3), 1), ((3000, 300), 1), ((300, 3000), 1), ((260, 17000), 1), ((3, 20000), 1),
              ((3, 2000), 0), ((40, 700), 0), ((700, 70), 0), ((700, 1030), 0), ((1500, 300), 0), ((3000, 40), 0),
-             ((5000, 33), 0), ((2049, 300), 0)]
+             ((5000, 33), 0), ((2049, 300), 0), ((520, 8192), 0), ((9000, 8), 0), ((9000, 24), 0)]
 
 
 @pytest.mark.parametrize("items", [1024, 4096])
