@@ -404,7 +404,11 @@ sv_status sv_probe_read_bandwidth(const float *x, int64_t n, float *out, void *s
  *                    held by one workgroup and read once (0..1024, default
  *                    1024); longer columns are reduced in row chunks
  *   "var_cols_waves" axis 0, chunked: waves per workgroup, 4, 8 or 16
- *                    (default): chunks of 64, 128 or 256 rows
+ *                    (chunks of 16 rows per wave times the row groups per
+ *                    wave), or 0 (default): 16, or 8 for matrices of at
+ *                    most 32 columns with 16-byte loads (8 of other widths)
+ *                    and where a grid of 16-wave workgroups, one per CU at
+ *                    a time, would leave its last round mostly empty
  *   "var_cols_once"  axis 0, columns of 1025..4096 rows: 1 (default) = 16
  *                    whole columns per workgroup of up to 16 waves, one
  *                    column per lane, the input read once, when that grid

@@ -263,6 +263,14 @@ constexpr ColsLongPlan cols_long_plan(int64_t R, int64_t C) {
   return {e, (int)((R + 4 * e - 1) / (4 * e)), (R == 2048 || R == 4096) ? 1 : 2, (C + 15) / 16};
 }
 
+// A grid of `blocks` workgroups, one per CU at a time on `cus` CUs, fills
+// at least three quarters of its last round (false without a CU count).
+constexpr bool one_round_fill(int64_t blocks, int64_t cus) {
+  if (cus <= 0) return false;
+  const int64_t rounds = (blocks + cus - 1) / cus;
+  return 4 * blocks >= 3 * rounds * cus;
+}
+
 // Axis 0 in row chunks: G row groups per wave (lanes stay on columns: G = 1
 // for at least 64 groups of V columns, 4 for 9..63, 8 for 5..8, 16 for 3..4,
 // 32 for two, 64 for one, so that at most 64/G groups of lanes hold more
@@ -278,6 +286,15 @@ constexpr ColsChunkPlan cols_chunk_plan(int V, int W, int64_t R, int64_t C) {
   const int64_t ch = 16LL * W * g;
   const int nc = V * (64 / g);
   return {g, (R + ch - 1) / ch, (C + nc - 1) / nc};
+}
+// Waves per chunk workgroup when var_cols_waves is 0 (auto): 16, or 8 for
+// narrow matrices (8 or more row groups per wave) and where the grid of
+// 16-wave workgroups (one per CU at a time) leaves its last round mostly
+// empty; 16 without a CU count.
+constexpr int cols_chunk_waves(int V, int64_t R, int64_t C, int64_t cus) {
+  const ColsChunkPlan p = cols_chunk_plan(V, 16, R, C);
+  if (cus <= 0) return 16;
+  return (p.G >= 8 || !one_round_fill(p.nch * p.ncb, cus)) ? 8 : 16;
 }
 
 // ---------------------------------------------------------------- float32 variance routes
@@ -415,13 +432,6 @@ struct ColsOne64Plan {
   int64_t blocks;
 };
 constexpr bool cols_one64_wide_ok(int64_t R, bool vec16) { return vec16 && (R == 2048 || R == 4096); }
-// A grid of `blocks` workgroups, one per CU at a time on `cus` CUs, fills
-// at least three quarters of its last round (false without a CU count).
-constexpr bool one_round_fill(int64_t blocks, int64_t cus) {
-  if (cus <= 0) return false;
-  const int64_t rounds = (blocks + cus - 1) / cus;
-  return 4 * blocks >= 3 * rounds * cus;
-}
 constexpr ColsOne64Plan cols_one64_plan(int64_t R, int64_t C, bool vec16, bool wide = false) {
   if (wide && cols_one64_wide_ok(R, vec16))
     return R == 4096 ? ColsOne64Plan{2, 16, 16, (C + 7) / 8} : ColsOne64Plan{2, 8, 16, (C + 15) / 16};

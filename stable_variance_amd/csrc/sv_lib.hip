@@ -1567,7 +1567,7 @@ struct Tuning {
   int var_split = 0;          // waves per 4096 values of a row of 1025..16384 values (1, 2, 4, 8; 0 auto)
   int var_lds_pad = 0;        // unused dynamic LDS bytes per row workgroup (caps resident waves)
   int var_cols_single_max = 1024;  // axis 0: rows up to which one workgroup holds a column tile (<= 1024)
-  int var_cols_waves = 16;    // axis 0, chunked: waves per workgroup (4, 8, 16); chunks of 16 * waves rows
+  int var_cols_waves = 0;     // axis 0, chunked: waves per workgroup (4, 8, 16; 0 auto); chunks of 16 * waves rows
   int var_short_rows = 1;     // rows of <= 512 values share waves (0: one workgroup per row)
   int var_cols_one = 1;       // axis 0, 65..1024 rows: 1 auto, 2 four columns per lane, 3 one, 0 the lane kernel
   int var_long_rows = 1;      // rows of 16385..65536 values, 256+ rows: 1 one workgroup per row, 0 chunked
@@ -1736,8 +1736,16 @@ void launch_cols_g(const float *x, int64_t R, int64_t C, int64_t ddof, const Col
 template <int V>
 void launch_cols_v(const float *x, int64_t R, int64_t C, int64_t ddof, const ColsWs &ws, float *var, float *mean,
                    hipStream_t st) {
-  if (g_tune.var_cols_waves == 16) launch_cols_g<V, 16>(x, R, C, ddof, ws, var, mean, st);
-  else if (g_tune.var_cols_waves == 8) launch_cols_g<V, 8>(x, R, C, ddof, ws, var, mean, st);
+  int waves = g_tune.var_cols_waves;
+  if (waves == 0) {  // auto: svx::cols_chunk_waves on this device's CU count
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 0;
+    waves = svx::cols_chunk_waves(V, R, C, cus);
+  }
+  if (waves == 16) launch_cols_g<V, 16>(x, R, C, ddof, ws, var, mean, st);
+  else if (waves == 8) launch_cols_g<V, 8>(x, R, C, ddof, ws, var, mean, st);
   else launch_cols_g<V, 4>(x, R, C, ddof, ws, var, mean, st);
 }
 
@@ -2929,8 +2937,8 @@ sv_status sv_set_tuning(const char *key, int64_t value) {
     return ok();
   }
   if (strcmp(key, "var_cols_waves") == 0) {
-    if (value != 4 && value != 8 && value != 16)
-      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_waves must be 4, 8 or 16");
+    if (value != 0 && value != 4 && value != 8 && value != 16)
+      return fail(SV_ERR_INVALID_ARGUMENT, "sv_set_tuning: var_cols_waves must be 0, 4, 8 or 16");
     g_tune.var_cols_waves = (int)value;
     return ok();
   }

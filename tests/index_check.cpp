@@ -396,7 +396,9 @@ void variance_f32(int64_t rows, int64_t cols, int axis, int off, const Knobs &k,
     }
     case Route::COLS_CHUNKED: {
       const int V = vec16 ? 4 : 1;
-      cols_chunked(c, rows, cols, V, k.cols_waves, cols_chunk_plan(V, k.cols_waves, rows, cols),
+      // cols_waves 0: the automatic choice on 256 CUs
+      const int cw = k.cols_waves ? k.cols_waves : cols_chunk_waves(V, rows, cols, 256);
+      cols_chunked(c, rows, cols, V, cw, cols_chunk_plan(V, cw, rows, cols),
                    (rows + CC_E * CC_MIN_W - 1) / (CC_E * CC_MIN_W), CC_GROUP);
       break;
     }
@@ -793,11 +795,11 @@ int main() {
                            8193, 12345, 16383, 16384, 16385, 20000, 32768, 32769, 65535, 65536, 65537, 100003};
   const RouteKnobs dflt{1, 1, 1024, 1, 1, 1, 1};
   std::vector<Knobs> knobs;
-  knobs.push_back({dflt, 0, 1, 1, 16});
+  knobs.push_back({dflt, 0, 1, 1, 0});
   for (int split : {1, 2, 4, 8}) knobs.push_back({dflt, split, 1, 1, 16});
   for (int lp : {0, 2}) knobs.push_back({dflt, 0, lp, 1, 16});
   knobs.push_back({dflt, 0, 1, 0, 16});
-  for (int cw : {4, 8}) knobs.push_back({{1, 0, 1024, 1, 1, 1, 0}, 0, 1, 1, cw});
+  for (int cw : {4, 8, 16}) knobs.push_back({{1, 0, 1024, 1, 1, 1, 0}, 0, 1, 1, cw});
   knobs.push_back({{0, 1, 1024, 0, 0, 0, 1}, 0, 1, 1, 16});
   knobs.push_back({{1, 1, 1024, 1, 1, 2, 1}, 0, 1, 1, 16});
   knobs.push_back({{1, 1, 1024, 1, 1, 3, 1}, 0, 1, 1, 16});
