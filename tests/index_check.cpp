@@ -775,6 +775,27 @@ void route_expectations() {
       {3000, 4100, true, false, "not a whole tile: no wide tile"},
       {4096, 2050, false, false, "513 and 257 tiles: the last round nearly empty"},
   };
+  // float32 column chunks under var_cols_waves 0 on 256 CUs (16-byte loads)
+  struct Waves {
+    int64_t R, C;
+    int want;
+    const char *why;
+  };
+  const Waves waves[] = {
+      {16384, 1024, 16, "256 workgroups of 16 waves: one full round"},
+      {65536, 256, 16, "256 workgroups: one full round"},
+      {20001, 1000, 8, "316 workgroups: the second round nearly empty"},
+      {4097, 4097, 8, "289 workgroups"},
+      {8000000, 8, 8, "two column groups: 32 row groups per wave"},
+      {3200000, 20, 8, "five column groups: 8 row groups per wave"},
+  };
+  for (const Waves &e : waves) {
+    const int got = cols_chunk_waves(4, e.R, e.C, 256);
+    if (got != e.want) {
+      printf("FAIL chunk waves [%lld, %lld]: %d, want %d (%s)\n", (long long)e.R, (long long)e.C, got, e.want, e.why);
+      ++g_fail;
+    }
+  }
   for (const Fill64 &e : fill64) {
     const bool wide = cols_one64_wide_ok(e.R, true) && one_round_fill(cols_one64_plan(e.R, e.C, true, true).blocks, 256);
     const bool one = one_round_fill(cols_one64_plan(e.R, e.C, true).blocks, 256) || wide;
